@@ -1,0 +1,432 @@
+"""Float64 CPU oracle of the GPTQ single-layer solver.
+
+TEST INFRASTRUCTURE. Only the test suite, the smoke check in __graft_entry__ and the CPU-baseline
+leg of bench.py may import this module. The product path (the HIP library and its Python binding)
+never imports, links or runs anything here, and this module imports nothing from the product.
+
+It is a plain, slow, step-by-step statement of what the solver computes, written from these pages:
+
+* GPTQ tools page (ozercemkelahmet.com/tools/gptq), "How it works", Steps 3-8, "Optional
+  refinements" and the section "A minimal Python sketch" (the sketch is read as a description of
+  the computation, not transcribed).
+* "GPTQ Quantization: Complete Technical Guide" (notes.jayaprakash.net), sections "Quantization
+  Equation", "Example: Quantizing a Single Weight", "Computing the Hessian", "Damping Factor".
+* "Paper breakdown: GPTQ" (ai360xpert.com), "How It Works" (lazy batching).
+* "What Is GPTQ? Classic 4-Bit LLM Quantization" (ai-tldr.dev), "How it works", Step 3 (groups).
+
+Arithmetic is float64 throughout (inputs are upcast exactly), with one exception: the two
+rounding decisions (a code from w / scale, a zero point from -wmin / scale) divide in float32,
+because the pages' sketch computes on float32 tensors and the GPU kernels decide in float32.
+Dense algebra uses library primitives: BLAS matrix products and the LAPACK Cholesky routines
+(potrf / potri) that the sketch's cholesky / cholesky_inverse / cholesky(upper) calls name.
+
+Readings taken where the pages are silent, garbled or disagree (each is listed in the design doc):
+
+* H is accumulated as the sum over token chunks of 2 X_c^T X_c and normalised by the token count
+  n before damping (the sketch's 2 X^T X / n).
+* Damping adds damp * mean(diag(H/n)) to the diagonal (tools page Step 4 and the sketch), not
+  damp * trace(H) (Technical Guide, "Damping Factor").
+* Grids are asymmetric min/max grids with unsigned codes in [0, 2^bits - 1]; a group is g
+  consecutive columns of one row in processing order; group_size <= 0 means one group per row.
+* A group's grid is computed from the current (error-updated) weights at the group's first column.
+* Blocks and groups must nest (B % g == 0 or g % B == 0); the last block and last group may be short.
+* Act-order processes columns by descending diag(H); ties keep the lower original index first.
+* Rounding is round-half-to-even (numpy rint), as torch.round in the sketch.
+
+Parity unpinned (no example on the pages fixes them; they rest on the readings above): the moment a
+group grid is taken when g < d, and the act-order tie-break.
+"""
+
+from __future__ import annotations
+
+from dataclasses import dataclass, field
+from typing import Iterable, Optional, Tuple
+
+import numpy as np
+from scipy.linalg import lapack
+
+
+class NotPositiveDefinite(ArithmeticError):
+    """The damped Hessian has a non-positive pivot (1-based index `pivot`, LAPACK convention)."""
+
+    def __init__(self, pivot: int):
+        super().__init__(f"leading minor {pivot} is not positive definite")
+        self.pivot = int(pivot)
+
+
+# --------------------------------------------------------------------------------------------
+# Hessian, damping, ordering, factor  (tools page Steps 3, 4, 6; sketch; "Optional refinements")
+# --------------------------------------------------------------------------------------------
+
+def hessian(chunks: Iterable[np.ndarray]) -> Tuple[np.ndarray, int]:
+    """Unnormalised Hessian sum over token chunks: sum_c 2 X_c^T X_c, and the token count n.
+
+    Each X_c is (tokens x d). The layer Hessian is proportional to X X^T in the pages' feature-major
+    notation (tools page, Step 3); the sketch forms 2 X^T X / n with X = (samples x features), and
+    the Technical Guide ("Computing the Hessian") sums outer products and then averages.
+    """
+    H = None
+    n = 0
+    for xc in chunks:
+        x = np.asarray(xc, dtype=np.float64)
+        if H is None:
+            H = np.zeros((x.shape[1], x.shape[1]), dtype=np.float64)
+        H += 2.0 * (x.T @ x)
+        n += x.shape[0]
+    if H is None:
+        raise ValueError("no calibration chunks")
+    return H, n
+
+
+def act_order_perm(H: np.ndarray) -> np.ndarray:
+    """Processing order for act-order: columns by descending diag(H), ties by lower index first.
+
+    Tools page, "Optional refinements", Act-order.
+    """
+    diag = np.diag(H)
+    return np.argsort(-diag, kind="stable").astype(np.int64)
+
+
+def damp_and_order(H: np.ndarray, n: int, damp: float, act_order: bool,
+                   perm: Optional[np.ndarray] = None) -> Tuple[np.ndarray, np.ndarray, float]:
+    """Normalise, damp and (optionally) reorder: Hhat = (H/n + lam I)[perm][:, perm].
+
+    lam = damp * mean(diag(H/n)) (tools page, Step 4: about one percent of the average diagonal).
+    `perm` may be given to impose a processing order (a test uses it to follow another
+    implementation's order among keys equal within rounding); otherwise it is act_order_perm(H)
+    when act_order is set and the identity when not.
+    """
+    d = H.shape[0]
+    Hn = np.asarray(H, dtype=np.float64) / float(n)
+    mean_diag = float(np.mean(np.diag(Hn)))
+    if not (mean_diag > 0.0):
+        raise ValueError("mean of diag(H) must be positive")
+    lam = float(damp) * mean_diag
+    Hd = Hn + lam * np.eye(d)
+    if perm is None:
+        perm = act_order_perm(H) if act_order else np.arange(d, dtype=np.int64)
+    perm = np.asarray(perm, dtype=np.int64)
+    return Hd[np.ix_(perm, perm)], perm, lam
+
+
+def inverse_cholesky_upper(Hhat: np.ndarray) -> np.ndarray:
+    """U: the upper Cholesky factor of Hhat^-1, so that Hhat^-1 = U^T U.
+
+    Tools page, Step 6 (the Cholesky factor of the inverse Hessian is computed once) and the
+    sketch's three calls: the Cholesky factor of Hhat, the inverse from that factor, then the
+    upper Cholesky factor of the inverse. Raises NotPositiveDefinite with the failing pivot.
+    """
+    c, info = lapack.dpotrf(np.asarray(Hhat, dtype=np.float64), lower=1, clean=1)
+    if info > 0:
+        raise NotPositiveDefinite(info)
+    if info < 0:
+        raise ValueError(f"dpotrf argument {-info}")
+    inv, info = lapack.dpotri(c, lower=1)
+    if info != 0:
+        raise NotPositiveDefinite(info)
+    inv = np.tril(inv) + np.tril(inv, -1).T
+    u, info = lapack.dpotrf(inv, lower=0, clean=1)
+    if info != 0:
+        raise NotPositiveDefinite(info)
+    return np.triu(u)
+
+
+# --------------------------------------------------------------------------------------------
+# The grid  (sketch's quantize_to_grid and its per-row min/max grid; Technical Guide,
+# "Quantization Equation"; What Is GPTQ?, Step 3 for groups)
+# --------------------------------------------------------------------------------------------
+
+def _round_ratio(num: np.ndarray, den: np.ndarray) -> np.ndarray:
+    """rint(num / den) with the division taken in float32 (the decision precision)."""
+    return np.rint(np.asarray(num, dtype=np.float32) / np.asarray(den, dtype=np.float32)).astype(np.float64)
+
+
+def _ratio32(num, den) -> np.ndarray:
+    return (np.asarray(num, dtype=np.float32) / np.asarray(den, dtype=np.float32)).astype(np.float64)
+
+
+def group_grid(wg: np.ndarray, maxq: int) -> Tuple[np.ndarray, np.ndarray]:
+    """Asymmetric min/max grid of each row of wg (rows x columns of one group).
+
+    scale = max(wmax - wmin, 1e-8) / maxq and zero = round(-wmin / scale).
+    """
+    wmin = np.min(wg, axis=1)
+    wmax = np.max(wg, axis=1)
+    scale = np.maximum(wmax - wmin, 1e-8) / float(maxq)
+    zero = _round_ratio(-wmin, scale)
+    return scale, zero
+
+
+def quantize_to_grid(w: np.ndarray, scale: np.ndarray, zero: np.ndarray, maxq: int) -> Tuple[np.ndarray, np.ndarray]:
+    """Code q = clamp(round(w / scale) + zero, 0, maxq) and its value scale * (q - zero)."""
+    q = np.clip(_round_ratio(w, scale) + zero, 0.0, float(maxq))
+    return q, scale * (q - zero)
+
+
+# --------------------------------------------------------------------------------------------
+# The column loop with lazy blocks  (tools page Steps 5, 7, 8; Paper breakdown "How It Works")
+# --------------------------------------------------------------------------------------------
+
+@dataclass
+class QuantResult:
+    codes: np.ndarray       # uint8 rows x d, original column order
+    scales: np.ndarray      # float64 rows x ngroups (groups in processing order)
+    zeros: np.ndarray       # int32 rows x ngroups
+    g_idx: np.ndarray       # int32 d: group of each original column
+    perm: np.ndarray        # int64 d: processing order (perm[j] = original column processed j-th)
+    loss: float             # sum over rows and columns of err^2
+    row_loss: np.ndarray    # float64 rows
+    Q: np.ndarray           # float64 rows x d dequantised weights, original column order
+    codes_proc: np.ndarray  # uint8 rows x d, processing order
+    w_seen: Optional[np.ndarray] = None  # rows x d, processing order: each weight when it was quantized
+    adopted: int = 0        # follow mode: tie-window decisions taken from the followed result
+    adopted_diff: int = 0   # ... of which differ from this oracle's own choice
+    near_ties: int = 0      # decisions whose ratio lay inside the tie window
+    extra: dict = field(default_factory=dict)
+
+
+def check_geometry(d: int, group_size: int, block_size: int) -> int:
+    """Effective group size; raises ValueError for shapes the solver rejects."""
+    if d <= 0:
+        raise ValueError("d must be positive")
+    g = d if group_size <= 0 else int(group_size)
+    if g == 1:
+        raise ValueError("group_size 1 is rejected (Technical Guide, Don'ts: group_size=1 will fail)")
+    if block_size <= 0:
+        raise ValueError("block_size must be positive")
+    if g < d and not (block_size % g == 0 or g % block_size == 0):
+        raise ValueError("block_size and group_size must nest")
+    return g
+
+
+def _follow_pick(own: np.ndarray, ratio: np.ndarray, offset: np.ndarray, lo: float, hi: float,
+                 other: Optional[np.ndarray], tau: float):
+    """Take `other` where ratio lies within tau of a half-integer and other is a neighbour choice."""
+    frac = ratio - np.floor(ratio)
+    tie = np.abs(frac - 0.5) < tau
+    if other is None or not np.any(tie):
+        return own, 0, 0, int(np.count_nonzero(tie))
+    c1 = np.clip(np.floor(ratio) + offset, lo, hi)
+    c2 = np.clip(np.ceil(ratio) + offset, lo, hi)
+    ok = tie & ((other == c1) | (other == c2))
+    out = np.where(ok, other, own)
+    return out, int(np.count_nonzero(ok)), int(np.count_nonzero(ok & (other != own))), int(np.count_nonzero(tie))
+
+
+def quantize_layer(W: np.ndarray, U: np.ndarray, bits: int, group_size: int, block_size: int,
+                   perm: Optional[np.ndarray] = None, grid: Optional[Tuple[np.ndarray, np.ndarray]] = None,
+                   follow: Optional[Tuple[np.ndarray, np.ndarray]] = None, tau: float = 1e-3) -> QuantResult:
+    """Quantize W (rows x d, original column order) with U (upper, processing order).
+
+    For each block of B columns in processing order, and each column i in it:
+      * at a group's first column, the group grid comes from the current weights of its columns;
+      * q = clamp(round(w/s) + z, 0, maxq); err = (w - s (q - z)) / U[i, i]   (Step 5, parts 1-3);
+      * the columns after i inside the block take -err * U[i, j] at once       (Step 5, part 4);
+      * the block's errors are kept and, at block end, the columns after the block take
+        -Err @ U[block, after] in one product                                  (Step 7, lazy batch).
+    Step 8: one (scale, zero) per group; codes are returned in the original column order with g_idx.
+
+    grid: optional fixed (scales, zeros), rows x ngroups, used instead of min/max grids.
+    follow: optional (codes, zeros) of another implementation in processing order; at decisions whose
+    float32 ratio lies within `tau` of a half-integer this oracle takes that implementation's choice
+    when it is one of the two nearest grid points (both are correct roundings within the tie window).
+    """
+    W = np.asarray(W, dtype=np.float64)
+    rows, d = W.shape
+    U = np.asarray(U, dtype=np.float64)
+    if U.shape != (d, d):
+        raise ValueError("U shape")
+    g = check_geometry(d, group_size, block_size)
+    B = int(block_size)
+    maxq = (1 << int(bits)) - 1
+    ngroups = (d + g - 1) // g
+    perm = np.arange(d, dtype=np.int64) if perm is None else np.asarray(perm, dtype=np.int64)
+
+    Wp = W[:, perm].copy()                      # working copy, processing order
+    codes_p = np.zeros((rows, d), dtype=np.float64)
+    Qp = np.zeros((rows, d), dtype=np.float64)
+    seen = np.zeros((rows, d), dtype=np.float64)
+    scales = np.zeros((rows, ngroups), dtype=np.float64)
+    zeros = np.zeros((rows, ngroups), dtype=np.float64)
+    row_loss = np.zeros(rows, dtype=np.float64)
+    f_codes = None if follow is None else np.asarray(follow[0], dtype=np.float64)
+    f_zeros = None if follow is None else np.asarray(follow[1], dtype=np.float64)
+    adopted = adopted_diff = near = 0
+
+    s = z = None
+    for b in range(0, d, B):
+        e_blk = min(b + B, d)
+        Err = np.zeros((rows, e_blk - b), dtype=np.float64)
+        for i in range(b, e_blk):
+            if i % g == 0:
+                gi = i // g
+                if grid is not None:
+                    s = np.asarray(grid[0], dtype=np.float64)[:, gi]
+                    z = np.asarray(grid[1], dtype=np.float64)[:, gi]
+                else:
+                    s, z = group_grid(Wp[:, i:min(i + g, d)], maxq)
+                    if f_zeros is not None:
+                        wmin = np.min(Wp[:, i:min(i + g, d)], axis=1)
+                        z, a, ad, nt = _follow_pick(z, _ratio32(-wmin, s), np.zeros(rows), -np.inf, np.inf,
+                                                    f_zeros[:, gi], tau)
+                        adopted += a
+                        adopted_diff += ad
+                        near += nt
+                scales[:, gi] = s
+                zeros[:, gi] = z
+            w = Wp[:, i].copy()
+            seen[:, i] = w
+            q, dq = quantize_to_grid(w, s, z, maxq)
+            if f_codes is not None:
+                q2, a, ad, nt = _follow_pick(q, _ratio32(w, s), z, 0.0, float(maxq), f_codes[:, i], tau)
+                if a:
+                    q = q2
+                    dq = s * (q - z)
+                adopted += a
+                adopted_diff += ad
+                near += nt
+            codes_p[:, i] = q
+            Qp[:, i] = dq
+            err = (w - dq) / U[i, i]
+            Err[:, i - b] = err
+            row_loss += err * err
+            if i + 1 < e_blk:
+                Wp[:, i + 1:e_blk] -= np.outer(err, U[i, i + 1:e_blk])
+        if e_blk < d:
+            Wp[:, e_blk:] -= Err @ U[b:e_blk, e_blk:]
+
+    codes = np.zeros((rows, d), dtype=np.uint8)
+    codes[:, perm] = codes_p.astype(np.uint8)
+    Q = np.zeros((rows, d), dtype=np.float64)
+    Q[:, perm] = Qp
+    g_idx = np.zeros(d, dtype=np.int32)
+    g_idx[perm] = (np.arange(d) // g).astype(np.int32)
+    return QuantResult(codes=codes, scales=scales, zeros=zeros.astype(np.int32), g_idx=g_idx, perm=perm,
+                       loss=float(np.sum(row_loss)), row_loss=row_loss, Q=Q,
+                       codes_proc=codes_p.astype(np.uint8), w_seen=seen, adopted=adopted, adopted_diff=adopted_diff,
+                       near_ties=near)
+
+
+# --------------------------------------------------------------------------------------------
+# Packing  (tools page, Step 8: eight 4-bit codes per 32-bit word)
+# --------------------------------------------------------------------------------------------
+
+def pack(codes: np.ndarray, bits: int) -> np.ndarray:
+    """int32 words: nibble t (bits 4t..4t+3) of word k in a row holds column 8k + t."""
+    c = np.asarray(codes)
+    rows, d = c.shape
+    if d % 8 != 0:
+        raise ValueError("d must be a multiple of 8")
+    if not (1 <= bits <= 4):
+        raise ValueError("nibble packing holds codes of at most 4 bits")
+    if np.any(c.astype(np.int64) >= (1 << bits)) or np.any(c.astype(np.int64) < 0):
+        raise ValueError("code out of range")
+    words = np.zeros((rows, d // 8), dtype=np.uint64)
+    for t in range(8):
+        words |= c[:, t::8].astype(np.uint64) << np.uint64(4 * t)
+    return words.astype(np.uint32).view(np.int32)
+
+
+def unpack(packed: np.ndarray, d: int) -> np.ndarray:
+    """Inverse of pack."""
+    p = np.asarray(packed).view(np.uint32).astype(np.uint64)
+    out = np.zeros((p.shape[0], d), dtype=np.uint8)
+    for t in range(8):
+        out[:, t::8] = ((p >> np.uint64(4 * t)) & np.uint64(15)).astype(np.uint8)
+    return out
+
+
+def bits_per_weight(bits: int, group_size: int, scale_bits: int = 16, zero_bits: int = 4) -> float:
+    """Storage cost per weight with one scale and zero per group (tools page, "Memory arithmetic")."""
+    return bits + (scale_bits + zero_bits) / float(group_size)
+
+
+# --------------------------------------------------------------------------------------------
+# Whole layer, baselines and the objective
+# --------------------------------------------------------------------------------------------
+
+@dataclass
+class LayerResult:
+    H: np.ndarray
+    n: int
+    Hhat: np.ndarray
+    lam: float
+    U: np.ndarray
+    quant: QuantResult
+    packed: Optional[np.ndarray]
+
+
+def gptq(W: np.ndarray, chunks: Iterable[np.ndarray], bits: int, group_size: int, block_size: int,
+         act_order: bool = False, damp: float = 0.01, perm: Optional[np.ndarray] = None,
+         follow: Optional[Tuple[np.ndarray, np.ndarray]] = None, tau: float = 1e-3,
+         H: Optional[np.ndarray] = None, n: Optional[int] = None) -> LayerResult:
+    """The whole single-layer solver: Hessian, damping and order, factor, column loop, packing."""
+    if H is None:
+        H, n = hessian(chunks)
+    Hhat, p, lam = damp_and_order(H, n, damp, act_order, perm)
+    U = inverse_cholesky_upper(Hhat)
+    qr = quantize_layer(W, U, bits, group_size, block_size, perm=p, follow=follow, tau=tau)
+    d = qr.codes.shape[1]
+    packed = pack(qr.codes, bits) if (d % 8 == 0 and bits <= 4) else None
+    return LayerResult(H=H, n=n, Hhat=Hhat, lam=lam, U=U, quant=qr, packed=packed)
+
+
+def rtn(W: np.ndarray, bits: int, group_size: int, perm: Optional[np.ndarray] = None) -> QuantResult:
+    """Round-to-nearest baseline: the same grids, taken from the unmodified weights, no feedback."""
+    W = np.asarray(W, dtype=np.float64)
+    rows, d = W.shape
+    g = d if group_size <= 0 else int(group_size)
+    maxq = (1 << int(bits)) - 1
+    perm = np.arange(d, dtype=np.int64) if perm is None else np.asarray(perm, dtype=np.int64)
+    Wp = W[:, perm]
+    ngroups = (d + g - 1) // g
+    codes_p = np.zeros((rows, d))
+    Qp = np.zeros((rows, d))
+    scales = np.zeros((rows, ngroups))
+    zeros = np.zeros((rows, ngroups))
+    for gi in range(ngroups):
+        sl = slice(gi * g, min((gi + 1) * g, d))
+        s, z = group_grid(Wp[:, sl], maxq)
+        q, dq = quantize_to_grid(Wp[:, sl], s[:, None], z[:, None], maxq)
+        codes_p[:, sl] = q
+        Qp[:, sl] = dq
+        scales[:, gi] = s
+        zeros[:, gi] = z
+    codes = np.zeros((rows, d), dtype=np.uint8)
+    codes[:, perm] = codes_p.astype(np.uint8)
+    Q = np.zeros((rows, d))
+    Q[:, perm] = Qp
+    g_idx = np.zeros(d, dtype=np.int32)
+    g_idx[perm] = (np.arange(d) // g).astype(np.int32)
+    return QuantResult(codes=codes, scales=scales, zeros=zeros.astype(np.int32), g_idx=g_idx, perm=perm,
+                       loss=float("nan"), row_loss=np.full(rows, np.nan), Q=Q, codes_proc=codes_p.astype(np.uint8))
+
+
+def objective(W: np.ndarray, Q: np.ndarray, Hhat: np.ndarray) -> float:
+    """sum over rows of (W - Q)_r Hhat (W - Q)_r^T (tools page, Step 2, with the damped Hessian).
+
+    W, Q and Hhat must be in the same column order.
+    """
+    D = np.asarray(W, dtype=np.float64) - np.asarray(Q, dtype=np.float64)
+    return float(np.sum((D @ Hhat) * D))
+
+
+def brute_force(W: np.ndarray, Hhat: np.ndarray, bits: int) -> Tuple[float, np.ndarray]:
+    """Exhaustive minimum of the objective over each row's grid (one group per row; tiny d only)."""
+    W = np.asarray(W, dtype=np.float64)
+    rows, d = W.shape
+    if d > 8:
+        raise ValueError("brute force is for d <= 8")
+    maxq = (1 << int(bits)) - 1
+    s, z = group_grid(W, maxq)
+    grids = np.stack(np.meshgrid(*([np.arange(maxq + 1, dtype=np.float64)] * d), indexing="ij"), -1).reshape(-1, d)
+    best = 0.0
+    bestQ = np.zeros_like(W)
+    for r in range(rows):
+        dq = s[r] * (grids - z[r])
+        D = W[r][None, :] - dq
+        f = np.sum((D @ Hhat) * D, axis=1)
+        k = int(np.argmin(f))
+        best += float(f[k])
+        bestQ[r] = dq[k]
+    return best, bestQ

@@ -1,0 +1,119 @@
+"""Planted mistakes in the oracle must be caught by its pins (CPU only).
+
+Each case edits one line of the oracle's source in memory (a dropped term, a wrong sign, a wrong
+index, a transposed operand), loads the edited copy as a separate module and checks that at least
+one pin-style check rejects it. The committed oracle is never modified.
+"""
+
+import inspect
+import sys
+import types
+
+import numpy as np
+import pytest
+
+from oracle import gptq_ref as ref
+
+MUTATIONS = [
+    ("drop lazy update", "Wp[:, e_blk:] -= Err @ U[b:e_blk, e_blk:]", "pass"),
+    ("wrong update sign", "Wp[:, i + 1:e_blk] -= np.outer(err, U[i, i + 1:e_blk])",
+     "Wp[:, i + 1:e_blk] += np.outer(err, U[i, i + 1:e_blk])"),
+    ("transposed factor row", "Wp[:, i + 1:e_blk] -= np.outer(err, U[i, i + 1:e_blk])",
+     "Wp[:, i + 1:e_blk] -= np.outer(err, U[i + 1:e_blk, i])"),
+    ("unscaled error", "err = (w - dq) / U[i, i]", "err = (w - dq)"),
+    ("transposed lazy operand", "Wp[:, e_blk:] -= Err @ U[b:e_blk, e_blk:]",
+     "Wp[:, e_blk:] -= Err @ U[e_blk:, b:e_blk].T[:, :U.shape[0] - e_blk]"),
+    ("grid from original weights", "s, z = group_grid(Wp[:, i:min(i + g, d)], maxq)",
+     "s, z = group_grid(W[:, perm][:, i:min(i + g, d)], maxq)"),
+    ("zero not added", "q = np.clip(_round_ratio(w, scale) + zero, 0.0, float(maxq))",
+     "q = np.clip(_round_ratio(w, scale), 0.0, float(maxq))"),
+    ("inverse not factored", "    u, info = lapack.dpotrf(inv, lower=0, clean=1)",
+     "    u, info = np.triu(inv), 0"),
+    ("damping on trace", "lam = float(damp) * mean_diag", "lam = float(damp) * mean_diag * d"),
+    ("act-order ascending", "return np.argsort(-diag, kind=\"stable\").astype(np.int64)",
+     "return np.argsort(diag, kind=\"stable\").astype(np.int64)"),
+    ("hessian without factor 2", "H += 2.0 * (x.T @ x)", "H += (x.T @ x)"),
+    ("pack nibble order", "words |= c[:, t::8].astype(np.uint64) << np.uint64(4 * t)",
+     "words |= c[:, t::8].astype(np.uint64) << np.uint64(4 * (7 - t))"),
+]
+
+
+def _mutant(old, new):
+    src = inspect.getsource(ref)
+    assert src.count(old) >= 1, old
+    mod = types.ModuleType("gptq_ref_mutant")
+    sys.modules["gptq_ref_mutant"] = mod      # dataclasses look their module up by name
+    try:
+        exec(compile(src.replace(old, new), "gptq_ref_mutant", "exec"), mod.__dict__)
+    finally:
+        sys.modules.pop("gptq_ref_mutant", None)
+    return mod
+
+
+def _checks(m):
+    """Return the names of the pin-style checks the module fails."""
+    failed = []
+    rng = np.random.default_rng(5)
+    d, rows, n = 64, 8, 96
+    z = rng.standard_normal((n, d))
+    X = z @ (0.2 * np.eye(d) + 0.8 * rng.standard_normal((d, d)) / np.sqrt(d))
+    X = X * rng.uniform(0.5, 2.0, d)[None, :]
+    W = rng.standard_normal((rows, d)) * 0.02
+    try:
+        r = m.gptq(W, [X], 4, 16, 32, act_order=True, damp=0.01)
+        p = r.quant.perm
+        obj = ref.objective(W[:, p], r.quant.Q[:, p], r.Hhat)
+        if not np.isclose(r.quant.loss, obj, rtol=1e-9):
+            failed.append("loss identity")
+        D = W - r.quant.Q
+        if not np.isclose(np.sum((X @ D.T) ** 2), n / 2 * (r.quant.loss - r.lam * np.sum(D * D)), rtol=1e-8):
+            failed.append("output identity")
+        r1 = m.gptq(W, [X], 4, 16, 1, act_order=True, damp=0.01)
+        if not np.array_equal(r1.quant.codes, r.quant.codes):
+            failed.append("blocked == unblocked")
+        if not np.allclose(r.U.T @ r.U @ r.Hhat, np.eye(d), atol=1e-8) or np.any(np.tril(r.U, -1) != 0):
+            failed.append("factor")
+        # each group's grid is the min/max grid of its weights as they stood at the group's first
+        # column: original weights minus the closed-form total update Err[:, :k] @ U[:k, group]
+        Wp = W[:, p]
+        err = (r.quant.w_seen - r.quant.Q[:, p]) / np.diag(r.U)[None, :]
+        for gi in range(1, d // 16):
+            k = gi * 16
+            cur = Wp[:, k:k + 16] - err[:, :k] @ r.U[:k, k:k + 16]
+            s_want = np.maximum(cur.max(1) - cur.min(1), 1e-8) / 15
+            if not np.allclose(r.quant.scales[:, gi], s_want, rtol=1e-9):
+                failed.append("grid at group start")
+                break
+        if not np.all(np.diff(np.diag(r.H)[p]) <= 0):
+            failed.append("act-order")
+        Xi = rng.integers(-3, 4, size=(5, 4)).astype(np.float64)
+        want = np.zeros((4, 4))
+        for t in range(5):
+            want += 2 * np.outer(Xi[t], Xi[t])
+        if not np.array_equal(m.hessian([Xi])[0], want):
+            failed.append("hessian definition")
+        if m.pack(np.array([[1, 2, 3, 4, 5, 6, 7, 8]], np.uint8), 4)[0, 0] != np.array(
+                [0x87654321], np.uint32).view(np.int32)[0]:
+            failed.append("pack closed form")
+        Hs = np.diag([2.0, 4.0, 6.0]) * 10
+        if not np.isclose(m.damp_and_order(Hs, 10, 0.01, False)[2], 0.04):
+            failed.append("damping mean diag")
+        q, _ = m.quantize_to_grid(np.array([0.75]), np.array([0.1]), np.array([2.0]), 15)
+        if q[0] != 10:
+            failed.append("grid primitive")
+        # H = I must reduce to round-to-nearest with dynamic grids
+        rI = m.gptq(W, None, 4, 16, 32, H=np.eye(d) * 2.0, n=1)
+        if not np.array_equal(rI.quant.codes, ref.rtn(W, 4, 16).codes):
+            failed.append("identity -> rtn")
+    except Exception as e:  # a crash is also a rejection
+        failed.append(f"raised {type(e).__name__}")
+    return failed
+
+
+def test_unmodified_oracle_passes_checks():
+    assert _checks(ref) == []
+
+
+@pytest.mark.parametrize("name,old,new", MUTATIONS, ids=[m[0] for m in MUTATIONS])
+def test_planted_mistake_is_caught(name, old, new):
+    assert _checks(_mutant(old, new)), name

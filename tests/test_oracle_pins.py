@@ -1,0 +1,424 @@
+"""Pins of the float64 oracle against what the pages and the mathematics fix (CPU only).
+
+Each test names the passage or the closed form it checks. Together they are chosen so that a
+dropped term, a wrong sign or index, or a transposed operand anywhere in the oracle fails one of them.
+"""
+
+import json
+import os
+
+import numpy as np
+import pytest
+
+from oracle import gptq_ref as ref
+
+GOLD = json.load(open(os.path.join(os.path.dirname(__file__), "golden", "worked_examples.json")))
+
+
+def _correlated_x(rng, n, d, mix=0.8):
+    z = rng.standard_normal((n, d))
+    m = np.eye(d) * (1 - mix) + mix * rng.standard_normal((d, d)) / np.sqrt(d)
+    return z @ m
+
+
+def _solve(W, X, bits, g, B, act=False, damp=0.01):
+    return ref.gptq(W, [X], bits, g, B, act_order=act, damp=damp)
+
+
+# ---------------------------------------------------------------- grid primitive (page examples)
+
+def test_quantization_equation_example():
+    e = GOLD["quantization_equation"]
+    q, dq = ref.quantize_to_grid(np.array([e["original"]]), np.array([e["scale"]]), np.array([0.0]), 15)
+    assert q[0] == e["quantized"]
+    assert dq[0] == pytest.approx(e["recovered"], abs=1e-15)
+    assert abs(e["original"] - dq[0]) == pytest.approx(e["abs_error"], abs=1e-15)
+
+
+def test_quantization_equation_through_solver():
+    # A row whose min/max are 0 and 1.5 at 4 bits has scale 1.5/15 = 0.1; with H = I there is no
+    # feedback, so the weight 0.75 must take code 8 (value 0.8).
+    W = np.array([[0.0, 1.5, 0.75, 0.3]])
+    X = np.eye(4) * np.sqrt(0.5)          # 2 X^T X = I
+    r = ref.gptq(W, [X], 4, 0, 4, damp=0.01, H=np.eye(4) * 4.0, n=4)
+    assert r.quant.scales[0, 0] == pytest.approx(0.1, rel=1e-15)
+    assert r.quant.zeros[0, 0] == 0
+    assert r.quant.codes[0, 2] == 8
+    assert r.quant.Q[0, 2] == pytest.approx(0.8, abs=1e-15)
+
+
+def test_single_weight_example():
+    e = GOLD["single_weight"]
+    q, dq = ref.quantize_to_grid(np.array([e["original"]]), np.array([e["scale"]]), np.array([0.0]), 15)
+    assert q[0] == e["quantized"]
+    assert dq[0] == pytest.approx(e["dequantized"], abs=1e-15)
+    assert e["original"] - dq[0] == pytest.approx(e["error"], abs=1e-12)
+
+
+def test_two_weight_correlated_example():
+    e = GOLD["two_weights"]
+    rho = e["correlation_near_one"]
+    Hh = np.array([[1.0, rho], [rho, 1.0]])
+    U = ref.inverse_cholesky_upper(Hh)
+    W = np.array([e["weights"]])
+    step = e["grid_step"]
+    grid = (np.full((1, 1), step), np.zeros((1, 1)))
+    r = ref.quantize_layer(W, U, 2, 0, 2, grid=grid)
+    # first weight rounds as RTN does
+    assert r.Q[0, 0] == pytest.approx(e["rtn"][0], abs=1e-15)
+    # the correction reduces the second weight: 0.31 - 0.1 * rho = 0.2101, "about 0.21"
+    w2 = r.w_seen[0, 1]
+    assert w2 == pytest.approx(0.31 - 0.1 * rho, abs=1e-12)
+    assert abs(w2 - e["second_weight_after_correction_about"]) < 0.005
+    assert r.Q[0, 1] == pytest.approx(e["second_weight_rounds_to"], abs=1e-15)
+    # plain rounding of the pair and its errors
+    rq = np.rint(W / step) * step
+    assert np.allclose(rq[0], e["rtn"], atol=1e-15)
+    assert np.allclose(rq[0] - W[0], e["rtn_errors"], atol=1e-12)
+
+
+# ---------------------------------------------------------------- reductions to RTN
+
+@pytest.mark.parametrize("g,B", [(16, 32), (32, 16), (0, 16), (64, 64)])
+def test_identity_hessian_is_rtn(g, B):
+    rng = np.random.default_rng(11)
+    W = rng.standard_normal((24, 64)) * 0.02
+    r = ref.gptq(W, None, 4, g, B, H=np.eye(64) * 2.0, n=1)
+    t = ref.rtn(W, 4, g)
+    assert np.array_equal(r.quant.codes, t.codes)
+    assert np.allclose(r.quant.scales, t.scales, rtol=0, atol=0)
+    assert np.array_equal(r.quant.zeros, t.zeros)
+
+
+@pytest.mark.parametrize("act", [False, True])
+def test_diagonal_hessian_is_rtn(act):
+    rng = np.random.default_rng(12)
+    d = 48
+    W = rng.standard_normal((10, d)) * 0.02
+    H = np.diag(rng.uniform(0.5, 4.0, d))
+    r = ref.gptq(W, None, 3, 16, 16, act_order=act, H=H, n=1)
+    t = ref.rtn(W, 3, 16, perm=r.quant.perm)
+    assert np.array_equal(r.quant.codes, t.codes)
+    if act:
+        assert not np.array_equal(r.quant.perm, np.arange(d))
+
+
+# ---------------------------------------------------------------- loss identities
+
+@pytest.mark.parametrize("bits,g,B,act", [(4, 16, 32, False), (3, 0, 16, False), (2, 8, 8, True), (4, 32, 16, True)])
+def test_loss_identity(bits, g, B, act):
+    """sum err^2 == sum_r (W-Q)_r Hhat (W-Q)_r^T, and == (2/n)||X (W-Q)^T||^2 + lam ||W-Q||^2.
+
+    The sequential updates are exact minimisers of the damped quadratic over the not yet quantized
+    columns (tools page, Steps 5-6), so the accumulated squared scaled errors equal the objective.
+    """
+    rng = np.random.default_rng(100 + bits + g + B)
+    d, rows, n = 64, 12, 96
+    X = _correlated_x(rng, n, d)
+    W = rng.standard_normal((rows, d)) * 0.02
+    r = _solve(W, X, bits, g, B, act)
+    p = r.quant.perm
+    obj = ref.objective(W[:, p], r.quant.Q[:, p], r.Hhat)
+    assert r.quant.loss == pytest.approx(obj, rel=1e-10)
+    D = W - r.quant.Q
+    outputs = np.sum((X @ D.T) ** 2)
+    assert outputs == pytest.approx(n / 2 * (r.quant.loss - r.lam * np.sum(D * D)), rel=1e-9)
+
+
+def test_cholesky_rows_are_sequential_inverse():
+    """U[k,k]^2 = [Hhat_FF^-1]_kk and U[k,F]/U[k,k] = Hhat_FF^-1[k,:]/[Hhat_FF^-1]_kk, F = {k..d-1}."""
+    rng = np.random.default_rng(3)
+    d = 12
+    X = _correlated_x(rng, 40, d)
+    Hh = 2 * X.T @ X / 40 + 0.01 * np.eye(d)
+    U = ref.inverse_cholesky_upper(Hh)
+    for k in range(d):
+        inv = np.linalg.inv(Hh[k:, k:])
+        assert U[k, k] ** 2 == pytest.approx(inv[0, 0], rel=1e-10)
+        assert np.allclose(U[k, k:] / U[k, k], inv[0, :] / inv[0, 0], rtol=1e-9, atol=1e-12)
+
+
+def test_factor_properties():
+    rng = np.random.default_rng(4)
+    d = 40
+    X = _correlated_x(rng, 200, d)
+    Hh = 2 * X.T @ X / 200 + 0.05 * np.eye(d)
+    U = ref.inverse_cholesky_upper(Hh)
+    assert np.allclose(np.tril(U, -1), 0)
+    assert np.all(np.diag(U) > 0)
+    assert np.allclose(U.T @ U @ Hh, np.eye(d), atol=1e-10)
+    # the reversed-order route: U = J chol(J Hhat J)^-1 J
+    J = np.eye(d)[::-1]
+    U2 = J @ np.linalg.inv(np.linalg.cholesky(J @ Hh @ J)) @ J
+    assert np.allclose(U, U2, rtol=1e-9, atol=1e-12)
+
+
+# ---------------------------------------------------------------- lazy blocks
+
+@pytest.mark.parametrize("act", [False, True])
+def test_blocked_equals_unblocked(act):
+    """Lazy batching is a reorganisation (tools page, Step 7): every nesting block size gives the
+    same codes as the column-at-a-time loop."""
+    rng = np.random.default_rng(21)
+    d, rows = 128, 16
+    X = _correlated_x(rng, 160, d)
+    W = rng.standard_normal((rows, d)) * 0.02
+    base = _solve(W, X, 4, 32, 1, act)
+    for B in (8, 32, 64, 128):
+        r = _solve(W, X, 4, 32, B, act)
+        assert np.array_equal(r.quant.codes, base.quant.codes), B
+        assert np.array_equal(r.quant.zeros, base.quant.zeros), B
+        assert r.quant.loss == pytest.approx(base.quant.loss, rel=1e-10)
+
+
+def test_ragged_block_and_group():
+    rng = np.random.default_rng(22)
+    d = 100   # last block and last group are short
+    X = _correlated_x(rng, 150, d)
+    W = rng.standard_normal((8, d)) * 0.02
+    a = _solve(W, X, 4, 16, 32)
+    b = _solve(W, X, 4, 16, 1)
+    assert a.quant.scales.shape == (8, 7)
+    assert np.array_equal(a.quant.codes, b.quant.codes)
+    p = a.quant.perm
+    assert a.quant.loss == pytest.approx(ref.objective(W[:, p], a.quant.Q[:, p], a.Hhat), rel=1e-10)
+
+
+def test_group_grid_is_taken_from_updated_weights():
+    """Each group's grid is the min/max grid of its weights as they stand at the group's first
+    column (the reading taken for when a grid is computed). The weights at that moment are
+    reconstructed independently: the original weights minus the closed-form total update
+    Err[:, :k] @ U[:k, group] from every earlier column k, whatever the blocking."""
+    rng = np.random.default_rng(23)
+    d, g = 64, 8
+    X = _correlated_x(rng, 80, d)
+    W = rng.standard_normal((6, d)) * 0.02
+    for B in (8, 32, 64):
+        r = _solve(W, X, 4, g, B)
+        err = (r.quant.w_seen - r.quant.Q) / np.diag(r.U)[None, :]
+        for gi in range(d // g):
+            k = gi * g
+            cur = W[:, k:k + g] - err[:, :k] @ r.U[:k, k:k + g]
+            s_want = np.maximum(cur.max(1) - cur.min(1), 1e-8) / 15
+            z_want = np.rint((-cur.min(1)).astype(np.float32) / s_want.astype(np.float32))
+            assert np.allclose(r.quant.scales[:, gi], s_want, rtol=1e-9)
+            assert np.array_equal(r.quant.zeros[:, gi], z_want.astype(np.int32))
+    t = ref.rtn(W, 4, g)
+    assert np.allclose(r.quant.scales[:, 0], t.scales[:, 0], rtol=0, atol=0)
+    assert not np.allclose(r.quant.scales[:, 1:], t.scales[:, 1:])
+
+
+# ---------------------------------------------------------------- optimality checks
+
+def test_no_lower_than_brute_force():
+    """On layers of <= 8 weights at 2 bits the solver's objective is >= the exhaustive optimum over
+    the same per-row grid (tools page, Step 2 objective)."""
+    rng = np.random.default_rng(31)
+    for trial in range(150):
+        d = int(rng.integers(2, 9))
+        X = _correlated_x(rng, 3 * d, d, mix=0.9)
+        W = rng.standard_normal((2, d)) * 0.02
+        r = _solve(W, X, 2, 0, d)
+        best, _ = ref.brute_force(W, r.Hhat, 2)
+        obj = ref.objective(W, r.quant.Q, r.Hhat)
+        assert obj >= best * (1 - 1e-12) - 1e-18, trial
+        assert obj == pytest.approx(r.quant.loss, rel=1e-9)
+
+
+def test_two_weight_never_worse_than_rtn():
+    """d = 2, one group: the second code is the nearest grid point to the conditional optimum, so the
+    damped objective can only improve on round-to-nearest."""
+    rng = np.random.default_rng(32)
+    for _ in range(1000):
+        X = _correlated_x(rng, 4, 2, mix=0.95)
+        W = rng.standard_normal((1, 2)) * 0.02
+        r = _solve(W, X, 2, 0, 2)
+        t = ref.rtn(W, 2, 0)
+        assert ref.objective(W, r.quant.Q, r.Hhat) <= ref.objective(W, t.Q, r.Hhat) * (1 + 1e-12) + 1e-20
+
+
+@pytest.mark.parametrize("d", [4, 8])
+def test_better_than_rtn_in_aggregate(d):
+    """GPTQ beats round-to-nearest in aggregate over seeded correlated layers (Paper breakdown, The
+    Problem; tools page remark after the sketch). Per instance it can lose, so only the sum is asserted."""
+    rng = np.random.default_rng(33 + d)
+    g_sum = r_sum = 0.0
+    worse = 0
+    for _ in range(1000):
+        X = _correlated_x(rng, 2 * d, d, mix=0.9)
+        W = rng.standard_normal((1, d)) * 0.02
+        r = _solve(W, X, 2, 0, d)
+        t = ref.rtn(W, 2, 0)
+        a = ref.objective(W, r.quant.Q, r.Hhat)
+        b = ref.objective(W, t.Q, r.Hhat)
+        g_sum += a
+        r_sum += b
+        worse += a > b * (1 + 1e-12)
+    assert g_sum < 0.9 * r_sum
+    assert worse < 500
+
+
+# ---------------------------------------------------------------- act-order
+
+def test_act_order_descending_diag_is_identity_order():
+    rng = np.random.default_rng(41)
+    d = 32
+    X = _correlated_x(rng, 100, d)
+    X = X[:, np.argsort(-np.sum(X * X, axis=0))]       # features already in descending diag order
+    W = rng.standard_normal((8, d)) * 0.02
+    H, n = ref.hessian([X])
+    assert np.all(np.diff(np.diag(H)) < 0)
+    a = ref.gptq(W, None, 4, 8, 8, act_order=True, H=H, n=n)
+    b = ref.gptq(W, None, 4, 8, 8, act_order=False, H=H, n=n)
+    assert np.array_equal(a.quant.perm, np.arange(d))
+    assert np.array_equal(a.quant.codes, b.quant.codes)
+
+
+def test_act_order_permutation_equivariance():
+    """Permuting input features (W columns and X columns together) leaves act-order results unchanged
+    up to that permutation when diag(H) has no ties."""
+    rng = np.random.default_rng(42)
+    d = 48
+    X = _correlated_x(rng, 120, d)
+    W = rng.standard_normal((8, d)) * 0.02
+    sig = rng.permutation(d)
+    a = _solve(W, X, 4, 16, 16, act=True)
+    b = _solve(W[:, sig], X[:, sig], 4, 16, 16, act=True)
+    assert np.array_equal(b.quant.codes, a.quant.codes[:, sig])
+    assert np.array_equal(b.quant.g_idx, a.quant.g_idx[sig])
+    assert np.array_equal(sig[b.quant.perm], a.quant.perm)
+    assert b.quant.loss == pytest.approx(a.quant.loss, rel=1e-12)
+
+
+def test_act_order_ties_keep_lower_index_first():
+    H = np.diag([1.0, 3.0, 1.0, 3.0, 2.0])
+    assert list(ref.act_order_perm(H)) == [1, 3, 4, 0, 2]
+
+
+def test_g_idx_maps_original_columns_to_processing_groups():
+    rng = np.random.default_rng(43)
+    d = 32
+    X = _correlated_x(rng, 64, d) * rng.uniform(0.5, 2, d)[None, :]
+    W = rng.standard_normal((4, d)) * 0.02
+    r = _solve(W, X, 4, 8, 8, act=True)
+    p = r.quant.perm
+    for j in range(d):
+        assert r.quant.g_idx[p[j]] == j // 8
+
+
+# ---------------------------------------------------------------- Hessian
+
+def test_hessian_matches_definition_exactly():
+    """H = sum over tokens of 2 x x^T (Technical Guide, Computing the Hessian), small integers so the
+    float64 sums are exact; chunked accumulation equals the one-shot sum."""
+    rng = np.random.default_rng(51)
+    X = rng.integers(-3, 4, size=(7, 5)).astype(np.float64)
+    want = [[0.0] * 5 for _ in range(5)]
+    for t in range(7):
+        for i in range(5):
+            for j in range(5):
+                want[i][j] += 2.0 * X[t, i] * X[t, j]
+    H, n = ref.hessian([X[:3], X[3:5], X[5:]])
+    assert n == 7
+    assert np.array_equal(H, np.array(want))
+    H1, _ = ref.hessian([X])
+    assert np.array_equal(H, H1)
+
+
+def test_damping_is_mean_of_diagonal():
+    H = np.diag([2.0, 4.0, 6.0]) * 10
+    Hh, perm, lam = ref.damp_and_order(H, 10, 0.01, False)
+    assert lam == pytest.approx(0.04, rel=1e-15)
+    assert np.allclose(np.diag(Hh), [2.04, 4.04, 6.04], rtol=1e-15)
+
+
+# ---------------------------------------------------------------- packing and format
+
+def test_pack_closed_form():
+    codes = np.array([[1, 2, 3, 4, 5, 6, 7, 8], [15] * 8, [0] * 8], dtype=np.uint8)
+    p = ref.pack(codes, 4)
+    assert p.dtype == np.int32
+    assert p[0, 0] == np.array([0x87654321], dtype=np.uint32).view(np.int32)[0]
+    assert p[1, 0] == -1
+    assert p[2, 0] == 0
+    for k in range(3):
+        for t in range(8):
+            c = np.zeros((1, 24), dtype=np.uint8)
+            c[0, 8 * k + t] = 1
+            w = ref.pack(c, 4)
+            assert w[0, k] == np.int32(1 << (4 * t))
+            assert np.count_nonzero(w) == 1
+
+
+def test_pack_round_trip():
+    rng = np.random.default_rng(61)
+    for bits in (2, 3, 4):
+        c = rng.integers(0, 1 << bits, size=(5, 64)).astype(np.uint8)
+        assert np.array_equal(ref.unpack(ref.pack(c, bits), 64), c)
+    with pytest.raises(ValueError):
+        ref.pack(np.full((1, 8), 8, np.uint8), 3)
+
+
+def test_format_overhead():
+    e = GOLD["memory_arithmetic"]
+    bpw = ref.bits_per_weight(e["bits"], e["group_size"], e["scale_bits"], e["zero_bits"])
+    assert round(bpw, 2) == e["bits_per_weight_about"]
+    assert round(bpw - e["bits"], 2) == e["overhead_bits_per_weight_about"]
+    ratio = (ref.bits_per_weight(4, 32) - 4) / (bpw - 4)
+    assert ratio == pytest.approx(e["group32_overhead_ratio_about"])
+    assert GOLD["packing"]["codes_per_word"] * 4 == GOLD["packing"]["word_bits"]
+
+
+# ---------------------------------------------------------------- failure paths and edge cases
+
+def test_rank_deficient_undamped_fails_with_pivot():
+    """A dead feature with no damping leaves the Hessian singular (tools page, "When the method
+    breaks down"; "Forgetting damping"): the factor reports the failing pivot."""
+    rng = np.random.default_rng(71)
+    X = rng.standard_normal((50, 6))
+    X[:, 3] = 0.0
+    H, n = ref.hessian([X])
+    Hh, _, _ = ref.damp_and_order(H, n, 0.0, False)
+    with pytest.raises(ref.NotPositiveDefinite) as ei:
+        ref.inverse_cholesky_upper(Hh)
+    assert ei.value.pivot == 4
+    # damping repairs it
+    Hh, _, _ = ref.damp_and_order(H, n, 0.01, False)
+    ref.inverse_cholesky_upper(Hh)
+
+
+def test_rejected_shapes():
+    with pytest.raises(ValueError):
+        ref.check_geometry(64, 1, 16)          # group_size 1 (Technical Guide, Don'ts)
+    with pytest.raises(ValueError):
+        ref.check_geometry(64, 24, 16)         # groups and blocks do not nest
+    with pytest.raises(ValueError):
+        ref.damp_and_order(np.zeros((4, 4)), 1, 0.01, False)
+
+
+def test_constant_group():
+    W = np.full((2, 8), 0.3)
+    W[1] = -0.7
+    r = ref.gptq(W, None, 4, 0, 8, H=np.eye(8), n=1)
+    assert np.allclose(r.quant.scales, 1e-8 / 15)
+    assert np.all(r.quant.codes == 0)
+    assert np.allclose(r.quant.Q, W, atol=1e-9)
+
+
+def test_follow_adopts_only_inside_tie_window():
+    """The follow mode used by parity tests may only change decisions that lie inside the tie window."""
+    rng = np.random.default_rng(81)
+    d = 64
+    X = _correlated_x(rng, 100, d)
+    W = rng.standard_normal((16, d)) * 0.02
+    base = _solve(W, X, 4, 16, 16)
+    flipped = base.quant.codes_proc.astype(np.int64)
+    flipped = np.where(flipped < 15, flipped + 1, flipped - 1)    # every code moved by one
+    r = ref.quantize_layer(W, base.U, 4, 16, 16, follow=(flipped, base.quant.zeros), tau=1e-3)
+    # only near-tie decisions may be adopted; with a tiny window almost none are
+    assert r.adopted_diff <= r.near_ties
+    r0 = ref.quantize_layer(W, base.U, 4, 16, 16, follow=(flipped, base.quant.zeros), tau=0.0)
+    assert r0.adopted == 0
+    assert np.array_equal(r0.codes, base.quant.codes)
+    rall = ref.quantize_layer(W, base.U, 4, 16, 16, follow=(flipped, base.quant.zeros), tau=0.5)
+    assert rall.adopted_diff > 0
