@@ -1,0 +1,167 @@
+/*
+ * GPTQ single-layer solver for AMD Instinct MI355X (gfx950): C ABI.
+ *
+ * The solver quantizes one linear layer's weights W (rows x d, d = input features) to low-bit
+ * integer codes with a scale and zero point per group, pushing each column's rounding error onto the
+ * columns not yet quantized through the Cholesky factor of the inverse Hessian of the layer's
+ * calibration inputs X (tokens x d). The four calls below are its steps, in order:
+ *
+ *   gptq_hessian_accumulate  H += 2 X_c^T X_c for each token chunk X_c
+ *   gptq_factor              damping, optional act-order, U = upper Cholesky factor of Hhat^-1
+ *   gptq_quantize_layer      the column loop with lazy block updates; codes, scales, zeros, loss
+ *   gptq_pack                eight 4-bit codes per 32-bit word
+ *
+ * Sources (web pages on GPTQ): the GPTQ tools page at ozercemkelahmet.com ("How it works",
+ * Steps 3-8, "Optional refinements", "A minimal Python sketch", "Memory arithmetic"); "GPTQ
+ * Quantization: Complete Technical Guide" (notes.jayaprakash.net; "Quantization Equation",
+ * "Computing the Hessian", "Damping Factor", "Configuration Deep Dive"); "Paper breakdown: GPTQ"
+ * (ai360xpert.com; "How It Works", lazy batching); "What Is GPTQ?" (ai-tldr.dev; "How it works",
+ * Step 3, groups).
+ *
+ * Conventions for every call:
+ *   - Matrices are row-major. Pointers named as device memory must be device memory of the current
+ *     HIP device; the caller allocates and owns every buffer, the library allocates nothing and
+ *     keeps no state between calls.
+ *   - `stream` is a hipStream_t (NULL: the default stream). Work is queued on it and the call returns
+ *     without waiting, except gptq_factor, which waits once for its own work (see there).
+ *   - Arguments are checked on the host before anything is queued. A rejected call returns a negative
+ *     status and has no effect. HIP launch failures return GPTQ_EHIP.
+ *   - Calls that share no output buffer may run concurrently on different streams.
+ */
+#ifndef GPTQ_H
+#define GPTQ_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef int32_t gptq_status_t;
+
+enum {
+  GPTQ_OK = 0,
+  GPTQ_EINVAL = -1,       /* invalid argument (null pointer, bad size, inconsistent settings)   */
+  GPTQ_ENOTPD = -2,       /* damped Hessian not positive definite (see gptq_factor's info)      */
+  GPTQ_EUNSUPPORTED = -3, /* a setting this library does not implement (symmetric grid, ...)   */
+  GPTQ_EHIP = -4,         /* a HIP runtime call or kernel launch failed                         */
+  GPTQ_ENOMEM = -5        /* the workspace passed is smaller than gptq_workspace_bytes asks     */
+};
+
+/* Element types of W and X. */
+enum { GPTQ_F32 = 0, GPTQ_F16 = 1, GPTQ_BF16 = 2 };
+
+/* Workspace kinds for gptq_workspace_bytes. */
+enum { GPTQ_WS_HESSIAN = 0, GPTQ_WS_FACTOR = 1, GPTQ_WS_QUANTIZE = 2 };
+
+/* Quantization settings (the configuration surface of the Technical Guide's AutoGPTQ example:
+ * bits, group_size, desc_act, damp_percent; the lazy-batch block size of the tools page, Step 7). */
+typedef struct {
+  int32_t bits;          /* code width, 2..8; codes are unsigned in [0, 2^bits - 1]             */
+  int32_t group_size;    /* columns per group (>= 2); <= 0: one group per row. Groups and blocks
+                            must nest: block_size % group_size == 0 or group_size % block_size == 0.
+                            A group size of 1 is rejected (Technical Guide, "Don'ts").          */
+  int32_t block_size;    /* lazy-batch width B, 1..128 (tools page, Step 7: "often 128")        */
+  int32_t act_order;     /* 1: process columns by descending diag(H) (tools page, Act-order)     */
+  int32_t sym;           /* must be 0: only the asymmetric min/max grid is implemented           */
+  int32_t static_groups; /* must be 0: group grids are taken when a group starts                 */
+  double damp;           /* relative damping >= 0: lambda = damp * mean(diag(H / n)) (Step 4)     */
+} gptq_params_t;
+
+/*
+ * H += 2 * X^T X over one chunk of calibration tokens (GPTQ tools page, "How it works", Step 3;
+ * Technical Guide, "Computing the Hessian": a sum of outer products of the layer inputs).
+ *
+ *   H      device float[d * d]. Accumulated in place; zero it before the first chunk. Only the
+ *          upper triangle (i <= j) is written and authoritative; entries below the diagonal are
+ *          left as they were except inside 256 x 256 diagonal tiles.
+ *   d      number of input features, >= 1.
+ *   X      device array [n_tok x ld_x] of x_dtype (GPTQ_F32, GPTQ_F16 or GPTQ_BF16), token-major:
+ *          row t holds the d features of token t. Not modified. May be NULL when n_tok == 0.
+ *   n_tok  tokens in this chunk, >= 0 (0: nothing is queued).
+ *   ld_x   row pitch of X in elements, >= d.
+ *   work   device workspace of work_bytes bytes, or NULL. With at least
+ *          gptq_workspace_bytes(GPTQ_WS_HESSIAN, n_tok, d, NULL) bytes the token range is split
+ *          across more workgroups; with less (or NULL) the result is identical but may be slower.
+ *          The workspace must not be shared with a concurrent call.
+ * fp16 / bf16 products are exact in fp32; sums are fp32. The result does not depend on scheduling.
+ */
+gptq_status_t gptq_hessian_accumulate(float *H, int64_t d, const void *X, int32_t x_dtype, int64_t n_tok,
+                                      int64_t ld_x, void *work, size_t work_bytes, void *stream);
+
+/*
+ * Damping, processing order and the upper Cholesky factor of the damped inverse Hessian
+ * (GPTQ tools page, "How it works", Steps 4 and 6; "Optional refinements", Act-order).
+ *
+ *   H        device float[d * d], the accumulated sum of gptq_hessian_accumulate (upper triangle
+ *            read). Not modified.
+ *   n_total  number of tokens summed into H (> 0); Hhat = H / n_total + lambda I with
+ *            lambda = p->damp * mean(diag(H / n_total)).
+ *   p        settings; reads damp, act_order, sym, static_groups.
+ *   U        device float[d * d], output, must not overlap H: upper-triangular U with
+ *            Hhat_perm^-1 = U^T U, in processing order (row/column j is original column perm[j]);
+ *            zeros below the diagonal.
+ *   perm     device int32[d], output: the processing order. Identity without act-order; with it,
+ *            columns by descending diag(H), equal values by lower index first.
+ *   work     device workspace of at least gptq_workspace_bytes(GPTQ_WS_FACTOR, 0, d, p) bytes.
+ *   info     host int64 output: 0 on success; k > 0 when the k-th pivot (1-based, in the reversed
+ *            order the factorization runs in) was not positive.
+ * This call waits for the stream once, to read the pivot check. Returns GPTQ_ENOTPD when info != 0
+ * (damping "helps but does not fix" a rank-deficient Hessian: retry with a larger damp), GPTQ_EINVAL
+ * when mean(diag(H)) is not positive and finite.
+ */
+gptq_status_t gptq_factor(const float *H, int64_t d, int64_t n_total, const gptq_params_t *p, float *U,
+                          int32_t *perm, void *work, size_t work_bytes, int64_t *info, void *stream);
+
+/*
+ * The GPTQ column loop for one layer (GPTQ tools page, "How it works", Steps 5, 7 and 8; the
+ * Technical Guide's "Quantization Equation" grid; "What Is GPTQ?", Step 3 groups).
+ *
+ *   W       device array [rows x ld_w] of w_dtype (GPTQ_F32, GPTQ_F16 or GPTQ_BF16), original column
+ *           order. Not modified.
+ *   rows    output features, >= 0 (0: only g_idx is written and loss is set to 0).
+ *   d       input features, >= 1; ld_w >= d.
+ *   U, perm from gptq_factor with the same d and act_order.
+ *   p       settings; reads bits, group_size, block_size, sym, static_groups.
+ *   codes   device uint8[rows * d], output: codes in [0, 2^bits - 1], original column order.
+ *   scales  device float[rows * ngroups], zeros device int32[rows * ngroups], output, with
+ *           ngroups = ceil(d / g) and g = group_size (d when group_size <= 0). Group j of a row
+ *           covers processing positions [j g, (j+1) g); dequantized value = scale * (code - zero).
+ *   g_idx   device int32[d], output: the group of each original column.
+ *   loss    device double[1], output: the sum over rows and columns of err^2, where err is a
+ *           column's rounding error divided by the factor's diagonal entry; it equals
+ *           sum_r (W - Q)_r Hhat (W - Q)_r^T (the damped layer objective, tools page Step 2).
+ *   work    device workspace of at least gptq_workspace_bytes(GPTQ_WS_QUANTIZE, rows, d, p) bytes.
+ * Rounding is to nearest, ties to even; the rounding ratios are taken in fp32 with correctly rounded
+ * division. Rows are independent: splitting W by rows over calls gives the same results.
+ */
+gptq_status_t gptq_quantize_layer(const void *W, int32_t w_dtype, int64_t rows, int64_t d, int64_t ld_w,
+                                  const float *U, const int32_t *perm, const gptq_params_t *p, uint8_t *codes,
+                                  float *scales, int32_t *zeros, int32_t *g_idx, double *loss, void *work,
+                                  size_t work_bytes, void *stream);
+
+/*
+ * Packs codes eight per 32-bit word along the columns (GPTQ tools page, "How it works", Step 8).
+ *
+ *   codes   device uint8[rows * d]; every code must be < 2^bits (bits above the low 4 are dropped).
+ *   rows    >= 0; d >= 8 and a multiple of 8; bits in 1..4 (3-bit codes also take a nibble).
+ *   packed  device int32[rows * d / 8], output: bits 4t..4t+3 of word k of a row hold column 8k + t.
+ */
+gptq_status_t gptq_pack(const uint8_t *codes, int64_t rows, int64_t d, int32_t bits, int32_t *packed,
+                        void *stream);
+
+/*
+ * Workspace bytes for a call: kind GPTQ_WS_HESSIAN (a = n_tok of the chunk), GPTQ_WS_FACTOR (a unused)
+ * or GPTQ_WS_QUANTIZE (a = rows; p->block_size is read). Returns 0 for invalid arguments.
+ */
+size_t gptq_workspace_bytes(int32_t kind, int64_t a, int64_t d, const gptq_params_t *p);
+
+/* A static, human-readable name for a status code. */
+const char *gptq_status_string(gptq_status_t s);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GPTQ_H */

@@ -1,0 +1,30 @@
+"""GPTQ layer-wise weight quantization solver for AMD Instinct MI355X (gfx950).
+
+The solver's steps are HIP kernels behind a C ABI (include/gptq.h, libgptq.so); this package is its
+Python binding. Build the library with `python -m post_weight_quantization_20_amd.build`.
+"""
+
+from .solver import (  # noqa: F401
+    GPTQ_BF16,
+    GPTQ_EHIP,
+    GPTQ_EINVAL,
+    GPTQ_ENOMEM,
+    GPTQ_ENOTPD,
+    GPTQ_EUNSUPPORTED,
+    GPTQ_F16,
+    GPTQ_F32,
+    GPTQ_OK,
+    GPTQ_WS_FACTOR,
+    GPTQ_WS_HESSIAN,
+    GPTQ_WS_QUANTIZE,
+    GPTQError,
+    LayerResult,
+    Params,
+    QuantOutput,
+    gptq_factor,
+    gptq_hessian_accumulate,
+    gptq_pack,
+    gptq_quantize_layer,
+    gptq_workspace_bytes,
+    quantize_layer,
+)

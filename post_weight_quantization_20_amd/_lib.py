@@ -1,0 +1,63 @@
+"""ctypes loader for libgptq.so: the C ABI declared in include/gptq.h.
+
+Loading fails loudly when the library is missing; there is no fallback implementation.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+import threading
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libgptq.so")
+
+c_int32, c_int64, c_size_t, c_void_p, c_double = (ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t,
+                                                   ctypes.c_void_p, ctypes.c_double)
+
+
+class gptq_params_t(ctypes.Structure):
+    _fields_ = [
+        ("bits", c_int32),
+        ("group_size", c_int32),
+        ("block_size", c_int32),
+        ("act_order", c_int32),
+        ("sym", c_int32),
+        ("static_groups", c_int32),
+        ("damp", c_double),
+    ]
+
+
+# name -> (restype, argtypes), mirroring include/gptq.h
+SIGNATURES = {
+    "gptq_hessian_accumulate": (c_int32, [c_void_p, c_int64, c_void_p, c_int32, c_int64, c_int64, c_void_p, c_size_t,
+                                          c_void_p]),
+    "gptq_factor": (c_int32, [c_void_p, c_int64, c_int64, ctypes.POINTER(gptq_params_t), c_void_p, c_void_p, c_void_p,
+                              c_size_t, ctypes.POINTER(c_int64), c_void_p]),
+    "gptq_quantize_layer": (c_int32, [c_void_p, c_int32, c_int64, c_int64, c_int64, c_void_p, c_void_p,
+                                      ctypes.POINTER(gptq_params_t), c_void_p, c_void_p, c_void_p, c_void_p, c_void_p,
+                                      c_void_p, c_size_t, c_void_p]),
+    "gptq_pack": (c_int32, [c_void_p, c_int64, c_int64, c_int32, c_void_p, c_void_p]),
+    "gptq_workspace_bytes": (c_size_t, [c_int32, c_int64, c_int64, ctypes.POINTER(gptq_params_t)]),
+    "gptq_status_string": (ctypes.c_char_p, [c_int32]),
+}
+
+_lock = threading.Lock()
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded library (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        with _lock:
+            if _lib is None:
+                if not os.path.exists(LIB_PATH):
+                    raise ImportError(f"{LIB_PATH} is missing: build it with "
+                                      "`python -m post_weight_quantization_20_amd.build` (needs ROCm hipcc)")
+                L = ctypes.CDLL(LIB_PATH)
+                for name, (res, args) in SIGNATURES.items():
+                    f = getattr(L, name)
+                    f.restype = res
+                    f.argtypes = args
+                _lib = L
+    return _lib

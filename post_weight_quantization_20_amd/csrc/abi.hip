@@ -1,0 +1,130 @@
+// C-ABI entry points: host-side argument checks, then launches on the caller's stream.
+#include <cmath>
+#include <cstring>
+
+#include "../../include/gptq.h"
+#include "common.hpp"
+
+
+namespace {
+
+constexpr int64_t kMaxDim = (int64_t)1 << 31;  // d * d and rows * d stay far inside int64
+
+bool dtype_ok(int32_t t) { return t == GPTQ_F32 || t == GPTQ_F16 || t == GPTQ_BF16; }
+
+// Validates the settings shared by factor and quantize. Returns GPTQ_OK or the error.
+gptq_status_t check_params(const gptq_params_t* p, int64_t d, bool quant) {
+  if (!p) return GPTQ_EINVAL;
+  if (p->sym != 0 || p->static_groups != 0) return GPTQ_EUNSUPPORTED;
+  if (p->act_order != 0 && p->act_order != 1) return GPTQ_EINVAL;
+  if (!(p->damp >= 0.0) || !std::isfinite(p->damp)) return GPTQ_EINVAL;
+  if (!quant) return GPTQ_OK;
+  if (p->bits < 2 || p->bits > 8) return GPTQ_EINVAL;
+  if (p->block_size < 1) return GPTQ_EINVAL;
+  if (p->block_size > 128) return GPTQ_EUNSUPPORTED;
+  const int64_t g = p->group_size <= 0 ? d : p->group_size;
+  if (g == 1) return GPTQ_EINVAL;
+  if (g < d && !(p->block_size % g == 0 || g % p->block_size == 0)) return GPTQ_EINVAL;
+  return GPTQ_OK;
+}
+
+gptq_status_t hip_status(hipError_t e) { return e == hipSuccess ? GPTQ_OK : GPTQ_EHIP; }
+
+}  // namespace
+
+extern "C" {
+
+const char* gptq_status_string(gptq_status_t s) {
+  switch (s) {
+    case GPTQ_OK: return "ok";
+    case GPTQ_EINVAL: return "invalid argument";
+    case GPTQ_ENOTPD: return "damped Hessian is not positive definite";
+    case GPTQ_EUNSUPPORTED: return "unsupported setting";
+    case GPTQ_EHIP: return "HIP runtime error";
+    case GPTQ_ENOMEM: return "workspace too small";
+    default: return "unknown status";
+  }
+}
+
+size_t gptq_workspace_bytes(int32_t kind, int64_t a, int64_t d, const gptq_params_t* p) {
+  if (d <= 0 || d > kMaxDim || a < 0 || a > kMaxDim) return 0;
+  switch (kind) {
+    case GPTQ_WS_HESSIAN: return gptq::hessian_workspace_bytes(a, d);
+    case GPTQ_WS_FACTOR: return gptq::factor_workspace_bytes(d);
+    case GPTQ_WS_QUANTIZE: {
+      if (!p || p->block_size < 1 || p->block_size > 128) return 0;
+      return gptq::quant_layout(a, d, p->block_size).total;
+    }
+    default: return 0;
+  }
+}
+
+gptq_status_t gptq_hessian_accumulate(float* H, int64_t d, const void* X, int32_t x_dtype, int64_t n_tok,
+                                      int64_t ld_x, void* work, size_t work_bytes, void* stream) {
+  if (!H || d <= 0 || d > kMaxDim || n_tok < 0 || n_tok > kMaxDim || !dtype_ok(x_dtype)) return GPTQ_EINVAL;
+  if (n_tok == 0) return GPTQ_OK;
+  if (!X || ld_x < d) return GPTQ_EINVAL;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (x_dtype == GPTQ_F32) {
+    gptq::GemmArgs a{};
+    a.M = d; a.N = d; a.K = n_tok;
+    a.A = static_cast<const float*>(X); a.lda = ld_x; a.transA = 1;
+    a.B = static_cast<const float*>(X); a.ldb = ld_x; a.transB = 0;
+    a.C = H; a.ldc = d;
+    a.alpha = 2.0f; a.beta = 1.0f; a.tri = 2;
+    return hip_status(gptq::gemm_f32(a, s));
+  }
+  return hip_status(gptq::hessian_f16(H, d, X, x_dtype, n_tok, ld_x, work, work_bytes, s));
+}
+
+gptq_status_t gptq_factor(const float* H, int64_t d, int64_t n_total, const gptq_params_t* p, float* U,
+                          int32_t* perm, void* work, size_t work_bytes, int64_t* info, void* stream) {
+  if (!H || !U || !perm || !info || !work || d <= 0 || d > kMaxDim || n_total <= 0) return GPTQ_EINVAL;
+  gptq_status_t st = check_params(p, d, false);
+  if (st != GPTQ_OK) return st;
+  const char* h0 = reinterpret_cast<const char*>(H);
+  const char* u0 = reinterpret_cast<const char*>(U);
+  const size_t bytes = (size_t)d * d * sizeof(float);
+  if (h0 < u0 + bytes && u0 < h0 + bytes) return GPTQ_EINVAL;
+  if (work_bytes < gptq::factor_workspace_bytes(d)) return GPTQ_ENOMEM;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  int* status_dev = nullptr;
+  int64_t* info_dev = nullptr;
+  hipError_t e = gptq::factor(H, d, n_total, p->damp, p->act_order, U, perm, work, s, &status_dev, &info_dev);
+  if (e != hipSuccess) return GPTQ_EHIP;
+  int64_t dev_info = 0;
+  int dev_status = 0;
+  if (hipMemcpyAsync(&dev_info, info_dev, sizeof(dev_info), hipMemcpyDeviceToHost, s) != hipSuccess) return GPTQ_EHIP;
+  if (hipMemcpyAsync(&dev_status, status_dev, sizeof(dev_status), hipMemcpyDeviceToHost, s) != hipSuccess)
+    return GPTQ_EHIP;
+  if (hipStreamSynchronize(s) != hipSuccess) return GPTQ_EHIP;
+  // the factorization runs on the reversed order; report the processing-order column (1-based)
+  *info = dev_info > 0 ? d - dev_info + 1 : 0;
+  if (dev_status != 0) return GPTQ_EINVAL;
+  return dev_info != 0 ? GPTQ_ENOTPD : GPTQ_OK;
+}
+
+gptq_status_t gptq_quantize_layer(const void* W, int32_t w_dtype, int64_t rows, int64_t d, int64_t ld_w,
+                                  const float* U, const int32_t* perm, const gptq_params_t* p, uint8_t* codes,
+                                  float* scales, int32_t* zeros, int32_t* g_idx, double* loss, void* work,
+                                  size_t work_bytes, void* stream) {
+  if (rows < 0 || rows > kMaxDim || d <= 0 || d > kMaxDim || !dtype_ok(w_dtype)) return GPTQ_EINVAL;
+  if (!U || !perm || !g_idx || !loss || !work) return GPTQ_EINVAL;
+  if (rows > 0 && (!W || !codes || !scales || !zeros || ld_w < d)) return GPTQ_EINVAL;
+  gptq_status_t st = check_params(p, d, true);
+  if (st != GPTQ_OK) return st;
+  if (work_bytes < gptq::quant_layout(rows, d, p->block_size).total) return GPTQ_ENOMEM;
+  const int64_t g = p->group_size <= 0 ? d : p->group_size;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  return hip_status(gptq::quantize(W, w_dtype, rows, d, ld_w, U, perm, p->bits, g, p->block_size, codes, scales,
+                                   zeros, g_idx, loss, work, s));
+}
+
+gptq_status_t gptq_pack(const uint8_t* codes, int64_t rows, int64_t d, int32_t bits, int32_t* packed, void* stream) {
+  if (rows < 0 || rows > kMaxDim || d < 8 || d > kMaxDim || d % 8 != 0 || bits < 1 || bits > 4) return GPTQ_EINVAL;
+  if (rows == 0) return GPTQ_OK;
+  if (!codes || !packed) return GPTQ_EINVAL;
+  return hip_status(gptq::pack(codes, rows, d, packed, static_cast<hipStream_t>(stream)));
+}
+
+}  // extern "C"

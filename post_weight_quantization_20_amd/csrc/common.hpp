@@ -1,0 +1,113 @@
+// Shared device helpers and the internal launcher interface of the GPTQ layer-solver library.
+// CDNA4 (gfx950) only: wave64, MFMA matrix cores, 160 KB LDS per CU.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <type_traits>
+#include <stdint.h>
+#include <stddef.h>
+
+#define GPTQ_DEV __device__ __forceinline__
+
+namespace gptq {
+
+typedef _Float16 half8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float floatx16 __attribute__((ext_vector_type(16)));
+typedef float floatx4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+enum DType { F32 = 0, F16 = 1, BF16 = 2 };
+
+// ------------------------------------------------------------------ element conversion
+GPTQ_DEV float bf16_bits_to_f32(uint16_t b) { return __builtin_bit_cast(float, (uint32_t)b << 16); }
+
+GPTQ_DEV float load_as_f32(const void* p, int dtype, int64_t idx) {
+  if (dtype == F32) return static_cast<const float*>(p)[idx];
+  if (dtype == F16) return (float)static_cast<const _Float16*>(p)[idx];
+  return bf16_bits_to_f32(static_cast<const uint16_t*>(p)[idx]);
+}
+
+// ------------------------------------------------------------------ the quantization grid
+// Asymmetric min/max grid of one group: scale = max(wmax - wmin, 1e-8) / maxq,
+// zero = round(-wmin / scale) (GPTQ tools page, "A minimal Python sketch"; round half to even).
+// rs is the correctly rounded reciprocal of the scale, used by div_rn.
+GPTQ_DEV void make_grid(float wmin, float wmax, float maxq, float& s, float& z, float& rs) {
+  s = fmaxf(wmax - wmin, 1e-8f) / maxq;
+  z = rintf(-wmin / s);
+  rs = 1.0f / s;
+}
+
+// Correctly rounded w / s from rs = RN(1 / s): one product and one fma-based correction
+// (Markstein's division theorem for round-to-nearest with an fma). Equal to the IEEE quotient
+// away from overflow and underflow, which the grid's scales (>= 1e-8 / 255) and weights avoid.
+GPTQ_DEV float div_rn(float w, float s, float rs) {
+  float q0 = w * rs;
+  float r = __builtin_fmaf(-q0, s, w);
+  return __builtin_fmaf(r, rs, q0);
+}
+
+// ------------------------------------------------------------------ lane broadcast
+// Calls f(std::integral_constant<int, K>) for K = B .. E-1 (compile-time column indices).
+template <int B, int E, typename F>
+GPTQ_DEV void static_for(F&& f) {
+  if constexpr (B < E) {
+    f(std::integral_constant<int, B>{});
+    static_for<B + 1, E>(f);
+  }
+}
+
+template <int SRC>
+GPTQ_DEV float row_bcast(float v) {
+  // DPP row_newbcast: lane SRC of each 16-lane row to the whole row
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x150 + SRC, 0xF, 0xF, false));
+}
+
+// DPP row_ror:15 - lane i of each 16-lane row takes the value of lane (i + 1) mod 16
+GPTQ_DEV float row_ror15(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x12F, 0xF, 0xF, false));
+}
+
+// ------------------------------------------------------------------ internal launchers
+
+// C[M x N] = alpha * op(A) * op(B) + beta * C, row-major fp32, on MFMA.
+// op(A) is A (M x K, lda) or A^T (A stored K x M); op(B) is B (K x N, ldb) or B^T (B stored N x K).
+// tri: 0 every element, 1 only elements with m >= n, 2 only m <= n.
+// beta == 0 never reads C. In place is safe for an operand that shares rows (A, no transpose)
+// with C when N <= 128, or columns (B, no transpose) with C when M <= 128: one workgroup then
+// reads the whole reduction range of its output strip before it writes.
+struct GemmArgs {
+  int64_t M, N, K;
+  const float* A; int64_t lda; int transA;
+  const float* B; int64_t ldb; int transB;
+  float* C; int64_t ldc;
+  float alpha, beta;
+  int tri;
+};
+hipError_t gemm_f32(const GemmArgs& a, hipStream_t s);
+
+// H (upper tiles) += 2 X^T X for X = [n x d] fp16 / bf16 (leading dimension ldx) on MFMA.
+size_t hessian_workspace_bytes(int64_t n, int64_t d);
+hipError_t hessian_f16(float* H, int64_t d, const void* X, int dtype, int64_t n, int64_t ldx,
+                       void* work, size_t work_bytes, hipStream_t s);
+
+// Factor: damping, processing order and U (see factor.hip). status_dev / info_dev receive device
+// addresses of the mean-diagonal check and the first failed pivot (1-based, reversed order).
+size_t factor_workspace_bytes(int64_t d);
+hipError_t factor(const float* H, int64_t d, int64_t n, double damp, int act_order, float* U, int32_t* perm,
+                  void* work, hipStream_t s, int** status_dev, int64_t** info_dev);
+
+// Column loop workspace layout (see quant.hip).
+struct QuantLayout {
+  int64_t ldw, bp;
+  size_t off_wp, off_codes, off_err, off_loss, off_iperm, total;
+};
+QuantLayout quant_layout(int64_t rows, int64_t d, int block);
+hipError_t quantize(const void* W, int w_dtype, int64_t rows, int64_t d, int64_t ld_w, const float* U,
+                    const int32_t* perm, int bits, int64_t g, int B, uint8_t* codes, float* scales,
+                    int32_t* zeros, int32_t* g_idx, double* loss, void* work, hipStream_t s);
+hipError_t pack(const uint8_t* codes, int64_t rows, int64_t d, int32_t* packed, hipStream_t s);
+
+}  // namespace gptq

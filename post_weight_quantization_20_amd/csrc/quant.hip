@@ -1,0 +1,383 @@
+// The GPTQ column loop with lazy block updates, and the nibble packer.
+//
+// GPTQ tools page, "How it works":
+//   Step 5 - columns are quantized one at a time in a fixed order; each column's rounding error,
+//            divided by the matching diagonal entry of the factor, is subtracted from the columns
+//            not yet quantized through the matching row of the factor;
+//   Step 7 - columns are processed in blocks; inside a block updates are applied at once, updates to
+//            later columns are collected and applied once when the block ends (lazy batch);
+//   Step 8 - one scale and zero point per group of weights; codes packed eight 4-bit values per word.
+// "What Is GPTQ?" (ai-tldr.dev), "How it works", Step 3: groups are runs of consecutive weights of a
+// row, each with its own scale and zero point.
+//
+// Rows of W are independent once U is known, so the block kernel gives each row 16 lanes of a
+// wave64 (4 rows per wave, 16 rows per 256-thread workgroup). A lane holds B/16 consecutive columns
+// of its row in registers; the block's part of U sits in LDS, and the row of U for column k is read
+// by all rows of the workgroup at once. Column k's weight is broadcast from its owning lane to the
+// 16 lanes of its row with a DPP row broadcast, every lane then runs the rounding chain, and each lane
+// applies the update to its own columns. Group minima and maxima are butterfly reductions across the
+// 16 lanes. The block's scaled errors go to a rows x B buffer that the trailing update (an fp32 MFMA
+// GEMM) multiplies into the columns after the block.
+#include "common.hpp"
+
+namespace gptq {
+namespace {
+
+struct QArgs {
+  float* Wp;             // working weights, processing order, [rows x ldw]
+  int64_t ldw;
+  int64_t rows, d;
+  int64_t b;             // first column of the block
+  int ncols;             // columns in this block (<= 16 * CPL)
+  const float* U;        // [d x d], processing order
+  int64_t g;             // group size (columns)
+  int grid_in_block;     // groups start inside blocks (g <= B); else the grid was computed for the block
+  float maxq;
+  uint8_t* codes_p;      // [rows x d], processing order
+  float* scales;         // [rows x ngroups]
+  int32_t* zeros;        // [rows x ngroups]
+  int64_t ngroups;
+  float* err;            // [rows x 16 * CPL]
+  double* row_loss;      // [rows]
+};
+
+// Loads N consecutive floats from LDS (16-byte aligned when N >= 4) into registers.
+template <int N>
+GPTQ_DEV void lds_load(const float* p, float (&v)[N]) {
+  if constexpr (N >= 4) {
+#pragma unroll
+    for (int i = 0; i < N; i += 4) {
+      const float4 q = *reinterpret_cast<const float4*>(p + i);
+      v[i] = q.x; v[i + 1] = q.y; v[i + 2] = q.z; v[i + 3] = q.w;
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < N; ++i) v[i] = p[i];
+  }
+}
+
+template <int CPL>
+__global__ __launch_bounds__(256) void quant_block_kernel(QArgs a) {
+  constexpr int BP = 16 * CPL;
+  extern __shared__ float sm[];
+  float* Us = sm;                  // [BP][BP]: strict upper part of U's block, zeros elsewhere
+  float* invd = Us + BP * BP;      // [BP]: 1 / U[k][k]
+  float* Es = invd + BP;           // [16 rows][BP]: scaled errors of the block
+  uint8_t* Qs = reinterpret_cast<uint8_t*>(Es + 16 * BP);  // [16 rows][BP]: codes of the block
+
+  const int tid = threadIdx.x;
+  const int nc = a.ncols;
+  for (int e = tid; e < BP * BP; e += 256) {
+    const int k = e / BP, j = e % BP;
+    Us[e] = (j > k && j < nc) ? a.U[(a.b + k) * a.d + a.b + j] : 0.0f;
+  }
+  for (int k = tid; k < BP; k += 256) invd[k] = (k < nc) ? 1.0f / a.U[(a.b + k) * a.d + a.b + k] : 0.0f;
+  __syncthreads();
+
+  const int lane = tid & 63, wave = tid >> 6;
+  const int lr = lane & 15;
+  const int rloc = wave * 4 + (lane >> 4);
+  const int64_t row = (int64_t)blockIdx.x * 16 + rloc;
+  const bool row_ok = row < a.rows;
+
+  // lane lr starts with block columns lr*CPL .. lr*CPL+CPL-1 in w[0..CPL-1]
+  float w[CPL];
+  const float* wrow = a.Wp + row * a.ldw + a.b;
+#pragma unroll
+  for (int c = 0; c < CPL; ++c) w[c] = (row_ok && lr * CPL + c < nc) ? wrow[lr * CPL + c] : 0.0f;
+
+  float s = 1.0f, z = 0.0f, rs = 1.0f;
+  if (!a.grid_in_block) {
+    const int64_t gi = a.b / a.g;
+    if (row_ok) {
+      s = a.scales[row * a.ngroups + gi];
+      z = (float)a.zeros[row * a.ngroups + gi];
+    }
+    rs = 1.0f / s;
+  }
+  float loss = 0.0f;
+  // groups nest inside blocks when g <= B, so they start at block columns 0, g, 2g, ...
+  int next_group = a.grid_in_block ? 0 : (1 << 30);
+  const int gsz = (int)min<int64_t>(a.g, (int64_t)BP);
+
+  // Chunk o quantizes block columns o*CPL .. o*CPL+CPL-1. Before it, the lanes of each row have
+  // been rotated o times by one lane, so lane 0 holds those columns and lane l holds the columns
+  // of original lane (l + o) mod 16 (already quantized ones meet zeros in U and stay unchanged).
+  const int nchunks = (nc + CPL - 1) / CPL;
+  for (int o = 0; o < nchunks; ++o) {
+    const int cbase = ((lr + o) & 15) * CPL;  // block column of w[0] in this lane
+    // everything this chunk reads from LDS, loaded up front (no LDS stores until the chunk ends)
+    float iv[CPL], ur[CPL][CPL];
+    lds_load<CPL>(invd + o * CPL, iv);
+#pragma unroll
+    for (int c = 0; c < CPL; ++c) lds_load<CPL>(Us + (o * CPL + c) * BP + cbase, ur[c]);
+    float qv[CPL], ev[CPL];
+#pragma unroll
+    for (int c = 0; c < CPL; ++c) {
+      const int k = o * CPL + c;
+      if (k == next_group) {
+        next_group += gsz;
+        // group grid from the current weights of block columns [k, k + g)
+        const int kend = min(k + gsz, nc);
+        float mn = INFINITY, mx = -INFINITY;
+#pragma unroll
+        for (int t = 0; t < CPL; ++t) {
+          const int col = cbase + t;
+          if (col >= k && col < kend) { mn = fminf(mn, w[t]); mx = fmaxf(mx, w[t]); }
+        }
+#pragma unroll
+        for (int m = 8; m > 0; m >>= 1) {
+          mn = fminf(mn, __shfl_xor(mn, m, 16));
+          mx = fmaxf(mx, __shfl_xor(mx, m, 16));
+        }
+        make_grid(mn, mx, a.maxq, s, z, rs);
+        if (lr == 0 && row_ok && k < nc) {
+          const int64_t gi = (a.b + k) / a.g;
+          a.scales[row * a.ngroups + gi] = s;
+          a.zeros[row * a.ngroups + gi] = (int32_t)z;
+        }
+      }
+      const float wk = row_bcast<0>(w[c]);
+      const float x = div_rn(wk, s, rs);
+      const float q = fminf(fmaxf(rintf(x) + z, 0.0f), a.maxq);
+      const float dq = s * (q - z);
+      float e = (wk - dq) * iv[c];
+      e = (k < nc) ? e : 0.0f;
+      loss = __builtin_fmaf(e, e, loss);
+#pragma unroll
+      for (int t = 0; t < CPL; ++t) w[t] = __builtin_fmaf(-e, ur[c][t], w[t]);
+      qv[c] = q;
+      ev[c] = e;
+    }
+    if (lr == 0) {
+#pragma unroll
+      for (int c = 0; c < CPL; ++c) {
+        Qs[rloc * BP + o * CPL + c] = (uint8_t)qv[c];
+        Es[rloc * BP + o * CPL + c] = ev[c];
+      }
+    }
+#pragma unroll
+    for (int t = 0; t < CPL; ++t) w[t] = row_ror15(w[t]);
+  }
+  __syncthreads();
+
+  if (row_ok) {
+    uint8_t* crow = a.codes_p + row * a.d + a.b;
+    float* erow = a.err + row * BP;
+#pragma unroll
+    for (int t = 0; t < CPL; ++t) {
+      const int j = lr * CPL + t;
+      if (j < nc) crow[j] = Qs[rloc * BP + j];
+      erow[j] = (j < nc) ? Es[rloc * BP + j] : 0.0f;
+    }
+    if (lr == 0) a.row_loss[row] += (double)loss;
+  }
+}
+
+// Group grid for groups longer than a block: min/max of the current weights of columns
+// [b, b + len) of each row, one wave per row.
+__global__ __launch_bounds__(256) void group_grid_kernel(const float* __restrict__ Wp, int64_t ldw, int64_t rows,
+                                                         int64_t b, int64_t len, float maxq, int64_t gi,
+                                                         float* __restrict__ scales, int32_t* __restrict__ zeros,
+                                                         int64_t ngroups) {
+  const int lane = threadIdx.x & 63;
+  const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (row >= rows) return;
+  const float* p = Wp + row * ldw + b;
+  float mn = INFINITY, mx = -INFINITY;
+  for (int64_t j = lane; j < len; j += 64) {
+    const float v = p[j];
+    mn = fminf(mn, v);
+    mx = fmaxf(mx, v);
+  }
+#pragma unroll
+  for (int m = 32; m > 0; m >>= 1) {
+    mn = fminf(mn, __shfl_xor(mn, m, 64));
+    mx = fmaxf(mx, __shfl_xor(mx, m, 64));
+  }
+  if (lane == 0) {
+    float s, z, rs;
+    make_grid(mn, mx, maxq, s, z, rs);
+    scales[row * ngroups + gi] = s;
+    zeros[row * ngroups + gi] = (int32_t)z;
+  }
+}
+
+// Working copy in processing order: Wp[r][j] = W[r][perm[j]] as fp32; zero padding to ldw.
+__global__ __launch_bounds__(256) void gather_w_kernel(const void* __restrict__ W, int dtype, int64_t ldw_in,
+                                                       int64_t rows, int64_t d, const int32_t* __restrict__ perm,
+                                                       float* __restrict__ Wp, int64_t ldw) {
+  for (int64_t r = blockIdx.y; r < rows; r += gridDim.y)
+    for (int64_t j = (int64_t)blockIdx.x * 256 + threadIdx.x; j < ldw; j += (int64_t)gridDim.x * 256)
+      Wp[r * ldw + j] = (j < d) ? load_as_f32(W, dtype, r * ldw_in + perm[j]) : 0.0f;
+}
+
+// iperm[perm[j]] = j and g_idx[perm[j]] = j / g.
+__global__ void index_kernel(const int32_t* __restrict__ perm, int64_t d, int64_t g, int32_t* __restrict__ iperm,
+                             int32_t* __restrict__ g_idx) {
+  const int64_t j = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (j < d) {
+    const int32_t c = perm[j];
+    iperm[c] = (int32_t)j;
+    g_idx[c] = (int32_t)(j / g);
+  }
+}
+
+// codes[r][c] = codes_p[r][iperm[c]] (back to the original column order).
+__global__ __launch_bounds__(256) void unpermute_kernel(const uint8_t* __restrict__ codes_p, int64_t rows, int64_t d,
+                                                        const int32_t* __restrict__ iperm, uint8_t* __restrict__ codes) {
+  for (int64_t r = blockIdx.y; r < rows; r += gridDim.y)
+    for (int64_t c = (int64_t)blockIdx.x * 256 + threadIdx.x; c < d; c += (int64_t)gridDim.x * 256)
+      codes[r * d + c] = codes_p[r * d + iperm[c]];
+}
+
+__global__ void zero_f64(double* p, int64_t n) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) p[i] = 0.0;
+}
+
+// loss = sum of the row losses in a fixed order.
+__global__ __launch_bounds__(1024) void loss_kernel(const double* __restrict__ row_loss, int64_t rows,
+                                                    double* __restrict__ loss) {
+  __shared__ double part[1024];
+  double acc = 0.0;
+  for (int64_t i = threadIdx.x; i < rows; i += 1024) acc += row_loss[i];
+  part[threadIdx.x] = acc;
+  __syncthreads();
+  for (int s = 512; s > 0; s >>= 1) {
+    if ((int)threadIdx.x < s) part[threadIdx.x] += part[threadIdx.x + s];
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) *loss = part[0];
+}
+
+// packed[r][k] = sum_t (codes[r][8k + t] & 15) << 4t.
+__global__ __launch_bounds__(256) void pack_kernel(const uint8_t* __restrict__ codes, int64_t rows, int64_t d,
+                                                   int32_t* __restrict__ packed, int vec) {
+  const int64_t words = d / 8;
+  const int64_t total = rows * words;
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < total; i += (int64_t)gridDim.x * 256) {
+    const int64_t r = i / words, k = i % words;
+    const uint8_t* p = codes + r * d + 8 * k;
+    uint32_t lo, hi;
+    if (vec) {
+      const uint2 v = *reinterpret_cast<const uint2*>(p);
+      lo = v.x; hi = v.y;
+    } else {
+      lo = p[0] | (p[1] << 8) | (p[2] << 16) | ((uint32_t)p[3] << 24);
+      hi = p[4] | (p[5] << 8) | (p[6] << 16) | ((uint32_t)p[7] << 24);
+    }
+    // byte t of lo/hi -> nibble t / t + 4
+    uint32_t out = 0;
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      out |= ((lo >> (8 * t)) & 15u) << (4 * t);
+      out |= ((hi >> (8 * t)) & 15u) << (4 * (t + 4));
+    }
+    packed[i] = (int32_t)out;
+  }
+}
+
+template <int CPL>
+size_t qsmem() {
+  constexpr size_t BP = 16 * CPL;
+  return (BP * BP + BP + 16 * BP) * sizeof(float) + 16 * BP;
+}
+
+template <int CPL>
+void launch_block(const QArgs& a, hipStream_t s) {
+  static bool attr = false;
+  if (!attr) {
+    (void)hipFuncSetAttribute((const void*)quant_block_kernel<CPL>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                        (int)qsmem<CPL>());
+    attr = true;
+  }
+  hipLaunchKernelGGL(quant_block_kernel<CPL>, dim3((unsigned)((a.rows + 15) / 16)), dim3(256), qsmem<CPL>(), s, a);
+}
+
+int cpl_for(int B) { return B <= 16 ? 1 : B <= 32 ? 2 : B <= 64 ? 4 : 8; }
+
+}  // namespace
+
+QuantLayout quant_layout(int64_t rows, int64_t d, int block) {
+  QuantLayout L;
+  L.ldw = (d + 3) / 4 * 4;
+  L.bp = 16 * cpl_for(block);
+  auto up = [](size_t x) { return (x + 255) / 256 * 256; };
+  size_t o = 0;
+  L.off_wp = o; o = up(o + (size_t)rows * L.ldw * sizeof(float));
+  L.off_codes = o; o = up(o + (size_t)rows * d);
+  L.off_err = o; o = up(o + (size_t)rows * L.bp * sizeof(float));
+  L.off_loss = o; o = up(o + (size_t)rows * sizeof(double));
+  L.off_iperm = o; o = up(o + (size_t)d * sizeof(int32_t));
+  L.total = o;
+  return L;
+}
+
+hipError_t quantize(const void* W, int w_dtype, int64_t rows, int64_t d, int64_t ld_w, const float* U,
+                    const int32_t* perm, int bits, int64_t g, int B, uint8_t* codes, float* scales,
+                    int32_t* zeros, int32_t* g_idx, double* loss, void* work, hipStream_t s) {
+  const QuantLayout L = quant_layout(rows, d, B);
+  char* wb = static_cast<char*>(work);
+  float* Wp = reinterpret_cast<float*>(wb + L.off_wp);
+  uint8_t* codes_p = reinterpret_cast<uint8_t*>(wb + L.off_codes);
+  float* err = reinterpret_cast<float*>(wb + L.off_err);
+  double* row_loss = reinterpret_cast<double*>(wb + L.off_loss);
+  int32_t* iperm = reinterpret_cast<int32_t*>(wb + L.off_iperm);
+  const int64_t ngroups = (d + g - 1) / g;
+  const float maxq = (float)((1 << bits) - 1);
+
+  hipLaunchKernelGGL(index_kernel, dim3((unsigned)((d + 255) / 256)), dim3(256), 0, s, perm, d, g, iperm, g_idx);
+  if (rows > 0) {
+    const unsigned gx = (unsigned)std::min<int64_t>((L.ldw + 255) / 256, 64);
+    hipLaunchKernelGGL(gather_w_kernel, dim3(gx, (unsigned)std::min<int64_t>(rows, 65535)), dim3(256), 0, s, W, w_dtype, ld_w, rows, d, perm,
+                       Wp, L.ldw);
+    hipLaunchKernelGGL(zero_f64, dim3((unsigned)((rows + 255) / 256)), dim3(256), 0, s, row_loss, rows);
+  }
+  hipError_t e;
+  const int cpl = cpl_for(B);
+  for (int64_t b = 0; b < d && rows > 0; b += B) {
+    const int nc = (int)std::min<int64_t>(B, d - b);
+    const bool in_block = g <= B;
+    if (!in_block && b % g == 0) {
+      hipLaunchKernelGGL(group_grid_kernel, dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, s, Wp, L.ldw, rows, b,
+                         std::min<int64_t>(g, d - b), maxq, b / g, scales, zeros, ngroups);
+    }
+    QArgs a;
+    a.Wp = Wp; a.ldw = L.ldw; a.rows = rows; a.d = d; a.b = b; a.ncols = nc; a.U = U; a.g = g;
+    a.grid_in_block = in_block; a.maxq = maxq; a.codes_p = codes_p; a.scales = scales; a.zeros = zeros;
+    a.ngroups = ngroups; a.err = err; a.row_loss = row_loss;
+    switch (cpl) {
+      case 1: launch_block<1>(a, s); break;
+      case 2: launch_block<2>(a, s); break;
+      case 4: launch_block<4>(a, s); break;
+      default: launch_block<8>(a, s); break;
+    }
+    if (b + nc < d) {
+      GemmArgs t{};  // lazy batch: W[:, b+nc:] -= Err U[b:b+nc, b+nc:]
+      t.M = rows; t.N = d - b - nc; t.K = nc;
+      t.A = err; t.lda = L.bp; t.transA = 0;
+      t.B = U + b * d + b + nc; t.ldb = d; t.transB = 0;
+      t.C = Wp + b + nc; t.ldc = L.ldw;
+      t.alpha = -1.0f; t.beta = 1.0f; t.tri = 0;
+      if ((e = gemm_f32(t, s)) != hipSuccess) return e;
+    }
+  }
+  if (rows > 0) {
+    const unsigned gx = (unsigned)std::min<int64_t>((d + 255) / 256, 64);
+    hipLaunchKernelGGL(unpermute_kernel, dim3(gx, (unsigned)std::min<int64_t>(rows, 65535)), dim3(256), 0, s, codes_p, rows, d, iperm, codes);
+  }
+  hipLaunchKernelGGL(loss_kernel, dim3(1), dim3(1024), 0, s, row_loss, rows, loss);
+  return hipGetLastError();
+}
+
+hipError_t pack(const uint8_t* codes, int64_t rows, int64_t d, int32_t* packed, hipStream_t s) {
+  const int64_t total = rows * (d / 8);
+  if (total <= 0) return hipSuccess;
+  const unsigned grid = (unsigned)std::min<int64_t>((total + 255) / 256, 65536);
+  const int vec = ((uintptr_t)codes % 8 == 0);
+  hipLaunchKernelGGL(pack_kernel, dim3(grid), dim3(256), 0, s, codes, rows, d, packed, vec);
+  return hipGetLastError();
+}
+
+}  // namespace gptq

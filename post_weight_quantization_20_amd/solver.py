@@ -1,0 +1,200 @@
+"""Python binding of the GPTQ layer-solver C ABI (include/gptq.h).
+
+Argument marshalling only: tensors are torch device tensors, their data pointers and the current
+HIP stream are handed to libgptq.so, and every step of the solver runs in its HIP kernels. Outputs
+that the caller does not pass are allocated with torch.
+"""
+
+from __future__ import annotations
+
+import ctypes
+from dataclasses import dataclass
+from typing import Optional, Tuple
+
+import torch
+
+from . import _lib
+
+GPTQ_OK, GPTQ_EINVAL, GPTQ_ENOTPD, GPTQ_EUNSUPPORTED, GPTQ_EHIP, GPTQ_ENOMEM = 0, -1, -2, -3, -4, -5
+GPTQ_F32, GPTQ_F16, GPTQ_BF16 = 0, 1, 2
+GPTQ_WS_HESSIAN, GPTQ_WS_FACTOR, GPTQ_WS_QUANTIZE = 0, 1, 2
+
+_DTYPE = {torch.float32: GPTQ_F32, torch.float16: GPTQ_F16, torch.bfloat16: GPTQ_BF16}
+
+
+class GPTQError(RuntimeError):
+    """A non-zero status from the library; `info` carries gptq_factor's failed pivot."""
+
+    def __init__(self, status: int, info: int = 0):
+        msg = _lib.lib().gptq_status_string(status).decode()
+        super().__init__(f"GPTQ status {status}: {msg}" + (f" (pivot {info})" if info else ""))
+        self.status = status
+        self.info = info
+
+
+@dataclass
+class Params:
+    """Quantization settings (gptq_params_t)."""
+
+    bits: int = 4
+    group_size: int = 128
+    block_size: int = 128
+    act_order: bool = False
+    sym: bool = False
+    static_groups: bool = False
+    damp: float = 0.01
+
+    def c(self) -> _lib.gptq_params_t:
+        return _lib.gptq_params_t(int(self.bits), int(self.group_size), int(self.block_size), int(bool(self.act_order)),
+                                  int(bool(self.sym)), int(bool(self.static_groups)), float(self.damp))
+
+    def groups(self, d: int) -> int:
+        g = d if self.group_size <= 0 else self.group_size
+        return (d + g - 1) // g
+
+
+@dataclass
+class QuantOutput:
+    codes: torch.Tensor    # uint8 [rows, d], original column order
+    scales: torch.Tensor   # float32 [rows, ngroups]
+    zeros: torch.Tensor    # int32 [rows, ngroups]
+    g_idx: torch.Tensor    # int32 [d]
+    loss: torch.Tensor     # float64 [1]
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return ctypes.c_void_p(0 if t is None else t.data_ptr())
+
+
+def _stream(stream) -> ctypes.c_void_p:
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _check(status: int, info: int = 0) -> None:
+    if status != GPTQ_OK:
+        raise GPTQError(status, info)
+
+
+def _need_cuda(*ts) -> None:
+    for t in ts:
+        if t is not None and not t.is_cuda:
+            raise ValueError("tensors must be on the GPU")
+
+
+def gptq_workspace_bytes(kind: int, a: int, d: int, params: Optional[Params] = None) -> int:
+    p = ctypes.byref(params.c()) if params is not None else None
+    return int(_lib.lib().gptq_workspace_bytes(kind, a, d, p))
+
+
+def _workspace(kind: int, a: int, d: int, params: Optional[Params], device) -> torch.Tensor:
+    n = gptq_workspace_bytes(kind, a, d, params)
+    return torch.empty(max(n, 1), dtype=torch.uint8, device=device)
+
+
+def gptq_hessian_accumulate(H: torch.Tensor, X: torch.Tensor, work: Optional[torch.Tensor] = None,
+                            stream=None) -> None:
+    """H (float32 [d, d], upper triangle) += 2 X^T X for X [tokens, d] (fp32 / fp16 / bf16)."""
+    _need_cuda(H, X, work)
+    d = H.shape[0]
+    if H.dtype != torch.float32 or H.shape != (d, d) or not H.is_contiguous():
+        raise ValueError("H must be a contiguous float32 [d, d] tensor")
+    if X.dim() != 2 or X.shape[1] != d or X.stride(1) != 1 or X.dtype not in _DTYPE:
+        raise ValueError("X must be [tokens, d] with unit column stride, fp32/fp16/bf16")
+    n = X.shape[0]
+    if work is None:
+        work = _workspace(GPTQ_WS_HESSIAN, n, d, None, H.device)
+    _check(_lib.lib().gptq_hessian_accumulate(_ptr(H), d, _ptr(X), _DTYPE[X.dtype], n, X.stride(0), _ptr(work),
+                                              work.numel(), _stream(stream)))
+
+
+def gptq_factor(H: torch.Tensor, n_total: int, params: Params, U: Optional[torch.Tensor] = None,
+                perm: Optional[torch.Tensor] = None, work: Optional[torch.Tensor] = None,
+                stream=None) -> Tuple[torch.Tensor, torch.Tensor]:
+    """(U, perm): U upper with (H/n + lambda I)[perm][:, perm]^-1 = U^T U. Raises GPTQError (with
+    .info) when the damped Hessian is not positive definite."""
+    _need_cuda(H, U, perm, work)
+    d = H.shape[0]
+    if H.dtype != torch.float32 or H.shape != (d, d) or not H.is_contiguous():
+        raise ValueError("H must be a contiguous float32 [d, d] tensor")
+    if U is None:
+        U = torch.empty((d, d), dtype=torch.float32, device=H.device)
+    if perm is None:
+        perm = torch.empty(d, dtype=torch.int32, device=H.device)
+    if work is None:
+        work = _workspace(GPTQ_WS_FACTOR, 0, d, params, H.device)
+    info = ctypes.c_int64(0)
+    st = _lib.lib().gptq_factor(_ptr(H), d, int(n_total), ctypes.byref(params.c()), _ptr(U), _ptr(perm), _ptr(work),
+                                work.numel(), ctypes.byref(info), _stream(stream))
+    _check(st, info.value)
+    return U, perm
+
+
+def gptq_quantize_layer(W: torch.Tensor, U: torch.Tensor, perm: torch.Tensor, params: Params,
+                        out: Optional[QuantOutput] = None, work: Optional[torch.Tensor] = None,
+                        stream=None) -> QuantOutput:
+    """The column loop: codes (original order), per-group scales and zeros, g_idx and the loss."""
+    _need_cuda(W, U, perm, work)
+    rows, d = W.shape
+    if W.stride(1) != 1 or W.dtype not in _DTYPE:
+        raise ValueError("W must be [rows, d] with unit column stride, fp32/fp16/bf16")
+    if U.shape != (d, d) or U.dtype != torch.float32 or not U.is_contiguous():
+        raise ValueError("U must be a contiguous float32 [d, d] tensor")
+    if perm.shape != (d,) or perm.dtype != torch.int32:
+        raise ValueError("perm must be int32 [d]")
+    dev = W.device
+    if out is None:
+        ng = params.groups(d)
+        out = QuantOutput(codes=torch.empty((rows, d), dtype=torch.uint8, device=dev),
+                          scales=torch.empty((rows, ng), dtype=torch.float32, device=dev),
+                          zeros=torch.empty((rows, ng), dtype=torch.int32, device=dev),
+                          g_idx=torch.empty(d, dtype=torch.int32, device=dev),
+                          loss=torch.empty(1, dtype=torch.float64, device=dev))
+    if work is None:
+        work = _workspace(GPTQ_WS_QUANTIZE, rows, d, params, dev)
+    st = _lib.lib().gptq_quantize_layer(_ptr(W), _DTYPE[W.dtype], rows, d, W.stride(0), _ptr(U), _ptr(perm),
+                                        ctypes.byref(params.c()), _ptr(out.codes), _ptr(out.scales),
+                                        _ptr(out.zeros), _ptr(out.g_idx), _ptr(out.loss), _ptr(work), work.numel(),
+                                        _stream(stream))
+    _check(st)
+    return out
+
+
+def gptq_pack(codes: torch.Tensor, bits: int, packed: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """int32 [rows, d / 8]: eight codes per word, column 8k + t in bits 4t..4t+3 of word k."""
+    _need_cuda(codes, packed)
+    rows, d = codes.shape
+    if codes.dtype != torch.uint8 or not codes.is_contiguous():
+        raise ValueError("codes must be contiguous uint8 [rows, d]")
+    if packed is None:
+        packed = torch.empty((rows, d // 8), dtype=torch.int32, device=codes.device)
+    _check(_lib.lib().gptq_pack(_ptr(codes), rows, d, int(bits), _ptr(packed), _stream(stream)))
+    return packed
+
+
+@dataclass
+class LayerResult:
+    H: torch.Tensor
+    U: torch.Tensor
+    perm: torch.Tensor
+    quant: QuantOutput
+    packed: Optional[torch.Tensor]
+
+
+def quantize_layer(W: torch.Tensor, X_chunks, params: Params, stream=None) -> LayerResult:
+    """The four calls in order for one layer: Hessian over the chunks, factor, column loop, pack."""
+    d = W.shape[1]
+    H = torch.zeros((d, d), dtype=torch.float32, device=W.device)
+    n = 0
+    work = None
+    for xc in X_chunks:
+        if work is None:
+            work = _workspace(GPTQ_WS_HESSIAN, xc.shape[0], d, None, W.device)
+        elif work.numel() < gptq_workspace_bytes(GPTQ_WS_HESSIAN, xc.shape[0], d):
+            work = _workspace(GPTQ_WS_HESSIAN, xc.shape[0], d, None, W.device)
+        gptq_hessian_accumulate(H, xc, work=work, stream=stream)
+        n += xc.shape[0]
+    U, perm = gptq_factor(H, n, params, stream=stream)
+    q = gptq_quantize_layer(W, U, perm, params, stream=stream)
+    packed = gptq_pack(q.codes, params.bits, stream=stream) if (d % 8 == 0 and params.bits <= 4) else None
+    return LayerResult(H=H, U=U, perm=perm, quant=q, packed=packed)

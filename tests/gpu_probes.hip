@@ -1,0 +1,99 @@
+// Probes of compiler builtins and device helpers the solver's kernels rely on, run by the GPU tests:
+// the lane layouts of the MFMA instructions, the DPP row broadcast, and the division helper.
+// Every kernel is launched with exactly the grid its indexing assumes (checked on the host first).
+#include "../post_weight_quantization_20_amd/csrc/common.hpp"
+
+using namespace gptq;
+
+namespace {
+
+// D (32 x 32) = A (32 x 16) B (16 x 32), fp16 or bf16 bit patterns, row-major; one wave.
+template <typename V, typename E>
+__global__ void mfma16_kernel(const uint16_t* A, const uint16_t* B, float* D) {
+  const int l = threadIdx.x;
+  V a, b;
+  for (int e = 0; e < 8; ++e) {
+    a[e] = __builtin_bit_cast(E, A[(l % 32) * 16 + 8 * (l / 32) + e]);
+    b[e] = __builtin_bit_cast(E, B[(8 * (l / 32) + e) * 32 + l % 32]);
+  }
+  floatx16 acc;
+  for (int r = 0; r < 16; ++r) acc[r] = 0.0f;
+  if constexpr (sizeof(E) == 2 && std::is_same<E, _Float16>::value)
+    acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, acc, 0, 0, 0);
+  else
+    acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, acc, 0, 0, 0);
+  for (int r = 0; r < 16; ++r) D[(8 * (r / 4) + 4 * (l / 32) + r % 4) * 32 + l % 32] = acc[r];
+}
+
+// D (32 x 32) = A (32 x 2) B (2 x 32), fp32; one wave.
+__global__ void mfma_f32_kernel(const float* A, const float* B, float* D) {
+  const int l = threadIdx.x;
+  floatx16 acc;
+  for (int r = 0; r < 16; ++r) acc[r] = 0.0f;
+  acc = __builtin_amdgcn_mfma_f32_32x32x2f32(A[(l % 32) * 2 + l / 32], B[(l / 32) * 32 + l % 32], acc, 0, 0, 0);
+  for (int r = 0; r < 16; ++r) D[(8 * (r / 4) + 4 * (l / 32) + r % 4) * 32 + l % 32] = acc[r];
+}
+
+// out[src * 64 + lane] = value of lane (16 * (lane / 16) + src), through row_bcast<src>; one wave.
+__global__ void bcast_kernel(const float* in, float* out) {
+  const int l = threadIdx.x;
+  const float v = in[l];
+  static_for<0, 16>([&](auto sc) {
+    constexpr int src = decltype(sc)::value;
+    out[src * 64 + l] = row_bcast<src>(v);
+  });
+}
+
+// out[lane] = value of lane 16 * (lane / 16) + (lane + 1) % 16, through row_ror15; one wave.
+__global__ void ror_kernel(const float* in, float* out) {
+  const int l = threadIdx.x;
+  out[l] = row_ror15(in[l]);
+}
+
+__global__ void div_kernel(const float* w, const float* s, int64_t n, float* fast, float* ieee) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) {
+    const float rs = 1.0f / s[i];
+    fast[i] = div_rn(w[i], s[i], rs);
+    ieee[i] = w[i] / s[i];
+  }
+}
+
+int sync_status() { return hipDeviceSynchronize() == hipSuccess && hipGetLastError() == hipSuccess ? 0 : -4; }
+
+}  // namespace
+
+extern "C" {
+
+int probe_mfma_f16(const uint16_t* A, const uint16_t* B, float* D) {
+  hipLaunchKernelGGL((mfma16_kernel<half8, _Float16>), dim3(1), dim3(64), 0, 0, A, B, D);
+  return sync_status();
+}
+
+int probe_mfma_bf16(const uint16_t* A, const uint16_t* B, float* D) {
+  hipLaunchKernelGGL((mfma16_kernel<bf16x8, __bf16>), dim3(1), dim3(64), 0, 0, A, B, D);
+  return sync_status();
+}
+
+int probe_mfma_f32(const float* A, const float* B, float* D) {
+  hipLaunchKernelGGL(mfma_f32_kernel, dim3(1), dim3(64), 0, 0, A, B, D);
+  return sync_status();
+}
+
+int probe_row_bcast(const float* in, float* out) {
+  hipLaunchKernelGGL(bcast_kernel, dim3(1), dim3(64), 0, 0, in, out);
+  return sync_status();
+}
+
+int probe_row_ror15(const float* in, float* out) {
+  hipLaunchKernelGGL(ror_kernel, dim3(1), dim3(64), 0, 0, in, out);
+  return sync_status();
+}
+
+int probe_div(const float* w, const float* s, int64_t n, float* fast, float* ieee) {
+  if (n <= 0) return 0;
+  hipLaunchKernelGGL(div_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, 0, w, s, n, fast, ieee);
+  return sync_status();
+}
+
+}  // extern "C"

@@ -1,0 +1,313 @@
+"""Parity of the HIP path (through the C ABI) with the float64 oracle on seeded synthetic layers.
+
+Sizes span several tiles of every kernel and end in ragged tails: 256x256 Hessian tiles and 64-token
+stages, 128x128 GEMM tiles, 16-row column-loop workgroups, 128-column blocks and short last groups.
+
+Bars: integer outputs bit-exact (perm, g_idx, packed words); codes and zero points identical outside
+rounding ties (the oracle follows the GPU only where its own float32 rounding ratio lies within
+1e-3 of a half-integer) with at most 0.1% of codes decided differently at ties; scales within 1e-5
+relative; the loss (layer reconstruction error) within 1e-3 relative. Hessian and factor outputs are
+compared with bounds derived from float32 arithmetic (in each test).
+"""
+
+import numpy as np
+import pytest
+
+import synth
+from gpu_util import (LOSS_RTOL, TAU, check_quant_parity, dequant, dev_tensor, gpu_layer, params_of,
+                      torch_cuda)
+from oracle import gptq_ref as ref
+
+pytestmark = pytest.mark.gpu
+
+U32 = 2.0 ** -24
+
+
+def _case(name, seed, **kw):
+    base = dict(rows=200, d=300, n=1000, w_std=0.02, w_dtype="f16", x_dist="normal", x_dtype="f16",
+                outlier_frac=0.01, outlier_scale=20.0, chunk=512, bits=4, group_size=128, block_size=128)
+    base.update(kw)
+    return synth.make_case(name=name, seed=seed, **base)
+
+
+def _oracle_follow(case, W, chunks, out, tau=TAU):
+    """The oracle on the same stored inputs, following the GPU at ties and (act-order) in the order of
+    keys equal within float32 rounding."""
+    H, n = ref.hessian([synth.to_f64(x, case.x_dtype) for x in chunks])
+    perm = None
+    if case.act_order:
+        perm = _checked_perm(out["perm"], H)
+    return ref.gptq(synth.to_f64(W, case.w_dtype), None, case.bits, case.group_size, case.block_size,
+                    act_order=case.act_order, damp=case.damp, perm=perm,
+                    follow=(out["codes"][:, out["perm"]], out["zeros"]), tau=tau, H=H, n=n)
+
+
+def _checked_perm(gperm, H, rtol=1e-5):
+    """The GPU's processing order, after checking it sorts diag(H) descending up to float32 rounding
+    of the sums (equal keys in any order)."""
+    d = H.shape[0]
+    assert np.array_equal(np.sort(gperm), np.arange(d))
+    own = ref.act_order_perm(H)
+    if np.array_equal(own, gperm):
+        return own
+    dk = np.diag(H)[gperm]
+    assert np.all(dk[1:] <= dk[:-1] * (1 + rtol)), "GPU order is not descending in diag(H)"
+    return gperm
+
+
+# ------------------------------------------------------------------ Hessian
+
+@pytest.mark.parametrize("x_dtype,d,n,chunk", [("f16", 300, 1000, 512), ("bf16", 300, 1000, 512),
+                                               ("f32", 300, 1000, 512), ("f16", 300, 4500, 4500),
+                                               ("f16", 520, 2100, 2048), ("bf16", 8, 70, 64)])
+def test_hessian_parity(x_dtype, d, n, chunk):
+    """Upper triangle of H = sum 2 X_c^T X_c vs the float64 sum, within the float32 summation bound
+    gamma_n * sum |2 x_i x_j| (products of fp16/bf16 values are exact in float32)."""
+    torch = torch_cuda()
+    import post_weight_quantization_20_amd as g
+    case = _case("h", 11, d=d, n=n, chunk=chunk, x_dtype=x_dtype)
+    chunks = [synth.x_chunk(case, c) for c in range(case.n_chunks)]
+    H = torch.zeros((d, d), dtype=torch.float32, device="cuda")
+    for x in chunks:
+        g.gptq_hessian_accumulate(H, dev_tensor(x, x_dtype))
+    torch.cuda.synchronize()
+    got = np.triu(H.cpu().numpy().astype(np.float64))
+    x64 = [synth.to_f64(x, x_dtype) for x in chunks]
+    want, _ = ref.hessian(x64)
+    absH, _ = ref.hessian([np.abs(x) for x in x64])
+    bound = (n * U32 / (1 - n * U32)) * absH + 1e-30
+    diff = np.abs(got - np.triu(want))
+    assert np.all(np.triu(diff) <= np.triu(bound))
+    assert np.linalg.norm(np.triu(diff)) <= 1e-5 * np.linalg.norm(np.triu(want))
+
+
+def test_hessian_deterministic_with_token_splits():
+    """One long chunk (token splits with the ordered fixup) gives the same H twice, bit for bit."""
+    torch = torch_cuda()
+    import post_weight_quantization_20_amd as g
+    case = _case("h2", 12, d=260, n=8192, chunk=8192)
+    x = dev_tensor(synth.x_chunk(case, 0), "f16")
+    outs = []
+    for _ in range(2):
+        H = torch.zeros((260, 260), dtype=torch.float32, device="cuda")
+        g.gptq_hessian_accumulate(H, x)
+        outs.append(np.triu(H.cpu().numpy()))
+    assert g.gptq_workspace_bytes(g.GPTQ_WS_HESSIAN, 8192, 260) > 0
+    assert np.array_equal(outs[0].view(np.uint32), outs[1].view(np.uint32))
+
+
+# ------------------------------------------------------------------ factor
+
+@pytest.mark.parametrize("d,act", [(300, False), (300, True), (129, True), (7, False), (640, False)])
+def test_factor_parity(d, act):
+    """U from the same float32 H: max elementwise error relative to max|U| and the residual
+    U^T U Hhat - I within d * kappa * u32 (the first-order float32 error of a Cholesky-based
+    inverse factor), U upper with a positive diagonal, and perm identical."""
+    torch = torch_cuda()
+    import post_weight_quantization_20_amd as g
+    case = _case("f", 20 + d, d=d, n=3 * d + 50, chunk=4096, x_dtype="f32")
+    x = synth.to_f64(synth.x_chunk(case, 0), "f32")
+    H64, n = ref.hessian([x])
+    H32 = H64.astype(np.float32)
+    Hh, perm, lam = ref.damp_and_order(H32.astype(np.float64), n, 0.01, act)
+    U_ref = ref.inverse_cholesky_upper(Hh)
+    Ud, pd = g.gptq_factor(torch.from_numpy(H32).cuda(), n, g.Params(act_order=act, damp=0.01))
+    U = Ud.cpu().numpy().astype(np.float64)
+    assert np.array_equal(pd.cpu().numpy().astype(np.int64), perm)
+    assert np.all(np.tril(U, -1) == 0)
+    assert np.all(np.diag(U) > 0)
+    ev = np.linalg.eigvalsh(Hh)
+    kappa = ev[-1] / ev[0]
+    tol = max(1e-4, d * kappa * U32)
+    err = np.max(np.abs(U - U_ref)) / np.max(np.abs(U_ref))
+    assert err <= tol, (err, kappa)
+    resid = np.max(np.abs(U.T @ U @ Hh - np.eye(d)))
+    assert resid <= tol, (resid, kappa)
+    print(f"d={d} kappa={kappa:.3g} max rel err {err:.3g} residual {resid:.3g}")
+
+
+def test_factor_not_positive_definite():
+    """A dead input feature with no damping: the factor reports GPTQ_ENOTPD and the feature's
+    1-based position (tools page, "When the method breaks down")."""
+    torch = torch_cuda()
+    import post_weight_quantization_20_amd as g
+    rng = np.random.default_rng(5)
+    X = rng.standard_normal((80, 40)).astype(np.float32)
+    X[:, 17] = 0
+    H = (2 * X.T.astype(np.float64) @ X).astype(np.float32)
+    with pytest.raises(g.GPTQError) as ei:
+        g.gptq_factor(torch.from_numpy(H).cuda(), 80, g.Params(damp=0.0))
+    assert ei.value.status == g.GPTQ_ENOTPD
+    assert ei.value.info == 18
+    Hh, _, _ = ref.damp_and_order(H.astype(np.float64), 80, 0.0, False)
+    with pytest.raises(ref.NotPositiveDefinite) as eo:
+        ref.inverse_cholesky_upper(Hh)
+    assert eo.value.pivot == 18
+    g.gptq_factor(torch.from_numpy(H).cuda(), 80, g.Params(damp=0.01))   # damping repairs it
+    with pytest.raises(g.GPTQError) as ez:
+        g.gptq_factor(torch.zeros((8, 8), dtype=torch.float32, device="cuda"), 10, g.Params())
+    assert ez.value.status == g.GPTQ_EINVAL
+
+
+# ------------------------------------------------------------------ column loop (same U)
+
+QCASES = [
+    dict(bits=4, group_size=128, block_size=128),
+    dict(bits=3, group_size=0, block_size=128),
+    dict(bits=2, group_size=32, block_size=32),
+    dict(bits=4, group_size=16, block_size=64),
+    dict(bits=4, group_size=256, block_size=64, d=700),
+    dict(bits=4, group_size=50, block_size=100, d=300),
+    dict(bits=8, group_size=64, block_size=128),
+    dict(bits=4, group_size=128, block_size=8),
+]
+
+
+@pytest.mark.parametrize("kw", QCASES, ids=[str(i) for i in range(len(QCASES))])
+@pytest.mark.parametrize("act", [False, True])
+def test_quantize_parity_same_factor(kw, act):
+    """gptq_quantize_layer fed the oracle's U (rounded to float32) against the oracle on that U."""
+    torch = torch_cuda()
+    import post_weight_quantization_20_amd as g
+    kw = dict(kw)
+    d = kw.pop("d", 300)
+    case = _case("q", 30 + d, d=d, n=2 * d, chunk=4096, x_dtype="f32", w_dtype="f32", act_order=act, **kw)
+    W = synth.weight(case)
+    H, n = ref.hessian([synth.to_f64(synth.x_chunk(case, 0), "f32")])
+    Hh, perm, lam = ref.damp_and_order(H, n, case.damp, act)
+    U32 = ref.inverse_cholesky_upper(Hh).astype(np.float32)
+    p = params_of(case)
+    q = g.gptq_quantize_layer(torch.from_numpy(W).cuda(), torch.from_numpy(U32).cuda(),
+                              torch.from_numpy(perm.astype(np.int32)).cuda(), p)
+    torch.cuda.synchronize()
+    out = dict(codes=q.codes.cpu().numpy(), scales=q.scales.cpu().numpy(), zeros=q.zeros.cpu().numpy(),
+               g_idx=q.g_idx.cpu().numpy(), loss=float(q.loss.cpu().numpy()[0]))
+    o = ref.quantize_layer(W.astype(np.float64), U32.astype(np.float64), case.bits, case.group_size,
+                           case.block_size, perm=perm, follow=(out["codes"][:, perm], out["zeros"]), tau=TAU)
+    check_quant_parity(out, o)
+    # the dequantized weights equal the oracle's
+    assert np.allclose(dequant(out["codes"], out["scales"], out["zeros"], out["g_idx"]), o.Q, rtol=1e-5, atol=1e-7)
+
+
+# ------------------------------------------------------------------ whole layer
+
+ECASES = [
+    dict(rows=200, d=300, bits=4, group_size=128, block_size=128),
+    dict(rows=200, d=300, bits=4, group_size=128, block_size=128, act_order=True, x_dist="laplace",
+         outlier_frac=0.005, outlier_scale=30.0),
+    dict(rows=77, d=384, bits=3, group_size=0, block_size=128, w_std=0.01),
+    dict(rows=33, d=200, bits=2, group_size=32, block_size=32, act_order=True, w_dtype="bf16", x_dtype="bf16"),
+    dict(rows=1, d=72, bits=4, group_size=8, block_size=16, w_dtype="f32", x_dtype="f32"),
+    dict(rows=130, d=520, bits=4, group_size=256, block_size=64, act_order=True, n=2100, chunk=2048),
+]
+
+
+@pytest.mark.parametrize("kw", ECASES, ids=[str(i) for i in range(len(ECASES))])
+def test_layer_parity(kw):
+    """The four calls from X and W against the oracle's whole layer on the same stored inputs."""
+    case = _case("e", 40 + len(str(kw)), **kw)
+    W, chunks, out = gpu_layer(case)
+    o = _oracle_follow(case, W, chunks, out)
+    check_quant_parity(out, o.quant)
+    if out["packed"] is not None:
+        assert np.array_equal(out["packed"], ref.pack(out["codes"], case.bits))
+    # layer output error ||X (W - Q)^T||^2 from each side's dequantized weights
+    X = np.concatenate([synth.to_f64(x, case.x_dtype) for x in chunks])
+    W64 = synth.to_f64(W, case.w_dtype)
+    e_gpu = np.sum((X @ (W64 - dequant(out["codes"], out["scales"], out["zeros"], out["g_idx"])).T) ** 2)
+    e_ref = np.sum((X @ (W64 - o.quant.Q).T) ** 2)
+    assert abs(e_gpu - e_ref) <= LOSS_RTOL * e_ref
+
+
+def test_tiny_config():
+    """The tiny layer workload (64x128 fp32, 512 tokens, 4-bit g32 B32): codes identical."""
+    case = synth.case_from_config("tiny")
+    W, chunks, out = gpu_layer(case)
+    o = _oracle_follow(case, W, chunks, out)
+    check_quant_parity(out, o.quant)
+    assert o.quant.adopted_diff == 0
+    assert np.array_equal(out["packed"], ref.pack(out["codes"], 4))
+
+
+def test_identity_hessian_gives_rtn():
+    """H = I: the GPU reproduces per-group round-to-nearest exactly, including the page's example
+    (a row with min 0 and max 1.5 at 4 bits has scale 0.1 and 0.75 takes code 8)."""
+    torch = torch_cuda()
+    import post_weight_quantization_20_amd as g
+    rng = np.random.default_rng(9)
+    W = (rng.standard_normal((40, 64)) * 0.02).astype(np.float32)
+    W[0, :4] = [0.0, 1.5, 0.75, 0.3]
+    p = g.Params(bits=4, group_size=16, block_size=32)
+    H = torch.eye(64, dtype=torch.float32, device="cuda") * 2
+    U, perm = g.gptq_factor(H, 1, p)
+    q = g.gptq_quantize_layer(torch.from_numpy(W).cuda(), U, perm, p)
+    t = ref.rtn(W.astype(np.float64), 4, 16)
+    assert np.array_equal(q.codes.cpu().numpy(), t.codes)
+    assert q.codes[0, 2].item() == 8
+    assert np.isclose(q.scales[0, 0].item(), np.float32(1.5) / np.float32(15), rtol=0)
+
+
+def test_determinism():
+    case = _case("det", 77, rows=100, d=260, n=3000, chunk=3000, act_order=True)
+    _, _, a = gpu_layer(case)
+    _, _, b = gpu_layer(case)
+    for k in ("H", "U", "codes", "scales", "zeros", "perm", "packed"):
+        assert np.array_equal(np.asarray(a[k]).view(np.uint8), np.asarray(b[k]).view(np.uint8)), k
+    assert a["loss"] == b["loss"]
+
+
+def test_rows_split_across_calls():
+    """Rows are independent: quantizing W in two row slices gives the same outputs as one call."""
+    torch = torch_cuda()
+    import post_weight_quantization_20_amd as g
+    case = _case("rows", 78, rows=96, d=256, n=600, x_dtype="f32", w_dtype="f32")
+    W = synth.weight(case)
+    H, n = ref.hessian([synth.to_f64(synth.x_chunk(case, 0), "f32")])
+    Hh, perm, _ = ref.damp_and_order(H, n, 0.01, False)
+    U = torch.from_numpy(ref.inverse_cholesky_upper(Hh).astype(np.float32)).cuda()
+    pd = torch.from_numpy(perm.astype(np.int32)).cuda()
+    p = params_of(case)
+    Wd = torch.from_numpy(W).cuda()
+    full = g.gptq_quantize_layer(Wd, U, pd, p)
+    a = g.gptq_quantize_layer(Wd[:40], U, pd, p)
+    b = g.gptq_quantize_layer(Wd[40:], U, pd, p)
+    assert torch.equal(torch.cat([a.codes, b.codes]), full.codes)
+    assert torch.equal(torch.cat([a.scales, b.scales]), full.scales)
+
+
+def test_empty_and_degenerate_inputs():
+    torch = torch_cuda()
+    import post_weight_quantization_20_amd as g
+    p = g.Params(bits=4, group_size=8, block_size=16)
+    d = 32
+    H = torch.zeros((d, d), dtype=torch.float32, device="cuda")
+    g.gptq_hessian_accumulate(H, torch.zeros((0, d), dtype=torch.float16, device="cuda"))   # empty chunk
+    assert torch.count_nonzero(H).item() == 0
+    U, perm = g.gptq_factor(torch.eye(d, device="cuda") * 2, 1, p)
+    q = g.gptq_quantize_layer(torch.zeros((0, d), dtype=torch.float16, device="cuda"), U, perm, p)  # no rows
+    assert q.loss.item() == 0.0
+    assert torch.equal(q.g_idx.cpu(), torch.arange(d, dtype=torch.int32) // 8)
+    # constant rows: scale 1e-8 / maxq, every code 0, dequantized value = the constant
+    W = torch.full((3, d), 0.3, dtype=torch.float32, device="cuda")
+    W[1] = -0.7
+    W[2] = 0.0
+    q = g.gptq_quantize_layer(W, U, perm, p)
+    assert torch.count_nonzero(q.codes).item() == 0
+    Q = dequant(q.codes.cpu().numpy(), q.scales.cpu().numpy(), q.zeros.cpu().numpy(), q.g_idx.cpu().numpy())
+    assert np.allclose(Q, W.cpu().numpy(), atol=1e-7)
+
+
+def test_pack_bit_exact():
+    torch = torch_cuda()
+    import post_weight_quantization_20_amd as g
+    rng = np.random.default_rng(4)
+    for rows, d, bits in ((37, 8, 4), (5, 1032, 3), (300, 4096, 4), (1, 64, 2)):
+        c = rng.integers(0, 1 << bits, size=(rows, d)).astype(np.uint8)
+        c[0, :8] = [1, 2, 3, 4, 5, 6, 7, 8][: 8] if bits == 4 else c[0, :8]
+        got = g.gptq_pack(torch.from_numpy(c).cuda(), bits).cpu().numpy()
+        assert np.array_equal(got, ref.pack(c, bits))
+    # an unaligned view of the codes (odd byte offset) takes the scalar path
+    big = torch.from_numpy(rng.integers(0, 16, size=(4 * 64 + 1,)).astype(np.uint8)).cuda()
+    view = big[1:].view(4, 64)
+    assert view.is_contiguous() and view.data_ptr() % 8 != 0
+    assert np.array_equal(g.gptq_pack(view, 4).cpu().numpy(), ref.pack(view.cpu().numpy(), 4))
