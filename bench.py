@@ -1,0 +1,244 @@
+"""Throughput of the GPTQ layer solver on one MI355X.
+
+A step is one pass of the whole hot path for one layer: the Hessian over all calibration tokens, the
+damped factor, the column loop with lazy block updates, and packing, on inputs already resident in
+HBM. The default workload is the Llama-7B q_proj-shaped layer (W 4096x4096 fp16, X 262144 tokens x
+4096 fp16 with 1% outlier channels x20, 4-bit asymmetric, groups of 128, blocks of 128, damp 0.01).
+
+Prints one JSON line: weight-columns/s (d / seconds per layer), the per-phase times, the roofline
+of the dominant kernel (live HIP-event timing on the launch stream), and the float64 oracle timed on
+a bounded sample of the same workload on the host cores.
+
+    python bench.py [--steps K] [--warmup W] [--gpus 1] [--workload q_proj] [--no-cpu-baseline]
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_F16_TFLOPS = 2500.0      # MI355X dense fp16/bf16 matrix peak
+PEAK_F32_TFLOPS = 157.3       # MI355X fp32 matrix peak
+PEAK_HBM_GBS = 8000.0         # MI355X HBM3E
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.json")
+KERNEL_SOURCES = {"hess_kernel": "post_weight_quantization_20_amd/csrc/hessian.hip"}
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="q_proj", choices=["q_proj", "down_proj", "fc2", "tiny"])
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-sample-seconds", type=float, default=20.0)
+    return ap.parse_args()
+
+
+def source_hash(rel: str) -> str:
+    with open(os.path.join(ROOT, rel), "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def load_traffic(kernel: str, workload: str):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, if it was taken on the
+    current source of the kernel and this workload; otherwise None."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            rec = json.load(f)[kernel]
+    except (OSError, KeyError, ValueError):
+        return None
+    if rec.get("workload") != workload or rec.get("source_sha256_16") != source_hash(KERNEL_SOURCES[kernel]):
+        return None
+    return rec.get("bytes_per_launch")
+
+
+def cpu_baseline(case, budget_s: float):
+    """The oracle, as it stands, on a bounded sample of the workload: a few token chunks for the
+    Hessian, the full-size factor, a slice of rows for the column loop, the pack of that slice;
+    each phase time scaled to the full layer."""
+    import synth
+    from oracle import gptq_ref as ref
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([i.get("num_threads", 1) for i in threadpool_info()] or [os.cpu_count() or 1])
+    except Exception:
+        cores = os.cpu_count() or 1
+    d = case.d
+    # Hessian: chunks until ~1/3 of the budget (at least one)
+    t_h, used = 0.0, 0
+    H = np.zeros((d, d))
+    outl = synth.outlier_channels(case)
+    while used < case.n_chunks:
+        x = synth.to_f64(synth.x_chunk(case, used, outl), case.x_dtype)
+        t0 = time.perf_counter()
+        Hc, _ = ref.hessian([x])
+        t_h += time.perf_counter() - t0
+        H += Hc
+        used += 1
+        if t_h > budget_s / 3:
+            break
+    tok_sample = sum(case.chunk_tokens(c) for c in range(used))
+    hess_full = t_h * case.n / tok_sample
+    # factor at full size (its input only needs to be a valid Hessian; the sampled one is)
+    t0 = time.perf_counter()
+    Hh, perm, _ = ref.damp_and_order(H, tok_sample, case.damp, case.act_order)
+    U = ref.inverse_cholesky_upper(Hh)
+    fac = time.perf_counter() - t0
+    # column loop on a row slice
+    W = synth.to_f64(synth.weight(case), case.w_dtype)
+    rows = max(16, min(case.rows, int(case.rows * 0.02)))
+    t0 = time.perf_counter()
+    q = ref.quantize_layer(W[:rows], U, case.bits, case.group_size, case.block_size, perm=perm)
+    tq = time.perf_counter() - t0
+    quant_full = tq * case.rows / rows
+    t0 = time.perf_counter()
+    if d % 8 == 0 and case.bits <= 4:
+        ref.pack(q.codes, case.bits)
+    tp = (time.perf_counter() - t0) * case.rows / rows
+    total = hess_full + fac + quant_full + tp
+    return {
+        "value": d / total,
+        "unit": "weight-columns/s",
+        "cores": int(cores),
+        "kind": "oracle",
+        "sec_per_layer": total,
+        "phases_s": {"hessian": hess_full, "factor": fac, "quantize": quant_full, "pack": tp},
+        "sample": (f"float64 oracle: Hessian on {tok_sample} of {case.n} tokens, factor at full d={d}, "
+                   f"column loop and pack on {rows} of {case.rows} rows; each phase scaled to the full layer"),
+    }
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU only: the solver runs on a single MI355X and this build has no "
+              "multi-GPU path (rows of W are independent, so a layer would shard by rows; see DESIGN.md).",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import post_weight_quantization_20_amd as g
+    import synth
+
+    case = synth.case_from_config(args.workload)
+    dev = torch.device("cuda:0")
+    params = g.Params(bits=case.bits, group_size=case.group_size, block_size=case.block_size,
+                      act_order=case.act_order, damp=case.damp)
+    d, rows, n = case.d, case.rows, case.n
+    print(f"[bench] generating {args.workload}: W {rows}x{d} {case.w_dtype}, X {n}x{d} {case.x_dtype}",
+          file=sys.stderr, flush=True)
+    t0 = time.perf_counter()
+    X_host = synth.x_tokens(case)
+    W_host = synth.weight(case)
+    to_t = {"f16": torch.float16, "f32": torch.float32}
+    X = torch.from_numpy(X_host).to(dev)
+    W = torch.from_numpy(W_host).to(dev)
+    del X_host
+    torch.cuda.synchronize()
+    print(f"[bench] inputs resident in HBM ({time.perf_counter() - t0:.1f} s)", file=sys.stderr, flush=True)
+
+    # buffers and workspaces allocated once, outside the timed region
+    H = torch.empty((d, d), dtype=torch.float32, device=dev)
+    U = torch.empty((d, d), dtype=torch.float32, device=dev)
+    perm = torch.empty(d, dtype=torch.int32, device=dev)
+    ng = params.groups(d)
+    qout = g.QuantOutput(codes=torch.empty((rows, d), dtype=torch.uint8, device=dev),
+                         scales=torch.empty((rows, ng), dtype=torch.float32, device=dev),
+                         zeros=torch.empty((rows, ng), dtype=torch.int32, device=dev),
+                         g_idx=torch.empty(d, dtype=torch.int32, device=dev),
+                         loss=torch.empty(1, dtype=torch.float64, device=dev))
+    packed = torch.empty((rows, d // 8), dtype=torch.int32, device=dev)
+    ws_h = torch.empty(max(1, g.gptq_workspace_bytes(g.GPTQ_WS_HESSIAN, n, d)), dtype=torch.uint8, device=dev)
+    ws_f = torch.empty(g.gptq_workspace_bytes(g.GPTQ_WS_FACTOR, 0, d, params), dtype=torch.uint8, device=dev)
+    ws_q = torch.empty(g.gptq_workspace_bytes(g.GPTQ_WS_QUANTIZE, rows, d, params), dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream()
+
+    def step(ev=None):
+        H.zero_()
+        if ev is not None:
+            ev[0].record(stream)
+        g.gptq_hessian_accumulate(H, X, work=ws_h)
+        if ev is not None:
+            ev[1].record(stream)
+        g.gptq_factor(H, n, params, U=U, perm=perm, work=ws_f)
+        if ev is not None:
+            ev[2].record(stream)
+        g.gptq_quantize_layer(W, U, perm, params, out=qout, work=ws_q)
+        if ev is not None:
+            ev[3].record(stream)
+        g.gptq_pack(qout.codes, case.bits, packed=packed)
+        if ev is not None:
+            ev[4].record(stream)
+
+    for i in range(args.warmup):
+        step()
+        print(f"[bench] warmup {i + 1}/{args.warmup}", file=sys.stderr, flush=True)
+    torch.cuda.synchronize()
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(events[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    print(f"[bench] timed {args.steps} steps in {wall:.3f} s", file=sys.stderr, flush=True)
+    ph = np.array([[e[j].elapsed_time(e[j + 1]) for j in range(4)] for e in events])  # ms
+    hess_ms, fac_ms, quant_ms, pack_ms = ph.mean(axis=0)
+    ms_per_step = wall * 1000.0 / args.steps
+    sec_layer = ms_per_step / 1000.0
+
+    # The Hessian call launches the MFMA kernel (and, when the token range is split, a fill of its
+    # tile counters); the event interval covers both, so the kernel's rate below is a lower bound.
+    flops = float(n) * d * (d + 1)           # the symmetric half of 2 n d^2
+    hess_kernel_ms = hess_ms
+    achieved = flops / (hess_kernel_ms / 1000.0) / 1e12
+    traffic = load_traffic("hess_kernel", args.workload)
+    roof = {"kernel": "hess_kernel (Hessian, fp16 MFMA)", "bound": "mfma", "achieved": round(achieved, 2),
+            "peak": PEAK_F16_TFLOPS, "unit": "TFLOP/s", "frac": round(achieved / PEAK_F16_TFLOPS, 4),
+            "traffic": traffic, "flops_per_launch": flops, "avg_launch_ms": round(hess_kernel_ms, 4)}
+
+    out = {
+        "metric": "GPTQ sec/layer + weight-columns/s at 4096x4096 int4 g128; % MFMA / HBM peak",
+        "value": round(d / sec_layer, 1),
+        "unit": "weight-columns/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic (seeded; Llama-7B-shaped layer, no trained weights or datasets)",
+        "config": {"workload": f"{args.workload}: W {rows}x{d} {case.w_dtype}, X {n} tokens {case.x_dtype}, "
+                               f"{case.bits}-bit g{case.group_size if case.group_size > 0 else d} "
+                               f"B{case.block_size} damp {case.damp} act_order {int(case.act_order)}",
+                   "rows": rows, "d": d, "tokens": n, "bits": case.bits,
+                   "group_size": case.group_size, "block_size": case.block_size},
+        "sec_per_layer": round(sec_layer, 6),
+        "phases_ms": {"hessian": round(float(hess_ms), 4), "factor": round(float(fac_ms), 4),
+                      "quantize": round(float(quant_ms), 4), "pack": round(float(pack_ms), 4)},
+        "solver_only_ms": round(float(fac_ms + quant_ms + pack_ms), 4),
+        "weights_per_s": round(rows * d / sec_layer, 1),
+        "roofline": roof,
+    }
+    if not args.no_cpu_baseline:
+        print("[bench] timing the float64 oracle on a bounded sample", file=sys.stderr, flush=True)
+        out["cpu_baseline"] = cpu_baseline(case, args.cpu_sample_seconds)
+    else:
+        out["cpu_baseline"] = None
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

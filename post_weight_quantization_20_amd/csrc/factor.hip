@@ -20,7 +20,6 @@ namespace gptq {
 namespace {
 
 constexpr int NB = 128;
-constexpr int NBP = NB + 1;  // LDS row length (odd: column walks do not collide on banks)
 
 struct FactorWork {
   double* lam;     // damping added to the diagonal
@@ -105,79 +104,195 @@ __global__ __launch_bounds__(256) void gather_kernel(const float* __restrict__ H
   }
 }
 
-// Factors the diagonal block at (k0, k0) in LDS (A = L L^T, lower) and replaces the whole block in A
-// by the inverse of L (lower triangle; zeros above). A first non-positive pivot is recorded in info
-// and replaced by 1 so the remaining arithmetic stays finite.
+// ---------------------------------------------------------------- diagonal block: factor + inverse
+//
+// The 128 x 128 diagonal block is factored and inverted in LDS by one 256-thread workgroup, blocked
+// by 32: for each 32-column sub-panel, one wave factors and inverts the 32 x 32 diagonal sub-block in
+// registers (lane i holds row i; columns are broadcast with readlane, so no barriers), then the
+// waves apply the sub-panel solve and the symmetric update to the rest of the block as 32 x 32
+// MFMA tiles. The off-diagonal blocks of the inverse follow from block forward substitution,
+// X_qp = -X_qq sum_{t=p}^{q-1} L_qt X_tp, again as MFMA tiles.
+constexpr int LDB = NB + 1;   // LDS leading dimension (odd: row and column walks are conflict-free)
+constexpr int SB = 32;        // sub-block
+
+// acc (+)= op(A) op(B) over K for one 32 x 32 tile; A, B in LDS. op(A): A[i][k] or (TA) A[k][i];
+// op(B): B[k][j] or (TB) B[j][k]. One wave; lane l reads row/column l % 32 at k + l / 32.
+template <bool TA, bool TB>
+GPTQ_DEV floatx16 mma32(floatx16 acc, const float* A, int lda, const float* B, int ldb, int K, int lane,
+                        float sa = 1.0f) {
+  const int r = lane & 31, kk = lane >> 5;
+  for (int k = 0; k < K; k += 2) {
+    const float av = TA ? A[(k + kk) * lda + r] : A[r * lda + k + kk];
+    const float bv = TB ? B[r * ldb + k + kk] : B[(k + kk) * ldb + r];
+    acc = __builtin_amdgcn_mfma_f32_32x32x2f32(sa * av, bv, acc, 0, 0, 0);
+  }
+  return acc;
+}
+
+GPTQ_DEV floatx16 tile_load(const float* T, int ld, int lane) {
+  floatx16 v;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) v[r] = T[(8 * (r >> 2) + 4 * (lane >> 5) + (r & 3)) * ld + (lane & 31)];
+  return v;
+}
+
+GPTQ_DEV void tile_store(float* T, int ld, int lane, floatx16 v, float scale = 1.0f) {
+#pragma unroll
+  for (int r = 0; r < 16; ++r) T[(8 * (r >> 2) + 4 * (lane >> 5) + (r & 3)) * ld + (lane & 31)] = scale * v[r];
+}
+
+GPTQ_DEV floatx16 zero16() {
+  floatx16 v;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) v[r] = 0.0f;
+  return v;
+}
+
+// One wave: Cholesky factor of the 32 x 32 lower block at S (in place) and its inverse into Xs.
+// Lanes 32..63 repeat lanes 0..31. A non-positive pivot is recorded in info (1-based index
+// gbase + j + 1, when the column is real, j < valid) and replaced by 1.
+GPTQ_DEV void chol_inv32(float* S, float* Xs, int lane, int64_t* info, int64_t gbase, int valid) {
+  const int i = lane & 31;
+  float a[SB];
+#pragma unroll
+  for (int c = 0; c < SB; ++c) a[c] = (c <= i) ? S[i * LDB + c] : 0.0f;
+  static_for<0, SB>([&](auto jc) {
+    constexpr int j = decltype(jc)::value;
+    float p = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, a[j]), j));
+    if (!(p > 0.0f)) {
+      if (lane == 0 && j < valid && *info == 0) *info = gbase + j + 1;
+      p = 1.0f;
+    }
+    const float dj = sqrtf(p);
+    const float inv = 1.0f / dj;
+    const float lij = a[j] * inv;                   // L[i][j] for rows i > j
+    a[j] = (i > j) ? lij : ((i == j) ? dj : 0.0f);
+    static_for<j + 1, SB>([&](auto cc) {
+      constexpr int c = decltype(cc)::value;
+      const float lcj = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, lij), c));
+      if (i >= c) a[c] = __builtin_fmaf(-lij, lcj, a[c]);
+    });
+  });
+#pragma unroll
+  for (int c = 0; c < SB; ++c)
+    if (lane < SB) S[i * LDB + c] = (c <= i) ? a[c] : 0.0f;
+  // inverse by forward elimination, right-looking; row j is final once divided by L[j][j]
+  float x[SB];
+#pragma unroll
+  for (int c = 0; c < SB; ++c) x[c] = (c == i) ? 1.0f : 0.0f;
+  static_for<0, SB>([&](auto jc) {
+    constexpr int j = decltype(jc)::value;
+    const float ljj = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, a[j]), j));
+    const float inv = 1.0f / ljj;
+    if (i == j) {
+#pragma unroll
+      for (int c = 0; c <= j; ++c) x[c] *= inv;
+    }
+    static_for<0, j + 1>([&](auto cc) {
+      constexpr int c = decltype(cc)::value;
+      const float xjc = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x[c]), j));
+      if (i > j) x[c] = __builtin_fmaf(-a[j], xjc, x[c]);
+    });
+  });
+#pragma unroll
+  for (int c = 0; c < SB; ++c)
+    if (lane < SB) Xs[i * LDB + c] = x[c];
+}
+
+// Factors the diagonal block at (k0, k0) (A = L L^T, lower) and replaces the whole block in A by the
+// inverse of L (lower triangle; zeros above). A last block narrower than NB is padded with an
+// identity, which leaves the factor and inverse of the real part unchanged.
 __global__ __launch_bounds__(256) void chol_diag_kernel(float* __restrict__ A, int64_t d, int64_t k0, int nb,
                                                         int64_t* __restrict__ info) {
   extern __shared__ float sm[];
-  float* L = sm;              // [NB][NBP]
-  float* X = sm + NB * NBP;   // [NB][NBP]
-  __shared__ float dia[NB];
-  __shared__ float piv;
-  const int tid = threadIdx.x;
-  for (int e = tid; e < NB * NB; e += 256) {
-    const int r = e / NB, c = e % NB;
-    L[r * NBP + c] = (r < nb && c <= r) ? A[(k0 + r) * d + k0 + c] : 0.0f;
-    X[r * NBP + c] = (r == c) ? 1.0f : 0.0f;
+  float* La = sm;                 // [NB][LDB]: the block, then its Cholesky factor
+  float* Xa = sm + NB * LDB;      // [NB][LDB]: the inverse of the factor
+  float* Tt = sm + 2 * NB * LDB;  // [3][SB][SB + 1]: per-wave temporaries
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  constexpr int PER = NB * NB / 256;
+  if (nb == NB) {
+    float v[PER];
+#pragma unroll
+    for (int q = 0; q < PER; ++q) {
+      const int e = tid + q * 256, r = e / NB, c = e % NB;
+      v[q] = A[(k0 + r) * d + k0 + c];
+    }
+#pragma unroll
+    for (int q = 0; q < PER; ++q) {
+      const int e = tid + q * 256, r = e / NB, c = e % NB;
+      La[r * LDB + c] = (c <= r) ? v[q] : 0.0f;
+      Xa[r * LDB + c] = 0.0f;
+    }
+  } else {
+    for (int q = 0; q < PER; ++q) {
+      const int e = tid + q * 256, r = e / NB, c = e % NB;
+      float x = (r == c) ? 1.0f : 0.0f;
+      if (r < nb && c <= r) x = A[(k0 + r) * d + k0 + c];
+      La[r * LDB + c] = (c <= r) ? x : 0.0f;
+      Xa[r * LDB + c] = 0.0f;
+    }
   }
   __syncthreads();
-  // Right-looking Cholesky. Column j is read unscaled in step j (products divided by the pivot)
-  // and scaled in step j + 1, so each step needs two barriers.
-  for (int j = 0; j < nb; ++j) {
-    if (tid == 0) {
-      float p = L[j * NBP + j];
-      if (!(p > 0.0f)) {
-        if (*info == 0) *info = k0 + j + 1;
-        p = 1.0f;
+
+  constexpr int NS = NB / SB;
+  for (int p = 0; p < NS; ++p) {
+    float* Dpp = La + (SB * p) * LDB + SB * p;
+    float* Xpp = Xa + (SB * p) * LDB + SB * p;
+    if (wave == 0) chol_inv32(Dpp, Xpp, lane, info, k0 + SB * p, nb - SB * p);
+    __syncthreads();
+    // sub-panel solve: L_qp = A_qp X_pp^T for q > p (one wave per tile)
+    {
+      const int q = p + 1 + wave;
+      if (q < NS) {
+        float* Aqp = La + (SB * q) * LDB + SB * p;
+        floatx16 acc = mma32<false, true>(zero16(), Aqp, LDB, Xpp, LDB, SB, lane);
+        tile_store(Aqp, LDB, lane, acc);
       }
-      piv = p;
-      dia[j] = sqrtf(p);
     }
     __syncthreads();
-    const float inv_p = 1.0f / piv;
-    if (j > 0) {
-      const float dprev = dia[j - 1];
-      for (int i = j + tid; i < nb; i += 256) L[i * NBP + (j - 1)] /= dprev;
-    }
-    // trailing update: L[i][c] -= L[i][j] L[c][j] / p for j < c <= i
-    const int m = nb - j - 1;
-    const int cnt = m * (m + 1) / 2;
-    for (int e = tid; e < cnt; e += 256) {
-      int ii = (int)((sqrtf(8.0f * e + 1.0f) - 1.0f) * 0.5f);
-      while ((ii + 1) * (ii + 2) / 2 <= e) ++ii;
-      while (ii * (ii + 1) / 2 > e) --ii;
-      const int cc = e - ii * (ii + 1) / 2;
-      const int i = j + 1 + ii, c = j + 1 + cc;
-      L[i * NBP + c] -= L[i * NBP + j] * L[c * NBP + j] * inv_p;
+    // symmetric update: A_qr -= L_qp L_rp^T for p < r <= q
+    {
+      int t = 0;
+      for (int q = p + 1; q < NS; ++q)
+        for (int r = p + 1; r <= q; ++r, ++t) {
+          if (t % 4 != wave) continue;
+          float* Aqr = La + (SB * q) * LDB + SB * r;
+          floatx16 acc = tile_load(Aqr, LDB, lane);
+          acc = mma32<false, true>(acc, La + (SB * q) * LDB + SB * p, LDB, La + (SB * r) * LDB + SB * p, LDB, SB,
+                                   lane, -1.0f);
+          tile_store(Aqr, LDB, lane, acc);
+        }
     }
     __syncthreads();
   }
-  for (int j = tid; j < nb; j += 256) L[j * NBP + j] = dia[j];
-  __syncthreads();
-  // Inverse of L by forward elimination on [L | I], right-looking: when row j is reached it holds
-  // e_j - sum_{t<j} L[j][t] X[t]; dividing by L[j][j] finishes it (done one step late, like above).
-  for (int j = 0; j < nb; ++j) {
-    const float inv_l = 1.0f / L[j * NBP + j];
-    if (j > 0) {
-      const float inv_prev = 1.0f / L[(j - 1) * NBP + (j - 1)];
-      for (int c = tid; c <= j - 1; c += 256) X[(j - 1) * NBP + c] *= inv_prev;
-    }
-    const int rows_below = nb - j - 1, cols = j + 1;
-    for (int e = tid; e < rows_below * cols; e += 256) {
-      const int i = j + 1 + e / cols, c = e % cols;
-      X[i * NBP + c] -= L[i * NBP + j] * X[j * NBP + c] * inv_l;
+  // off-diagonal blocks of the inverse, block row by block row
+  for (int q = 1; q < NS; ++q) {
+    const int pb = wave;
+    if (pb < q) {
+      floatx16 acc = zero16();
+      for (int t = pb; t < q; ++t)
+        acc = mma32<false, false>(acc, La + (SB * q) * LDB + SB * t, LDB, Xa + (SB * t) * LDB + SB * pb, LDB, SB,
+                                  lane);
+      float* T = Tt + pb * SB * (SB + 1);
+      tile_store(T, SB + 1, lane, acc);
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+      __builtin_amdgcn_wave_barrier();
+      acc = mma32<false, false>(zero16(), Xa + (SB * q) * LDB + SB * q, LDB, T, SB + 1, SB, lane);
+      tile_store(Xa + (SB * q) * LDB + SB * pb, LDB, lane, acc, -1.0f);
     }
     __syncthreads();
   }
-  if (nb > 0) {
-    const float inv_last = 1.0f / L[(nb - 1) * NBP + (nb - 1)];
-    for (int c = tid; c < nb; c += 256) X[(nb - 1) * NBP + c] *= inv_last;
-  }
-  __syncthreads();
-  for (int e = tid; e < NB * NB; e += 256) {
-    const int r = e / NB, c = e % NB;
-    if (r < nb && c < nb) A[(k0 + r) * d + k0 + c] = (c <= r) ? X[r * NBP + c] : 0.0f;
+  if (nb == NB) {
+#pragma unroll
+    for (int q = 0; q < PER; ++q) {
+      const int e = tid + q * 256, r = e / NB, c = e % NB;
+      A[(k0 + r) * d + k0 + c] = (c <= r) ? Xa[r * LDB + c] : 0.0f;
+    }
+  } else {
+    for (int q = 0; q < PER; ++q) {
+      const int e = tid + q * 256, r = e / NB, c = e % NB;
+      if (r < nb && c < nb) A[(k0 + r) * d + k0 + c] = (c <= r) ? Xa[r * LDB + c] : 0.0f;
+    }
   }
 }
 
@@ -197,7 +312,7 @@ __global__ __launch_bounds__(256) void flip_kernel(float* __restrict__ A, int64_
   }
 }
 
-size_t chol_smem() { return (size_t)2 * NB * NBP * sizeof(float); }
+size_t chol_smem() { return ((size_t)2 * NB * LDB + 3 * SB * (SB + 1)) * sizeof(float); }
 
 }  // namespace
 

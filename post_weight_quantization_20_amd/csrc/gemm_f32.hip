@@ -4,101 +4,145 @@
 // loop (GPTQ tools page, "How it works", Step 7), the panel solves, symmetric rank-k updates and
 // triangular-inverse products of the factor (Step 6), and the Hessian of fp32 activations (Step 3).
 //
-// Tiling: a 256-thread workgroup (4 wave64s in a 2x2 grid) owns a 128x128 tile of C; each wave
-// owns 64x64 = 2x2 MFMA blocks of 32x32 held in 64 accumulator registers per lane. The reduction
-// dimension is staged through LDS 16 at a time, k-major (As[k][m], Bs[k][n]), double buffered,
-// with the next stage's global loads in flight while the current stage feeds the MFMAs.
+// A 256-thread workgroup (4 wave64s in a 2x2 grid) owns a T x T tile of C (T = 128: each wave holds
+// 2x2 MFMA blocks of 32x32; T = 64: one block per wave). The reduction dimension is staged through LDS
+// 32 at a time, double buffered, with the next stage's global loads in flight while the current
+// stage feeds the MFMAs. An operand whose reduction index is contiguous in memory is kept
+// row-major in LDS ([row][k]) and read with one 16-byte load per lane for four MFMAs, the lane's two
+// k-halves taking k = 4h..4h+3 in turn; the other kind is kept k-major ([k][row]) and read 4 bytes
+// per MFMA. Lower- or upper-triangle products launch only the tiles that touch the triangle.
 #include "common.hpp"
+
+#include <cmath>
 
 namespace gptq {
 namespace {
 
-constexpr int GT = 128;   // tile rows / cols
-constexpr int GK = 16;    // k per LDS stage
-constexpr int GP = 4;     // LDS row padding (floats)
+constexpr int GK = 32;   // k per LDS stage
 
-// One operand tile stage: logical element (k, r) for k in [0, GK), r in [0, GT).
-// KCONTIG: the stored matrix has k contiguous (element at P[r * ld + k]); otherwise r is
-// contiguous (element at P[k * ld + r]). Each of the 256 threads moves two float4.
-template <bool KCONTIG>
-struct TileLoader {
-  float4 v[2];
+template <int T, bool KC>
+struct Stage {
+  // LDS footprint of one operand stage, in floats
+  static constexpr int ROWLEN = KC ? GK + 4 : T + 4;
+  static constexpr int ROWS = KC ? T : GK;
+  static constexpr int SIZE = ROWS * ROWLEN;
+  static constexpr int NV = T * GK / 4 / 256;  // float4 per thread per stage
+};
+
+// Global -> registers -> LDS for one operand stage: logical element (k, r), k in [0, GK), r in [0, T).
+// KC: stored matrix has k contiguous (P[r * ld + k]); otherwise r contiguous (P[k * ld + r]).
+template <int T, bool KC>
+struct Loader {
+  using S = Stage<T, KC>;
+  float4 v[S::NV];
+
+  GPTQ_DEV static void coord(int idx, int& r, int& k) {
+    if (KC) { r = idx / (GK / 4); k = (idx % (GK / 4)) * 4; }
+    else    { k = idx / (T / 4);  r = (idx % (T / 4)) * 4; }
+  }
 
   GPTQ_DEV void load(const float* __restrict__ P, int64_t ld, int64_t r0, int64_t R, int64_t k0, int64_t K,
                      bool vec, int tid) {
+    if (vec && r0 + T <= R && k0 + GK <= K) {
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      int idx = tid + i * 256;
-      int64_t r, k;
-      if (KCONTIG) { r = r0 + (idx >> 2); k = k0 + ((idx & 3) << 2); }
-      else         { k = k0 + (idx >> 5); r = r0 + ((idx & 31) << 2); }
+      for (int i = 0; i < S::NV; ++i) {
+        int r, k;
+        coord(tid + i * 256, r, k);
+        v[i] = KC ? *reinterpret_cast<const float4*>(P + (r0 + r) * ld + k0 + k)
+                  : *reinterpret_cast<const float4*>(P + (k0 + k) * ld + r0 + r);
+      }
+      return;
+    }
+#pragma unroll
+    for (int i = 0; i < S::NV; ++i) {
+      int r, k;
+      coord(tid + i * 256, r, k);
       float t[4];
-      if (KCONTIG) {
-        const float* p = P + r * ld + k;
-        if (vec && r < R && k + 3 < K) {
-          float4 q = *reinterpret_cast<const float4*>(p);
-          t[0] = q.x; t[1] = q.y; t[2] = q.z; t[3] = q.w;
-        } else {
 #pragma unroll
-          for (int e = 0; e < 4; ++e) t[e] = (r < R && k + e < K) ? p[e] : 0.0f;
-        }
-      } else {
-        const float* p = P + k * ld + r;
-        if (vec && k < K && r + 3 < R) {
-          float4 q = *reinterpret_cast<const float4*>(p);
-          t[0] = q.x; t[1] = q.y; t[2] = q.z; t[3] = q.w;
-        } else {
-#pragma unroll
-          for (int e = 0; e < 4; ++e) t[e] = (k < K && r + e < R) ? p[e] : 0.0f;
-        }
+      for (int e = 0; e < 4; ++e) {
+        const int64_t rr = r0 + r + (KC ? 0 : e), kk = k0 + k + (KC ? e : 0);
+        t[e] = (rr < R && kk < K) ? (KC ? P[rr * ld + kk] : P[kk * ld + rr]) : 0.0f;
       }
       v[i] = make_float4(t[0], t[1], t[2], t[3]);
     }
   }
 
-  GPTQ_DEV void store(float (*S)[GT + GP], int tid) const {
+  GPTQ_DEV void store(float* Sm, int tid) const {
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      int idx = tid + i * 256;
-      if (KCONTIG) {
-        int r = idx >> 2, k = (idx & 3) << 2;
-        S[k + 0][r] = v[i].x; S[k + 1][r] = v[i].y; S[k + 2][r] = v[i].z; S[k + 3][r] = v[i].w;
-      } else {
-        int k = idx >> 5, r = (idx & 31) << 2;
-        *reinterpret_cast<float4*>(&S[k][r]) = v[i];
-      }
+    for (int i = 0; i < S::NV; ++i) {
+      int r, k;
+      coord(tid + i * 256, r, k);
+      if (KC) *reinterpret_cast<float4*>(Sm + r * S::ROWLEN + k) = v[i];
+      else    *reinterpret_cast<float4*>(Sm + k * S::ROWLEN + r) = v[i];
     }
   }
 };
 
-template <bool AK, bool BK>
-__global__ __launch_bounds__(256) void gemm_f32_kernel(GemmArgs a, int64_t tiles_n, int vecA, int vecB) {
-  const int64_t tile = blockIdx.x;
-  const int64_t tm = tile / tiles_n, tn = tile % tiles_n;
-  const int64_t m0 = tm * GT, n0 = tn * GT;
-  if (a.tri == 1 && m0 + GT - 1 < n0) return;
-  if (a.tri == 2 && n0 + GT - 1 < m0) return;
+// Operand values for four consecutive MFMAs (k = 4h + e of the current group of 8) of the block
+// whose rows start at `row`.
+template <int T, bool KC>
+GPTQ_DEV float4 operand4(const float* Sm, int row, int kg, int lane) {
+  using S = Stage<T, KC>;
+  const int li = lane & 31, h = lane >> 5;
+  if (KC) return *reinterpret_cast<const float4*>(Sm + (row + li) * S::ROWLEN + kg + 4 * h);
+  return make_float4(Sm[(kg + 4 * h + 0) * S::ROWLEN + row + li], Sm[(kg + 4 * h + 1) * S::ROWLEN + row + li],
+                     Sm[(kg + 4 * h + 2) * S::ROWLEN + row + li], Sm[(kg + 4 * h + 3) * S::ROWLEN + row + li]);
+}
 
-  __shared__ float As[2][GK][GT + GP];
-  __shared__ float Bs[2][GK][GT + GP];
+GPTQ_DEV float f4(const float4& v, int e) { return e == 0 ? v.x : e == 1 ? v.y : e == 2 ? v.z : v.w; }
+
+// Tile t of a triangle of n x n tiles in row order: lower (tn <= tm) or upper (tn >= tm).
+GPTQ_DEV void tri_tile(int64_t t, int64_t n, bool lower, int64_t& tm, int64_t& tn) {
+  if (lower) {
+    int64_t r = (int64_t)((sqrt(8.0 * (double)t + 1.0) - 1.0) * 0.5);
+    while ((r + 1) * (r + 2) / 2 <= t) ++r;
+    while (r * (r + 1) / 2 > t) --r;
+    tm = r;
+    tn = t - r * (r + 1) / 2;
+  } else {
+    // row r holds tiles (r, r..n-1): offset(r) = r n - r (r - 1) / 2
+    int64_t r = 0, off = 0;
+    // invert offset(r) <= t with a square root, then correct
+    const double nn = (double)n + 0.5;
+    r = (int64_t)(nn - sqrt(nn * nn - 2.0 * (double)t));
+    if (r < 0) r = 0;
+    while (r > 0 && r * n - r * (r - 1) / 2 > t) --r;
+    while ((r + 1) * n - (r + 1) * r / 2 <= t) ++r;
+    off = r * n - r * (r - 1) / 2;
+    tm = r;
+    tn = r + (t - off);
+  }
+}
+
+template <int T, bool AK, bool BK>
+__global__ __launch_bounds__(256) void gemm_f32_kernel(GemmArgs a, int64_t tiles_n, int vecA, int vecB) {
+  constexpr int WB = T / 64;  // 32x32 blocks per wave per dimension
+  int64_t tm, tn;
+  if (a.tri == 0) { tm = blockIdx.x / tiles_n; tn = blockIdx.x % tiles_n; }
+  else tri_tile(blockIdx.x, tiles_n, a.tri == 1, tm, tn);
+  const int64_t m0 = tm * T, n0 = tn * T;
+
+  using SA = Stage<T, AK>;
+  using SB = Stage<T, BK>;
+  __shared__ __align__(16) float As[2][SA::SIZE];
+  __shared__ __align__(16) float Bs[2][SB::SIZE];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
   const int wm = wave >> 1, wn = wave & 1;
   const int li = lane & 31, lk = lane >> 5;
 
-  floatx16 acc[2][2];
+  floatx16 acc[WB][WB];
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+  for (int i = 0; i < WB; ++i)
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
+    for (int j = 0; j < WB; ++j)
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
 
-  TileLoader<AK> la;  // op(A) tile: rows m, reduction k
-  TileLoader<BK> lb;  // op(B) tile: cols n, reduction k
+  Loader<T, AK> la;
+  Loader<T, BK> lb;
   const int64_t nk = (a.K + GK - 1) / GK;
-
   if (nk > 0) {
     la.load(a.A, a.lda, m0, a.M, 0, a.K, vecA, tid);
     lb.load(a.B, a.ldb, n0, a.N, 0, a.K, vecB, tid);
@@ -115,17 +159,19 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmArgs a, int64_t tiles
       lb.load(a.B, a.ldb, n0, a.N, (kt + 1) * GK, a.K, vecB, tid);
     }
 #pragma unroll
-    for (int ks = 0; ks < GK; ks += 2) {
-      float av[2], bv[2];
+    for (int kg = 0; kg < GK; kg += 8) {
+      float4 av[WB], bv[WB];
 #pragma unroll
-      for (int i = 0; i < 2; ++i) av[i] = As[cur][ks + lk][wm * 64 + i * 32 + li];
+      for (int i = 0; i < WB; ++i) av[i] = operand4<T, AK>(As[cur], wm * (T / 2) + i * 32, kg, lane);
 #pragma unroll
-      for (int j = 0; j < 2; ++j) bv[j] = Bs[cur][ks + lk][wn * 64 + j * 32 + li];
+      for (int j = 0; j < WB; ++j) bv[j] = operand4<T, BK>(Bs[cur], wn * (T / 2) + j * 32, kg, lane);
 #pragma unroll
-      for (int i = 0; i < 2; ++i)
+      for (int e = 0; e < 4; ++e)
 #pragma unroll
-        for (int j = 0; j < 2; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(av[i], bv[j], acc[i][j], 0, 0, 0);
+        for (int i = 0; i < WB; ++i)
+#pragma unroll
+          for (int j = 0; j < WB; ++j)
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(f4(av[i], e), f4(bv[j], e), acc[i][j], 0, 0, 0);
     }
     if (more) {
       la.store(As[cur ^ 1], tid);
@@ -136,14 +182,40 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmArgs a, int64_t tiles
 
   // Epilogue. Accumulator register r of lane l holds row 8*(r/4) + 4*(l/32) + r%4, column l%32
   // of its 32x32 block.
+  const bool full = m0 + T <= a.M && n0 + T <= a.N;
+  if (full) {
+    // tile inside C, one 32x32 block at a time: its reads of C, then its writes (on a triangle's
+    // diagonal tile, only the elements inside the triangle are written)
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+    for (int i = 0; i < WB; ++i)
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
+      for (int j = 0; j < WB; ++j) {
+        float* cb = a.C + (m0 + wm * (T / 2) + i * 32 + 4 * lk) * a.ldc + n0 + wn * (T / 2) + j * 32 + li;
+        float cv[16];
+        if (a.beta != 0.0f) {
+#pragma unroll
+          for (int r = 0; r < 16; ++r) cv[r] = cb[(8 * (r >> 2) + (r & 3)) * a.ldc];
+        }
+        const int64_t mb = m0 + wm * (T / 2) + i * 32 + 4 * lk, nb = n0 + wn * (T / 2) + j * 32 + li;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          float v = a.alpha * acc[i][j][r];
+          if (a.beta != 0.0f) v = __builtin_fmaf(a.beta, cv[r], v);
+          const int64_t m = mb + 8 * (r >> 2) + (r & 3);
+          const bool keep = a.tri == 0 || (a.tri == 1 ? m >= nb : m <= nb);
+          if (keep) cb[(8 * (r >> 2) + (r & 3)) * a.ldc] = v;
+        }
+      }
+    return;
+  }
+#pragma unroll
+  for (int i = 0; i < WB; ++i)
+#pragma unroll
+    for (int j = 0; j < WB; ++j)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const int64_t m = m0 + wm * 64 + i * 32 + 8 * (r >> 2) + 4 * lk + (r & 3);
-        const int64_t n = n0 + wn * 64 + j * 32 + li;
+        const int64_t m = m0 + wm * (T / 2) + i * 32 + 8 * (r >> 2) + 4 * lk + (r & 3);
+        const int64_t n = n0 + wn * (T / 2) + j * 32 + li;
         if (m >= a.M || n >= a.N) continue;
         if (a.tri == 1 && m < n) continue;
         if (a.tri == 2 && m > n) continue;
@@ -156,23 +228,39 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmArgs a, int64_t tiles
 
 bool aligned16(const void* p, int64_t ld) { return ((uintptr_t)p % 16 == 0) && (ld % 4 == 0); }
 
+template <int T>
+hipError_t launch(const GemmArgs& a, hipStream_t s) {
+  const int64_t tiles_m = (a.M + T - 1) / T, tiles_n = (a.N + T - 1) / T;
+  int64_t tiles = tiles_m * tiles_n;
+  int64_t tn_arg = tiles_n;
+  if (a.tri != 0) {
+    // square triangle of tiles (M == N for the symmetric products)
+    tiles = tiles_n * (tiles_n + 1) / 2;
+  }
+  const dim3 grid((unsigned)tiles);
+  // op(A) has k contiguous when A is not transposed; op(B) has k contiguous when B is transposed.
+  const int vecA = aligned16(a.A, a.lda), vecB = aligned16(a.B, a.ldb);
+  if (!a.transA && !a.transB)
+    hipLaunchKernelGGL((gemm_f32_kernel<T, true, false>), grid, dim3(256), 0, s, a, tn_arg, vecA, vecB);
+  else if (!a.transA && a.transB)
+    hipLaunchKernelGGL((gemm_f32_kernel<T, true, true>), grid, dim3(256), 0, s, a, tn_arg, vecA, vecB);
+  else if (a.transA && !a.transB)
+    hipLaunchKernelGGL((gemm_f32_kernel<T, false, false>), grid, dim3(256), 0, s, a, tn_arg, vecA, vecB);
+  else
+    hipLaunchKernelGGL((gemm_f32_kernel<T, false, true>), grid, dim3(256), 0, s, a, tn_arg, vecA, vecB);
+  return hipGetLastError();
+}
+
 }  // namespace
 
 hipError_t gemm_f32(const GemmArgs& a, hipStream_t s) {
   if (a.M <= 0 || a.N <= 0) return hipSuccess;
-  const int64_t tiles_m = (a.M + GT - 1) / GT, tiles_n = (a.N + GT - 1) / GT;
-  const dim3 grid((unsigned)(tiles_m * tiles_n));
-  // op(A) has k contiguous when A is not transposed; op(B) has k contiguous when B is transposed.
-  const int vecA = aligned16(a.A, a.lda), vecB = aligned16(a.B, a.ldb);
-  if (!a.transA && !a.transB)
-    hipLaunchKernelGGL((gemm_f32_kernel<true, false>), grid, dim3(256), 0, s, a, tiles_n, vecA, vecB);
-  else if (!a.transA && a.transB)
-    hipLaunchKernelGGL((gemm_f32_kernel<true, true>), grid, dim3(256), 0, s, a, tiles_n, vecA, vecB);
-  else if (a.transA && !a.transB)
-    hipLaunchKernelGGL((gemm_f32_kernel<false, false>), grid, dim3(256), 0, s, a, tiles_n, vecA, vecB);
-  else
-    hipLaunchKernelGGL((gemm_f32_kernel<false, true>), grid, dim3(256), 0, s, a, tiles_n, vecA, vecB);
-  return hipGetLastError();
+  if (a.tri != 0 && a.M != a.N) return hipErrorInvalidValue;
+  // Large products use 128 x 128 tiles; when those would leave most of the 256 CUs idle, 64 x 64
+  // tiles give four times as many workgroups, each a quarter of the work.
+  const int64_t t128 = ((a.M + 127) / 128) * ((a.N + 127) / 128) / (a.tri ? 2 : 1);
+  if (t128 < 256) return launch<64>(a, s);
+  return launch<128>(a, s);
 }
 
 }  // namespace gptq

@@ -67,9 +67,35 @@ __global__ __launch_bounds__(256) void quant_block_kernel(QArgs a) {
 
   const int tid = threadIdx.x;
   const int nc = a.ncols;
-  for (int e = tid; e < BP * BP; e += 256) {
-    const int k = e / BP, j = e % BP;
-    Us[e] = (j > k && j < nc) ? a.U[(a.b + k) * a.d + a.b + j] : 0.0f;
+  bool filled = false;
+  if constexpr (CPL >= 4) {
+   if (nc == BP && a.d % 4 == 0 && a.b % 4 == 0) {
+    // full block: unconditional 16-byte loads, all in flight together
+    filled = true;
+    constexpr int Q = BP / 4;  // float4 per row
+    float4 v[BP * Q / 256];
+#pragma unroll
+    for (int i = 0; i < BP * Q / 256; ++i) {
+      const int e = tid + i * 256, k = e / Q, j = (e % Q) * 4;
+      v[i] = *reinterpret_cast<const float4*>(a.U + (a.b + k) * a.d + a.b + j);
+    }
+#pragma unroll
+    for (int i = 0; i < BP * Q / 256; ++i) {
+      const int e = tid + i * 256, k = e / Q, j = (e % Q) * 4;
+      float4 u = v[i];
+      u.x = (j + 0 > k) ? u.x : 0.0f;
+      u.y = (j + 1 > k) ? u.y : 0.0f;
+      u.z = (j + 2 > k) ? u.z : 0.0f;
+      u.w = (j + 3 > k) ? u.w : 0.0f;
+      *reinterpret_cast<float4*>(Us + k * BP + j) = u;
+    }
+   }
+  }
+  if (!filled) {
+    for (int e = tid; e < BP * BP; e += 256) {
+      const int k = e / BP, j = e % BP;
+      Us[e] = (j > k && j < nc) ? a.U[(a.b + k) * a.d + a.b + j] : 0.0f;
+    }
   }
   for (int k = tid; k < BP; k += 256) invd[k] = (k < nc) ? 1.0f / a.U[(a.b + k) * a.d + a.b + k] : 0.0f;
   __syncthreads();
