@@ -41,6 +41,8 @@ def parse():
     ap.add_argument("--workload", default="q_proj", choices=["q_proj", "down_proj", "fc2", "tiny"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample-seconds", type=float, default=20.0)
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also run one plain 1 GiB device-to-device copy (a known-size reference for HBM counters)")
     return ap.parse_args()
 
 
@@ -232,6 +234,14 @@ def main():
         "weights_per_s": round(rows * d / sec_layer, 1),
         "roofline": roof,
     }
+    if args.copy_calibration:
+        src = torch.empty(1 << 28, dtype=torch.float32, device=dev).fill_(1.0)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        out["copy_calibration_bytes"] = {"read": src.numel() * 4, "write": dst.numel() * 4}
+        del src, dst
     if not args.no_cpu_baseline:
         print("[bench] timing the float64 oracle on a bounded sample", file=sys.stderr, flush=True)
         out["cpu_baseline"] = cpu_baseline(case, args.cpu_sample_seconds)

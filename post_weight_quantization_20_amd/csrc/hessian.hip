@@ -7,10 +7,11 @@
 // X arrives token-major ([tokens x d], features contiguous) and the product contracts over tokens,
 // so both MFMA operands need 8 consecutive tokens of one feature per lane. Each thread loads an
 // 8-token x 8-feature block with eight 16-byte loads, transposes it in registers and stores eight
-// 16-byte rows into a feature-major LDS tile. A 512-thread workgroup (8 wave64s, 4x2) owns a
-// 256x256 tile of H in the upper triangle; each wave owns 64x128 (2x4 blocks of
-// v_mfma_f32_32x32x16_{f16,bf16}, 128 accumulators per lane). Products of fp16/bf16 values are
-// exact in fp32; accumulation is fp32.
+// 16-byte rows into a feature-major LDS tile (double buffered: the next stage's stores overlap the
+// current stage's MFMAs, one barrier per stage). A 256-thread workgroup (4 wave64s, 2x2) owns a
+// 256x256 tile of H in the upper triangle; each wave owns 128x128 (4x4 blocks of
+// v_mfma_f32_32x32x16_{f16,bf16}, 256 accumulators per lane), which needs half the LDS reads per
+// MFMA of a 64x128 wave tile. Products of fp16/bf16 values are exact in fp32; accumulation is fp32.
 //
 // When the upper-triangle tiles alone cannot fill the 256 CUs, the token range is split S ways.
 // Each split writes its partial tile to the workspace, and the last split to finish a tile (an
@@ -34,23 +35,47 @@ struct HessArgs {
   const uint16_t* X;   // fp16 or bf16 bit patterns
   int64_t n, ldx;
   int T;               // tiles per dimension
-  int S;               // token splits
+  int ntiles;          // T (T + 1) / 2
+  int S;               // token splits: 1, or a multiple of 8 (split s runs on XCD s % 8)
+  int per_xcd;         // S == 1: tiles per XCD (contiguous in the tile order)
   int64_t split_len;   // tokens per split (multiple of HK)
   float* partial;      // [ntiles * S][HT * HT] when S > 1
   int* counters;       // [ntiles] when S > 1
   int vec;             // 16-byte loads allowed
 };
 
-GPTQ_DEV void tile_of(int t, int T, int& ti, int& tj) {
-  // upper-triangle tile pairs in row order: row ti holds tiles (ti, ti..T-1)
-  int r = 0, off = 0;
-  while (off + (T - r) <= t) { off += T - r; ++r; }
-  ti = r;
-  tj = r + (t - off);
+// Upper-triangle tile pairs (ti <= tj) in an order that keeps neighbours close: super-blocks of
+// G x G tiles in row order of the upper triangle of super-blocks, row order inside each. Workgroups
+// that run together on one XCD take consecutive slots, so they share few feature blocks of X and
+// reuse them from that XCD's L2.
+constexpr int G = 8;
+
+GPTQ_DEV void tile_at(int slot, int T, int& ti, int& tj) {
+  const int NSB = (T + G - 1) / G;
+  for (int R = 0; R < NSB; ++R) {
+    const int r0 = R * G, r1 = min(T, r0 + G);
+    for (int C = R; C < NSB; ++C) {
+      const int c0 = C * G, c1 = min(T, c0 + G);
+      for (int r = r0; r < r1; ++r) {
+        const int cs = max(c0, r);
+        const int cnt = max(0, c1 - cs);
+        if (slot < cnt) { ti = r; tj = cs + slot; return; }
+        slot -= cnt;
+      }
+    }
+  }
+  ti = tj = 0;
 }
 
 // Loads an 8-token x 8-feature block starting at (tok, f) into 8 registers of 8 halves.
 GPTQ_DEV void load_block(const HessArgs& a, int64_t tok, int64_t tok_end, int64_t f, u32x4 (&r)[8]) {
+  if (a.vec && tok + 8 <= tok_end && f + 8 <= a.d) {
+    // whole block in range: eight unconditional 16-byte loads in flight together
+    const uint16_t* p = a.X + tok * a.ldx + f;
+#pragma unroll
+    for (int t = 0; t < 8; ++t) r[t] = *reinterpret_cast<const u32x4*>(p + t * a.ldx);
+    return;
+  }
 #pragma unroll
   for (int t = 0; t < 8; ++t) {
     const int64_t tt = tok + t;
@@ -92,14 +117,25 @@ GPTQ_DEV floatx16 mfma16<bf16x8>(bf16x8 a, bf16x8 b, floatx16 c) {
 }
 
 template <typename V>
-__global__ __launch_bounds__(512) void hess_kernel(HessArgs a) {
+__global__ __launch_bounds__(256) void hess_kernel(HessArgs a) {
   extern __shared__ __align__(16) uint16_t smem[];
-  uint16_t* Xa = smem;
-  uint16_t* Xb = smem + HT * HROW;
+  constexpr int TILE = HT * HROW;   // halves per operand tile
+  // buffers: [stage][operand] -> smem + (2 * stage + operand) * TILE
 
-  const int tile = blockIdx.x / a.S, split = blockIdx.x % a.S;
+  // Workgroup b runs on XCD b % 8. With token splits, XCD x takes splits x, x + 8, ... and walks
+  // every tile for each; without, it takes a contiguous run of tiles over all tokens.
+  const int xcd = blockIdx.x % 8, slot = blockIdx.x / 8;
+  int tile, split;
+  if (a.S > 1) {
+    tile = slot % a.ntiles;
+    split = xcd + 8 * (slot / a.ntiles);
+  } else {
+    tile = xcd * a.per_xcd + slot;
+    split = 0;
+    if (slot >= a.per_xcd || tile >= a.ntiles) return;
+  }
   int ti, tj;
-  tile_of(tile, a.T, ti, tj);
+  tile_at(tile, a.T, ti, tj);
   const bool diag = ti == tj;
   const int64_t fa = (int64_t)ti * HT, fb = (int64_t)tj * HT;
   const int64_t t_begin = (int64_t)split * a.split_len;
@@ -109,58 +145,80 @@ __global__ __launch_bounds__(512) void hess_kernel(HessArgs a) {
   const int wm = wave >> 1, wn = wave & 1;
   const int li = lane & 31, lk = lane >> 5;
 
-  // loader role: threads 0..255 fill Xa, 256..511 fill Xb (idle on diagonal tiles)
-  const bool loadB = tid >= 256;
-  const int bi = tid & 255;
-  // 8 consecutive lanes take 8 token blocks of one feature block: 128-byte global segments and
-  // conflict-free 16-byte LDS row stores
-  const int fl = (bi >> 3) * 8, tl = (bi & 7) * 8;
-  const int64_t fsrc = (loadB ? fb : fa) + fl;
-  const bool loader = !(loadB && diag);
-  uint16_t* dst = loadB ? Xb : Xa;
-  const uint16_t* Bt = diag ? Xa : Xb;
+  // loader: each thread moves one 8-token x 8-feature block of each operand per stage; 8
+  // consecutive lanes take 8 token blocks of one feature block (128-byte global segments,
+  // conflict-free 16-byte LDS row stores)
+  const int fl = (tid >> 3) * 8, tl = (tid & 7) * 8;
 
-  floatx16 acc[2][4];
+  floatx16 acc[4][4];
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+  for (int i = 0; i < 4; ++i)
 #pragma unroll
     for (int j = 0; j < 4; ++j)
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
 
-  u32x4 rb[8];
+  u32x4 ra[8], rb[8];
   int64_t t0 = t_begin;
-  if (loader && t0 < t_end) load_block(a, t0 + tl, t_end, fsrc, rb);
+  int buf = 0;
+  if (t0 < t_end) {
+    load_block(a, t0 + tl, t_end, fa + fl, ra);
+    if (!diag) load_block(a, t0 + tl, t_end, fb + fl, rb);
+    store_block(smem, fl, tl, ra);
+    if (!diag) store_block(smem + TILE, fl, tl, rb);
+  }
+  __syncthreads();
   for (; t0 < t_end; t0 += HK) {
-    if (loader) store_block(dst, fl, tl, rb);
-    __syncthreads();
-    if (loader && t0 + HK < t_end) load_block(a, t0 + HK + tl, t_end, fsrc, rb);
+    const bool more = t0 + HK < t_end;
+    if (more) {
+      load_block(a, t0 + HK + tl, t_end, fa + fl, ra);
+      if (!diag) load_block(a, t0 + HK + tl, t_end, fb + fl, rb);
+    }
+    const uint16_t* Xa = smem + (2 * buf) * TILE;
+    const uint16_t* Xb = diag ? Xa : Xa + TILE;
+    // operands of the next 16 tokens are read from LDS while the MFMAs of the current 16 run
+    V av[2][4], bv[2][4];
 #pragma unroll
-    for (int ks = 0; ks < HK; ks += 16) {
-      V av[2], bv[4];
+    for (int i = 0; i < 4; ++i) {
+      av[0][i] = *reinterpret_cast<const V*>(Xa + (wm * 128 + i * 32 + li) * HROW + 8 * lk);
+      bv[0][i] = *reinterpret_cast<const V*>(Xb + (wn * 128 + i * 32 + li) * HROW + 8 * lk);
+    }
 #pragma unroll
-      for (int i = 0; i < 2; ++i)
-        av[i] = *reinterpret_cast<const V*>(Xa + (wm * 64 + i * 32 + li) * HROW + ks + 8 * lk);
+    for (int s4 = 0; s4 < HK / 16; ++s4) {
+      const int c = s4 & 1, n = c ^ 1;
+      if (s4 + 1 < HK / 16) {
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
-        bv[j] = *reinterpret_cast<const V*>(Bt + (wn * 128 + j * 32 + li) * HROW + ks + 8 * lk);
+        for (int i = 0; i < 4; ++i) {
+          av[n][i] = *reinterpret_cast<const V*>(Xa + (wm * 128 + i * 32 + li) * HROW + (s4 + 1) * 16 + 8 * lk);
+          bv[n][i] = *reinterpret_cast<const V*>(Xb + (wn * 128 + i * 32 + li) * HROW + (s4 + 1) * 16 + 8 * lk);
+        }
+      }
+      // keep the reads above ahead of this step's MFMAs (the scheduler would sink them)
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-      for (int i = 0; i < 2; ++i)
+      for (int i = 0; i < 4; ++i)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) acc[i][j] = mfma16<V>(av[i], bv[j], acc[i][j]);
+        for (int j = 0; j < 4; ++j) acc[i][j] = mfma16<V>(av[c][i], bv[c][j], acc[i][j]);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    if (more) {
+      uint16_t* nb = smem + (2 * (buf ^ 1)) * TILE;
+      store_block(nb, fl, tl, ra);
+      if (!diag) store_block(nb + TILE, fl, tl, rb);
     }
     __syncthreads();
+    buf ^= 1;
   }
 
   // Epilogue: accumulator register r of lane l holds row 8*(r/4) + 4*(l/32) + r%4, column l%32.
   if (a.S == 1) {
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
+    for (int i = 0; i < 4; ++i)
 #pragma unroll
       for (int j = 0; j < 4; ++j)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const int64_t m = fa + wm * 64 + i * 32 + 8 * (r >> 2) + 4 * lk + (r & 3);
+          const int64_t m = fa + wm * 128 + i * 32 + 8 * (r >> 2) + 4 * lk + (r & 3);
           const int64_t c = fb + wn * 128 + j * 32 + li;
           if (m < a.d && c < a.d) {
             float* h = a.H + m * a.d + c;
@@ -172,12 +230,12 @@ __global__ __launch_bounds__(512) void hess_kernel(HessArgs a) {
 
   float* part = a.partial + ((int64_t)tile * a.S + split) * (HT * HT);
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+  for (int i = 0; i < 4; ++i)
 #pragma unroll
     for (int j = 0; j < 4; ++j)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const int m = wm * 64 + i * 32 + 8 * (r >> 2) + 4 * lk + (r & 3);
+        const int m = wm * 128 + i * 32 + 8 * (r >> 2) + 4 * lk + (r & 3);
         const int c = wn * 128 + j * 32 + li;
         part[m * HT + c] = acc[i][j][r];
       }
@@ -192,7 +250,7 @@ __global__ __launch_bounds__(512) void hess_kernel(HessArgs a) {
   if (!last) return;
   __threadfence();
   const float* base = a.partial + (int64_t)tile * a.S * (HT * HT);
-  for (int e = tid * 4; e < HT * HT; e += 512 * 4) {
+  for (int e = tid * 4; e < HT * HT; e += 256 * 4) {
     floatx4 s = *reinterpret_cast<const floatx4*>(base + e);
     for (int q = 1; q < a.S; ++q) s += *reinterpret_cast<const floatx4*>(base + (int64_t)q * HT * HT + e);
     const int m = e / HT, c = e % HT;
@@ -213,21 +271,20 @@ __global__ void zero_ints(int* p, int n) {
   if (i < n) p[i] = 0;
 }
 
+// Token splits: none when the tiles alone give every CU several workgroups; otherwise 8 (one per
+// XCD), or a larger multiple of 8 when the last round would be less than 80% full, as long as
+// each split keeps 16 stages.
 int choose_splits(int64_t ntiles, int64_t n) {
-  const int64_t max_s = std::max<int64_t>(1, std::min<int64_t>(32, n / (16 * HK)));
   if (ntiles >= 3 * NCU) return 1;
-  int best = 1;
-  double best_eff = 0.0;
-  for (int s = 1; s <= max_s; ++s) {
+  if (n < 8 * 16 * HK) return 1;
+  for (int s = 8; s <= 32 && n >= (int64_t)s * 16 * HK; s += 8) {
     const double w = (double)(ntiles * s) / NCU;
-    const double eff = w / std::ceil(w);
-    if (eff >= 0.9) return s;
-    if (eff > best_eff + 1e-9) { best_eff = eff; best = s; }
+    if (w / std::ceil(w) >= 0.8) return s;
   }
-  return best;
+  return 8;
 }
 
-size_t smem_bytes() { return (size_t)2 * HT * HROW * sizeof(uint16_t); }
+size_t smem_bytes() { return (size_t)4 * HT * HROW * sizeof(uint16_t); }
 
 }  // namespace
 
@@ -249,10 +306,13 @@ hipError_t hessian_f16(float* H, int64_t d, const void* X, int dtype, int64_t n,
   a.ldx = ldx;
   a.T = (int)((d + HT - 1) / HT);
   const int64_t ntiles = (int64_t)a.T * (a.T + 1) / 2;
+  a.ntiles = (int)ntiles;
   int S = choose_splits(ntiles, n);
   const size_t need = hessian_workspace_bytes(n, d);
   if (S > 1 && (work == nullptr || work_bytes < need)) S = 1;  // correct, fewer workgroups
   a.S = S;
+  a.per_xcd = (int)((ntiles + 7) / 8);
+  const int64_t grid = S > 1 ? ntiles * S : 8 * (int64_t)a.per_xcd;
   a.split_len = ((n + S - 1) / S + HK - 1) / HK * HK;
   a.vec = ((uintptr_t)X % 16 == 0) && (ldx % 8 == 0);
   if (S > 1) {
@@ -267,14 +327,14 @@ hipError_t hessian_f16(float* H, int64_t d, const void* X, int dtype, int64_t n,
       (void)hipFuncSetAttribute((const void*)hess_kernel<half8>, hipFuncAttributeMaxDynamicSharedMemorySize, (int)sm);
       attr_f16 = true;
     }
-    hipLaunchKernelGGL(hess_kernel<half8>, dim3((unsigned)(ntiles * S)), dim3(512), sm, s, a);
+    hipLaunchKernelGGL(hess_kernel<half8>, dim3((unsigned)grid), dim3(256), sm, s, a);
   } else {
     static bool attr_bf16 = false;
     if (!attr_bf16) {
       (void)hipFuncSetAttribute((const void*)hess_kernel<bf16x8>, hipFuncAttributeMaxDynamicSharedMemorySize, (int)sm);
       attr_bf16 = true;
     }
-    hipLaunchKernelGGL(hess_kernel<bf16x8>, dim3((unsigned)(ntiles * S)), dim3(512), sm, s, a);
+    hipLaunchKernelGGL(hess_kernel<bf16x8>, dim3((unsigned)grid), dim3(256), sm, s, a);
   }
   return hipGetLastError();
 }
