@@ -83,7 +83,8 @@ typedef struct {
  *   ld_x   row pitch of X in elements, >= d.
  *   work   device workspace of work_bytes bytes, or NULL. With at least
  *          gptq_workspace_bytes(GPTQ_WS_HESSIAN, n_tok, d, NULL) bytes the token range is split
- *          across more workgroups; with less (or NULL) the result is identical but may be slower.
+ *          across more workgroups (partial sums are added in token order); with less (or NULL) it
+ *          is not split, which sums in another order (same float32 error bound) and may be slower.
  *          The workspace must not be shared with a concurrent call.
  * fp16 / bf16 products are exact in fp32; sums are fp32. The result does not depend on scheduling.
  */

@@ -4,19 +4,24 @@
 // and is shared by every row of W (GPTQ tools page, "How it works", Step 3; the sketch forms
 // 2 X^T X / n, and the normalisation by n happens when the Hessian is damped).
 //
+// A 256-thread workgroup (4 wave64s, 2x2) owns a 256x256 tile of H in the upper triangle; each wave
+// owns 128x128 (4x4 blocks of v_mfma_f32_32x32x16_{f16,bf16}, 256 accumulators per lane). Products
+// of fp16/bf16 values are exact in fp32; accumulation is fp32.
+//
 // X arrives token-major ([tokens x d], features contiguous) and the product contracts over tokens,
-// so both MFMA operands need 8 consecutive tokens of one feature per lane. Each thread loads an
-// 8-token x 8-feature block with eight 16-byte loads, transposes it in registers and stores eight
-// 16-byte rows into a feature-major LDS tile (double buffered: the next stage's stores overlap the
-// current stage's MFMAs, one barrier per stage). A 256-thread workgroup (4 wave64s, 2x2) owns a
-// 256x256 tile of H in the upper triangle; each wave owns 128x128 (4x4 blocks of
-// v_mfma_f32_32x32x16_{f16,bf16}, 256 accumulators per lane), which needs half the LDS reads per
-// MFMA of a 64x128 wave tile. Products of fp16/bf16 values are exact in fp32; accumulation is fp32.
+// so each MFMA lane needs 8 consecutive tokens of one feature. The main path streams X straight
+// into LDS (buffer_load ... lds, 16 bytes a lane, no registers in between) through a ring of four
+// 32-token stages, keeping three stages in flight while the fourth is multiplied, and gives each
+// lane its tokens with the transposing LDS read ds_read_b64_tr_b16 (two reads of four tokens).
+// Rows of a stage are XOR-swizzled in 16-byte units so that the four token rows one transposing
+// read touches fall in distinct banks. Out-of-range tokens and features read as zero through the
+// buffer descriptor's range check. A register-staged path (8x8 transposes in registers, then LDS)
+// covers X that is not 16-byte aligned or whose width is not a multiple of 8.
 //
 // When the upper-triangle tiles alone cannot fill the 256 CUs, the token range is split S ways.
-// Each split writes its partial tile to the workspace, and the last split to finish a tile (an
-// agent-scope atomic counter) adds the partials to H in split order, so the result does not
-// depend on scheduling.
+// Each split writes its partial tile to the workspace and a second kernel adds the partials of
+// every tile to H in token order across the whole GPU, so the result does not depend on
+// scheduling.
 #include "common.hpp"
 
 #include <cmath>
@@ -25,9 +30,23 @@ namespace gptq {
 namespace {
 
 constexpr int HT = 256;            // tile edge (features)
+constexpr int NCU = 256;
+constexpr int SPLIT_ALIGN = 64;    // split lengths are multiples of both paths' stage lengths
+
+// register-staged path
 constexpr int HK = 64;             // tokens per LDS stage
 constexpr int HROW = HK + 8;       // LDS row length in halves (16-byte pad)
-constexpr int NCU = 256;
+
+// LDS-DMA path
+constexpr int DK = 32;             // tokens per stage
+constexpr int NST = 4;             // stages in the LDS ring (128 KB; a deeper ring crowds L2)
+constexpr int ROWB = HT * 2;       // bytes of one token row of a 256-feature strip
+constexpr int STRIPB = DK * ROWB;  // one operand of one stage (16 KB)
+constexpr int STAGEB = 2 * STRIPB;
+
+typedef short v4s __attribute__((ext_vector_type(4)));
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+#define GPTQ_LDS __attribute__((address_space(3)))
 
 struct HessArgs {
   float* H;
@@ -38,9 +57,10 @@ struct HessArgs {
   int ntiles;          // T (T + 1) / 2
   int S;               // token splits: 1, or a multiple of 8 (split s runs on XCD s % 8)
   int per_xcd;         // S == 1: tiles per XCD (contiguous in the tile order)
-  int64_t split_len;   // tokens per split (multiple of HK)
-  float* partial;      // [ntiles * S][HT * HT] when S > 1
-  int* counters;       // [ntiles] when S > 1
+  int full;            // S > 1: workgroup slots per XCD that take a whole (tile, split) item
+  int q;               // S > 1: parts each remaining item is cut into
+  int64_t split_len;   // tokens per split (multiple of SPLIT_ALIGN)
+  float* partial;      // S > 1: one HT x HT partial tile per workgroup
   int vec;             // 16-byte loads allowed
 };
 
@@ -66,6 +86,155 @@ GPTQ_DEV void tile_at(int slot, int T, int& ti, int& tj) {
   }
   ti = tj = 0;
 }
+
+// Workgroup b runs on XCD b % 8 (32 CUs each). Without token splits, XCD x takes a contiguous run
+// of tiles over all tokens. With S = 8 m splits, XCD x takes splits x, x + 8, ...: its m * ntiles
+// (tile, split) items run 32 at a time in tile order, so the workgroups running together share
+// feature strips at the same tokens. Whole rounds of 32 items come first; the items of the last,
+// partial round are each cut into q token ranges so that that round fills the XCD too.
+struct Work {
+  int tile, split, part, nparts;
+  int64_t fa, fb, t_begin, t_end;
+  bool diag;
+};
+
+GPTQ_DEV int xcd_items(const HessArgs& a) { return (a.S / 8) * a.ntiles; }
+
+GPTQ_DEV bool map_block(const HessArgs& a, Work& w) {
+  const int xcd = blockIdx.x % 8, slot = blockIdx.x / 8;
+  int64_t lo, hi;
+  if (a.S > 1) {
+    int k;
+    if (slot < a.full) {
+      k = slot;
+      w.part = 0;
+      w.nparts = 1;
+    } else {
+      k = a.full + (slot - a.full) / a.q;
+      w.part = (slot - a.full) % a.q;
+      w.nparts = a.q;
+      if (k >= xcd_items(a)) return false;
+    }
+    w.tile = k % a.ntiles;
+    w.split = xcd + 8 * (k / a.ntiles);
+    lo = (int64_t)w.split * a.split_len;
+    hi = lo + a.split_len;
+    if (w.nparts > 1) {
+      const int64_t plen = (a.split_len / w.nparts + SPLIT_ALIGN - 1) / SPLIT_ALIGN * SPLIT_ALIGN;
+      const int64_t end = hi;
+      lo = min(end, lo + w.part * plen);
+      hi = min(end, lo + plen);
+    }
+  } else {
+    w.tile = xcd * a.per_xcd + slot;
+    w.split = w.part = 0;
+    w.nparts = 1;
+    if (slot >= a.per_xcd || w.tile >= a.ntiles) return false;
+    lo = 0;
+    hi = a.n;
+  }
+  int ti, tj;
+  tile_at(w.tile, a.T, ti, tj);
+  w.diag = ti == tj;
+  w.fa = (int64_t)ti * HT;
+  w.fb = (int64_t)tj * HT;
+  w.t_begin = min(lo, a.n);
+  w.t_end = min(hi, a.n);
+  return true;
+}
+
+// Workgroups holding partials of `tile`, in token order (split, then part).
+template <typename F>
+GPTQ_DEV void for_each_partial(const HessArgs& a, int tile, F&& f) {
+  for (int split = 0; split < a.S; ++split) {
+    const int k = (split / 8) * a.ntiles + tile, xcd = split % 8;
+    if (k < a.full) {
+      f(8 * k + xcd);
+    } else {
+      for (int p = 0; p < a.q; ++p) f(8 * (a.full + (k - a.full) * a.q + p) + xcd);
+    }
+  }
+}
+
+template <typename V>
+GPTQ_DEV floatx16 mfma16(V a, V b, floatx16 c);
+template <>
+GPTQ_DEV floatx16 mfma16<half8>(half8 a, half8 b, floatx16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
+}
+template <>
+GPTQ_DEV floatx16 mfma16<bf16x8>(bf16x8 a, bf16x8 b, floatx16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+GPTQ_DEV void zero_acc(floatx16 (&acc)[4][4]) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+}
+
+// Adds 2 * acc to H (one split), or stores the split's partial tile for reduce_partials.
+// Accumulator register r of lane l holds row 8*(r/4) + 4*(l/32) + r%4, column l%32 of its 32x32
+// block.
+GPTQ_DEV void finish_tile(const HessArgs& a, const Work& w, const floatx16 (&acc)[4][4]) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+  const int li = lane & 31, lk = lane >> 5;
+  if (a.S == 1) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int64_t m = w.fa + wm * 128 + i * 32 + 8 * (r >> 2) + 4 * lk + (r & 3);
+          const int64_t c = w.fb + wn * 128 + j * 32 + li;
+          if (m < a.d && c < a.d) {
+            float* h = a.H + m * a.d + c;
+            *h = __builtin_fmaf(2.0f, acc[i][j][r], *h);
+          }
+        }
+    return;
+  }
+  float* part = a.partial + (int64_t)blockIdx.x * (HT * HT);
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int m = wm * 128 + i * 32 + 8 * (r >> 2) + 4 * lk + (r & 3);
+        const int c = wn * 128 + j * 32 + li;
+        part[m * HT + c] = acc[i][j][r];
+      }
+}
+
+// H (upper tiles) += 2 * the sum of each tile's partials in token order. Workgroup (tile, chunk)
+// takes 1024 consecutive elements of one tile, four per thread.
+__global__ __launch_bounds__(256) void reduce_partials(HessArgs a) {
+  constexpr int CHUNKS = HT * HT / 1024;
+  const int tile = blockIdx.x / CHUNKS;
+  const int e = (blockIdx.x % CHUNKS) * 1024 + threadIdx.x * 4;
+  floatx4 s = {0.0f, 0.0f, 0.0f, 0.0f};
+  for_each_partial(a, tile, [&](int b) { s += *reinterpret_cast<const floatx4*>(a.partial + (int64_t)b * HT * HT + e); });
+  int ti, tj;
+  tile_at(tile, a.T, ti, tj);
+  const int64_t gm = (int64_t)ti * HT + e / HT;
+  if (gm >= a.d) return;
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const int64_t gc = (int64_t)tj * HT + e % HT + k;
+    if (gc < a.d) {
+      float* h = a.H + gm * a.d + gc;
+      *h = __builtin_fmaf(2.0f, s[k], *h);
+    }
+  }
+}
+
+// ------------------------------------------------------------------ register-staged path
 
 // Loads an 8-token x 8-feature block starting at (tok, f) into 8 registers of 8 halves.
 GPTQ_DEV void load_block(const HessArgs& a, int64_t tok, int64_t tok_end, int64_t f, u32x4 (&r)[8]) {
@@ -106,40 +275,12 @@ GPTQ_DEV void store_block(uint16_t* tile, int fl, int tl, const u32x4 (&r)[8]) {
 }
 
 template <typename V>
-GPTQ_DEV floatx16 mfma16(V a, V b, floatx16 c);
-template <>
-GPTQ_DEV floatx16 mfma16<half8>(half8 a, half8 b, floatx16 c) {
-  return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
-}
-template <>
-GPTQ_DEV floatx16 mfma16<bf16x8>(bf16x8 a, bf16x8 b, floatx16 c) {
-  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
-}
-
-template <typename V>
-__global__ __launch_bounds__(256) void hess_kernel(HessArgs a) {
+__global__ __launch_bounds__(256) void hess_reg_kernel(HessArgs a) {
   extern __shared__ __align__(16) uint16_t smem[];
-  constexpr int TILE = HT * HROW;   // halves per operand tile
-  // buffers: [stage][operand] -> smem + (2 * stage + operand) * TILE
-
-  // Workgroup b runs on XCD b % 8. With token splits, XCD x takes splits x, x + 8, ... and walks
-  // every tile for each; without, it takes a contiguous run of tiles over all tokens.
-  const int xcd = blockIdx.x % 8, slot = blockIdx.x / 8;
-  int tile, split;
-  if (a.S > 1) {
-    tile = slot % a.ntiles;
-    split = xcd + 8 * (slot / a.ntiles);
-  } else {
-    tile = xcd * a.per_xcd + slot;
-    split = 0;
-    if (slot >= a.per_xcd || tile >= a.ntiles) return;
-  }
-  int ti, tj;
-  tile_at(tile, a.T, ti, tj);
-  const bool diag = ti == tj;
-  const int64_t fa = (int64_t)ti * HT, fb = (int64_t)tj * HT;
-  const int64_t t_begin = (int64_t)split * a.split_len;
-  const int64_t t_end = min(a.n, t_begin + a.split_len);
+  constexpr int TILE = HT * HROW;   // halves per operand tile; buffer [stage][operand]
+  Work w;
+  if (!map_block(a, w)) return;
+  const bool diag = w.diag;
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave >> 1, wn = wave & 1;
@@ -151,28 +292,23 @@ __global__ __launch_bounds__(256) void hess_kernel(HessArgs a) {
   const int fl = (tid >> 3) * 8, tl = (tid & 7) * 8;
 
   floatx16 acc[4][4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-#pragma unroll
-    for (int j = 0; j < 4; ++j)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+  zero_acc(acc);
 
   u32x4 ra[8], rb[8];
-  int64_t t0 = t_begin;
+  int64_t t0 = w.t_begin;
   int buf = 0;
-  if (t0 < t_end) {
-    load_block(a, t0 + tl, t_end, fa + fl, ra);
-    if (!diag) load_block(a, t0 + tl, t_end, fb + fl, rb);
+  if (t0 < w.t_end) {
+    load_block(a, t0 + tl, w.t_end, w.fa + fl, ra);
+    if (!diag) load_block(a, t0 + tl, w.t_end, w.fb + fl, rb);
     store_block(smem, fl, tl, ra);
     if (!diag) store_block(smem + TILE, fl, tl, rb);
   }
   __syncthreads();
-  for (; t0 < t_end; t0 += HK) {
-    const bool more = t0 + HK < t_end;
+  for (; t0 < w.t_end; t0 += HK) {
+    const bool more = t0 + HK < w.t_end;
     if (more) {
-      load_block(a, t0 + HK + tl, t_end, fa + fl, ra);
-      if (!diag) load_block(a, t0 + HK + tl, t_end, fb + fl, rb);
+      load_block(a, t0 + HK + tl, w.t_end, w.fa + fl, ra);
+      if (!diag) load_block(a, t0 + HK + tl, w.t_end, w.fb + fl, rb);
     }
     const uint16_t* Xa = smem + (2 * buf) * TILE;
     const uint16_t* Xb = diag ? Xa : Xa + TILE;
@@ -209,133 +345,259 @@ __global__ __launch_bounds__(256) void hess_kernel(HessArgs a) {
     __syncthreads();
     buf ^= 1;
   }
+  finish_tile(a, w, acc);
+}
 
-  // Epilogue: accumulator register r of lane l holds row 8*(r/4) + 4*(l/32) + r%4, column l%32.
-  if (a.S == 1) {
+// ------------------------------------------------------------------ LDS-DMA path
+
+// Swizzle of the 16-byte units of token row t (XOR on unit-index bits 1..3). The transposing read
+// takes 4 consecutive token rows at once (t % 4 = 0..3); their units land in distinct 16-byte bank
+// groups for both 16- and 32-lane read phases.
+GPTQ_DEV int row_swizzle(int t) {
+  t &= 3;
+  return (t << 1) ^ (t << 2);
+}
+
+// One 16-byte buffer load per lane into LDS: lane j's bytes land at lds_addr + 16 j (lds_addr is
+// wave-uniform, in M0; the s_nop is the wait state an M0 write needs before an LDS-DMA load). The
+// load is completed by the s_waitcnt vmcnt in stage_barrier; it is written as asm so the compiler
+// does not wait for it before every LDS read.
+GPTQ_DEV void dma16(i32x4 rsrc, uint32_t voff, uint32_t lds_addr) {
+  asm volatile("s_nop 0\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds" ::"v"(voff), "s"(rsrc), "{m0}"(lds_addr)
+               : "memory");
+}
+
+// Waits until at most N of this thread's DMA loads are in flight and all its LDS reads are done,
+// then synchronises the workgroup (no memory fence: a fence would drain every load in flight).
+template <int N>
+GPTQ_DEV void stage_barrier() {
+  // the builtin tells the compiler that no LDS read is pending any more (so it adds no waits for
+  // them later); the asm waits for the loads, which the compiler does not track
+  __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0), vmcnt and expcnt not waited for
+  asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(N) : "memory");
+}
+
+// Barrier once at most `after` stages of this thread's loads (L per stage) are still in flight.
+template <int L>
+GPTQ_DEV void stage_wait(int after) {
+  if (after >= 4) stage_barrier<4 * L>();
+  else if (after == 3) stage_barrier<3 * L>();
+  else if (after == 2) stage_barrier<2 * L>();
+  else if (after == 1) stage_barrier<L>();
+  else stage_barrier<0>();
+}
+
+template <typename V, bool DIAG>
+GPTQ_DEV void dma_tile(const HessArgs& a, const Work& w, floatx16 (&acc)[4][4], GPTQ_LDS char* lds) {
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave >> 1, wn = wave & 1;
+  const int nst = (int)((w.t_end - w.t_begin + DK - 1) / DK);
+  const uint32_t lds_base = (uint32_t)(uintptr_t)lds;
+
+  // loader: load q (0..3) of wave v fills token rows 8v + 2q and 8v + 2q + 1 of a stage's strip;
+  // lane j takes row (j / 32), 16-byte unit j % 32 in LDS, holding features 8 * (unit ^ swizzle)
+  constexpr uint32_t OOB = 0x80000000u;   // beyond any descriptor range: reads as zero
+  uint32_t voa[4], vob[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int t = 8 * wave + 2 * q + (lane >> 5);
+    const int u = (lane & 31) ^ row_swizzle(t);
+    const int64_t f1 = w.fa + 8 * u, f2 = w.fb + 8 * u;
+    voa[q] = f1 < a.d ? (uint32_t)((t * a.ldx + f1) * 2) : OOB;
+    vob[q] = f2 < a.d ? (uint32_t)((t * a.ldx + f2) * 2) : OOB;
+  }
+  auto stage_rsrc = [&](int s) {
+    const int64_t t = w.t_begin + (int64_t)s * DK;
+    const int64_t rows = min((int64_t)DK, w.t_end - t);
+    const uint64_t base = (uint64_t)(uintptr_t)(a.X + t * a.ldx);
+    const int nrec = (int)(((rows - 1) * a.ldx + a.d) * 2);   // bytes of the stage's valid tokens
+    return i32x4{(int)(uint32_t)base, (int)(uint32_t)(base >> 32), nrec, 0x00020000};
+  };
+  auto stage_dst = [&](int s) { return lds_base + (uint32_t)((s % NST) * STAGEB + wave * 4096); };
+  auto issue_a = [&](int s, const i32x4& rs) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) dma16(rs, voa[q], stage_dst(s) + q * 1024);
+  };
+  auto issue_b = [&](int s, const i32x4& rs) {
+    if (!DIAG) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) dma16(rs, vob[q], stage_dst(s) + STRIPB + q * 1024);
+    }
+  };
+  auto issue = [&](int s) {
+    const i32x4 rs = stage_rsrc(s);
+    issue_a(s, rs);
+    issue_b(s, rs);
+  };
+
+  // reader: the transposing read gives lane i of each 16-lane group element i % 4 of the 4-element
+  // reads of lanes i / 4 + 4k (k = 0..3). Lane l of the MFMA needs feature l % 32 at tokens
+  // 8 (l / 32) .. + 7, so reading lane s takes token row 8 (l / 32) + s / 4 (+4 for the second
+  // read), features 16 ((l / 16) % 2) + 4 (s % 4) .. + 3 of its 32-feature block.
+  const int g = lane >> 4;
+  const int row_lane = ((lane & 15) >> 2) + 8 * (g >> 1);
+  const int sw = row_swizzle((lane & 15) >> 2);
+  int offa[4], offb[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int unit = 4 * i + 2 * (g & 1) + ((lane & 3) >> 1);
+    offa[i] = row_lane * ROWB + ((unit ^ sw) + 16 * wm) * 16 + 8 * (lane & 1);
+    offb[i] = row_lane * ROWB + ((unit ^ sw) + 16 * wn) * 16 + 8 * (lane & 1) + (DIAG ? 0 : STRIPB);
+  }
+
+  // operands of one 16-token step: two transposing reads per 32-feature block
+  auto read_step = [&](int stage, int ks, V (&av)[4], V (&bv)[4]) {
+    GPTQ_LDS char* buf = lds + (stage % NST) * STAGEB + 16 * ks * ROWB;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const v4s a0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((GPTQ_LDS v4s*)(buf + offa[i]));
+      const v4s a1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((GPTQ_LDS v4s*)(buf + offa[i] + 4 * ROWB));
+      av[i] = __builtin_bit_cast(V, __builtin_shufflevector(a0, a1, 0, 1, 2, 3, 4, 5, 6, 7));
+      const v4s b0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((GPTQ_LDS v4s*)(buf + offb[i]));
+      const v4s b1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((GPTQ_LDS v4s*)(buf + offb[i] + 4 * ROWB));
+      bv[i] = __builtin_bit_cast(V, __builtin_shufflevector(b0, b1, 0, 1, 2, 3, 4, 5, 6, 7));
+    }
+  };
+  auto mma_step = [&](const V (&av)[4], const V (&bv)[4]) {
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int64_t m = fa + wm * 128 + i * 32 + 8 * (r >> 2) + 4 * lk + (r & 3);
-          const int64_t c = fb + wn * 128 + j * 32 + li;
-          if (m < a.d && c < a.d) {
-            float* h = a.H + m * a.d + c;
-            *h = __builtin_fmaf(2.0f, acc[i][j][r], *h);
-          }
-        }
-    return;
-  }
+      for (int j = 0; j < 4; ++j) acc[i][j] = mfma16<V>(av[i], bv[j], acc[i][j]);
+  };
 
-  float* part = a.partial + ((int64_t)tile * a.S + split) * (HT * HT);
+  // Every buffer of the ring is filled up front. In iteration `it` the barrier sits between the
+  // two 16-token steps of stage `it`: after it, stage it + 1 is complete in LDS (each thread has
+  // waited for its own loads of it) and no wave still reads stage `it` (each has waited for its
+  // reads), so the loads of stage it + NST go into that buffer while the second step multiplies
+  // and the first operands of stage it + 1 are read.
+  constexpr int L = DIAG ? 4 : 8;   // loads per thread per stage
+  for (int s = 0; s < NST && s < nst; ++s) issue(s);
+  if (nst <= 0) return;
+  stage_wait<L>(min(NST - 1, nst - 1));
+  V a0[4], b0[4], a1[4], b1[4];
+  read_step(0, 0, a0, b0);
+  for (int it = 0; it < nst; ++it) {
+    read_step(it, 1, a1, b1);
+    mma_step(a0, b0);
+    // stages issued after stage it + 1 so far: min(it + NST - 1, nst - 1) - (it + 1)
+    stage_wait<L>(min(NST - 2, nst - 2 - it));
+    if (it + 1 < nst) read_step(it + 1, 0, a0, b0);
+    // the next loads are issued between the second step's MFMAs
+    const bool more = it + NST < nst;
+    const i32x4 rs = stage_rsrc(it + NST);
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < 4; ++i) {
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int m = wm * 128 + i * 32 + 8 * (r >> 2) + 4 * lk + (r & 3);
-        const int c = wn * 128 + j * 32 + li;
-        part[m * HT + c] = acc[i][j][r];
-      }
-  __threadfence();
-  __syncthreads();
-  __shared__ int last;
-  if (tid == 0) {
-    const int prev = __hip_atomic_fetch_add(a.counters + tile, 1, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
-    last = (prev == a.S - 1);
-  }
-  __syncthreads();
-  if (!last) return;
-  __threadfence();
-  const float* base = a.partial + (int64_t)tile * a.S * (HT * HT);
-  for (int e = tid * 4; e < HT * HT; e += 256 * 4) {
-    floatx4 s = *reinterpret_cast<const floatx4*>(base + e);
-    for (int q = 1; q < a.S; ++q) s += *reinterpret_cast<const floatx4*>(base + (int64_t)q * HT * HT + e);
-    const int m = e / HT, c = e % HT;
-    const int64_t gm = fa + m;
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      const int64_t gc = fb + c + k;
-      if (gm < a.d && gc < a.d) {
-        float* h = a.H + gm * a.d + gc;
-        *h = __builtin_fmaf(2.0f, s[k], *h);
-      }
+      for (int j = 0; j < 4; ++j) acc[i][j] = mfma16<V>(a1[i], b1[j], acc[i][j]);
+      if (more && i == 0) issue_a(it + NST, rs);
+      if (more && i == 1) issue_b(it + NST, rs);
     }
   }
 }
 
-__global__ void zero_ints(int* p, int n) {
-  int i = blockIdx.x * blockDim.x + threadIdx.x;
-  if (i < n) p[i] = 0;
+template <typename V>
+__global__ __launch_bounds__(256) void hess_kernel(HessArgs a) {
+  extern __shared__ __align__(16) char smem_raw[];
+  Work w;
+  if (!map_block(a, w)) return;
+  floatx16 acc[4][4];
+  zero_acc(acc);
+  GPTQ_LDS char* lds = (GPTQ_LDS char*)smem_raw;
+  if (w.diag) dma_tile<V, true>(a, w, acc, lds);
+  else dma_tile<V, false>(a, w, acc, lds);
+  finish_tile(a, w, acc);
 }
 
-// Token splits: none when the tiles alone give every CU several workgroups; otherwise 8 (one per
-// XCD), or a larger multiple of 8 when the last round would be less than 80% full, as long as
-// each split keeps 16 stages.
+// Token splits: none when the tiles alone give every CU three or more workgroups or when there are
+// too few tokens; otherwise 8, one per XCD (the partial last round is cut finer, see map_block).
 int choose_splits(int64_t ntiles, int64_t n) {
   if (ntiles >= 3 * NCU) return 1;
   if (n < 8 * 16 * HK) return 1;
-  for (int s = 8; s <= 32 && n >= (int64_t)s * 16 * HK; s += 8) {
-    const double w = (double)(ntiles * s) / NCU;
-    if (w / std::ceil(w) >= 0.8) return s;
-  }
   return 8;
 }
 
-size_t smem_bytes() { return (size_t)4 * HT * HROW * sizeof(uint16_t); }
+template <typename V>
+hipError_t launch(const HessArgs& a, int64_t grid, bool dma, hipStream_t s) {
+  static bool attr_set[2] = {false, false};
+  const void* fn = dma ? (const void*)hess_kernel<V> : (const void*)hess_reg_kernel<V>;
+  const size_t sm = dma ? (size_t)NST * STAGEB : (size_t)4 * HT * HROW * sizeof(uint16_t);
+  if (!attr_set[dma]) {
+    const hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)sm);
+    if (e != hipSuccess) return e;
+    attr_set[dma] = true;
+  }
+  if (dma) hipLaunchKernelGGL(hess_kernel<V>, dim3((unsigned)grid), dim3(256), sm, s, a);
+  else hipLaunchKernelGGL(hess_reg_kernel<V>, dim3((unsigned)grid), dim3(256), sm, s, a);
+  return hipGetLastError();
+}
+
+struct Plan {
+  int T, ntiles, S, per_xcd, full, q;
+  int64_t grid, split_len;
+};
+
+Plan plan(int64_t n, int64_t d) {
+  Plan p{};
+  p.T = (int)((d + HT - 1) / HT);
+  p.ntiles = p.T * (p.T + 1) / 2;
+  p.S = choose_splits(p.ntiles, n);
+  p.split_len = ((n + p.S - 1) / p.S + SPLIT_ALIGN - 1) / SPLIT_ALIGN * SPLIT_ALIGN;
+  p.per_xcd = (p.ntiles + 7) / 8;
+  if (p.S > 1) {
+    constexpr int PER = NCU / 8;    // CUs per XCD
+    const int items = (p.S / 8) * p.ntiles;
+    p.full = items / PER * PER;
+    const int r = items - p.full;
+    p.q = r > 0 ? std::max(1, PER / r) : 1;
+    // parts shorter than a few stages are not worth their partial tiles
+    while (p.q > 1 && p.split_len / p.q < 8 * SPLIT_ALIGN) --p.q;
+    p.grid = 8 * (int64_t)(p.full + r * p.q);
+  } else {
+    p.grid = 8 * (int64_t)p.per_xcd;
+  }
+  return p;
+}
 
 }  // namespace
 
 size_t hessian_workspace_bytes(int64_t n, int64_t d) {
-  const int64_t T = (d + HT - 1) / HT, ntiles = T * (T + 1) / 2;
-  const int S = choose_splits(ntiles, n);
-  if (S <= 1) return 0;
-  return (size_t)ntiles * S * HT * HT * sizeof(float) + (size_t)ntiles * sizeof(int) + 256;
+  const Plan p = plan(n, d);
+  if (p.S <= 1) return 0;
+  return (size_t)p.grid * HT * HT * sizeof(float);
 }
 
 hipError_t hessian_f16(float* H, int64_t d, const void* X, int dtype, int64_t n, int64_t ldx, void* work,
                        size_t work_bytes, hipStream_t s) {
   if (n <= 0 || d <= 0) return hipSuccess;
+  Plan p = plan(n, d);
+  if (p.S > 1 && (work == nullptr || work_bytes < hessian_workspace_bytes(n, d))) {
+    // correct with fewer workgroups: no token splits
+    p.S = 1;
+    p.split_len = n;
+    p.grid = 8 * (int64_t)p.per_xcd;
+  }
   HessArgs a{};
   a.H = H;
   a.d = d;
   a.X = static_cast<const uint16_t*>(X);
   a.n = n;
   a.ldx = ldx;
-  a.T = (int)((d + HT - 1) / HT);
-  const int64_t ntiles = (int64_t)a.T * (a.T + 1) / 2;
-  a.ntiles = (int)ntiles;
-  int S = choose_splits(ntiles, n);
-  const size_t need = hessian_workspace_bytes(n, d);
-  if (S > 1 && (work == nullptr || work_bytes < need)) S = 1;  // correct, fewer workgroups
-  a.S = S;
-  a.per_xcd = (int)((ntiles + 7) / 8);
-  const int64_t grid = S > 1 ? ntiles * S : 8 * (int64_t)a.per_xcd;
-  a.split_len = ((n + S - 1) / S + HK - 1) / HK * HK;
+  a.T = p.T;
+  a.ntiles = p.ntiles;
+  a.S = p.S;
+  a.per_xcd = p.per_xcd;
+  a.full = p.full;
+  a.q = p.q;
+  a.split_len = p.split_len;
   a.vec = ((uintptr_t)X % 16 == 0) && (ldx % 8 == 0);
-  if (S > 1) {
-    a.partial = static_cast<float*>(work);
-    a.counters = reinterpret_cast<int*>(static_cast<char*>(work) + (size_t)ntiles * S * HT * HT * sizeof(float));
-    hipLaunchKernelGGL(zero_ints, dim3((unsigned)((ntiles + 255) / 256)), dim3(256), 0, s, a.counters, (int)ntiles);
-  }
-  const size_t sm = smem_bytes();
-  if (dtype == F16) {
-    static bool attr_f16 = false;
-    if (!attr_f16) {
-      (void)hipFuncSetAttribute((const void*)hess_kernel<half8>, hipFuncAttributeMaxDynamicSharedMemorySize, (int)sm);
-      attr_f16 = true;
-    }
-    hipLaunchKernelGGL(hess_kernel<half8>, dim3((unsigned)grid), dim3(256), sm, s, a);
-  } else {
-    static bool attr_bf16 = false;
-    if (!attr_bf16) {
-      (void)hipFuncSetAttribute((const void*)hess_kernel<bf16x8>, hipFuncAttributeMaxDynamicSharedMemorySize, (int)sm);
-      attr_bf16 = true;
-    }
-    hipLaunchKernelGGL(hess_kernel<bf16x8>, dim3((unsigned)grid), dim3(256), sm, s, a);
-  }
+  // the DMA path needs 16-byte units that never straddle the end of a row, and 32-bit offsets
+  // within a stage
+  const bool dma = a.vec && d % 8 == 0 && (int64_t)DK * ldx * 2 < ((int64_t)1 << 31);
+  if (p.S > 1) a.partial = static_cast<float*>(work);
+  const hipError_t e = dtype == F16 ? launch<half8>(a, p.grid, dma, s) : launch<bf16x8>(a, p.grid, dma, s);
+  if (e != hipSuccess || p.S == 1) return e;
+  hipLaunchKernelGGL(reduce_partials, dim3((unsigned)((int64_t)p.ntiles * (HT * HT / 1024))), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 

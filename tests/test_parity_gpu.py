@@ -57,21 +57,11 @@ def _checked_perm(gperm, H, rtol=1e-5):
 
 # ------------------------------------------------------------------ Hessian
 
-@pytest.mark.parametrize("x_dtype,d,n,chunk", [("f16", 300, 1000, 512), ("bf16", 300, 1000, 512),
-                                               ("f32", 300, 1000, 512), ("f16", 300, 4500, 4500),
-                                               ("f16", 520, 2100, 2048), ("bf16", 8, 70, 64)])
-def test_hessian_parity(x_dtype, d, n, chunk):
+def _check_hessian(got, chunks, x_dtype):
     """Upper triangle of H = sum 2 X_c^T X_c vs the float64 sum, within the float32 summation bound
     gamma_n * sum |2 x_i x_j| (products of fp16/bf16 values are exact in float32)."""
-    torch = torch_cuda()
-    import post_weight_quantization_20_amd as g
-    case = _case("h", 11, d=d, n=n, chunk=chunk, x_dtype=x_dtype)
-    chunks = [synth.x_chunk(case, c) for c in range(case.n_chunks)]
-    H = torch.zeros((d, d), dtype=torch.float32, device="cuda")
-    for x in chunks:
-        g.gptq_hessian_accumulate(H, dev_tensor(x, x_dtype))
-    torch.cuda.synchronize()
-    got = np.triu(H.cpu().numpy().astype(np.float64))
+    n = sum(x.shape[0] for x in chunks)
+    got = np.triu(got.astype(np.float64))
     x64 = [synth.to_f64(x, x_dtype) for x in chunks]
     want, _ = ref.hessian(x64)
     absH, _ = ref.hessian([np.abs(x) for x in x64])
@@ -81,19 +71,61 @@ def test_hessian_parity(x_dtype, d, n, chunk):
     assert np.linalg.norm(np.triu(diff)) <= 1e-5 * np.linalg.norm(np.triu(want))
 
 
-def test_hessian_deterministic_with_token_splits():
-    """One long chunk (token splits with the ordered fixup) gives the same H twice, bit for bit."""
+# d % 8 == 0 with 16-byte aligned rows streams X into LDS directly (ragged last tiles at d = 8, 264,
+# 520, 776; ragged last stages everywhere); d = 300 takes the register-staged path
+@pytest.mark.parametrize("x_dtype,d,n,chunk", [("f16", 300, 1000, 512), ("bf16", 300, 1000, 512),
+                                               ("f32", 300, 1000, 512), ("f16", 300, 4500, 4500),
+                                               ("f16", 520, 2100, 2048), ("bf16", 8, 70, 64),
+                                               ("f16", 264, 1000, 512), ("bf16", 264, 3000, 3000),
+                                               ("f16", 776, 700, 700), ("f16", 256, 33, 33)])
+def test_hessian_parity(x_dtype, d, n, chunk):
     torch = torch_cuda()
     import post_weight_quantization_20_amd as g
-    case = _case("h2", 12, d=260, n=8192, chunk=8192)
-    x = dev_tensor(synth.x_chunk(case, 0), "f16")
+    case = _case("h", 11, d=d, n=n, chunk=chunk, x_dtype=x_dtype)
+    chunks = [synth.x_chunk(case, c) for c in range(case.n_chunks)]
+    H = torch.zeros((d, d), dtype=torch.float32, device="cuda")
+    for x in chunks:
+        g.gptq_hessian_accumulate(H, dev_tensor(x, x_dtype))
+    torch.cuda.synchronize()
+    _check_hessian(H.cpu().numpy(), chunks, x_dtype)
+
+
+@pytest.mark.parametrize("width,offset", [(1040, 16), (1040, 3), (1037, 0)])
+def test_hessian_strided_views(width, offset):
+    """X as a column window of a wider matrix (leading dimension > d): an aligned window (16-byte
+    rows) streams through LDS directly, the others take the register-staged path."""
+    torch = torch_cuda()
+    import post_weight_quantization_20_amd as g
+    d, n = 520, 1500
+    case = _case("hs", 13, d=d, n=n, chunk=n)
+    x = synth.x_chunk(case, 0)
+    big = np.zeros((n, width), dtype=np.float16)
+    big[:, offset:offset + d] = x
+    X = dev_tensor(big, "f16")[:, offset:offset + d]
+    assert X.stride(0) == width
+    H = torch.zeros((d, d), dtype=torch.float32, device="cuda")
+    g.gptq_hessian_accumulate(H, X)
+    torch.cuda.synchronize()
+    _check_hessian(H.cpu().numpy(), [x], "f16")
+
+
+@pytest.mark.parametrize("d", [260, 264])
+def test_hessian_deterministic_with_token_splits(d):
+    """One long chunk (token splits with the ordered fixup) gives the same H twice, bit for bit, and
+    matches the float64 sum (d = 264 streams through LDS directly, d = 260 through registers)."""
+    torch = torch_cuda()
+    import post_weight_quantization_20_amd as g
+    case = _case("h2", 12, d=d, n=8192, chunk=8192)
+    xh = synth.x_chunk(case, 0)
+    x = dev_tensor(xh, "f16")
     outs = []
     for _ in range(2):
-        H = torch.zeros((260, 260), dtype=torch.float32, device="cuda")
+        H = torch.zeros((d, d), dtype=torch.float32, device="cuda")
         g.gptq_hessian_accumulate(H, x)
         outs.append(np.triu(H.cpu().numpy()))
-    assert g.gptq_workspace_bytes(g.GPTQ_WS_HESSIAN, 8192, 260) > 0
+    assert g.gptq_workspace_bytes(g.GPTQ_WS_HESSIAN, 8192, d) > 0
     assert np.array_equal(outs[0].view(np.uint32), outs[1].view(np.uint32))
+    _check_hessian(outs[0], [xh], "f16")
 
 
 # ------------------------------------------------------------------ factor
