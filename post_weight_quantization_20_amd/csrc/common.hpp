@@ -61,8 +61,9 @@ GPTQ_DEV void static_for(F&& f) {
 
 template <int SRC>
 GPTQ_DEV float row_bcast(float v) {
-  // DPP row_newbcast: lane SRC of each 16-lane row to the whole row
-  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x150 + SRC, 0xF, 0xF, false));
+  // DPP row_newbcast: lane SRC of each 16-lane row to the whole row (every lane has a valid
+  // source, so no old value is needed)
+  return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0x150 + SRC, 0xF, 0xF, true));
 }
 
 // DPP row_ror:15 - lane i of each 16-lane row takes the value of lane (i + 1) mod 16

@@ -107,96 +107,93 @@ __global__ __launch_bounds__(256) void gather_kernel(const float* __restrict__ H
 // ---------------------------------------------------------------- diagonal block: factor + inverse
 //
 // The 128 x 128 diagonal block is factored and inverted in LDS by one 256-thread workgroup, blocked
-// by 32: for each 32-column sub-panel, one wave factors and inverts the 32 x 32 diagonal sub-block in
-// registers (lane i holds row i; columns are broadcast with readlane, so no barriers), then the
-// waves apply the sub-panel solve and the symmetric update to the rest of the block as 32 x 32
-// MFMA tiles. The off-diagonal blocks of the inverse follow from block forward substitution,
+// by 16: for each 16-column sub-panel, one wave factors and inverts the 16 x 16 diagonal sub-block
+// in registers (lane i holds row i; every value a lane needs from another lane arrives by a DPP
+// row broadcast, so a column step costs a few VALU latencies), then the four waves apply the
+// sub-panel solve and the symmetric update to the rest of the block as 16 x 16 MFMA tiles. The
+// off-diagonal blocks of the inverse follow from block forward substitution,
 // X_qp = -X_qq sum_{t=p}^{q-1} L_qt X_tp, again as MFMA tiles.
-constexpr int LDB = NB + 1;   // LDS leading dimension (odd: row and column walks are conflict-free)
-constexpr int SB = 32;        // sub-block
+constexpr int LDB = NB + 4;   // LDS leading dimension: 16 x 16 tiles read by rows or columns are conflict-free
+constexpr int SB = 16;        // sub-block
+constexpr int LDT = SB + 1;   // per-wave temporary tile
 
-// acc (+)= op(A) op(B) over K for one 32 x 32 tile; A, B in LDS. op(A): A[i][k] or (TA) A[k][i];
-// op(B): B[k][j] or (TB) B[j][k]. One wave; lane l reads row/column l % 32 at k + l / 32.
+// acc (+)= sa op(A) op(B) over K (a multiple of 4) for one 16 x 16 tile; A, B in LDS. op(A): A[i][k]
+// or (TA) A[k][i]; op(B): B[k][j] or (TB) B[j][k]. One wave: v_mfma_f32_16x16x4f32 takes
+// A[l % 16][k + l / 16] and B[k + l / 16][l % 16] from lane l.
 template <bool TA, bool TB>
-GPTQ_DEV floatx16 mma32(floatx16 acc, const float* A, int lda, const float* B, int ldb, int K, int lane,
-                        float sa = 1.0f) {
-  const int r = lane & 31, kk = lane >> 5;
-  for (int k = 0; k < K; k += 2) {
+GPTQ_DEV floatx4 mma16(floatx4 acc, const float* A, int lda, const float* B, int ldb, int K, int lane,
+                       float sa = 1.0f) {
+  const int r = lane & 15, kk = lane >> 4;
+  for (int k = 0; k < K; k += 4) {
     const float av = TA ? A[(k + kk) * lda + r] : A[r * lda + k + kk];
     const float bv = TB ? B[r * ldb + k + kk] : B[(k + kk) * ldb + r];
-    acc = __builtin_amdgcn_mfma_f32_32x32x2f32(sa * av, bv, acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(sa * av, bv, acc, 0, 0, 0);
   }
   return acc;
 }
 
-GPTQ_DEV floatx16 tile_load(const float* T, int ld, int lane) {
-  floatx16 v;
+// Register r of lane l of a 16 x 16 MFMA result holds row 4 (l / 16) + r, column l % 16.
+GPTQ_DEV floatx4 tile_load(const float* T, int ld, int lane) {
+  floatx4 v;
 #pragma unroll
-  for (int r = 0; r < 16; ++r) v[r] = T[(8 * (r >> 2) + 4 * (lane >> 5) + (r & 3)) * ld + (lane & 31)];
+  for (int r = 0; r < 4; ++r) v[r] = T[(4 * (lane >> 4) + r) * ld + (lane & 15)];
   return v;
 }
 
-GPTQ_DEV void tile_store(float* T, int ld, int lane, floatx16 v, float scale = 1.0f) {
+GPTQ_DEV void tile_store(float* T, int ld, int lane, floatx4 v, float scale = 1.0f) {
 #pragma unroll
-  for (int r = 0; r < 16; ++r) T[(8 * (r >> 2) + 4 * (lane >> 5) + (r & 3)) * ld + (lane & 31)] = scale * v[r];
+  for (int r = 0; r < 4; ++r) T[(4 * (lane >> 4) + r) * ld + (lane & 15)] = scale * v[r];
 }
 
-GPTQ_DEV floatx16 zero16() {
-  floatx16 v;
-#pragma unroll
-  for (int r = 0; r < 16; ++r) v[r] = 0.0f;
-  return v;
-}
+GPTQ_DEV floatx4 zero4() { return floatx4{0.0f, 0.0f, 0.0f, 0.0f}; }
 
-// One wave: Cholesky factor of the 32 x 32 lower block at S (in place) and its inverse into Xs.
-// Lanes 32..63 repeat lanes 0..31. A non-positive pivot is recorded in info (1-based index
-// gbase + j + 1, when the column is real, j < valid) and replaced by 1.
-GPTQ_DEV void chol_inv32(float* S, float* Xs, int lane, int64_t* info, int64_t gbase, int valid) {
-  const int i = lane & 31;
-  float a[SB];
+// One wave: Cholesky factor of the 16 x 16 lower block at S (in place) and its inverse into Xs.
+// Lane i holds row i of the block and row i of the inverse in registers (each 16-lane row of the
+// wave computes the same thing). Column step j computes l_jj and column j of the factor; the same
+// step is the j-th step of forward elimination for the inverse (row j of L^-1 is final once divided
+// by l_jj, then rows i > j subtract l_ij times it). The pivot, column j of L and row j of L^-1
+// reach the other lanes by DPP row broadcasts, and no step branches. Entries above the diagonal
+// are never read and are zeroed on the way out. A non-positive pivot is recorded in info (1-based
+// index gbase + j + 1, when the column is real, j < valid) and replaced by 1.
+GPTQ_DEV void chol_inv16(float* S, float* Xs, int lane, int64_t* info, int64_t gbase, int valid) {
+  const int i = lane & 15;
+  float a[SB], x[SB];
 #pragma unroll
-  for (int c = 0; c < SB; ++c) a[c] = (c <= i) ? S[i * LDB + c] : 0.0f;
+  for (int c = 0; c < SB; ++c) {
+    a[c] = (c <= i) ? S[i * LDB + c] : 0.0f;
+    x[c] = (c == i) ? 1.0f : 0.0f;
+  }
+  int bad = SB;   // first non-positive pivot
   static_for<0, SB>([&](auto jc) {
     constexpr int j = decltype(jc)::value;
-    float p = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, a[j]), j));
-    if (!(p > 0.0f)) {
-      if (lane == 0 && j < valid && *info == 0) *info = gbase + j + 1;
-      p = 1.0f;
-    }
-    const float dj = sqrtf(p);
-    const float inv = 1.0f / dj;
-    const float lij = a[j] * inv;                   // L[i][j] for rows i > j
-    a[j] = (i > j) ? lij : ((i == j) ? dj : 0.0f);
+    float p = row_bcast<j>(a[j]);
+    const bool ok = p > 0.0f;
+    bad = (!ok && j < bad) ? j : bad;
+    p = ok ? p : 1.0f;
+    const float r = __builtin_amdgcn_rsqf(p);   // 1 / l_jj
+    const float lij = a[j] * r;                 // l_ij for rows i > j
+    const float sx = (i == j) ? r : 1.0f;
+#pragma unroll
+    for (int c = 0; c <= j; ++c) x[c] *= sx;
+    a[j] = (i > j) ? lij : ((i == j) ? p * r : 0.0f);
     static_for<j + 1, SB>([&](auto cc) {
       constexpr int c = decltype(cc)::value;
-      const float lcj = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, lij), c));
-      if (i >= c) a[c] = __builtin_fmaf(-lij, lcj, a[c]);
+      a[c] = __builtin_fmaf(-lij, row_bcast<c>(lij), a[c]);
     });
-  });
-#pragma unroll
-  for (int c = 0; c < SB; ++c)
-    if (lane < SB) S[i * LDB + c] = (c <= i) ? a[c] : 0.0f;
-  // inverse by forward elimination, right-looking; row j is final once divided by L[j][j]
-  float x[SB];
-#pragma unroll
-  for (int c = 0; c < SB; ++c) x[c] = (c == i) ? 1.0f : 0.0f;
-  static_for<0, SB>([&](auto jc) {
-    constexpr int j = decltype(jc)::value;
-    const float ljj = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, a[j]), j));
-    const float inv = 1.0f / ljj;
-    if (i == j) {
-#pragma unroll
-      for (int c = 0; c <= j; ++c) x[c] *= inv;
-    }
+    const float lx = (i > j) ? lij : 0.0f;
     static_for<0, j + 1>([&](auto cc) {
       constexpr int c = decltype(cc)::value;
-      const float xjc = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x[c]), j));
-      if (i > j) x[c] = __builtin_fmaf(-a[j], xjc, x[c]);
+      x[c] = __builtin_fmaf(-lx, row_bcast<j>(x[c]), x[c]);
     });
   });
+  if (bad < SB && bad < valid && lane == 0 && *info == 0) *info = gbase + bad + 1;
+  if (lane < SB) {
 #pragma unroll
-  for (int c = 0; c < SB; ++c)
-    if (lane < SB) Xs[i * LDB + c] = x[c];
+    for (int c = 0; c < SB; ++c) {
+      S[i * LDB + c] = (c <= i) ? a[c] : 0.0f;
+      Xs[i * LDB + c] = (c <= i) ? x[c] : 0.0f;
+    }
+  }
 }
 
 // Factors the diagonal block at (k0, k0) (A = L L^T, lower) and replaces the whole block in A by the
@@ -207,7 +204,7 @@ __global__ __launch_bounds__(256) void chol_diag_kernel(float* __restrict__ A, i
   extern __shared__ float sm[];
   float* La = sm;                 // [NB][LDB]: the block, then its Cholesky factor
   float* Xa = sm + NB * LDB;      // [NB][LDB]: the inverse of the factor
-  float* Tt = sm + 2 * NB * LDB;  // [3][SB][SB + 1]: per-wave temporaries
+  float* Tt = sm + 2 * NB * LDB;  // [4][SB][LDT]: per-wave temporaries
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   constexpr int PER = NB * NB / 256;
   if (nb == NB) {
@@ -238,16 +235,12 @@ __global__ __launch_bounds__(256) void chol_diag_kernel(float* __restrict__ A, i
   for (int p = 0; p < NS; ++p) {
     float* Dpp = La + (SB * p) * LDB + SB * p;
     float* Xpp = Xa + (SB * p) * LDB + SB * p;
-    if (wave == 0) chol_inv32(Dpp, Xpp, lane, info, k0 + SB * p, nb - SB * p);
+    if (wave == 0) chol_inv16(Dpp, Xpp, lane, info, k0 + SB * p, nb - SB * p);
     __syncthreads();
-    // sub-panel solve: L_qp = A_qp X_pp^T for q > p (one wave per tile)
-    {
-      const int q = p + 1 + wave;
-      if (q < NS) {
-        float* Aqp = La + (SB * q) * LDB + SB * p;
-        floatx16 acc = mma32<false, true>(zero16(), Aqp, LDB, Xpp, LDB, SB, lane);
-        tile_store(Aqp, LDB, lane, acc);
-      }
+    // sub-panel solve: L_qp = A_qp X_pp^T for q > p
+    for (int q = p + 1 + wave; q < NS; q += 4) {
+      float* Aqp = La + (SB * q) * LDB + SB * p;
+      tile_store(Aqp, LDB, lane, mma16<false, true>(zero4(), Aqp, LDB, Xpp, LDB, SB, lane));
     }
     __syncthreads();
     // symmetric update: A_qr -= L_qp L_rp^T for p < r <= q
@@ -257,8 +250,8 @@ __global__ __launch_bounds__(256) void chol_diag_kernel(float* __restrict__ A, i
         for (int r = p + 1; r <= q; ++r, ++t) {
           if (t % 4 != wave) continue;
           float* Aqr = La + (SB * q) * LDB + SB * r;
-          floatx16 acc = tile_load(Aqr, LDB, lane);
-          acc = mma32<false, true>(acc, La + (SB * q) * LDB + SB * p, LDB, La + (SB * r) * LDB + SB * p, LDB, SB,
+          floatx4 acc = tile_load(Aqr, LDB, lane);
+          acc = mma16<false, true>(acc, La + (SB * q) * LDB + SB * p, LDB, La + (SB * r) * LDB + SB * p, LDB, SB,
                                    lane, -1.0f);
           tile_store(Aqr, LDB, lane, acc);
         }
@@ -267,18 +260,18 @@ __global__ __launch_bounds__(256) void chol_diag_kernel(float* __restrict__ A, i
   }
   // off-diagonal blocks of the inverse, block row by block row
   for (int q = 1; q < NS; ++q) {
-    const int pb = wave;
-    if (pb < q) {
-      floatx16 acc = zero16();
+    for (int pb = wave; pb < q; pb += 4) {
+      floatx4 acc = zero4();
       for (int t = pb; t < q; ++t)
-        acc = mma32<false, false>(acc, La + (SB * q) * LDB + SB * t, LDB, Xa + (SB * t) * LDB + SB * pb, LDB, SB,
+        acc = mma16<false, false>(acc, La + (SB * q) * LDB + SB * t, LDB, Xa + (SB * t) * LDB + SB * pb, LDB, SB,
                                   lane);
-      float* T = Tt + pb * SB * (SB + 1);
-      tile_store(T, SB + 1, lane, acc);
+      float* T = Tt + wave * SB * LDT;
+      tile_store(T, LDT, lane, acc);
       __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
       __builtin_amdgcn_wave_barrier();
-      acc = mma32<false, false>(zero16(), Xa + (SB * q) * LDB + SB * q, LDB, T, SB + 1, SB, lane);
+      acc = mma16<false, false>(zero4(), Xa + (SB * q) * LDB + SB * q, LDB, T, LDT, SB, lane);
       tile_store(Xa + (SB * q) * LDB + SB * pb, LDB, lane, acc, -1.0f);
+      __builtin_amdgcn_wave_barrier();
     }
     __syncthreads();
   }
@@ -312,7 +305,7 @@ __global__ __launch_bounds__(256) void flip_kernel(float* __restrict__ A, int64_
   }
 }
 
-size_t chol_smem() { return ((size_t)2 * NB * LDB + 3 * SB * (SB + 1)) * sizeof(float); }
+size_t chol_smem() { return ((size_t)2 * NB * LDB + 4 * SB * LDT) * sizeof(float); }
 
 }  // namespace
 

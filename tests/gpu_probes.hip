@@ -34,6 +34,15 @@ __global__ void mfma_f32_kernel(const float* A, const float* B, float* D) {
   for (int r = 0; r < 16; ++r) D[(8 * (r / 4) + 4 * (l / 32) + r % 4) * 32 + l % 32] = acc[r];
 }
 
+// D (16 x 16) = A (16 x 4) B (4 x 16), fp32; one wave. Lane l supplies A[l % 16][l / 16] and
+// B[l / 16][l % 16]; register r of lane l is taken to hold D[4 (l / 16) + r][l % 16].
+__global__ void mfma_f32_16_kernel(const float* A, const float* B, float* D) {
+  const int l = threadIdx.x;
+  floatx4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
+  acc = __builtin_amdgcn_mfma_f32_16x16x4f32(A[(l % 16) * 4 + l / 16], B[(l / 16) * 16 + l % 16], acc, 0, 0, 0);
+  for (int r = 0; r < 4; ++r) D[(4 * (l / 16) + r) * 16 + l % 16] = acc[r];
+}
+
 // out[src * 64 + lane] = value of lane (16 * (lane / 16) + src), through row_bcast<src>; one wave.
 __global__ void bcast_kernel(const float* in, float* out) {
   const int l = threadIdx.x;
@@ -77,6 +86,11 @@ int probe_mfma_bf16(const uint16_t* A, const uint16_t* B, float* D) {
 
 int probe_mfma_f32(const float* A, const float* B, float* D) {
   hipLaunchKernelGGL(mfma_f32_kernel, dim3(1), dim3(64), 0, 0, A, B, D);
+  return sync_status();
+}
+
+int probe_mfma_f32_16(const float* A, const float* B, float* D) {
+  hipLaunchKernelGGL(mfma_f32_16_kernel, dim3(1), dim3(64), 0, 0, A, B, D);
   return sync_status();
 }
 

@@ -42,6 +42,18 @@ def test_mfma_f32_layout():
     assert np.array_equal(d.cpu().numpy(), A @ B)
 
 
+def test_mfma_f32_16x16_layout():
+    torch = torch_cuda()
+    L = load_probes()
+    rng = np.random.default_rng(4)
+    A = rng.integers(-8, 9, size=(16, 4)).astype(np.float32)
+    B = rng.integers(-8, 9, size=(4, 16)).astype(np.float32)
+    a, b = torch.from_numpy(A).cuda(), torch.from_numpy(B).cuda()
+    d = torch.zeros((16, 16), dtype=torch.float32, device="cuda")
+    assert L.probe_mfma_f32_16(_p(a), _p(b), _p(d)) == 0
+    assert np.array_equal(d.cpu().numpy(), A @ B)
+
+
 def test_row_broadcast_and_rotation():
     torch = torch_cuda()
     L = load_probes()
