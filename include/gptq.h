@@ -20,10 +20,13 @@
  *
  * Conventions for every call:
  *   - Matrices are row-major. Pointers named as device memory must be device memory of the current
- *     HIP device; the caller allocates and owns every buffer, the library allocates nothing and
- *     keeps no state between calls.
+ *     HIP device; the caller allocates and owns every buffer and the library allocates no device
+ *     memory. The only state it keeps: on first use on a device it creates two helper streams and a
+ *     few events there (kept until the process ends), on which parts of a call run concurrently.
  *   - `stream` is a hipStream_t (NULL: the default stream). Work is queued on it and the call returns
- *     without waiting, except gptq_factor, which waits once for its own work (see there).
+ *     without waiting, except gptq_factor, which waits once for its own work (see there). Work a call
+ *     places on the helper streams starts after the work queued on `stream` before the call and
+ *     ends before the call's later work on `stream`, so the call is ordered on `stream` as a whole.
  *   - Arguments are checked on the host before anything is queued. A rejected call returns a negative
  *     status and has no effect. HIP launch failures return GPTQ_EHIP.
  *   - Calls that share no output buffer may run concurrently on different streams.

@@ -100,6 +100,18 @@ size_t factor_workspace_bytes(int64_t d);
 hipError_t factor(const float* H, int64_t d, int64_t n, double damp, int act_order, float* U, int32_t* perm,
                   void* work, hipStream_t s, int** status_dev, int64_t** info_dev);
 
+// Helper streams and events of the current device for work that overlaps within one call (created
+// on first use, kept until the process ends; default priority). Hold `mu` while queueing work that
+// records or waits on these events: concurrent callers share them.
+struct Helpers {
+  hipStream_t stream[2];
+  hipEvent_t event[8];
+  void* mu;   // std::mutex
+};
+hipError_t helpers(Helpers** out);
+void helpers_lock(Helpers* h);
+void helpers_unlock(Helpers* h);
+
 // Column loop workspace layout (see quant.hip).
 struct QuantLayout {
   int64_t ldw, bp;

@@ -337,10 +337,18 @@ hipError_t factor(const float* H, int64_t d, int64_t n, double damp, int act_ord
                         (int)chol_smem());
     attr = true;
   }
-  hipError_t e;
+  // Blocked right-looking Cholesky of the reversed matrix on the caller's stream (diagonal blocks end
+  // up inverted), and the blocked right-looking inverse of the factor on a helper stream: inverse
+  // step j needs only Cholesky step j (its diagonal block and column panel) and touches only
+  // columns left of block j + 1, which the later Cholesky steps neither read nor write.
+  Helpers* hp = nullptr;
+  hipError_t e = helpers(&hp);
+  if (e != hipSuccess) return e;
+  hipStream_t hs = hp->stream[1];
+  hipEvent_t ev_step = hp->event[4], ev_done = hp->event[5];
+  helpers_lock(hp);
   const int64_t nblk = (d + NB - 1) / NB;
-  // blocked right-looking Cholesky of the reversed matrix; diagonal blocks end up inverted
-  for (int64_t k = 0; k < nblk; ++k) {
+  for (int64_t k = 0; k < nblk && e == hipSuccess; ++k) {
     const int64_t k0 = k * NB, k1 = std::min(d, k0 + NB), kb = k1 - k0;
     hipLaunchKernelGGL(chol_diag_kernel, dim3(1), dim3(256), chol_smem(), s, U, d, k0, (int)kb, w.info);
     if (k1 < d) {
@@ -350,19 +358,21 @@ hipError_t factor(const float* H, int64_t d, int64_t n, double damp, int act_ord
       t.B = U + k0 * d + k0; t.ldb = d; t.transB = 1;
       t.C = U + k1 * d + k0; t.ldc = d;
       t.alpha = 1.0f; t.beta = 0.0f; t.tri = 0;
-      if ((e = gemm_f32(t, s)) != hipSuccess) return e;
+      if ((e = gemm_f32(t, s)) != hipSuccess) break;
+    }
+    if ((e = hipEventRecord(ev_step, s)) != hipSuccess) break;
+    if (k1 < d) {
       GemmArgs u{};  // trailing update: A22 -= P P^T (lower part)
       u.M = d - k1; u.N = d - k1; u.K = kb;
       u.A = U + k1 * d + k0; u.lda = d; u.transA = 0;
       u.B = U + k1 * d + k0; u.ldb = d; u.transB = 1;
       u.C = U + k1 * d + k1; u.ldc = d;
       u.alpha = -1.0f; u.beta = 1.0f; u.tri = 1;
-      if ((e = gemm_f32(u, s)) != hipSuccess) return e;
+      if ((e = gemm_f32(u, s)) != hipSuccess) break;
     }
-  }
-  // blocked right-looking inverse of the lower factor, in place (diagonal blocks already inverted)
-  for (int64_t j = 0; j < nblk; ++j) {
-    const int64_t j0 = j * NB, j1 = std::min(d, j0 + NB), jb = j1 - j0;
+    // inverse step k on the helper stream (the diagonal block is already inverted)
+    if ((e = hipStreamWaitEvent(hs, ev_step, 0)) != hipSuccess) break;
+    const int64_t j0 = k0, j1 = k1, jb = kb;
     if (j0 > 0) {
       GemmArgs r{};  // row panel: R <- -X_jj R
       r.M = jb; r.N = j0; r.K = jb;
@@ -370,7 +380,7 @@ hipError_t factor(const float* H, int64_t d, int64_t n, double damp, int act_ord
       r.B = U + j0 * d; r.ldb = d; r.transB = 0;
       r.C = U + j0 * d; r.ldc = d;
       r.alpha = -1.0f; r.beta = 0.0f; r.tri = 0;
-      if ((e = gemm_f32(r, s)) != hipSuccess) return e;
+      if ((e = gemm_f32(r, hs)) != hipSuccess) break;
       if (j1 < d) {
         GemmArgs q{};  // rectangle: A[j1:, :j0] += L[j1:, j] R
         q.M = d - j1; q.N = j0; q.K = jb;
@@ -378,7 +388,7 @@ hipError_t factor(const float* H, int64_t d, int64_t n, double damp, int act_ord
         q.B = U + j0 * d; q.ldb = d; q.transB = 0;
         q.C = U + j1 * d; q.ldc = d;
         q.alpha = 1.0f; q.beta = 1.0f; q.tri = 0;
-        if ((e = gemm_f32(q, s)) != hipSuccess) return e;
+        if ((e = gemm_f32(q, hs)) != hipSuccess) break;
       }
     }
     if (j1 < d) {
@@ -388,9 +398,15 @@ hipError_t factor(const float* H, int64_t d, int64_t n, double damp, int act_ord
       c.B = U + j0 * d + j0; c.ldb = d; c.transB = 0;
       c.C = U + j1 * d + j0; c.ldc = d;
       c.alpha = 1.0f; c.beta = 0.0f; c.tri = 0;
-      if ((e = gemm_f32(c, s)) != hipSuccess) return e;
+      if ((e = gemm_f32(c, hs)) != hipSuccess) break;
     }
   }
+  // join the helper stream (also after a failed launch, so nothing is left behind)
+  hipError_t j = hipEventRecord(ev_done, hs);
+  if (j == hipSuccess) j = hipStreamWaitEvent(s, ev_done, 0);
+  helpers_unlock(hp);
+  if (e == hipSuccess) e = j;
+  if (e != hipSuccess) return e;
   hipLaunchKernelGGL(flip_kernel, dim3((unsigned)d), dim3(256), 0, s, U, d);
   return hipGetLastError();
 }
