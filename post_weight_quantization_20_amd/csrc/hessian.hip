@@ -446,11 +446,11 @@ GPTQ_DEV void dma_tile(const HessArgs& a, const Work& w, floatx16 (&acc)[4][4], 
     offb[i] = row_lane * ROWB + ((unit ^ sw) + 16 * wn) * 16 + 8 * (lane & 1) + (DIAG ? 0 : STRIPB);
   }
 
-  // operands of one 16-token step: two transposing reads per 32-feature block
-  auto read_step = [&](int stage, int ks, V (&av)[4], V (&bv)[4]) {
+  // operands of one 16-token step: two transposing reads per 32-feature block (blocks i0..i1-1)
+  auto read_step = [&](int stage, int ks, V (&av)[4], V (&bv)[4], int i0 = 0, int i1 = 4) {
     GPTQ_LDS char* buf = lds + (stage % NST) * STAGEB + 16 * ks * ROWB;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
+    for (int i = i0; i < i1; ++i) {
       const v4s a0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((GPTQ_LDS v4s*)(buf + offa[i]));
       const v4s a1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((GPTQ_LDS v4s*)(buf + offa[i] + 4 * ROWB));
       av[i] = __builtin_bit_cast(V, __builtin_shufflevector(a0, a1, 0, 1, 2, 3, 4, 5, 6, 7));
@@ -478,20 +478,43 @@ GPTQ_DEV void dma_tile(const HessArgs& a, const Work& w, floatx16 (&acc)[4][4], 
   V a0[4], b0[4], a1[4], b1[4];
   read_step(0, 0, a0, b0);
   for (int it = 0; it < nst; ++it) {
+    // The first step's operands were read a whole step ago: waiting for them here (instead of
+    // after the next reads are queued, where the 15-deep LDS counter would force waiting for those
+    // too) lets the reads of the second step run under the first step's MFMAs.
+    __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0)
     read_step(it, 1, a1, b1);
     mma_step(a0, b0);
+#pragma unroll
+    for (int q = 0; q < 16; ++q) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // one MFMA
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // one LDS read
+    }
     // stages issued after stage it + 1 so far: min(it + NST - 1, nst - 1) - (it + 1)
     stage_wait<L>(min(NST - 2, nst - 2 - it));
-    if (it + 1 < nst) read_step(it + 1, 0, a0, b0);
-    // the next loads are issued between the second step's MFMAs
+    // second step, with the first operands of stage it + 1 read under its MFMAs and the loads of
+    // stage it + NST issued half way through (after the last stage those reads take a stale buffer
+    // of the ring and are not used)
     const bool more = it + NST < nst;
-    const i32x4 rs = stage_rsrc(it + NST);
+    read_step(it + 1, 0, a0, b0, 0, 2);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
+    for (int i = 0; i < 2; ++i)
 #pragma unroll
       for (int j = 0; j < 4; ++j) acc[i][j] = mfma16<V>(a1[i], b1[j], acc[i][j]);
-      if (more && i == 0) issue_a(it + NST, rs);
-      if (more && i == 1) issue_b(it + NST, rs);
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 1);
+    }
+    if (more) issue(it + NST);
+    read_step(it + 1, 0, a0, b0, 2, 4);
+#pragma unroll
+    for (int i = 2; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) acc[i][j] = mfma16<V>(a1[i], b1[j], acc[i][j]);
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 2);
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 2);
     }
   }
 }
