@@ -76,9 +76,8 @@ GPTQ_DEV float row_ror15(float v) {
 // C[M x N] = alpha * op(A) * op(B) + beta * C, row-major fp32, on MFMA.
 // op(A) is A (M x K, lda) or A^T (A stored K x M); op(B) is B (K x N, ldb) or B^T (B stored N x K).
 // tri: 0 every element, 1 only elements with m >= n, 2 only m <= n.
-// beta == 0 never reads C. In place is safe for an operand that shares rows (A, no transpose)
-// with C when N <= 128, or columns (B, no transpose) with C when M <= 128: one workgroup then
-// reads the whole reduction range of its output strip before it writes.
+// beta == 0 never reads C. C must not overlap A or B: several workgroups can share one output
+// strip, and one may store while another still reads its operand.
 struct GemmArgs {
   int64_t M, N, K;
   const float* A; int64_t lda; int transA;

@@ -81,6 +81,21 @@ __global__ __launch_bounds__(256) void rank_perm_kernel(const float* __restrict_
   if (i < d) perm[rank] = (int32_t)i;
 }
 
+// dst[r][c] = src[r][c] for a rows x cols block (leading dimensions ldd, lds); used to stage the
+// operand of a product whose output overwrites it.
+__global__ __launch_bounds__(256) void copy2d_kernel(float* __restrict__ dst, int64_t ldd, const float* __restrict__ src,
+                                                     int64_t lds, int64_t rows, int64_t cols) {
+  for (int64_t r = blockIdx.x; r < rows; r += gridDim.x)
+    for (int64_t c = threadIdx.x; c < cols; c += 256) dst[r * ldd + c] = src[r * lds + c];
+}
+
+hipError_t copy2d(float* dst, int64_t ldd, const float* src, int64_t lds, int64_t rows, int64_t cols, hipStream_t s) {
+  if (rows <= 0 || cols <= 0) return hipSuccess;
+  hipLaunchKernelGGL(copy2d_kernel, dim3((unsigned)std::min<int64_t>(rows, 8192)), dim3(256), 0, s, dst, ldd, src, lds,
+                     rows, cols);
+  return hipGetLastError();
+}
+
 __global__ void iota_kernel(int32_t* perm, int64_t d) {
   const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (i < d) perm[i] = (int32_t)i;
@@ -309,7 +324,10 @@ size_t chol_smem() { return ((size_t)2 * NB * LDB + 4 * SB * LDT) * sizeof(float
 
 }  // namespace
 
-size_t factor_workspace_bytes(int64_t d) { return 256 + (size_t)d * sizeof(float); }
+// Workspace: the status words, the sort keys, and two panel buffers of d x NB floats (one per stream)
+// that stage the operand of the three products that overwrite their own input.
+size_t factor_keys_bytes(int64_t d) { return ((size_t)d * sizeof(float) + 255) / 256 * 256; }
+size_t factor_workspace_bytes(int64_t d) { return 256 + factor_keys_bytes(d) + 2 * (size_t)d * NB * sizeof(float); }
 
 // Returns hipSuccess after queueing everything; *status_out / *info_out are device addresses of the
 // status word and pivot index (read by the caller after a stream synchronisation).
@@ -321,6 +339,8 @@ hipError_t factor(const float* H, int64_t d, int64_t n, double damp, int act_ord
   w.info = reinterpret_cast<int64_t*>(wb + 8);
   w.status = reinterpret_cast<int*>(wb + 16);
   w.keys = reinterpret_cast<float*>(wb + 256);
+  float* stage_main = reinterpret_cast<float*>(wb + 256 + factor_keys_bytes(d));   // d x NB, caller's stream
+  float* stage_help = stage_main + d * NB;                                          // d x NB, helper stream
   *status_dev = w.status;
   *info_dev = w.info;
 
@@ -338,9 +358,10 @@ hipError_t factor(const float* H, int64_t d, int64_t n, double damp, int act_ord
     attr = true;
   }
   // Blocked right-looking Cholesky of the reversed matrix on the caller's stream (diagonal blocks end
-  // up inverted), and the blocked right-looking inverse of the factor on a helper stream: inverse
-  // step j needs only Cholesky step j (its diagonal block and column panel) and touches only
-  // columns left of block j + 1, which the later Cholesky steps neither read nor write.
+  // up inverted), and the blocked right-looking inverse of the factor on a helper stream. Inverse
+  // step j starts after Cholesky step j is complete, its trailing update included (that update reads
+  // the column panel the inverse step overwrites), and touches only columns left of block j + 1,
+  // which the later Cholesky steps neither read nor write.
   Helpers* hp = nullptr;
   hipError_t e = helpers(&hp);
   if (e != hipSuccess) return e;
@@ -352,15 +373,17 @@ hipError_t factor(const float* H, int64_t d, int64_t n, double damp, int act_ord
     const int64_t k0 = k * NB, k1 = std::min(d, k0 + NB), kb = k1 - k0;
     hipLaunchKernelGGL(chol_diag_kernel, dim3(1), dim3(256), chol_smem(), s, U, d, k0, (int)kb, w.info);
     if (k1 < d) {
-      GemmArgs t{};  // panel solve: P <- P L_kk^-T
+      // panel solve: P <- P L_kk^-T (P staged: workgroups of one row strip must not overwrite the
+      // columns another one still reads)
+      if ((e = copy2d(stage_main, kb, U + k1 * d + k0, d, d - k1, kb, s)) != hipSuccess) break;
+      GemmArgs t{};
       t.M = d - k1; t.N = kb; t.K = kb;
-      t.A = U + k1 * d + k0; t.lda = d; t.transA = 0;
+      t.A = stage_main; t.lda = kb; t.transA = 0;
       t.B = U + k0 * d + k0; t.ldb = d; t.transB = 1;
       t.C = U + k1 * d + k0; t.ldc = d;
       t.alpha = 1.0f; t.beta = 0.0f; t.tri = 0;
       if ((e = gemm_f32(t, s)) != hipSuccess) break;
     }
-    if ((e = hipEventRecord(ev_step, s)) != hipSuccess) break;
     if (k1 < d) {
       GemmArgs u{};  // trailing update: A22 -= P P^T (lower part)
       u.M = d - k1; u.N = d - k1; u.K = kb;
@@ -370,14 +393,17 @@ hipError_t factor(const float* H, int64_t d, int64_t n, double damp, int act_ord
       u.alpha = -1.0f; u.beta = 1.0f; u.tri = 1;
       if ((e = gemm_f32(u, s)) != hipSuccess) break;
     }
+    if ((e = hipEventRecord(ev_step, s)) != hipSuccess) break;
     // inverse step k on the helper stream (the diagonal block is already inverted)
     if ((e = hipStreamWaitEvent(hs, ev_step, 0)) != hipSuccess) break;
     const int64_t j0 = k0, j1 = k1, jb = kb;
     if (j0 > 0) {
-      GemmArgs r{};  // row panel: R <- -X_jj R
+      // row panel: R <- -X_jj R (R staged)
+      if ((e = copy2d(stage_help, j0, U + j0 * d, d, jb, j0, hs)) != hipSuccess) break;
+      GemmArgs r{};
       r.M = jb; r.N = j0; r.K = jb;
       r.A = U + j0 * d + j0; r.lda = d; r.transA = 0;
-      r.B = U + j0 * d; r.ldb = d; r.transB = 0;
+      r.B = stage_help; r.ldb = j0; r.transB = 0;
       r.C = U + j0 * d; r.ldc = d;
       r.alpha = -1.0f; r.beta = 0.0f; r.tri = 0;
       if ((e = gemm_f32(r, hs)) != hipSuccess) break;
@@ -392,9 +418,11 @@ hipError_t factor(const float* H, int64_t d, int64_t n, double damp, int act_ord
       }
     }
     if (j1 < d) {
-      GemmArgs c{};  // column panel: L[j1:, j] <- L[j1:, j] X_jj
+      // column panel: L[j1:, j] <- L[j1:, j] X_jj (L[j1:, j] staged)
+      if ((e = copy2d(stage_help, jb, U + j1 * d + j0, d, d - j1, jb, hs)) != hipSuccess) break;
+      GemmArgs c{};
       c.M = d - j1; c.N = jb; c.K = jb;
-      c.A = U + j1 * d + j0; c.lda = d; c.transA = 0;
+      c.A = stage_help; c.lda = jb; c.transA = 0;
       c.B = U + j0 * d + j0; c.ldb = d; c.transB = 0;
       c.C = U + j1 * d + j0; c.ldc = d;
       c.alpha = 1.0f; c.beta = 0.0f; c.tri = 0;

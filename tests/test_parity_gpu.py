@@ -158,6 +158,30 @@ def test_factor_parity(d, act):
     print(f"d={d} kappa={kappa:.3g} max rel err {err:.3g} residual {resid:.3g}")
 
 
+def test_factor_deterministic():
+    """Three factors of one act-order Hessian (12 diagonal blocks; the triangular inverse overlaps
+    the Cholesky on a helper stream) are identical bit for bit, so scheduling never changes the
+    result, and within 1e-4 of max |U| of the oracle's (float32 LAPACK reaches about 1e-6 here)."""
+    torch = torch_cuda()
+    import post_weight_quantization_20_amd as g
+    case = _case("fd", 14, d=1536, n=3072, chunk=3072, x_dtype="f32", act_order=True, x_dist="laplace")
+    x = synth.x_chunk(case, 0)
+    H, n = ref.hessian([synth.to_f64(x, "f32")])
+    Hd = torch.from_numpy(H.astype(np.float32)).cuda()
+    p = params_of(case)
+    outs = []
+    for _ in range(3):
+        U, perm = g.gptq_factor(Hd.clone(), n, p)
+        torch.cuda.synchronize()
+        outs.append((U.cpu().numpy(), perm.cpu().numpy()))
+    for U, perm in outs[1:]:
+        assert np.array_equal(U.view(np.uint32), outs[0][0].view(np.uint32))
+        assert np.array_equal(perm, outs[0][1])
+    Hh, _, _ = ref.damp_and_order(H, n, case.damp, True, perm=_checked_perm(outs[0][1].astype(np.int64), H))
+    Uo = ref.inverse_cholesky_upper(Hh)
+    assert np.max(np.abs(outs[0][0] - Uo)) / np.max(np.abs(Uo)) <= 1e-4
+
+
 def test_factor_not_positive_definite():
     """A dead input feature with no damping: the factor reports GPTQ_ENOTPD and the feature's
     1-based position (tools page, "When the method breaks down")."""
