@@ -201,3 +201,95 @@ def test_q_proj_full_size():
 def test_down_proj_width_act_order():
     """down_proj's 4096 x 11008 layer with act-order and 4096 Laplace-distributed tokens."""
     _fullsize(synth.case_from_config("down_proj", n=4096), 102)
+
+
+def _tie(num, den, tau=TAU):
+    """Positions where the float32 ratio num / den lies within tau of a half-integer."""
+    x = np.float32(num) / np.float32(den) if np.ndim(num) == 0 else num.astype(np.float32) / den.astype(np.float32)
+    f = np.asarray(x, dtype=np.float64) - np.floor(np.asarray(x, dtype=np.float64))
+    return np.abs(f - 0.5) < tau
+
+
+def test_fc2_full_size_properties():
+    """OPT-175B fc2-shaped layer at full size (12288 x 49152, 131072 tokens, 3-bit, one group per
+    row). The oracle cannot factor a 49152-wide Hessian within a test, so it checks what it computes
+    one by one and what holds at any size: sampled Hessian entries and the whole diagonal; the
+    factor's residual (U^T U Hhat - I) e_k on sampled columns, with Hhat e_k formed from X; every
+    row's scale and zero point (one group per row: the grid of the unmodified row); every row's code
+    of the first processed column (no error feedback has reached it); the packed words; and, in
+    aggregate over sampled rows, a lower damped objective than round-to-nearest."""
+    torch = torch_cuda()
+    case = synth.case_from_config("fc2")
+    rng = np.random.default_rng(103)
+    X = synth.x_tokens(case)
+    W_host = synth.weight(case)
+    print(f"[fullsize] fc2: W {case.rows}x{case.d}, X {case.n}x{case.d}", flush=True)
+    out = _run_gpu(case, X, W_host)
+    d, n, maxq = case.d, case.n, (1 << case.bits) - 1
+    Hg = out.pop("H")
+    # Hessian: sampled entries within the float32 summation bound, and the whole diagonal
+    i = rng.integers(0, d, SAMPLE_PAIRS)
+    j = rng.integers(0, d, SAMPLE_PAIRS)
+    i, j = np.minimum(i, j), np.maximum(i, j)
+    col = lambda c: synth.to_f64(X[:, c], case.x_dtype)
+    exact = np.array([2.0 * np.dot(col(a), col(b)) for a, b in zip(i, j)])
+    absH = np.array([2.0 * np.dot(np.abs(col(a)), np.abs(col(b))) for a, b in zip(i, j)])
+    assert np.all(np.abs(Hg[i, j] - exact) <= (n * U32 / (1 - n * U32)) * absH + 1e-30)
+    # one pass over X: the diagonal, H e_k for sampled k, and X (W - Q)^T for sampled rows
+    W = synth.to_f64(W_host, case.w_dtype)
+    ks = rng.choice(d, 4, replace=False)
+    rows = rng.choice(case.rows, 16, replace=False)
+    Qg = dequant(out["codes"][rows], out["scales"][rows], out["zeros"][rows], out["g_idx"])
+    Qr = ref.rtn(W[rows], case.bits, case.group_size).Q
+    DT = np.concatenate([W[rows] - Qg, W[rows] - Qr]).T
+    diag = np.zeros(d)
+    HE = np.zeros((d, len(ks)))
+    XD = np.zeros(2 * len(rows))
+    for t0 in range(0, n, 8192):
+        xs = synth.to_f64(X[t0:t0 + 8192], case.x_dtype)
+        diag += 2.0 * np.einsum("ij,ij->j", xs, xs)
+        HE += 2.0 * xs.T @ xs[:, ks]
+        XD += np.sum((xs @ DT) ** 2, axis=0)
+    assert np.all(np.abs(np.diag(Hg) - diag) <= (n * U32 / (1 - n * U32)) * diag)
+    del Hg, X
+    # factor: residual on sampled columns, Hhat e_k = (H e_k) / n + lam e_k
+    lam = case.damp * float(np.mean(diag)) / n
+    HE /= n
+    HE[ks, np.arange(len(ks))] += lam
+    Ug = out.pop("U")
+    V = np.zeros_like(HE)
+    for r0 in range(0, d, 4096):
+        V[r0:r0 + 4096] = Ug[r0:r0 + 4096].astype(np.float64) @ HE
+    R = np.zeros_like(HE)
+    for r0 in range(0, d, 4096):
+        R += Ug[r0:r0 + 4096].astype(np.float64).T @ V[r0:r0 + 4096]
+    R[ks, np.arange(len(ks))] -= 1.0
+    print(f"[fullsize] fc2 factor residual {np.max(np.abs(R)):.3g}", flush=True)
+    # float32 arithmetic leaves about 5e-6 here; an operand read while being overwritten left 1e-2
+    assert np.max(np.abs(R)) <= 1e-3
+    del Ug
+    # one group per row: every row's grid comes from the unmodified row
+    s_o, z_o = ref.group_grid(W, maxq)
+    s_g = out["scales"][:, 0].astype(np.float64)
+    assert float(np.max(np.abs(s_g - s_o) / s_o)) <= SCALE_RTOL
+    wmin = W.min(axis=1)
+    zt = _tie(-wmin, s_g)
+    zdiff = out["zeros"][:, 0] != z_o.astype(np.int32)
+    assert not np.any(zdiff & ~zt), "zero points differ outside tie windows"
+    assert int(np.count_nonzero(zdiff)) <= 1e-3 * case.rows
+    # the first processed column (no feedback yet); perm is the identity without act-order
+    assert np.array_equal(out["perm"], np.arange(d))
+    q0, _ = ref.quantize_to_grid(W[:, 0], s_o, z_o, maxq)
+    ct = _tie(W[:, 0], s_g) | zt
+    cdiff = out["codes"][:, 0] != q0.astype(np.uint8)
+    assert not np.any(cdiff & ~ct), "first-column codes differ outside tie windows"
+    assert int(np.count_nonzero(cdiff)) <= 1e-3 * case.rows
+    # codes in range, packed words at their bit positions
+    assert int(out["codes"].max()) <= maxq
+    _check_pack(case, out)
+    # aggregate comparison with round-to-nearest on the sampled rows (damped objective from X)
+    Dg, Dr = DT[:, :len(rows)], DT[:, len(rows):]
+    obj_g = 2.0 / n * XD[:len(rows)].sum() + lam * np.sum(Dg ** 2)
+    obj_r = 2.0 / n * XD[len(rows):].sum() + lam * np.sum(Dr ** 2)
+    print(f"[fullsize] fc2 damped objective on {len(rows)} rows: GPTQ {obj_g:.4g}, RTN {obj_r:.4g}", flush=True)
+    assert obj_g < obj_r
