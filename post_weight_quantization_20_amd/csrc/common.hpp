@@ -113,7 +113,7 @@ void helpers_unlock(Helpers* h);
 
 // Column loop workspace layout (see quant.hip).
 struct QuantLayout {
-  int64_t ldw, bp;
+  int64_t ldw, bp, ld_err;
   size_t off_wp, off_codes, off_err, off_loss, off_iperm, total;
 };
 QuantLayout quant_layout(int64_t rows, int64_t d, int block);

@@ -37,7 +37,8 @@ struct QArgs {
   float* scales;         // [rows x ngroups]
   int32_t* zeros;        // [rows x ngroups]
   int64_t ngroups;
-  float* err;            // [rows x 16 * CPL]
+  float* err;            // this block's errors: [rows x 16 * CPL] at leading dimension err_ld
+  int64_t err_ld;
   double* row_loss;      // [rows]
 };
 
@@ -189,7 +190,7 @@ __global__ __launch_bounds__(256) void quant_block_kernel(QArgs a) {
 
   if (row_ok) {
     uint8_t* crow = a.codes_p + row * a.d + a.b;
-    float* erow = a.err + row * BP;
+    float* erow = a.err + row * a.err_ld;
 #pragma unroll
     for (int t = 0; t < CPL; ++t) {
       const int j = lr * CPL + t;
@@ -322,8 +323,22 @@ void launch_block(const QArgs& a, hipStream_t s) {
 }
 
 int cpl_for(int B) { return B <= 16 ? 1 : B <= 32 ? 2 : B <= 64 ? 4 : 8; }
+int64_t super_width_max(int B) { return std::max<int64_t>(1, 512 / B) * B; }
 
 }  // namespace
+
+// Width of a super-block: the lazy updates of a block reach only the rest of its super-block, and
+// the columns beyond are updated once per super-block (a product over the super-block's width
+// instead of one per block). A group wider than a block reads columns that still lack the
+// super-block's deferred updates unless groups and super-blocks nest, so the width is chosen to
+// nest with such groups (a single group per row starts before any update and needs nothing).
+int64_t super_width(int B, int64_t g, int64_t d) {
+  for (int64_t m = std::max<int64_t>(1, 512 / B); m >= 1; --m) {
+    const int64_t sw = m * B;
+    if (g <= B || g >= d || sw % g == 0 || g % sw == 0) return sw;
+  }
+  return B;
+}
 
 QuantLayout quant_layout(int64_t rows, int64_t d, int block) {
   QuantLayout L;
@@ -333,7 +348,9 @@ QuantLayout quant_layout(int64_t rows, int64_t d, int block) {
   size_t o = 0;
   L.off_wp = o; o = up(o + (size_t)rows * L.ldw * sizeof(float));
   L.off_codes = o; o = up(o + (size_t)rows * d);
-  L.off_err = o; o = up(o + (size_t)rows * L.bp * sizeof(float));
+  // errors of one super-block (the last block writes up to bp columns past its start)
+  L.ld_err = (super_width_max(block) + L.bp + 3) / 4 * 4;
+  L.off_err = o; o = up(o + (size_t)rows * L.ld_err * sizeof(float));
   L.off_loss = o; o = up(o + (size_t)rows * sizeof(double));
   L.off_iperm = o; o = up(o + (size_t)d * sizeof(int32_t));
   L.total = o;
@@ -362,30 +379,38 @@ hipError_t quantize(const void* W, int w_dtype, int64_t rows, int64_t d, int64_t
   }
   hipError_t e;
   const int cpl = cpl_for(B);
-  for (int64_t b = 0; b < d && rows > 0; b += B) {
-    const int nc = (int)std::min<int64_t>(B, d - b);
-    const bool in_block = g <= B;
-    if (!in_block && b % g == 0) {
-      hipLaunchKernelGGL(group_grid_kernel, dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, s, Wp, L.ldw, rows, b,
-                         std::min<int64_t>(g, d - b), maxq, b / g, scales, zeros, ngroups);
+  const int64_t sw = super_width(B, g, d);
+  GemmArgs t{};  // W[:, c0:c1] -= Err U[rows of the errors, c0:c1]
+  t.M = rows; t.transA = 0; t.ldb = d; t.transB = 0; t.ldc = L.ldw;
+  t.alpha = -1.0f; t.beta = 1.0f; t.tri = 0; t.lda = L.ld_err;
+  for (int64_t s0 = 0; s0 < d && rows > 0; s0 += sw) {
+    const int64_t s1 = std::min(d, s0 + sw);
+    for (int64_t b = s0; b < s1; b += B) {
+      const int nc = (int)std::min<int64_t>(B, d - b);
+      const bool in_block = g <= B;
+      if (!in_block && b % g == 0) {
+        hipLaunchKernelGGL(group_grid_kernel, dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, s, Wp, L.ldw, rows, b,
+                           std::min<int64_t>(g, d - b), maxq, b / g, scales, zeros, ngroups);
+      }
+      QArgs a;
+      a.Wp = Wp; a.ldw = L.ldw; a.rows = rows; a.d = d; a.b = b; a.ncols = nc; a.U = U; a.g = g;
+      a.grid_in_block = in_block; a.maxq = maxq; a.codes_p = codes_p; a.scales = scales; a.zeros = zeros;
+      a.ngroups = ngroups; a.err = err + (b - s0); a.err_ld = L.ld_err; a.row_loss = row_loss;
+      switch (cpl) {
+        case 1: launch_block<1>(a, s); break;
+        case 2: launch_block<2>(a, s); break;
+        case 4: launch_block<4>(a, s); break;
+        default: launch_block<8>(a, s); break;
+      }
+      if (b + nc < s1) {  // lazy batch inside the super-block
+        t.N = s1 - b - nc; t.K = nc;
+        t.A = err + (b - s0); t.B = U + b * d + b + nc; t.C = Wp + b + nc;
+        if ((e = gemm_f32(t, s)) != hipSuccess) return e;
+      }
     }
-    QArgs a;
-    a.Wp = Wp; a.ldw = L.ldw; a.rows = rows; a.d = d; a.b = b; a.ncols = nc; a.U = U; a.g = g;
-    a.grid_in_block = in_block; a.maxq = maxq; a.codes_p = codes_p; a.scales = scales; a.zeros = zeros;
-    a.ngroups = ngroups; a.err = err; a.row_loss = row_loss;
-    switch (cpl) {
-      case 1: launch_block<1>(a, s); break;
-      case 2: launch_block<2>(a, s); break;
-      case 4: launch_block<4>(a, s); break;
-      default: launch_block<8>(a, s); break;
-    }
-    if (b + nc < d) {
-      GemmArgs t{};  // lazy batch: W[:, b+nc:] -= Err U[b:b+nc, b+nc:]
-      t.M = rows; t.N = d - b - nc; t.K = nc;
-      t.A = err; t.lda = L.bp; t.transA = 0;
-      t.B = U + b * d + b + nc; t.ldb = d; t.transB = 0;
-      t.C = Wp + b + nc; t.ldc = L.ldw;
-      t.alpha = -1.0f; t.beta = 1.0f; t.tri = 0;
+    if (s1 < d) {  // the super-block's errors to every later column at once
+      t.N = d - s1; t.K = s1 - s0;
+      t.A = err; t.B = U + s0 * d + s1; t.C = Wp + s1;
       if ((e = gemm_f32(t, s)) != hipSuccess) return e;
     }
   }
