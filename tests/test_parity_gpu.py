@@ -216,6 +216,8 @@ QCASES = [
     dict(bits=4, group_size=50, block_size=100, d=300),
     dict(bits=8, group_size=64, block_size=128),
     dict(bits=4, group_size=128, block_size=8),
+    dict(bits=4, group_size=384, block_size=128, d=1000),   # super-blocks narrowed to nest with groups
+    dict(bits=4, group_size=200, block_size=100, d=700),    # padded error slots overlap the next block's
 ]
 
 
