@@ -110,7 +110,7 @@ gptq_status_t gptq_hessian_accumulate(float *H, int64_t d, const void *X, int32_
  *            columns by descending diag(H), equal values by lower index first.
  *   work     device workspace of at least gptq_workspace_bytes(GPTQ_WS_FACTOR, 0, d, p) bytes.
  *   info     host int64 output: 0 on success; k > 0 when the k-th pivot (1-based, in the reversed
- *            order the factorization runs in) was not positive.
+ *            order the factorization runs in) was not positive (U is then unspecified).
  * This call waits for the stream once, to read the pivot check. Returns GPTQ_ENOTPD when info != 0
  * (damping "helps but does not fix" a rank-deficient Hessian: retry with a larger damp), GPTQ_EINVAL
  * when mean(diag(H)) is not positive and finite.

@@ -16,6 +16,8 @@
 // update, the triangular-inverse products) is an fp32 MFMA GEMM on the whole device.
 #include "common.hpp"
 
+#include <cfloat>
+
 namespace gptq {
 namespace {
 
@@ -81,29 +83,44 @@ __global__ __launch_bounds__(256) void rank_perm_kernel(const float* __restrict_
   if (i < d) perm[rank] = (int32_t)i;
 }
 
-// dst[r][c] = src[r][c] for a rows x cols block (leading dimensions ldd, lds); used to stage the
-// operand of a product whose output overwrites it. One thread per 4 consecutive elements of a row,
-// moved as one 16-byte access when both sides allow it.
-__global__ __launch_bounds__(256) void copy2d_kernel(float* __restrict__ dst, int64_t ldd, const float* __restrict__ src,
-                                                     int64_t lds, int64_t rows, int64_t cols, int vec) {
-  const int64_t c4 = (cols + 3) / 4, total = rows * c4;
-  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < total; i += (int64_t)gridDim.x * 256) {
-    const int64_t r = i / c4, c = (i % c4) * 4;
-    if (vec && c + 4 <= cols) {
-      *reinterpret_cast<float4*>(dst + r * ldd + c) = *reinterpret_cast<const float4*>(src + r * lds + c);
+// dst[r][c] = src[r][c] for a rows x cols block (leading dimensions ldd, lds); stages the operand of a
+// product whose output overwrites it. Unit `part` of `nparts` moves every nparts-th group of 256
+// four-element row pieces, as 16-byte accesses when both sides allow it.
+struct Copy2D {
+  float* dst;
+  const float* src;
+  int64_t ldd, lds, rows, cols;
+  int vec;
+};
+
+GPTQ_DEV void copy_part(const Copy2D& c, int64_t part, int64_t nparts) {
+  const int64_t c4 = (c.cols + 3) / 4, total = c.rows * c4;
+  for (int64_t i = part * 256 + threadIdx.x; i < total; i += nparts * 256) {
+    const int64_t r = i / c4, col = (i % c4) * 4;
+    if (c.vec && col + 4 <= c.cols) {
+      *reinterpret_cast<float4*>(c.dst + r * c.ldd + col) = *reinterpret_cast<const float4*>(c.src + r * c.lds + col);
     } else {
-      for (int64_t e = c; e < cols && e < c + 4; ++e) dst[r * ldd + e] = src[r * lds + e];
+      for (int64_t e = col; e < c.cols && e < col + 4; ++e) c.dst[r * c.ldd + e] = c.src[r * c.lds + e];
     }
   }
 }
 
-hipError_t copy2d(float* dst, int64_t ldd, const float* src, int64_t lds, int64_t rows, int64_t cols, hipStream_t s) {
-  if (rows <= 0 || cols <= 0) return hipSuccess;
-  const int vec = (uintptr_t)dst % 16 == 0 && (uintptr_t)src % 16 == 0 && ldd % 4 == 0 && lds % 4 == 0;
-  const int64_t work = rows * ((cols + 3) / 4);
-  const unsigned grid = (unsigned)std::min<int64_t>((work + 255) / 256, 4096);
-  hipLaunchKernelGGL(copy2d_kernel, dim3(grid), dim3(256), 0, s, dst, ldd, src, lds, rows, cols, vec);
-  return hipGetLastError();
+Copy2D make_copy(float* dst, int64_t ldd, const float* src, int64_t lds, int64_t rows, int64_t cols) {
+  Copy2D c{dst, src, ldd, lds, std::max<int64_t>(rows, 0), std::max<int64_t>(cols, 0), 0};
+  c.vec = (uintptr_t)dst % 16 == 0 && (uintptr_t)src % 16 == 0 && ldd % 4 == 0 && lds % 4 == 0;
+  return c;
+}
+
+// Workgroups for a copy of `rows` rows of up to NB columns (one per 4096 four-element pieces).
+unsigned copy_groups(int64_t rows, int64_t cols) {
+  const int64_t pieces = std::max<int64_t>(rows, 0) * ((std::max<int64_t>(cols, 0) + 3) / 4);
+  return (unsigned)std::min<int64_t>((pieces + 4095) / 4096, 1024);
+}
+
+// Two independent copies in one launch: blocks [0, g0) take the first, the rest the second.
+__global__ __launch_bounds__(256) void copy2_kernel(Copy2D c0, Copy2D c1, unsigned g0) {
+  if (blockIdx.x < g0) copy_part(c0, blockIdx.x, g0);
+  else copy_part(c1, blockIdx.x - g0, gridDim.x - g0);
 }
 
 __global__ void iota_kernel(int32_t* perm, int64_t d) {
@@ -132,118 +149,308 @@ __global__ __launch_bounds__(256) void gather_kernel(const float* __restrict__ H
 // ---------------------------------------------------------------- diagonal block: factor + inverse
 //
 // The 128 x 128 diagonal block is factored and inverted in LDS by one 256-thread workgroup, blocked
-// by 16: for each 16-column sub-panel, one wave factors and inverts the 16 x 16 diagonal sub-block
-// in registers (lane i holds row i; every value a lane needs from another lane arrives by a DPP
-// row broadcast, so a column step costs a few VALU latencies), then the four waves apply the
-// sub-panel solve and the symmetric update to the rest of the block as 16 x 16 MFMA tiles. The
-// off-diagonal blocks of the inverse follow from block forward substitution,
-// X_qp = -X_qq sum_{t=p}^{q-1} L_qt X_tp, again as MFMA tiles.
+// by 16. One wave factors and inverts each 16 x 16 diagonal sub-block in registers (every value a
+// lane needs from another lane arrives by a DPP row broadcast). Everything else is 16 x 16 MFMA
+// tiles on the four waves, in two phases per sub-block step p:
+//   A: the sub-panel solve L_qp = A_qp X_pp^T (q > p), and the finished blocks of row p of the
+//      inverse, X_pj = -X_pp W_pj (j < p);
+//   B: the symmetric update A_qr -= L_qp L_rp^T (p < r <= q) and the inverse's right-looking update
+//      W_qj += L_qp X_pj (q > p, j <= p), where W_qj = sum_{t=j}^{q-1} L_qt X_tj accumulates in the
+//      inverse's own tile (block forward substitution for L^-1, X_qj = -X_qq W_qj). Wave 0 instead
+//      updates tile (p + 1, p + 1) and factors sub-block p + 1 while waves 1..3 do the rest.
 constexpr int LDB = NB + 4;   // LDS leading dimension: 16 x 16 tiles read by rows or columns are conflict-free
 constexpr int SB = 16;        // sub-block
+constexpr int NS = NB / SB;   // sub-blocks per block
 constexpr int LDT = SB + 1;   // per-wave temporary tile
 
-// acc (+)= sa op(A) op(B) over K (a multiple of 4) for one 16 x 16 tile; A, B in LDS. op(A): A[i][k]
-// or (TA) A[k][i]; op(B): B[k][j] or (TB) B[j][k]. One wave: v_mfma_f32_16x16x4f32 takes
-// A[l % 16][k + l / 16] and B[k + l / 16][l % 16] from lane l.
-template <bool TA, bool TB>
-GPTQ_DEV floatx4 mma16(floatx4 acc, const float* A, int lda, const float* B, int ldb, int K, int lane,
-                       float sa = 1.0f) {
-  const int r = lane & 15, kk = lane >> 4;
-  for (int k = 0; k < K; k += 4) {
-    const float av = TA ? A[(k + kk) * lda + r] : A[r * lda + k + kk];
-    const float bv = TB ? B[r * ldb + k + kk] : B[(k + kk) * ldb + r];
-    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(sa * av, bv, acc, 0, 0, 0);
-  }
-  return acc;
-}
-
 // Register r of lane l of a 16 x 16 MFMA result holds row 4 (l / 16) + r, column l % 16.
-GPTQ_DEV floatx4 tile_load(const float* T, int ld, int lane) {
+GPTQ_DEV floatx4 tile_load(const float* T, int lane) {
   floatx4 v;
 #pragma unroll
-  for (int r = 0; r < 4; ++r) v[r] = T[(4 * (lane >> 4) + r) * ld + (lane & 15)];
+  for (int r = 0; r < 4; ++r) v[r] = T[(4 * (lane >> 4) + r) * LDB + (lane & 15)];
   return v;
 }
 
-GPTQ_DEV void tile_store(float* T, int ld, int lane, floatx4 v, float scale = 1.0f) {
+GPTQ_DEV void tile_store(float* T, int lane, floatx4 v) {
 #pragma unroll
-  for (int r = 0; r < 4; ++r) T[(4 * (lane >> 4) + r) * ld + (lane & 15)] = scale * v[r];
+  for (int r = 0; r < 4; ++r) T[(4 * (lane >> 4) + r) * LDB + (lane & 15)] = v[r];
 }
 
-GPTQ_DEV floatx4 zero4() { return floatx4{0.0f, 0.0f, 0.0f, 0.0f}; }
+// One tile product in LDS: C = (acc ? C : 0) + sgn * A op(B), with op(B) = B^T (bt) or B, all
+// 16 x 16 tiles with leading dimension LDB (offsets in floats from the LDS base). C may be A or B
+// (acc = 0 then): every read of a task precedes its store.
+struct TileTask {
+  int c, a, b, bt, acc;
+  float sgn;
+};
 
-// One wave: Cholesky factor of the 16 x 16 lower block at S (in place) and its inverse into Xs.
-// Lane i holds row i of the block and row i of the inverse in registers (each 16-lane row of the
-// wave computes the same thing). Column step j computes l_jj and column j of the factor; the same
-// step is the j-th step of forward elimination for the inverse (row j of L^-1 is final once divided
-// by l_jj, then rows i > j subtract l_ij times it). The pivot, column j of L and row j of L^-1
-// reach the other lanes by DPP row broadcasts, and no step branches. Entries above the diagonal
-// are never read and are zeroed on the way out. A non-positive pivot is recorded in info (1-based
-// index gbase + j + 1, when the column is real, j < valid) and replaced by 1.
-GPTQ_DEV void chol_inv16(float* S, float* Xs, int lane, int64_t* info, int64_t gbase, int valid) {
-  const int i = lane & 15;
-  float a[SB], x[SB];
+// v_mfma_f32_16x16x4f32 takes A[l % 16][k + l / 16] and B[k + l / 16][l % 16] from lane l. All of a
+// task's operands are read before its first MFMA, so the LDS latency is paid once per task.
+struct TileOps {
+  float a[4], b[4];
+  floatx4 c;
+};
+
+GPTQ_DEV TileOps tile_fetch(const float* sm, const TileTask& t, int lane) {
+  TileOps o;
+  const int r = lane & 15, kk = lane >> 4;
+  const float* pa = sm + t.a + r * LDB + kk;
+  const float* pb = sm + t.b + (t.bt ? r * LDB + kk : kk * LDB + r);
+  const int sb = t.bt ? 4 : 4 * LDB;
 #pragma unroll
-  for (int c = 0; c < SB; ++c) {
-    a[c] = (c <= i) ? S[i * LDB + c] : 0.0f;
-    x[c] = (c == i) ? 1.0f : 0.0f;
+  for (int k = 0; k < 4; ++k) {
+    o.a[k] = pa[4 * k];
+    o.b[k] = pb[k * sb];
   }
-  int bad = SB;   // first non-positive pivot
-  static_for<0, SB>([&](auto jc) {
-    constexpr int j = decltype(jc)::value;
-    float p = row_bcast<j>(a[j]);
-    const bool ok = p > 0.0f;
-    bad = (!ok && j < bad) ? j : bad;
-    p = ok ? p : 1.0f;
-    const float r = __builtin_amdgcn_rsqf(p);   // 1 / l_jj
-    const float lij = a[j] * r;                 // l_ij for rows i > j
-    const float sx = (i == j) ? r : 1.0f;
+  o.c = t.acc ? tile_load(sm + t.c, lane) : floatx4{0.0f, 0.0f, 0.0f, 0.0f};
+  return o;
+}
+
+GPTQ_DEV floatx4 tile_mma(const TileOps& o, float sgn) {
+  floatx4 acc = o.c;
 #pragma unroll
-    for (int c = 0; c <= j; ++c) x[c] *= sx;
-    a[j] = (i > j) ? lij : ((i == j) ? p * r : 0.0f);
-    static_for<j + 1, SB>([&](auto cc) {
-      constexpr int c = decltype(cc)::value;
-      a[c] = __builtin_fmaf(-lij, row_bcast<c>(lij), a[c]);
-    });
-    const float lx = (i > j) ? lij : 0.0f;
-    static_for<0, j + 1>([&](auto cc) {
-      constexpr int c = decltype(cc)::value;
-      x[c] = __builtin_fmaf(-lx, row_bcast<j>(x[c]), x[c]);
-    });
-  });
-  if (bad < SB && bad < valid && lane == 0 && *info == 0) *info = gbase + bad + 1;
-  if (lane < SB) {
-#pragma unroll
-    for (int c = 0; c < SB; ++c) {
-      S[i * LDB + c] = (c <= i) ? a[c] : 0.0f;
-      Xs[i * LDB + c] = (c <= i) ? x[c] : 0.0f;
+  for (int k = 0; k < 4; ++k) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(sgn * o.a[k], o.b[k], acc, 0, 0, 0);
+  return acc;
+}
+
+GPTQ_DEV void run_task(float* sm, const TileTask& t, int lane) {
+  const TileOps o = tile_fetch(sm, t, lane);
+  __builtin_amdgcn_sched_barrier(0);
+  tile_store(sm + t.c, lane, tile_mma(o, t.sgn));
+}
+
+// Two independent tasks at once, so that the loads and MFMAs of both overlap.
+GPTQ_DEV void run_task2(float* sm, const TileTask& t0, const TileTask& t1, int lane) {
+  const TileOps o0 = tile_fetch(sm, t0, lane);
+  const TileOps o1 = tile_fetch(sm, t1, lane);
+  __builtin_amdgcn_sched_barrier(0);   // every read ahead of the first MFMA
+  const floatx4 r0 = tile_mma(o0, t0.sgn);
+  const floatx4 r1 = tile_mma(o1, t1.sgn);
+  tile_store(sm + t0.c, lane, r0);
+  tile_store(sm + t1.c, lane, r1);
+}
+
+// Runs the tasks a wave is given (a wave-uniform list) two at a time. No task of one phase reads a
+// tile that another task of the phase writes.
+struct TaskPair {
+  float* sm;
+  int lane, have;
+  TileTask held;
+  GPTQ_DEV void push(const TileTask& t) {
+    if (have) {
+      run_task2(sm, held, t, lane);
+      have = 0;
+    } else {
+      held = t;
+      have = 1;
     }
   }
+  GPTQ_DEV void flush() {
+    if (have) run_task(sm, held, lane);
+    have = 0;
+  }
+};
+
+// Column step J's updates of the 16 x 16 factor-and-inverse (see chol_inv16) as one block of DPP
+// multiply-adds: a[c] -= (lane c's l) * l for c > J, and y[k] -= (lane J's y[k]) * m for the
+// columns 4k + g that row J can reach (4k <= J). A DPP read needs two wait states after a VALU
+// write of its source, which the compiler does not track through inline assembly: the leading s_nop
+// covers the sources written before the block (none is written inside it), the trailing one covers
+// a DPP read of the block's results right after it.
+#define FA(c) "v_fmac_f32_dpp %[a" #c "], -%[l], %[l] row_newbcast:" #c " row_mask:0xf bank_mask:0xf bound_ctrl:1\n\t"
+#define FY(k, j) "v_fmac_f32_dpp %[y" #k "], %[y" #k "], -%[m] row_newbcast:" #j " row_mask:0xf bank_mask:0xf bound_ctrl:1\n\t"
+#define CHOL16_OPERANDS                                                                                     \
+  [a0] "+v"(a[0]), [a1] "+v"(a[1]), [a2] "+v"(a[2]), [a3] "+v"(a[3]), [a4] "+v"(a[4]), [a5] "+v"(a[5]),     \
+      [a6] "+v"(a[6]), [a7] "+v"(a[7]), [a8] "+v"(a[8]), [a9] "+v"(a[9]), [a10] "+v"(a[10]),               \
+      [a11] "+v"(a[11]), [a12] "+v"(a[12]), [a13] "+v"(a[13]), [a14] "+v"(a[14]), [a15] "+v"(a[15]),       \
+      [y0] "+v"(y[0]), [y1] "+v"(y[1]), [y2] "+v"(y[2]), [y3] "+v"(y[3])                                  \
+      : [l] "v"(l), [m] "v"(m)
+template <int J>
+GPTQ_DEV void chol16_step(float (&a)[SB], float (&y)[4], float l, float m) {
+  if constexpr (J == 0) asm("s_nop 1\n\t" FA(1) FA(2) FA(3) FA(4) FA(5) FA(6) FA(7) FA(8) FA(9) FA(10) FA(11) FA(12) FA(13) FA(14) FA(15) FY(0, 0) "s_nop 1" : CHOL16_OPERANDS);
+  if constexpr (J == 1) asm("s_nop 1\n\t" FA(2) FA(3) FA(4) FA(5) FA(6) FA(7) FA(8) FA(9) FA(10) FA(11) FA(12) FA(13) FA(14) FA(15) FY(0, 1) "s_nop 1" : CHOL16_OPERANDS);
+  if constexpr (J == 2) asm("s_nop 1\n\t" FA(3) FA(4) FA(5) FA(6) FA(7) FA(8) FA(9) FA(10) FA(11) FA(12) FA(13) FA(14) FA(15) FY(0, 2) "s_nop 1" : CHOL16_OPERANDS);
+  if constexpr (J == 3) asm("s_nop 1\n\t" FA(4) FA(5) FA(6) FA(7) FA(8) FA(9) FA(10) FA(11) FA(12) FA(13) FA(14) FA(15) FY(0, 3) "s_nop 1" : CHOL16_OPERANDS);
+  if constexpr (J == 4) asm("s_nop 1\n\t" FA(5) FA(6) FA(7) FA(8) FA(9) FA(10) FA(11) FA(12) FA(13) FA(14) FA(15) FY(0, 4) FY(1, 4) "s_nop 1" : CHOL16_OPERANDS);
+  if constexpr (J == 5) asm("s_nop 1\n\t" FA(6) FA(7) FA(8) FA(9) FA(10) FA(11) FA(12) FA(13) FA(14) FA(15) FY(0, 5) FY(1, 5) "s_nop 1" : CHOL16_OPERANDS);
+  if constexpr (J == 6) asm("s_nop 1\n\t" FA(7) FA(8) FA(9) FA(10) FA(11) FA(12) FA(13) FA(14) FA(15) FY(0, 6) FY(1, 6) "s_nop 1" : CHOL16_OPERANDS);
+  if constexpr (J == 7) asm("s_nop 1\n\t" FA(8) FA(9) FA(10) FA(11) FA(12) FA(13) FA(14) FA(15) FY(0, 7) FY(1, 7) "s_nop 1" : CHOL16_OPERANDS);
+  if constexpr (J == 8) asm("s_nop 1\n\t" FA(9) FA(10) FA(11) FA(12) FA(13) FA(14) FA(15) FY(0, 8) FY(1, 8) FY(2, 8) "s_nop 1" : CHOL16_OPERANDS);
+  if constexpr (J == 9) asm("s_nop 1\n\t" FA(10) FA(11) FA(12) FA(13) FA(14) FA(15) FY(0, 9) FY(1, 9) FY(2, 9) "s_nop 1" : CHOL16_OPERANDS);
+  if constexpr (J == 10) asm("s_nop 1\n\t" FA(11) FA(12) FA(13) FA(14) FA(15) FY(0, 10) FY(1, 10) FY(2, 10) "s_nop 1" : CHOL16_OPERANDS);
+  if constexpr (J == 11) asm("s_nop 1\n\t" FA(12) FA(13) FA(14) FA(15) FY(0, 11) FY(1, 11) FY(2, 11) "s_nop 1" : CHOL16_OPERANDS);
+  if constexpr (J == 12) asm("s_nop 1\n\t" FA(13) FA(14) FA(15) FY(0, 12) FY(1, 12) FY(2, 12) FY(3, 12) "s_nop 1" : CHOL16_OPERANDS);
+  if constexpr (J == 13) asm("s_nop 1\n\t" FA(14) FA(15) FY(0, 13) FY(1, 13) FY(2, 13) FY(3, 13) "s_nop 1" : CHOL16_OPERANDS);
+  if constexpr (J == 14) asm("s_nop 1\n\t" FA(15) FY(0, 14) FY(1, 14) FY(2, 14) FY(3, 14) "s_nop 1" : CHOL16_OPERANDS);
+  if constexpr (J == 15) asm("s_nop 1\n\t" FY(0, 15) FY(1, 15) FY(2, 15) FY(3, 15) "s_nop 1" : CHOL16_OPERANDS);
+}
+#undef FA
+#undef FY
+#undef CHOL16_OPERANDS
+
+// One wave: Cholesky factor of the 16 x 16 lower block at S (in place) and its inverse into Xs.
+// Lane l holds row i = l % 16 of the block in registers (the four 16-lane groups alike) and a
+// quarter of row i of the inverse: group g = l / 16 holds columns 4k + g, k = 0..3. Column step j
+// computes r_j = 1 / l_jj and column j of the factor; the same step is the j-th step of forward
+// elimination for the inverse, kept with a unit diagonal (rows i > j subtract l_ij r_j times row j)
+// and scaled by 1 / l_ii at the end, which gives the same rows as dividing row j by l_jj at its
+// step. The pivot, column j of L and row j of the inverse reach the other lanes by DPP row
+// broadcasts, and no step branches. Entries above the diagonal hold unread values and are zeroed on
+// the way out. A pivot that is not positive gives l_jj <= 0 (or NaN); the first one is recorded in
+// info (1-based index gbase + j + 1, when the column is real, j < valid), and the rest of the block
+// is then unspecified.
+GPTQ_DEV void chol_inv16(float* S, float* Xs, int lane, int64_t* info, int64_t gbase, int valid) {
+  int ln = lane;
+  asm("" : "+v"(ln));   // row tests derived per call, not hoisted out of the caller's loop
+  const int i = ln & 15, g = ln >> 4;
+  float a[SB], y[4], below[SB];
+#pragma unroll
+  for (int c = 0; c < SB; ++c) {
+    const float v = S[i * LDB + c];
+    a[c] = (c <= i) ? v : 0.0f;
+    below[c] = (i > c) ? 1.0f : 0.0f;
+    asm("" : "+v"(below[c]));   // used as a multiplier, not turned back into a select
+  }
+#pragma unroll
+  for (int k = 0; k < 4; ++k) y[k] = (4 * k + g == i) ? 1.0f : 0.0f;
+  static_for<0, SB>([&](auto jc) {
+    constexpr int j = decltype(jc)::value;
+    const float p = row_bcast<j>(a[j]);
+    const float r = fminf(__builtin_amdgcn_rsqf(p), FLT_MAX);   // 1 / l_jj (finite for any pivot)
+    const float l = a[j] * r;                                    // l_ij
+    const float m = l * r * below[j];                            // l_ij / l_jj for rows i > j, else 0
+    a[j] = l;
+    chol16_step<j>(a, y, l, m);
+  });
+  int ie = i;
+  asm("" : "+v"(ie));   // fresh row tests for the stores (the load's would stay live throughout)
+  if (lane < SB) {
+#pragma unroll
+    for (int c = 0; c < SB; ++c) S[ie * LDB + c] = (c <= ie) ? a[c] : 0.0f;
+  }
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+  __builtin_amdgcn_wave_barrier();
+  const float lii = S[ie * LDB + ie];
+  // first non-positive pivot (lanes 0..15 hold steps 0..15)
+  const uint64_t badm = __builtin_amdgcn_ballot_w64(!(lii > 0.0f)) & 0xFFFFull;
+  const int bad = badm ? __builtin_ctzll(badm) : SB;
+  if (bad < SB && bad < valid && lane == 0 && *info == 0) *info = gbase + bad + 1;
+  const float ri = __builtin_amdgcn_rcpf(lii);
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const int c = 4 * k + g;
+    Xs[ie * LDB + c] = (c <= ie) ? y[k] * ri : 0.0f;
+  }
 }
 
-// Factors the diagonal block at (k0, k0) (A = L L^T, lower) and replaces the whole block in A by the
-// inverse of L (lower triangle; zeros above). A last block narrower than NB is padded with an
-// identity, which leaves the factor and inverse of the real part unchanged.
+GPTQ_DEV int tile_off(int base, int q, int r) { return base + (SB * q) * LDB + SB * r; }
+
+// Block (q, pb) of the inverse, X_qp = -X_qq sum_{t=pb}^{q-1} L_qt X_tp, by one wave; T is the wave's
+// 16 x 16 temporary (leading dimension LDT). The operands of two terms are read before their MFMAs.
+GPTQ_DEV void inv_tile(float* sm, float* T, int q, int pb, int lane) {
+  const int LA = 0, XA = NB * LDB;
+  const int r = lane & 15, kk = lane >> 4;
+  floatx4 acc = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
+  int t = pb;
+  for (; t + 1 < q; t += 2) {
+    const float* a0 = sm + tile_off(LA, q, t) + r * LDB + kk;
+    const float* b0 = sm + tile_off(XA, t, pb) + kk * LDB + r;
+    const float* a1 = a0 + SB;
+    const float* b1 = sm + tile_off(XA, t + 1, pb) + kk * LDB + r;
+    float av0[4], bv0[4], av1[4], bv1[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      av0[k] = a0[4 * k];
+      bv0[k] = b0[4 * k * LDB];
+      av1[k] = a1[4 * k];
+      bv1[k] = b1[4 * k * LDB];
+    }
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int k = 0; k < 4; ++k) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(av0[k], bv0[k], acc, 0, 0, 0);
+#pragma unroll
+    for (int k = 0; k < 4; ++k) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(av1[k], bv1[k], acc, 0, 0, 0);
+  }
+  if (t < q) {
+    const float* a0 = sm + tile_off(LA, q, t) + r * LDB + kk;
+    const float* b0 = sm + tile_off(XA, t, pb) + kk * LDB + r;
+    float av0[4], bv0[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      av0[k] = a0[4 * k];
+      bv0[k] = b0[4 * k * LDB];
+    }
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int k = 0; k < 4; ++k) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(av0[k], bv0[k], acc, 0, 0, 0);
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) T[(4 * kk + i) * LDT + r] = acc[i];
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+  __builtin_amdgcn_wave_barrier();
+  const float* xq = sm + tile_off(XA, q, q) + r * LDB + kk;
+  float av[4], bv[4];
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    av[k] = xq[4 * k];
+    bv[k] = T[(4 * k + kk) * LDT + r];
+  }
+  __builtin_amdgcn_sched_barrier(0);
+  acc = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+  for (int k = 0; k < 4; ++k) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(-av[k], bv[k], acc, 0, 0, 0);
+  tile_store(sm + tile_off(XA, q, pb), lane, acc);
+  __builtin_amdgcn_wave_barrier();   // T is reused by this wave's next tile
+}
+
+// Block row q of the inverse (blocks pb < q) on waves w = 0..nw-1: the chains are q - pb terms long,
+// dealt longest first to the least-loaded wave (every wave computes the same deal).
+GPTQ_DEV void inv_row(float* sm, float* T, int q, int w, int nw, int lane) {
+  int load[4] = {0, 0, 0, 0};
+  for (int pb = 0; pb < q; ++pb) {
+    int best = 0;
+    for (int u = 1; u < nw; ++u) best = load[u] < load[best] ? u : best;
+    load[best] += q - pb + 1;
+    if (best == w) inv_tile(sm, T, q, pb, lane);
+  }
+}
+
+// Workgroup 0 factors the diagonal block at (k0, k0) (A = L L^T, lower) and replaces the whole block
+// in A by the inverse of L (lower triangle; zeros above). A last block narrower than NB is padded with
+// an identity, which leaves the factor and inverse of the real part unchanged. vec: A and d allow
+// 16-byte row accesses. Workgroups 1.. copy `panel` (the column panel below the block, which the
+// diagonal workgroup does not touch) to its staging buffer.
 __global__ __launch_bounds__(256) void chol_diag_kernel(float* __restrict__ A, int64_t d, int64_t k0, int nb,
-                                                        int64_t* __restrict__ info) {
+                                                        int vec, int64_t* __restrict__ info, Copy2D panel) {
+  if (blockIdx.x > 0) {   // the other workgroups stage the column panel below the block
+    copy_part(panel, blockIdx.x - 1, gridDim.x - 1);
+    return;
+  }
   extern __shared__ float sm[];
   float* La = sm;                 // [NB][LDB]: the block, then its Cholesky factor
   float* Xa = sm + NB * LDB;      // [NB][LDB]: the inverse of the factor
   float* Tt = sm + 2 * NB * LDB;  // [4][SB][LDT]: per-wave temporaries
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform: task loops branch on scalars
   constexpr int PER = NB * NB / 256;
-  if (nb == NB) {
-    float v[PER];
+  constexpr int PER4 = PER / 4;
+  if (nb == NB && vec) {
+    float4 v[PER4];
 #pragma unroll
-    for (int q = 0; q < PER; ++q) {
-      const int e = tid + q * 256, r = e / NB, c = e % NB;
-      v[q] = A[(k0 + r) * d + k0 + c];
+    for (int q = 0; q < PER4; ++q) {
+      const int e = tid + q * 256, r = e / (NB / 4), c = e % (NB / 4) * 4;
+      v[q] = *reinterpret_cast<const float4*>(A + (k0 + r) * d + k0 + c);
     }
 #pragma unroll
-    for (int q = 0; q < PER; ++q) {
-      const int e = tid + q * 256, r = e / NB, c = e % NB;
-      La[r * LDB + c] = (c <= r) ? v[q] : 0.0f;
-      Xa[r * LDB + c] = 0.0f;
+    for (int q = 0; q < PER4; ++q) {
+      const int e = tid + q * 256, r = e / (NB / 4), c = e % (NB / 4) * 4;
+      float4 x = v[q];
+      x.x = (c <= r) ? x.x : 0.0f;
+      x.y = (c + 1 <= r) ? x.y : 0.0f;
+      x.z = (c + 2 <= r) ? x.z : 0.0f;
+      x.w = (c + 3 <= r) ? x.w : 0.0f;
+      *reinterpret_cast<float4*>(La + r * LDB + c) = x;
+      *reinterpret_cast<float4*>(Xa + r * LDB + c) = float4{0.0f, 0.0f, 0.0f, 0.0f};
     }
   } else {
     for (int q = 0; q < PER; ++q) {
@@ -256,55 +463,53 @@ __global__ __launch_bounds__(256) void chol_diag_kernel(float* __restrict__ A, i
   }
   __syncthreads();
 
-  constexpr int NS = NB / SB;
-  for (int p = 0; p < NS; ++p) {
-    float* Dpp = La + (SB * p) * LDB + SB * p;
-    float* Xpp = Xa + (SB * p) * LDB + SB * p;
-    if (wave == 0) chol_inv16(Dpp, Xpp, lane, info, k0 + SB * p, nb - SB * p);
-    __syncthreads();
-    // sub-panel solve: L_qp = A_qp X_pp^T for q > p
-    for (int q = p + 1 + wave; q < NS; q += 4) {
-      float* Aqp = La + (SB * q) * LDB + SB * p;
-      tile_store(Aqp, LDB, lane, mma16<false, true>(zero4(), Aqp, LDB, Xpp, LDB, SB, lane));
+  const int LA = 0, XA = NB * LDB;
+  float* T = Tt + wave * SB * LDT;
+  if (wave == 0) chol_inv16(La, Xa, lane, info, k0, nb);
+  __syncthreads();
+  for (int p = 0; p + 1 < NS; ++p) {
+    {   // sub-panel solve: L_qp = A_qp X_pp^T for q > p
+      TaskPair tp{sm, lane, 0, {}};
+      for (int q = p + 1 + wave; q < NS; q += 4)
+        tp.push(TileTask{tile_off(LA, q, p), tile_off(LA, q, p), tile_off(XA, p, p), 1, 0, 1.0f});
+      tp.flush();
     }
     __syncthreads();
-    // symmetric update: A_qr -= L_qp L_rp^T for p < r <= q
-    {
-      int t = 0;
-      for (int q = p + 1; q < NS; ++q)
-        for (int r = p + 1; r <= q; ++r, ++t) {
-          if (t % 4 != wave) continue;
-          float* Aqr = La + (SB * q) * LDB + SB * r;
-          floatx4 acc = tile_load(Aqr, LDB, lane);
-          acc = mma16<false, true>(acc, La + (SB * q) * LDB + SB * p, LDB, La + (SB * r) * LDB + SB * p, LDB, SB,
-                                   lane, -1.0f);
-          tile_store(Aqr, LDB, lane, acc);
-        }
-    }
-    __syncthreads();
-  }
-  // off-diagonal blocks of the inverse, block row by block row
-  for (int q = 1; q < NS; ++q) {
-    for (int pb = wave; pb < q; pb += 4) {
-      floatx4 acc = zero4();
-      for (int t = pb; t < q; ++t)
-        acc = mma16<false, false>(acc, La + (SB * q) * LDB + SB * t, LDB, Xa + (SB * t) * LDB + SB * pb, LDB, SB,
-                                  lane);
-      float* T = Tt + wave * SB * LDT;
-      tile_store(T, LDT, lane, acc);
+    // symmetric update A_qr -= L_qp L_rp^T for p < r <= q: tile (p + 1, p + 1) and the factor of
+    // sub-block p + 1 on wave 0, the other tiles on waves 1..3
+    if (wave == 0) {
+      run_task(sm, TileTask{tile_off(LA, p + 1, p + 1), tile_off(LA, p + 1, p), tile_off(LA, p + 1, p), 1, 1, -1.0f},
+               lane);
       __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
       __builtin_amdgcn_wave_barrier();
-      acc = mma16<false, false>(zero4(), Xa + (SB * q) * LDB + SB * q, LDB, T, LDT, SB, lane);
-      tile_store(Xa + (SB * q) * LDB + SB * pb, LDB, lane, acc, -1.0f);
-      __builtin_amdgcn_wave_barrier();
+      chol_inv16(La + (SB * (p + 1)) * LDB + SB * (p + 1), Xa + (SB * (p + 1)) * LDB + SB * (p + 1), lane, info,
+                 k0 + SB * (p + 1), nb - SB * (p + 1));
+    } else {
+      TaskPair tp{sm, lane, 0, {}};
+      int t = 0;
+      for (int q = p + 2; q < NS; ++q)
+        for (int r = p + 1; r <= q; ++r, ++t)
+          if (t % 3 == wave - 1)
+            tp.push(TileTask{tile_off(LA, q, r), tile_off(LA, q, p), tile_off(LA, r, p), 1, 1, -1.0f});
+      tp.flush();
+      // block row p of the inverse: its inputs (L_pt for t < p, X_pp, earlier rows) are final, and
+      // nothing else in this phase touches it
+      if (p > 0) inv_row(sm, T, p, wave - 1, 3, lane);
     }
     __syncthreads();
   }
-  if (nb == NB) {
+  inv_row(sm, T, NS - 1, wave, 4, lane);   // the last block row of the inverse
+  __syncthreads();
+  if (nb == NB && vec) {
 #pragma unroll
-    for (int q = 0; q < PER; ++q) {
-      const int e = tid + q * 256, r = e / NB, c = e % NB;
-      A[(k0 + r) * d + k0 + c] = (c <= r) ? Xa[r * LDB + c] : 0.0f;
+    for (int q = 0; q < PER4; ++q) {
+      const int e = tid + q * 256, r = e / (NB / 4), c = e % (NB / 4) * 4;
+      float4 x = *reinterpret_cast<const float4*>(Xa + r * LDB + c);
+      x.x = (c <= r) ? x.x : 0.0f;
+      x.y = (c + 1 <= r) ? x.y : 0.0f;
+      x.z = (c + 2 <= r) ? x.z : 0.0f;
+      x.w = (c + 3 <= r) ? x.w : 0.0f;
+      *reinterpret_cast<float4*>(A + (k0 + r) * d + k0 + c) = x;
     }
   } else {
     for (int q = 0; q < PER; ++q) {
@@ -334,10 +539,11 @@ size_t chol_smem() { return ((size_t)2 * NB * LDB + 4 * SB * LDT) * sizeof(float
 
 }  // namespace
 
-// Workspace: the status words, the sort keys, and two panel buffers of d x NB floats (one per stream)
-// that stage the operand of the three products that overwrite their own input.
+// Workspace: the status words, the sort keys, and three panel buffers of d x NB floats that stage the
+// operand of the three products that overwrite their own input (one on the caller's stream, two on
+// the helper stream).
 size_t factor_keys_bytes(int64_t d) { return ((size_t)d * sizeof(float) + 255) / 256 * 256; }
-size_t factor_workspace_bytes(int64_t d) { return 256 + factor_keys_bytes(d) + 2 * (size_t)d * NB * sizeof(float); }
+size_t factor_workspace_bytes(int64_t d) { return 256 + factor_keys_bytes(d) + 3 * (size_t)d * NB * sizeof(float); }
 
 // Returns hipSuccess after queueing everything; *status_out / *info_out are device addresses of the
 // status word and pivot index (read by the caller after a stream synchronisation).
@@ -350,7 +556,8 @@ hipError_t factor(const float* H, int64_t d, int64_t n, double damp, int act_ord
   w.status = reinterpret_cast<int*>(wb + 16);
   w.keys = reinterpret_cast<float*>(wb + 256);
   float* stage_main = reinterpret_cast<float*>(wb + 256 + factor_keys_bytes(d));   // d x NB, caller's stream
-  float* stage_help = stage_main + d * NB;                                          // d x NB, helper stream
+  float* stage_row = stage_main + d * NB;                                           // NB x d, helper stream
+  float* stage_col = stage_row + d * NB;                                            // d x NB, helper stream
   *status_dev = w.status;
   *info_dev = w.info;
 
@@ -379,13 +586,17 @@ hipError_t factor(const float* H, int64_t d, int64_t n, double damp, int act_ord
   hipEvent_t ev_step = hp->event[4], ev_done = hp->event[5];
   helpers_lock(hp);
   const int64_t nblk = (d + NB - 1) / NB;
+  const int vec = d % 4 == 0 && (uintptr_t)U % 16 == 0;
   for (int64_t k = 0; k < nblk && e == hipSuccess; ++k) {
     const int64_t k0 = k * NB, k1 = std::min(d, k0 + NB), kb = k1 - k0;
-    hipLaunchKernelGGL(chol_diag_kernel, dim3(1), dim3(256), chol_smem(), s, U, d, k0, (int)kb, w.info);
+    // the diagonal block, and the column panel P below it staged for the panel solve (the product's
+    // workgroups of one row strip must not overwrite the columns another one still reads)
+    const Copy2D pc = make_copy(stage_main, kb, U + k1 * d + k0, d, d - k1, kb);
+    hipLaunchKernelGGL(chol_diag_kernel, dim3(1 + copy_groups(d - k1, kb)), dim3(256), chol_smem(), s, U, d, k0,
+                       (int)kb, vec, w.info, pc);
+    if ((e = hipGetLastError()) != hipSuccess) break;
     if (k1 < d) {
-      // panel solve: P <- P L_kk^-T (P staged: workgroups of one row strip must not overwrite the
-      // columns another one still reads)
-      if ((e = copy2d(stage_main, kb, U + k1 * d + k0, d, d - k1, kb, s)) != hipSuccess) break;
+      // panel solve: P <- P L_kk^-T
       GemmArgs t{};
       t.M = d - k1; t.N = kb; t.K = kb;
       t.A = stage_main; t.lda = kb; t.transA = 0;
@@ -407,13 +618,23 @@ hipError_t factor(const float* H, int64_t d, int64_t n, double damp, int act_ord
     // inverse step k on the helper stream (the diagonal block is already inverted)
     if ((e = hipStreamWaitEvent(hs, ev_step, 0)) != hipSuccess) break;
     const int64_t j0 = k0, j1 = k1, jb = kb;
+    {
+      // stage the row panel R = U[j0:j1, :j0] and the column panel L[j1:, j] together: nothing in
+      // this step changes the column panel before its own product
+      const Copy2D rc = make_copy(stage_row, j0, U + j0 * d, d, jb, j0);
+      const Copy2D cc = make_copy(stage_col, jb, U + j1 * d + j0, d, d - j1, jb);
+      const unsigned g0 = copy_groups(jb, j0), g1 = copy_groups(d - j1, jb);
+      if (g0 + g1 > 0) {
+        hipLaunchKernelGGL(copy2_kernel, dim3(g0 + g1), dim3(256), 0, hs, rc, cc, g0);
+        if ((e = hipGetLastError()) != hipSuccess) break;
+      }
+    }
     if (j0 > 0) {
-      // row panel: R <- -X_jj R (R staged)
-      if ((e = copy2d(stage_help, j0, U + j0 * d, d, jb, j0, hs)) != hipSuccess) break;
+      // row panel: R <- -X_jj R
       GemmArgs r{};
       r.M = jb; r.N = j0; r.K = jb;
       r.A = U + j0 * d + j0; r.lda = d; r.transA = 0;
-      r.B = stage_help; r.ldb = j0; r.transB = 0;
+      r.B = stage_row; r.ldb = j0; r.transB = 0;
       r.C = U + j0 * d; r.ldc = d;
       r.alpha = -1.0f; r.beta = 0.0f; r.tri = 0;
       if ((e = gemm_f32(r, hs)) != hipSuccess) break;
@@ -428,11 +649,10 @@ hipError_t factor(const float* H, int64_t d, int64_t n, double damp, int act_ord
       }
     }
     if (j1 < d) {
-      // column panel: L[j1:, j] <- L[j1:, j] X_jj (L[j1:, j] staged)
-      if ((e = copy2d(stage_help, jb, U + j1 * d + j0, d, d - j1, jb, hs)) != hipSuccess) break;
+      // column panel: L[j1:, j] <- L[j1:, j] X_jj
       GemmArgs c{};
       c.M = d - j1; c.N = jb; c.K = jb;
-      c.A = stage_help; c.lda = jb; c.transA = 0;
+      c.A = stage_col; c.lda = jb; c.transA = 0;
       c.B = U + j0 * d + j0; c.ldb = d; c.transB = 0;
       c.C = U + j1 * d + j0; c.ldc = d;
       c.alpha = 1.0f; c.beta = 0.0f; c.tri = 0;
