@@ -17,8 +17,12 @@ those). Compared:
 
 q_proj runs exactly the benchmark's workload (4096 x 4096, 262144 tokens). down_proj keeps its width,
 rows and act-order with 4096 tokens, so the oracle's factor of an 11008-wide Hessian stays affordable;
-its Hessian then takes the path without token splits, as the full token count does.
+its Hessian then takes the path without token splits, as the full token count does. The Llama-7B
+decoder block keeps every layer's rows and width and shares each input's Hessian and factor among the
+layers that read it, with 8192 tokens (4096 for the 11008-wide input).
 """
+
+import dataclasses
 
 import numpy as np
 import pytest
@@ -293,3 +297,61 @@ def test_fc2_full_size_properties():
     obj_r = 2.0 / n * XD[len(rows):].sum() + lam * np.sum(Dr ** 2)
     print(f"[fullsize] fc2 damped objective on {len(rows)} rows: GPTQ {obj_g:.4g}, RTN {obj_r:.4g}", flush=True)
     assert obj_g < obj_r
+
+
+# ------------------------------------------------------------------ Llama-7B decoder block
+
+BLOCK_TOKENS = {0: 8192, 1: 8192, 2: 8192, 3: 4096}   # per input; the 11008-wide one as in the down_proj test
+
+
+@pytest.mark.parametrize("input_id", [0, 1, 2, 3], ids=["attn_in_qkv", "o_in", "mlp_in_gate_up", "down_in"])
+def test_llama7b_block_shared_hessians(input_id):
+    """The decoder-block workload, one shared input at a time: a single Hessian and factor on the GPU
+    (act-order), reused by every layer that reads that input (q, k and v; o; gate and up; down), each
+    quantized with its own weights at full rows and width. The Hessian and factor are checked as in
+    the single-layer tests, and every layer's sampled rows, loss and packing against the oracle."""
+    torch = torch_cuda()
+    import post_weight_quantization_20_amd as g
+    layers = [c for c in synth.CONFIGS["block"].layers if c.input_id == input_id]
+    n = BLOCK_TOKENS[input_id]
+    layers = [dataclasses.replace(c, n=n) for c in layers]
+    case = layers[0]
+    rng = np.random.default_rng(200 + input_id)
+    X_host = synth.x_tokens(case)
+    print(f"[block] input {input_id}: X {n}x{case.d}, layers {[c.name for c in layers]}", flush=True)
+    dev = torch.device("cuda:0")
+    params = g.Params(bits=case.bits, group_size=case.group_size, block_size=case.block_size,
+                      act_order=case.act_order, damp=case.damp)
+    X = torch.from_numpy(X_host).to(dev)
+    H = torch.zeros((case.d, case.d), dtype=torch.float32, device=dev)
+    ws_h = torch.empty(max(1, g.gptq_workspace_bytes(g.GPTQ_WS_HESSIAN, n, case.d)), dtype=torch.uint8, device=dev)
+    g.gptq_hessian_accumulate(H, X, work=ws_h)
+    U, perm = g.gptq_factor(H, n, params)
+    outs = []
+    for c in layers:
+        W_host = synth.weight(c)
+        q = g.gptq_quantize_layer(torch.from_numpy(W_host).to(dev), U, perm, params)
+        packed = g.gptq_pack(q.codes, c.bits)
+        torch.cuda.synchronize()
+        outs.append((c, W_host, dict(codes=q.codes.cpu().numpy(), scales=q.scales.cpu().numpy(),
+                                     zeros=q.zeros.cpu().numpy(), g_idx=q.g_idx.cpu().numpy(),
+                                     loss=float(q.loss.cpu().numpy()[0]), packed=packed.cpu().numpy())))
+    Hg, Ug, pg = H.cpu().numpy(), U.cpu().numpy(), perm.cpu().numpy().astype(np.int64)
+    del X, H, ws_h, U, perm
+    torch.cuda.empty_cache()
+    print("[block] GPU done; oracle", flush=True)
+    Ho, n_o = _oracle_hessian(case, X_host)
+    assert n_o == n
+    _check_hessian(Hg, Ho, X_host, case, rng)
+    del X_host
+    p = _checked_perm(pg, Ho)
+    Hh, p, lam = ref.damp_and_order(Ho, n, case.damp, True, perm=p)
+    Uo = ref.inverse_cholesky_upper(Hh)
+    _check_factor(Ug, Hh, Uo, lam, rng)
+    for c, W_host, out in outs:
+        rows = np.unique(np.concatenate([np.arange(8), rng.choice(c.rows, 24, replace=False),
+                                         np.arange(c.rows - 8, c.rows)]))
+        print(f"[block] {c.name}: sampled rows, loss, pack", flush=True)
+        _check_rows(c, W_host, out, Hh, Uo, p, rows)
+        _check_loss_identity(c, W_host, out, Hh, p)
+        _check_pack(c, out)
