@@ -66,6 +66,12 @@ GPTQ_DEV float row_bcast(float v) {
   return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0x150 + SRC, 0xF, 0xF, true));
 }
 
+// DPP row_ror:N - lane i of each 16-lane row takes the value of lane (i + N) mod 16
+template <int N>
+GPTQ_DEV float row_ror(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0x120 + N, 0xF, 0xF, true));
+}
+
 // DPP row_ror:15 - lane i of each 16-lane row takes the value of lane (i + 1) mod 16
 GPTQ_DEV float row_ror15(float v) {
   return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x12F, 0xF, 0xF, false));

@@ -68,6 +68,19 @@ __global__ __launch_bounds__(256) void quant_block_kernel(QArgs a) {
 
   const int tid = threadIdx.x;
   const int nc = a.ncols;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int lr = lane & 15;
+  const int rloc = wave * 4 + (lane >> 4);
+  const int64_t row = (int64_t)blockIdx.x * 16 + rloc;
+  const bool row_ok = row < a.rows;
+
+  // lane lr starts with block columns lr*CPL .. lr*CPL+CPL-1 in w[0..CPL-1] (read first, so that
+  // these loads overlap the staging of U's block)
+  float w[CPL];
+  const float* wrow = a.Wp + row * a.ldw + a.b;
+#pragma unroll
+  for (int c = 0; c < CPL; ++c) w[c] = (row_ok && lr * CPL + c < nc) ? wrow[lr * CPL + c] : 0.0f;
+
   bool filled = false;
   if constexpr (CPL >= 4) {
    if (nc == BP && a.d % 4 == 0 && a.b % 4 == 0) {
@@ -101,18 +114,6 @@ __global__ __launch_bounds__(256) void quant_block_kernel(QArgs a) {
   for (int k = tid; k < BP; k += 256) invd[k] = (k < nc) ? 1.0f / a.U[(a.b + k) * a.d + a.b + k] : 0.0f;
   __syncthreads();
 
-  const int lane = tid & 63, wave = tid >> 6;
-  const int lr = lane & 15;
-  const int rloc = wave * 4 + (lane >> 4);
-  const int64_t row = (int64_t)blockIdx.x * 16 + rloc;
-  const bool row_ok = row < a.rows;
-
-  // lane lr starts with block columns lr*CPL .. lr*CPL+CPL-1 in w[0..CPL-1]
-  float w[CPL];
-  const float* wrow = a.Wp + row * a.ldw + a.b;
-#pragma unroll
-  for (int c = 0; c < CPL; ++c) w[c] = (row_ok && lr * CPL + c < nc) ? wrow[lr * CPL + c] : 0.0f;
-
   float s = 1.0f, z = 0.0f, rs = 1.0f;
   if (!a.grid_in_block) {
     const int64_t gi = a.b / a.g;
@@ -130,21 +131,29 @@ __global__ __launch_bounds__(256) void quant_block_kernel(QArgs a) {
   // Chunk o quantizes block columns o*CPL .. o*CPL+CPL-1. Before it, the lanes of each row have
   // been rotated o times by one lane, so lane 0 holds those columns and lane l holds the columns
   // of original lane (l + o) mod 16 (already quantized ones meet zeros in U and stay unchanged).
+  // What a chunk reads from LDS (U's rows for its columns, their reciprocal diagonal) is read one
+  // chunk ahead, into the other of two register sets; U and the diagonal are not written after the
+  // barrier above, and the chunk's own stores go to the codes and errors.
   const int nchunks = (nc + CPL - 1) / CPL;
-  for (int o = 0; o < nchunks; ++o) {
-    const int cbase = ((lr + o) & 15) * CPL;  // block column of w[0] in this lane
-    // everything this chunk reads from LDS, loaded up front (no LDS stores until the chunk ends)
-    float iv[CPL], ur[CPL][CPL];
+  auto fetch = [&](int o, float (&iv)[CPL], float (&ur)[CPL][CPL]) {
+    const int cbase = ((lr + o) & 15) * CPL;
     lds_load<CPL>(invd + o * CPL, iv);
 #pragma unroll
     for (int c = 0; c < CPL; ++c) lds_load<CPL>(Us + (o * CPL + c) * BP + cbase, ur[c]);
+  };
+  // CHECKS: the chunk may start a group or run past the block's last column (a plain chunk, full
+  // and without a group start, runs the column chain with no branch or select)
+  auto chunk = [&](int o, const float (&iv)[CPL], const float (&ur)[CPL][CPL], auto checks) {
+    constexpr bool CHECKS = decltype(checks)::value;
+    const int cbase = ((lr + o) & 15) * CPL;  // block column of w[0] in this lane
     float qv[CPL], ev[CPL];
 #pragma unroll
     for (int c = 0; c < CPL; ++c) {
       const int k = o * CPL + c;
-      if (k == next_group) {
+      if (CHECKS && k == next_group) {
         next_group += gsz;
-        // group grid from the current weights of block columns [k, k + g)
+        // group grid from the current weights of block columns [k, k + g); min and max over the
+        // row's 16 lanes by DPP rotations
         const int kend = min(k + gsz, nc);
         float mn = INFINITY, mx = -INFINITY;
 #pragma unroll
@@ -152,14 +161,14 @@ __global__ __launch_bounds__(256) void quant_block_kernel(QArgs a) {
           const int col = cbase + t;
           if (col >= k && col < kend) { mn = fminf(mn, w[t]); mx = fmaxf(mx, w[t]); }
         }
-#pragma unroll
-        for (int m = 8; m > 0; m >>= 1) {
-          mn = fminf(mn, __shfl_xor(mn, m, 16));
-          mx = fmaxf(mx, __shfl_xor(mx, m, 16));
-        }
+        mn = fminf(mn, row_ror<8>(mn)); mx = fmaxf(mx, row_ror<8>(mx));
+        mn = fminf(mn, row_ror<4>(mn)); mx = fmaxf(mx, row_ror<4>(mx));
+        mn = fminf(mn, row_ror<2>(mn)); mx = fmaxf(mx, row_ror<2>(mx));
+        mn = fminf(mn, row_ror<1>(mn)); mx = fmaxf(mx, row_ror<1>(mx));
         make_grid(mn, mx, a.maxq, s, z, rs);
         if (lr == 0 && row_ok && k < nc) {
-          const int64_t gi = (a.b + k) / a.g;
+          // column and group indices stay below 2^31
+          const int64_t gi = (uint32_t)(a.b + k) / (uint32_t)a.g;
           a.scales[row * a.ngroups + gi] = s;
           a.zeros[row * a.ngroups + gi] = (int32_t)z;
         }
@@ -169,7 +178,7 @@ __global__ __launch_bounds__(256) void quant_block_kernel(QArgs a) {
       const float q = fminf(fmaxf(rintf(x) + z, 0.0f), a.maxq);
       const float dq = s * (q - z);
       float e = (wk - dq) * iv[c];
-      e = (k < nc) ? e : 0.0f;
+      if (CHECKS) e = (k < nc) ? e : 0.0f;
       loss = __builtin_fmaf(e, e, loss);
 #pragma unroll
       for (int t = 0; t < CPL; ++t) w[t] = __builtin_fmaf(-e, ur[c][t], w[t]);
@@ -185,17 +194,43 @@ __global__ __launch_bounds__(256) void quant_block_kernel(QArgs a) {
     }
 #pragma unroll
     for (int t = 0; t < CPL; ++t) w[t] = row_ror15(w[t]);
+  };
+  auto run = [&](int o, const float (&iv)[CPL], const float (&ur)[CPL][CPL]) {
+    if (o * CPL + CPL <= nc && next_group >= o * CPL + CPL) chunk(o, iv, ur, std::false_type{});
+    else chunk(o, iv, ur, std::true_type{});
+  };
+  float ivA[CPL], urA[CPL][CPL], ivB[CPL], urB[CPL][CPL];
+  if (nchunks > 0) fetch(0, ivA, urA);
+  for (int o = 0; o < nchunks; o += 2) {
+    if (o + 1 < nchunks) fetch(o + 1, ivB, urB);
+    run(o, ivA, urA);
+    if (o + 1 < nchunks) {
+      if (o + 2 < nchunks) fetch(o + 2, ivA, urA);
+      run(o + 1, ivB, urB);
+    }
   }
   __syncthreads();
 
   if (row_ok) {
     uint8_t* crow = a.codes_p + row * a.d + a.b;
     float* erow = a.err + row * a.err_ld;
+    const int j0 = lr * CPL;
+    const bool vec = CPL == 8 && nc == BP && a.d % 8 == 0 && a.b % 8 == 0 && a.err_ld % 4 == 0 &&
+                     (uintptr_t)a.codes_p % 8 == 0 && (uintptr_t)a.err % 16 == 0;
+    if constexpr (CPL == 8) {
+      if (vec) {
+        *reinterpret_cast<uint2*>(crow + j0) = *reinterpret_cast<const uint2*>(Qs + rloc * BP + j0);
+        *reinterpret_cast<float4*>(erow + j0) = *reinterpret_cast<const float4*>(Es + rloc * BP + j0);
+        *reinterpret_cast<float4*>(erow + j0 + 4) = *reinterpret_cast<const float4*>(Es + rloc * BP + j0 + 4);
+      }
+    }
+    if (!(CPL == 8 && vec)) {
 #pragma unroll
-    for (int t = 0; t < CPL; ++t) {
-      const int j = lr * CPL + t;
-      if (j < nc) crow[j] = Qs[rloc * BP + j];
-      erow[j] = (j < nc) ? Es[rloc * BP + j] : 0.0f;
+      for (int t = 0; t < CPL; ++t) {
+        const int j = j0 + t;
+        if (j < nc) crow[j] = Qs[rloc * BP + j];
+        erow[j] = (j < nc) ? Es[rloc * BP + j] : 0.0f;
+      }
     }
     if (lr == 0) a.row_loss[row] += (double)loss;
   }
