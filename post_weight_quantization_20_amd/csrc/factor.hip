@@ -574,119 +574,101 @@ hipError_t factor(const float* H, int64_t d, int64_t n, double damp, int act_ord
                         (int)chol_smem());
     attr = true;
   }
-  // Blocked right-looking Cholesky of the reversed matrix (diagonal blocks end up inverted), with a
-  // look-ahead of one block: step k's trailing update is split into the next column block (on the
-  // caller's stream, right before the next diagonal block needs it) and the rest (on side stream ss),
-  // which overlaps the next diagonal block and panel solve. The next-column-block update of step k
-  // waits for the rest of step k - 1, whose region contains that column block.
-  // The blocked right-looking inverse of the factor runs on a second helper stream hs. Inverse step j
-  // starts after both parts of Cholesky step j's trailing update (they read the column panel the
-  // inverse step overwrites), and touches only columns left of block j + 1, which the later Cholesky
-  // steps neither read nor write.
+  // Blocked right-looking Cholesky of the reversed matrix on the caller's stream (diagonal blocks end
+  // up inverted), and the blocked right-looking inverse of the factor on a helper stream hs. Inverse
+  // step j starts after Cholesky step j is complete, its trailing update included (that update reads
+  // the column panel the inverse step overwrites), and touches only columns left of block j + 1,
+  // which the later Cholesky steps neither read nor write. A cross-stream wait costs the host several
+  // microseconds, so hs waits once per TB Cholesky steps and then runs those TB inverse steps.
+  constexpr int64_t TB = 4;
   Helpers* hp = nullptr;
   hipError_t e = helpers(&hp);
   if (e != hipSuccess) return e;
-  hipStream_t ss = hp->stream[0], hs = hp->stream[1];
-  hipEvent_t ev_panel = hp->event[2], ev_rest = hp->event[3], ev_step = hp->event[4], ev_done = hp->event[5],
-             ev_side = hp->event[6];
+  hipStream_t hs = hp->stream[1];
+  hipEvent_t ev_step = hp->event[4], ev_done = hp->event[5];
   helpers_lock(hp);
   const int64_t nblk = (d + NB - 1) / NB;
   const int vec = d % 4 == 0 && (uintptr_t)U % 16 == 0;
-  // side-stream work from an earlier call on these streams is ordered before this call's work
-  if ((e = hipEventRecord(ev_rest, s)) == hipSuccess) e = hipStreamWaitEvent(ss, ev_rest, 0);
-  for (int64_t k = 0; k < nblk && e == hipSuccess; ++k) {
-    const int64_t k0 = k * NB, k1 = std::min(d, k0 + NB), kb = k1 - k0, k2 = std::min(d, k1 + NB);
-    // the diagonal block, and the column panel P below it staged for the panel solve (the product's
-    // workgroups of one row strip must not overwrite the columns another one still reads)
-    const Copy2D pc = make_copy(stage_main, kb, U + k1 * d + k0, d, d - k1, kb);
-    hipLaunchKernelGGL(chol_diag_kernel, dim3(1 + copy_groups(d - k1, kb)), dim3(256), chol_smem(), s, U, d, k0,
-                       (int)kb, vec, w.info, pc);
-    if ((e = hipGetLastError()) != hipSuccess) break;
-    if (k1 < d) {
-      // panel solve: P <- P L_kk^-T
-      GemmArgs t{};
-      t.M = d - k1; t.N = kb; t.K = kb;
-      t.A = stage_main; t.lda = kb; t.transA = 0;
-      t.B = U + k0 * d + k0; t.ldb = d; t.transB = 1;
-      t.C = U + k1 * d + k0; t.ldc = d;
-      t.alpha = 1.0f; t.beta = 0.0f; t.tri = 0;
-      if ((e = gemm_f32(t, s)) != hipSuccess) break;
-      // the caller's stream first takes the rest of step k - 1 (recorded on ss before this point)
-      if ((e = hipStreamWaitEvent(s, ev_rest, 0)) != hipSuccess) break;
-      if ((e = hipEventRecord(ev_panel, s)) != hipSuccess) break;
-      // rest of the trailing update on ss: A[k2:, k2:] -= P2 P2^T (lower part), P2 = P's rows from k2
-      if ((e = hipStreamWaitEvent(ss, ev_panel, 0)) != hipSuccess) break;
-      if (k2 < d) {
-        GemmArgs u{};
-        u.M = d - k2; u.N = d - k2; u.K = kb;
-        u.A = U + k2 * d + k0; u.lda = d; u.transA = 0;
-        u.B = U + k2 * d + k0; u.ldb = d; u.transB = 1;
-        u.C = U + k2 * d + k2; u.ldc = d;
+  for (int64_t kt = 0; kt < nblk && e == hipSuccess; kt += TB) {
+    const int64_t kend = std::min(nblk, kt + TB);
+    for (int64_t k = kt; k < kend && e == hipSuccess; ++k) {
+      const int64_t k0 = k * NB, k1 = std::min(d, k0 + NB), kb = k1 - k0;
+      // the diagonal block, and the column panel P below it staged for the panel solve (the
+      // product's workgroups of one row strip must not overwrite the columns another one still reads)
+      const Copy2D pc = make_copy(stage_main, kb, U + k1 * d + k0, d, d - k1, kb);
+      hipLaunchKernelGGL(chol_diag_kernel, dim3(1 + copy_groups(d - k1, kb)), dim3(256), chol_smem(), s, U, d, k0,
+                         (int)kb, vec, w.info, pc);
+      if ((e = hipGetLastError()) != hipSuccess) break;
+      if (k1 < d) {
+        // panel solve: P <- P L_kk^-T
+        GemmArgs t{};
+        t.M = d - k1; t.N = kb; t.K = kb;
+        t.A = stage_main; t.lda = kb; t.transA = 0;
+        t.B = U + k0 * d + k0; t.ldb = d; t.transB = 1;
+        t.C = U + k1 * d + k0; t.ldc = d;
+        t.alpha = 1.0f; t.beta = 0.0f; t.tri = 0;
+        if ((e = gemm_f32(t, s)) != hipSuccess) break;
+        GemmArgs u{};  // trailing update: A22 -= P P^T (lower part)
+        u.M = d - k1; u.N = d - k1; u.K = kb;
+        u.A = U + k1 * d + k0; u.lda = d; u.transA = 0;
+        u.B = U + k1 * d + k0; u.ldb = d; u.transB = 1;
+        u.C = U + k1 * d + k1; u.ldc = d;
         u.alpha = -1.0f; u.beta = 1.0f; u.tri = 1;
-        if ((e = gemm_f32(u, ss)) != hipSuccess) break;
+        if ((e = gemm_f32(u, s)) != hipSuccess) break;
       }
-      if ((e = hipEventRecord(ev_rest, ss)) != hipSuccess) break;
-      // next column block: A[k1:, k1:k2] -= P P1^T, P1 = P's first k2 - k1 rows (the diagonal tile
-      // gets its upper part too, which the next diagonal step ignores and overwrites)
-      GemmArgs v{};
-      v.M = d - k1; v.N = k2 - k1; v.K = kb;
-      v.A = U + k1 * d + k0; v.lda = d; v.transA = 0;
-      v.B = U + k1 * d + k0; v.ldb = d; v.transB = 1;
-      v.C = U + k1 * d + k1; v.ldc = d;
-      v.alpha = -1.0f; v.beta = 1.0f; v.tri = 0;
-      if ((e = gemm_f32(v, s)) != hipSuccess) break;
     }
+    if (e != hipSuccess) break;
     if ((e = hipEventRecord(ev_step, s)) != hipSuccess) break;
-    // inverse step k on hs (the diagonal block is already inverted), after both update parts
     if ((e = hipStreamWaitEvent(hs, ev_step, 0)) != hipSuccess) break;
-    if ((e = hipStreamWaitEvent(hs, ev_rest, 0)) != hipSuccess) break;
-    const int64_t j0 = k0, j1 = k1, jb = kb;
-    {
-      // stage the row panel R = U[j0:j1, :j0] and the column panel L[j1:, j] together: nothing in
-      // this step changes the column panel before its own product
-      const Copy2D rc = make_copy(stage_row, j0, U + j0 * d, d, jb, j0);
-      const Copy2D cc = make_copy(stage_col, jb, U + j1 * d + j0, d, d - j1, jb);
-      const unsigned g0 = copy_groups(jb, j0), g1 = copy_groups(d - j1, jb);
-      if (g0 + g1 > 0) {
-        hipLaunchKernelGGL(copy2_kernel, dim3(g0 + g1), dim3(256), 0, hs, rc, cc, g0);
-        if ((e = hipGetLastError()) != hipSuccess) break;
+    // inverse steps kt .. kend - 1 on hs (their diagonal blocks are already inverted)
+    for (int64_t k = kt; k < kend && e == hipSuccess; ++k) {
+      const int64_t k0 = k * NB, k1 = std::min(d, k0 + NB), kb = k1 - k0;
+      const int64_t j0 = k0, j1 = k1, jb = kb;
+      {
+        // stage the row panel R = U[j0:j1, :j0] and the column panel L[j1:, j] together: nothing in
+        // this step changes the column panel before its own product
+        const Copy2D rc = make_copy(stage_row, j0, U + j0 * d, d, jb, j0);
+        const Copy2D cc = make_copy(stage_col, jb, U + j1 * d + j0, d, d - j1, jb);
+        const unsigned g0 = copy_groups(jb, j0), g1 = copy_groups(d - j1, jb);
+        if (g0 + g1 > 0) {
+          hipLaunchKernelGGL(copy2_kernel, dim3(g0 + g1), dim3(256), 0, hs, rc, cc, g0);
+          if ((e = hipGetLastError()) != hipSuccess) break;
+        }
       }
-    }
-    if (j0 > 0) {
-      // row panel: R <- -X_jj R
-      GemmArgs r{};
-      r.M = jb; r.N = j0; r.K = jb;
-      r.A = U + j0 * d + j0; r.lda = d; r.transA = 0;
-      r.B = stage_row; r.ldb = j0; r.transB = 0;
-      r.C = U + j0 * d; r.ldc = d;
-      r.alpha = -1.0f; r.beta = 0.0f; r.tri = 0;
-      if ((e = gemm_f32(r, hs)) != hipSuccess) break;
+      if (j0 > 0) {
+        // row panel: R <- -X_jj R
+        GemmArgs r{};
+        r.M = jb; r.N = j0; r.K = jb;
+        r.A = U + j0 * d + j0; r.lda = d; r.transA = 0;
+        r.B = stage_row; r.ldb = j0; r.transB = 0;
+        r.C = U + j0 * d; r.ldc = d;
+        r.alpha = -1.0f; r.beta = 0.0f; r.tri = 0;
+        if ((e = gemm_f32(r, hs)) != hipSuccess) break;
+        if (j1 < d) {
+          GemmArgs q{};  // rectangle: A[j1:, :j0] += L[j1:, j] R
+          q.M = d - j1; q.N = j0; q.K = jb;
+          q.A = U + j1 * d + j0; q.lda = d; q.transA = 0;
+          q.B = U + j0 * d; q.ldb = d; q.transB = 0;
+          q.C = U + j1 * d; q.ldc = d;
+          q.alpha = 1.0f; q.beta = 1.0f; q.tri = 0;
+          if ((e = gemm_f32(q, hs)) != hipSuccess) break;
+        }
+      }
       if (j1 < d) {
-        GemmArgs q{};  // rectangle: A[j1:, :j0] += L[j1:, j] R
-        q.M = d - j1; q.N = j0; q.K = jb;
-        q.A = U + j1 * d + j0; q.lda = d; q.transA = 0;
-        q.B = U + j0 * d; q.ldb = d; q.transB = 0;
-        q.C = U + j1 * d; q.ldc = d;
-        q.alpha = 1.0f; q.beta = 1.0f; q.tri = 0;
-        if ((e = gemm_f32(q, hs)) != hipSuccess) break;
+        // column panel: L[j1:, j] <- L[j1:, j] X_jj
+        GemmArgs c{};
+        c.M = d - j1; c.N = jb; c.K = jb;
+        c.A = stage_col; c.lda = jb; c.transA = 0;
+        c.B = U + j0 * d + j0; c.ldb = d; c.transB = 0;
+        c.C = U + j1 * d + j0; c.ldc = d;
+        c.alpha = 1.0f; c.beta = 0.0f; c.tri = 0;
+        if ((e = gemm_f32(c, hs)) != hipSuccess) break;
       }
-    }
-    if (j1 < d) {
-      // column panel: L[j1:, j] <- L[j1:, j] X_jj
-      GemmArgs c{};
-      c.M = d - j1; c.N = jb; c.K = jb;
-      c.A = stage_col; c.lda = jb; c.transA = 0;
-      c.B = U + j0 * d + j0; c.ldb = d; c.transB = 0;
-      c.C = U + j1 * d + j0; c.ldc = d;
-      c.alpha = 1.0f; c.beta = 0.0f; c.tri = 0;
-      if ((e = gemm_f32(c, hs)) != hipSuccess) break;
     }
   }
-  // join the helper streams (also after a failed launch, so nothing is left behind)
+  // join the helper stream (also after a failed launch, so nothing is left behind)
   hipError_t j = hipEventRecord(ev_done, hs);
   if (j == hipSuccess) j = hipStreamWaitEvent(s, ev_done, 0);
-  if (j == hipSuccess) j = hipEventRecord(ev_side, ss);
-  if (j == hipSuccess) j = hipStreamWaitEvent(s, ev_side, 0);
   helpers_unlock(hp);
   if (e == hipSuccess) e = j;
   if (e != hipSuccess) return e;
