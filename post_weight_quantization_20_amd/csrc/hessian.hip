@@ -224,14 +224,18 @@ __global__ __launch_bounds__(256) void reduce_partials(HessArgs a) {
   tile_at(tile, a.T, ti, tj);
   const int64_t gm = (int64_t)ti * HT + e / HT;
   if (gm >= a.d) return;
+  const int64_t gc0 = (int64_t)tj * HT + e % HT;
+  float* h = a.H + gm * a.d + gc0;
+  if (a.d % 4 == 0 && (uintptr_t)a.H % 16 == 0 && gc0 + 4 <= a.d) {   // one 16-byte read-modify-write
+    floatx4 v = *reinterpret_cast<const floatx4*>(h);
 #pragma unroll
-  for (int k = 0; k < 4; ++k) {
-    const int64_t gc = (int64_t)tj * HT + e % HT + k;
-    if (gc < a.d) {
-      float* h = a.H + gm * a.d + gc;
-      *h = __builtin_fmaf(2.0f, s[k], *h);
-    }
+    for (int k = 0; k < 4; ++k) v[k] = __builtin_fmaf(2.0f, s[k], v[k]);
+    *reinterpret_cast<floatx4*>(h) = v;
+    return;
   }
+#pragma unroll
+  for (int k = 0; k < 4; ++k)
+    if (gc0 + k < a.d) h[k] = __builtin_fmaf(2.0f, s[k], h[k]);
 }
 
 // ------------------------------------------------------------------ register-staged path

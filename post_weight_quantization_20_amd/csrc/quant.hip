@@ -265,13 +265,24 @@ __global__ __launch_bounds__(256) void group_grid_kernel(const float* __restrict
   }
 }
 
-// Working copy in processing order: Wp[r][j] = W[r][perm[j]] as fp32; zero padding to ldw.
+// Working copy in processing order: Wp[r][j] = W[r][perm[j]] as fp32; zero padding to ldw (a
+// multiple of 4). A thread writes four consecutive columns, as one 16-byte store when Wp allows.
 __global__ __launch_bounds__(256) void gather_w_kernel(const void* __restrict__ W, int dtype, int64_t ldw_in,
                                                        int64_t rows, int64_t d, const int32_t* __restrict__ perm,
-                                                       float* __restrict__ Wp, int64_t ldw) {
+                                                       float* __restrict__ Wp, int64_t ldw, int vec) {
   for (int64_t r = blockIdx.y; r < rows; r += gridDim.y)
-    for (int64_t j = (int64_t)blockIdx.x * 256 + threadIdx.x; j < ldw; j += (int64_t)gridDim.x * 256)
-      Wp[r * ldw + j] = (j < d) ? load_as_f32(W, dtype, r * ldw_in + perm[j]) : 0.0f;
+    for (int64_t j = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4; j < ldw; j += (int64_t)gridDim.x * 1024) {
+      float v[4];
+#pragma unroll
+      for (int t = 0; t < 4; ++t) v[t] = (j + t < d) ? load_as_f32(W, dtype, r * ldw_in + perm[j + t]) : 0.0f;
+      float* o = Wp + r * ldw + j;
+      if (vec) {
+        *reinterpret_cast<float4*>(o) = make_float4(v[0], v[1], v[2], v[3]);
+      } else {
+#pragma unroll
+        for (int t = 0; t < 4; ++t) o[t] = v[t];
+      }
+    }
 }
 
 // iperm[perm[j]] = j and g_idx[perm[j]] = j / g.
@@ -285,12 +296,23 @@ __global__ void index_kernel(const int32_t* __restrict__ perm, int64_t d, int64_
   }
 }
 
-// codes[r][c] = codes_p[r][iperm[c]] (back to the original column order).
+// codes[r][c] = codes_p[r][iperm[c]] (back to the original column order). A thread writes four
+// consecutive codes, as one 4-byte store when the row allows.
 __global__ __launch_bounds__(256) void unpermute_kernel(const uint8_t* __restrict__ codes_p, int64_t rows, int64_t d,
-                                                        const int32_t* __restrict__ iperm, uint8_t* __restrict__ codes) {
+                                                        const int32_t* __restrict__ iperm, uint8_t* __restrict__ codes,
+                                                        int vec) {
   for (int64_t r = blockIdx.y; r < rows; r += gridDim.y)
-    for (int64_t c = (int64_t)blockIdx.x * 256 + threadIdx.x; c < d; c += (int64_t)gridDim.x * 256)
-      codes[r * d + c] = codes_p[r * d + iperm[c]];
+    for (int64_t c = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4; c < d; c += (int64_t)gridDim.x * 1024) {
+      const uint8_t* src = codes_p + r * d;
+      uint8_t* dst = codes + r * d + c;
+      if (vec && c + 4 <= d) {
+        const uint32_t w = src[iperm[c]] | (src[iperm[c + 1]] << 8) | (src[iperm[c + 2]] << 16) |
+                           ((uint32_t)src[iperm[c + 3]] << 24);
+        *reinterpret_cast<uint32_t*>(dst) = w;
+      } else {
+        for (int64_t t = 0; t < 4 && c + t < d; ++t) dst[t] = src[iperm[c + t]];
+      }
+    }
 }
 
 __global__ void zero_f64(double* p, int64_t n) {
@@ -407,9 +429,10 @@ hipError_t quantize(const void* W, int w_dtype, int64_t rows, int64_t d, int64_t
 
   hipLaunchKernelGGL(index_kernel, dim3((unsigned)((d + 255) / 256)), dim3(256), 0, s, perm, d, g, iperm, g_idx);
   if (rows > 0) {
-    const unsigned gx = (unsigned)std::min<int64_t>((L.ldw + 255) / 256, 64);
-    hipLaunchKernelGGL(gather_w_kernel, dim3(gx, (unsigned)std::min<int64_t>(rows, 65535)), dim3(256), 0, s, W, w_dtype, ld_w, rows, d, perm,
-                       Wp, L.ldw);
+    const unsigned gx = (unsigned)std::min<int64_t>((L.ldw + 1023) / 1024, 64);
+    const int vec = (uintptr_t)Wp % 16 == 0;
+    hipLaunchKernelGGL(gather_w_kernel, dim3(gx, (unsigned)std::min<int64_t>(rows, 65535)), dim3(256), 0, s, W, w_dtype,
+                       ld_w, rows, d, perm, Wp, L.ldw, vec);
     hipLaunchKernelGGL(zero_f64, dim3((unsigned)((rows + 255) / 256)), dim3(256), 0, s, row_loss, rows);
   }
   hipError_t e;
@@ -450,8 +473,10 @@ hipError_t quantize(const void* W, int w_dtype, int64_t rows, int64_t d, int64_t
     }
   }
   if (rows > 0) {
-    const unsigned gx = (unsigned)std::min<int64_t>((d + 255) / 256, 64);
-    hipLaunchKernelGGL(unpermute_kernel, dim3(gx, (unsigned)std::min<int64_t>(rows, 65535)), dim3(256), 0, s, codes_p, rows, d, iperm, codes);
+    const unsigned gx = (unsigned)std::min<int64_t>((d + 1023) / 1024, 64);
+    const int vec = (uintptr_t)codes % 4 == 0 && d % 4 == 0;
+    hipLaunchKernelGGL(unpermute_kernel, dim3(gx, (unsigned)std::min<int64_t>(rows, 65535)), dim3(256), 0, s, codes_p,
+                       rows, d, iperm, codes, vec);
   }
   hipLaunchKernelGGL(loss_kernel, dim3(1), dim3(1024), 0, s, row_loss, rows, loss);
   return hipGetLastError();
