@@ -256,11 +256,13 @@ hipError_t launch(const GemmArgs& a, hipStream_t s) {
 hipError_t gemm_f32(const GemmArgs& a, hipStream_t s) {
   if (a.M <= 0 || a.N <= 0) return hipSuccess;
   if (a.tri != 0 && a.M != a.N) return hipErrorInvalidValue;
-  // Large products use 128 x 128 tiles; when those would leave most of the 256 CUs idle, 64 x 64
-  // tiles give four times as many workgroups, each a quarter of the work.
+  // 128 x 128 tiles do more work per byte staged but run two to a CU (512 at a time on 256 CUs), so
+  // they pay off when their count fills those slots evenly, or when there are so many that the last
+  // partial round hardly matters; otherwise 64 x 64 tiles (four times as many workgroups) balance
+  // better. Measured on the solver's shapes (fp32, K = 128 and 512).
   const int64_t t128 = ((a.M + 127) / 128) * ((a.N + 127) / 128) / (a.tri ? 2 : 1);
-  if (t128 < 256) return launch<64>(a, s);
-  return launch<128>(a, s);
+  if (t128 >= 4096 || (t128 >= 512 && t128 % 256 == 0)) return launch<128>(a, s);
+  return launch<64>(a, s);
 }
 
 }  // namespace gptq
