@@ -8,7 +8,8 @@ It is a plain, slow, step-by-step statement of what the solver computes, written
 
 * GPTQ tools page (ozercemkelahmet.com/tools/gptq), "How it works", Steps 3-8, "Optional
   refinements" and the section "A minimal Python sketch" (the sketch is read as a description of
-  the computation, not transcribed).
+  the computation, not transcribed). Step 8 also gives the inference use of the stored layer
+  (unpack, scale, multiply), stated here as dequantize / dequant_matmul.
 * "GPTQ Quantization: Complete Technical Guide" (notes.jayaprakash.net), sections "Quantization
   Equation", "Example: Quantizing a Single Weight", "Computing the Hessian", "Damping Factor".
 * "Paper breakdown: GPTQ" (ai360xpert.com), "How It Works" (lazy batching).
@@ -334,6 +335,29 @@ def unpack(packed: np.ndarray, d: int) -> np.ndarray:
     for t in range(8):
         out[:, t::8] = ((p >> np.uint64(4 * t)) & np.uint64(15)).astype(np.uint8)
     return out
+
+
+# --------------------------------------------------------------------------------------------
+# Using the stored layer  (tools page Step 8: at inference a kernel unpacks, scales and multiplies;
+# What Is GPTQ, "How it works": each group is expanded back to higher precision for the product)
+# --------------------------------------------------------------------------------------------
+
+def dequantize(packed: np.ndarray, scales: np.ndarray, zeros: np.ndarray, g_idx: np.ndarray,
+               d: int) -> np.ndarray:
+    """Weights rows x d, original column order: column j of row r is
+    scales[r, g] * (code[r, j] - zeros[r, g]) with g = g_idx[j], the group column j was quantized in."""
+    codes = unpack(packed, d).astype(np.float64)
+    g = np.asarray(g_idx, dtype=np.int64)
+    s = np.asarray(scales, dtype=np.float64)[:, g]
+    z = np.asarray(zeros, dtype=np.float64)[:, g]
+    return s * (codes - z)
+
+
+def dequant_matmul(x: np.ndarray, packed: np.ndarray, scales: np.ndarray, zeros: np.ndarray,
+                   g_idx: np.ndarray, d: int) -> np.ndarray:
+    """The layer's output y = x W^T (m x rows) for inputs x (m x d), W the dequantized weights."""
+    W = dequantize(packed, scales, zeros, g_idx, d)
+    return np.asarray(x, dtype=np.float64) @ W.T
 
 
 def bits_per_weight(bits: int, group_size: int, scale_bits: int = 16, zero_bits: int = 4) -> float:

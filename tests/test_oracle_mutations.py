@@ -35,6 +35,11 @@ MUTATIONS = [
     ("hessian without factor 2", "H += 2.0 * (x.T @ x)", "H += (x.T @ x)"),
     ("pack nibble order", "words |= c[:, t::8].astype(np.uint64) << np.uint64(4 * t)",
      "words |= c[:, t::8].astype(np.uint64) << np.uint64(4 * (7 - t))"),
+    ("dequant zero not subtracted", "return s * (codes - z)", "return s * codes"),
+    ("dequant groups by position", "g = np.asarray(g_idx, dtype=np.int64)",
+     "g = np.arange(d) * len(np.unique(g_idx)) // d"),
+    ("dequant product transposed", "return np.asarray(x, dtype=np.float64) @ W.T",
+     "return (np.asarray(x, dtype=np.float64)[:, :W.shape[0]] @ W).T"),
 ]
 
 
@@ -101,6 +106,15 @@ def _checks(m):
         q, _ = m.quantize_to_grid(np.array([0.75]), np.array([0.1]), np.array([2.0]), 15)
         if q[0] != 10:
             failed.append("grid primitive")
+        # the stored layer, expanded and multiplied, worked by hand (interleaved groups)
+        codes = np.array([list(range(16)), list(range(15, -1, -1))], np.uint8)
+        xs = np.zeros((2, 16))
+        xs[0, 0] = xs[0, 15] = 1.0
+        xs[1, [0, 1, 2, 5, 12]] = [1.0, -1.0, 2.0, 0.5, -2.0]
+        y = m.dequant_matmul(xs, ref.pack(codes, 4), np.array([[0.5, 0.25], [2.0, 1.0]]),
+                             np.array([[2, 12], [8, 0]]), np.array([0, 0, 1, 1] * 4), 16)
+        if y.shape != (2, 2) or not np.array_equal(y, np.array([[-0.25, 14.0], [-14.75, 50.0]])):
+            failed.append("dequant hand example")
         # H = I must reduce to round-to-nearest with dynamic grids
         rI = m.gptq(W, None, 4, 16, 32, H=np.eye(d) * 2.0, n=1)
         if not np.array_equal(rI.quant.codes, ref.rtn(W, 4, 16).codes):

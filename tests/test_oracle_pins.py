@@ -422,3 +422,52 @@ def test_follow_adopts_only_inside_tie_window():
     assert np.array_equal(r0.codes, base.quant.codes)
     rall = ref.quantize_layer(W, base.U, 4, 16, 16, follow=(flipped, base.quant.zeros), tau=0.5)
     assert rall.adopted_diff > 0
+
+
+# ---------------------------------------------------------------- using the stored layer (Step 8)
+
+def test_dequantize_worked_example_values():
+    """Technical Guide, 'Quantization Equation' and 'Example: Quantizing a Single Weight': code 8 at
+    scale 0.1 recovers 0.8, code 7 recovers 0.7 (zero point 0)."""
+    e1, e2 = GOLD["quantization_equation"], GOLD["single_weight"]
+    codes = np.zeros((1, 8), np.uint8)
+    codes[0, 0], codes[0, 5] = e1["quantized"], e2["quantized"]
+    w = ref.dequantize(ref.pack(codes, 4), np.array([[0.1]]), np.array([[0]]), np.zeros(8, np.int32), 8)
+    assert w[0, 0] == pytest.approx(e1["recovered"], abs=1e-15)
+    assert w[0, 5] == pytest.approx(e2["dequantized"], abs=1e-15)
+    assert np.all(w[0, [1, 2, 3, 4, 6, 7]] == 0)
+
+
+def test_dequant_matmul_hand_example():
+    """y = x W^T with W[r, j] = s[r, g_idx[j]] (code - z[r, g_idx[j]]), worked by hand on two rows of
+    16 columns whose groups interleave (as act-order leaves them)."""
+    codes = np.array([list(range(16)), list(range(15, -1, -1))], np.uint8)
+    g_idx = np.array([0, 0, 1, 1] * 4, np.int32)
+    s = np.array([[0.5, 0.25], [2.0, 1.0]])
+    z = np.array([[2, 12], [8, 0]], np.int32)
+    x = np.zeros((2, 16))
+    x[0, 0] = x[0, 15] = 1.0
+    x[1, [0, 1, 2, 5, 12]] = [1.0, -1.0, 2.0, 0.5, -2.0]
+    y = ref.dequant_matmul(x, ref.pack(codes, 4), s, z, g_idx, 16)
+    # row 0 weights at columns 0, 1, 2, 5, 12, 15: .5(0-2), .5(1-2), .25(2-12), .5(5-2), .5(12-2), .25(15-12)
+    # row 1 weights at the same columns: 2(15-8), 2(14-8), 1(13-0), 2(10-8), 2(3-8), 1(0-0)
+    want = np.array([[-1.0 + 0.75, 14.0 + 0.0],
+                     [1 * -1.0 - 1 * -0.5 + 2 * -2.5 + 0.5 * 1.5 - 2 * 5.0,
+                      1 * 14.0 - 1 * 12.0 + 2 * 13.0 + 0.5 * 4.0 - 2 * -10.0]])
+    assert np.array_equal(y, want)
+
+
+@pytest.mark.parametrize("act", [False, True])
+def test_dequantize_reproduces_column_loop_weights(act):
+    """Unpacking the codes and expanding each column with its group's scale and zero gives exactly
+    the weights the column loop dequantized, in the original column order, with or without act-order."""
+    rng = np.random.default_rng(17)
+    d = 64
+    X = _correlated_x(rng, 96, d) * rng.uniform(0.3, 3.0, d)[None, :]
+    W = rng.standard_normal((12, d)) * 0.02
+    r = _solve(W, X, 4, 16, 32, act=act)
+    q = r.quant
+    w = ref.dequantize(ref.pack(q.codes, 4), q.scales, q.zeros, q.g_idx, d)
+    assert np.array_equal(w, q.Q)
+    y = ref.dequant_matmul(X[:5], ref.pack(q.codes, 4), q.scales, q.zeros, q.g_idx, d)
+    assert np.allclose(y, X[:5] @ q.Q.T, rtol=1e-13, atol=1e-13)
