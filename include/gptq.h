@@ -11,6 +11,10 @@
  *   gptq_quantize_layer      the column loop with lazy block updates; codes, scales, zeros, loss
  *   gptq_pack                eight 4-bit codes per 32-bit word
  *
+ * and one call that uses the stored layer:
+ *
+ *   gptq_dequant_gemm        y = x W^T for a few input rows, read straight from the packed codes
+ *
  * Sources (web pages on GPTQ): the GPTQ tools page at ozercemkelahmet.com ("How it works",
  * Steps 3-8, "Optional refinements", "A minimal Python sketch", "Memory arithmetic"); "GPTQ
  * Quantization: Complete Technical Guide" (notes.jayaprakash.net; "Quantization Equation",
@@ -154,6 +158,41 @@ gptq_status_t gptq_quantize_layer(const void *W, int32_t w_dtype, int64_t rows, 
  */
 gptq_status_t gptq_pack(const uint8_t *codes, int64_t rows, int64_t d, int32_t bits, int32_t *packed,
                         void *stream);
+
+/*
+ * The stored layer at inference: y = x W^T for a few rows of inputs x, with W expanded from the packed
+ * codes, scales and zeros inside the kernel (GPTQ tools page, "How it works", Step 8: a fused kernel
+ * unpacks, scales and multiplies; "What Is GPTQ?", "How it works", Step 3: each group is expanded
+ * back to higher precision just in time for the product). Small-batch products like this are bound
+ * by reading the weights, about half a byte per weight here.
+ *
+ *   x       device array [m x ld_x] of x_dtype (GPTQ_F32, GPTQ_F16 or GPTQ_BF16): one row per token,
+ *           d features each. Not modified.
+ *   m       input rows, >= 0 (0: nothing is queued). Rows are taken eight at a time, and each group
+ *           of eight reads the codes once.
+ *   ld_x    row pitch of x in elements, >= d.
+ *   packed  device int32[rows * d / 8] in gptq_pack's layout: nibble t of word k of a row is the
+ *           code of column 8k + t. Not modified.
+ *   bits    the code width, 1..4 (wider codes return GPTQ_EUNSUPPORTED: they do not fit a nibble).
+ *   scales  device float[rows * ngroups] and zeros device int32[rows * ngroups], as
+ *           gptq_quantize_layer writes them, with ngroups = ceil(d / g) and g = group_size (d when
+ *           group_size <= 0).
+ *   g_idx   device int32[d], the group of each column (gptq_quantize_layer's g_idx, needed after
+ *           act-order), or NULL when column k is in group k / g. Entries outside [0, ngroups) are
+ *           clamped into it.
+ *   rows    weight rows (outputs), >= 0 (0: nothing is queued); d input columns, >= 8, a multiple
+ *           of 8.
+ *   y       device float[m x ld_y], output, ld_y >= rows: y[i, r] = sum_k x[i, k] W[r, k] with
+ *           W[r, k] = scales[r, G] * (code[r, k] - zeros[r, G]) and G the group of column k.
+ * Products and sums are fp32 (fp16 x times a code is exact in fp32). A faster kernel runs when x is
+ * fp16, g_idx is NULL, g is a multiple of 32 or at least d, d is a multiple of 32, and the rows of x
+ * and the codes are 16-byte aligned; otherwise a general one does. Results do not depend on
+ * scheduling.
+ */
+gptq_status_t gptq_dequant_gemm(const void *x, int32_t x_dtype, int64_t m, int64_t ld_x, const int32_t *packed,
+                                int32_t bits, const float *scales, const int32_t *zeros, const int32_t *g_idx,
+                                int64_t rows, int64_t d, int32_t group_size, float *y, int64_t ld_y,
+                                void *stream);
 
 /*
  * Workspace bytes for a call: kind GPTQ_WS_HESSIAN (a = n_tok of the chunk), GPTQ_WS_FACTOR (a unused)

@@ -21,6 +21,7 @@ from .solver import (  # noqa: F401
     LayerResult,
     Params,
     QuantOutput,
+    gptq_dequant_gemm,
     gptq_factor,
     gptq_hessian_accumulate,
     gptq_pack,

@@ -172,6 +172,36 @@ def gptq_pack(codes: torch.Tensor, bits: int, packed: Optional[torch.Tensor] = N
     return packed
 
 
+def gptq_dequant_gemm(x: torch.Tensor, packed: torch.Tensor, scales: torch.Tensor, zeros: torch.Tensor,
+                      d: int, group_size: int, g_idx: Optional[torch.Tensor] = None, bits: int = 4,
+                      y: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """y = x W^T (float32 [m, rows]) with W expanded from the packed codes, scales and zeros inside the
+    kernel; g_idx (int32 [d]) maps columns to groups, None meaning column k is in group k // g."""
+    _need_cuda(x, packed, scales, zeros, g_idx, y)
+    if x.dim() != 2 or x.shape[1] != d or x.stride(1) != 1 or x.dtype not in _DTYPE:
+        raise ValueError("x must be [m, d] with unit column stride, fp32/fp16/bf16")
+    rows = packed.shape[0]
+    g = d if group_size <= 0 else group_size
+    ng = (d + g - 1) // g
+    if packed.dtype != torch.int32 or packed.shape != (rows, d // 8) or not packed.is_contiguous():
+        raise ValueError("packed must be contiguous int32 [rows, d / 8]")
+    if scales.dtype != torch.float32 or scales.shape != (rows, ng) or not scales.is_contiguous():
+        raise ValueError("scales must be contiguous float32 [rows, ngroups]")
+    if zeros.dtype != torch.int32 or zeros.shape != (rows, ng) or not zeros.is_contiguous():
+        raise ValueError("zeros must be contiguous int32 [rows, ngroups]")
+    if g_idx is not None and (g_idx.dtype != torch.int32 or g_idx.shape != (d,) or not g_idx.is_contiguous()):
+        raise ValueError("g_idx must be contiguous int32 [d]")
+    m = x.shape[0]
+    if y is None:
+        y = torch.empty((m, rows), dtype=torch.float32, device=x.device)
+    if y.dtype != torch.float32 or y.dim() != 2 or y.shape != (m, rows) or y.stride(1) != 1:
+        raise ValueError("y must be float32 [m, rows] with unit column stride")
+    _check(_lib.lib().gptq_dequant_gemm(_ptr(x), _DTYPE[x.dtype], m, x.stride(0), _ptr(packed), int(bits),
+                                        _ptr(scales), _ptr(zeros), _ptr(g_idx), rows, d, int(group_size), _ptr(y),
+                                        y.stride(0), _stream(stream)))
+    return y
+
+
 @dataclass
 class LayerResult:
     H: torch.Tensor

@@ -3,12 +3,15 @@
 from .gen import (  # noqa: F401
     CONFIGS,
     LayerCase,
+    StoredLayer,
     Workload,
     bf16_bits_to_f64,
     case_from_config,
+    inference_x,
     make_case,
     outlier_channels,
     round_to_dtype,
+    stored_layer,
     to_f64,
     weight,
     x_chunk,

@@ -226,3 +226,53 @@ def case_from_config(name: str, layer: int = 0, **overrides) -> LayerCase:
     """A layer of a named workload, optionally with fields overridden (e.g. fewer rows or tokens)."""
     c = CONFIGS[name].layers[layer]
     return replace(c, **overrides) if overrides else c
+
+
+# ------------------------------------------------------------------ stored layers for inference
+
+@dataclass
+class StoredLayer:
+    """A quantized layer in the stored format: codes uint8 rows x d (original column order),
+    scales float32 and zeros int32 rows x ngroups, and g_idx int32 [d] (None: column k in group k // g)."""
+    codes: np.ndarray
+    scales: np.ndarray
+    zeros: np.ndarray
+    g_idx: Optional[np.ndarray]
+    group_size: int
+
+
+def stored_layer(seed: int, rows: int, d: int, bits: int = 4, group_size: int = 128, act_order: bool = False,
+                 exact: bool = False) -> StoredLayer:
+    """Random draws in the stored format, keyed (300, seed).
+
+    codes: uniform over [0, 2^bits). scales: log-uniform in [1e-3, 3e-2], or with exact=True powers of
+    two 2^-k, k uniform in 0..3. zeros: uniform over [0, 2^bits), except 5% drawn uniformly from
+    [-4, 2^bits + 4) (a group whose weights all share one sign has its zero outside the code range).
+    act_order: the groups are g consecutive positions of a uniformly random column order, so g_idx of
+    column perm[j] is j // g, the shape the column loop leaves after act-order.
+    """
+    rng = _rng(300, seed)
+    g = d if group_size <= 0 else group_size
+    ng = (d + g - 1) // g
+    codes = rng.integers(0, 1 << bits, size=(rows, d), dtype=np.uint8)
+    if exact:
+        scales = np.ldexp(1.0, -rng.integers(0, 4, size=(rows, ng))).astype(np.float32)
+    else:
+        scales = np.exp(rng.uniform(np.log(1e-3), np.log(3e-2), size=(rows, ng))).astype(np.float32)
+    zeros = rng.integers(0, 1 << bits, size=(rows, ng), dtype=np.int64)
+    wide = rng.random((rows, ng)) < 0.05
+    zeros[wide] = rng.integers(-4, (1 << bits) + 4, size=int(wide.sum()))
+    g_idx = None
+    if act_order:
+        perm = rng.permutation(d)
+        g_idx = np.empty(d, dtype=np.int32)
+        g_idx[perm] = (np.arange(d) // g).astype(np.int32)
+    return StoredLayer(codes=codes, scales=scales, zeros=zeros.astype(np.int32), g_idx=g_idx, group_size=group_size)
+
+
+def inference_x(seed: int, m: int, d: int, dtype: str = "f16", exact: bool = False) -> np.ndarray:
+    """m rows of layer inputs, keyed (301, seed): N(0, 1) rounded to dtype, or with exact=True integers
+    uniform in [-2, 2]. Stored as in round_to_dtype."""
+    rng = _rng(301, seed)
+    x = rng.integers(-2, 3, size=(m, d)).astype(np.float64) if exact else rng.standard_normal((m, d))
+    return round_to_dtype(x, dtype)

@@ -145,6 +145,35 @@ def test_pack_rejects_bad_arguments():
     assert f(FAKE, 0, 16, 4, FAKE, None) == 0      # no rows: nothing to do
 
 
+def test_dequant_gemm_rejects_bad_arguments():
+    lib = _lib().lib()
+    f = lib.gptq_dequant_gemm
+    # (x, dtype, m, ld_x, packed, bits, scales, zeros, g_idx, rows, d, group_size, y, ld_y, stream)
+    ok = (FAKE, 1, 2, 64, FAKE, 4, FAKE, FAKE, None, 16, 64, 32, FAKE, 16, None)
+
+    def call(**kw):
+        a = list(ok)
+        for k, v in kw.items():
+            a[["x", "dtype", "m", "ldx", "packed", "bits", "scales", "zeros", "gidx", "rows", "d", "g", "y", "ldy",
+               "s"].index(k)] = v
+        return f(*a)
+
+    assert call(d=60) == -1                 # not a multiple of 8
+    assert call(d=4) == -1
+    assert call(ldx=63) == -1               # ld_x < d
+    assert call(ldy=15) == -1               # ld_y < rows
+    assert call(dtype=7) == -1
+    assert call(m=-1) == -1
+    assert call(bits=0) == -1
+    assert call(bits=8) == -3               # wider than a nibble: unsupported
+    assert call(x=None) == -1
+    assert call(packed=None) == -1
+    assert call(scales=None) == -1
+    assert call(y=None) == -1
+    assert call(m=0) == 0                   # nothing to do
+    assert call(rows=0) == 0
+
+
 def test_workspace_sizes():
     L = _lib()
     lib = L.lib()
