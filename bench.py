@@ -10,6 +10,11 @@ of the dominant kernel (live HIP-event timing on the launch stream), and the flo
 a bounded sample of the same workload on the host cores.
 
     python bench.py [--steps K] [--warmup W] [--gpus 1] [--workload q_proj] [--no-cpu-baseline]
+
+With --dequant WORKLOAD it measures instead the stored layer's product y = x W^T
+(gptq_dequant_gemm) for --batch input rows, on a random stored layer of that workload's shape and
+format (fc2: 12288x49152 3-bit codes, one group per row; q_proj: 4096x4096 4-bit g128; down_proj:
+4096x11008 4-bit g128 with act-order g_idx), and prints one JSON line for it.
 """
 
 from __future__ import annotations
@@ -41,6 +46,9 @@ def parse():
     ap.add_argument("--workload", default="q_proj", choices=["q_proj", "down_proj", "fc2", "tiny"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample-seconds", type=float, default=20.0)
+    ap.add_argument("--dequant", default=None, choices=["fc2", "q_proj", "down_proj"],
+                    help="measure gptq_dequant_gemm on a stored layer of this workload's shape instead")
+    ap.add_argument("--batch", type=int, default=1, help="input rows for --dequant")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run one plain 1 GiB device-to-device copy (a known-size reference for HBM counters)")
     return ap.parse_args()
@@ -120,6 +128,113 @@ def cpu_baseline(case, budget_s: float):
     }
 
 
+DEQUANT_LAYERS = {
+    # workload: (rows, d, bits, group_size, act_order), the stored format the solver writes for it
+    "fc2": (12288, 49152, 3, 0, False),
+    "q_proj": (4096, 4096, 4, 128, False),
+    "down_proj": (4096, 11008, 4, 128, True),
+}
+
+
+def dequant_bytes(rows: int, d: int, m: int, ngroups: int, act: bool) -> int:
+    """Algorithmic HBM bytes of one y = x W^T: the nibble codes, scales and zeros, g_idx, x, y."""
+    return rows * d // 2 + rows * ngroups * 8 + (d * 4 if act else 0) + m * d * 2 + m * rows * 4
+
+
+def dequant_cpu_baseline(L, x64, d: int, bits: int, budget_s: float):
+    """The oracle's dequant_matmul on a slice of rows until about budget_s, scaled to all rows."""
+    from oracle import gptq_ref as ref
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([i.get("num_threads", 1) for i in threadpool_info()] or [os.cpu_count() or 1])
+    except Exception:
+        cores = os.cpu_count() or 1
+    rows = L.codes.shape[0]
+    g = d if L.group_size <= 0 else L.group_size
+    gidx = np.arange(d) // g if L.g_idx is None else L.g_idx
+    done, t = 0, 0.0
+    step = 64
+    while done < rows and t < budget_s:
+        sl = slice(done, min(rows, done + step))
+        t0 = time.perf_counter()
+        ref.dequant_matmul(x64, ref.pack(L.codes[sl], bits), L.scales[sl], L.zeros[sl], gidx, d)
+        t += time.perf_counter() - t0
+        done = sl.stop
+    sec = t * rows / done
+    return {"value": rows * d / sec, "unit": "weights/s", "cores": int(cores), "kind": "oracle",
+            "sample": f"float64 oracle dequant_matmul (unpack, expand, product) on {done} of {rows} rows, "
+                      f"scaled to all rows"}
+
+
+def bench_dequant(args):
+    import torch
+    import post_weight_quantization_20_amd as g
+    import synth
+
+    rows, d, bits, gs, act = DEQUANT_LAYERS[args.dequant]
+    m = args.batch
+    dev = torch.device("cuda:0")
+    print(f"[bench] generating a stored {args.dequant} layer: {rows}x{d} {bits}-bit, m={m}", file=sys.stderr,
+          flush=True)
+    L = synth.stored_layer(400, rows, d, bits, gs, act_order=act)
+    x = synth.inference_x(401, m, d, "f16")
+    codes = torch.from_numpy(L.codes).to(dev)
+    packed = g.gptq_pack(codes, bits)
+    del codes
+    scales = torch.from_numpy(L.scales).to(dev)
+    zeros = torch.from_numpy(L.zeros).to(dev)
+    gidx = torch.from_numpy(L.g_idx).to(dev) if act else None
+    xd = torch.from_numpy(x).to(dev)
+    y = torch.empty((m, rows), dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream()
+
+    def call():
+        g.gptq_dequant_gemm(xd, packed, scales, zeros, d, gs, g_idx=gidx, bits=bits, y=y)
+
+    for _ in range(args.warmup):
+        call()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    e0.record(stream)
+    for _ in range(args.steps):
+        call()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms = e0.elapsed_time(e1) / args.steps
+    ng = L.scales.shape[1]
+    byts = dequant_bytes(rows, d, m, ng, act)
+    achieved = byts / (ms / 1000.0) / 1e9
+    out = {
+        "metric": "stored-layer product y = x W^T from packed codes: weights/s; % HBM peak",
+        "value": round(rows * d / (ms / 1000.0), 1),
+        "unit": "weights/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(wall * 1000.0 / args.steps, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f16",
+        "data": "synthetic (seeded random stored layer; no trained weights)",
+        "config": {"workload": f"dequant {args.dequant}: W {rows}x{d} {bits}-bit nibble codes, "
+                               f"g{gs if gs > 0 else d}{' act-order g_idx' if act else ''}, x {m}x{d} fp16",
+                   "rows": rows, "d": d, "batch": m, "bits": bits, "group_size": gs, "act_order": int(act)},
+        "roofline": {"kernel": "gptq_dequant_gemm", "bound": "hbm", "achieved": round(achieved, 1),
+                     "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4),
+                     "traffic": None, "bytes_per_launch": byts, "avg_launch_ms": round(ms, 5)},
+    }
+    if not args.no_cpu_baseline:
+        print("[bench] timing the float64 oracle on a bounded sample", file=sys.stderr, flush=True)
+        out["cpu_baseline"] = dequant_cpu_baseline(L, synth.to_f64(x, "f16"), d, bits,
+                                                   min(args.cpu_sample_seconds, 10.0))
+    else:
+        out["cpu_baseline"] = None
+    print(json.dumps(out), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
@@ -127,6 +242,9 @@ def main():
               "multi-GPU path (rows of W are independent, so a layer would shard by rows; see DESIGN.md).",
               file=sys.stderr)
         sys.exit(2)
+    if args.dequant:
+        bench_dequant(args)
+        return
 
     import torch
     import post_weight_quantization_20_amd as g

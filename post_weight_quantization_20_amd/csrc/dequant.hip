@@ -8,16 +8,20 @@
 // W[r, k] = s[r, G(k)] * (q[r, k] - z[r, G(k)]), where q is nibble k % 8 of word k / 8 of row r and
 // G(k) is g_idx[k], or k / g when no g_idx is given (groups of g consecutive columns).
 //
-// Two kernels:
-//   dq_fast_kernel     fp16 x, groups of g consecutive columns with g % 32 == 0 (or one group per
-//                      row), d % 32 == 0, 16-byte aligned rows of x. A lane takes 32 columns (one
-//                      16-byte load per weight row) that share a group, so per lane and row
-//                      sum_k x_k W[r,k] = s * (sum_k x_k q_k - z * sum_k x_k). The codes become
+// Three kernels, picked on the host:
+//   dq_fast_kernel     one or two input rows (or more when the matrix-core kernel does not apply):
+//                      fp16 x, groups of g consecutive columns with g % 32 == 0 (or one group per
+//                      row), d % 32 == 0, 16-byte aligned rows of x and codes. A lane takes 32
+//                      columns (one 16-byte load per weight row) that share a group, so per lane and
+//                      row sum_k x_k W[r,k] = s * (sum_k x_k q_k - z * sum_k x_k). The codes become
 //                      exact fp16 integers with the 0x6400 exponent trick, and v_dot2_f32_f16 sums
 //                      fp16 products (exact in fp32) into fp32. The sum of x over the 32 columns is
 //                      shared by every weight row a wave holds.
-//   dq_general_kernel  any x type, any g_idx: per column W[r, k] = s * (q - z) in fp32.
-// Both are HBM-bound at small m: 0.5 byte of codes per weight against m FMAs.
+//   dq_mfma_kernel     3..16 input rows with the same layout conditions and g % 128 == 0: the same
+//                      decoded codes feed v_mfma_f32_16x16x16f16, so the input rows cost no VALU.
+//   dq_general_kernel  any x type, any g_idx (act-order), any g: per column W[r, k] = s * (q - z) in
+//                      fp32, with the rows' (scale, zero) tables staged in LDS when they fit.
+// At small m all three are bound by reading the codes: half a byte per weight against m FMAs.
 #include <hip/hip_runtime.h>
 
 #include "common.hpp"
@@ -26,6 +30,7 @@ namespace gptq {
 namespace {
 
 typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 struct DqArgs {
   const void* x;
@@ -36,8 +41,10 @@ struct DqArgs {
   const float* scales;        // rows x ngroups
   const int32_t* zeros;       // rows x ngroups
   int64_t ngroups, g;
-  uint32_t cpg;               // fast kernel: 32-column chunks per group (0: one group per row)
+  uint32_t cpg;               // dot2 / matrix-core kernels: 32- or 128-column chunks per group (0: one group)
   const int32_t* gidx;        // null: G(k) = k / g
+  int xvec;                   // general kernel: rows of x are 16-byte aligned (vector loads)
+  int gvec;                   // general kernel: gidx is 16-byte aligned
   float* y;                   // m x rows, row pitch ldy
   int64_t ldy;
 };
@@ -58,16 +65,24 @@ GPTQ_DEV float wave_sum(float v) {
 
 GPTQ_DEV half2_t as_h2(uint32_t u) { return __builtin_bit_cast(half2_t, u); }
 
+// (w & mask) | magic in one v_and_or_b32. Written out because a VOP3 instruction takes no literal and
+// one scalar operand here, so the compiler otherwise emits separate AND and OR instructions.
+GPTQ_DEV uint32_t and_or(uint32_t w, uint32_t mask, uint32_t magic) {
+  uint32_t r;
+  asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(r) : "v"(w), "s"(mask), "v"(magic));
+  return r;
+}
+
 // The eight codes of one word as four fp16 pairs (n_t, n_{t+4}), t = 0..3, exact small integers:
 // OR-ing a nibble into the mantissa of 1024.0 (0x6400) gives 1024 + n; a nibble in bits 4..7 gives
 // 1024 + 16 n, which times 1/16 minus 64 is n again. Both steps are exact in fp16.
 GPTQ_DEV void decode_word(uint32_t w, half2_t (&q)[4]) {
   const half2_t m1024 = as_h2(0xE400E400u), r16 = as_h2(0x2C002C00u), m64 = as_h2(0xD400D400u);
   const uint32_t w8 = w >> 8;
-  q[0] = as_h2((w & 0x000F000Fu) | 0x64006400u) + m1024;
-  q[1] = as_h2((w & 0x00F000F0u) | 0x64006400u) * r16 + m64;
-  q[2] = as_h2((w8 & 0x000F000Fu) | 0x64006400u) + m1024;
-  q[3] = as_h2((w8 & 0x00F000F0u) | 0x64006400u) * r16 + m64;
+  q[0] = as_h2(and_or(w, 0x000F000Fu, 0x64006400u)) + m1024;
+  q[1] = as_h2(and_or(w, 0x00F000F0u, 0x64006400u)) * r16 + m64;
+  q[2] = as_h2(and_or(w8, 0x000F000Fu, 0x64006400u)) + m1024;
+  q[3] = as_h2(and_or(w8, 0x00F000F0u, 0x64006400u)) * r16 + m64;
 }
 
 // The matching fp16 pairs (x_t, x_{t+4}) of the eight inputs of one word's columns.
@@ -107,17 +122,61 @@ __global__ __launch_bounds__(256) void dq_fast_kernel(DqArgs a) {
 #pragma unroll
     for (int r = 0; r < R; ++r) acc[i][r] = 0.f;
 
-  for (int64_t v = lane; v < nv; v += 64) {
-    u32x4 w[R];
-#pragma unroll
-    for (int r = 0; r < R; ++r) w[r] = __builtin_nontemporal_load(prow[r] + v);
+  // the next chunk's codes, scales and zeros are loaded before the current chunk is computed
+  // with one or two input rows, their 32 inputs are prefetched too
+  constexpr bool kPreX = MT <= 2;
+  // codes, scales and zeros of the next two chunks (and the next chunk's inputs) are in flight while
+  // a chunk is computed
+  u32x4 wn[R], wn2[R];
+  float sn[R], sn2[R];
+  int32_t zn[R], zn2[R];
+  u32x4 xn[kPreX ? MT : 1][4];
+  auto fetch_codes = [&](int64_t v, u32x4 (&w)[R], float (&sc)[R], int32_t (&zz)[R]) {
     const uint32_t grp = a.cpg ? (uint32_t)v / a.cpg : 0u;
-    float s[R], z[R];
 #pragma unroll
     for (int r = 0; r < R; ++r) {
-      s[r] = srow[r][grp];
-      z[r] = (float)zrow[r][grp];
+      w[r] = __builtin_nontemporal_load(prow[r] + v);
+      sc[r] = srow[r][grp];
+      zz[r] = zrow[r][grp];
     }
+  };
+  auto fetch_inputs = [&](int64_t v) {
+    if constexpr (kPreX) {
+#pragma unroll
+      for (int i = 0; i < MT; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) xn[i][j] = xrow[i][4 * v + j];
+    }
+  };
+  if (lane < nv) {
+    fetch_codes(lane, wn, sn, zn);
+    fetch_inputs(lane);
+  }
+  if (lane + 64 < nv) fetch_codes(lane + 64, wn2, sn2, zn2);
+  for (int64_t v = lane; v < nv; v += 64) {
+    u32x4 w[R];
+    float s[R], z[R];
+    u32x4 xc[kPreX ? MT : 1][4];
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      w[r] = wn[r];
+      s[r] = sn[r];
+      z[r] = (float)zn[r];
+    }
+    if constexpr (kPreX) {
+#pragma unroll
+      for (int i = 0; i < MT; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) xc[i][j] = xn[i][j];
+    }
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      wn[r] = wn2[r];
+      sn[r] = sn2[r];
+      zn[r] = zn2[r];
+    }
+    if (v + 128 < nv) fetch_codes(v + 128, wn2, sn2, zn2);
+    if (v + 64 < nv) fetch_inputs(v + 64);
     float inner[MT][R], sx[MT];
 #pragma unroll
     for (int i = 0; i < MT; ++i) {
@@ -130,7 +189,8 @@ __global__ __launch_bounds__(256) void dq_fast_kernel(DqArgs a) {
       half2_t xp[MT][4];
 #pragma unroll
       for (int i = 0; i < MT; ++i) {
-        pair_inputs(xrow[i][4 * v + j], xp[i]);
+        if constexpr (kPreX) pair_inputs(xc[i][j], xp[i]);
+        else pair_inputs(xrow[i][4 * v + j], xp[i]);
 #pragma unroll
         for (int t = 0; t < 4; ++t) sx[i] = __builtin_amdgcn_fdot2(xp[i][t], ones, sx[i], false);
       }
@@ -160,6 +220,125 @@ __global__ __launch_bounds__(256) void dq_fast_kernel(DqArgs a) {
     }
 }
 
+typedef _Float16 half4_t __attribute__((ext_vector_type(4)));
+
+// 3..16 input rows on the matrix cores. A workgroup owns 16 weight rows; its KS waves split the
+// columns into 128-column units (wave w takes unit pairs w, w + KS, ...), each unit inside one group.
+// v_mfma_f32_16x16x16f16 with A = x (16 input rows, rows >= m zero) and B = the codes as exact fp16
+// integers accumulates T = sum x q over a unit; a second product with B = 1 gives sum x in the same
+// lanes, and s (T - z sum x) is added per unit. Lane l holds B[k][j] and A[i][k] for j, i = l % 16 and
+// k = 4 (l / 16) + 0..3; the k slots of lane group c = l / 16 map to the 32 columns c of the unit in
+// the order (0,4,1,5), (2,6,3,7) of each word, which the decoded pairs and the permuted inputs share.
+// The KS partial tiles are summed in LDS in wave order.
+template <int KS>
+__global__ __launch_bounds__(64 * KS) void dq_mfma_kernel(DqArgs a) {
+  __shared__ floatx4 part[KS][64];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int jl = lane & 15, c = lane >> 4;
+  const int64_t j0 = (int64_t)blockIdx.x * 16;
+  const int64_t row = min(j0 + jl, a.rows - 1);
+  const int64_t nw = a.d >> 3;
+  const u32x4* prow = reinterpret_cast<const u32x4*>(a.packed + row * nw);
+  const float* srow = a.scales + row * a.ngroups;
+  const int32_t* zrow = a.zeros + row * a.ngroups;
+  const bool xval = jl < a.m;
+  const u32x4* xr = reinterpret_cast<const u32x4*>(static_cast<const _Float16*>(a.x) + (int64_t)min(jl, a.m - 1) * a.ldx);
+  const uint32_t units = (uint32_t)(a.d >> 7);
+  const half4_t ones = {(_Float16)1, (_Float16)1, (_Float16)1, (_Float16)1};
+  const half2_t m1024 = as_h2(0xE400E400u), r16 = as_h2(0x2C002C00u), m64 = as_h2(0xD400D400u);
+
+  floatx4 acc = {0.f, 0.f, 0.f, 0.f};
+  // A 128-column unit u: this lane's codes are words 16u + 4c .. +3 of its row and its inputs
+  // columns 128u + 32c .. +31 of input row l % 16; one scale and zero per unit.
+  struct Codes {
+    u32x4 w;
+    float sc;
+    int32_t z;
+  };
+  struct Inputs {
+    u32x4 x[4];
+  };
+  auto load_codes = [&](uint32_t u, Codes& t) {
+    t.w = __builtin_nontemporal_load(prow + 4 * (int64_t)u + c);
+    const uint32_t grp = a.cpg ? u / a.cpg : 0u;
+    t.sc = srow[grp];
+    t.z = zrow[grp];
+  };
+  auto load_inputs = [&](uint32_t u, Inputs& t) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) t.x[q] = xval ? xr[16 * (int64_t)u + 4 * c + q] : u32x4{0u, 0u, 0u, 0u};
+  };
+  auto unit = [&](const Codes& cd, const Inputs& in) {
+    floatx4 T = {0.f, 0.f, 0.f, 0.f}, S = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      half2_t p[4];
+      pair_inputs(in.x[q], p);
+      const uint32_t wd = cd.w[q], w8 = wd >> 8;
+      const half2_t q0 = as_h2(and_or(wd, 0x000F000Fu, 0x64006400u)) + m1024;
+      const half2_t q1 = as_h2(and_or(wd, 0x00F000F0u, 0x64006400u)) * r16 + m64;
+      const half2_t q2 = as_h2(and_or(w8, 0x000F000Fu, 0x64006400u)) + m1024;
+      const half2_t q3 = as_h2(and_or(w8, 0x00F000F0u, 0x64006400u)) * r16 + m64;
+      const half4_t a0 = __builtin_shufflevector(p[0], p[1], 0, 1, 2, 3);
+      const half4_t a1 = __builtin_shufflevector(p[2], p[3], 0, 1, 2, 3);
+      T = __builtin_amdgcn_mfma_f32_16x16x16f16(a0, __builtin_shufflevector(q0, q1, 0, 1, 2, 3), T, 0, 0, 0);
+      S = __builtin_amdgcn_mfma_f32_16x16x16f16(a0, ones, S, 0, 0, 0);
+      T = __builtin_amdgcn_mfma_f32_16x16x16f16(a1, __builtin_shufflevector(q2, q3, 0, 1, 2, 3), T, 0, 0, 0);
+      S = __builtin_amdgcn_mfma_f32_16x16x16f16(a1, ones, S, 0, 0, 0);
+    }
+    const float z = (float)cd.z;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) acc[r] = __builtin_fmaf(cd.sc, __builtin_fmaf(-z, S[r], T[r]), acc[r]);
+  };
+
+  // Unit pairs w, w + KS, ... The codes of the next two pairs and the inputs of the next one are in
+  // flight while a pair is computed (the inputs come from L2, the codes from HBM).
+  const uint32_t pairs = (units + 1) / 2;
+  Codes c1[2], c2[2];
+  Inputs x1[2];
+  auto fetch_codes = [&](uint32_t pr, Codes (&t)[2]) {
+    load_codes(2 * pr, t[0]);
+    if (2 * pr + 1 < units) load_codes(2 * pr + 1, t[1]);
+  };
+  auto fetch_inputs = [&](uint32_t pr) {
+    load_inputs(2 * pr, x1[0]);
+    if (2 * pr + 1 < units) load_inputs(2 * pr + 1, x1[1]);
+  };
+  const uint32_t p0 = wave;
+  if (p0 < pairs) {
+    fetch_codes(p0, c1);
+    fetch_inputs(p0);
+  }
+  if (p0 + KS < pairs) fetch_codes(p0 + KS, c2);
+  for (uint32_t pr = p0; pr < pairs; pr += KS) {
+    const Codes k0 = c1[0], k1 = c1[1];
+    const Inputs i0 = x1[0], i1 = x1[1];
+    c1[0] = c2[0];
+    c1[1] = c2[1];
+    if (pr + 2 * KS < pairs) fetch_codes(pr + 2 * KS, c2);
+    if (pr + KS < pairs) fetch_inputs(pr + KS);
+    unit(k0, i0);
+    if (2 * pr + 1 < units) unit(k1, i1);
+  }
+
+  part[wave][lane] = acc;
+  __syncthreads();
+  if (wave == 0) {
+    floatx4 t = part[0][lane];
+#pragma unroll
+    for (int w = 1; w < KS; ++w) {
+      const floatx4 o = part[w][lane];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) t[r] += o[r];
+    }
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int i = 4 * c + r;
+      if (i < a.m && j0 + jl < a.rows) a.y[(int64_t)i * a.ldy + j0 + jl] = t[r];
+    }
+  }
+}
+
 template <int XT>
 GPTQ_DEV float load_x(const void* x, int64_t idx) {
   if constexpr (XT == F32) return static_cast<const float*>(x)[idx];
@@ -167,16 +346,65 @@ GPTQ_DEV float load_x(const void* x, int64_t idx) {
   else return bf16_bits_to_f32(static_cast<const uint16_t*>(x)[idx]);
 }
 
+// x[row][8 wv .. 8 wv + 7] as floats: one or two 16-byte loads when the rows are 16-byte aligned.
+template <int XT>
+GPTQ_DEV void load_x8(const void* x, int64_t base, bool vec, float (&v)[8]) {
+  if (vec) {
+    if constexpr (XT == F32) {
+      const floatx4 a = *reinterpret_cast<const floatx4*>(static_cast<const float*>(x) + base);
+      const floatx4 b = *reinterpret_cast<const floatx4*>(static_cast<const float*>(x) + base + 4);
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        v[t] = a[t];
+        v[4 + t] = b[t];
+      }
+    } else {
+      const u32x4 u = *reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(x) + base);
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        const uint32_t lo = u[t] & 0xFFFFu, hi = u[t] >> 16;
+        if constexpr (XT == F16) {
+          v[2 * t] = (float)__builtin_bit_cast(_Float16, (uint16_t)lo);
+          v[2 * t + 1] = (float)__builtin_bit_cast(_Float16, (uint16_t)hi);
+        } else {
+          v[2 * t] = __builtin_bit_cast(float, lo << 16);
+          v[2 * t + 1] = __builtin_bit_cast(float, hi << 16);
+        }
+      }
+    }
+  } else {
+#pragma unroll
+    for (int t = 0; t < 8; ++t) v[t] = load_x<XT>(x, base + t);
+  }
+}
+
 // Any input type and any column-to-group map. Lane l takes words l, l + 64, ... of R weight rows.
-template <int XT, int MT, int R>
+// With TAB the workgroup's rows' (scale, zero) tables are first copied to LDS, so that each weight
+// reads its group's pair with one LDS load instead of two global gathers.
+template <int XT, int MT, int R, bool TAB>
 __global__ __launch_bounds__(256) void dq_general_kernel(DqArgs a) {
-  const int lane = threadIdx.x & 63;
-  const int64_t r0 = ((int64_t)blockIdx.x * 4 + (threadIdx.x >> 6)) * R;
+  extern __shared__ u32x2 tab[];   // [4 R][ngroups]: scale bits, zero
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int64_t rb = (int64_t)blockIdx.x * 4 * R;
+  if constexpr (TAB) {
+    const int64_t n = 4 * R * a.ngroups;
+    for (int64_t i = threadIdx.x; i < n; i += 256) {
+      const int64_t wr = i / a.ngroups, G = i - wr * a.ngroups;
+      const int64_t row = min(rb + wr, a.rows - 1);
+      u32x2 e;
+      e.x = __builtin_bit_cast(uint32_t, a.scales[row * a.ngroups + G]);
+      e.y = (uint32_t)a.zeros[row * a.ngroups + G];
+      tab[i] = e;
+    }
+    __syncthreads();
+  }
+  const int64_t r0 = rb + (int64_t)wave * R;
   if (r0 >= a.rows) return;
   const int64_t nw = a.d >> 3;
   int64_t rr[R];
 #pragma unroll
   for (int r = 0; r < R; ++r) rr[r] = min(r0 + r, a.rows - 1);
+  const bool xvec = a.xvec != 0;
   float acc[MT][R];
 #pragma unroll
   for (int i = 0; i < MT; ++i)
@@ -187,20 +415,42 @@ __global__ __launch_bounds__(256) void dq_general_kernel(DqArgs a) {
     uint32_t w[R];
 #pragma unroll
     for (int r = 0; r < R; ++r) w[r] = a.packed[rr[r] * nw + wv];
+    int32_t gk[8];
+    if (a.gidx && a.gvec) {
+      const u32x4 g0 = *reinterpret_cast<const u32x4*>(a.gidx + 8 * wv);
+      const u32x4 g1 = *reinterpret_cast<const u32x4*>(a.gidx + 8 * wv + 4);
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        gk[t] = (int32_t)g0[t];
+        gk[4 + t] = (int32_t)g1[t];
+      }
+    } else if (a.gidx) {
+#pragma unroll
+      for (int t = 0; t < 8; ++t) gk[t] = a.gidx[8 * wv + t];
+    } else {
+#pragma unroll
+      for (int t = 0; t < 8; ++t) gk[t] = (int32_t)((8 * wv + t) / a.g);
+    }
     float xv[MT][8];
 #pragma unroll
-    for (int i = 0; i < MT; ++i)
-#pragma unroll
-      for (int t = 0; t < 8; ++t) xv[i][t] = load_x<XT>(a.x, (int64_t)min(i, a.m - 1) * a.ldx + 8 * wv + t);
+    for (int i = 0; i < MT; ++i) load_x8<XT>(a.x, (int64_t)min(i, a.m - 1) * a.ldx + 8 * wv, xvec, xv[i]);
 #pragma unroll
     for (int t = 0; t < 8; ++t) {
-      const int64_t k = 8 * wv + t;
-      int64_t G = a.gidx ? (int64_t)a.gidx[k] : k / a.g;
-      G = G < 0 ? 0 : G >= a.ngroups ? a.ngroups - 1 : G;   // out-of-range entries are clamped
+      const int64_t G = gk[t] < 0 ? 0 : gk[t] >= a.ngroups ? a.ngroups - 1 : gk[t];   // clamped
 #pragma unroll
       for (int r = 0; r < R; ++r) {
         const int32_t q = (int32_t)((w[r] >> (4 * t)) & 15u);
-        const float wq = a.scales[rr[r] * a.ngroups + G] * (float)(q - a.zeros[rr[r] * a.ngroups + G]);
+        float sc;
+        int32_t z;
+        if constexpr (TAB) {
+          const u32x2 e = tab[(wave * R + r) * a.ngroups + G];
+          sc = __builtin_bit_cast(float, e.x);
+          z = (int32_t)e.y;
+        } else {
+          sc = a.scales[rr[r] * a.ngroups + G];
+          z = a.zeros[rr[r] * a.ngroups + G];
+        }
+        const float wq = sc * (float)(q - z);
 #pragma unroll
         for (int i = 0; i < MT; ++i) acc[i][r] = __builtin_fmaf(xv[i][t], wq, acc[i][r]);
       }
@@ -233,7 +483,11 @@ hipError_t launch_fast(const DqArgs& a, hipStream_t s) {
 template <int XT, int MT, int R>
 hipError_t launch_general(const DqArgs& a, hipStream_t s) {
   const int64_t wgs = (a.rows + 4 * R - 1) / (4 * R);
-  hipLaunchKernelGGL((dq_general_kernel<XT, MT, R>), dim3((unsigned)wgs), dim3(256), 0, s, a);
+  const int64_t tab_bytes = 4 * R * a.ngroups * (int64_t)sizeof(u32x2);
+  if (tab_bytes <= 65536)
+    hipLaunchKernelGGL((dq_general_kernel<XT, MT, R, true>), dim3((unsigned)wgs), dim3(256), (size_t)tab_bytes, s, a);
+  else
+    hipLaunchKernelGGL((dq_general_kernel<XT, MT, R, false>), dim3((unsigned)wgs), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 
@@ -259,6 +513,13 @@ hipError_t dispatch(const DqArgs& a, int dtype, bool fast, int R, hipStream_t s)
 
 }  // namespace
 
+// The matrix-core kernel: fp16 inputs, groups of whole 128-column units, aligned rows.
+bool dequant_mfma_path(const void* x, int dtype, int64_t ldx, const int32_t* packed, const int32_t* gidx, int64_t d,
+                       int64_t g) {
+  return dtype == F16 && !gidx && d % 128 == 0 && (g >= d || g % 128 == 0) && ldx % 8 == 0 &&
+         reinterpret_cast<uintptr_t>(x) % 16 == 0 && reinterpret_cast<uintptr_t>(packed) % 16 == 0;
+}
+
 bool dequant_fast_path(const void* x, int dtype, int64_t ldx, const int32_t* packed, const int32_t* gidx, int64_t d,
                        int64_t g) {
   return dtype == F16 && !gidx && d % 32 == 0 && (g >= d || g % 32 == 0) && ldx % 8 == 0 &&
@@ -269,13 +530,16 @@ hipError_t dequant_gemm(const void* x, int dtype, int64_t m, int64_t ldx, const 
                         const int32_t* zeros, const int32_t* gidx, int64_t rows, int64_t d, int64_t g, float* y,
                         int64_t ldy, hipStream_t s) {
   const bool fast = dequant_fast_path(x, dtype, ldx, packed, gidx, d, g);
+  // two input rows still run faster on the dot2 kernel (fc2: 90 against 108 us); three or more do not
+  const bool mfma = m >= 3 && dequant_mfma_path(x, dtype, ldx, packed, gidx, d, g);
   const int R = rows_per_wave(rows);
   const int64_t esz = dtype == F32 ? 4 : 2;
-  for (int64_t i0 = 0; i0 < m; i0 += 8) {
+  const int64_t step = mfma ? 16 : 8;
+  for (int64_t i0 = 0; i0 < m; i0 += step) {
     DqArgs a{};
     a.x = static_cast<const char*>(x) + i0 * ldx * esz;
     a.ldx = ldx;
-    a.m = (int)std::min<int64_t>(8, m - i0);
+    a.m = (int)std::min<int64_t>(step, m - i0);
     a.packed = reinterpret_cast<const uint32_t*>(packed);
     a.rows = rows;
     a.d = d;
@@ -283,15 +547,32 @@ hipError_t dequant_gemm(const void* x, int dtype, int64_t m, int64_t ldx, const 
     a.zeros = zeros;
     a.g = g;
     a.ngroups = (d + g - 1) / g;
-    a.cpg = g >= d ? 0u : (uint32_t)(g / 32);
     a.gidx = gidx;
     a.y = y + i0 * ldy;
     a.ldy = ldy;
-    // weight rows per wave times input rows stays at most 8 (the accumulators' registers)
-    hipError_t e = a.m == 1   ? dispatch<1>(a, dtype, fast, R, s)
-                   : a.m == 2 ? dispatch<2>(a, dtype, fast, R, s)
-                   : a.m <= 4 ? dispatch<4>(a, dtype, fast, std::min(R, 2), s)
-                              : dispatch<8>(a, dtype, fast, 1, s);
+    hipError_t e;
+    if (mfma && a.m >= 3) {
+      // units per group; waves per workgroup so that about 12 waves per CU are in flight
+      a.cpg = g >= d ? 0u : (uint32_t)(g / 128);
+      const int64_t wgs = (rows + 15) / 16;
+      if (wgs >= 768) {
+        hipLaunchKernelGGL(dq_mfma_kernel<4>, dim3((unsigned)wgs), dim3(256), 0, s, a);
+      } else if (wgs >= 384) {
+        hipLaunchKernelGGL(dq_mfma_kernel<8>, dim3((unsigned)wgs), dim3(512), 0, s, a);
+      } else {
+        hipLaunchKernelGGL(dq_mfma_kernel<16>, dim3((unsigned)wgs), dim3(1024), 0, s, a);
+      }
+      e = hipGetLastError();
+    } else {
+      a.cpg = fast && g < d ? (uint32_t)(g / 32) : 0u;
+      a.xvec = ldx % (dtype == F32 ? 4 : 8) == 0 && reinterpret_cast<uintptr_t>(a.x) % 16 == 0;
+      a.gvec = gidx && reinterpret_cast<uintptr_t>(gidx) % 16 == 0;
+      // weight rows per wave times input rows stays at most 8 (the accumulators' registers)
+      e = a.m == 1   ? dispatch<1>(a, dtype, fast, R, s)
+          : a.m == 2 ? dispatch<2>(a, dtype, fast, R, s)
+          : a.m <= 4 ? dispatch<4>(a, dtype, fast, std::min(R, 2), s)
+                     : dispatch<8>(a, dtype, fast, 1, s);
+    }
     if (e != hipSuccess) return e;
   }
   return hipSuccess;

@@ -34,7 +34,7 @@ def _bound(x64, L, d):
     return 2.0 * (d / 64 + 48) * U32 * S
 
 
-def _gpu(L, x, xdtype, d, bits=4, pass_gidx=True, ldx_pad=0):
+def _gpu(L, x, xdtype, d, bits=4, pass_gidx=True, ldx_pad=0, gidx_offset=0):
     torch = torch_cuda()
     import post_weight_quantization_20_amd as g
     codes = dev_tensor(L.codes, "u8")
@@ -44,7 +44,10 @@ def _gpu(L, x, xdtype, d, bits=4, pass_gidx=True, ldx_pad=0):
         xs = np.zeros((x.shape[0], d + ldx_pad), dtype=x.dtype)
         xs[:, :d] = x
     xd = dev_tensor(xs, xdtype)[:, :d]
-    gi = dev_tensor(L.g_idx, "i32") if (L.g_idx is not None and pass_gidx) else None
+    gi = None
+    if L.g_idx is not None and pass_gidx:
+        # gidx_offset > 0 hands over a g_idx that is not 16-byte aligned (a view one element in)
+        gi = dev_tensor(np.concatenate([np.zeros(gidx_offset, np.int32), L.g_idx]), "i32")[gidx_offset:]
     y = g.gptq_dequant_gemm(xd, packed, dev_tensor(L.scales, "f32"), dev_tensor(L.zeros, "i32"), d, L.group_size,
                             g_idx=gi, bits=bits)
     torch.cuda.synchronize()
@@ -79,6 +82,27 @@ def test_exact_inputs_bit_identical(name, xdt, rows, d, m, gs, act):
     assert np.array_equal(y.astype(np.float64), want)
 
 
+MFMA_CASES = [
+    # (rows, d, m, group_size): the matrix-core kernel takes fp16 inputs, 3..16 rows per pass and
+    # groups of whole 128-column units; 16, 8 or 4 waves per workgroup by the row count
+    (300, 4096, 3, 128),
+    (300, 1152, 16, 128),       # an odd number of 128-column units
+    (45, 384, 17, 0),           # 16 rows on the matrix cores, then one on the dot2 kernel
+    (45, 384, 18, 0),           # then two on the dot2 kernel
+    (8200, 512, 5, 256),        # 8 waves per workgroup
+    (12300, 256, 33, 128),      # 4 waves per workgroup; passes of 16, 16 and 1
+]
+
+
+@pytest.mark.parametrize("rows,d,m,gs", MFMA_CASES, ids=[f"r{c[0]}-d{c[1]}-m{c[2]}-g{c[3]}" for c in MFMA_CASES])
+def test_matrix_core_kernel_exact(rows, d, m, gs):
+    print(f"[dequant mfma exact] rows {rows} d {d} m {m} g {gs}", flush=True)
+    L = synth.stored_layer(21, rows, d, 4, gs, exact=True)
+    x = synth.inference_x(22, m, d, "f16", exact=True)
+    y = _gpu(L, x, "f16", d)
+    assert np.array_equal(y.astype(np.float64), _oracle(L, synth.to_f64(x, "f16"), d))
+
+
 @pytest.mark.parametrize("rows,m", [(8200, 2), (4100, 1), (4100, 8), (8193, 4)])
 def test_rows_per_wave_variants_exact(rows, m):
     """Row counts that select four, two and one weight rows per wave, each with a ragged last wave."""
@@ -91,9 +115,13 @@ def test_rows_per_wave_variants_exact(rows, m):
 
 
 BOUND_CASES = [
-    ("fast g128", "f16", 500, 4096, 3, 128, False, 0),
+    ("fast g128", "f16", 500, 4096, 1, 128, False, 0),
+    ("mfma g128", "f16", 500, 4096, 3, 128, False, 0),
+    ("mfma per-row m16", "f16", 300, 8192, 16, 0, False, 0),
     ("fast per-row 3-bit", "f16", 64, 8192, 1, 0, False, 0),
     ("general act-order", "f16", 200, 4096, 4, 128, True, 0),
+    ("general act-order unaligned g_idx", "f16", 70, 1024, 1, 64, True, 0),
+    ("general act-order many groups", "f16", 70, 8192, 2, 16, True, 0),     # tables too big for LDS
     ("general unaligned x", "f16", 50, 2048, 2, 128, False, 3),
     ("general bf16", "bf16", 50, 2048, 6, 32, False, 0),
     ("general f32", "f32", 50, 2048, 16, 128, True, 0),
@@ -106,7 +134,8 @@ def test_normal_inputs_within_bound(name, xdt, rows, d, m, gs, act, pad):
     bits = 3 if "3-bit" in name else 4
     L = synth.stored_layer(15, rows, d, bits, gs, act_order=act)
     x = synth.inference_x(16, m, d, xdt)
-    y = _gpu(L, x, xdt, d, bits=bits, ldx_pad=pad).astype(np.float64)
+    y = _gpu(L, x, xdt, d, bits=bits, ldx_pad=pad, gidx_offset=1 if "unaligned g_idx" in name else 0)
+    y = y.astype(np.float64)
     x64 = synth.to_f64(x, xdt)
     want = _oracle(L, x64, d, bits)
     err = np.abs(y - want)
