@@ -29,13 +29,18 @@ Readings taken where the pages are silent, garbled or disagree (each is listed i
   damp * trace(H) (Technical Guide, "Damping Factor").
 * Grids are asymmetric min/max grids with unsigned codes in [0, 2^bits - 1]; a group is g
   consecutive columns of one row in processing order; group_size <= 0 means one group per row.
-* A group's grid is computed from the current (error-updated) weights at the group's first column.
+* A symmetric grid is the same min/max recipe on [-max|w|, max|w|] with the zero fixed at the middle
+  code 2^(bits - 1) (the Technical Guide's signed int4 range [-8, 7] as unsigned codes).
+* A group's grid is computed from the current (error-updated) weights at the group's first column;
+  with static groups, from the original weights of g consecutive original columns, before the loop.
 * Blocks and groups must nest (B % g == 0 or g % B == 0); the last block and last group may be short.
 * Act-order processes columns by descending diag(H); ties keep the lower original index first.
 * Rounding is round-half-to-even (numpy rint), as torch.round in the sketch.
 
 Parity unpinned (no example on the pages fixes them; they rest on the readings above): the moment a
-group grid is taken when g < d, and the act-order tie-break.
+group grid is taken when g < d, the act-order tie-break, the symmetric grid's scale (the pages give
+its code range and value = code x scale, not how the scale is chosen) and what static groups mean
+(the pages give only the setting's name).
 """
 
 from __future__ import annotations
@@ -146,13 +151,21 @@ def _ratio32(num, den) -> np.ndarray:
     return (np.asarray(num, dtype=np.float32) / np.asarray(den, dtype=np.float32)).astype(np.float64)
 
 
-def group_grid(wg: np.ndarray, maxq: int) -> Tuple[np.ndarray, np.ndarray]:
-    """Asymmetric min/max grid of each row of wg (rows x columns of one group).
+def group_grid(wg: np.ndarray, maxq: int, sym: bool = False) -> Tuple[np.ndarray, np.ndarray]:
+    """Min/max grid of each row of wg (rows x columns of one group).
 
-    scale = max(wmax - wmin, 1e-8) / maxq and zero = round(-wmin / scale).
+    Asymmetric (the sketch): scale = max(wmax - wmin, 1e-8) / maxq and zero = round(-wmin / scale).
+    Symmetric (tools page, "Optional refinements", grids without a zero point to fit; the Technical
+    Guide's int4 range [-8, 7] with value = code x scale): the same recipe on the range [-m, m],
+    m = max(|wmin|, |wmax|), so scale = max(2 m, 1e-8) / maxq, with the zero fixed at the middle code
+    (maxq + 1) / 2 = 2^(bits - 1), which turns the signed range into unsigned codes [0, maxq].
     """
     wmin = np.min(wg, axis=1)
     wmax = np.max(wg, axis=1)
+    if sym:
+        m = np.maximum(np.abs(wmin), np.abs(wmax))
+        scale = np.maximum(2.0 * m, 1e-8) / float(maxq)
+        return scale, np.full(scale.shape, float((maxq + 1) // 2))
     scale = np.maximum(wmax - wmin, 1e-8) / float(maxq)
     zero = _round_ratio(-wmin, scale)
     return scale, zero
@@ -216,7 +229,8 @@ def _follow_pick(own: np.ndarray, ratio: np.ndarray, offset: np.ndarray, lo: flo
 
 def quantize_layer(W: np.ndarray, U: np.ndarray, bits: int, group_size: int, block_size: int,
                    perm: Optional[np.ndarray] = None, grid: Optional[Tuple[np.ndarray, np.ndarray]] = None,
-                   follow: Optional[Tuple[np.ndarray, np.ndarray]] = None, tau: float = 1e-3) -> QuantResult:
+                   follow: Optional[Tuple[np.ndarray, np.ndarray]] = None, tau: float = 1e-3,
+                   sym: bool = False, static_groups: bool = False) -> QuantResult:
     """Quantize W (rows x d, original column order) with U (upper, processing order).
 
     For each block of B columns in processing order, and each column i in it:
@@ -228,6 +242,11 @@ def quantize_layer(W: np.ndarray, U: np.ndarray, bits: int, group_size: int, blo
     Step 8: one (scale, zero) per group; codes are returned in the original column order with g_idx.
 
     grid: optional fixed (scales, zeros), rows x ngroups, used instead of min/max grids.
+    sym: symmetric grids (see group_grid).
+    static_groups: every group's grid is fixed before the loop from the original weights of g
+    consecutive original columns (the Technical Guide's static_groups setting; the pages give only
+    its name, so this plain reading of "static" is parity-unpinned); column i then uses the grid of
+    group perm[i] // g, and g_idx is k // g whatever the order.
     follow: optional (codes, zeros) of another implementation in processing order; at decisions whose
     float32 ratio lies within `tau` of a half-integer this oracle takes that implementation's choice
     when it is one of the two nearest grid points (both are correct roundings within the tie window).
@@ -254,19 +273,36 @@ def quantize_layer(W: np.ndarray, U: np.ndarray, bits: int, group_size: int, blo
     f_zeros = None if follow is None else np.asarray(follow[1], dtype=np.float64)
     adopted = adopted_diff = near = 0
 
+    if static_groups and grid is None:
+        for gi in range(ngroups):
+            cols = slice(gi * g, min((gi + 1) * g, d))
+            sg, zg = group_grid(W[:, cols], maxq, sym)
+            if f_zeros is not None and not sym:
+                wmin = np.min(W[:, cols], axis=1)
+                zg, a, ad, nt = _follow_pick(zg, _ratio32(-wmin, sg), np.zeros(rows), -np.inf, np.inf,
+                                             f_zeros[:, gi], tau)
+                adopted += a
+                adopted_diff += ad
+                near += nt
+            scales[:, gi] = sg
+            zeros[:, gi] = zg
+
     s = z = None
     for b in range(0, d, B):
         e_blk = min(b + B, d)
         Err = np.zeros((rows, e_blk - b), dtype=np.float64)
         for i in range(b, e_blk):
-            if i % g == 0:
+            if static_groups and grid is None:
+                s = scales[:, perm[i] // g]
+                z = zeros[:, perm[i] // g]
+            elif i % g == 0:
                 gi = i // g
                 if grid is not None:
                     s = np.asarray(grid[0], dtype=np.float64)[:, gi]
                     z = np.asarray(grid[1], dtype=np.float64)[:, gi]
                 else:
-                    s, z = group_grid(Wp[:, i:min(i + g, d)], maxq)
-                    if f_zeros is not None:
+                    s, z = group_grid(Wp[:, i:min(i + g, d)], maxq, sym)
+                    if f_zeros is not None and not sym:
                         wmin = np.min(Wp[:, i:min(i + g, d)], axis=1)
                         z, a, ad, nt = _follow_pick(z, _ratio32(-wmin, s), np.zeros(rows), -np.inf, np.inf,
                                                     f_zeros[:, gi], tau)
@@ -301,7 +337,10 @@ def quantize_layer(W: np.ndarray, U: np.ndarray, bits: int, group_size: int, blo
     Q = np.zeros((rows, d), dtype=np.float64)
     Q[:, perm] = Qp
     g_idx = np.zeros(d, dtype=np.int32)
-    g_idx[perm] = (np.arange(d) // g).astype(np.int32)
+    if static_groups:
+        g_idx[:] = (np.arange(d) // g).astype(np.int32)
+    else:
+        g_idx[perm] = (np.arange(d) // g).astype(np.int32)
     return QuantResult(codes=codes, scales=scales, zeros=zeros.astype(np.int32), g_idx=g_idx, perm=perm,
                        loss=float(np.sum(row_loss)), row_loss=row_loss, Q=Q,
                        codes_proc=codes_p.astype(np.uint8), w_seen=seen, adopted=adopted, adopted_diff=adopted_diff,
@@ -383,19 +422,22 @@ class LayerResult:
 def gptq(W: np.ndarray, chunks: Iterable[np.ndarray], bits: int, group_size: int, block_size: int,
          act_order: bool = False, damp: float = 0.01, perm: Optional[np.ndarray] = None,
          follow: Optional[Tuple[np.ndarray, np.ndarray]] = None, tau: float = 1e-3,
-         H: Optional[np.ndarray] = None, n: Optional[int] = None) -> LayerResult:
+         H: Optional[np.ndarray] = None, n: Optional[int] = None, sym: bool = False,
+         static_groups: bool = False) -> LayerResult:
     """The whole single-layer solver: Hessian, damping and order, factor, column loop, packing."""
     if H is None:
         H, n = hessian(chunks)
     Hhat, p, lam = damp_and_order(H, n, damp, act_order, perm)
     U = inverse_cholesky_upper(Hhat)
-    qr = quantize_layer(W, U, bits, group_size, block_size, perm=p, follow=follow, tau=tau)
+    qr = quantize_layer(W, U, bits, group_size, block_size, perm=p, follow=follow, tau=tau, sym=sym,
+                        static_groups=static_groups)
     d = qr.codes.shape[1]
     packed = pack(qr.codes, bits) if (d % 8 == 0 and bits <= 4) else None
     return LayerResult(H=H, n=n, Hhat=Hhat, lam=lam, U=U, quant=qr, packed=packed)
 
 
-def rtn(W: np.ndarray, bits: int, group_size: int, perm: Optional[np.ndarray] = None) -> QuantResult:
+def rtn(W: np.ndarray, bits: int, group_size: int, perm: Optional[np.ndarray] = None,
+        sym: bool = False) -> QuantResult:
     """Round-to-nearest baseline: the same grids, taken from the unmodified weights, no feedback."""
     W = np.asarray(W, dtype=np.float64)
     rows, d = W.shape
@@ -410,7 +452,7 @@ def rtn(W: np.ndarray, bits: int, group_size: int, perm: Optional[np.ndarray] = 
     zeros = np.zeros((rows, ngroups))
     for gi in range(ngroups):
         sl = slice(gi * g, min((gi + 1) * g, d))
-        s, z = group_grid(Wp[:, sl], maxq)
+        s, z = group_grid(Wp[:, sl], maxq, sym)
         q, dq = quantize_to_grid(Wp[:, sl], s[:, None], z[:, None], maxq)
         codes_p[:, sl] = q
         Qp[:, sl] = dq

@@ -23,8 +23,8 @@ MUTATIONS = [
     ("unscaled error", "err = (w - dq) / U[i, i]", "err = (w - dq)"),
     ("transposed lazy operand", "Wp[:, e_blk:] -= Err @ U[b:e_blk, e_blk:]",
      "Wp[:, e_blk:] -= Err @ U[e_blk:, b:e_blk].T[:, :U.shape[0] - e_blk]"),
-    ("grid from original weights", "s, z = group_grid(Wp[:, i:min(i + g, d)], maxq)",
-     "s, z = group_grid(W[:, perm][:, i:min(i + g, d)], maxq)"),
+    ("grid from original weights", "s, z = group_grid(Wp[:, i:min(i + g, d)], maxq, sym)",
+     "s, z = group_grid(W[:, perm][:, i:min(i + g, d)], maxq, sym)"),
     ("zero not added", "q = np.clip(_round_ratio(w, scale) + zero, 0.0, float(maxq))",
      "q = np.clip(_round_ratio(w, scale), 0.0, float(maxq))"),
     ("inverse not factored", "    u, info = lapack.dpotrf(inv, lower=0, clean=1)",
@@ -36,6 +36,13 @@ MUTATIONS = [
     ("pack nibble order", "words |= c[:, t::8].astype(np.uint64) << np.uint64(4 * t)",
      "words |= c[:, t::8].astype(np.uint64) << np.uint64(4 * (7 - t))"),
     ("dequant zero not subtracted", "return s * (codes - z)", "return s * codes"),
+    ("symmetric zero at code 0", "return scale, np.full(scale.shape, float((maxq + 1) // 2))",
+     "return scale, np.zeros(scale.shape)"),
+    ("symmetric scale from one side", "m = np.maximum(np.abs(wmin), np.abs(wmax))", "m = np.abs(wmax)"),
+    ("static grid in processing order", "sg, zg = group_grid(W[:, cols], maxq, sym)",
+     "sg, zg = group_grid(W[:, perm][:, cols], maxq, sym)"),
+    ("static g_idx follows the order", "g_idx[:] = (np.arange(d) // g).astype(np.int32)",
+     "g_idx[perm] = (np.arange(d) // g).astype(np.int32)"),
     ("dequant groups by position", "g = np.asarray(g_idx, dtype=np.int64)",
      "g = np.arange(d) * len(np.unique(g_idx)) // d"),
     ("dequant product transposed", "return np.asarray(x, dtype=np.float64) @ W.T",
@@ -115,6 +122,16 @@ def _checks(m):
                              np.array([[2, 12], [8, 0]]), np.array([0, 0, 1, 1] * 4), 16)
         if y.shape != (2, 2) or not np.array_equal(y, np.array([[-0.25, 14.0], [-14.75, 50.0]])):
             failed.append("dequant hand example")
+        # symmetric grids: H = I reduces to symmetric round-to-nearest; the zero is the middle code
+        rs = m.gptq(W, None, 4, 16, 32, H=np.eye(d) * 2.0, n=1, sym=True)
+        if not np.array_equal(rs.quant.codes, ref.rtn(W, 4, 16, sym=True).codes) or np.any(rs.quant.zeros != 8):
+            failed.append("symmetric identity -> rtn")
+        # static groups with act-order: H diagonal reduces to round-to-nearest over original columns
+        Hd = np.diag(np.linspace(3.0, 1.0, d)[::-1]) * 2.0
+        rst = m.gptq(W, None, 4, 16, 32, H=Hd, n=1, act_order=True, static_groups=True)
+        if (not np.array_equal(rst.quant.codes, ref.rtn(W, 4, 16).codes)
+                or not np.array_equal(rst.quant.g_idx, np.arange(d) // 16)):
+            failed.append("static identity -> original-order rtn")
         # H = I must reduce to round-to-nearest with dynamic grids
         rI = m.gptq(W, None, 4, 16, 32, H=np.eye(d) * 2.0, n=1)
         if not np.array_equal(rI.quant.codes, ref.rtn(W, 4, 16).codes):

@@ -471,3 +471,76 @@ def test_dequantize_reproduces_column_loop_weights(act):
     assert np.array_equal(w, q.Q)
     y = ref.dequant_matmul(X[:5], ref.pack(q.codes, 4), q.scales, q.zeros, q.g_idx, d)
     assert np.allclose(y, X[:5] @ q.Q.T, rtol=1e-13, atol=1e-13)
+
+
+# ---------------------------------------------------------------- symmetric grid and static groups
+
+def test_symmetric_grid_single_weight_example():
+    """Technical Guide, 'Example: Quantizing a Single Weight': int4 range [-8, 7], scale 0.1, the weight
+    0.7382594 takes the signed code 7 and dequantizes to 0.7 (error 0.0382594). As unsigned codes with
+    the symmetric zero 8 that is code 15."""
+    e = GOLD["single_weight"]
+    q, dq = ref.quantize_to_grid(np.array([e["original"]]), np.array([e["scale"]]), np.array([8.0]), 15)
+    assert q[0] - 8 == e["quantized"]
+    assert dq[0] == pytest.approx(e["dequantized"], abs=1e-12)
+    assert e["original"] - dq[0] == pytest.approx(e["error"], abs=1e-12)
+    _, z = ref.group_grid(np.array([[-0.2, 0.5]]), 15, sym=True)
+    assert z[0] == 8                                   # the middle code of [0, 15], signed range [-8, 7]
+
+
+@pytest.mark.parametrize("bits,zero", [(4, 8), (3, 4), (2, 2)])
+def test_symmetric_grid_closed_form(bits, zero):
+    maxq = (1 << bits) - 1
+    wg = np.array([[-0.3, 0.7, 0.1], [-0.9, 0.2, 0.0], [0.0, 0.0, 0.0]])
+    s, z = ref.group_grid(wg, maxq, sym=True)
+    assert np.allclose(s, [1.4 / maxq, 1.8 / maxq, 1e-8 / maxq], rtol=1e-15)
+    assert np.all(z == zero)
+    # values are (code - zero) steps, so the range is [-zero, maxq - zero] steps: the positive
+    # extreme m = 0.9 (m / s = maxq / 2) clips to maxq - zero steps; 0.2 rounds to nearest
+    q, dq = ref.quantize_to_grid(np.array([0.9, 0.2]), s[[1, 1]], z[[1, 1]], maxq)
+    assert q[0] == maxq and dq[0] == pytest.approx((maxq - zero) * 1.8 / maxq)
+    assert q[1] == zero + np.rint(0.2 * maxq / 1.8) and dq[1] == pytest.approx((q[1] - zero) * 1.8 / maxq)
+
+
+def test_symmetric_identity_hessian_is_rtn():
+    """With H = I there is no error feedback: symmetric GPTQ equals symmetric round-to-nearest."""
+    rng = np.random.default_rng(23)
+    W = rng.standard_normal((8, 64)) * 0.02
+    r = ref.gptq(W, None, 4, 16, 32, H=np.eye(64) * 2.0, n=1, sym=True)
+    t = ref.rtn(W, 4, 16, sym=True)
+    assert np.array_equal(r.quant.codes, t.codes)
+    assert np.all(r.quant.zeros == 8)
+
+
+@pytest.mark.parametrize("act", [False, True])
+def test_static_groups_take_original_column_grids(act):
+    """Static groups: every group's grid is the min/max grid of g consecutive original columns of the
+    original weights, g_idx is k // g, and the stored layer dequantizes to the loop's weights."""
+    rng = np.random.default_rng(29)
+    d, g = 64, 16
+    X = _correlated_x(rng, 96, d) * rng.uniform(0.3, 3.0, d)[None, :]
+    W = rng.standard_normal((10, d)) * 0.02
+    r = ref.gptq(W, [X], 4, g, 32, act_order=act, static_groups=True)
+    q = r.quant
+    for G in range(d // g):
+        wg = W[:, G * g:(G + 1) * g]
+        s_want = np.maximum(wg.max(1) - wg.min(1), 1e-8) / 15
+        assert np.allclose(q.scales[:, G], s_want, rtol=1e-14)
+        assert np.array_equal(q.zeros[:, G], np.rint((-wg.min(1)).astype(np.float32) / s_want.astype(np.float32)))
+    assert np.array_equal(q.g_idx, np.arange(d) // g)
+    assert np.array_equal(ref.dequantize(ref.pack(q.codes, 4), q.scales, q.zeros, q.g_idx, d), q.Q)
+    r1 = ref.gptq(W, [X], 4, g, 1, act_order=act, static_groups=True)
+    assert np.array_equal(r1.quant.codes, q.codes)          # blocked == unblocked
+
+
+def test_static_groups_identity_hessian_is_original_order_rtn():
+    """With H = I and act-order, static groups reduce to round-to-nearest over groups of consecutive
+    original columns (dynamic groups would instead group consecutive processing positions)."""
+    rng = np.random.default_rng(31)
+    d = 64
+    W = rng.standard_normal((8, d)) * 0.02
+    H = np.diag(rng.uniform(1.0, 3.0, d)) * 2.0
+    r = ref.gptq(W, None, 4, 16, 32, H=H, n=1, act_order=True, static_groups=True)
+    assert np.array_equal(r.quant.codes, ref.rtn(W, 4, 16).codes)
+    rd = ref.gptq(W, None, 4, 16, 32, H=H, n=1, act_order=True)
+    assert np.array_equal(rd.quant.codes, ref.rtn(W, 4, 16, perm=rd.quant.perm).codes)
