@@ -51,7 +51,7 @@ enum {
   GPTQ_OK = 0,
   GPTQ_EINVAL = -1,       /* invalid argument (null pointer, bad size, inconsistent settings)   */
   GPTQ_ENOTPD = -2,       /* damped Hessian not positive definite (see gptq_factor's info)      */
-  GPTQ_EUNSUPPORTED = -3, /* a setting this library does not implement (symmetric grid, ...)   */
+  GPTQ_EUNSUPPORTED = -3, /* a setting this library does not implement (e.g. block_size > 128)  */
   GPTQ_EHIP = -4,         /* a HIP runtime call or kernel launch failed                         */
   GPTQ_ENOMEM = -5        /* the workspace passed is smaller than gptq_workspace_bytes asks     */
 };
@@ -71,8 +71,17 @@ typedef struct {
                             A group size of 1 is rejected (Technical Guide, "Don'ts").          */
   int32_t block_size;    /* lazy-batch width B, 1..128 (tools page, Step 7: "often 128")        */
   int32_t act_order;     /* 1: process columns by descending diag(H) (tools page, Act-order)     */
-  int32_t sym;           /* must be 0: only the asymmetric min/max grid is implemented           */
-  int32_t static_groups; /* must be 0: group grids are taken when a group starts                 */
+  int32_t sym;           /* 0: asymmetric min/max grid, zero = round(-wmin / scale); 1: symmetric
+                            grid (tools page, "Optional refinements"): scale = max(2 max|w|, 1e-8)
+                            / maxq and zero = 2^(bits-1), the middle code, so value = scale x
+                            (code - zero) spans the Technical Guide's signed range [-8, 7] steps
+                            at 4 bits. Codes stay unsigned in [0, 2^bits - 1].                  */
+  int32_t static_groups; /* 0: a group's grid is taken from the current, error-updated weights
+                            when the loop reaches the group's first column (groups are g
+                            consecutive processing positions); 1: every grid is fixed before the
+                            loop from the original weights of g consecutive original columns,
+                            each column uses its original group's grid, and g_idx = k / g also
+                            with act-order (the Technical Guide's static_groups setting).        */
   double damp;           /* relative damping >= 0: lambda = damp * mean(diag(H / n)) (Step 4)     */
 } gptq_params_t;
 
@@ -135,7 +144,8 @@ gptq_status_t gptq_factor(const float *H, int64_t d, int64_t n_total, const gptq
  *   codes   device uint8[rows * d], output: codes in [0, 2^bits - 1], original column order.
  *   scales  device float[rows * ngroups], zeros device int32[rows * ngroups], output, with
  *           ngroups = ceil(d / g) and g = group_size (d when group_size <= 0). Group j of a row
- *           covers processing positions [j g, (j+1) g); dequantized value = scale * (code - zero).
+ *           covers processing positions [j g, (j+1) g), or original columns [j g, (j+1) g) with
+ *           static_groups; dequantized value = scale * (code - zero).
  *   g_idx   device int32[d], output: the group of each original column.
  *   loss    device double[1], output: the sum over rows and columns of err^2, where err is a
  *           column's rounding error divided by the factor's diagonal entry; it equals

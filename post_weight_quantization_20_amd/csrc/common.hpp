@@ -31,12 +31,21 @@ GPTQ_DEV float load_as_f32(const void* p, int dtype, int64_t idx) {
 }
 
 // ------------------------------------------------------------------ the quantization grid
-// Asymmetric min/max grid of one group: scale = max(wmax - wmin, 1e-8) / maxq,
+// Min/max grid of one group. Asymmetric: scale = max(wmax - wmin, 1e-8) / maxq,
 // zero = round(-wmin / scale) (GPTQ tools page, "A minimal Python sketch"; round half to even).
-// rs is the correctly rounded reciprocal of the scale, used by div_rn.
-GPTQ_DEV void make_grid(float wmin, float wmax, float maxq, float& s, float& z, float& rs) {
-  s = fmaxf(wmax - wmin, 1e-8f) / maxq;
-  z = rintf(-wmin / s);
+// Symmetric (tools page, "Optional refinements"; the Technical Guide's signed int4 range [-8, 7]):
+// the same recipe on [-m, m] with m = max(|wmin|, |wmax|), scale = max(2 m, 1e-8) / maxq, and the
+// zero fixed at the middle code (maxq + 1) / 2. rs is the correctly rounded reciprocal of the
+// scale, used by div_rn.
+GPTQ_DEV void make_grid(float wmin, float wmax, float maxq, bool sym, float& s, float& z, float& rs) {
+  if (sym) {
+    const float m = fmaxf(fabsf(wmin), fabsf(wmax));
+    s = fmaxf(2.0f * m, 1e-8f) / maxq;
+    z = 0.5f * (maxq + 1.0f);
+  } else {
+    s = fmaxf(wmax - wmin, 1e-8f) / maxq;
+    z = rintf(-wmin / s);
+  }
   rs = 1.0f / s;
 }
 
@@ -120,12 +129,13 @@ void helpers_unlock(Helpers* h);
 // Column loop workspace layout (see quant.hip).
 struct QuantLayout {
   int64_t ldw, bp, ld_err;
-  size_t off_wp, off_codes, off_err, off_loss, off_iperm, total;
+  size_t off_wp, off_codes, off_err, off_loss, off_iperm, off_colgrp, total;
 };
 QuantLayout quant_layout(int64_t rows, int64_t d, int block);
+// sym: symmetric grids; static_groups: grids of original column groups fixed before the loop.
 hipError_t quantize(const void* W, int w_dtype, int64_t rows, int64_t d, int64_t ld_w, const float* U,
-                    const int32_t* perm, int bits, int64_t g, int B, uint8_t* codes, float* scales,
-                    int32_t* zeros, int32_t* g_idx, double* loss, void* work, hipStream_t s);
+                    const int32_t* perm, int bits, int64_t g, int B, int sym, int static_groups, uint8_t* codes,
+                    float* scales, int32_t* zeros, int32_t* g_idx, double* loss, void* work, hipStream_t s);
 hipError_t pack(const uint8_t* codes, int64_t rows, int64_t d, int32_t* packed, hipStream_t s);
 
 // y = x W^T from the packed nibble codes, scales, zeros and column groups (see dequant.hip).

@@ -37,6 +37,8 @@ struct QArgs {
   float* scales;         // [rows x ngroups]
   int32_t* zeros;        // [rows x ngroups]
   int64_t ngroups;
+  int sym;               // symmetric grids (in-block grids only)
+  const int32_t* colgrp; // static groups: group of each processing column (its grid is in scales/zeros)
   float* err;            // this block's errors: [rows x 16 * CPL] at leading dimension err_ld
   int64_t err_ld;
   double* row_loss;      // [rows]
@@ -57,7 +59,9 @@ GPTQ_DEV void lds_load(const float* p, float (&v)[N]) {
   }
 }
 
-template <int CPL>
+// STATIC: every column takes the grid of its static group, colgrp[b + k] (loaded one chunk ahead with
+// U's rows); no grid is computed here.
+template <int CPL, bool STATIC>
 __global__ __launch_bounds__(256) void quant_block_kernel(QArgs a) {
   constexpr int BP = 16 * CPL;
   extern __shared__ float sm[];
@@ -115,7 +119,7 @@ __global__ __launch_bounds__(256) void quant_block_kernel(QArgs a) {
   __syncthreads();
 
   float s = 1.0f, z = 0.0f, rs = 1.0f;
-  if (!a.grid_in_block) {
+  if (!STATIC && !a.grid_in_block) {
     const int64_t gi = a.b / a.g;
     if (row_ok) {
       s = a.scales[row * a.ngroups + gi];
@@ -125,7 +129,7 @@ __global__ __launch_bounds__(256) void quant_block_kernel(QArgs a) {
   }
   float loss = 0.0f;
   // groups nest inside blocks when g <= B, so they start at block columns 0, g, 2g, ...
-  int next_group = a.grid_in_block ? 0 : (1 << 30);
+  int next_group = (!STATIC && a.grid_in_block) ? 0 : (1 << 30);
   const int gsz = (int)min<int64_t>(a.g, (int64_t)BP);
 
   // Chunk o quantizes block columns o*CPL .. o*CPL+CPL-1. Before it, the lanes of each row have
@@ -135,6 +139,19 @@ __global__ __launch_bounds__(256) void quant_block_kernel(QArgs a) {
   // chunk ahead, into the other of two register sets; U and the diagonal are not written after the
   // barrier above, and the chunk's own stores go to the codes and errors.
   const int nchunks = (nc + CPL - 1) / CPL;
+  // static groups: the scale and zero of each of a chunk's columns (one chunk ahead, like U's rows)
+  float sA[STATIC ? CPL : 1], zA[STATIC ? CPL : 1], sB[STATIC ? CPL : 1], zB[STATIC ? CPL : 1];
+  auto fetch_grid = [&](int o, float (&sv)[STATIC ? CPL : 1], float (&zv)[STATIC ? CPL : 1]) {
+    if constexpr (STATIC) {
+#pragma unroll
+      for (int c = 0; c < CPL; ++c) {
+        const int k = min(o * CPL + c, nc - 1);
+        const int64_t G = a.colgrp[a.b + k];
+        sv[c] = row_ok ? a.scales[row * a.ngroups + G] : 1.0f;
+        zv[c] = row_ok ? (float)a.zeros[row * a.ngroups + G] : 0.0f;
+      }
+    }
+  };
   auto fetch = [&](int o, float (&iv)[CPL], float (&ur)[CPL][CPL]) {
     const int cbase = ((lr + o) & 15) * CPL;
     lds_load<CPL>(invd + o * CPL, iv);
@@ -143,13 +160,24 @@ __global__ __launch_bounds__(256) void quant_block_kernel(QArgs a) {
   };
   // CHECKS: the chunk may start a group or run past the block's last column (a plain chunk, full
   // and without a group start, runs the column chain with no branch or select)
-  auto chunk = [&](int o, const float (&iv)[CPL], const float (&ur)[CPL][CPL], auto checks) {
+  auto chunk = [&](int o, const float (&iv)[CPL], const float (&ur)[CPL][CPL], const float (&sv)[STATIC ? CPL : 1],
+                   const float (&zv)[STATIC ? CPL : 1], auto checks) {
     constexpr bool CHECKS = decltype(checks)::value;
     const int cbase = ((lr + o) & 15) * CPL;  // block column of w[0] in this lane
     float qv[CPL], ev[CPL];
+    float rsv[STATIC ? CPL : 1];
+    if constexpr (STATIC) {
+#pragma unroll
+      for (int c = 0; c < CPL; ++c) rsv[c] = 1.0f / sv[c];
+    }
 #pragma unroll
     for (int c = 0; c < CPL; ++c) {
       const int k = o * CPL + c;
+      if constexpr (STATIC) {
+        s = sv[c];
+        z = zv[c];
+        rs = rsv[c];
+      }
       if (CHECKS && k == next_group) {
         next_group += gsz;
         // group grid from the current weights of block columns [k, k + g); min and max over the
@@ -165,7 +193,7 @@ __global__ __launch_bounds__(256) void quant_block_kernel(QArgs a) {
         mn = fminf(mn, row_ror<4>(mn)); mx = fmaxf(mx, row_ror<4>(mx));
         mn = fminf(mn, row_ror<2>(mn)); mx = fmaxf(mx, row_ror<2>(mx));
         mn = fminf(mn, row_ror<1>(mn)); mx = fmaxf(mx, row_ror<1>(mx));
-        make_grid(mn, mx, a.maxq, s, z, rs);
+        make_grid(mn, mx, a.maxq, a.sym != 0, s, z, rs);
         if (lr == 0 && row_ok && k < nc) {
           // column and group indices stay below 2^31
           const int64_t gi = (uint32_t)(a.b + k) / (uint32_t)a.g;
@@ -195,18 +223,28 @@ __global__ __launch_bounds__(256) void quant_block_kernel(QArgs a) {
 #pragma unroll
     for (int t = 0; t < CPL; ++t) w[t] = row_ror15(w[t]);
   };
-  auto run = [&](int o, const float (&iv)[CPL], const float (&ur)[CPL][CPL]) {
-    if (o * CPL + CPL <= nc && next_group >= o * CPL + CPL) chunk(o, iv, ur, std::false_type{});
-    else chunk(o, iv, ur, std::true_type{});
+  auto run = [&](int o, const float (&iv)[CPL], const float (&ur)[CPL][CPL], const float (&sv)[STATIC ? CPL : 1],
+                 const float (&zv)[STATIC ? CPL : 1]) {
+    if (o * CPL + CPL <= nc && next_group >= o * CPL + CPL) chunk(o, iv, ur, sv, zv, std::false_type{});
+    else chunk(o, iv, ur, sv, zv, std::true_type{});
   };
   float ivA[CPL], urA[CPL][CPL], ivB[CPL], urB[CPL][CPL];
-  if (nchunks > 0) fetch(0, ivA, urA);
+  if (nchunks > 0) {
+    fetch(0, ivA, urA);
+    fetch_grid(0, sA, zA);
+  }
   for (int o = 0; o < nchunks; o += 2) {
-    if (o + 1 < nchunks) fetch(o + 1, ivB, urB);
-    run(o, ivA, urA);
     if (o + 1 < nchunks) {
-      if (o + 2 < nchunks) fetch(o + 2, ivA, urA);
-      run(o + 1, ivB, urB);
+      fetch(o + 1, ivB, urB);
+      fetch_grid(o + 1, sB, zB);
+    }
+    run(o, ivA, urA, sA, zA);
+    if (o + 1 < nchunks) {
+      if (o + 2 < nchunks) {
+        fetch(o + 2, ivA, urA);
+        fetch_grid(o + 2, sA, zA);
+      }
+      run(o + 1, ivB, urB, sB, zB);
     }
   }
   __syncthreads();
@@ -239,7 +277,7 @@ __global__ __launch_bounds__(256) void quant_block_kernel(QArgs a) {
 // Group grid for groups longer than a block: min/max of the current weights of columns
 // [b, b + len) of each row, one wave per row.
 __global__ __launch_bounds__(256) void group_grid_kernel(const float* __restrict__ Wp, int64_t ldw, int64_t rows,
-                                                         int64_t b, int64_t len, float maxq, int64_t gi,
+                                                         int64_t b, int64_t len, float maxq, int sym, int64_t gi,
                                                          float* __restrict__ scales, int32_t* __restrict__ zeros,
                                                          int64_t ngroups) {
   const int lane = threadIdx.x & 63;
@@ -259,9 +297,39 @@ __global__ __launch_bounds__(256) void group_grid_kernel(const float* __restrict
   }
   if (lane == 0) {
     float s, z, rs;
-    make_grid(mn, mx, maxq, s, z, rs);
+    make_grid(mn, mx, maxq, sym != 0, s, z, rs);
     scales[row * ngroups + gi] = s;
     zeros[row * ngroups + gi] = (int32_t)z;
+  }
+}
+
+// Static groups: the grid of group G of every row from the original weights W[row][G g .. G g + g),
+// one wave per (row, group); before any column is quantized.
+__global__ __launch_bounds__(256) void static_grid_kernel(const void* __restrict__ W, int dtype, int64_t ld_w,
+                                                          int64_t rows, int64_t d, int64_t g, int64_t ngroups,
+                                                          float maxq, int sym, float* __restrict__ scales,
+                                                          int32_t* __restrict__ zeros) {
+  const int lane = threadIdx.x & 63;
+  const int64_t item = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (item >= rows * ngroups) return;
+  const int64_t row = item / ngroups, G = item - row * ngroups;
+  const int64_t c0 = G * g, c1 = min(c0 + g, d);
+  float mn = INFINITY, mx = -INFINITY;
+  for (int64_t j = c0 + lane; j < c1; j += 64) {
+    const float v = load_as_f32(W, dtype, row * ld_w + j);
+    mn = fminf(mn, v);
+    mx = fmaxf(mx, v);
+  }
+#pragma unroll
+  for (int m = 32; m > 0; m >>= 1) {
+    mn = fminf(mn, __shfl_xor(mn, m, 64));
+    mx = fmaxf(mx, __shfl_xor(mx, m, 64));
+  }
+  if (lane == 0) {
+    float s, z, rs;
+    make_grid(mn, mx, maxq, sym != 0, s, z, rs);
+    scales[item] = s;
+    zeros[item] = (int32_t)z;
   }
 }
 
@@ -285,14 +353,20 @@ __global__ __launch_bounds__(256) void gather_w_kernel(const void* __restrict__ 
     }
 }
 
-// iperm[perm[j]] = j and g_idx[perm[j]] = j / g.
+// iperm[perm[j]] = j, and g_idx[perm[j]] = j / g; with static groups g_idx[j] = j / g and
+// colgrp[j] = perm[j] / g, the group whose grid processing column j takes.
 __global__ void index_kernel(const int32_t* __restrict__ perm, int64_t d, int64_t g, int32_t* __restrict__ iperm,
-                             int32_t* __restrict__ g_idx) {
+                             int32_t* __restrict__ g_idx, int32_t* __restrict__ colgrp) {
   const int64_t j = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (j < d) {
     const int32_t c = perm[j];
     iperm[c] = (int32_t)j;
-    g_idx[c] = (int32_t)(j / g);
+    if (colgrp) {
+      g_idx[j] = (int32_t)(j / g);
+      colgrp[j] = (int32_t)(c / g);
+    } else {
+      g_idx[c] = (int32_t)(j / g);
+    }
   }
 }
 
@@ -368,15 +442,22 @@ size_t qsmem() {
   return (BP * BP + BP + 16 * BP) * sizeof(float) + 16 * BP;
 }
 
-template <int CPL>
+template <int CPL, bool STATIC>
 void launch_block(const QArgs& a, hipStream_t s) {
   static bool attr = false;
   if (!attr) {
-    (void)hipFuncSetAttribute((const void*)quant_block_kernel<CPL>, hipFuncAttributeMaxDynamicSharedMemorySize,
-                        (int)qsmem<CPL>());
+    (void)hipFuncSetAttribute((const void*)quant_block_kernel<CPL, STATIC>,
+                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)qsmem<CPL>());
     attr = true;
   }
-  hipLaunchKernelGGL(quant_block_kernel<CPL>, dim3((unsigned)((a.rows + 15) / 16)), dim3(256), qsmem<CPL>(), s, a);
+  hipLaunchKernelGGL((quant_block_kernel<CPL, STATIC>), dim3((unsigned)((a.rows + 15) / 16)), dim3(256), qsmem<CPL>(),
+                     s, a);
+}
+
+template <int CPL>
+void launch_block(const QArgs& a, bool is_static, hipStream_t s) {
+  if (is_static) launch_block<CPL, true>(a, s);
+  else launch_block<CPL, false>(a, s);
 }
 
 int cpl_for(int B) { return B <= 16 ? 1 : B <= 32 ? 2 : B <= 64 ? 4 : 8; }
@@ -410,13 +491,14 @@ QuantLayout quant_layout(int64_t rows, int64_t d, int block) {
   L.off_err = o; o = up(o + (size_t)rows * L.ld_err * sizeof(float));
   L.off_loss = o; o = up(o + (size_t)rows * sizeof(double));
   L.off_iperm = o; o = up(o + (size_t)d * sizeof(int32_t));
+  L.off_colgrp = o; o = up(o + (size_t)d * sizeof(int32_t));
   L.total = o;
   return L;
 }
 
 hipError_t quantize(const void* W, int w_dtype, int64_t rows, int64_t d, int64_t ld_w, const float* U,
-                    const int32_t* perm, int bits, int64_t g, int B, uint8_t* codes, float* scales,
-                    int32_t* zeros, int32_t* g_idx, double* loss, void* work, hipStream_t s) {
+                    const int32_t* perm, int bits, int64_t g, int B, int sym, int static_groups, uint8_t* codes,
+                    float* scales, int32_t* zeros, int32_t* g_idx, double* loss, void* work, hipStream_t s) {
   const QuantLayout L = quant_layout(rows, d, B);
   char* wb = static_cast<char*>(work);
   float* Wp = reinterpret_cast<float*>(wb + L.off_wp);
@@ -424,10 +506,17 @@ hipError_t quantize(const void* W, int w_dtype, int64_t rows, int64_t d, int64_t
   float* err = reinterpret_cast<float*>(wb + L.off_err);
   double* row_loss = reinterpret_cast<double*>(wb + L.off_loss);
   int32_t* iperm = reinterpret_cast<int32_t*>(wb + L.off_iperm);
+  int32_t* colgrp = static_groups ? reinterpret_cast<int32_t*>(wb + L.off_colgrp) : nullptr;
   const int64_t ngroups = (d + g - 1) / g;
   const float maxq = (float)((1 << bits) - 1);
 
-  hipLaunchKernelGGL(index_kernel, dim3((unsigned)((d + 255) / 256)), dim3(256), 0, s, perm, d, g, iperm, g_idx);
+  hipLaunchKernelGGL(index_kernel, dim3((unsigned)((d + 255) / 256)), dim3(256), 0, s, perm, d, g, iperm, g_idx,
+                     colgrp);
+  if (static_groups && rows > 0) {
+    const int64_t items = rows * ngroups;
+    hipLaunchKernelGGL(static_grid_kernel, dim3((unsigned)((items + 3) / 4)), dim3(256), 0, s, W, w_dtype, ld_w, rows,
+                       d, g, ngroups, maxq, sym, scales, zeros);
+  }
   if (rows > 0) {
     const unsigned gx = (unsigned)std::min<int64_t>((L.ldw + 1023) / 1024, 64);
     const int vec = (uintptr_t)Wp % 16 == 0;
@@ -446,19 +535,21 @@ hipError_t quantize(const void* W, int w_dtype, int64_t rows, int64_t d, int64_t
     for (int64_t b = s0; b < s1; b += B) {
       const int nc = (int)std::min<int64_t>(B, d - b);
       const bool in_block = g <= B;
-      if (!in_block && b % g == 0) {
+      if (!static_groups && !in_block && b % g == 0) {
         hipLaunchKernelGGL(group_grid_kernel, dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, s, Wp, L.ldw, rows, b,
-                           std::min<int64_t>(g, d - b), maxq, b / g, scales, zeros, ngroups);
+                           std::min<int64_t>(g, d - b), maxq, sym, b / g, scales, zeros, ngroups);
       }
       QArgs a;
       a.Wp = Wp; a.ldw = L.ldw; a.rows = rows; a.d = d; a.b = b; a.ncols = nc; a.U = U; a.g = g;
       a.grid_in_block = in_block; a.maxq = maxq; a.codes_p = codes_p; a.scales = scales; a.zeros = zeros;
       a.ngroups = ngroups; a.err = err + (b - s0); a.err_ld = L.ld_err; a.row_loss = row_loss;
+      a.sym = sym; a.colgrp = colgrp;
+      const bool st = static_groups != 0;
       switch (cpl) {
-        case 1: launch_block<1>(a, s); break;
-        case 2: launch_block<2>(a, s); break;
-        case 4: launch_block<4>(a, s); break;
-        default: launch_block<8>(a, s); break;
+        case 1: launch_block<1>(a, st, s); break;
+        case 2: launch_block<2>(a, st, s); break;
+        case 4: launch_block<4>(a, st, s); break;
+        default: launch_block<8>(a, st, s); break;
       }
       if (b + nc < s1) {  // lazy batch inside the super-block
         t.N = s1 - b - nc; t.K = nc;

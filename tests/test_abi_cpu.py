@@ -100,10 +100,10 @@ def test_factor_rejects_bad_arguments():
     assert f(FAKE, 16, 0, ctypes.byref(p), ctypes.c_void_p(0x100000), FAKE, FAKE, big, ctypes.byref(info), None) == -1
     # U overlapping H
     assert f(FAKE, 16, 10, ctypes.byref(p), ctypes.c_void_p(0x1000 + 64), FAKE, FAKE, big, ctypes.byref(info), None) == -1
-    assert f(FAKE, 16, 10, ctypes.byref(_p(L, sym=1)), ctypes.c_void_p(0x100000), FAKE, FAKE, big,
-             ctypes.byref(info), None) == -3
-    assert f(FAKE, 16, 10, ctypes.byref(_p(L, static_groups=1)), ctypes.c_void_p(0x100000), FAKE, FAKE, big,
-             ctypes.byref(info), None) == -3
+    assert f(FAKE, 16, 10, ctypes.byref(_p(L, sym=2)), ctypes.c_void_p(0x100000), FAKE, FAKE, big,
+             ctypes.byref(info), None) == -1
+    assert f(FAKE, 16, 10, ctypes.byref(_p(L, static_groups=-1)), ctypes.c_void_p(0x100000), FAKE, FAKE, big,
+             ctypes.byref(info), None) == -1
     assert f(FAKE, 16, 10, ctypes.byref(_p(L, damp=-1.0)), ctypes.c_void_p(0x100000), FAKE, FAKE, big,
              ctypes.byref(info), None) == -1
     assert f(FAKE, 16, 10, ctypes.byref(_p(L, damp=float("nan"))), ctypes.c_void_p(0x100000), FAKE, FAKE, big,
@@ -128,7 +128,8 @@ def test_quantize_rejects_bad_arguments():
     assert call(_p(L, bits=9)) == -1
     assert call(_p(L, block_size=0)) == -1
     assert call(_p(L, block_size=256)) == -3
-    assert call(_p(L, sym=1)) == -3
+    assert call(_p(L, sym=2)) == -1                     # flags are 0 or 1
+    assert call(_p(L, static_groups=3)) == -1
     assert call(_p(L), ld=255) == -1
     assert call(_p(L), dtype=5) == -1
     assert call(_p(L), d=0) == -1
