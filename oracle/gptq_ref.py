@@ -351,28 +351,75 @@ def quantize_layer(W: np.ndarray, U: np.ndarray, bits: int, group_size: int, blo
 # Packing  (tools page, Step 8: eight 4-bit codes per 32-bit word)
 # --------------------------------------------------------------------------------------------
 
+def field_bits(bits: int) -> int:
+    """Width of the field pack() gives a code: a nibble for up to 4 bits, a byte for 5 to 8."""
+    if not (1 <= bits <= 8):
+        raise ValueError("codes have 1 to 8 bits")
+    return 4 if bits <= 4 else 8
+
+
 def pack(codes: np.ndarray, bits: int) -> np.ndarray:
-    """int32 words: nibble t (bits 4t..4t+3) of word k in a row holds column 8k + t."""
+    """int32 words of fixed fields along each row: with f = field_bits(bits), field t (bits f t ..
+    f t + f - 1) of word k holds column (32 / f) k + t, so eight 4-bit codes per word (tools page,
+    Step 8) or four 8-bit codes."""
     c = np.asarray(codes)
     rows, d = c.shape
-    if d % 8 != 0:
-        raise ValueError("d must be a multiple of 8")
-    if not (1 <= bits <= 4):
-        raise ValueError("nibble packing holds codes of at most 4 bits")
+    f = field_bits(bits)
+    per = 32 // f
+    if d % per != 0:
+        raise ValueError(f"d must be a multiple of {per}")
     if np.any(c.astype(np.int64) >= (1 << bits)) or np.any(c.astype(np.int64) < 0):
         raise ValueError("code out of range")
-    words = np.zeros((rows, d // 8), dtype=np.uint64)
-    for t in range(8):
-        words |= c[:, t::8].astype(np.uint64) << np.uint64(4 * t)
+    words = np.zeros((rows, d // per), dtype=np.uint64)
+    for t in range(per):
+        words |= c[:, t::per].astype(np.uint64) << np.uint64(f * t)
     return words.astype(np.uint32).view(np.int32)
 
 
-def unpack(packed: np.ndarray, d: int) -> np.ndarray:
+def unpack(packed: np.ndarray, d: int, bits: int = 4) -> np.ndarray:
     """Inverse of pack."""
+    f = field_bits(bits)
+    per = 32 // f
     p = np.asarray(packed).view(np.uint32).astype(np.uint64)
     out = np.zeros((p.shape[0], d), dtype=np.uint8)
-    for t in range(8):
-        out[:, t::8] = ((p >> np.uint64(4 * t)) & np.uint64(15)).astype(np.uint8)
+    for t in range(per):
+        out[:, t::per] = ((p >> np.uint64(f * t)) & np.uint64((1 << f) - 1)).astype(np.uint8)
+    return out
+
+
+def pack_dense(codes: np.ndarray, bits: int) -> np.ndarray:
+    """Each row as one little-endian bit stream of exactly `bits` bits per code: code k takes stream
+    bits bits k .. bits k + bits - 1, and stream bit t is bit t % 32 of word t // 32 (so 32 three-bit
+    codes fill three words). Needs d * bits to be a multiple of 32."""
+    c = np.asarray(codes).astype(np.int64)
+    rows, d = c.shape
+    if not (1 <= bits <= 8) or (d * bits) % 32 != 0:
+        raise ValueError("bits in 1..8 and d * bits a multiple of 32")
+    if np.any(c >= (1 << bits)) or np.any(c < 0):
+        raise ValueError("code out of range")
+    nw = d * bits // 32
+    words = np.zeros((rows, nw), dtype=np.uint64)
+    for k in range(d):
+        pos = k * bits
+        w, sh = pos // 32, pos % 32
+        v = c[:, k].astype(np.uint64) << np.uint64(sh)          # up to 39 bits
+        words[:, w] |= v & np.uint64(0xFFFFFFFF)
+        if sh + bits > 32:
+            words[:, w + 1] |= v >> np.uint64(32)
+    return words.astype(np.uint32).view(np.int32)
+
+
+def unpack_dense(packed: np.ndarray, d: int, bits: int) -> np.ndarray:
+    """Inverse of pack_dense."""
+    p = np.asarray(packed).view(np.uint32).astype(np.uint64)
+    out = np.zeros((p.shape[0], d), dtype=np.uint8)
+    for k in range(d):
+        pos = k * bits
+        w, sh = pos // 32, pos % 32
+        v = p[:, w] >> np.uint64(sh)
+        if sh + bits > 32:
+            v |= p[:, w + 1] << np.uint64(32 - sh)
+        out[:, k] = (v & np.uint64((1 << bits) - 1)).astype(np.uint8)
     return out
 
 
@@ -382,10 +429,11 @@ def unpack(packed: np.ndarray, d: int) -> np.ndarray:
 # --------------------------------------------------------------------------------------------
 
 def dequantize(packed: np.ndarray, scales: np.ndarray, zeros: np.ndarray, g_idx: np.ndarray,
-               d: int) -> np.ndarray:
+               d: int, bits: int = 4, dense: bool = False) -> np.ndarray:
     """Weights rows x d, original column order: column j of row r is
-    scales[r, g] * (code[r, j] - zeros[r, g]) with g = g_idx[j], the group column j was quantized in."""
-    codes = unpack(packed, d).astype(np.float64)
+    scales[r, g] * (code[r, j] - zeros[r, g]) with g = g_idx[j], the group column j was quantized in.
+    `packed` is in pack()'s layout, or pack_dense()'s with dense=True."""
+    codes = (unpack_dense(packed, d, bits) if dense else unpack(packed, d, bits)).astype(np.float64)
     g = np.asarray(g_idx, dtype=np.int64)
     s = np.asarray(scales, dtype=np.float64)[:, g]
     z = np.asarray(zeros, dtype=np.float64)[:, g]
@@ -393,9 +441,9 @@ def dequantize(packed: np.ndarray, scales: np.ndarray, zeros: np.ndarray, g_idx:
 
 
 def dequant_matmul(x: np.ndarray, packed: np.ndarray, scales: np.ndarray, zeros: np.ndarray,
-                   g_idx: np.ndarray, d: int) -> np.ndarray:
+                   g_idx: np.ndarray, d: int, bits: int = 4, dense: bool = False) -> np.ndarray:
     """The layer's output y = x W^T (m x rows) for inputs x (m x d), W the dequantized weights."""
-    W = dequantize(packed, scales, zeros, g_idx, d)
+    W = dequantize(packed, scales, zeros, g_idx, d, bits, dense)
     return np.asarray(x, dtype=np.float64) @ W.T
 
 
@@ -432,7 +480,7 @@ def gptq(W: np.ndarray, chunks: Iterable[np.ndarray], bits: int, group_size: int
     qr = quantize_layer(W, U, bits, group_size, block_size, perm=p, follow=follow, tau=tau, sym=sym,
                         static_groups=static_groups)
     d = qr.codes.shape[1]
-    packed = pack(qr.codes, bits) if (d % 8 == 0 and bits <= 4) else None
+    packed = pack(qr.codes, bits) if d % (32 // field_bits(bits)) == 0 else None
     return LayerResult(H=H, n=n, Hhat=Hhat, lam=lam, U=U, quant=qr, packed=packed)
 
 

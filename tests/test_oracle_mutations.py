@@ -33,8 +33,12 @@ MUTATIONS = [
     ("act-order ascending", "return np.argsort(-diag, kind=\"stable\").astype(np.int64)",
      "return np.argsort(diag, kind=\"stable\").astype(np.int64)"),
     ("hessian without factor 2", "H += 2.0 * (x.T @ x)", "H += (x.T @ x)"),
-    ("pack nibble order", "words |= c[:, t::8].astype(np.uint64) << np.uint64(4 * t)",
-     "words |= c[:, t::8].astype(np.uint64) << np.uint64(4 * (7 - t))"),
+    ("pack nibble order", "words |= c[:, t::per].astype(np.uint64) << np.uint64(f * t)",
+     "words |= c[:, t::per].astype(np.uint64) << np.uint64(f * (per - 1 - t))"),
+    ("dense pack drops the straddling bits", "            words[:, w + 1] |= v >> np.uint64(32)",
+     "            pass"),
+    ("dense pack big-endian codes", "        v = c[:, k].astype(np.uint64) << np.uint64(sh)",
+     "        v = c[:, d - 1 - k].astype(np.uint64) << np.uint64(sh)"),
     ("dequant zero not subtracted", "return s * (codes - z)", "return s * codes"),
     ("symmetric zero at code 0", "return scale, np.full(scale.shape, float((maxq + 1) // 2))",
      "return scale, np.zeros(scale.shape)"),
@@ -107,6 +111,11 @@ def _checks(m):
         if m.pack(np.array([[1, 2, 3, 4, 5, 6, 7, 8]], np.uint8), 4)[0, 0] != np.array(
                 [0x87654321], np.uint32).view(np.int32)[0]:
             failed.append("pack closed form")
+        # a row's dense stream read as one integer is its codes as digits in base 2^bits
+        cd = np.array([[k % 8 for k in range(32)]], np.uint8)
+        pd = m.pack_dense(cd, 3).view(np.uint32).astype(object)
+        if int(pd[0, 0] + (pd[0, 1] << 32) + (pd[0, 2] << 64)) != sum(int(cd[0, k]) << (3 * k) for k in range(32)):
+            failed.append("dense pack positional value")
         Hs = np.diag([2.0, 4.0, 6.0]) * 10
         if not np.isclose(m.damp_and_order(Hs, 10, 0.01, False)[2], 0.04):
             failed.append("damping mean diag")

@@ -544,3 +544,44 @@ def test_static_groups_identity_hessian_is_original_order_rtn():
     assert np.array_equal(r.quant.codes, ref.rtn(W, 4, 16).codes)
     rd = ref.gptq(W, None, 4, 16, 32, H=H, n=1, act_order=True)
     assert np.array_equal(rd.quant.codes, ref.rtn(W, 4, 16, perm=rd.quant.perm).codes)
+
+
+# ---------------------------------------------------------------- storage layouts
+
+@pytest.mark.parametrize("bits", [1, 2, 3, 4, 5, 6, 7, 8])
+def test_dense_stream_is_positional_notation(bits):
+    """A row's dense stream, read as one little-endian integer, is the row's codes as the digits of a
+    number in base 2^bits (code k is digit k)."""
+    rng = np.random.default_rng(bits)
+    d = 96
+    c = rng.integers(0, 1 << bits, size=(3, d)).astype(np.uint8)
+    p = ref.pack_dense(c, bits).view(np.uint32)
+    assert p.shape == (3, d * bits // 32)
+    for r in range(3):
+        value = sum(int(w) << (32 * i) for i, w in enumerate(p[r]))
+        assert value == sum(int(c[r, k]) << (bits * k) for k in range(d))
+    assert np.array_equal(ref.unpack_dense(ref.pack_dense(c, bits), d, bits), c)
+
+
+@pytest.mark.parametrize("bits", [4, 8])
+def test_dense_stream_equals_field_layout_at_full_fields(bits):
+    """At 4 and 8 bits a code fills its field exactly, so the dense stream and pack() agree."""
+    rng = np.random.default_rng(40 + bits)
+    c = rng.integers(0, 1 << bits, size=(5, 64)).astype(np.uint8)
+    assert np.array_equal(ref.pack_dense(c, bits), ref.pack(c, bits))
+
+
+def test_byte_fields_closed_form():
+    """Four 8-bit codes per word: column 4k + t in bits 8t .. 8t + 7 of word k."""
+    c = np.array([[0x11, 0x22, 0x33, 0x44, 0xFF, 0x00, 0x80, 0x01]], np.uint8)
+    p = ref.pack(c, 8).view(np.uint32)
+    assert p.tolist() == [[0x44332211, 0x018000FF]]
+    assert np.array_equal(ref.unpack(ref.pack(c, 8), 8, 8), c)
+    assert ref.pack(c[:, :8] & 0x1F, 5).view(np.uint32)[0, 0] == 0x04130211    # 5-bit codes, byte fields
+
+
+def test_dense_three_bit_saves_a_quarter():
+    """Three-bit codes: 32 codes in 3 words, against 4 words in nibbles (tools page, Memory arithmetic:
+    storage follows the bit width)."""
+    c = np.zeros((1, 256), np.uint8)
+    assert ref.pack_dense(c, 3).shape[1] == 24 and ref.pack(c, 3).shape[1] == 32
