@@ -9,7 +9,8 @@
  *   gptq_hessian_accumulate  H += 2 X_c^T X_c for each token chunk X_c
  *   gptq_factor              damping, optional act-order, U = upper Cholesky factor of Hhat^-1
  *   gptq_quantize_layer      the column loop with lazy block updates; codes, scales, zeros, loss
- *   gptq_pack                eight 4-bit codes per 32-bit word
+ *   gptq_pack                eight 4-bit codes per 32-bit word (four 8-bit ones)
+ *   gptq_pack_dense          the codes as one dense bit stream per row
  *
  * and one call that uses the stored layer:
  *
@@ -58,6 +59,12 @@ enum {
 
 /* Element types of W and X. */
 enum { GPTQ_F32 = 0, GPTQ_F16 = 1, GPTQ_BF16 = 2 };
+
+/* Storage layouts of packed codes (gptq_dequant_gemm's `layout`). */
+enum {
+  GPTQ_LAYOUT_FIELDS = 0, /* gptq_pack: a nibble per code up to 4 bits (8 per word), a byte above    */
+  GPTQ_LAYOUT_DENSE = 1   /* gptq_pack_dense: exactly `bits` bits per code in one bit stream per row */
+};
 
 /* Workspace kinds for gptq_workspace_bytes. */
 enum { GPTQ_WS_HESSIAN = 0, GPTQ_WS_FACTOR = 1, GPTQ_WS_QUANTIZE = 2 };
@@ -160,14 +167,29 @@ gptq_status_t gptq_quantize_layer(const void *W, int32_t w_dtype, int64_t rows, 
                                   size_t work_bytes, void *stream);
 
 /*
- * Packs codes eight per 32-bit word along the columns (GPTQ tools page, "How it works", Step 8).
+ * Packs codes in fixed fields along the columns (GPTQ tools page, "How it works", Step 8: eight 4-bit
+ * codes per 32-bit word): a nibble per code for bits 1..4, a byte per code for bits 5..8.
  *
- *   codes   device uint8[rows * d]; every code must be < 2^bits (bits above the low 4 are dropped).
- *   rows    >= 0; d >= 8 and a multiple of 8; bits in 1..4 (3-bit codes also take a nibble).
- *   packed  device int32[rows * d / 8], output: bits 4t..4t+3 of word k of a row hold column 8k + t.
+ *   codes   device uint8[rows * d]; every code must be < 2^bits (bits above the field are dropped).
+ *   rows    >= 0; d >= 8 and a multiple of 8; bits in 1..8 (3-bit codes also take a nibble).
+ *   packed  device int32[rows * d * f / 32], output, f = 4 or 8: bits f t .. f t + f - 1 of word k of
+ *           a row hold column (32 / f) k + t.
  */
 gptq_status_t gptq_pack(const uint8_t *codes, int64_t rows, int64_t d, int32_t bits, int32_t *packed,
                         void *stream);
+
+/*
+ * Packs codes as one dense bit stream per row, exactly `bits` bits per code, so 3-bit codes take 3
+ * bits, not a nibble (the tools page's "Memory arithmetic": storage follows the bit width). At 4 and
+ * 8 bits the words equal gptq_pack's.
+ *
+ *   codes   device uint8[rows * d]; every code must be < 2^bits (higher bits are dropped).
+ *   rows    >= 0; d >= 1 with d * bits a multiple of 32; bits in 1..8.
+ *   packed  device int32[rows * d * bits / 32], output: code k of a row occupies stream bits
+ *           bits k .. bits k + bits - 1, and stream bit t is bit t % 32 of word t / 32 of the row.
+ */
+gptq_status_t gptq_pack_dense(const uint8_t *codes, int64_t rows, int64_t d, int32_t bits, int32_t *packed,
+                              void *stream);
 
 /*
  * The stored layer at inference: y = x W^T for a few rows of inputs x, with W expanded from the packed
@@ -181,9 +203,12 @@ gptq_status_t gptq_pack(const uint8_t *codes, int64_t rows, int64_t d, int32_t b
  *   m       input rows, >= 0 (0: nothing is queued). Rows are taken eight at a time, and each group
  *           of eight reads the codes once.
  *   ld_x    row pitch of x in elements, >= d.
- *   packed  device int32[rows * d / 8] in gptq_pack's layout: nibble t of word k of a row is the
- *           code of column 8k + t. Not modified.
- *   bits    the code width, 1..4 (wider codes return GPTQ_EUNSUPPORTED: they do not fit a nibble).
+ *   packed  device int32 codes of rows x d weights in `layout`: GPTQ_LAYOUT_FIELDS is gptq_pack's
+ *           (rows * d / 8 words of nibbles for bits <= 4, rows * d / 4 words of bytes above),
+ *           GPTQ_LAYOUT_DENSE is gptq_pack_dense's (rows * d * bits / 32 words; d * bits must be
+ *           a multiple of 32). Not modified.
+ *   bits    the code width, 1..8.
+ *   layout  GPTQ_LAYOUT_FIELDS or GPTQ_LAYOUT_DENSE.
  *   scales  device float[rows * ngroups] and zeros device int32[rows * ngroups], as
  *           gptq_quantize_layer writes them, with ngroups = ceil(d / g) and g = group_size (d when
  *           group_size <= 0).
@@ -194,15 +219,15 @@ gptq_status_t gptq_pack(const uint8_t *codes, int64_t rows, int64_t d, int32_t b
  *           of 8.
  *   y       device float[m x ld_y], output, ld_y >= rows: y[i, r] = sum_k x[i, k] W[r, k] with
  *           W[r, k] = scales[r, G] * (code[r, k] - zeros[r, G]) and G the group of column k.
- * Products and sums are fp32 (fp16 x times a code is exact in fp32). A faster kernel runs when x is
- * fp16, g_idx is NULL, g is a multiple of 32 or at least d, d is a multiple of 32, and the rows of x
- * and the codes are 16-byte aligned; otherwise a general one does. Results do not depend on
- * scheduling.
+ * Products and sums are fp32 (fp16 x times a code is exact in fp32). Faster kernels run for nibble
+ * fields when x is fp16, g_idx is NULL, g is a multiple of 32 or at least d, d is a multiple of 32,
+ * and the rows of x and the codes are 16-byte aligned (for 3 or more input rows also g a multiple of
+ * 128 and d of 128); otherwise a general one does. Results do not depend on scheduling.
  */
 gptq_status_t gptq_dequant_gemm(const void *x, int32_t x_dtype, int64_t m, int64_t ld_x, const int32_t *packed,
-                                int32_t bits, const float *scales, const int32_t *zeros, const int32_t *g_idx,
-                                int64_t rows, int64_t d, int32_t group_size, float *y, int64_t ld_y,
-                                void *stream);
+                                int32_t bits, int32_t layout, const float *scales, const int32_t *zeros,
+                                const int32_t *g_idx, int64_t rows, int64_t d, int32_t group_size, float *y,
+                                int64_t ld_y, void *stream);
 
 /*
  * Workspace bytes for a call: kind GPTQ_WS_HESSIAN (a = n_tok of the chunk), GPTQ_WS_FACTOR (a unused)

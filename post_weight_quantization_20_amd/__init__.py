@@ -13,6 +13,8 @@ from .solver import (  # noqa: F401
     GPTQ_EUNSUPPORTED,
     GPTQ_F16,
     GPTQ_F32,
+    GPTQ_LAYOUT_DENSE,
+    GPTQ_LAYOUT_FIELDS,
     GPTQ_OK,
     GPTQ_WS_FACTOR,
     GPTQ_WS_HESSIAN,
@@ -25,6 +27,8 @@ from .solver import (  # noqa: F401
     gptq_factor,
     gptq_hessian_accumulate,
     gptq_pack,
+    gptq_pack_dense,
+    packed_words,
     gptq_quantize_layer,
     gptq_workspace_bytes,
     quantize_layer,

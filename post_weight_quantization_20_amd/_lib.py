@@ -37,8 +37,9 @@ SIGNATURES = {
                                       ctypes.POINTER(gptq_params_t), c_void_p, c_void_p, c_void_p, c_void_p, c_void_p,
                                       c_void_p, c_size_t, c_void_p]),
     "gptq_pack": (c_int32, [c_void_p, c_int64, c_int64, c_int32, c_void_p, c_void_p]),
-    "gptq_dequant_gemm": (c_int32, [c_void_p, c_int32, c_int64, c_int64, c_void_p, c_int32, c_void_p, c_void_p,
-                                    c_void_p, c_int64, c_int64, c_int32, c_void_p, c_int64, c_void_p]),
+    "gptq_pack_dense": (c_int32, [c_void_p, c_int64, c_int64, c_int32, c_void_p, c_void_p]),
+    "gptq_dequant_gemm": (c_int32, [c_void_p, c_int32, c_int64, c_int64, c_void_p, c_int32, c_int32, c_void_p,
+                                    c_void_p, c_void_p, c_int64, c_int64, c_int32, c_void_p, c_int64, c_void_p]),
     "gptq_workspace_bytes": (c_size_t, [c_int32, c_int64, c_int64, ctypes.POINTER(gptq_params_t)]),
     "gptq_status_string": (ctypes.c_char_p, [c_int32]),
 }

@@ -121,24 +121,35 @@ gptq_status_t gptq_quantize_layer(const void* W, int32_t w_dtype, int64_t rows, 
 }
 
 gptq_status_t gptq_pack(const uint8_t* codes, int64_t rows, int64_t d, int32_t bits, int32_t* packed, void* stream) {
-  if (rows < 0 || rows > kMaxDim || d < 8 || d > kMaxDim || d % 8 != 0 || bits < 1 || bits > 4) return GPTQ_EINVAL;
+  if (rows < 0 || rows > kMaxDim || d < 8 || d > kMaxDim || d % 8 != 0 || bits < 1 || bits > 8) return GPTQ_EINVAL;
   if (rows == 0) return GPTQ_OK;
   if (!codes || !packed) return GPTQ_EINVAL;
-  return hip_status(gptq::pack(codes, rows, d, packed, static_cast<hipStream_t>(stream)));
+  return hip_status(gptq::pack(codes, rows, d, bits, packed, static_cast<hipStream_t>(stream)));
+}
+
+gptq_status_t gptq_pack_dense(const uint8_t* codes, int64_t rows, int64_t d, int32_t bits, int32_t* packed,
+                              void* stream) {
+  if (rows < 0 || rows > kMaxDim || d < 1 || d > kMaxDim || bits < 1 || bits > 8 || (d * bits) % 32 != 0)
+    return GPTQ_EINVAL;
+  if (rows == 0) return GPTQ_OK;
+  if (!codes || !packed) return GPTQ_EINVAL;
+  return hip_status(gptq::pack_dense(codes, rows, d, bits, packed, static_cast<hipStream_t>(stream)));
 }
 
 gptq_status_t gptq_dequant_gemm(const void* x, int32_t x_dtype, int64_t m, int64_t ld_x, const int32_t* packed,
-                                int32_t bits, const float* scales, const int32_t* zeros, const int32_t* g_idx,
-                                int64_t rows, int64_t d, int32_t group_size, float* y, int64_t ld_y, void* stream) {
+                                int32_t bits, int32_t layout, const float* scales, const int32_t* zeros,
+                                const int32_t* g_idx, int64_t rows, int64_t d, int32_t group_size, float* y,
+                                int64_t ld_y, void* stream) {
   if (m < 0 || m > kMaxDim || rows < 0 || rows > kMaxDim || d < 8 || d > kMaxDim || d % 8 != 0) return GPTQ_EINVAL;
   if (!dtype_ok(x_dtype) || ld_x < d || ld_x > kMaxDim || ld_y < rows || ld_y > kMaxDim) return GPTQ_EINVAL;
   if (bits < 1 || bits > 8) return GPTQ_EINVAL;
-  if (bits > 4) return GPTQ_EUNSUPPORTED;
+  if (layout != GPTQ_LAYOUT_FIELDS && layout != GPTQ_LAYOUT_DENSE) return GPTQ_EINVAL;
+  if (layout == GPTQ_LAYOUT_DENSE && (d * bits) % 32 != 0) return GPTQ_EINVAL;
   if (m == 0 || rows == 0) return GPTQ_OK;
   if (!x || !packed || !scales || !zeros || !y) return GPTQ_EINVAL;
   const int64_t g = group_size <= 0 ? d : group_size;
-  return hip_status(gptq::dequant_gemm(x, x_dtype, m, ld_x, packed, scales, zeros, g_idx, rows, d, g, y, ld_y,
-                                       static_cast<hipStream_t>(stream)));
+  return hip_status(gptq::dequant_gemm(x, x_dtype, m, ld_x, packed, bits, layout == GPTQ_LAYOUT_DENSE, scales, zeros,
+                                       g_idx, rows, d, g, y, ld_y, static_cast<hipStream_t>(stream)));
 }
 
 }  // extern "C"

@@ -136,14 +136,16 @@ QuantLayout quant_layout(int64_t rows, int64_t d, int block);
 hipError_t quantize(const void* W, int w_dtype, int64_t rows, int64_t d, int64_t ld_w, const float* U,
                     const int32_t* perm, int bits, int64_t g, int B, int sym, int static_groups, uint8_t* codes,
                     float* scales, int32_t* zeros, int32_t* g_idx, double* loss, void* work, hipStream_t s);
-hipError_t pack(const uint8_t* codes, int64_t rows, int64_t d, int32_t* packed, hipStream_t s);
+// Field layout (nibbles up to 4 bits, bytes above) and the dense bit stream.
+hipError_t pack(const uint8_t* codes, int64_t rows, int64_t d, int bits, int32_t* packed, hipStream_t s);
+hipError_t pack_dense(const uint8_t* codes, int64_t rows, int64_t d, int bits, int32_t* packed, hipStream_t s);
 
 // y = x W^T from the packed nibble codes, scales, zeros and column groups (see dequant.hip).
 // g is the group width (>= 1); gidx may be null (column k in group k / g).
 bool dequant_fast_path(const void* x, int dtype, int64_t ldx, const int32_t* packed, const int32_t* gidx, int64_t d,
                        int64_t g);
-hipError_t dequant_gemm(const void* x, int dtype, int64_t m, int64_t ldx, const int32_t* packed, const float* scales,
-                        const int32_t* zeros, const int32_t* gidx, int64_t rows, int64_t d, int64_t g, float* y,
-                        int64_t ldy, hipStream_t s);
+hipError_t dequant_gemm(const void* x, int dtype, int64_t m, int64_t ldx, const int32_t* packed, int bits, int dense,
+                        const float* scales, const int32_t* zeros, const int32_t* gidx, int64_t rows, int64_t d,
+                        int64_t g, float* y, int64_t ldy, hipStream_t s);
 
 }  // namespace gptq

@@ -45,6 +45,9 @@ struct DqArgs {
   const int32_t* gidx;        // null: G(k) = k / g
   int xvec;                   // general kernel: rows of x are 16-byte aligned (vector loads)
   int gvec;                   // general kernel: gidx is 16-byte aligned
+  int bits;                   // code width
+  int dense;                  // general kernel: 1 = dense bit stream, 0 = nibble / byte fields
+  int64_t nwr;                // words per row of packed
   float* y;                   // m x rows, row pitch ldy
   int64_t ldy;
 };
@@ -346,6 +349,40 @@ GPTQ_DEV float load_x(const void* x, int64_t idx) {
   else return bf16_bits_to_f32(static_cast<const uint16_t*>(x)[idx]);
 }
 
+// The codes of columns 8 wv .. 8 wv + 7 of one row. Fields: one word of nibbles (bits <= 4) or two
+// words of bytes. Dense stream: the 8 bits-wide codes start at stream bit 8 wv bits and span at most
+// three words (8 bits <= 64 bits from an offset below 32).
+GPTQ_DEV void codes8(const uint32_t* __restrict__ row, int64_t nwr, int64_t wv, int bits, int dense,
+                     uint32_t (&q)[8]) {
+  if (!dense) {
+    if (bits <= 4) {
+      const uint32_t w = row[wv];
+#pragma unroll
+      for (int t = 0; t < 8; ++t) q[t] = (w >> (4 * t)) & 15u;
+    } else {
+      const uint32_t w0 = row[2 * wv], w1 = row[2 * wv + 1];
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        q[t] = (w0 >> (8 * t)) & 255u;
+        q[4 + t] = (w1 >> (8 * t)) & 255u;
+      }
+    }
+    return;
+  }
+  const int64_t b0 = 8 * wv * bits;
+  const int64_t w0 = b0 >> 5;
+  const int off = (int)(b0 & 31);
+  const uint32_t a0 = row[w0];
+  const uint32_t a1 = w0 + 1 < nwr ? row[w0 + 1] : 0u;
+  const uint32_t a2 = w0 + 2 < nwr ? row[w0 + 2] : 0u;
+  // the 96-bit window a2:a1:a0 shifted right by off, as two 64-bit halves
+  const uint64_t lo = ((uint64_t)a1 << 32) | a0, hi = a2;
+  const uint64_t win = off ? (lo >> off) | (hi << (64 - off)) : lo;   // bits off .. off + 63
+  const uint32_t mask = (1u << bits) - 1u;
+#pragma unroll
+  for (int t = 0; t < 8; ++t) q[t] = (uint32_t)(win >> (t * bits)) & mask;
+}
+
 // x[row][8 wv .. 8 wv + 7] as floats: one or two 16-byte loads when the rows are 16-byte aligned.
 template <int XT>
 GPTQ_DEV void load_x8(const void* x, int64_t base, bool vec, float (&v)[8]) {
@@ -412,9 +449,9 @@ __global__ __launch_bounds__(256) void dq_general_kernel(DqArgs a) {
     for (int r = 0; r < R; ++r) acc[i][r] = 0.f;
 
   for (int64_t wv = lane; wv < nw; wv += 64) {
-    uint32_t w[R];
+    uint32_t qc[R][8];
 #pragma unroll
-    for (int r = 0; r < R; ++r) w[r] = a.packed[rr[r] * nw + wv];
+    for (int r = 0; r < R; ++r) codes8(a.packed + rr[r] * a.nwr, a.nwr, wv, a.bits, a.dense, qc[r]);
     int32_t gk[8];
     if (a.gidx && a.gvec) {
       const u32x4 g0 = *reinterpret_cast<const u32x4*>(a.gidx + 8 * wv);
@@ -439,7 +476,7 @@ __global__ __launch_bounds__(256) void dq_general_kernel(DqArgs a) {
       const int64_t G = gk[t] < 0 ? 0 : gk[t] >= a.ngroups ? a.ngroups - 1 : gk[t];   // clamped
 #pragma unroll
       for (int r = 0; r < R; ++r) {
-        const int32_t q = (int32_t)((w[r] >> (4 * t)) & 15u);
+        const int32_t q = (int32_t)qc[r][t];
         float sc;
         int32_t z;
         if constexpr (TAB) {
@@ -526,12 +563,14 @@ bool dequant_fast_path(const void* x, int dtype, int64_t ldx, const int32_t* pac
          reinterpret_cast<uintptr_t>(x) % 16 == 0 && reinterpret_cast<uintptr_t>(packed) % 16 == 0;
 }
 
-hipError_t dequant_gemm(const void* x, int dtype, int64_t m, int64_t ldx, const int32_t* packed, const float* scales,
-                        const int32_t* zeros, const int32_t* gidx, int64_t rows, int64_t d, int64_t g, float* y,
-                        int64_t ldy, hipStream_t s) {
-  const bool fast = dequant_fast_path(x, dtype, ldx, packed, gidx, d, g);
+hipError_t dequant_gemm(const void* x, int dtype, int64_t m, int64_t ldx, const int32_t* packed, int bits, int dense,
+                        const float* scales, const int32_t* zeros, const int32_t* gidx, int64_t rows, int64_t d,
+                        int64_t g, float* y, int64_t ldy, hipStream_t s) {
+  // the dot2 and matrix-core kernels decode nibble fields; other layouts take the general kernel
+  const bool nibbles = !dense && bits <= 4;
+  const bool fast = nibbles && dequant_fast_path(x, dtype, ldx, packed, gidx, d, g);
   // two input rows still run faster on the dot2 kernel (fc2: 90 against 108 us); three or more do not
-  const bool mfma = m >= 3 && dequant_mfma_path(x, dtype, ldx, packed, gidx, d, g);
+  const bool mfma = nibbles && m >= 3 && dequant_mfma_path(x, dtype, ldx, packed, gidx, d, g);
   const int R = rows_per_wave(rows);
   const int64_t esz = dtype == F32 ? 4 : 2;
   const int64_t step = mfma ? 16 : 8;
@@ -550,6 +589,9 @@ hipError_t dequant_gemm(const void* x, int dtype, int64_t m, int64_t ldx, const 
     a.gidx = gidx;
     a.y = y + i0 * ldy;
     a.ldy = ldy;
+    a.bits = bits;
+    a.dense = dense;
+    a.nwr = dense ? d * bits / 32 : bits <= 4 ? d / 8 : d / 4;
     hipError_t e;
     if (mfma && a.m >= 3) {
       // units per group; waves per workgroup so that about 12 waves per CU are in flight

@@ -409,6 +409,39 @@ __global__ __launch_bounds__(1024) void loss_kernel(const double* __restrict__ r
   if (threadIdx.x == 0) *loss = part[0];
 }
 
+// Byte fields (codes of 5 to 8 bits): word k of a row holds columns 4k .. 4k + 3 in bytes 0..3,
+// which is the code array's own byte order, so the words are a copy of the codes.
+__global__ __launch_bounds__(256) void pack_bytes_kernel(const uint8_t* __restrict__ codes, int64_t n,
+                                                         uint8_t* __restrict__ packed, int vec) {
+  const int64_t n16 = vec ? n / 16 : 0;
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n16; i += (int64_t)gridDim.x * 256)
+    reinterpret_cast<uint4*>(packed)[i] = reinterpret_cast<const uint4*>(codes)[i];
+  for (int64_t i = n16 * 16 + (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256)
+    packed[i] = codes[i];
+}
+
+// Dense bit stream: code k of a row takes stream bits bits k .. bits k + bits - 1 and stream bit t is
+// bit t % 32 of word t / 32. One thread per output word ORs in every code that overlaps it.
+__global__ __launch_bounds__(256) void pack_dense_kernel(const uint8_t* __restrict__ codes, int64_t rows, int64_t d,
+                                                         int bits, int32_t* __restrict__ packed) {
+  const int64_t words = d * bits / 32;
+  const int64_t total = rows * words;
+  const uint32_t mask = (1u << bits) - 1u;
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < total; i += (int64_t)gridDim.x * 256) {
+    const int64_t r = i / words, w = i % words;
+    const int64_t b0 = 32 * w;
+    const int64_t k0 = b0 / bits, k1 = min((b0 + 31) / bits, d - 1);
+    const uint8_t* p = codes + r * d;
+    uint32_t out = 0;
+    for (int64_t k = k0; k <= k1; ++k) {
+      const int64_t pos = k * bits - b0;   // in (-bits, 32)
+      const uint32_t v = p[k] & mask;
+      out |= pos >= 0 ? (v << pos) : (v >> -pos);
+    }
+    packed[i] = (int32_t)out;
+  }
+}
+
 // packed[r][k] = sum_t (codes[r][8k + t] & 15) << 4t.
 __global__ __launch_bounds__(256) void pack_kernel(const uint8_t* __restrict__ codes, int64_t rows, int64_t d,
                                                    int32_t* __restrict__ packed, int vec) {
@@ -573,12 +606,29 @@ hipError_t quantize(const void* W, int w_dtype, int64_t rows, int64_t d, int64_t
   return hipGetLastError();
 }
 
-hipError_t pack(const uint8_t* codes, int64_t rows, int64_t d, int32_t* packed, hipStream_t s) {
+hipError_t pack(const uint8_t* codes, int64_t rows, int64_t d, int bits, int32_t* packed, hipStream_t s) {
+  if (bits > 4) {
+    const int64_t n = rows * d;
+    if (n <= 0) return hipSuccess;
+    const unsigned grid = (unsigned)std::min<int64_t>((n / 16 + 255) / 256 + 1, 65536);
+    const int vec = (uintptr_t)codes % 16 == 0 && (uintptr_t)packed % 16 == 0;
+    hipLaunchKernelGGL(pack_bytes_kernel, dim3(grid), dim3(256), 0, s, codes, n, reinterpret_cast<uint8_t*>(packed),
+                       vec);
+    return hipGetLastError();
+  }
   const int64_t total = rows * (d / 8);
   if (total <= 0) return hipSuccess;
   const unsigned grid = (unsigned)std::min<int64_t>((total + 255) / 256, 65536);
   const int vec = ((uintptr_t)codes % 8 == 0);
   hipLaunchKernelGGL(pack_kernel, dim3(grid), dim3(256), 0, s, codes, rows, d, packed, vec);
+  return hipGetLastError();
+}
+
+hipError_t pack_dense(const uint8_t* codes, int64_t rows, int64_t d, int bits, int32_t* packed, hipStream_t s) {
+  const int64_t total = rows * (d * bits / 32);
+  if (total <= 0) return hipSuccess;
+  const unsigned grid = (unsigned)std::min<int64_t>((total + 255) / 256, 65536);
+  hipLaunchKernelGGL(pack_dense_kernel, dim3(grid), dim3(256), 0, s, codes, rows, d, bits, packed);
   return hipGetLastError();
 }
 

@@ -18,6 +18,7 @@ from . import _lib
 GPTQ_OK, GPTQ_EINVAL, GPTQ_ENOTPD, GPTQ_EUNSUPPORTED, GPTQ_EHIP, GPTQ_ENOMEM = 0, -1, -2, -3, -4, -5
 GPTQ_F32, GPTQ_F16, GPTQ_BF16 = 0, 1, 2
 GPTQ_WS_HESSIAN, GPTQ_WS_FACTOR, GPTQ_WS_QUANTIZE = 0, 1, 2
+GPTQ_LAYOUT_FIELDS, GPTQ_LAYOUT_DENSE = 0, 1
 
 _DTYPE = {torch.float32: GPTQ_F32, torch.float16: GPTQ_F16, torch.bfloat16: GPTQ_BF16}
 
@@ -160,21 +161,40 @@ def gptq_quantize_layer(W: torch.Tensor, U: torch.Tensor, perm: torch.Tensor, pa
     return out
 
 
+def packed_words(d: int, bits: int, dense: bool = False) -> int:
+    """int32 words per row of packed codes: d/8 nibble fields, d/4 byte fields, or d*bits/32 dense."""
+    return d * bits // 32 if dense else (d // 8 if bits <= 4 else d // 4)
+
+
 def gptq_pack(codes: torch.Tensor, bits: int, packed: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
-    """int32 [rows, d / 8]: eight codes per word, column 8k + t in bits 4t..4t+3 of word k."""
+    """int32 [rows, words]: eight 4-bit fields per word (bits <= 4; column 8k + t in bits 4t..4t+3 of
+    word k) or four 8-bit fields (bits 5..8)."""
     _need_cuda(codes, packed)
     rows, d = codes.shape
     if codes.dtype != torch.uint8 or not codes.is_contiguous():
         raise ValueError("codes must be contiguous uint8 [rows, d]")
     if packed is None:
-        packed = torch.empty((rows, d // 8), dtype=torch.int32, device=codes.device)
+        packed = torch.empty((rows, packed_words(d, bits)), dtype=torch.int32, device=codes.device)
     _check(_lib.lib().gptq_pack(_ptr(codes), rows, d, int(bits), _ptr(packed), _stream(stream)))
+    return packed
+
+
+def gptq_pack_dense(codes: torch.Tensor, bits: int, packed: Optional[torch.Tensor] = None,
+                    stream=None) -> torch.Tensor:
+    """int32 [rows, d * bits / 32]: each row as one bit stream, exactly `bits` bits per code."""
+    _need_cuda(codes, packed)
+    rows, d = codes.shape
+    if codes.dtype != torch.uint8 or not codes.is_contiguous():
+        raise ValueError("codes must be contiguous uint8 [rows, d]")
+    if packed is None:
+        packed = torch.empty((rows, packed_words(d, bits, True)), dtype=torch.int32, device=codes.device)
+    _check(_lib.lib().gptq_pack_dense(_ptr(codes), rows, d, int(bits), _ptr(packed), _stream(stream)))
     return packed
 
 
 def gptq_dequant_gemm(x: torch.Tensor, packed: torch.Tensor, scales: torch.Tensor, zeros: torch.Tensor,
                       d: int, group_size: int, g_idx: Optional[torch.Tensor] = None, bits: int = 4,
-                      y: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+                      y: Optional[torch.Tensor] = None, dense: bool = False, stream=None) -> torch.Tensor:
     """y = x W^T (float32 [m, rows]) with W expanded from the packed codes, scales and zeros inside the
     kernel; g_idx (int32 [d]) maps columns to groups, None meaning column k is in group k // g."""
     _need_cuda(x, packed, scales, zeros, g_idx, y)
@@ -183,8 +203,8 @@ def gptq_dequant_gemm(x: torch.Tensor, packed: torch.Tensor, scales: torch.Tenso
     rows = packed.shape[0]
     g = d if group_size <= 0 else group_size
     ng = (d + g - 1) // g
-    if packed.dtype != torch.int32 or packed.shape != (rows, d // 8) or not packed.is_contiguous():
-        raise ValueError("packed must be contiguous int32 [rows, d / 8]")
+    if packed.dtype != torch.int32 or packed.shape != (rows, packed_words(d, bits, dense)) or not packed.is_contiguous():
+        raise ValueError("packed must be contiguous int32 [rows, words] in the chosen layout")
     if scales.dtype != torch.float32 or scales.shape != (rows, ng) or not scales.is_contiguous():
         raise ValueError("scales must be contiguous float32 [rows, ngroups]")
     if zeros.dtype != torch.int32 or zeros.shape != (rows, ng) or not zeros.is_contiguous():
@@ -196,7 +216,8 @@ def gptq_dequant_gemm(x: torch.Tensor, packed: torch.Tensor, scales: torch.Tenso
         y = torch.empty((m, rows), dtype=torch.float32, device=x.device)
     if y.dtype != torch.float32 or y.dim() != 2 or y.shape != (m, rows) or y.stride(1) != 1:
         raise ValueError("y must be float32 [m, rows] with unit column stride")
-    _check(_lib.lib().gptq_dequant_gemm(_ptr(x), _DTYPE[x.dtype], m, x.stride(0), _ptr(packed), int(bits),
+    layout = GPTQ_LAYOUT_DENSE if dense else GPTQ_LAYOUT_FIELDS
+    _check(_lib.lib().gptq_dequant_gemm(_ptr(x), _DTYPE[x.dtype], m, x.stride(0), _ptr(packed), int(bits), layout,
                                         _ptr(scales), _ptr(zeros), _ptr(g_idx), rows, d, int(group_size), _ptr(y),
                                         y.stride(0), _stream(stream)))
     return y
@@ -226,5 +247,5 @@ def quantize_layer(W: torch.Tensor, X_chunks, params: Params, stream=None) -> La
         n += xc.shape[0]
     U, perm = gptq_factor(H, n, params, stream=stream)
     q = gptq_quantize_layer(W, U, perm, params, stream=stream)
-    packed = gptq_pack(q.codes, params.bits, stream=stream) if (d % 8 == 0 and params.bits <= 4) else None
+    packed = gptq_pack(q.codes, params.bits, stream=stream) if d % 8 == 0 else None
     return LayerResult(H=H, U=U, perm=perm, quant=q, packed=packed)

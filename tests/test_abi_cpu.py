@@ -140,23 +140,33 @@ def test_pack_rejects_bad_arguments():
     lib = _lib().lib()
     f = lib.gptq_pack
     assert f(FAKE, 4, 12, 4, FAKE, None) == -1     # d not a multiple of 8
-    assert f(FAKE, 4, 16, 5, FAKE, None) == -1     # more than a nibble
+    assert f(FAKE, 4, 16, 9, FAKE, None) == -1     # more than a byte
     assert f(FAKE, 4, 16, 0, FAKE, None) == -1
     assert f(None, 4, 16, 4, FAKE, None) == -1
     assert f(FAKE, 0, 16, 4, FAKE, None) == 0      # no rows: nothing to do
 
 
+def test_pack_dense_rejects_bad_arguments():
+    lib = _lib().lib()
+    f = lib.gptq_pack_dense
+    assert f(FAKE, 4, 20, 3, FAKE, None) == -1     # d * bits not a multiple of 32
+    assert f(FAKE, 4, 32, 9, FAKE, None) == -1
+    assert f(FAKE, 4, 32, 0, FAKE, None) == -1
+    assert f(None, 4, 32, 3, FAKE, None) == -1
+    assert f(FAKE, 0, 32, 3, FAKE, None) == 0      # no rows: nothing to do
+
+
 def test_dequant_gemm_rejects_bad_arguments():
     lib = _lib().lib()
     f = lib.gptq_dequant_gemm
-    # (x, dtype, m, ld_x, packed, bits, scales, zeros, g_idx, rows, d, group_size, y, ld_y, stream)
-    ok = (FAKE, 1, 2, 64, FAKE, 4, FAKE, FAKE, None, 16, 64, 32, FAKE, 16, None)
+    # (x, dtype, m, ld_x, packed, bits, layout, scales, zeros, g_idx, rows, d, group_size, y, ld_y, stream)
+    ok = (FAKE, 1, 2, 64, FAKE, 4, 0, FAKE, FAKE, None, 16, 64, 32, FAKE, 16, None)
 
     def call(**kw):
         a = list(ok)
         for k, v in kw.items():
-            a[["x", "dtype", "m", "ldx", "packed", "bits", "scales", "zeros", "gidx", "rows", "d", "g", "y", "ldy",
-               "s"].index(k)] = v
+            a[["x", "dtype", "m", "ldx", "packed", "bits", "layout", "scales", "zeros", "gidx", "rows", "d", "g", "y",
+               "ldy", "s"].index(k)] = v
         return f(*a)
 
     assert call(d=60) == -1                 # not a multiple of 8
@@ -166,7 +176,9 @@ def test_dequant_gemm_rejects_bad_arguments():
     assert call(dtype=7) == -1
     assert call(m=-1) == -1
     assert call(bits=0) == -1
-    assert call(bits=8) == -3               # wider than a nibble: unsupported
+    assert call(bits=9) == -1
+    assert call(layout=2) == -1
+    assert call(layout=1, bits=3, d=40) == -1   # dense needs d * bits to be a multiple of 32
     assert call(x=None) == -1
     assert call(packed=None) == -1
     assert call(scales=None) == -1

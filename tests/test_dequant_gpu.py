@@ -34,11 +34,11 @@ def _bound(x64, L, d):
     return 2.0 * (d / 64 + 48) * U32 * S
 
 
-def _gpu(L, x, xdtype, d, bits=4, pass_gidx=True, ldx_pad=0, gidx_offset=0):
+def _gpu(L, x, xdtype, d, bits=4, pass_gidx=True, ldx_pad=0, gidx_offset=0, dense=False):
     torch = torch_cuda()
     import post_weight_quantization_20_amd as g
     codes = dev_tensor(L.codes, "u8")
-    packed = g.gptq_pack(codes, bits)
+    packed = g.gptq_pack_dense(codes, bits) if dense else g.gptq_pack(codes, bits)
     xs = x
     if ldx_pad:
         xs = np.zeros((x.shape[0], d + ldx_pad), dtype=x.dtype)
@@ -49,14 +49,15 @@ def _gpu(L, x, xdtype, d, bits=4, pass_gidx=True, ldx_pad=0, gidx_offset=0):
         # gidx_offset > 0 hands over a g_idx that is not 16-byte aligned (a view one element in)
         gi = dev_tensor(np.concatenate([np.zeros(gidx_offset, np.int32), L.g_idx]), "i32")[gidx_offset:]
     y = g.gptq_dequant_gemm(xd, packed, dev_tensor(L.scales, "f32"), dev_tensor(L.zeros, "i32"), d, L.group_size,
-                            g_idx=gi, bits=bits)
+                            g_idx=gi, bits=bits, dense=dense)
     torch.cuda.synchronize()
     return y.cpu().numpy()
 
 
-def _oracle(L, x64, d, bits=4):
+def _oracle(L, x64, d, bits=4, dense=False):
     gidx = _groups(L, d)
-    return ref.dequant_matmul(x64, ref.pack(L.codes, bits), L.scales, L.zeros, gidx, d)
+    packed = ref.pack_dense(L.codes, bits) if dense else ref.pack(L.codes, bits)
+    return ref.dequant_matmul(x64, packed, L.scales, L.zeros, gidx, d, bits, dense)
 
 
 EXACT_CASES = [
@@ -101,6 +102,31 @@ def test_matrix_core_kernel_exact(rows, d, m, gs):
     x = synth.inference_x(22, m, d, "f16", exact=True)
     y = _gpu(L, x, "f16", d)
     assert np.array_equal(y.astype(np.float64), _oracle(L, synth.to_f64(x, "f16"), d))
+
+
+LAYOUT_CASES = [
+    # (bits, dense, x dtype, rows, d, m, group_size, act_order)
+    (8, False, "f16", 70, 1024, 1, 128, False),
+    (8, False, "bf16", 33, 512, 5, 64, True),
+    (5, False, "f32", 20, 256, 2, 0, False),
+    (3, True, "f16", 70, 2048, 1, 128, False),
+    (3, True, "f16", 40, 1056, 9, 32, True),
+    (2, True, "bf16", 33, 512, 3, 64, False),
+    (5, True, "f16", 25, 96 * 8, 2, 96, False),
+    (7, True, "f32", 17, 32 * 8, 4, 0, True),
+    (4, True, "f16", 64, 1024, 3, 128, False),     # dense at 4 bits is the nibble layout
+]
+
+
+@pytest.mark.parametrize("bits,dense,xdt,rows,d,m,gs,act", LAYOUT_CASES,
+                         ids=[f"{c[0]}bit-{'dense' if c[1] else 'fields'}-{c[2]}-m{c[5]}" for c in LAYOUT_CASES])
+def test_storage_layouts_exact(bits, dense, xdt, rows, d, m, gs, act):
+    """Byte fields (5 to 8 bits) and dense bit streams (codes straddling words) through the product."""
+    print(f"[dequant layout] bits {bits} dense {dense} x {xdt} rows {rows} d {d} m {m} g {gs} act {act}", flush=True)
+    L = synth.stored_layer(23, rows, d, bits, gs, act_order=act, exact=True)
+    x = synth.inference_x(24, m, d, xdt, exact=True)
+    y = _gpu(L, x, xdt, d, bits=bits, dense=dense)
+    assert np.array_equal(y.astype(np.float64), _oracle(L, synth.to_f64(x, xdt), d, bits, dense))
 
 
 @pytest.mark.parametrize("rows,m", [(8200, 2), (4100, 1), (4100, 8), (8193, 4)])
