@@ -151,7 +151,19 @@ def _ratio32(num, den) -> np.ndarray:
     return (np.asarray(num, dtype=np.float32) / np.asarray(den, dtype=np.float32)).astype(np.float64)
 
 
-def group_grid(wg: np.ndarray, maxq: int, sym: bool = False) -> Tuple[np.ndarray, np.ndarray]:
+FP16_MIN_SUB = 2.0 ** -24      # smallest positive float16
+FP16_MAX = 65504.0
+
+
+def fp16_scale(scale32: np.ndarray) -> np.ndarray:
+    """The scale as stored in 16 bits: the float32 scale rounded to the nearest float16 (ties to
+    even), kept positive and finite (a scale below half the smallest subnormal takes that subnormal,
+    one above the largest finite float16 takes that)."""
+    s = np.asarray(scale32, dtype=np.float32).astype(np.float16).astype(np.float64)
+    return np.clip(np.where(s == 0.0, FP16_MIN_SUB, s), FP16_MIN_SUB, FP16_MAX)
+
+
+def group_grid(wg: np.ndarray, maxq: int, sym: bool = False, compact: bool = False) -> Tuple[np.ndarray, np.ndarray]:
     """Min/max grid of each row of wg (rows x columns of one group).
 
     Asymmetric (the sketch): scale = max(wmax - wmin, 1e-8) / maxq and zero = round(-wmin / scale).
@@ -165,10 +177,21 @@ def group_grid(wg: np.ndarray, maxq: int, sym: bool = False) -> Tuple[np.ndarray
     if sym:
         m = np.maximum(np.abs(wmin), np.abs(wmax))
         scale = np.maximum(2.0 * m, 1e-8) / float(maxq)
+        if compact:
+            scale = fp16_scale(_scale32(2.0 * m, maxq))
         return scale, np.full(scale.shape, float((maxq + 1) // 2))
     scale = np.maximum(wmax - wmin, 1e-8) / float(maxq)
+    if compact:
+        scale = fp16_scale(_scale32(wmax - wmin, maxq))
+        return scale, np.clip(_round_ratio(-wmin, scale), 0.0, float(maxq))
     zero = _round_ratio(-wmin, scale)
     return scale, zero
+
+
+def _scale32(span: np.ndarray, maxq: int) -> np.ndarray:
+    """max(span, 1e-8) / maxq in float32, the precision in which the scale's 16-bit rounding is decided."""
+    sp = np.maximum(np.asarray(span, dtype=np.float32), np.float32(1e-8))
+    return (sp / np.float32(maxq)).astype(np.float64)
 
 
 def quantize_to_grid(w: np.ndarray, scale: np.ndarray, zero: np.ndarray, maxq: int) -> Tuple[np.ndarray, np.ndarray]:
@@ -227,10 +250,22 @@ def _follow_pick(own: np.ndarray, ratio: np.ndarray, offset: np.ndarray, lo: flo
     return out, int(np.count_nonzero(ok)), int(np.count_nonzero(ok & (other != own))), int(np.count_nonzero(tie))
 
 
+def _follow_scale(own: np.ndarray, s32: np.ndarray, other: Optional[np.ndarray], rtol: float = 1e-5):
+    """Compact grids: take the other implementation's 16-bit scale where this oracle's float32 scale
+    lies within rtol of a float16 rounding boundary and the other scale is one of the two neighbours."""
+    if other is None:
+        return own, 0
+    lo = fp16_scale(s32 * (1.0 - rtol))
+    hi = fp16_scale(s32 * (1.0 + rtol))
+    other = np.asarray(other, dtype=np.float64)
+    ok = (lo != hi) & ((other == lo) | (other == hi))
+    return np.where(ok, other, own), int(np.count_nonzero(ok & (other != own)))
+
+
 def quantize_layer(W: np.ndarray, U: np.ndarray, bits: int, group_size: int, block_size: int,
                    perm: Optional[np.ndarray] = None, grid: Optional[Tuple[np.ndarray, np.ndarray]] = None,
-                   follow: Optional[Tuple[np.ndarray, np.ndarray]] = None, tau: float = 1e-3,
-                   sym: bool = False, static_groups: bool = False) -> QuantResult:
+                   follow: Optional[Tuple[np.ndarray, ...]] = None, tau: float = 1e-3,
+                   sym: bool = False, static_groups: bool = False, compact: bool = False) -> QuantResult:
     """Quantize W (rows x d, original column order) with U (upper, processing order).
 
     For each block of B columns in processing order, and each column i in it:
@@ -247,6 +282,10 @@ def quantize_layer(W: np.ndarray, U: np.ndarray, bits: int, group_size: int, blo
     consecutive original columns (the Technical Guide's static_groups setting; the pages give only
     its name, so this plain reading of "static" is parity-unpinned); column i then uses the grid of
     group perm[i] // g, and g_idx is k // g whatever the order.
+    compact: each grid is stored as a 16-bit scale and a zero of the code width (tools page, "Memory
+    arithmetic"), and the loop quantizes with exactly those: the scale rounded to float16 (see
+    fp16_scale), the zero clamped to [0, maxq]. With follow=(codes, zeros, scales) the oracle takes
+    the other side's float16 scale where its own float32 scale sits on a rounding boundary.
     follow: optional (codes, zeros) of another implementation in processing order; at decisions whose
     float32 ratio lies within `tau` of a half-integer this oracle takes that implementation's choice
     when it is one of the two nearest grid points (both are correct roundings within the tie window).
@@ -271,21 +310,32 @@ def quantize_layer(W: np.ndarray, U: np.ndarray, bits: int, group_size: int, blo
     row_loss = np.zeros(rows, dtype=np.float64)
     f_codes = None if follow is None else np.asarray(follow[0], dtype=np.float64)
     f_zeros = None if follow is None else np.asarray(follow[1], dtype=np.float64)
+    f_scales = None if (follow is None or len(follow) < 3) else np.asarray(follow[2], dtype=np.float64)
+
+    def grid_of(wg, gi):
+        """A group's grid from its current weights wg, following the other side at ties."""
+        nonlocal adopted, adopted_diff, near
+        sg, zg = group_grid(wg, maxq, sym, compact)
+        wmin = np.min(wg, axis=1)
+        if compact and f_scales is not None:
+            span = 2.0 * np.maximum(np.abs(wmin), np.abs(np.max(wg, axis=1))) if sym else np.max(wg, axis=1) - wmin
+            sg, ad = _follow_scale(sg, _scale32(span, maxq), f_scales[:, gi])
+            adopted_diff += ad
+            if not sym:
+                zg = np.clip(_round_ratio(-wmin, sg), 0.0, float(maxq))
+        if f_zeros is not None and not sym:
+            lo, hi = (0.0, float(maxq)) if compact else (-np.inf, np.inf)
+            zg, a, ad, nt = _follow_pick(zg, _ratio32(-wmin, sg), np.zeros(len(zg)), lo, hi, f_zeros[:, gi], tau)
+            adopted += a
+            adopted_diff += ad
+            near += nt
+        return sg, zg
     adopted = adopted_diff = near = 0
 
     if static_groups and grid is None:
         for gi in range(ngroups):
             cols = slice(gi * g, min((gi + 1) * g, d))
-            sg, zg = group_grid(W[:, cols], maxq, sym)
-            if f_zeros is not None and not sym:
-                wmin = np.min(W[:, cols], axis=1)
-                zg, a, ad, nt = _follow_pick(zg, _ratio32(-wmin, sg), np.zeros(rows), -np.inf, np.inf,
-                                             f_zeros[:, gi], tau)
-                adopted += a
-                adopted_diff += ad
-                near += nt
-            scales[:, gi] = sg
-            zeros[:, gi] = zg
+            scales[:, gi], zeros[:, gi] = grid_of(W[:, cols], gi)
 
     s = z = None
     for b in range(0, d, B):
@@ -301,14 +351,7 @@ def quantize_layer(W: np.ndarray, U: np.ndarray, bits: int, group_size: int, blo
                     s = np.asarray(grid[0], dtype=np.float64)[:, gi]
                     z = np.asarray(grid[1], dtype=np.float64)[:, gi]
                 else:
-                    s, z = group_grid(Wp[:, i:min(i + g, d)], maxq, sym)
-                    if f_zeros is not None and not sym:
-                        wmin = np.min(Wp[:, i:min(i + g, d)], axis=1)
-                        z, a, ad, nt = _follow_pick(z, _ratio32(-wmin, s), np.zeros(rows), -np.inf, np.inf,
-                                                    f_zeros[:, gi], tau)
-                        adopted += a
-                        adopted_diff += ad
-                        near += nt
+                    s, z = grid_of(Wp[:, i:min(i + g, d)], gi)
                 scales[:, gi] = s
                 zeros[:, gi] = z
             w = Wp[:, i].copy()
@@ -471,14 +514,14 @@ def gptq(W: np.ndarray, chunks: Iterable[np.ndarray], bits: int, group_size: int
          act_order: bool = False, damp: float = 0.01, perm: Optional[np.ndarray] = None,
          follow: Optional[Tuple[np.ndarray, np.ndarray]] = None, tau: float = 1e-3,
          H: Optional[np.ndarray] = None, n: Optional[int] = None, sym: bool = False,
-         static_groups: bool = False) -> LayerResult:
+         static_groups: bool = False, compact: bool = False) -> LayerResult:
     """The whole single-layer solver: Hessian, damping and order, factor, column loop, packing."""
     if H is None:
         H, n = hessian(chunks)
     Hhat, p, lam = damp_and_order(H, n, damp, act_order, perm)
     U = inverse_cholesky_upper(Hhat)
     qr = quantize_layer(W, U, bits, group_size, block_size, perm=p, follow=follow, tau=tau, sym=sym,
-                        static_groups=static_groups)
+                        static_groups=static_groups, compact=compact)
     d = qr.codes.shape[1]
     packed = pack(qr.codes, bits) if d % (32 // field_bits(bits)) == 0 else None
     return LayerResult(H=H, n=n, Hhat=Hhat, lam=lam, U=U, quant=qr, packed=packed)

@@ -23,8 +23,8 @@ MUTATIONS = [
     ("unscaled error", "err = (w - dq) / U[i, i]", "err = (w - dq)"),
     ("transposed lazy operand", "Wp[:, e_blk:] -= Err @ U[b:e_blk, e_blk:]",
      "Wp[:, e_blk:] -= Err @ U[e_blk:, b:e_blk].T[:, :U.shape[0] - e_blk]"),
-    ("grid from original weights", "s, z = group_grid(Wp[:, i:min(i + g, d)], maxq, sym)",
-     "s, z = group_grid(W[:, perm][:, i:min(i + g, d)], maxq, sym)"),
+    ("grid from original weights", "s, z = grid_of(Wp[:, i:min(i + g, d)], gi)",
+     "s, z = grid_of(W[:, perm][:, i:min(i + g, d)], gi)"),
     ("zero not added", "q = np.clip(_round_ratio(w, scale) + zero, 0.0, float(maxq))",
      "q = np.clip(_round_ratio(w, scale), 0.0, float(maxq))"),
     ("inverse not factored", "    u, info = lapack.dpotrf(inv, lower=0, clean=1)",
@@ -43,8 +43,12 @@ MUTATIONS = [
     ("symmetric zero at code 0", "return scale, np.full(scale.shape, float((maxq + 1) // 2))",
      "return scale, np.zeros(scale.shape)"),
     ("symmetric scale from one side", "m = np.maximum(np.abs(wmin), np.abs(wmax))", "m = np.abs(wmax)"),
-    ("static grid in processing order", "sg, zg = group_grid(W[:, cols], maxq, sym)",
-     "sg, zg = group_grid(W[:, perm][:, cols], maxq, sym)"),
+    ("static grid in processing order", "scales[:, gi], zeros[:, gi] = grid_of(W[:, cols], gi)",
+     "scales[:, gi], zeros[:, gi] = grid_of(W[:, perm][:, cols], gi)"),
+    ("compact scale not rounded to 16 bits", "    s = np.asarray(scale32, dtype=np.float32).astype(np.float16).astype(np.float64)",
+     "    s = np.asarray(scale32, dtype=np.float64)"),
+    ("compact zero not clamped", "        return scale, np.clip(_round_ratio(-wmin, scale), 0.0, float(maxq))",
+     "        return scale, _round_ratio(-wmin, scale)"),
     ("static g_idx follows the order", "g_idx[:] = (np.arange(d) // g).astype(np.int32)",
      "g_idx[perm] = (np.arange(d) // g).astype(np.int32)"),
     ("dequant groups by position", "g = np.asarray(g_idx, dtype=np.int64)",
@@ -141,6 +145,16 @@ def _checks(m):
         if (not np.array_equal(rst.quant.codes, ref.rtn(W, 4, 16).codes)
                 or not np.array_equal(rst.quant.g_idx, np.arange(d) // 16)):
             failed.append("static identity -> original-order rtn")
+        # compact metadata: every scale is a float16 value, zeros fit the code width, and the
+        # stored layer dequantizes to the weights the loop used
+        Wc = W.copy()
+        Wc[0] = np.abs(Wc[0]) + 0.05           # a one-signed row: its zero would lie below 0
+        rc = m.gptq(Wc, [X], 4, 16, 32, act_order=True, damp=0.01, compact=True)
+        qc = rc.quant
+        if (not np.array_equal(qc.scales, qc.scales.astype(np.float16).astype(np.float64))
+                or qc.zeros.min() < 0 or qc.zeros.max() > 15
+                or not np.array_equal(ref.dequantize(ref.pack(qc.codes, 4), qc.scales, qc.zeros, qc.g_idx, d), qc.Q)):
+            failed.append("compact metadata")
         # H = I must reduce to round-to-nearest with dynamic grids
         rI = m.gptq(W, None, 4, 16, 32, H=np.eye(d) * 2.0, n=1)
         if not np.array_equal(rI.quant.codes, ref.rtn(W, 4, 16).codes):

@@ -585,3 +585,45 @@ def test_dense_three_bit_saves_a_quarter():
     storage follows the bit width)."""
     c = np.zeros((1, 256), np.uint8)
     assert ref.pack_dense(c, 3).shape[1] == 24 and ref.pack(c, 3).shape[1] == 32
+
+
+# ---------------------------------------------------------------- compact metadata
+
+def test_compact_metadata_bits_per_weight():
+    """Tools page, 'Memory arithmetic': 4-bit weights with a 16-bit scale and a 4-bit zero per group of
+    128 cost about 0.16 extra bits per weight; groups of 32 cost about four times as much."""
+    e = GOLD["memory_arithmetic"]
+    over = ref.bits_per_weight(e["bits"], e["group_size"], e["scale_bits"], e["zero_bits"]) - e["bits"]
+    assert over == pytest.approx(e["overhead_bits_per_weight_about"], abs=0.01)
+    assert ref.bits_per_weight(4, 32, 16, 4) - 4 == pytest.approx(4 * over)
+
+
+def test_compact_grid_closed_form():
+    """A compact grid holds exactly what 16 bits of scale and a code-width zero can store, and the
+    codes come from that stored grid."""
+    wg = np.array([[-0.3, 0.7, 0.1], [0.5, 0.9, 0.6], [-0.9, -0.2, -0.5], [1e-12, 1e-12, 1e-12]])
+    s, z = ref.group_grid(wg, 15, compact=True)
+    s_exact = np.array([1.0, 0.4, 0.7, 1e-8]) / 15
+    assert np.array_equal(s[:3], s_exact[:3].astype(np.float32).astype(np.float16).astype(np.float64))
+    assert s[3] == 2.0 ** -24                      # below float16 range: the smallest subnormal
+    assert z[0] == np.rint(0.3 / s[0]) and z[1] == 0 and z[2] == 15   # one-signed rows clamp
+    q, dq = ref.quantize_to_grid(wg[:, :1], s[:, None], z[:, None], 15)
+    assert np.allclose(dq[:, 0], s * (q[:, 0] - z))
+
+
+@pytest.mark.parametrize("act,static,sym", [(False, False, False), (True, False, False), (True, True, False),
+                                            (False, False, True)])
+def test_compact_layer_stores_what_it_used(act, static, sym):
+    rng = np.random.default_rng(37)
+    d = 64
+    X = _correlated_x(rng, 96, d) * rng.uniform(0.3, 3.0, d)[None, :]
+    W = rng.standard_normal((10, d)) * 0.02
+    W[0] += 0.08                                   # positive row: zeros clamp at 0
+    r = ref.gptq(W, [X], 4, 16, 32, act_order=act, static_groups=static, sym=sym, compact=True)
+    q = r.quant
+    assert np.array_equal(q.scales, q.scales.astype(np.float16).astype(np.float64))
+    assert q.zeros.min() >= 0 and q.zeros.max() <= 15
+    assert np.array_equal(ref.dequantize(ref.pack(q.codes, 4), q.scales.astype(np.float16).astype(np.float64),
+                                         q.zeros, q.g_idx, d), q.Q)
+    r1 = ref.gptq(W, [X], 4, 16, 1, act_order=act, static_groups=static, sym=sym, compact=True)
+    assert np.array_equal(r1.quant.codes, q.codes)
