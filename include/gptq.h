@@ -89,6 +89,12 @@ typedef struct {
                             loop from the original weights of g consecutive original columns,
                             each column uses its original group's grid, and g_idx = k / g also
                             with act-order (the Technical Guide's static_groups setting).        */
+  int32_t compact_meta;  /* 1: each grid is what a 16-bit scale and a zero of the code width store
+                            (tools page, "Memory arithmetic"), and the loop quantizes with exactly
+                            that: the scale rounded to the nearest float16 (the smallest positive
+                            float16 if it would round to zero), the zero clamped to [0, maxq].
+                            The fp32 scales and int32 zeros written then convert to that storage
+                            without loss.                                                      */
   double damp;           /* relative damping >= 0: lambda = damp * mean(diag(H / n)) (Step 4)     */
 } gptq_params_t;
 

@@ -23,6 +23,7 @@ class gptq_params_t(ctypes.Structure):
         ("act_order", c_int32),
         ("sym", c_int32),
         ("static_groups", c_int32),
+        ("compact_meta", c_int32),
         ("damp", c_double),
     ]
 

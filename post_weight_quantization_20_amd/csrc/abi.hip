@@ -15,7 +15,9 @@ bool dtype_ok(int32_t t) { return t == GPTQ_F32 || t == GPTQ_F16 || t == GPTQ_BF
 // Validates the settings shared by factor and quantize. Returns GPTQ_OK or the error.
 gptq_status_t check_params(const gptq_params_t* p, int64_t d, bool quant) {
   if (!p) return GPTQ_EINVAL;
-  if ((p->sym != 0 && p->sym != 1) || (p->static_groups != 0 && p->static_groups != 1)) return GPTQ_EINVAL;
+  if ((p->sym != 0 && p->sym != 1) || (p->static_groups != 0 && p->static_groups != 1) ||
+      (p->compact_meta != 0 && p->compact_meta != 1))
+    return GPTQ_EINVAL;
   if (p->act_order != 0 && p->act_order != 1) return GPTQ_EINVAL;
   if (!(p->damp >= 0.0) || !std::isfinite(p->damp)) return GPTQ_EINVAL;
   if (!quant) return GPTQ_OK;
@@ -117,7 +119,7 @@ gptq_status_t gptq_quantize_layer(const void* W, int32_t w_dtype, int64_t rows, 
   const int64_t g = p->group_size <= 0 ? d : p->group_size;
   hipStream_t s = static_cast<hipStream_t>(stream);
   return hip_status(gptq::quantize(W, w_dtype, rows, d, ld_w, U, perm, p->bits, g, p->block_size, p->sym,
-                                   p->static_groups, codes, scales, zeros, g_idx, loss, work, s));
+                                   p->static_groups, p->compact_meta, codes, scales, zeros, g_idx, loss, work, s));
 }
 
 gptq_status_t gptq_pack(const uint8_t* codes, int64_t rows, int64_t d, int32_t bits, int32_t* packed, void* stream) {

@@ -37,14 +37,26 @@ GPTQ_DEV float load_as_f32(const void* p, int dtype, int64_t idx) {
 // the same recipe on [-m, m] with m = max(|wmin|, |wmax|), scale = max(2 m, 1e-8) / maxq, and the
 // zero fixed at the middle code (maxq + 1) / 2. rs is the correctly rounded reciprocal of the
 // scale, used by div_rn.
-GPTQ_DEV void make_grid(float wmin, float wmax, float maxq, bool sym, float& s, float& z, float& rs) {
+// The scale as stored in 16 bits (tools page, "Memory arithmetic"): rounded to the nearest float16,
+// ties to even, kept positive and finite (the smallest subnormal below, the largest float16 above).
+GPTQ_DEV float fp16_scale(float s) {
+  const float h = (float)(_Float16)s;
+  return fminf(h == 0.0f ? 0x1p-24f : h, 65504.0f);
+}
+
+// compact: the grid is what a 16-bit scale and a zero of the code width store, and the loop uses
+// exactly that (the scale rounded by fp16_scale, the zero clamped to [0, maxq]).
+GPTQ_DEV void make_grid(float wmin, float wmax, float maxq, bool sym, bool compact, float& s, float& z, float& rs) {
   if (sym) {
     const float m = fmaxf(fabsf(wmin), fabsf(wmax));
     s = fmaxf(2.0f * m, 1e-8f) / maxq;
+    if (compact) s = fp16_scale(s);
     z = 0.5f * (maxq + 1.0f);
   } else {
     s = fmaxf(wmax - wmin, 1e-8f) / maxq;
+    if (compact) s = fp16_scale(s);
     z = rintf(-wmin / s);
+    if (compact) z = fminf(fmaxf(z, 0.0f), maxq);
   }
   rs = 1.0f / s;
 }
@@ -132,10 +144,12 @@ struct QuantLayout {
   size_t off_wp, off_codes, off_err, off_loss, off_iperm, off_colgrp, total;
 };
 QuantLayout quant_layout(int64_t rows, int64_t d, int block);
-// sym: symmetric grids; static_groups: grids of original column groups fixed before the loop.
+// sym: symmetric grids; static_groups: grids of original column groups fixed before the loop;
+// compact: 16-bit scales and zeros clamped to the code width, used as stored.
 hipError_t quantize(const void* W, int w_dtype, int64_t rows, int64_t d, int64_t ld_w, const float* U,
-                    const int32_t* perm, int bits, int64_t g, int B, int sym, int static_groups, uint8_t* codes,
-                    float* scales, int32_t* zeros, int32_t* g_idx, double* loss, void* work, hipStream_t s);
+                    const int32_t* perm, int bits, int64_t g, int B, int sym, int static_groups, int compact,
+                    uint8_t* codes, float* scales, int32_t* zeros, int32_t* g_idx, double* loss, void* work,
+                    hipStream_t s);
 // Field layout (nibbles up to 4 bits, bytes above) and the dense bit stream.
 hipError_t pack(const uint8_t* codes, int64_t rows, int64_t d, int bits, int32_t* packed, hipStream_t s);
 hipError_t pack_dense(const uint8_t* codes, int64_t rows, int64_t d, int bits, int32_t* packed, hipStream_t s);

@@ -38,6 +38,7 @@ struct QArgs {
   int32_t* zeros;        // [rows x ngroups]
   int64_t ngroups;
   int sym;               // symmetric grids (in-block grids only)
+  int compact;           // 16-bit scales, zeros clamped to the code width (in-block grids only)
   const int32_t* colgrp; // static groups: group of each processing column (its grid is in scales/zeros)
   float* err;            // this block's errors: [rows x 16 * CPL] at leading dimension err_ld
   int64_t err_ld;
@@ -193,7 +194,7 @@ __global__ __launch_bounds__(256) void quant_block_kernel(QArgs a) {
         mn = fminf(mn, row_ror<4>(mn)); mx = fmaxf(mx, row_ror<4>(mx));
         mn = fminf(mn, row_ror<2>(mn)); mx = fmaxf(mx, row_ror<2>(mx));
         mn = fminf(mn, row_ror<1>(mn)); mx = fmaxf(mx, row_ror<1>(mx));
-        make_grid(mn, mx, a.maxq, a.sym != 0, s, z, rs);
+        make_grid(mn, mx, a.maxq, a.sym != 0, a.compact != 0, s, z, rs);
         if (lr == 0 && row_ok && k < nc) {
           // column and group indices stay below 2^31
           const int64_t gi = (uint32_t)(a.b + k) / (uint32_t)a.g;
@@ -277,7 +278,8 @@ __global__ __launch_bounds__(256) void quant_block_kernel(QArgs a) {
 // Group grid for groups longer than a block: min/max of the current weights of columns
 // [b, b + len) of each row, one wave per row.
 __global__ __launch_bounds__(256) void group_grid_kernel(const float* __restrict__ Wp, int64_t ldw, int64_t rows,
-                                                         int64_t b, int64_t len, float maxq, int sym, int64_t gi,
+                                                         int64_t b, int64_t len, float maxq, int sym, int compact,
+                                                         int64_t gi,
                                                          float* __restrict__ scales, int32_t* __restrict__ zeros,
                                                          int64_t ngroups) {
   const int lane = threadIdx.x & 63;
@@ -297,7 +299,7 @@ __global__ __launch_bounds__(256) void group_grid_kernel(const float* __restrict
   }
   if (lane == 0) {
     float s, z, rs;
-    make_grid(mn, mx, maxq, sym != 0, s, z, rs);
+    make_grid(mn, mx, maxq, sym != 0, compact != 0, s, z, rs);
     scales[row * ngroups + gi] = s;
     zeros[row * ngroups + gi] = (int32_t)z;
   }
@@ -307,8 +309,8 @@ __global__ __launch_bounds__(256) void group_grid_kernel(const float* __restrict
 // one wave per (row, group); before any column is quantized.
 __global__ __launch_bounds__(256) void static_grid_kernel(const void* __restrict__ W, int dtype, int64_t ld_w,
                                                           int64_t rows, int64_t d, int64_t g, int64_t ngroups,
-                                                          float maxq, int sym, float* __restrict__ scales,
-                                                          int32_t* __restrict__ zeros) {
+                                                          float maxq, int sym, int compact,
+                                                          float* __restrict__ scales, int32_t* __restrict__ zeros) {
   const int lane = threadIdx.x & 63;
   const int64_t item = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
   if (item >= rows * ngroups) return;
@@ -327,7 +329,7 @@ __global__ __launch_bounds__(256) void static_grid_kernel(const void* __restrict
   }
   if (lane == 0) {
     float s, z, rs;
-    make_grid(mn, mx, maxq, sym != 0, s, z, rs);
+    make_grid(mn, mx, maxq, sym != 0, compact != 0, s, z, rs);
     scales[item] = s;
     zeros[item] = (int32_t)z;
   }
@@ -530,8 +532,9 @@ QuantLayout quant_layout(int64_t rows, int64_t d, int block) {
 }
 
 hipError_t quantize(const void* W, int w_dtype, int64_t rows, int64_t d, int64_t ld_w, const float* U,
-                    const int32_t* perm, int bits, int64_t g, int B, int sym, int static_groups, uint8_t* codes,
-                    float* scales, int32_t* zeros, int32_t* g_idx, double* loss, void* work, hipStream_t s) {
+                    const int32_t* perm, int bits, int64_t g, int B, int sym, int static_groups, int compact,
+                    uint8_t* codes, float* scales, int32_t* zeros, int32_t* g_idx, double* loss, void* work,
+                    hipStream_t s) {
   const QuantLayout L = quant_layout(rows, d, B);
   char* wb = static_cast<char*>(work);
   float* Wp = reinterpret_cast<float*>(wb + L.off_wp);
@@ -548,7 +551,7 @@ hipError_t quantize(const void* W, int w_dtype, int64_t rows, int64_t d, int64_t
   if (static_groups && rows > 0) {
     const int64_t items = rows * ngroups;
     hipLaunchKernelGGL(static_grid_kernel, dim3((unsigned)((items + 3) / 4)), dim3(256), 0, s, W, w_dtype, ld_w, rows,
-                       d, g, ngroups, maxq, sym, scales, zeros);
+                       d, g, ngroups, maxq, sym, compact, scales, zeros);
   }
   if (rows > 0) {
     const unsigned gx = (unsigned)std::min<int64_t>((L.ldw + 1023) / 1024, 64);
@@ -570,13 +573,13 @@ hipError_t quantize(const void* W, int w_dtype, int64_t rows, int64_t d, int64_t
       const bool in_block = g <= B;
       if (!static_groups && !in_block && b % g == 0) {
         hipLaunchKernelGGL(group_grid_kernel, dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, s, Wp, L.ldw, rows, b,
-                           std::min<int64_t>(g, d - b), maxq, sym, b / g, scales, zeros, ngroups);
+                           std::min<int64_t>(g, d - b), maxq, sym, compact, b / g, scales, zeros, ngroups);
       }
       QArgs a;
       a.Wp = Wp; a.ldw = L.ldw; a.rows = rows; a.d = d; a.b = b; a.ncols = nc; a.U = U; a.g = g;
       a.grid_in_block = in_block; a.maxq = maxq; a.codes_p = codes_p; a.scales = scales; a.zeros = zeros;
       a.ngroups = ngroups; a.err = err + (b - s0); a.err_ld = L.ld_err; a.row_loss = row_loss;
-      a.sym = sym; a.colgrp = colgrp;
+      a.sym = sym; a.compact = compact; a.colgrp = colgrp;
       const bool st = static_groups != 0;
       switch (cpl) {
         case 1: launch_block<1>(a, st, s); break;

@@ -44,10 +44,12 @@ class Params:
     sym: bool = False
     static_groups: bool = False
     damp: float = 0.01
+    compact_meta: bool = False
 
     def c(self) -> _lib.gptq_params_t:
         return _lib.gptq_params_t(int(self.bits), int(self.group_size), int(self.block_size), int(bool(self.act_order)),
-                                  int(bool(self.sym)), int(bool(self.static_groups)), float(self.damp))
+                                  int(bool(self.sym)), int(bool(self.static_groups)), int(bool(self.compact_meta)),
+                                  float(self.damp))
 
     def groups(self, d: int) -> int:
         g = d if self.group_size <= 0 else self.group_size

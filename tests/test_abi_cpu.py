@@ -37,7 +37,7 @@ def test_header_is_plain_c():
     cc = shutil.which("gcc") or shutil.which("cc")
     if cc is None:
         pytest.skip("no C compiler")
-    src = '#include "gptq.h"\nint main(void){ gptq_params_t p; (void)p; return (int)sizeof(gptq_params_t) - 32; }\n'
+    src = '#include "gptq.h"\nint main(void){ gptq_params_t p; (void)p; return (int)sizeof(gptq_params_t) - 40; }\n'
     r = subprocess.run([cc, "-std=c99", "-Wall", "-Werror", "-pedantic", "-I", os.path.dirname(HEADER), "-x", "c",
                         "-fsyntax-only", "-"], input=src, text=True, capture_output=True)
     assert r.returncode == 0, r.stderr
@@ -56,14 +56,16 @@ def test_library_exports_every_declared_symbol():
 
 def test_params_struct_layout():
     L = _lib()
-    assert ctypes.sizeof(L.gptq_params_t) == 32
-    assert L.gptq_params_t.damp.offset == 24
+    assert ctypes.sizeof(L.gptq_params_t) == 40
+    assert L.gptq_params_t.compact_meta.offset == 24
+    assert L.gptq_params_t.damp.offset == 32
 
 
 def _p(L, **kw):
-    d = dict(bits=4, group_size=128, block_size=128, act_order=0, sym=0, static_groups=0, damp=0.01)
+    d = dict(bits=4, group_size=128, block_size=128, act_order=0, sym=0, static_groups=0, compact_meta=0, damp=0.01)
     d.update(kw)
     return L.gptq_params_t(d["bits"], d["group_size"], d["block_size"], d["act_order"], d["sym"], d["static_groups"],
+                           d["compact_meta"],
                            d["damp"])
 
 
@@ -130,6 +132,7 @@ def test_quantize_rejects_bad_arguments():
     assert call(_p(L, block_size=256)) == -3
     assert call(_p(L, sym=2)) == -1                     # flags are 0 or 1
     assert call(_p(L, static_groups=3)) == -1
+    assert call(_p(L, compact_meta=2)) == -1
     assert call(_p(L), ld=255) == -1
     assert call(_p(L), dtype=5) == -1
     assert call(_p(L), d=0) == -1

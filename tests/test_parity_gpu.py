@@ -291,6 +291,39 @@ def test_quantize_parity_sym_static(kw, act, sym, static):
     assert np.allclose(dequant(out["codes"], out["scales"], out["zeros"], out["g_idx"]), o.Q, rtol=1e-5, atol=1e-7)
 
 
+@pytest.mark.parametrize("kw", SYM_STATIC_CASES, ids=[str(i) for i in range(len(SYM_STATIC_CASES))])
+@pytest.mark.parametrize("act", [False, True])
+@pytest.mark.parametrize("sym,static", [(0, 0), (1, 0), (0, 1)], ids=["dynamic", "sym", "static"])
+def test_quantize_parity_compact(kw, act, sym, static):
+    """Compact metadata: float16 scales and code-width zeros, used by the loop as stored. The oracle
+    follows the GPU's float16 scale only where its own float32 scale sits on a rounding boundary."""
+    torch = torch_cuda()
+    import post_weight_quantization_20_amd as g
+    kw = dict(kw)
+    d = kw.pop("d", 300)
+    print(f"[compact] {kw} d {d} act {act} sym {sym} static {static}", flush=True)
+    case = _case("qc", 60 + d, d=d, n=2 * d, chunk=4096, x_dtype="f32", w_dtype="f32", act_order=act, **kw)
+    W = synth.weight(case)
+    W[::7] = np.abs(W[::7]) + 0.01          # one-signed rows: their zeros clamp to the code range
+    H, n = ref.hessian([synth.to_f64(synth.x_chunk(case, 0), "f32")])
+    Hh, perm, lam = ref.damp_and_order(H, n, case.damp, act)
+    U32 = ref.inverse_cholesky_upper(Hh).astype(np.float32)
+    p = params_of(case, sym=bool(sym), static_groups=bool(static), compact_meta=True)
+    q = g.gptq_quantize_layer(torch.from_numpy(W).cuda(), torch.from_numpy(U32).cuda(),
+                              torch.from_numpy(perm.astype(np.int32)).cuda(), p)
+    torch.cuda.synchronize()
+    out = dict(codes=q.codes.cpu().numpy(), scales=q.scales.cpu().numpy(), zeros=q.zeros.cpu().numpy(),
+               g_idx=q.g_idx.cpu().numpy(), loss=float(q.loss.cpu().numpy()[0]))
+    maxq = (1 << case.bits) - 1
+    assert np.array_equal(out["scales"], out["scales"].astype(np.float16).astype(np.float32))
+    assert out["zeros"].min() >= 0 and out["zeros"].max() <= maxq
+    o = ref.quantize_layer(W.astype(np.float64), U32.astype(np.float64), case.bits, case.group_size,
+                           case.block_size, perm=perm, follow=(out["codes"][:, perm], out["zeros"], out["scales"]),
+                           tau=TAU, sym=bool(sym), static_groups=bool(static), compact=True)
+    check_quant_parity(out, o)
+    assert np.array_equal(out["scales"].astype(np.float64), o.scales)
+
+
 # ------------------------------------------------------------------ whole layer
 
 ECASES = [
