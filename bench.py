@@ -35,7 +35,8 @@ PEAK_F16_TFLOPS = 2500.0      # MI355X dense fp16/bf16 matrix peak
 PEAK_F32_TFLOPS = 157.3       # MI355X fp32 matrix peak
 PEAK_HBM_GBS = 8000.0         # MI355X HBM3E
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.json")
-KERNEL_SOURCES = {"hess_kernel": "post_weight_quantization_20_amd/csrc/hessian.hip"}
+KERNEL_SOURCES = {"hess_kernel": "post_weight_quantization_20_amd/csrc/hessian.hip",
+                  "dq_fast_kernel": "post_weight_quantization_20_amd/csrc/dequant.hip"}
 
 
 def parse():
@@ -65,7 +66,7 @@ def load_traffic(kernel: str, workload: str):
     try:
         with open(TRAFFIC_FILE) as f:
             rec = json.load(f)[kernel]
-    except (OSError, KeyError, ValueError):
+    except (OSError, KeyError, ValueError, TypeError):
         return None
     if rec.get("workload") != workload or rec.get("source_sha256_16") != source_hash(KERNEL_SOURCES[kernel]):
         return None
@@ -224,8 +225,17 @@ def bench_dequant(args):
                    "rows": rows, "d": d, "batch": m, "bits": bits, "group_size": gs, "act_order": int(act)},
         "roofline": {"kernel": "gptq_dequant_gemm", "bound": "hbm", "achieved": round(achieved, 1),
                      "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4),
-                     "traffic": None, "bytes_per_launch": byts, "avg_launch_ms": round(ms, 5)},
+                     "traffic": load_traffic("dq_fast_kernel", f"dequant {args.dequant} m{m}"),
+                     "bytes_per_launch": byts, "avg_launch_ms": round(ms, 5)},
     }
+    if args.copy_calibration:
+        src = torch.empty(1 << 28, dtype=torch.float32, device=dev).fill_(1.0)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        out["copy_calibration_bytes"] = {"read": src.numel() * 4, "write": dst.numel() * 4}
+        del src, dst
     if not args.no_cpu_baseline:
         print("[bench] timing the float64 oracle on a bounded sample", file=sys.stderr, flush=True)
         out["cpu_baseline"] = dequant_cpu_baseline(L, synth.to_f64(x, "f16"), d, bits,
