@@ -129,6 +129,20 @@ def test_storage_layouts_exact(bits, dense, xdt, rows, d, m, gs, act):
     assert np.array_equal(y.astype(np.float64), _oracle(L, synth.to_f64(x, xdt), d, bits, dense))
 
 
+@pytest.mark.parametrize("m", [5, 16])
+def test_matrix_core_kernel_far_zeros_exact(m):
+    """Zeros far outside the code range (groups of one sign far from zero) through the matrix-core
+    kernel, which subtracts z sum x in fp32 after the product. Exact inputs, so bit-identical."""
+    rows, d = 40, 256
+    L = synth.stored_layer(25, rows, d, 4, 128, exact=True)
+    zeros = L.zeros.copy()
+    zeros[3, 0], zeros[7, 1], zeros[20, 0] = 3000, -2500, 1001
+    L = synth.StoredLayer(L.codes, L.scales, zeros, None, 128)
+    x = synth.inference_x(26, m, d, "f16", exact=True)
+    y = _gpu(L, x, "f16", d)
+    assert np.array_equal(y.astype(np.float64), _oracle(L, synth.to_f64(x, "f16"), d))
+
+
 @pytest.mark.parametrize("rows,m", [(8200, 2), (4100, 1), (4100, 8), (8193, 4)])
 def test_rows_per_wave_variants_exact(rows, m):
     """Row counts that select four, two and one weight rows per wave, each with a ragged last wave."""
