@@ -233,75 +233,97 @@ typedef _Float16 half4_t __attribute__((ext_vector_type(4)));
 // k = 4 (l / 16) + 0..3; the k slots of lane group c = l / 16 map to the 32 columns c of the unit in
 // the order (0,4,1,5), (2,6,3,7) of each word, which the decoded pairs and the permuted inputs share.
 // The KS partial tiles are summed in LDS in wave order.
-template <int KS>
+template <int KS, int NT>
 __global__ __launch_bounds__(64 * KS) void dq_mfma_kernel(DqArgs a) {
-  __shared__ floatx4 part[KS][64];
+  __shared__ floatx4 part[KS][NT][64];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int jl = lane & 15, c = lane >> 4;
-  const int64_t j0 = (int64_t)blockIdx.x * 16;
-  const int64_t row = min(j0 + jl, a.rows - 1);
+  // NT tiles of 16 weight rows share each unit's inputs (A operand) and its sum of x
+  const int64_t j0 = (int64_t)blockIdx.x * 16 * NT;
+  const u32x4* prow[NT];
+  const float* srow[NT];
+  const int32_t* zrow[NT];
   const int64_t nw = a.d >> 3;
-  const u32x4* prow = reinterpret_cast<const u32x4*>(a.packed + row * nw);
-  const float* srow = a.scales + row * a.ngroups;
-  const int32_t* zrow = a.zeros + row * a.ngroups;
+#pragma unroll
+  for (int t = 0; t < NT; ++t) {
+    const int64_t row = min(j0 + 16 * t + jl, a.rows - 1);
+    prow[t] = reinterpret_cast<const u32x4*>(a.packed + row * nw);
+    srow[t] = a.scales + row * a.ngroups;
+    zrow[t] = a.zeros + row * a.ngroups;
+  }
   const bool xval = jl < a.m;
   const u32x4* xr = reinterpret_cast<const u32x4*>(static_cast<const _Float16*>(a.x) + (int64_t)min(jl, a.m - 1) * a.ldx);
   const uint32_t units = (uint32_t)(a.d >> 7);
   const half4_t ones = {(_Float16)1, (_Float16)1, (_Float16)1, (_Float16)1};
   const half2_t m1024 = as_h2(0xE400E400u), r16 = as_h2(0x2C002C00u), m64 = as_h2(0xD400D400u);
 
-  floatx4 acc = {0.f, 0.f, 0.f, 0.f};
-  // A 128-column unit u: this lane's codes are words 16u + 4c .. +3 of its row and its inputs
-  // columns 128u + 32c .. +31 of input row l % 16; one scale and zero per unit.
+  floatx4 acc[NT];
+#pragma unroll
+  for (int t = 0; t < NT; ++t) acc[t] = floatx4{0.f, 0.f, 0.f, 0.f};
+  // A 128-column unit u: this lane's codes are words 16u + 4c .. +3 of its rows and its inputs
+  // columns 128u + 32c .. +31 of input row l % 16; one scale and zero per unit and row.
   struct Codes {
-    u32x4 w;
-    float sc;
-    int32_t z;
+    u32x4 w[NT];
+    float sc[NT];
+    int32_t z[NT];
   };
   struct Inputs {
     u32x4 x[4];
   };
-  auto load_codes = [&](uint32_t u, Codes& t) {
-    t.w = __builtin_nontemporal_load(prow + 4 * (int64_t)u + c);
+  auto load_codes = [&](uint32_t u, Codes& cd) {
     const uint32_t grp = a.cpg ? u / a.cpg : 0u;
-    t.sc = srow[grp];
-    t.z = zrow[grp];
-  };
-  auto load_inputs = [&](uint32_t u, Inputs& t) {
 #pragma unroll
-    for (int q = 0; q < 4; ++q) t.x[q] = xval ? xr[16 * (int64_t)u + 4 * c + q] : u32x4{0u, 0u, 0u, 0u};
+    for (int t = 0; t < NT; ++t) {
+      cd.w[t] = __builtin_nontemporal_load(prow[t] + 4 * (int64_t)u + c);
+      cd.sc[t] = srow[t][grp];
+      cd.z[t] = zrow[t][grp];
+    }
+  };
+  auto load_inputs = [&](uint32_t u, Inputs& in) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) in.x[q] = xval ? xr[16 * (int64_t)u + 4 * c + q] : u32x4{0u, 0u, 0u, 0u};
   };
   auto unit = [&](const Codes& cd, const Inputs& in) {
-    floatx4 T = {0.f, 0.f, 0.f, 0.f}, S = {0.f, 0.f, 0.f, 0.f};
+    floatx4 T[NT], S = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int t = 0; t < NT; ++t) T[t] = floatx4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       half2_t p[4];
       pair_inputs(in.x[q], p);
-      const uint32_t wd = cd.w[q], w8 = wd >> 8;
-      const half2_t q0 = as_h2(and_or(wd, 0x000F000Fu, 0x64006400u)) + m1024;
-      const half2_t q1 = as_h2(and_or(wd, 0x00F000F0u, 0x64006400u)) * r16 + m64;
-      const half2_t q2 = as_h2(and_or(w8, 0x000F000Fu, 0x64006400u)) + m1024;
-      const half2_t q3 = as_h2(and_or(w8, 0x00F000F0u, 0x64006400u)) * r16 + m64;
       const half4_t a0 = __builtin_shufflevector(p[0], p[1], 0, 1, 2, 3);
       const half4_t a1 = __builtin_shufflevector(p[2], p[3], 0, 1, 2, 3);
-      T = __builtin_amdgcn_mfma_f32_16x16x16f16(a0, __builtin_shufflevector(q0, q1, 0, 1, 2, 3), T, 0, 0, 0);
       S = __builtin_amdgcn_mfma_f32_16x16x16f16(a0, ones, S, 0, 0, 0);
-      T = __builtin_amdgcn_mfma_f32_16x16x16f16(a1, __builtin_shufflevector(q2, q3, 0, 1, 2, 3), T, 0, 0, 0);
       S = __builtin_amdgcn_mfma_f32_16x16x16f16(a1, ones, S, 0, 0, 0);
-    }
-    const float z = (float)cd.z;
 #pragma unroll
-    for (int r = 0; r < 4; ++r) acc[r] = __builtin_fmaf(cd.sc, __builtin_fmaf(-z, S[r], T[r]), acc[r]);
+      for (int t = 0; t < NT; ++t) {
+        const uint32_t wd = cd.w[t][q], w8 = wd >> 8;
+        const half2_t q0 = as_h2(and_or(wd, 0x000F000Fu, 0x64006400u)) + m1024;
+        const half2_t q1 = as_h2(and_or(wd, 0x00F000F0u, 0x64006400u)) * r16 + m64;
+        const half2_t q2 = as_h2(and_or(w8, 0x000F000Fu, 0x64006400u)) + m1024;
+        const half2_t q3 = as_h2(and_or(w8, 0x00F000F0u, 0x64006400u)) * r16 + m64;
+        T[t] = __builtin_amdgcn_mfma_f32_16x16x16f16(a0, __builtin_shufflevector(q0, q1, 0, 1, 2, 3), T[t], 0, 0, 0);
+        T[t] = __builtin_amdgcn_mfma_f32_16x16x16f16(a1, __builtin_shufflevector(q2, q3, 0, 1, 2, 3), T[t], 0, 0, 0);
+      }
+    }
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+      const float z = (float)cd.z[t];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) acc[t][r] = __builtin_fmaf(cd.sc[t], __builtin_fmaf(-z, S[r], T[t][r]), acc[t][r]);
+    }
   };
 
-  // Unit pairs w, w + KS, ... The codes of the next two pairs and the inputs of the next one are in
-  // flight while a pair is computed (the inputs come from L2, the codes from HBM).
+  // Unit pairs w, w + KS, ... The codes of the next two pairs (one with two tiles, for registers) and
+  // the inputs of the next one are in flight while a pair is computed (the inputs come from L2, the
+  // codes from HBM).
+  constexpr bool kDeep = NT == 1;
   const uint32_t pairs = (units + 1) / 2;
-  Codes c1[2], c2[2];
+  Codes c1[2], c2[kDeep ? 2 : 1];
   Inputs x1[2];
-  auto fetch_codes = [&](uint32_t pr, Codes (&t)[2]) {
-    load_codes(2 * pr, t[0]);
-    if (2 * pr + 1 < units) load_codes(2 * pr + 1, t[1]);
+  auto fetch_codes = [&](uint32_t pr, Codes* cd) {
+    load_codes(2 * pr, cd[0]);
+    if (2 * pr + 1 < units) load_codes(2 * pr + 1, cd[1]);
   };
   auto fetch_inputs = [&](uint32_t pr) {
     load_inputs(2 * pr, x1[0]);
@@ -312,32 +334,43 @@ __global__ __launch_bounds__(64 * KS) void dq_mfma_kernel(DqArgs a) {
     fetch_codes(p0, c1);
     fetch_inputs(p0);
   }
-  if (p0 + KS < pairs) fetch_codes(p0 + KS, c2);
+  if constexpr (kDeep) {
+    if (p0 + KS < pairs) fetch_codes(p0 + KS, c2);
+  }
   for (uint32_t pr = p0; pr < pairs; pr += KS) {
     const Codes k0 = c1[0], k1 = c1[1];
     const Inputs i0 = x1[0], i1 = x1[1];
-    c1[0] = c2[0];
-    c1[1] = c2[1];
-    if (pr + 2 * KS < pairs) fetch_codes(pr + 2 * KS, c2);
+    if constexpr (kDeep) {
+      c1[0] = c2[0];
+      c1[1] = c2[1];
+      if (pr + 2 * KS < pairs) fetch_codes(pr + 2 * KS, c2);
+    } else {
+      if (pr + KS < pairs) fetch_codes(pr + KS, c1);
+    }
     if (pr + KS < pairs) fetch_inputs(pr + KS);
     unit(k0, i0);
     if (2 * pr + 1 < units) unit(k1, i1);
   }
 
-  part[wave][lane] = acc;
+#pragma unroll
+  for (int t = 0; t < NT; ++t) part[wave][t][lane] = acc[t];
   __syncthreads();
   if (wave == 0) {
-    floatx4 t = part[0][lane];
 #pragma unroll
-    for (int w = 1; w < KS; ++w) {
-      const floatx4 o = part[w][lane];
+    for (int t = 0; t < NT; ++t) {
+      floatx4 sum = part[0][t][lane];
 #pragma unroll
-      for (int r = 0; r < 4; ++r) t[r] += o[r];
-    }
+      for (int w = 1; w < KS; ++w) {
+        const floatx4 o = part[w][t][lane];
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int i = 4 * c + r;
-      if (i < a.m && j0 + jl < a.rows) a.y[(int64_t)i * a.ldy + j0 + jl] = t[r];
+        for (int r = 0; r < 4; ++r) sum[r] += o[r];
+      }
+      const int64_t j = j0 + 16 * t + jl;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int i = 4 * c + r;
+        if (i < a.m && j < a.rows) a.y[(int64_t)i * a.ldy + j] = sum[r];
+      }
     }
   }
 }
@@ -352,8 +385,15 @@ GPTQ_DEV float load_x(const void* x, int64_t idx) {
 // The codes of columns 8 wv .. 8 wv + 7 of one row. Fields: one word of nibbles (bits <= 4) or two
 // words of bytes. Dense stream: the 8 bits-wide codes start at stream bit 8 wv bits and span at most
 // three words (8 bits <= 64 bits from an offset below 32).
+template <bool NIB>
 GPTQ_DEV void codes8(const uint32_t* __restrict__ row, int64_t nwr, int64_t wv, int bits, int dense,
                      uint32_t (&q)[8]) {
+  if (NIB) {
+    const uint32_t w = row[wv];
+#pragma unroll
+    for (int t = 0; t < 8; ++t) q[t] = (w >> (4 * t)) & 15u;
+    return;
+  }
   if (!dense) {
     if (bits <= 4) {
       const uint32_t w = row[wv];
@@ -417,8 +457,9 @@ GPTQ_DEV void load_x8(const void* x, int64_t base, bool vec, float (&v)[8]) {
 
 // Any input type and any column-to-group map. Lane l takes words l, l + 64, ... of R weight rows.
 // With TAB the workgroup's rows' (scale, zero) tables are first copied to LDS, so that each weight
-// reads its group's pair with one LDS load instead of two global gathers.
-template <int XT, int MT, int R, bool TAB>
+// reads its group's pair with one LDS load instead of two global gathers. NIB: nibble fields (the
+// common layout, decoded without the layout tests).
+template <int XT, int MT, int R, bool TAB, bool NIB>
 __global__ __launch_bounds__(256) void dq_general_kernel(DqArgs a) {
   extern __shared__ u32x2 tab[];   // [4 R][ngroups]: scale bits, zero
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -451,7 +492,7 @@ __global__ __launch_bounds__(256) void dq_general_kernel(DqArgs a) {
   for (int64_t wv = lane; wv < nw; wv += 64) {
     uint32_t qc[R][8];
 #pragma unroll
-    for (int r = 0; r < R; ++r) codes8(a.packed + rr[r] * a.nwr, a.nwr, wv, a.bits, a.dense, qc[r]);
+    for (int r = 0; r < R; ++r) codes8<NIB>(a.packed + rr[r] * a.nwr, a.nwr, wv, a.bits, a.dense, qc[r]);
     int32_t gk[8];
     if (a.gidx && a.gvec) {
       const u32x4 g0 = *reinterpret_cast<const u32x4*>(a.gidx + 8 * wv);
@@ -521,10 +562,20 @@ template <int XT, int MT, int R>
 hipError_t launch_general(const DqArgs& a, hipStream_t s) {
   const int64_t wgs = (a.rows + 4 * R - 1) / (4 * R);
   const int64_t tab_bytes = 4 * R * a.ngroups * (int64_t)sizeof(u32x2);
-  if (tab_bytes <= 65536)
-    hipLaunchKernelGGL((dq_general_kernel<XT, MT, R, true>), dim3((unsigned)wgs), dim3(256), (size_t)tab_bytes, s, a);
-  else
-    hipLaunchKernelGGL((dq_general_kernel<XT, MT, R, false>), dim3((unsigned)wgs), dim3(256), 0, s, a);
+  const bool nib = !a.dense && a.bits <= 4;
+  if (tab_bytes <= 65536) {
+    if (nib)
+      hipLaunchKernelGGL((dq_general_kernel<XT, MT, R, true, true>), dim3((unsigned)wgs), dim3(256), (size_t)tab_bytes,
+                         s, a);
+    else
+      hipLaunchKernelGGL((dq_general_kernel<XT, MT, R, true, false>), dim3((unsigned)wgs), dim3(256),
+                         (size_t)tab_bytes, s, a);
+  } else {
+    if (nib)
+      hipLaunchKernelGGL((dq_general_kernel<XT, MT, R, false, true>), dim3((unsigned)wgs), dim3(256), 0, s, a);
+    else
+      hipLaunchKernelGGL((dq_general_kernel<XT, MT, R, false, false>), dim3((unsigned)wgs), dim3(256), 0, s, a);
+  }
   return hipGetLastError();
 }
 
@@ -596,13 +647,12 @@ hipError_t dequant_gemm(const void* x, int dtype, int64_t m, int64_t ldx, const 
     if (mfma && a.m >= 3) {
       // units per group; waves per workgroup so that about 12 waves per CU are in flight
       a.cpg = g >= d ? 0u : (uint32_t)(g / 128);
-      const int64_t wgs = (rows + 15) / 16;
-      if (wgs >= 768) {
-        hipLaunchKernelGGL(dq_mfma_kernel<4>, dim3((unsigned)wgs), dim3(256), 0, s, a);
-      } else if (wgs >= 384) {
-        hipLaunchKernelGGL(dq_mfma_kernel<8>, dim3((unsigned)wgs), dim3(512), 0, s, a);
+      const int64_t tiles = (rows + 15) / 16;
+      if (tiles >= 768) {
+        // two 16-row tiles per wave share the inputs; 8 waves split the columns
+        hipLaunchKernelGGL((dq_mfma_kernel<8, 2>), dim3((unsigned)((tiles + 1) / 2)), dim3(512), 0, s, a);
       } else {
-        hipLaunchKernelGGL(dq_mfma_kernel<16>, dim3((unsigned)wgs), dim3(1024), 0, s, a);
+        hipLaunchKernelGGL((dq_mfma_kernel<8, 1>), dim3((unsigned)tiles), dim3(512), 0, s, a);
       }
       e = hipGetLastError();
     } else {
