@@ -202,11 +202,14 @@ __global__ __launch_bounds__(256) void quant_block_kernel(QArgs a) {
           a.zeros[row * a.ngroups + gi] = (int32_t)z;
         }
       }
+      // q = clamp(rint(w / s) + z, 0, maxq) and the value s (q - z). On the chain: q - z is
+      // rint(w / s) clamped to [-z, maxq - z] (exact in fp32: small integers), and w - s (q - z) is
+      // one fused multiply-add.
       const float wk = row_bcast<0>(w[c]);
       const float x = div_rn(wk, s, rs);
-      const float q = fminf(fmaxf(rintf(x) + z, 0.0f), a.maxq);
-      const float dq = s * (q - z);
-      float e = (wk - dq) * iv[c];
+      const float qd = __builtin_amdgcn_fmed3f(rintf(x), -z, a.maxq - z);
+      const float q = qd + z;
+      float e = __builtin_fmaf(-s, qd, wk) * iv[c];
       if (CHECKS) e = (k < nc) ? e : 0.0f;
       loss = __builtin_fmaf(e, e, loss);
 #pragma unroll
