@@ -154,10 +154,8 @@ hipError_t quantize(const void* W, int w_dtype, int64_t rows, int64_t d, int64_t
 hipError_t pack(const uint8_t* codes, int64_t rows, int64_t d, int bits, int32_t* packed, hipStream_t s);
 hipError_t pack_dense(const uint8_t* codes, int64_t rows, int64_t d, int bits, int32_t* packed, hipStream_t s);
 
-// y = x W^T from the packed nibble codes, scales, zeros and column groups (see dequant.hip).
-// g is the group width (>= 1); gidx may be null (column k in group k / g).
-bool dequant_fast_path(const void* x, int dtype, int64_t ldx, const int32_t* packed, const int32_t* gidx, int64_t d,
-                       int64_t g);
+// y = x W^T from the packed codes (fields or dense stream), scales, zeros and column groups (see
+// dequant.hip). g is the group width (>= 1); gidx may be null (column k in group k / g).
 hipError_t dequant_gemm(const void* x, int dtype, int64_t m, int64_t ldx, const int32_t* packed, int bits, int dense,
                         const float* scales, const int32_t* zeros, const int32_t* gidx, int64_t rows, int64_t d,
                         int64_t g, float* y, int64_t ldy, hipStream_t s);

@@ -599,8 +599,6 @@ hipError_t dispatch(const DqArgs& a, int dtype, bool fast, int R, hipStream_t s)
   return dispatch_general<BF16, MT>(a, R, s);
 }
 
-}  // namespace
-
 // The matrix-core kernel: fp16 inputs, groups of whole 128-column units, aligned rows.
 bool dequant_mfma_path(const void* x, int dtype, int64_t ldx, const int32_t* packed, const int32_t* gidx, int64_t d,
                        int64_t g) {
@@ -613,6 +611,8 @@ bool dequant_fast_path(const void* x, int dtype, int64_t ldx, const int32_t* pac
   return dtype == F16 && !gidx && d % 32 == 0 && (g >= d || g % 32 == 0) && ldx % 8 == 0 &&
          reinterpret_cast<uintptr_t>(x) % 16 == 0 && reinterpret_cast<uintptr_t>(packed) % 16 == 0;
 }
+
+}  // namespace
 
 hipError_t dequant_gemm(const void* x, int dtype, int64_t m, int64_t ldx, const int32_t* packed, int bits, int dense,
                         const float* scales, const int32_t* zeros, const int32_t* gidx, int64_t rows, int64_t d,
