@@ -202,3 +202,17 @@ def test_workspace_sizes():
     # the Hessian workspace is optional: zero when the tiles alone fill the device
     assert lib.gptq_workspace_bytes(0, 262144, 49152, None) == 0
     assert lib.gptq_workspace_bytes(0, 262144, 4096, None) > 0
+
+
+def test_binding_fails_loudly_without_the_library():
+    """No fallback: with the shared library missing, the first call raises ImportError (run in a fresh
+    interpreter whose package sees a library path that does not exist)."""
+    code = ("import post_weight_quantization_20_amd._lib as L\n"
+            "L.LIB_PATH = L.LIB_PATH + '.absent'\n"
+            "L._lib = None\n"
+            "try:\n"
+            "    L.lib()\n"
+            "except ImportError as e:\n"
+            "    print('raised', 'build' in str(e))\n")
+    r = subprocess.run(["python3", "-c", code], capture_output=True, text=True, cwd=ROOT)
+    assert r.stdout.strip() == "raised True", r.stdout + r.stderr

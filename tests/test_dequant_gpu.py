@@ -244,3 +244,25 @@ def test_benchmark_layers_full_size(name, m):
         else:
             assert np.all(np.abs(y - want) <= _bound(x64, Ls, d))
         del packed, L
+
+
+def test_three_bit_layer_dense_end_to_end():
+    """A 3-bit layer through the solver on the GPU, stored as a dense bit stream (3 bits per code)
+    and multiplied straight from it, against the oracle on the same stored outputs."""
+    torch = torch_cuda()
+    import post_weight_quantization_20_amd as g
+    case = synth.make_case("dq_dense", seed=27, rows=80, d=384, n=1500, bits=3, group_size=128, block_size=128,
+                           act_order=True)
+    W, chunks, out = gpu_layer(case)
+    packed = g.gptq_pack_dense(torch.from_numpy(out["codes"]).cuda(), 3)
+    assert np.array_equal(packed.cpu().numpy(), ref.pack_dense(out["codes"], 3))
+    x = synth.inference_x(28, 4, 384, "f16")
+    y = g.gptq_dequant_gemm(torch.from_numpy(x).cuda(), packed, torch.from_numpy(out["scales"]).cuda(),
+                            torch.from_numpy(out["zeros"]).cuda(), 384, 128,
+                            g_idx=torch.from_numpy(out["g_idx"]).cuda(), bits=3, dense=True)
+    torch.cuda.synchronize()
+    x64 = synth.to_f64(x, "f16")
+    want = ref.dequant_matmul(x64, ref.pack_dense(out["codes"], 3), out["scales"], out["zeros"], out["g_idx"], 384,
+                              3, True)
+    L = synth.StoredLayer(out["codes"], out["scales"], out["zeros"], out["g_idx"], 128)
+    assert np.all(np.abs(y.cpu().numpy().astype(np.float64) - want) <= _bound(x64, L, 384))
