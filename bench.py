@@ -50,6 +50,9 @@ def parse():
     ap.add_argument("--dequant", default=None, choices=["fc2", "q_proj", "down_proj"],
                     help="measure gptq_dequant_gemm on a stored layer of this workload's shape instead")
     ap.add_argument("--batch", type=int, default=1, help="input rows for --dequant")
+    ap.add_argument("--ordered", action="store_true",
+                    help="--dequant of an act-order layer: codes packed in processing order, inputs gathered by "
+                         "the same order in every call (gptq_pack_ordered, gptq_permute_columns)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run one plain 1 GiB device-to-device copy (a known-size reference for HBM counters)")
     return ap.parse_args()
@@ -179,18 +182,25 @@ def bench_dequant(args):
           flush=True)
     L = synth.stored_layer(400, rows, d, bits, gs, act_order=act)
     x = synth.inference_x(401, m, d, "f16")
+    ordered = bool(args.ordered and act)
     codes = torch.from_numpy(L.codes).to(dev)
-    packed = g.gptq_pack(codes, bits)
+    order = torch.from_numpy(np.argsort(L.g_idx, kind="stable").astype(np.int32)).to(dev) if ordered else None
+    packed = g.gptq_pack_ordered(codes, bits, order) if ordered else g.gptq_pack(codes, bits)
     del codes
     scales = torch.from_numpy(L.scales).to(dev)
     zeros = torch.from_numpy(L.zeros).to(dev)
-    gidx = torch.from_numpy(L.g_idx).to(dev) if act else None
+    gidx = torch.from_numpy(L.g_idx).to(dev) if (act and not ordered) else None
     xd = torch.from_numpy(x).to(dev)
+    xp = torch.empty_like(xd)
     y = torch.empty((m, rows), dtype=torch.float32, device=dev)
     stream = torch.cuda.current_stream()
 
     def call():
-        g.gptq_dequant_gemm(xd, packed, scales, zeros, d, gs, g_idx=gidx, bits=bits, y=y)
+        if ordered:
+            g.gptq_permute_columns(xd, order, out=xp)
+            g.gptq_dequant_gemm(xp, packed, scales, zeros, d, gs, bits=bits, y=y)
+        else:
+            g.gptq_dequant_gemm(xd, packed, scales, zeros, d, gs, g_idx=gidx, bits=bits, y=y)
 
     for _ in range(args.warmup):
         call()
@@ -221,7 +231,8 @@ def bench_dequant(args):
         "dtype": "f16",
         "data": "synthetic (seeded random stored layer; no trained weights)",
         "config": {"workload": f"dequant {args.dequant}: W {rows}x{d} {bits}-bit nibble codes, "
-                               f"g{gs if gs > 0 else d}{' act-order g_idx' if act else ''}, x {m}x{d} fp16",
+                               f"g{gs if gs > 0 else d}{' act-order g_idx' if act else ''}"
+                               f"{' stored in processing order' if ordered else ''}, x {m}x{d} fp16",
                    "rows": rows, "d": d, "batch": m, "bits": bits, "group_size": gs, "act_order": int(act)},
         "roofline": {"kernel": "gptq_dequant_gemm", "bound": "hbm", "achieved": round(achieved, 1),
                      "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4),

@@ -11,6 +11,8 @@
  *   gptq_quantize_layer      the column loop with lazy block updates; codes, scales, zeros, loss
  *   gptq_pack                eight 4-bit codes per 32-bit word (four 8-bit ones)
  *   gptq_pack_dense          the codes as one dense bit stream per row
+ *   gptq_pack_ordered        the codes in a column order (act-order layers stored in processing order)
+ *   gptq_permute_columns     inputs gathered by the same order
  *
  * and one call that uses the stored layer:
  *
@@ -196,6 +198,34 @@ gptq_status_t gptq_pack(const uint8_t *codes, int64_t rows, int64_t d, int32_t b
  */
 gptq_status_t gptq_pack_dense(const uint8_t *codes, int64_t rows, int64_t d, int32_t bits, int32_t *packed,
                               void *stream);
+
+/*
+ * Packs the codes in a given column order, in gptq_pack's field layout: column j of the output is
+ * column order[j] of the codes. With order = gptq_factor's perm (the act-order processing order), a
+ * group's columns are contiguous again (group j / g), so gptq_dequant_gemm can take its fast kernels
+ * with g_idx = NULL on inputs gathered by the same order (gptq_permute_columns). The product is the
+ * same sum taken in another order. This is the act-order trade-off of the tools page ("Optional
+ * refinements"; What Is GPTQ, kernel speed) paid once at storage time instead of in every product.
+ *
+ *   codes   device uint8[rows * d], original column order (gptq_quantize_layer's codes).
+ *   rows    >= 0; d >= 8 and a multiple of 8; bits in 1..8.
+ *   order   device int32[d], a permutation of 0..d-1 (values outside [0, d) are clamped into it).
+ *   packed  device int32[rows * d * f / 32], output, f = 4 for bits <= 4 and 8 above.
+ */
+gptq_status_t gptq_pack_ordered(const uint8_t *codes, int64_t rows, int64_t d, int32_t bits, const int32_t *order,
+                                int32_t *packed, void *stream);
+
+/*
+ * Gathers the columns of a row-major matrix: out[i][j] = in[i][order[j]] (the layer inputs in the
+ * order of codes packed by gptq_pack_ordered).
+ *
+ *   in      device array [m x ld_in] of dtype (GPTQ_F32, GPTQ_F16 or GPTQ_BF16). Not modified.
+ *   m       rows, >= 0 (0: nothing is queued); d columns, >= 1; ld_in, ld_out >= d.
+ *   order   device int32[d] (values outside [0, d) are clamped into it).
+ *   out     device array [m x ld_out] of dtype, output; must not overlap `in`.
+ */
+gptq_status_t gptq_permute_columns(const void *in, int32_t dtype, int64_t m, int64_t d, int64_t ld_in,
+                                   const int32_t *order, void *out, int64_t ld_out, void *stream);
 
 /*
  * The stored layer at inference: y = x W^T for a few rows of inputs x, with W expanded from the packed

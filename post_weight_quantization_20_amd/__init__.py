@@ -28,6 +28,8 @@ from .solver import (  # noqa: F401
     gptq_hessian_accumulate,
     gptq_pack,
     gptq_pack_dense,
+    gptq_pack_ordered,
+    gptq_permute_columns,
     packed_words,
     gptq_quantize_layer,
     gptq_workspace_bytes,

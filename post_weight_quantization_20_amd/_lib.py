@@ -39,6 +39,9 @@ SIGNATURES = {
                                       c_void_p, c_size_t, c_void_p]),
     "gptq_pack": (c_int32, [c_void_p, c_int64, c_int64, c_int32, c_void_p, c_void_p]),
     "gptq_pack_dense": (c_int32, [c_void_p, c_int64, c_int64, c_int32, c_void_p, c_void_p]),
+    "gptq_pack_ordered": (c_int32, [c_void_p, c_int64, c_int64, c_int32, c_void_p, c_void_p, c_void_p]),
+    "gptq_permute_columns": (c_int32, [c_void_p, c_int32, c_int64, c_int64, c_int64, c_void_p, c_void_p, c_int64,
+                                       c_void_p]),
     "gptq_dequant_gemm": (c_int32, [c_void_p, c_int32, c_int64, c_int64, c_void_p, c_int32, c_int32, c_void_p,
                                     c_void_p, c_void_p, c_int64, c_int64, c_int32, c_void_p, c_int64, c_void_p]),
     "gptq_workspace_bytes": (c_size_t, [c_int32, c_int64, c_int64, ctypes.POINTER(gptq_params_t)]),

@@ -138,6 +138,27 @@ gptq_status_t gptq_pack_dense(const uint8_t* codes, int64_t rows, int64_t d, int
   return hip_status(gptq::pack_dense(codes, rows, d, bits, packed, static_cast<hipStream_t>(stream)));
 }
 
+gptq_status_t gptq_pack_ordered(const uint8_t* codes, int64_t rows, int64_t d, int32_t bits, const int32_t* order,
+                                int32_t* packed, void* stream) {
+  if (rows < 0 || rows > kMaxDim || d < 8 || d > kMaxDim || d % 8 != 0 || bits < 1 || bits > 8) return GPTQ_EINVAL;
+  if (rows == 0) return GPTQ_OK;
+  if (!codes || !order || !packed) return GPTQ_EINVAL;
+  return hip_status(gptq::pack_ordered(codes, rows, d, order, bits, packed, static_cast<hipStream_t>(stream)));
+}
+
+gptq_status_t gptq_permute_columns(const void* in, int32_t dtype, int64_t m, int64_t d, int64_t ld_in,
+                                   const int32_t* order, void* out, int64_t ld_out, void* stream) {
+  if (m < 0 || m > kMaxDim || d < 1 || d > kMaxDim || !dtype_ok(dtype) || ld_in < d || ld_out < d) return GPTQ_EINVAL;
+  if (m == 0) return GPTQ_OK;
+  if (!in || !order || !out) return GPTQ_EINVAL;
+  const int esz = dtype == GPTQ_F32 ? 4 : 2;
+  const char* i0 = static_cast<const char*>(in);
+  const char* o0 = static_cast<const char*>(out);
+  const int64_t in_bytes = ((m - 1) * ld_in + d) * esz, out_bytes = ((m - 1) * ld_out + d) * esz;
+  if (i0 < o0 + out_bytes && o0 < i0 + in_bytes) return GPTQ_EINVAL;   // in place would race
+  return hip_status(gptq::permute_columns(in, m, d, ld_in, order, esz, out, ld_out, static_cast<hipStream_t>(stream)));
+}
+
 gptq_status_t gptq_dequant_gemm(const void* x, int32_t x_dtype, int64_t m, int64_t ld_x, const int32_t* packed,
                                 int32_t bits, int32_t layout, const float* scales, const int32_t* zeros,
                                 const int32_t* g_idx, int64_t rows, int64_t d, int32_t group_size, float* y,

@@ -153,6 +153,11 @@ hipError_t quantize(const void* W, int w_dtype, int64_t rows, int64_t d, int64_t
 // Field layout (nibbles up to 4 bits, bytes above) and the dense bit stream.
 hipError_t pack(const uint8_t* codes, int64_t rows, int64_t d, int bits, int32_t* packed, hipStream_t s);
 hipError_t pack_dense(const uint8_t* codes, int64_t rows, int64_t d, int bits, int32_t* packed, hipStream_t s);
+// Field layout of the codes taken in a column order; a column gather of a row-major matrix.
+hipError_t pack_ordered(const uint8_t* codes, int64_t rows, int64_t d, const int32_t* order, int bits, int32_t* packed,
+                        hipStream_t s);
+hipError_t permute_columns(const void* in, int64_t m, int64_t d, int64_t ld_in, const int32_t* order, int esz,
+                           void* out, int64_t ld_out, hipStream_t s);
 
 // y = x W^T from the packed codes (fields or dense stream), scales, zeros and column groups (see
 // dequant.hip). g is the group width (>= 1); gidx may be null (column k in group k / g).

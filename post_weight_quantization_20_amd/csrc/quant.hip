@@ -447,6 +447,42 @@ __global__ __launch_bounds__(256) void pack_dense_kernel(const uint8_t* __restri
   }
 }
 
+// Codes in processing order: column j of the output is column order[j] of the codes, packed in the
+// field layout (nibbles up to 4 bits, bytes above). One thread per output word.
+__global__ __launch_bounds__(256) void pack_ordered_kernel(const uint8_t* __restrict__ codes, int64_t rows, int64_t d,
+                                                           const int32_t* __restrict__ order, int bits,
+                                                           int32_t* __restrict__ packed) {
+  const int f = bits <= 4 ? 4 : 8, per = 32 / f;
+  const uint32_t mask = (1u << f) - 1u;
+  const int64_t words = d / per;
+  const int64_t total = rows * words;
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < total; i += (int64_t)gridDim.x * 256) {
+    const int64_t r = i / words, k = i % words;
+    const uint8_t* p = codes + r * d;
+    uint32_t out = 0;
+    for (int t = 0; t < per; ++t) {
+      const int64_t c = min(max((int64_t)order[per * k + t], (int64_t)0), d - 1);   // clamped into the row
+      out |= ((uint32_t)p[c] & mask) << (f * t);
+    }
+    packed[i] = (int32_t)out;
+  }
+}
+
+// Columns of a row-major matrix gathered by an order: out[i][j] = in[i][order[j]], elements of esz
+// bytes (2 or 4).
+__global__ __launch_bounds__(256) void permute_columns_kernel(const void* __restrict__ in, int64_t m, int64_t d,
+                                                              int64_t ld_in, const int32_t* __restrict__ order,
+                                                              int esz, void* __restrict__ out, int64_t ld_out) {
+  const int64_t total = m * d;
+  for (int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x; e < total; e += (int64_t)gridDim.x * 256) {
+    const int64_t i = e / d, j = e % d;
+    const int64_t c = min(max((int64_t)order[j], (int64_t)0), d - 1);   // clamped into the row
+    const int64_t src = i * ld_in + c, dst = i * ld_out + j;
+    if (esz == 2) static_cast<uint16_t*>(out)[dst] = static_cast<const uint16_t*>(in)[src];
+    else static_cast<uint32_t*>(out)[dst] = static_cast<const uint32_t*>(in)[src];
+  }
+}
+
 // packed[r][k] = sum_t (codes[r][8k + t] & 15) << 4t.
 __global__ __launch_bounds__(256) void pack_kernel(const uint8_t* __restrict__ codes, int64_t rows, int64_t d,
                                                    int32_t* __restrict__ packed, int vec) {
@@ -627,6 +663,24 @@ hipError_t pack(const uint8_t* codes, int64_t rows, int64_t d, int bits, int32_t
   const unsigned grid = (unsigned)std::min<int64_t>((total + 255) / 256, 65536);
   const int vec = ((uintptr_t)codes % 8 == 0);
   hipLaunchKernelGGL(pack_kernel, dim3(grid), dim3(256), 0, s, codes, rows, d, packed, vec);
+  return hipGetLastError();
+}
+
+hipError_t pack_ordered(const uint8_t* codes, int64_t rows, int64_t d, const int32_t* order, int bits, int32_t* packed,
+                        hipStream_t s) {
+  const int64_t total = rows * (d / (bits <= 4 ? 8 : 4));
+  if (total <= 0) return hipSuccess;
+  const unsigned grid = (unsigned)std::min<int64_t>((total + 255) / 256, 65536);
+  hipLaunchKernelGGL(pack_ordered_kernel, dim3(grid), dim3(256), 0, s, codes, rows, d, order, bits, packed);
+  return hipGetLastError();
+}
+
+hipError_t permute_columns(const void* in, int64_t m, int64_t d, int64_t ld_in, const int32_t* order, int esz,
+                           void* out, int64_t ld_out, hipStream_t s) {
+  const int64_t total = m * d;
+  if (total <= 0) return hipSuccess;
+  const unsigned grid = (unsigned)std::min<int64_t>((total + 255) / 256, 65536);
+  hipLaunchKernelGGL(permute_columns_kernel, dim3(grid), dim3(256), 0, s, in, m, d, ld_in, order, esz, out, ld_out);
   return hipGetLastError();
 }
 

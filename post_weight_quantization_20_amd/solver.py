@@ -194,6 +194,38 @@ def gptq_pack_dense(codes: torch.Tensor, bits: int, packed: Optional[torch.Tenso
     return packed
 
 
+def gptq_pack_ordered(codes: torch.Tensor, bits: int, order: torch.Tensor, packed: Optional[torch.Tensor] = None,
+                      stream=None) -> torch.Tensor:
+    """gptq_pack's layout with column j taken from codes[:, order[j]] (act-order layers stored in
+    processing order, so that groups are contiguous)."""
+    _need_cuda(codes, order, packed)
+    rows, d = codes.shape
+    if codes.dtype != torch.uint8 or not codes.is_contiguous():
+        raise ValueError("codes must be contiguous uint8 [rows, d]")
+    if order.dtype != torch.int32 or order.shape != (d,) or not order.is_contiguous():
+        raise ValueError("order must be contiguous int32 [d]")
+    if packed is None:
+        packed = torch.empty((rows, packed_words(d, bits)), dtype=torch.int32, device=codes.device)
+    _check(_lib.lib().gptq_pack_ordered(_ptr(codes), rows, d, int(bits), _ptr(order), _ptr(packed), _stream(stream)))
+    return packed
+
+
+def gptq_permute_columns(x: torch.Tensor, order: torch.Tensor, out: Optional[torch.Tensor] = None,
+                         stream=None) -> torch.Tensor:
+    """out[:, j] = x[:, order[j]] for a 2-D x with unit column stride."""
+    _need_cuda(x, order, out)
+    if x.dim() != 2 or x.stride(1) != 1 or x.dtype not in _DTYPE:
+        raise ValueError("x must be 2-D with unit column stride, fp32/fp16/bf16")
+    m, d = x.shape
+    if order.dtype != torch.int32 or order.shape != (d,) or not order.is_contiguous():
+        raise ValueError("order must be contiguous int32 [d]")
+    if out is None:
+        out = torch.empty((m, d), dtype=x.dtype, device=x.device)
+    _check(_lib.lib().gptq_permute_columns(_ptr(x), _DTYPE[x.dtype], m, d, x.stride(0), _ptr(order), _ptr(out),
+                                           out.stride(0), _stream(stream)))
+    return out
+
+
 def gptq_dequant_gemm(x: torch.Tensor, packed: torch.Tensor, scales: torch.Tensor, zeros: torch.Tensor,
                       d: int, group_size: int, g_idx: Optional[torch.Tensor] = None, bits: int = 4,
                       y: Optional[torch.Tensor] = None, dense: bool = False, stream=None) -> torch.Tensor:

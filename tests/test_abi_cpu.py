@@ -159,6 +159,22 @@ def test_pack_dense_rejects_bad_arguments():
     assert f(FAKE, 0, 32, 3, FAKE, None) == 0      # no rows: nothing to do
 
 
+def test_pack_ordered_and_permute_reject_bad_arguments():
+    lib = _lib().lib()
+    f = lib.gptq_pack_ordered
+    assert f(FAKE, 4, 12, 4, FAKE, FAKE, None) == -1     # d not a multiple of 8
+    assert f(FAKE, 4, 16, 9, FAKE, FAKE, None) == -1
+    assert f(FAKE, 4, 16, 4, None, FAKE, None) == -1     # no order
+    assert f(FAKE, 0, 16, 4, FAKE, FAKE, None) == 0
+    p = lib.gptq_permute_columns
+    # (in, dtype, m, d, ld_in, order, out, ld_out, stream)
+    assert p(FAKE, 1, 2, 16, 15, FAKE, ctypes.c_void_p(0x100000), 16, None) == -1    # ld_in < d
+    assert p(FAKE, 1, 2, 16, 16, FAKE, ctypes.c_void_p(0x100000), 8, None) == -1     # ld_out < d
+    assert p(FAKE, 7, 2, 16, 16, FAKE, ctypes.c_void_p(0x100000), 16, None) == -1    # dtype
+    assert p(FAKE, 1, 2, 16, 16, FAKE, ctypes.c_void_p(0x1000 + 8), 16, None) == -1  # overlapping output
+    assert p(FAKE, 1, 0, 16, 16, FAKE, FAKE, 16, None) == 0
+
+
 def test_dequant_gemm_rejects_bad_arguments():
     lib = _lib().lib()
     f = lib.gptq_dequant_gemm

@@ -266,3 +266,59 @@ def test_three_bit_layer_dense_end_to_end():
                               3, True)
     L = synth.StoredLayer(out["codes"], out["scales"], out["zeros"], out["g_idx"], 128)
     assert np.all(np.abs(y.cpu().numpy().astype(np.float64) - want) <= _bound(x64, L, 384))
+
+
+# ------------------------------------------------------------------ act-order layers stored in processing order
+
+@pytest.mark.parametrize("xdt,rows,d,m,gs,exact", [("f16", 300, 4096, 1, 128, True), ("f16", 200, 2048, 5, 128, True),
+                                                   ("f16", 100, 1024, 2, 64, False), ("bf16", 40, 512, 3, 32, True)])
+def test_act_order_reordered_product(xdt, rows, d, m, gs, exact):
+    """An act-order layer packed in processing order (groups contiguous) times inputs gathered by the
+    same order equals the oracle's product of the stored layer in its original order: exactly on
+    exact inputs, within the bound otherwise."""
+    torch = torch_cuda()
+    import post_weight_quantization_20_amd as g
+    print(f"[dequant reordered] x {xdt} rows {rows} d {d} m {m} g {gs} exact {exact}", flush=True)
+    L = synth.stored_layer(29, rows, d, 4, gs, act_order=True, exact=exact)
+    order = np.argsort(L.g_idx, kind="stable").astype(np.int32)
+    assert np.array_equal(L.g_idx[order], np.arange(d) // gs)
+    x = synth.inference_x(30, m, d, xdt, exact=exact)
+    od = torch.from_numpy(order).cuda()
+    packed = g.gptq_pack_ordered(torch.from_numpy(L.codes).cuda(), 4, od)
+    assert np.array_equal(packed.cpu().numpy(), ref.pack(L.codes[:, order], 4))
+    xd = dev_tensor(x, xdt)
+    xp = g.gptq_permute_columns(xd, od)
+    torch.cuda.synchronize()
+    xin = x if xdt != "bf16" else x.view(np.uint16)
+    got_xp = xp.cpu().view(torch.int16).numpy().view(np.uint16) if xdt == "bf16" else xp.cpu().numpy()
+    assert np.array_equal(got_xp, xin[:, order])
+    y = g.gptq_dequant_gemm(xp, packed, torch.from_numpy(L.scales).cuda(), torch.from_numpy(L.zeros).cuda(), d, gs)
+    torch.cuda.synchronize()
+    y = y.cpu().numpy().astype(np.float64)
+    x64 = synth.to_f64(x, xdt)
+    want = _oracle(L, x64, d)
+    if exact:
+        assert np.array_equal(y, want)
+    else:
+        assert np.all(np.abs(y - want) <= _bound(x64, L, d))
+
+
+def test_act_order_layer_reordered_end_to_end():
+    """A layer solved with act-order on the GPU, stored in its processing order (the factor's perm)
+    and multiplied on reordered inputs, against the oracle's product of the standard stored layer."""
+    torch = torch_cuda()
+    import post_weight_quantization_20_amd as g
+    case = synth.make_case("dq_ord", seed=31, rows=96, d=512, n=2048, bits=4, group_size=128, block_size=128,
+                           act_order=True)
+    W, chunks, out = gpu_layer(case)
+    od = torch.from_numpy(out["perm"].astype(np.int32)).cuda()
+    packed = g.gptq_pack_ordered(torch.from_numpy(out["codes"]).cuda(), 4, od)
+    x = synth.inference_x(32, 6, 512, "f16")
+    xp = g.gptq_permute_columns(torch.from_numpy(x).cuda(), od)
+    y = g.gptq_dequant_gemm(xp, packed, torch.from_numpy(out["scales"]).cuda(), torch.from_numpy(out["zeros"]).cuda(),
+                            512, 128)
+    torch.cuda.synchronize()
+    x64 = synth.to_f64(x, "f16")
+    want = ref.dequant_matmul(x64, ref.pack(out["codes"], 4), out["scales"], out["zeros"], out["g_idx"], 512)
+    L = synth.StoredLayer(out["codes"], out["scales"], out["zeros"], out["g_idx"], 128)
+    assert np.all(np.abs(y.cpu().numpy().astype(np.float64) - want) <= _bound(x64, L, 512))
