@@ -322,3 +322,23 @@ def test_act_order_layer_reordered_end_to_end():
     want = ref.dequant_matmul(x64, ref.pack(out["codes"], 4), out["scales"], out["zeros"], out["g_idx"], 512)
     L = synth.StoredLayer(out["codes"], out["scales"], out["zeros"], out["g_idx"], 128)
     assert np.all(np.abs(y.cpu().numpy().astype(np.float64) - want) <= _bound(x64, L, 512))
+
+
+@pytest.mark.parametrize("m,act", [(1, False), (5, False), (3, True)])
+def test_deterministic_and_strided_output(m, act):
+    """Two calls give bit-identical results (no atomics; fixed reduction order), and an output with a
+    row pitch wider than rows leaves its padding untouched."""
+    torch = torch_cuda()
+    import post_weight_quantization_20_amd as g
+    rows, d = 1000, 2048
+    L = synth.stored_layer(33, rows, d, 4, 128, act_order=act)
+    x = torch.from_numpy(synth.inference_x(34, m, d, "f16")).cuda()
+    packed = g.gptq_pack(torch.from_numpy(L.codes).cuda(), 4)
+    sc, ze = torch.from_numpy(L.scales).cuda(), torch.from_numpy(L.zeros).cuda()
+    gi = torch.from_numpy(L.g_idx).cuda() if act else None
+    y1 = g.gptq_dequant_gemm(x, packed, sc, ze, d, 128, g_idx=gi)
+    big = torch.full((m, rows + 24), 7.0, dtype=torch.float32, device="cuda")
+    y2 = g.gptq_dequant_gemm(x, packed, sc, ze, d, 128, g_idx=gi, y=big[:, :rows])
+    torch.cuda.synchronize()
+    assert torch.equal(y1, y2)
+    assert torch.all(big[:, rows:] == 7.0)
