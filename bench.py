@@ -259,8 +259,8 @@ def bench_dequant(args):
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
-        print("bench.py measures one GPU only: the solver runs on a single MI355X and this build has no "
-              "multi-GPU path (rows of W are independent, so a layer would shard by rows; see DESIGN.md).",
+        print("bench.py measures one GPU only: the solver runs on a single MI355X and the library has no "
+              "multi-GPU path (rows of W are independent, so a layer would shard by rows).",
               file=sys.stderr)
         sys.exit(2)
     if args.dequant:

@@ -21,7 +21,7 @@ because the pages' sketch computes on float32 tensors and the GPU kernels decide
 Dense algebra uses library primitives: BLAS matrix products and the LAPACK Cholesky routines
 (potrf / potri) that the sketch's cholesky / cholesky_inverse / cholesky(upper) calls name.
 
-Readings taken where the pages are silent, garbled or disagree (each is listed in the design doc):
+Readings taken where the pages are silent, garbled or disagree:
 
 * H is accumulated as the sum over token chunks of 2 X_c^T X_c and normalised by the token count
   n before damping (the sketch's 2 X^T X / n).
