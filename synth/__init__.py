@@ -2,10 +2,14 @@
 
 from .gen import (  # noqa: F401
     CONFIGS,
+    BlockCase,
     LayerCase,
     StoredLayer,
     Workload,
     bf16_bits_to_f64,
+    block_layer_dims,
+    block_weights,
+    block_x,
     case_from_config,
     inference_x,
     make_case,

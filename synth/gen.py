@@ -276,3 +276,49 @@ def inference_x(seed: int, m: int, d: int, dtype: str = "f16", exact: bool = Fal
     rng = _rng(301, seed)
     x = rng.integers(-2, 3, size=(m, d)).astype(np.float64) if exact else rng.standard_normal((m, d))
     return round_to_dtype(x, dtype)
+
+
+# ------------------------------------------------------------------ decoder block
+
+@dataclass(frozen=True)
+class BlockCase:
+    """A synthetic pre-norm decoder block: seven weights (q, k, v, o: hidden x hidden; gate, up:
+    inter x hidden; down: hidden x inter) ~ N(0, w_std^2) and a block input X of seqs * seq_len
+    tokens ~ N(0, 1) with round(outlier_frac * hidden) channels scaled by outlier_scale (the
+    layer configs' attention-input recipe)."""
+    hidden: int
+    heads: int
+    inter: int
+    seqs: int
+    seq_len: int
+    w_std: float = 0.02
+    w_dtype: str = "f16"
+    x_dtype: str = "f16"
+    outlier_frac: float = 0.01
+    outlier_scale: float = 20.0
+
+
+def block_layer_dims(case: BlockCase, i: int) -> Tuple[int, int]:
+    """(rows, d) of layer i in the order q, k, v, o, gate, up, down."""
+    rows = case.inter if i in (4, 5) else case.hidden
+    return rows, (case.inter if i == 6 else case.hidden)
+
+
+def block_weights(case: BlockCase, seed: int) -> List[np.ndarray]:
+    """The seven stored weights, layer i keyed (400, seed, i)."""
+    out = []
+    for i in range(7):
+        rows, d = block_layer_dims(case, i)
+        out.append(round_to_dtype(_rng(400, seed, i).standard_normal((rows, d)) * case.w_std, case.w_dtype))
+    return out
+
+
+def block_x(case: BlockCase, seed: int) -> np.ndarray:
+    """The stored block input [seqs * seq_len, hidden], keyed (401, seed); outlier channels keyed
+    (402, seed)."""
+    n = case.seqs * case.seq_len
+    k = int(round(case.outlier_frac * case.hidden))
+    ch = np.sort(_rng(402, seed).choice(case.hidden, size=k, replace=False))
+    x = _rng(401, seed).standard_normal((n, case.hidden))
+    x[:, ch] *= case.outlier_scale
+    return round_to_dtype(x, case.x_dtype)
