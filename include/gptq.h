@@ -266,6 +266,68 @@ gptq_status_t gptq_dequant_gemm(const void *x, int32_t x_dtype, int64_t m, int64
                                 int64_t ld_y, void *stream);
 
 /*
+ * One pre-norm decoder block for gptq_quantize_block. The pages fix the order in which a block's
+ * layers are solved but not the block itself; this one is RMSNorm -> multi-head causal
+ * self-attention (q, k, v, o; no positional rotation) -> residual -> RMSNorm -> SiLU-gated MLP
+ * (gate, up, down) -> residual, with no learned norm weights.
+ */
+typedef struct {
+  int64_t hidden;   /* model width, >= 8; q, k, v, o are hidden x hidden                          */
+  int64_t heads;    /* attention heads, >= 1, dividing hidden                                     */
+  int64_t inter;    /* MLP width, >= 8; gate and up are inter x hidden, down hidden x inter       */
+  int64_t seqs;     /* calibration sequences, >= 1                                                */
+  int64_t seq_len;  /* tokens per sequence, >= 1; attention is causal within each sequence        */
+  double eps;       /* RMSNorm epsilon, >= 0: y = x / sqrt(mean(x^2) + eps) over each token's row  */
+} gptq_block_shape_t;
+
+/* One layer of the block: its weights in, its gptq_quantize_layer outputs out. */
+typedef struct {
+  const void *W;    /* device [rows x d] of w_dtype, row-major with ld = d; not modified          */
+  uint8_t *codes;   /* device uint8[rows x d], original column order                              */
+  float *scales;    /* device float[rows x ngroups]                                               */
+  int32_t *zeros;   /* device int32[rows x ngroups]                                               */
+  int32_t *g_idx;   /* device int32[d]                                                            */
+  int32_t *perm;    /* device int32[d]: the processing order used (shared within a stage)         */
+  double *loss;     /* device double[1]                                                           */
+  int32_t w_dtype;  /* GPTQ_F32, GPTQ_F16 or GPTQ_BF16                                            */
+} gptq_block_layer_t;
+
+/* Workspace bytes for gptq_quantize_block (p->block_size is read); 0 for invalid arguments. */
+size_t gptq_block_workspace_bytes(const gptq_block_shape_t *shape, const gptq_params_t *p);
+
+/*
+ * Quantizes the seven linear layers of one decoder block in the true-sequential order (GPTQ tools
+ * page, "How it works", Step 9; the Technical Guide's "true_sequential" setting):
+ *   stage 0: q, k, v from the Hessian of the attention input RMSNorm(X);
+ *   stage 1: o from the Hessian of the attention output, recomputed through the quantized q, k, v;
+ *   stage 2: gate, up from the MLP input RMSNorm(X + attn o^T), through the quantized o;
+ *   stage 3: down from silu(x gate^T) * (x up^T), through the quantized gate and up.
+ * Each stage forms H = 2 A^T A over all tokens, factors it once (gptq_factor) and runs
+ * gptq_quantize_layer for each of its layers with that factor and order. With true_sequential = 0
+ * every stage input comes from the block with its original weights (the layers are solved from
+ * one unquantized forward pass). Activations are fp32.
+ *
+ *   shape   the block and calibration sizes (n = seqs * seq_len tokens).
+ *   X       device [n x hidden] of x_dtype, token-major, sequence after sequence. Not modified.
+ *   p       the quantization settings of every layer (as gptq_quantize_layer).
+ *   layers  host array of 7 descriptors, in the order q, k, v, o, gate, up, down.
+ *   Y       device float[n x hidden]: the block output through the quantized weights (the input
+ *           of the next block).
+ *   hess    NULL, or a host array of 4 pointers (each NULL or device float[d x d] for that stage's
+ *           input width d): receives each stage's H (upper triangle authoritative).
+ *   work    device workspace of gptq_block_workspace_bytes(shape, p) bytes.
+ *   info    host int64[2]: on GPTQ_ENOTPD the failed stage (0..3) and pivot; otherwise {-1, 0}.
+ *   stream  HIP stream; the call synchronizes it once per stage (to read each factor's status).
+ * Returns GPTQ_EINVAL for bad shapes, pointers or settings, GPTQ_ENOMEM for a short workspace,
+ * GPTQ_ENOTPD (see info) when a stage's damped Hessian is not positive definite, and the statuses
+ * of the calls it makes. Outputs of later stages are undefined after an error.
+ */
+gptq_status_t gptq_quantize_block(const gptq_block_shape_t *shape, const void *X, int32_t x_dtype,
+                                  const gptq_params_t *p, int32_t true_sequential, const gptq_block_layer_t *layers,
+                                  float *Y, float *const *hess, void *work, size_t work_bytes, int64_t *info,
+                                  void *stream);
+
+/*
  * Workspace bytes for a call: kind GPTQ_WS_HESSIAN (a = n_tok of the chunk), GPTQ_WS_FACTOR (a unused)
  * or GPTQ_WS_QUANTIZE (a = rows; p->block_size is read). Returns 0 for invalid arguments.
  */

@@ -5,6 +5,7 @@ Python binding. Build the library with `python -m post_weight_quantization_20_am
 """
 
 from .solver import (  # noqa: F401
+    BLOCK_LAYERS,
     GPTQ_BF16,
     GPTQ_EHIP,
     GPTQ_EINVAL,
@@ -19,10 +20,13 @@ from .solver import (  # noqa: F401
     GPTQ_WS_FACTOR,
     GPTQ_WS_HESSIAN,
     GPTQ_WS_QUANTIZE,
+    BlockResult,
+    BlockShape,
     GPTQError,
     LayerResult,
     Params,
     QuantOutput,
+    gptq_block_workspace_bytes,
     gptq_dequant_gemm,
     gptq_factor,
     gptq_hessian_accumulate,
@@ -31,6 +35,7 @@ from .solver import (  # noqa: F401
     gptq_pack_ordered,
     gptq_permute_columns,
     packed_words,
+    gptq_quantize_block,
     gptq_quantize_layer,
     gptq_workspace_bytes,
     quantize_layer,

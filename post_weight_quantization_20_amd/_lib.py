@@ -28,6 +28,16 @@ class gptq_params_t(ctypes.Structure):
     ]
 
 
+class gptq_block_shape_t(ctypes.Structure):
+    _fields_ = [("hidden", c_int64), ("heads", c_int64), ("inter", c_int64), ("seqs", c_int64), ("seq_len", c_int64),
+                ("eps", c_double)]
+
+
+class gptq_block_layer_t(ctypes.Structure):
+    _fields_ = [("W", c_void_p), ("codes", c_void_p), ("scales", c_void_p), ("zeros", c_void_p), ("g_idx", c_void_p),
+                ("perm", c_void_p), ("loss", c_void_p), ("w_dtype", c_int32)]
+
+
 # name -> (restype, argtypes), mirroring include/gptq.h
 SIGNATURES = {
     "gptq_hessian_accumulate": (c_int32, [c_void_p, c_int64, c_void_p, c_int32, c_int64, c_int64, c_void_p, c_size_t,
@@ -44,6 +54,11 @@ SIGNATURES = {
                                        c_void_p]),
     "gptq_dequant_gemm": (c_int32, [c_void_p, c_int32, c_int64, c_int64, c_void_p, c_int32, c_int32, c_void_p,
                                     c_void_p, c_void_p, c_int64, c_int64, c_int32, c_void_p, c_int64, c_void_p]),
+    "gptq_block_workspace_bytes": (c_size_t, [ctypes.POINTER(gptq_block_shape_t), ctypes.POINTER(gptq_params_t)]),
+    "gptq_quantize_block": (c_int32, [ctypes.POINTER(gptq_block_shape_t), c_void_p, c_int32,
+                                      ctypes.POINTER(gptq_params_t), c_int32, ctypes.POINTER(gptq_block_layer_t),
+                                      c_void_p, ctypes.POINTER(c_void_p), c_void_p, c_size_t,
+                                      ctypes.POINTER(c_int64), c_void_p]),
     "gptq_workspace_bytes": (c_size_t, [c_int32, c_int64, c_int64, ctypes.POINTER(gptq_params_t)]),
     "gptq_status_string": (ctypes.c_char_p, [c_int32]),
 }

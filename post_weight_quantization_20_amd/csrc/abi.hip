@@ -175,4 +175,41 @@ gptq_status_t gptq_dequant_gemm(const void* x, int32_t x_dtype, int64_t m, int64
                                        g_idx, rows, d, g, y, ld_y, static_cast<hipStream_t>(stream)));
 }
 
+namespace {
+
+bool block_shape_ok(const gptq_block_shape_t* sh) {
+  if (!sh) return false;
+  if (sh->hidden < 8 || sh->hidden > kMaxDim || sh->inter < 8 || sh->inter > kMaxDim) return false;
+  if (sh->heads < 1 || sh->hidden % sh->heads != 0) return false;
+  if (sh->seqs < 1 || sh->seq_len < 1 || sh->seq_len > kMaxDim || sh->seqs > kMaxDim / sh->seq_len) return false;
+  return std::isfinite(sh->eps) && sh->eps >= 0.0;
+}
+
+}  // namespace
+
+size_t gptq_block_workspace_bytes(const gptq_block_shape_t* shape, const gptq_params_t* p) {
+  if (!block_shape_ok(shape) || !p || p->block_size < 1 || p->block_size > 128) return 0;
+  return gptq::block_layout(*shape, *p).total;
+}
+
+gptq_status_t gptq_quantize_block(const gptq_block_shape_t* shape, const void* X, int32_t x_dtype,
+                                  const gptq_params_t* p, int32_t true_sequential, const gptq_block_layer_t* layers,
+                                  float* Y, float* const* hess, void* work, size_t work_bytes, int64_t* info,
+                                  void* stream) {
+  if (info) info[0] = -1, info[1] = 0;
+  if (!block_shape_ok(shape) || !X || !dtype_ok(x_dtype) || !layers || !Y || !work || !info) return GPTQ_EINVAL;
+  if (true_sequential != 0 && true_sequential != 1) return GPTQ_EINVAL;
+  gptq_status_t st = check_params(p, std::min(shape->hidden, shape->inter), true);
+  if (st != GPTQ_OK) return st;
+  if ((st = check_params(p, std::max(shape->hidden, shape->inter), true)) != GPTQ_OK) return st;
+  for (int i = 0; i < 7; ++i) {
+    const gptq_block_layer_t& l = layers[i];
+    if (!l.W || !l.codes || !l.scales || !l.zeros || !l.g_idx || !l.perm || !l.loss || !dtype_ok(l.w_dtype))
+      return GPTQ_EINVAL;
+  }
+  if (work_bytes < gptq::block_layout(*shape, *p).total) return GPTQ_ENOMEM;
+  return gptq::quantize_block(*shape, X, x_dtype, *p, true_sequential, layers, Y, hess, static_cast<char*>(work),
+                              info, static_cast<hipStream_t>(stream));
+}
+
 }  // extern "C"

@@ -1,0 +1,318 @@
+// The forward pass a true-sequential block driver needs between quantization steps.
+//
+// GPTQ tools page, "How it works", Step 9: a block is quantized layer by layer, and with "true
+// sequential" ordering the attention projections come first and the inputs of the following layers
+// are recomputed through the layers already quantized. The block here is a pre-norm decoder block
+// (the pages do not fix one): RMSNorm, multi-head causal self-attention, a residual, RMSNorm, and a
+// SiLU-gated MLP. These kernels compute its pieces in fp32:
+//   dequantize_kernel      W[r, k] = s[r, G(k)] (q[r, k] - z[r, G(k)]) as dense fp32
+//   rmsnorm_kernel         y = x / sqrt(mean(x^2) + eps), one workgroup per row
+//   causal_softmax_kernel  row i of S: softmax of scale * S[i, 0..i], zeros after i
+//   silu_mul_kernel        y = g / (1 + exp(-g)) * u
+//   to_f32_kernel          a fp32 copy of fp32 / fp16 / bf16 values
+// Products (x W^T, the attention scores and P V) run on gemm_f32. quantize_block (the body of
+// gptq_quantize_block) strings them together with the library's own Hessian, factor and column-loop
+// entry points.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+
+#include "../../include/gptq.h"
+#include "common.hpp"
+
+namespace gptq {
+namespace {
+
+__global__ __launch_bounds__(256) void dequantize_kernel(const uint8_t* __restrict__ codes, int64_t rows, int64_t d,
+                                                         const float* __restrict__ scales,
+                                                         const int32_t* __restrict__ zeros,
+                                                         const int32_t* __restrict__ gidx, int64_t g,
+                                                         int64_t ngroups, float* __restrict__ W, int64_t ldw) {
+  const int64_t total = rows * d;
+  for (int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x; e < total; e += (int64_t)gridDim.x * 256) {
+    const int64_t r = e / d, k = e - r * d;
+    int64_t G = gidx ? (int64_t)gidx[k] : k / g;
+    G = G < 0 ? 0 : G >= ngroups ? ngroups - 1 : G;   // out-of-range entries are clamped
+    const int32_t q = codes[e];
+    W[r * ldw + k] = scales[r * ngroups + G] * (float)(q - zeros[r * ngroups + G]);
+  }
+}
+
+// Sum over the workgroup's 256 threads.
+GPTQ_DEV float block_sum(float v, float* red) {
+#pragma unroll
+  for (int m = 32; m > 0; m >>= 1) v += __shfl_xor(v, m, 64);
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
+  __syncthreads();
+  const float t = red[0] + red[1] + red[2] + red[3];
+  __syncthreads();
+  return t;
+}
+
+__global__ __launch_bounds__(256) void rmsnorm_kernel(const float* __restrict__ x, int64_t d, int64_t ldx,
+                                                      float eps, float* __restrict__ y, int64_t ldy) {
+  __shared__ float red[4];
+  const float* xr = x + (int64_t)blockIdx.x * ldx;
+  float* yr = y + (int64_t)blockIdx.x * ldy;
+  float ss = 0.f;
+  for (int64_t k = threadIdx.x; k < d; k += 256) ss = __builtin_fmaf(xr[k], xr[k], ss);
+  const float inv = 1.0f / sqrtf(block_sum(ss, red) / (float)d + eps);
+  for (int64_t k = threadIdx.x; k < d; k += 256) yr[k] = xr[k] * inv;
+}
+
+// Row i of an L x L score block (leading dimension lds): p_j = exp(scale s_j - max) / sum over
+// j <= i, and 0 for j > i (the causal mask).
+__global__ __launch_bounds__(256) void causal_softmax_kernel(float* __restrict__ S, int64_t L, int64_t lds,
+                                                             float scale) {
+  __shared__ float red[4];
+  const int64_t i = blockIdx.x;
+  float* row = S + i * lds;
+  float mx = -INFINITY;
+  for (int64_t j = threadIdx.x; j <= i; j += 256) mx = fmaxf(mx, scale * row[j]);
+#pragma unroll
+  for (int m = 32; m > 0; m >>= 1) mx = fmaxf(mx, __shfl_xor(mx, m, 64));
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = mx;
+  __syncthreads();
+  mx = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+  __syncthreads();
+  float sum = 0.f;
+  for (int64_t j = threadIdx.x; j <= i; j += 256) {
+    const float p = expf(scale * row[j] - mx);
+    row[j] = p;
+    sum += p;
+  }
+  const float inv = 1.0f / block_sum(sum, red);
+  for (int64_t j = threadIdx.x; j < L; j += 256) row[j] = j <= i ? row[j] * inv : 0.0f;
+}
+
+// y may be g itself (each element reads its own g and u before writing)
+__global__ __launch_bounds__(256) void silu_mul_kernel(const float* g, const float* __restrict__ u, int64_t n,
+                                                       float* y) {
+  for (int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x; e < n; e += (int64_t)gridDim.x * 256) {
+    const float a = g[e];
+    y[e] = a / (1.0f + expf(-a)) * u[e];
+  }
+}
+
+__global__ __launch_bounds__(256) void to_f32_kernel(const void* __restrict__ x, int dtype, int64_t n,
+                                                     float* __restrict__ y) {
+  for (int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x; e < n; e += (int64_t)gridDim.x * 256)
+    y[e] = load_as_f32(x, dtype, e);
+}
+
+unsigned grid_for(int64_t n) { return (unsigned)std::min<int64_t>((n + 255) / 256, 65536); }
+
+}  // namespace
+
+hipError_t dequantize(const uint8_t* codes, int64_t rows, int64_t d, const float* scales, const int32_t* zeros,
+                      const int32_t* gidx, int64_t g, float* W, int64_t ldw, hipStream_t s) {
+  if (rows * d <= 0) return hipSuccess;
+  hipLaunchKernelGGL(dequantize_kernel, dim3(grid_for(rows * d)), dim3(256), 0, s, codes, rows, d, scales, zeros, gidx,
+                     g, (d + g - 1) / g, W, ldw);
+  return hipGetLastError();
+}
+
+hipError_t rmsnorm(const float* x, int64_t m, int64_t d, int64_t ldx, float eps, float* y, int64_t ldy, hipStream_t s) {
+  if (m <= 0) return hipSuccess;
+  hipLaunchKernelGGL(rmsnorm_kernel, dim3((unsigned)m), dim3(256), 0, s, x, d, ldx, eps, y, ldy);
+  return hipGetLastError();
+}
+
+hipError_t causal_attention(const float* Q, const float* K, const float* V, int64_t seqs, int64_t L, int64_t heads,
+                            int64_t dh, int64_t ld, float* O, int64_t ldo, float* S, hipStream_t s) {
+  const float scale = 1.0f / sqrtf((float)dh);
+  for (int64_t sq = 0; sq < seqs; ++sq)
+    for (int64_t h = 0; h < heads; ++h) {
+      const int64_t off = sq * L * ld + h * dh;
+      GemmArgs a{};   // S = Q_h K_h^T
+      a.M = L; a.N = L; a.K = dh;
+      a.A = Q + off; a.lda = ld; a.transA = 0;
+      a.B = K + off; a.ldb = ld; a.transB = 1;
+      a.C = S; a.ldc = L;
+      a.alpha = 1.0f; a.beta = 0.0f; a.tri = 0;
+      hipError_t e = gemm_f32(a, s);
+      if (e != hipSuccess) return e;
+      hipLaunchKernelGGL(causal_softmax_kernel, dim3((unsigned)L), dim3(256), 0, s, S, L, L, scale);
+      GemmArgs b{};   // O_h = P V_h
+      b.M = L; b.N = dh; b.K = L;
+      b.A = S; b.lda = L; b.transA = 0;
+      b.B = V + off; b.ldb = ld; b.transB = 0;
+      b.C = O + sq * L * ldo + h * dh; b.ldc = ldo;
+      b.alpha = 1.0f; b.beta = 0.0f; b.tri = 0;
+      if ((e = gemm_f32(b, s)) != hipSuccess) return e;
+    }
+  return hipGetLastError();
+}
+
+hipError_t silu_mul(const float* g, const float* u, int64_t n, float* y, hipStream_t s) {
+  if (n <= 0) return hipSuccess;
+  hipLaunchKernelGGL(silu_mul_kernel, dim3(grid_for(n)), dim3(256), 0, s, g, u, n, y);
+  return hipGetLastError();
+}
+
+hipError_t to_f32(const void* x, int dtype, int64_t n, float* y, hipStream_t s) {
+  if (n <= 0) return hipSuccess;
+  hipLaunchKernelGGL(to_f32_kernel, dim3(grid_for(n)), dim3(256), 0, s, x, dtype, n, y);
+  return hipGetLastError();
+}
+
+// ------------------------------------------------------------------ the block driver
+
+namespace {
+
+size_t up256(size_t b) { return (b + 255) & ~(size_t)255; }
+
+// Layer i of the block (q, k, v, o, gate, up, down): output features and input features.
+void layer_dims(const gptq_block_shape_t& sh, int i, int64_t& rows, int64_t& d) {
+  rows = (i == 4 || i == 5) ? sh.inter : sh.hidden;
+  d = i == 6 ? sh.inter : sh.hidden;
+}
+
+}  // namespace
+
+BlockLayout block_layout(const gptq_block_shape_t& sh, const gptq_params_t& p) {
+  BlockLayout L{};
+  const int64_t n = sh.seqs * sh.seq_len, hd = sh.hidden, di = sh.inter, dm = std::max(hd, di);
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    const size_t o = off;
+    off += up256(bytes);
+    return o;
+  };
+  const size_t act = (size_t)n * hd * 4;
+  L.off_xf = take(act);
+  L.off_xa = take(act);
+  L.off_q = take(act);
+  L.off_k = take(act);
+  L.off_v = take(act);
+  L.off_at = take(act);
+  L.off_h1 = take(act);
+  L.off_xm = take(act);
+  L.off_g = take((size_t)n * di * 4);
+  L.off_u = take((size_t)n * di * 4);
+  L.off_s = take((size_t)sh.seq_len * sh.seq_len * 4);
+  L.off_wf = take((size_t)di * hd * 4);
+  L.off_h = take((size_t)dm * dm * 4);
+  L.off_uf = take((size_t)dm * dm * 4);
+  L.factor_bytes = gptq_workspace_bytes(GPTQ_WS_FACTOR, 0, dm, &p);
+  L.off_fw = take(L.factor_bytes);
+  L.quant_bytes = 0;
+  for (int i = 0; i < 7; ++i) {
+    int64_t rows, d;
+    layer_dims(sh, i, rows, d);
+    L.quant_bytes = std::max(L.quant_bytes, gptq_workspace_bytes(GPTQ_WS_QUANTIZE, rows, d, &p));
+  }
+  L.off_qw = take(L.quant_bytes);
+  L.total = off;
+  return L;
+}
+
+// True-sequential order (GPTQ tools page, "How it works", Step 9): q, k and v share the attention
+// input; o's input is recomputed through the quantized q, k, v; gate and up share the MLP input,
+// recomputed through the quantized o; down's input through the quantized gate and up. With
+// true_sequential = 0 every input comes from the block with its original weights. The block output
+// Y always runs through the quantized weights (the next block's input).
+int quantize_block(const gptq_block_shape_t& sh, const void* X, int x_dtype, const gptq_params_t& p,
+                   int true_sequential, const gptq_block_layer_t* layers, float* Y, float* const* hess, char* work,
+                   int64_t* info, hipStream_t s) {
+  const BlockLayout L = block_layout(sh, p);
+  const int64_t n = sh.seqs * sh.seq_len, hd = sh.hidden, di = sh.inter;
+  float* xf = reinterpret_cast<float*>(work + L.off_xf);
+  float* xa = reinterpret_cast<float*>(work + L.off_xa);
+  float* q = reinterpret_cast<float*>(work + L.off_q);
+  float* k = reinterpret_cast<float*>(work + L.off_k);
+  float* v = reinterpret_cast<float*>(work + L.off_v);
+  float* at = reinterpret_cast<float*>(work + L.off_at);
+  float* h1 = reinterpret_cast<float*>(work + L.off_h1);
+  float* xm = reinterpret_cast<float*>(work + L.off_xm);
+  float* gb = reinterpret_cast<float*>(work + L.off_g);
+  float* ub = reinterpret_cast<float*>(work + L.off_u);
+  float* S = reinterpret_cast<float*>(work + L.off_s);
+  float* Wf = reinterpret_cast<float*>(work + L.off_wf);
+  float* H = reinterpret_cast<float*>(work + L.off_h);
+  float* U = reinterpret_cast<float*>(work + L.off_uf);
+  const float eps = (float)sh.eps;
+#define GPTQ_TRY(x)                                   \
+  do {                                                \
+    if ((x) != hipSuccess) return GPTQ_EHIP;          \
+  } while (0)
+
+  // H of one stage input A [n x d], then U, the order and the column loop of every layer reading A
+  auto stage = [&](int si, const float* A, int64_t d, int first, int last) -> int {
+    GPTQ_TRY(hipMemsetAsync(H, 0, (size_t)d * d * 4, s));
+    int st = gptq_hessian_accumulate(H, d, A, GPTQ_F32, n, d, nullptr, 0, s);
+    if (st != GPTQ_OK) return st;
+    if (hess && hess[si]) GPTQ_TRY(hipMemcpyAsync(hess[si], H, (size_t)d * d * 4, hipMemcpyDeviceToDevice, s));
+    int64_t piv = 0;
+    st = gptq_factor(H, d, n, &p, U, layers[first].perm, work + L.off_fw, L.factor_bytes, &piv, s);
+    if (st != GPTQ_OK) {
+      info[0] = si;
+      info[1] = piv;
+      return st;
+    }
+    for (int i = first; i <= last; ++i) {
+      int64_t rows, dd;
+      layer_dims(sh, i, rows, dd);
+      if (i != first && layers[i].perm != layers[first].perm)
+        GPTQ_TRY(hipMemcpyAsync(layers[i].perm, layers[first].perm, (size_t)d * 4, hipMemcpyDeviceToDevice, s));
+      st = gptq_quantize_layer(layers[i].W, layers[i].w_dtype, rows, d, d, U, layers[i].perm, &p, layers[i].codes,
+                               layers[i].scales, layers[i].zeros, layers[i].g_idx, layers[i].loss, work + L.off_qw,
+                               L.quant_bytes, s);
+      if (st != GPTQ_OK) return st;
+    }
+    return GPTQ_OK;
+  };
+  // dense fp32 weights of layer i: its quantized values or its original ones
+  auto weight = [&](int i, bool quantized) -> hipError_t {
+    int64_t rows, d;
+    layer_dims(sh, i, rows, d);
+    if (!quantized) return to_f32(layers[i].W, layers[i].w_dtype, rows * d, Wf, s);
+    const int64_t g = p.group_size <= 0 ? d : p.group_size;
+    return dequantize(layers[i].codes, rows, d, layers[i].scales, layers[i].zeros, layers[i].g_idx, g, Wf, d, s);
+  };
+  // out = in W_i^T (+ out when accumulate)
+  auto project = [&](int i, bool quantized, const float* in, float* out, bool accumulate) -> hipError_t {
+    int64_t rows, d;
+    layer_dims(sh, i, rows, d);
+    hipError_t e = weight(i, quantized);
+    if (e != hipSuccess) return e;
+    GemmArgs a{};
+    a.M = n; a.N = rows; a.K = d;
+    a.A = in; a.lda = d; a.transA = 0;
+    a.B = Wf; a.ldb = d; a.transB = 1;
+    a.C = out; a.ldc = rows;
+    a.alpha = 1.0f; a.beta = accumulate ? 1.0f : 0.0f; a.tri = 0;
+    return gemm_f32(a, s);
+  };
+  // one pass over the block; quantize: run each stage's solve before its layers are used
+  auto pass = [&](bool quantized, bool quantize) -> int {
+    int st;
+    GPTQ_TRY(rmsnorm(xf, n, hd, hd, eps, xa, hd, s));
+    if (quantize && (st = stage(0, xa, hd, 0, 2)) != GPTQ_OK) return st;
+    GPTQ_TRY(project(0, quantized, xa, q, false));
+    GPTQ_TRY(project(1, quantized, xa, k, false));
+    GPTQ_TRY(project(2, quantized, xa, v, false));
+    GPTQ_TRY(causal_attention(q, k, v, sh.seqs, sh.seq_len, sh.heads, hd / sh.heads, hd, at, hd, S, s));
+    if (quantize && (st = stage(1, at, hd, 3, 3)) != GPTQ_OK) return st;
+    GPTQ_TRY(hipMemcpyAsync(h1, xf, (size_t)n * hd * 4, hipMemcpyDeviceToDevice, s));
+    GPTQ_TRY(project(3, quantized, at, h1, true));
+    GPTQ_TRY(rmsnorm(h1, n, hd, hd, eps, xm, hd, s));
+    if (quantize && (st = stage(2, xm, hd, 4, 5)) != GPTQ_OK) return st;
+    GPTQ_TRY(project(4, quantized, xm, gb, false));
+    GPTQ_TRY(project(5, quantized, xm, ub, false));
+    GPTQ_TRY(silu_mul(gb, ub, n * di, gb, s));
+    if (quantize && (st = stage(3, gb, di, 6, 6)) != GPTQ_OK) return st;
+    GPTQ_TRY(hipMemcpyAsync(Y, h1, (size_t)n * hd * 4, hipMemcpyDeviceToDevice, s));
+    GPTQ_TRY(project(6, true, gb, Y, true));
+    return GPTQ_OK;
+  };
+#undef GPTQ_TRY
+  info[0] = -1;
+  info[1] = 0;
+  if (to_f32(X, x_dtype, n * hd, xf, s) != hipSuccess) return GPTQ_EHIP;
+  int st = pass(true_sequential != 0, true);
+  if (st == GPTQ_OK && !true_sequential) st = pass(true, false);
+  return st;
+}
+
+}  // namespace gptq

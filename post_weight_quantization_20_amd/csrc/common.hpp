@@ -9,6 +9,8 @@
 #include <stdint.h>
 #include <stddef.h>
 
+#include "../../include/gptq.h"
+
 #define GPTQ_DEV __device__ __forceinline__
 
 namespace gptq {
@@ -164,5 +166,31 @@ hipError_t permute_columns(const void* in, int64_t m, int64_t d, int64_t ld_in, 
 hipError_t dequant_gemm(const void* x, int dtype, int64_t m, int64_t ldx, const int32_t* packed, int bits, int dense,
                         const float* scales, const int32_t* zeros, const int32_t* gidx, int64_t rows, int64_t d,
                         int64_t g, float* y, int64_t ldy, hipStream_t s);
+
+// ------------------------------------------------------------------ decoder block (block.hip)
+// W[r, k] = scales[r, G] (codes[r, k] - zeros[r, G]), G = gidx[k] (or k / g when gidx is null),
+// as dense fp32 rows of leading dimension ldw.
+hipError_t dequantize(const uint8_t* codes, int64_t rows, int64_t d, const float* scales, const int32_t* zeros,
+                      const int32_t* gidx, int64_t g, float* W, int64_t ldw, hipStream_t s);
+// Row-wise x / sqrt(mean(x^2) + eps).
+hipError_t rmsnorm(const float* x, int64_t m, int64_t d, int64_t ldx, float eps, float* y, int64_t ldy, hipStream_t s);
+// Multi-head causal attention over seqs sequences of L tokens; Q, K, V, O are [seqs L x heads dh]
+// (leading dimensions ld, ld, ld, ldo); S is L x L fp32 scratch.
+hipError_t causal_attention(const float* Q, const float* K, const float* V, int64_t seqs, int64_t L, int64_t heads,
+                            int64_t dh, int64_t ld, float* O, int64_t ldo, float* S, hipStream_t s);
+// y = silu(g) * u elementwise; y may be g.
+hipError_t silu_mul(const float* g, const float* u, int64_t n, float* y, hipStream_t s);
+hipError_t to_f32(const void* x, int dtype, int64_t n, float* y, hipStream_t s);
+
+// Workspace of gptq_quantize_block: byte offsets of the fp32 activations, one dense weight, the
+// stage Hessian and factor, and the factor and column-loop workspaces.
+struct BlockLayout {
+  size_t off_xf, off_xa, off_q, off_k, off_v, off_at, off_h1, off_xm, off_g, off_u, off_s, off_wf, off_h, off_uf,
+      off_fw, off_qw, factor_bytes, quant_bytes, total;
+};
+BlockLayout block_layout(const gptq_block_shape_t& sh, const gptq_params_t& p);
+int quantize_block(const gptq_block_shape_t& sh, const void* X, int x_dtype, const gptq_params_t& p,
+                   int true_sequential, const gptq_block_layer_t* layers, float* Y, float* const* hess, char* work,
+                   int64_t* info, hipStream_t s);
 
 }  // namespace gptq

@@ -283,3 +283,87 @@ def quantize_layer(W: torch.Tensor, X_chunks, params: Params, stream=None) -> La
     q = gptq_quantize_layer(W, U, perm, params, stream=stream)
     packed = gptq_pack(q.codes, params.bits, stream=stream) if d % 8 == 0 else None
     return LayerResult(H=H, U=U, perm=perm, quant=q, packed=packed)
+
+
+BLOCK_LAYERS = ("q", "k", "v", "o", "gate", "up", "down")
+
+
+@dataclass
+class BlockShape:
+    """A pre-norm decoder block (gptq_block_shape_t): widths, heads and calibration sizes."""
+
+    hidden: int
+    heads: int
+    inter: int
+    seqs: int
+    seq_len: int
+    eps: float = 1e-6
+
+    def c(self) -> _lib.gptq_block_shape_t:
+        return _lib.gptq_block_shape_t(int(self.hidden), int(self.heads), int(self.inter), int(self.seqs),
+                                       int(self.seq_len), float(self.eps))
+
+    def layer_dims(self, i: int) -> Tuple[int, int]:
+        """(rows, d) of layer i in BLOCK_LAYERS order."""
+        rows = self.inter if i in (4, 5) else self.hidden
+        return rows, (self.inter if i == 6 else self.hidden)
+
+
+@dataclass
+class BlockResult:
+    layers: list                      # QuantOutput per layer, BLOCK_LAYERS order
+    perms: list                       # int32 [d] processing order per layer
+    Y: torch.Tensor                   # float32 [tokens, hidden]: block output through the quantized weights
+    hessians: Optional[list]          # float32 [d, d] per stage (upper triangle), when asked for
+
+
+def gptq_block_workspace_bytes(shape: BlockShape, params: Params) -> int:
+    return int(_lib.lib().gptq_block_workspace_bytes(ctypes.byref(shape.c()), ctypes.byref(params.c())))
+
+
+def gptq_quantize_block(X: torch.Tensor, weights, shape: BlockShape, params: Params, true_sequential: bool = True,
+                        return_hessians: bool = False, work: Optional[torch.Tensor] = None,
+                        stream=None) -> BlockResult:
+    """Quantizes the seven layers of one decoder block (weights in BLOCK_LAYERS order, each
+    contiguous [rows, d]) from its input X [seqs * seq_len, hidden], true-sequential by default."""
+    _need_cuda(X, work, *weights)
+    n = shape.seqs * shape.seq_len
+    if len(weights) != 7:
+        raise ValueError("seven weights: q, k, v, o, gate, up, down")
+    if X.dim() != 2 or tuple(X.shape) != (n, shape.hidden) or not X.is_contiguous() or X.dtype not in _DTYPE:
+        raise ValueError("X must be contiguous [seqs * seq_len, hidden], fp32/fp16/bf16")
+    dev = X.device
+    outs, perms = [], []
+    arr = (_lib.gptq_block_layer_t * 7)()
+    for i, W in enumerate(weights):
+        rows, d = shape.layer_dims(i)
+        if tuple(W.shape) != (rows, d) or not W.is_contiguous() or W.dtype not in _DTYPE:
+            raise ValueError(f"{BLOCK_LAYERS[i]}: weights must be contiguous [{rows}, {d}], fp32/fp16/bf16")
+        ng = params.groups(d)
+        o = QuantOutput(codes=torch.empty((rows, d), dtype=torch.uint8, device=dev),
+                        scales=torch.empty((rows, ng), dtype=torch.float32, device=dev),
+                        zeros=torch.empty((rows, ng), dtype=torch.int32, device=dev),
+                        g_idx=torch.empty(d, dtype=torch.int32, device=dev),
+                        loss=torch.empty(1, dtype=torch.float64, device=dev))
+        perm = torch.empty(d, dtype=torch.int32, device=dev)
+        arr[i] = _lib.gptq_block_layer_t(W.data_ptr(), o.codes.data_ptr(), o.scales.data_ptr(), o.zeros.data_ptr(),
+                                         o.g_idx.data_ptr(), perm.data_ptr(), o.loss.data_ptr(), _DTYPE[W.dtype])
+        outs.append(o)
+        perms.append(perm)
+    Y = torch.empty((n, shape.hidden), dtype=torch.float32, device=dev)
+    hess, hptr = None, None
+    if return_hessians:
+        widths = (shape.hidden, shape.hidden, shape.hidden, shape.inter)
+        hess = [torch.empty((w, w), dtype=torch.float32, device=dev) for w in widths]
+        hptr = (ctypes.c_void_p * 4)(*[h.data_ptr() for h in hess])
+    if work is None:
+        nb = gptq_block_workspace_bytes(shape, params)
+        if nb == 0:
+            raise ValueError("invalid block shape or settings")
+        work = torch.empty(nb, dtype=torch.uint8, device=dev)
+    info = (ctypes.c_int64 * 2)()
+    st = _lib.lib().gptq_quantize_block(ctypes.byref(shape.c()), _ptr(X), _DTYPE[X.dtype], ctypes.byref(params.c()),
+                                        int(bool(true_sequential)), arr, _ptr(Y), hptr, _ptr(work), work.numel(),
+                                        info, _stream(stream))
+    _check(st, int(info[1]))
+    return BlockResult(layers=outs, perms=perms, Y=Y, hessians=hess)

@@ -232,3 +232,55 @@ def test_binding_fails_loudly_without_the_library():
             "    print('raised', 'build' in str(e))\n")
     r = subprocess.run(["python3", "-c", code], capture_output=True, text=True, cwd=ROOT)
     assert r.stdout.strip() == "raised True", r.stdout + r.stderr
+
+
+def test_block_structs_and_workspace():
+    L = _lib()
+    lib = L.lib()
+    assert ctypes.sizeof(L.gptq_block_shape_t) == 48 and L.gptq_block_shape_t.eps.offset == 40
+    assert ctypes.sizeof(L.gptq_block_layer_t) == 64 and L.gptq_block_layer_t.w_dtype.offset == 56
+    p = _p(L)
+    sh = L.gptq_block_shape_t(256, 4, 688, 4, 200, 1e-6)
+    n = 800
+    w = lib.gptq_block_workspace_bytes(ctypes.byref(sh), ctypes.byref(p))
+    acts = (8 * n * 256 + 2 * n * 688 + 200 * 200 + 688 * 256 + 2 * 688 * 688) * 4
+    assert w >= acts
+    for bad in (L.gptq_block_shape_t(256, 3, 688, 4, 200, 1e-6), L.gptq_block_shape_t(4, 1, 688, 4, 200, 1e-6),
+                L.gptq_block_shape_t(256, 4, 688, 0, 200, 1e-6), L.gptq_block_shape_t(256, 4, 688, 4, 200, -1.0),
+                L.gptq_block_shape_t(256, 4, 688, 4, 200, float("nan"))):
+        assert lib.gptq_block_workspace_bytes(ctypes.byref(bad), ctypes.byref(p)) == 0
+    assert lib.gptq_block_workspace_bytes(ctypes.byref(sh), None) == 0
+    assert lib.gptq_block_workspace_bytes(ctypes.byref(sh), ctypes.byref(_p(L, block_size=129))) == 0
+
+
+def test_block_rejects_bad_arguments():
+    L = _lib()
+    lib = L.lib()
+    sh = L.gptq_block_shape_t(256, 4, 688, 4, 200, 1e-6)
+    p = _p(L)
+    big = lib.gptq_block_workspace_bytes(ctypes.byref(sh), ctypes.byref(p))
+    layers = (L.gptq_block_layer_t * 7)(*[L.gptq_block_layer_t(*([0x1000] * 7), 1) for _ in range(7)])
+    info = (ctypes.c_int64 * 2)(5, 5)
+
+    def call(shape=sh, X=FAKE, x_dtype=1, params=p, ts=1, lay=layers, Y=FAKE, work=FAKE, nbytes=big):
+        return lib.gptq_quantize_block(ctypes.byref(shape) if shape is not None else None, X, x_dtype,
+                                       ctypes.byref(params), ts, lay, Y, None, work, nbytes, info, None)
+
+    assert call(shape=None) == -1
+    assert list(info) == [-1, 0]
+    assert call(shape=L.gptq_block_shape_t(256, 5, 688, 4, 200, 1e-6)) == -1   # heads must divide hidden
+    assert call(X=None) == -1
+    assert call(x_dtype=7) == -1
+    assert call(ts=2) == -1
+    assert call(Y=None) == -1
+    assert call(work=None) == -1
+    assert call(params=_p(L, bits=9)) == -1
+    assert call(params=_p(L, group_size=96)) == -1          # groups and blocks must nest
+    assert call(params=_p(L, block_size=256)) == -3
+    bad = (L.gptq_block_layer_t * 7)(*[L.gptq_block_layer_t(*([0x1000] * 7), 1) for _ in range(7)])
+    bad[5].perm = None
+    assert call(lay=bad) == -1
+    bad[5].perm = 0x1000
+    bad[6].w_dtype = 3
+    assert call(lay=bad) == -1
+    assert call(nbytes=big - 1) == -5
