@@ -50,6 +50,8 @@ def parse():
     ap.add_argument("--dequant", default=None, choices=["fc2", "q_proj", "down_proj"],
                     help="measure gptq_dequant_gemm on a stored layer of this workload's shape instead")
     ap.add_argument("--batch", type=int, default=1, help="input rows for --dequant")
+    ap.add_argument("--block", action="store_true",
+                    help="time the true-sequential driver on a Llama-7B-shaped decoder block instead")
     ap.add_argument("--ordered", action="store_true",
                     help="--dequant of an act-order layer: codes packed in processing order, inputs gathered by "
                          "the same order in every call (gptq_pack_ordered, gptq_permute_columns)")
@@ -256,6 +258,152 @@ def bench_dequant(args):
     print(json.dumps(out), flush=True)
 
 
+BLOCK = dict(hidden=4096, heads=32, inter=11008, seqs=128, seq_len=2048)
+
+
+def block_flops(hd: int, heads: int, di: int, seqs: int, L: int) -> dict:
+    """Algorithmic fp32 flops of one block solve, by phase (a multiply-add counts 2)."""
+    n = seqs * L
+    dims = [(hd, hd)] * 4 + [(di, hd)] * 2 + [(hd, di)]
+    dh = hd // heads
+    return {
+        # x W^T for the seven layers
+        "projections": 2.0 * n * sum(r * d for r, d in dims),
+        # causal scores and P V: key j <= query i only
+        "attention": 2.0 * 2.0 * dh * (L * (L + 1) / 2) * heads * seqs,
+        # the d (d + 1) / 2 distinct entries of each stage's 2 X^T X
+        "hessians": float(n) * sum(d * (d + 1) for d in (hd, hd, hd, di)),
+        # Cholesky plus triangular inverse, d^3 / 3 each
+        "factors": sum(2.0 * d ** 3 / 3 for d in (hd, hd, hd, di)),
+        # error propagation through the factor: 2 rows d^2 per layer
+        "column_loops": sum(2.0 * r * d * d for r, d in dims),
+    }
+
+
+def block_cpu_baseline(case, W, X):
+    """The oracle on a bounded sample of the block solve, each phase scaled to the full block: the
+    forward pass and stage Hessians on one sequence, the factors at full width, the column loops on
+    16 rows of a 4096-wide and of the 11008-wide layer."""
+    import synth
+    from oracle import block_ref as blk
+    from oracle import gptq_ref as ref
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([i.get("num_threads", 1) for i in threadpool_info()] or [os.cpu_count() or 1])
+    except Exception:
+        cores = os.cpu_count() or 1
+    L = case.seq_len
+    sh = blk.BlockShape(case.hidden, case.heads, case.inter, 1, L, 1e-6)
+    W64 = [synth.to_f64(w, case.w_dtype) for w in W]
+    x1 = synth.to_f64(X[:L], case.x_dtype)
+    t0 = time.perf_counter()
+    inputs = blk.forward(x1, W64, sh)["inputs"]
+    t_fwd = (time.perf_counter() - t0) * case.seqs
+    t0 = time.perf_counter()
+    Hs = [ref.hessian([a])[0] for a in inputs]
+    t_h = (time.perf_counter() - t0) * case.seqs
+    fac, U = {}, {}
+    for si in (0, 3):
+        t0 = time.perf_counter()
+        Hh, perm, _ = ref.damp_and_order(Hs[si], L, 0.01, True)
+        U[si] = (ref.inverse_cholesky_upper(Hh), perm)
+        fac[si] = time.perf_counter() - t0
+    t_f = 3 * fac[0] + fac[3]
+    t_q = 0.0
+    for si, li in ((0, 0), (3, 6)):
+        t0 = time.perf_counter()
+        ref.quantize_layer(W64[li][:16], U[si][0], 4, 128, 128, perm=U[si][1])
+        per_row = (time.perf_counter() - t0) / 16
+        rows = [synth.block_layer_dims(case, i)[0] for i in range(7) if (i == 6) == (li == 6)]
+        t_q += per_row * sum(rows)
+    total = t_fwd + t_h + t_f + t_q
+    cols = sum(synth.block_layer_dims(case, i)[1] for i in range(7))
+    return {
+        "value": cols / total,
+        "unit": "weight-columns/s",
+        "cores": int(cores),
+        "kind": "oracle",
+        "sec_per_block": total,
+        "phases_s": {"forward": t_fwd, "hessians": t_h, "factors": t_f, "column_loops": t_q},
+        "sample": (f"float64 oracle: forward pass and stage Hessians on 1 of {case.seqs} sequences ({L} tokens), "
+                   f"factors at full width ({case.hidden} once for the three {case.hidden}-wide stages, {case.inter} "
+                   f"once), column loops on 16 rows of q and of down (per-row time applied to every layer of that width); each phase "
+                   f"scaled to the full block"),
+    }
+
+
+def bench_block(args):
+    import torch
+    import post_weight_quantization_20_amd as g
+    import synth
+
+    case = synth.BlockCase(**BLOCK)
+    dev = torch.device("cuda:0")
+    n = case.seqs * case.seq_len
+    print(f"[bench] generating a decoder block: hidden {case.hidden}, {case.heads} heads, MLP {case.inter}, "
+          f"X {n}x{case.hidden} fp16", file=sys.stderr, flush=True)
+    t0 = time.perf_counter()
+    W_host = synth.block_weights(case, 500)
+    X_host = synth.block_x(case, 500)
+    W = [torch.from_numpy(w).to(dev) for w in W_host]
+    X = torch.from_numpy(X_host).to(dev)
+    torch.cuda.synchronize()
+    print(f"[bench] inputs resident in HBM ({time.perf_counter() - t0:.1f} s)", file=sys.stderr, flush=True)
+    shape = g.BlockShape(case.hidden, case.heads, case.inter, case.seqs, case.seq_len, 1e-6)
+    params = g.Params(bits=4, group_size=128, block_size=128, act_order=True, damp=0.01)
+    work = torch.empty(g.gptq_block_workspace_bytes(shape, params), dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream()
+    for i in range(args.warmup):
+        g.gptq_quantize_block(X, W, shape, params, True, work=work)
+        torch.cuda.synchronize()
+        print(f"[bench] warmup {i + 1}/{args.warmup} done", file=sys.stderr, flush=True)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    e0.record(stream)
+    for i in range(args.steps):
+        r = g.gptq_quantize_block(X, W, shape, params, True, work=work)
+        print(f"[bench] step {i + 1}/{args.steps} queued", file=sys.stderr, flush=True)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms = e0.elapsed_time(e1) / args.steps
+    losses = [float(q.loss.item()) for q in r.layers]
+    cols = sum(shape.layer_dims(i)[1] for i in range(7))
+    fl = block_flops(case.hidden, case.heads, case.inter, case.seqs, case.seq_len)
+    achieved = sum(fl.values()) / (ms / 1000.0) / 1e12
+    out = {
+        "metric": "GPTQ sec/layer + weight-columns/s at 4096x4096 int4 g128; % MFMA / HBM peak",
+        "value": round(cols / (ms / 1000.0), 1),
+        "unit": "weight-columns/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(wall * 1000.0 / args.steps, 3),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic (seeded random block weights and block input; no trained weights)",
+        "config": {"workload": f"Llama-7B-shaped decoder block, true-sequential: q/k/v/o {case.hidden}x{case.hidden}, "
+                               f"gate/up {case.inter}x{case.hidden}, down {case.hidden}x{case.inter} fp16; X "
+                               f"{case.seqs}x{case.seq_len} tokens fp16; 4-bit g128 act-order, block 128, damp 0.01",
+                   "hidden": case.hidden, "heads": case.heads, "inter": case.inter, "seqs": case.seqs,
+                   "seq_len": case.seq_len, "sec_per_block": round(ms / 1000.0, 4),
+                   "sec_per_layer": round(ms / 1000.0 / 7, 4), "layer_losses": losses},
+        "roofline": {"kernel": "the block solve as a whole (fp32 MFMA products dominate)", "bound": "mfma",
+                     "achieved": round(achieved, 2), "peak": PEAK_F32_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(achieved / PEAK_F32_TFLOPS, 4), "traffic": None,
+                     "flops_per_block": {k: float(f"{v:.4g}") for k, v in fl.items()}, "avg_launch_ms": round(ms, 3)},
+    }
+    if not args.no_cpu_baseline:
+        print("[bench] timing the float64 oracle on a bounded sample", file=sys.stderr, flush=True)
+        out["cpu_baseline"] = block_cpu_baseline(case, W_host, X_host)
+    else:
+        out["cpu_baseline"] = None
+    print(json.dumps(out), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
@@ -265,6 +413,9 @@ def main():
         sys.exit(2)
     if args.dequant:
         bench_dequant(args)
+        return
+    if args.block:
+        bench_block(args)
         return
 
     import torch
