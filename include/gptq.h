@@ -273,7 +273,7 @@ gptq_status_t gptq_dequant_gemm(const void *x, int32_t x_dtype, int64_t m, int64
  */
 typedef struct {
   int64_t hidden;   /* model width, >= 8; q, k, v, o are hidden x hidden                          */
-  int64_t heads;    /* attention heads, >= 1, dividing hidden                                     */
+  int64_t heads;    /* attention heads, 1..65535, dividing hidden; heads * seq_len <= 2^31        */
   int64_t inter;    /* MLP width, >= 8; gate and up are inter x hidden, down hidden x inter       */
   int64_t seqs;     /* calibration sequences, >= 1                                                */
   int64_t seq_len;  /* tokens per sequence, >= 1; attention is causal within each sequence        */

@@ -180,8 +180,9 @@ namespace {
 bool block_shape_ok(const gptq_block_shape_t* sh) {
   if (!sh) return false;
   if (sh->hidden < 8 || sh->hidden > kMaxDim || sh->inter < 8 || sh->inter > kMaxDim) return false;
-  if (sh->heads < 1 || sh->hidden % sh->heads != 0) return false;
+  if (sh->heads < 1 || sh->heads > 65535 || sh->hidden % sh->heads != 0) return false;
   if (sh->seqs < 1 || sh->seq_len < 1 || sh->seq_len > kMaxDim || sh->seqs > kMaxDim / sh->seq_len) return false;
+  if (sh->heads * sh->seq_len > kMaxDim) return false;   // softmax rows of one sequence, one workgroup each
   return std::isfinite(sh->eps) && sh->eps >= 0.0;
 }
 

@@ -60,13 +60,13 @@ __global__ __launch_bounds__(256) void rmsnorm_kernel(const float* __restrict__ 
   for (int64_t k = threadIdx.x; k < d; k += 256) yr[k] = xr[k] * inv;
 }
 
-// Row i of an L x L score block (leading dimension lds): p_j = exp(scale s_j - max) / sum over
-// j <= i, and 0 for j > i (the causal mask).
-__global__ __launch_bounds__(256) void causal_softmax_kernel(float* __restrict__ S, int64_t L, int64_t lds,
-                                                             float scale) {
+// One row of a stack of L x L score blocks (row r is query i = r mod L of its block, leading
+// dimension L): p_j = exp(scale s_j - max) / sum over j <= i, and 0 for j > i (the causal mask).
+// Only entries j <= i are read.
+__global__ __launch_bounds__(256) void causal_softmax_kernel(float* __restrict__ S, int64_t L, float scale) {
   __shared__ float red[4];
-  const int64_t i = blockIdx.x;
-  float* row = S + i * lds;
+  const int64_t i = (int64_t)blockIdx.x % L;
+  float* row = S + (int64_t)blockIdx.x * L;
   float mx = -INFINITY;
   for (int64_t j = threadIdx.x; j <= i; j += 256) mx = fmaxf(mx, scale * row[j]);
 #pragma unroll
@@ -100,6 +100,19 @@ __global__ __launch_bounds__(256) void to_f32_kernel(const void* __restrict__ x,
     y[e] = load_as_f32(x, dtype, e);
 }
 
+// H[r, c] = sum over b < S of P[b][r, c] on and above the diagonal (a fixed order), 0 below.
+__global__ __launch_bounds__(256) void sum_upper_kernel(const float* __restrict__ P, int S, int64_t d,
+                                                        float* __restrict__ H) {
+  const int64_t total = d * d;
+  for (int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x; e < total; e += (int64_t)gridDim.x * 256) {
+    const int64_t r = e / d, c = e - r * d;
+    float v = 0.0f;
+    if (c >= r)
+      for (int b = 0; b < S; ++b) v += P[b * total + e];
+    H[e] = v;
+  }
+}
+
 unsigned grid_for(int64_t n) { return (unsigned)std::min<int64_t>((n + 255) / 256, 65536); }
 
 }  // namespace
@@ -118,29 +131,33 @@ hipError_t rmsnorm(const float* x, int64_t m, int64_t d, int64_t ldx, float eps,
   return hipGetLastError();
 }
 
+// One sequence at a time, every head in one batched product: S_h = Q_h K_h^T (lower triangle of
+// tiles only), the causal softmax over all heads' rows, then O_h = P_h V_h with the k loop of each
+// row tile stopping at its last row (P is zero above the diagonal). S holds heads x L x L floats.
 hipError_t causal_attention(const float* Q, const float* K, const float* V, int64_t seqs, int64_t L, int64_t heads,
                             int64_t dh, int64_t ld, float* O, int64_t ldo, float* S, hipStream_t s) {
   const float scale = 1.0f / sqrtf((float)dh);
-  for (int64_t sq = 0; sq < seqs; ++sq)
-    for (int64_t h = 0; h < heads; ++h) {
-      const int64_t off = sq * L * ld + h * dh;
-      GemmArgs a{};   // S = Q_h K_h^T
-      a.M = L; a.N = L; a.K = dh;
-      a.A = Q + off; a.lda = ld; a.transA = 0;
-      a.B = K + off; a.ldb = ld; a.transB = 1;
-      a.C = S; a.ldc = L;
-      a.alpha = 1.0f; a.beta = 0.0f; a.tri = 0;
-      hipError_t e = gemm_f32(a, s);
-      if (e != hipSuccess) return e;
-      hipLaunchKernelGGL(causal_softmax_kernel, dim3((unsigned)L), dim3(256), 0, s, S, L, L, scale);
-      GemmArgs b{};   // O_h = P V_h
-      b.M = L; b.N = dh; b.K = L;
-      b.A = S; b.lda = L; b.transA = 0;
-      b.B = V + off; b.ldb = ld; b.transB = 0;
-      b.C = O + sq * L * ldo + h * dh; b.ldc = ldo;
-      b.alpha = 1.0f; b.beta = 0.0f; b.tri = 0;
-      if ((e = gemm_f32(b, s)) != hipSuccess) return e;
-    }
+  for (int64_t sq = 0; sq < seqs; ++sq) {
+    const int64_t off = sq * L * ld;
+    GemmArgs a{};
+    a.M = L; a.N = L; a.K = dh;
+    a.A = Q + off; a.lda = ld; a.transA = 0;
+    a.B = K + off; a.ldb = ld; a.transB = 1;
+    a.C = S; a.ldc = L;
+    a.alpha = 1.0f; a.beta = 0.0f; a.tri = 1;
+    a.batch = heads; a.sA = dh; a.sB = dh; a.sC = L * L;
+    hipError_t e = gemm_f32(a, s);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(causal_softmax_kernel, dim3((unsigned)(heads * L)), dim3(256), 0, s, S, L, scale);
+    GemmArgs b{};
+    b.M = L; b.N = dh; b.K = L;
+    b.A = S; b.lda = L; b.transA = 0; b.lowerA = 1;
+    b.B = V + off; b.ldb = ld; b.transB = 0;
+    b.C = O + sq * L * ldo; b.ldc = ldo;
+    b.alpha = 1.0f; b.beta = 0.0f; b.tri = 0;
+    b.batch = heads; b.sA = L * L; b.sB = dh; b.sC = dh;
+    if ((e = gemm_f32(b, s)) != hipSuccess) return e;
+  }
   return hipGetLastError();
 }
 
@@ -161,6 +178,17 @@ hipError_t to_f32(const void* x, int dtype, int64_t n, float* y, hipStream_t s) 
 namespace {
 
 size_t up256(size_t b) { return (b + 255) & ~(size_t)255; }
+
+// Token splits of a stage Hessian: one pass of 2 A^T A over n tokens gives ceil(d/128) (ceil(d/128)
+// + 1) / 2 long-running 128-wide tiles, too few to fill 256 CUs evenly at d = 4096 (528 tiles: one
+// full round and a second one for 16). S equal slices of the tokens (S | n, at least 32 tokens
+// each, S <= 8) run as one batched product into S partial sums until there are >= 4096 tiles.
+int hess_split(int64_t d, int64_t n) {
+  const int64_t t = ((d + 127) / 128) * ((d + 127) / 128 + 1) / 2;
+  int S = 1;
+  while (S < 8 && t * S < 4096 && n % (2 * S) == 0 && n / (2 * S) >= 32) S *= 2;
+  return S;
+}
 
 // Layer i of the block (q, k, v, o, gate, up, down): output features and input features.
 void layer_dims(const gptq_block_shape_t& sh, int i, int64_t& rows, int64_t& d) {
@@ -190,10 +218,16 @@ BlockLayout block_layout(const gptq_block_shape_t& sh, const gptq_params_t& p) {
   L.off_xm = take(act);
   L.off_g = take((size_t)n * di * 4);
   L.off_u = take((size_t)n * di * 4);
-  L.off_s = take((size_t)sh.seq_len * sh.seq_len * 4);
+  L.off_s = take((size_t)sh.heads * sh.seq_len * sh.seq_len * 4);
   L.off_wf = take((size_t)di * hd * 4);
   L.off_h = take((size_t)dm * dm * 4);
   L.off_uf = take((size_t)dm * dm * 4);
+  size_t part = 0;
+  for (int64_t d : {hd, di}) {
+    const int S = hess_split(d, n);
+    if (S > 1) part = std::max(part, (size_t)S * d * d * 4);
+  }
+  L.off_hp = take(part);
   L.factor_bytes = gptq_workspace_bytes(GPTQ_WS_FACTOR, 0, dm, &p);
   L.off_fw = take(L.factor_bytes);
   L.quant_bytes = 0;
@@ -239,9 +273,25 @@ int quantize_block(const gptq_block_shape_t& sh, const void* X, int x_dtype, con
 
   // H of one stage input A [n x d], then U, the order and the column loop of every layer reading A
   auto stage = [&](int si, const float* A, int64_t d, int first, int last) -> int {
-    GPTQ_TRY(hipMemsetAsync(H, 0, (size_t)d * d * 4, s));
-    int st = gptq_hessian_accumulate(H, d, A, GPTQ_F32, n, d, nullptr, 0, s);
-    if (st != GPTQ_OK) return st;
+    int st;
+    const int S = hess_split(d, n);
+    if (S == 1) {
+      GPTQ_TRY(hipMemsetAsync(H, 0, (size_t)d * d * 4, s));
+      if ((st = gptq_hessian_accumulate(H, d, A, GPTQ_F32, n, d, nullptr, 0, s)) != GPTQ_OK) return st;
+    } else {
+      float* P = reinterpret_cast<float*>(work + L.off_hp);
+      const int64_t c = n / S;
+      GemmArgs a{};   // P[b] = 2 A_b^T A_b (upper tiles) for token slice b
+      a.M = d; a.N = d; a.K = c;
+      a.A = A; a.lda = d; a.transA = 1;
+      a.B = A; a.ldb = d; a.transB = 0;
+      a.C = P; a.ldc = d;
+      a.alpha = 2.0f; a.beta = 0.0f; a.tri = 2;
+      a.batch = S; a.sA = c * d; a.sB = c * d; a.sC = d * d;
+      GPTQ_TRY(gemm_f32(a, s));
+      hipLaunchKernelGGL(sum_upper_kernel, dim3(grid_for(d * d)), dim3(256), 0, s, P, S, d, H);
+      GPTQ_TRY(hipGetLastError());
+    }
     if (hess && hess[si]) GPTQ_TRY(hipMemcpyAsync(hess[si], H, (size_t)d * d * 4, hipMemcpyDeviceToDevice, s));
     int64_t piv = 0;
     st = gptq_factor(H, d, n, &p, U, layers[first].perm, work + L.off_fw, L.factor_bytes, &piv, s);

@@ -105,6 +105,8 @@ GPTQ_DEV float row_ror15(float v) {
 // C[M x N] = alpha * op(A) * op(B) + beta * C, row-major fp32, on MFMA.
 // op(A) is A (M x K, lda) or A^T (A stored K x M); op(B) is B (K x N, ldb) or B^T (B stored N x K).
 // tri: 0 every element, 1 only elements with m >= n, 2 only m <= n.
+// lowerA: op(A) is lower triangular (zero for k > m), so a row tile stops its k loop at its last row.
+// batch > 1: `batch` products, the b-th on A + b sA, B + b sB, C + b sC (0 and 1 mean one product).
 // beta == 0 never reads C. C must not overlap A or B: several workgroups can share one output
 // strip, and one may store while another still reads its operand.
 struct GemmArgs {
@@ -114,6 +116,8 @@ struct GemmArgs {
   float* C; int64_t ldc;
   float alpha, beta;
   int tri;
+  int lowerA;
+  int64_t batch, sA, sB, sC;
 };
 hipError_t gemm_f32(const GemmArgs& a, hipStream_t s);
 
@@ -175,7 +179,7 @@ hipError_t dequantize(const uint8_t* codes, int64_t rows, int64_t d, const float
 // Row-wise x / sqrt(mean(x^2) + eps).
 hipError_t rmsnorm(const float* x, int64_t m, int64_t d, int64_t ldx, float eps, float* y, int64_t ldy, hipStream_t s);
 // Multi-head causal attention over seqs sequences of L tokens; Q, K, V, O are [seqs L x heads dh]
-// (leading dimensions ld, ld, ld, ldo); S is L x L fp32 scratch.
+// (leading dimensions ld, ld, ld, ldo); S is heads x L x L fp32 scratch.
 hipError_t causal_attention(const float* Q, const float* K, const float* V, int64_t seqs, int64_t L, int64_t heads,
                             int64_t dh, int64_t ld, float* O, int64_t ldo, float* S, hipStream_t s);
 // y = silu(g) * u elementwise; y may be g.
@@ -183,10 +187,11 @@ hipError_t silu_mul(const float* g, const float* u, int64_t n, float* y, hipStre
 hipError_t to_f32(const void* x, int dtype, int64_t n, float* y, hipStream_t s);
 
 // Workspace of gptq_quantize_block: byte offsets of the fp32 activations, one dense weight, the
-// stage Hessian and factor, and the factor and column-loop workspaces.
+// stage Hessian, its partial sums over token slices and factor, and the factor and column-loop
+// workspaces.
 struct BlockLayout {
   size_t off_xf, off_xa, off_q, off_k, off_v, off_at, off_h1, off_xm, off_g, off_u, off_s, off_wf, off_h, off_uf,
-      off_fw, off_qw, factor_bytes, quant_bytes, total;
+      off_hp, off_fw, off_qw, factor_bytes, quant_bytes, total;
 };
 BlockLayout block_layout(const gptq_block_shape_t& sh, const gptq_params_t& p);
 int quantize_block(const gptq_block_shape_t& sh, const void* X, int x_dtype, const gptq_params_t& p,

@@ -121,6 +121,11 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmArgs a, int64_t tiles
   if (a.tri == 0) { tm = blockIdx.x / tiles_n; tn = blockIdx.x % tiles_n; }
   else tri_tile(blockIdx.x, tiles_n, a.tri == 1, tm, tn);
   const int64_t m0 = tm * T, n0 = tn * T;
+  if (blockIdx.y > 0) {
+    a.A += (int64_t)blockIdx.y * a.sA;
+    a.B += (int64_t)blockIdx.y * a.sB;
+    a.C += (int64_t)blockIdx.y * a.sC;
+  }
 
   using SA = Stage<T, AK>;
   using SB = Stage<T, BK>;
@@ -142,7 +147,9 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmArgs a, int64_t tiles
 
   Loader<T, AK> la;
   Loader<T, BK> lb;
-  const int64_t nk = (a.K + GK - 1) / GK;
+  // a lower-triangular A is zero past the tile's last row (T is a multiple of GK)
+  const int64_t kend = a.lowerA ? std::min<int64_t>(a.K, m0 + T) : a.K;
+  const int64_t nk = (kend + GK - 1) / GK;
   if (nk > 0) {
     la.load(a.A, a.lda, m0, a.M, 0, a.K, vecA, tid);
     lb.load(a.B, a.ldb, n0, a.N, 0, a.K, vecB, tid);
@@ -237,9 +244,11 @@ hipError_t launch(const GemmArgs& a, hipStream_t s) {
     // square triangle of tiles (M == N for the symmetric products)
     tiles = tiles_n * (tiles_n + 1) / 2;
   }
-  const dim3 grid((unsigned)tiles);
+  const unsigned nb = a.batch > 1 ? (unsigned)a.batch : 1u;
+  const dim3 grid((unsigned)tiles, nb);
   // op(A) has k contiguous when A is not transposed; op(B) has k contiguous when B is transposed.
-  const int vecA = aligned16(a.A, a.lda), vecB = aligned16(a.B, a.ldb);
+  const int vecA = aligned16(a.A, a.lda) && (nb == 1 || a.sA % 4 == 0);
+  const int vecB = aligned16(a.B, a.ldb) && (nb == 1 || a.sB % 4 == 0);
   if (!a.transA && !a.transB)
     hipLaunchKernelGGL((gemm_f32_kernel<T, true, false>), grid, dim3(256), 0, s, a, tn_arg, vecA, vecB);
   else if (!a.transA && a.transB)
@@ -256,11 +265,13 @@ hipError_t launch(const GemmArgs& a, hipStream_t s) {
 hipError_t gemm_f32(const GemmArgs& a, hipStream_t s) {
   if (a.M <= 0 || a.N <= 0) return hipSuccess;
   if (a.tri != 0 && a.M != a.N) return hipErrorInvalidValue;
+  if (a.batch > 65535) return hipErrorInvalidValue;
+  if (a.lowerA && a.transA) return hipErrorInvalidValue;
   // 128 x 128 tiles do more work per byte staged but run two to a CU (512 at a time on 256 CUs), so
   // they pay off when their count fills those slots evenly, or when there are so many that the last
   // partial round hardly matters; otherwise 64 x 64 tiles (four times as many workgroups) balance
   // better. Measured on the solver's shapes (fp32, K = 128 and 512).
-  const int64_t t128 = ((a.M + 127) / 128) * ((a.N + 127) / 128) / (a.tri ? 2 : 1);
+  const int64_t t128 = ((a.M + 127) / 128) * ((a.N + 127) / 128) / (a.tri ? 2 : 1) * std::max<int64_t>(a.batch, 1);
   if (t128 >= 4096 || (t128 >= 512 && t128 % 256 == 0)) return launch<128>(a, s);
   return launch<64>(a, s);
 }

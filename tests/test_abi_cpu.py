@@ -243,11 +243,12 @@ def test_block_structs_and_workspace():
     sh = L.gptq_block_shape_t(256, 4, 688, 4, 200, 1e-6)
     n = 800
     w = lib.gptq_block_workspace_bytes(ctypes.byref(sh), ctypes.byref(p))
-    acts = (8 * n * 256 + 2 * n * 688 + 200 * 200 + 688 * 256 + 2 * 688 * 688) * 4
+    acts = (8 * n * 256 + 2 * n * 688 + 4 * 200 * 200 + 688 * 256 + 2 * 688 * 688) * 4
     assert w >= acts
     for bad in (L.gptq_block_shape_t(256, 3, 688, 4, 200, 1e-6), L.gptq_block_shape_t(4, 1, 688, 4, 200, 1e-6),
                 L.gptq_block_shape_t(256, 4, 688, 0, 200, 1e-6), L.gptq_block_shape_t(256, 4, 688, 4, 200, -1.0),
-                L.gptq_block_shape_t(256, 4, 688, 4, 200, float("nan"))):
+                L.gptq_block_shape_t(256, 4, 688, 4, 200, float("nan")), L.gptq_block_shape_t(2 ** 17, 2 ** 16, 688, 1, 2, 0),
+                L.gptq_block_shape_t(256, 256, 688, 1, 2 ** 24, 0)):
         assert lib.gptq_block_workspace_bytes(ctypes.byref(bad), ctypes.byref(p)) == 0
     assert lib.gptq_block_workspace_bytes(ctypes.byref(sh), None) == 0
     assert lib.gptq_block_workspace_bytes(ctypes.byref(sh), ctypes.byref(_p(L, block_size=129))) == 0

@@ -11,8 +11,9 @@ original weights. Then:
   within 1e-5 relative, loss within 1e-3 relative; the processing order checked against diag(H));
 * the block output matches the oracle's forward pass through the GPU's quantized weights within
   1e-5 relative (Frobenius) and 1e-4 of max |Y| elementwise.
-Shapes are ragged against every tile (hidden 256 and 192, MLP width 688 and 520, 800 and 450 tokens,
-sequence lengths 200 and 150) and cover fp16, bf16 and fp32 storage.
+Shapes are ragged against every tile (hidden 256, 192 and 120, MLP width 688, 520 and 200, sequence
+lengths 200, 150 and 70), cover fp16, bf16 and fp32 storage, head widths 64, 30 and 8, and one
+2048-token sequence of 32 heads whose attention products run on the 128-wide tiles.
 """
 
 import numpy as np
@@ -28,12 +29,18 @@ pytestmark = pytest.mark.gpu
 
 MAIN = synth.BlockCase(hidden=256, heads=4, inter=688, seqs=4, seq_len=200)
 ROWWISE = synth.BlockCase(hidden=192, heads=3, inter=520, seqs=3, seq_len=150, w_dtype="bf16", x_dtype="f32")
+# 30-wide heads: head offsets not 16-byte aligned (scalar operand loads in the batched products)
+ODD_HEADS = synth.BlockCase(hidden=120, heads=4, inter=200, seqs=2, seq_len=70)
+# 32 heads of 2048 tokens: the attention products take 128-wide tiles, as at the Llama-7B shape
+LONG = synth.BlockCase(hidden=256, heads=32, inter=688, seqs=1, seq_len=2048)
 
 CASES = [
     ("g128", MAIN, dict(bits=4, group_size=128, act_order=False), True),
     ("g128-act", MAIN, dict(bits=4, group_size=128, act_order=True), True),
     ("g128-act-float-inputs", MAIN, dict(bits=4, group_size=128, act_order=True), False),
     ("3bit-per-row", ROWWISE, dict(bits=3, group_size=0, act_order=True), True),
+    ("odd-head-width", ODD_HEADS, dict(bits=4, group_size=32, act_order=False), True),
+    ("long-sequence-many-heads", LONG, dict(bits=4, group_size=128, act_order=True), True),
 ]
 
 
