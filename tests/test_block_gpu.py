@@ -109,3 +109,88 @@ def test_first_stage_does_not_depend_on_the_mode():
             assert np.array_equal(a[i][key], b[i][key]), (i, key)
     # later stages see different inputs in the two modes
     assert not np.array_equal(np.triu(ha[1]), np.triu(hb[1]))
+
+
+# ------------------------------------------------------------------ the Llama-7B block at full size
+
+def test_llama7b_block_full_size():
+    """The benchmarked solve itself: the Llama-7B-shaped block (q/k/v/o 4096^2, gate/up 11008x4096,
+    down 4096x11008, 128 x 2048 tokens, 4-bit g128 act-order) on the same seeded inputs and in the
+    same call as bench.py --block. Checked where the oracle can reach at this size:
+    * stage 0's Hessian on sampled entries (its input, RMSNorm(X), is cheap to form for every token),
+      within the float32 summation bound over one token slice plus the input's rounding;
+    * q and down (stages 0 and 3, widths 4096 and 11008): the oracle's factor of the GPU's Hessian,
+      sampled rows of the column loop to the layer bar, and the reported loss against the damped
+      quadratic form of the whole dequantized layer;
+    * the block output of the first sequence (2048 tokens, every head), against the oracle's forward
+      pass through all seven of the GPU's quantized layers."""
+    import types
+    from test_fullsize_gpu import _check_loss_identity, _check_rows
+
+    torch = torch_cuda()
+    import post_weight_quantization_20_amd as g
+    case = synth.BlockCase(hidden=4096, heads=32, inter=11008, seqs=128, seq_len=2048)
+    seed = 500
+    print("[block full] generating", flush=True)
+    W_host = synth.block_weights(case, seed)
+    X_host = synth.block_x(case, seed)
+    shape = g.BlockShape(case.hidden, case.heads, case.inter, case.seqs, case.seq_len, 1e-6)
+    params = g.Params(bits=4, group_size=128, block_size=128, act_order=True, damp=0.01)
+    print("[block full] GPU solve", flush=True)
+    r = g.gptq_quantize_block(dev_tensor(X_host, "f16"), [dev_tensor(w, "f16") for w in W_host], shape, params,
+                              true_sequential=True, return_hessians=True)
+    torch.cuda.synchronize()
+    L = case.seq_len
+    outs = [dict(codes=q.codes.cpu().numpy(), scales=q.scales.cpu().numpy(), zeros=q.zeros.cpu().numpy(),
+                 g_idx=q.g_idx.cpu().numpy(), loss=float(q.loss.cpu().numpy()[0]), packed=None,
+                 perm=p.cpu().numpy().astype(np.int64)) for q, p in zip(r.layers, r.perms)]
+    Y0 = r.Y[:L].cpu().numpy().astype(np.float64)
+    H0, H3 = r.hessians[0].cpu().numpy(), r.hessians[3].cpu().numpy()
+    del r
+    torch.cuda.empty_cache()
+    n = case.seqs * L
+    rng = np.random.default_rng(7)
+
+    # stage 0 Hessian on sampled entries: a = X / rms(X) per token
+    print("[block full] stage 0 Hessian entries", flush=True)
+    cols = np.unique(np.concatenate([rng.choice(case.hidden, 12, replace=False),
+                                     np.argsort(-np.abs(synth.to_f64(X_host[:64], "f16")).max(0))[:4]]))
+    A = np.empty((n, cols.size))
+    for t0 in range(0, n, 16384):
+        x = synth.to_f64(X_host[t0:t0 + 16384], "f16")
+        A[t0:t0 + 16384] = x[:, cols] / np.sqrt(np.mean(x * x, axis=1, keepdims=True) + 1e-6)
+    want = 2.0 * A.T @ A
+    absw = 2.0 * np.abs(A).T @ np.abs(A)
+    S = 8                                           # token slices of the 4096-wide Hessian
+    U32 = 2.0 ** -24
+    bound = (n // S + S) * U32 * absw + 1e-5 * np.sqrt(np.outer(np.diag(want), np.diag(want)))
+    got = _sym(H0)[np.ix_(cols, cols)]
+    assert np.all(np.abs(got - want) <= bound), float(np.max(np.abs(got - want) / bound))
+    print(f"[block full] max |dH|/bound {float(np.max(np.abs(got - want) / bound)):.3f}", flush=True)
+    del A
+
+    # q (stage 0) and down (stage 3): oracle factor of the GPU's Hessian, sampled rows, loss
+    for li, Hu in ((0, H0), (6, H3)):
+        rows_l, d = synth.block_layer_dims(case, li)
+        lc = types.SimpleNamespace(bits=4, group_size=128, block_size=128, w_dtype="f16", rows=rows_l, d=d)
+        Hs = _sym(Hu)
+        perm = _checked_perm(outs[li]["perm"], Hs)
+        Hh, perm, lam = ref.damp_and_order(Hs, n, 0.01, True, perm=perm)
+        print(f"[block full] oracle factor d={d}", flush=True)
+        Uo = ref.inverse_cholesky_upper(Hh)
+        rows = np.unique(np.concatenate([np.arange(8), rng.choice(rows_l, 16, replace=False),
+                                         np.arange(rows_l - 8, rows_l)]))
+        print(f"[block full] layer {blk.LAYERS[li]}: sampled rows and loss", flush=True)
+        _check_rows(lc, W_host[li], outs[li], Hh, Uo, perm, rows)
+        _check_loss_identity(lc, W_host[li], outs[li], Hh, perm)
+        del Hs, Hh, Uo
+
+    # the first sequence's block output through the GPU's quantized layers
+    print("[block full] oracle forward of sequence 0", flush=True)
+    Qg = [dequant(o["codes"], o["scales"], o["zeros"], o["g_idx"]) for o in outs]
+    sh = blk.BlockShape(case.hidden, case.heads, case.inter, 1, L, 1e-6)
+    want_y = blk.forward(synth.to_f64(X_host[:L], "f16"), Qg, sh)["out"]
+    dy = Y0 - want_y
+    fro, mx = np.linalg.norm(dy) / np.linalg.norm(want_y), np.max(np.abs(dy)) / np.max(np.abs(want_y))
+    print(f"[block full] output: Frobenius {fro:.2e}, max {mx:.2e}", flush=True)
+    assert fro <= 1e-5 and mx <= 1e-4
