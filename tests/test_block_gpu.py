@@ -41,6 +41,8 @@ CASES = [
     ("3bit-per-row", ROWWISE, dict(bits=3, group_size=0, act_order=True), True),
     ("odd-head-width", ODD_HEADS, dict(bits=4, group_size=32, act_order=False), True),
     ("long-sequence-many-heads", LONG, dict(bits=4, group_size=128, act_order=True), True),
+    ("sym-static-compact", MAIN, dict(bits=4, group_size=128, act_order=True, sym=True, static_groups=True,
+                                      compact_meta=True), True),
 ]
 
 
@@ -88,8 +90,12 @@ def test_block_parity(name, case, pkw, ts):
             gl = layers[i]
             assert np.array_equal(gl["perm"], layers[members[0]]["perm"])
             perm = _checked_perm(gl["perm"], got) if pkw["act_order"] else None
+            follow = (gl["codes"][:, gl["perm"]], gl["zeros"])
+            if pkw.get("compact_meta"):
+                follow = follow + (gl["scales"],)
             o = ref.gptq(W64[i], None, pkw["bits"], pkw["group_size"], 128, act_order=pkw["act_order"], damp=0.01,
-                         perm=perm, follow=(gl["codes"][:, gl["perm"]], gl["zeros"]), H=got, n=n)
+                         perm=perm, follow=follow, H=got, n=n, sym=pkw.get("sym", False),
+                         static_groups=pkw.get("static_groups", False), compact=pkw.get("compact_meta", False))
             check_quant_parity(gl, o.quant)
     want_y = blk.forward(X64, Qg, sh)["out"]
     dy = Y.astype(np.float64) - want_y
