@@ -100,15 +100,31 @@ __global__ __launch_bounds__(256) void to_f32_kernel(const void* __restrict__ x,
     y[e] = load_as_f32(x, dtype, e);
 }
 
-// H[r, c] = sum over b < S of P[b][r, c] on and above the diagonal (a fixed order), 0 below.
-__global__ __launch_bounds__(256) void sum_upper_kernel(const float* __restrict__ P, int S, int64_t d,
-                                                        float* __restrict__ H) {
-  const int64_t total = d * d;
+// X[t] = [hi(A[t]) | lo(A[t])] for each token row t of A [n x d]: hi = fp16(a), lo = fp16(a - hi), so
+// hi + lo = a to within 2^-22 |a| (or 2^-25 where lo is an fp16 subnormal). |a| must stay below the
+// fp16 maximum, 65504.
+__global__ __launch_bounds__(256) void split_f16_kernel(const float* __restrict__ A, int64_t n, int64_t d,
+                                                        _Float16* __restrict__ X) {
+  const int64_t total = n * d;
   for (int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x; e < total; e += (int64_t)gridDim.x * 256) {
-    const int64_t r = e / d, c = e - r * d;
+    const int64_t t = e / d, k = e - t * d;
+    const float a = A[e];
+    const _Float16 hi = (_Float16)a;
+    X[t * 2 * d + k] = hi;
+    X[t * 2 * d + d + k] = (_Float16)(a - (float)hi);
+  }
+}
+
+// H = hi^T hi + hi^T lo + lo^T hi + lo^T lo from the upper triangle of the 2d x 2d H2 of [hi | lo]:
+// H[i, j] = H2[i, j] + H2[i, d + j] + H2[j, d + i] + H2[d + i, d + j] for i <= j (all four entries lie
+// on or above H2's diagonal), in that order; 0 below the diagonal.
+__global__ __launch_bounds__(256) void fold_split_kernel(const float* __restrict__ H2, int64_t d,
+                                                         float* __restrict__ H) {
+  const int64_t total = d * d, l2 = 2 * d;
+  for (int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x; e < total; e += (int64_t)gridDim.x * 256) {
+    const int64_t i = e / d, j = e - i * d;
     float v = 0.0f;
-    if (c >= r)
-      for (int b = 0; b < S; ++b) v += P[b * total + e];
+    if (j >= i) v = ((H2[i * l2 + j] + H2[i * l2 + d + j]) + H2[j * l2 + d + i]) + H2[(d + i) * l2 + d + j];
     H[e] = v;
   }
 }
@@ -179,17 +195,6 @@ namespace {
 
 size_t up256(size_t b) { return (b + 255) & ~(size_t)255; }
 
-// Token splits of a stage Hessian: one pass of 2 A^T A over n tokens gives ceil(d/128) (ceil(d/128)
-// + 1) / 2 long-running 128-wide tiles, too few to fill 256 CUs evenly at d = 4096 (528 tiles: one
-// full round and a second one for 16). S equal slices of the tokens (S | n, at least 32 tokens
-// each, S <= 8) run as one batched product into S partial sums until there are >= 4096 tiles.
-int hess_split(int64_t d, int64_t n) {
-  const int64_t t = ((d + 127) / 128) * ((d + 127) / 128 + 1) / 2;
-  int S = 1;
-  while (S < 8 && t * S < 4096 && n % (2 * S) == 0 && n / (2 * S) >= 32) S *= 2;
-  return S;
-}
-
 // Layer i of the block (q, k, v, o, gate, up, down): output features and input features.
 void layer_dims(const gptq_block_shape_t& sh, int i, int64_t& rows, int64_t& d) {
   rows = (i == 4 || i == 5) ? sh.inter : sh.hidden;
@@ -222,12 +227,11 @@ BlockLayout block_layout(const gptq_block_shape_t& sh, const gptq_params_t& p) {
   L.off_wf = take((size_t)di * hd * 4);
   L.off_h = take((size_t)dm * dm * 4);
   L.off_uf = take((size_t)dm * dm * 4);
-  size_t part = 0;
-  for (int64_t d : {hd, di}) {
-    const int S = hess_split(d, n);
-    if (S > 1) part = std::max(part, (size_t)S * d * d * 4);
-  }
-  L.off_hp = take(part);
+  L.off_xs = take((size_t)n * dm * 4);             // n x 2 dm fp16
+  L.off_h2 = take((size_t)4 * dm * dm * 4);         // 2 dm x 2 dm fp32
+  L.hess_bytes = std::max(gptq_workspace_bytes(GPTQ_WS_HESSIAN, n, 2 * hd, nullptr),
+                          gptq_workspace_bytes(GPTQ_WS_HESSIAN, n, 2 * di, nullptr));
+  L.off_hw = take(L.hess_bytes);
   L.factor_bytes = gptq_workspace_bytes(GPTQ_WS_FACTOR, 0, dm, &p);
   L.off_fw = take(L.factor_bytes);
   L.quant_bytes = 0;
@@ -273,25 +277,18 @@ int quantize_block(const gptq_block_shape_t& sh, const void* X, int x_dtype, con
 
   // H of one stage input A [n x d], then U, the order and the column loop of every layer reading A
   auto stage = [&](int si, const float* A, int64_t d, int first, int last) -> int {
+    // H = 2 A^T A on the fp16 MFMA: A split into fp16 halves, H2 = 2 [hi | lo]^T [hi | lo], folded
     int st;
-    const int S = hess_split(d, n);
-    if (S == 1) {
-      GPTQ_TRY(hipMemsetAsync(H, 0, (size_t)d * d * 4, s));
-      if ((st = gptq_hessian_accumulate(H, d, A, GPTQ_F32, n, d, nullptr, 0, s)) != GPTQ_OK) return st;
-    } else {
-      float* P = reinterpret_cast<float*>(work + L.off_hp);
-      const int64_t c = n / S;
-      GemmArgs a{};   // P[b] = 2 A_b^T A_b (upper tiles) for token slice b
-      a.M = d; a.N = d; a.K = c;
-      a.A = A; a.lda = d; a.transA = 1;
-      a.B = A; a.ldb = d; a.transB = 0;
-      a.C = P; a.ldc = d;
-      a.alpha = 2.0f; a.beta = 0.0f; a.tri = 2;
-      a.batch = S; a.sA = c * d; a.sB = c * d; a.sC = d * d;
-      GPTQ_TRY(gemm_f32(a, s));
-      hipLaunchKernelGGL(sum_upper_kernel, dim3(grid_for(d * d)), dim3(256), 0, s, P, S, d, H);
-      GPTQ_TRY(hipGetLastError());
-    }
+    _Float16* Xs = reinterpret_cast<_Float16*>(work + L.off_xs);
+    float* H2 = reinterpret_cast<float*>(work + L.off_h2);
+    hipLaunchKernelGGL(split_f16_kernel, dim3(grid_for(n * d)), dim3(256), 0, s, A, n, d, Xs);
+    GPTQ_TRY(hipGetLastError());
+    GPTQ_TRY(hipMemsetAsync(H2, 0, (size_t)4 * d * d * 4, s));
+    if ((st = gptq_hessian_accumulate(H2, 2 * d, Xs, GPTQ_F16, n, 2 * d, work + L.off_hw, L.hess_bytes, s)) !=
+        GPTQ_OK)
+      return st;
+    hipLaunchKernelGGL(fold_split_kernel, dim3(grid_for(d * d)), dim3(256), 0, s, H2, d, H);
+    GPTQ_TRY(hipGetLastError());
     if (hess && hess[si]) GPTQ_TRY(hipMemcpyAsync(hess[si], H, (size_t)d * d * 4, hipMemcpyDeviceToDevice, s));
     int64_t piv = 0;
     st = gptq_factor(H, d, n, &p, U, layers[first].perm, work + L.off_fw, L.factor_bytes, &piv, s);

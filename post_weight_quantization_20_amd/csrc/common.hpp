@@ -187,11 +187,11 @@ hipError_t silu_mul(const float* g, const float* u, int64_t n, float* y, hipStre
 hipError_t to_f32(const void* x, int dtype, int64_t n, float* y, hipStream_t s);
 
 // Workspace of gptq_quantize_block: byte offsets of the fp32 activations, one dense weight, the
-// stage Hessian, its partial sums over token slices and factor, and the factor and column-loop
-// workspaces.
+// stage Hessian (with the fp16 halves of its input and their 2d-wide Hessian) and factor, and the
+// Hessian, factor and column-loop workspaces.
 struct BlockLayout {
   size_t off_xf, off_xa, off_q, off_k, off_v, off_at, off_h1, off_xm, off_g, off_u, off_s, off_wf, off_h, off_uf,
-      off_hp, off_fw, off_qw, factor_bytes, quant_bytes, total;
+      off_xs, off_h2, off_hw, off_fw, off_qw, hess_bytes, factor_bytes, quant_bytes, total;
 };
 BlockLayout block_layout(const gptq_block_shape_t& sh, const gptq_params_t& p);
 int quantize_block(const gptq_block_shape_t& sh, const void* X, int x_dtype, const gptq_params_t& p,
