@@ -305,10 +305,11 @@ size_t gptq_block_workspace_bytes(const gptq_block_shape_t *shape, const gptq_pa
  * Each stage forms H = 2 A^T A over all tokens, factors it once (gptq_factor) and runs
  * gptq_quantize_layer for each of its layers with that factor and order. With true_sequential = 0
  * every stage input comes from the block with its original weights (the layers are solved from
- * one unquantized forward pass). Activations are fp32; a stage's H is formed on the fp16 matrix
- * cores from the input split into two fp16 halves (hi + lo equals it to within 2^-22 relative), so
- * stage inputs must stay below 65504 in magnitude (beyond it H is not finite and the stage's
- * factor fails).
+ * one unquantized forward pass). Activations are fp32. The projections and each stage's H run on
+ * the fp16 matrix cores from operands split into two fp16 halves (hi + lo equals an fp32 value to
+ * within 2^-22 relative; weights are scaled by a power of two first), which matches fp32 products
+ * to within about their inputs' rounding. Stage inputs must stay below 65504 in magnitude (beyond
+ * it H is not finite and the stage's factor fails).
  *
  *   shape   the block and calibration sizes (n = seqs * seq_len tokens).
  *   X       device [n x hidden] of x_dtype, token-major, sequence after sequence. Not modified.

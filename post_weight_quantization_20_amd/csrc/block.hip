@@ -100,21 +100,6 @@ __global__ __launch_bounds__(256) void to_f32_kernel(const void* __restrict__ x,
     y[e] = load_as_f32(x, dtype, e);
 }
 
-// X[t] = [hi(A[t]) | lo(A[t])] for each token row t of A [n x d]: hi = fp16(a), lo = fp16(a - hi), so
-// hi + lo = a to within 2^-22 |a| (or 2^-25 where lo is an fp16 subnormal). |a| must stay below the
-// fp16 maximum, 65504.
-__global__ __launch_bounds__(256) void split_f16_kernel(const float* __restrict__ A, int64_t n, int64_t d,
-                                                        _Float16* __restrict__ X) {
-  const int64_t total = n * d;
-  for (int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x; e < total; e += (int64_t)gridDim.x * 256) {
-    const int64_t t = e / d, k = e - t * d;
-    const float a = A[e];
-    const _Float16 hi = (_Float16)a;
-    X[t * 2 * d + k] = hi;
-    X[t * 2 * d + d + k] = (_Float16)(a - (float)hi);
-  }
-}
-
 // H = hi^T hi + hi^T lo + lo^T hi + lo^T lo from the upper triangle of the 2d x 2d H2 of [hi | lo]:
 // H[i, j] = H2[i, j] + H2[i, d + j] + H2[j, d + i] + H2[d + i, d + j] for i <= j (all four entries lie
 // on or above H2's diagonal), in that order; 0 below the diagonal.
@@ -227,8 +212,16 @@ BlockLayout block_layout(const gptq_block_shape_t& sh, const gptq_params_t& p) {
   L.off_wf = take((size_t)di * hd * 4);
   L.off_h = take((size_t)dm * dm * 4);
   L.off_uf = take((size_t)dm * dm * 4);
-  L.off_xs = take((size_t)n * dm * 4);             // n x 2 dm fp16
-  L.off_h2 = take((size_t)4 * dm * dm * 4);         // 2 dm x 2 dm fp32
+  L.off_xs = take((size_t)n * split3_pitch(dm) * 2);   // a stage input as fp16 [hi | hi | lo | 0]
+  size_t w3 = 0;
+  for (int i = 0; i < 7; ++i) {
+    int64_t rows, d;
+    layer_dims(sh, i, rows, d);
+    w3 = std::max(w3, (size_t)rows * split3_pitch(d) * 2);
+  }
+  L.off_w3 = take(w3);                                  // a weight as fp16 [hi | lo | hi | 0]
+  L.off_mx = take((size_t)(kAbsmaxParts + 1) * 4);
+  L.off_h2 = take((size_t)4 * dm * dm * 4);             // 2 dm x 2 dm fp32
   L.hess_bytes = std::max(gptq_workspace_bytes(GPTQ_WS_HESSIAN, n, 2 * hd, nullptr),
                           gptq_workspace_bytes(GPTQ_WS_HESSIAN, n, 2 * di, nullptr));
   L.off_hw = take(L.hess_bytes);
@@ -275,17 +268,17 @@ int quantize_block(const gptq_block_shape_t& sh, const void* X, int x_dtype, con
     if ((x) != hipSuccess) return GPTQ_EHIP;          \
   } while (0)
 
-  // H of one stage input A [n x d], then U, the order and the column loop of every layer reading A
-  auto stage = [&](int si, const float* A, int64_t d, int first, int last) -> int {
-    // H = 2 A^T A on the fp16 MFMA: A split into fp16 halves, H2 = 2 [hi | lo]^T [hi | lo], folded
+  // H of the stage input (already split), then U, the order and the column loop of every layer
+  // reading it
+  auto stage = [&](int si, int64_t d, int first, int last) -> int {
+    // H = 2 A^T A on the fp16 MFMA: H2 = 2 [hi | lo]^T [hi | lo] from the split input (its columns
+    // d .. 3d - 1), folded
     int st;
-    _Float16* Xs = reinterpret_cast<_Float16*>(work + L.off_xs);
+    const _Float16* Xs = reinterpret_cast<const _Float16*>(work + L.off_xs) + d;
     float* H2 = reinterpret_cast<float*>(work + L.off_h2);
-    hipLaunchKernelGGL(split_f16_kernel, dim3(grid_for(n * d)), dim3(256), 0, s, A, n, d, Xs);
-    GPTQ_TRY(hipGetLastError());
     GPTQ_TRY(hipMemsetAsync(H2, 0, (size_t)4 * d * d * 4, s));
-    if ((st = gptq_hessian_accumulate(H2, 2 * d, Xs, GPTQ_F16, n, 2 * d, work + L.off_hw, L.hess_bytes, s)) !=
-        GPTQ_OK)
+    if ((st = gptq_hessian_accumulate(H2, 2 * d, Xs, GPTQ_F16, n, split3_pitch(d), work + L.off_hw, L.hess_bytes,
+                                      s)) != GPTQ_OK)
       return st;
     hipLaunchKernelGGL(fold_split_kernel, dim3(grid_for(d * d)), dim3(256), 0, s, H2, d, H);
     GPTQ_TRY(hipGetLastError());
@@ -317,40 +310,58 @@ int quantize_block(const gptq_block_shape_t& sh, const void* X, int x_dtype, con
     const int64_t g = p.group_size <= 0 ? d : p.group_size;
     return dequantize(layers[i].codes, rows, d, layers[i].scales, layers[i].zeros, layers[i].g_idx, g, Wf, d, s);
   };
-  // out = in W_i^T (+ out when accumulate)
-  auto project = [&](int i, bool quantized, const float* in, float* out, bool accumulate) -> hipError_t {
+  // the current input A [n x d] as fp16 [hi | hi | lo | 0]
+  auto split_input = [&](const float* A, int64_t d) -> hipError_t {
+    return split3(A, n, d, d, 1.0f, 1, reinterpret_cast<_Float16*>(work + L.off_xs), s);
+  };
+  // out = A W_i^T (+ out when accumulate) for the split input A: W_i scaled by 2^k (max |2^k W_i| in
+  // [2^14, 2^15), so its lo parts stay normal fp16) and split, one fp16 GEMM over 3d, alpha = 2^-k
+  float* mx = reinterpret_cast<float*>(work + L.off_mx);
+  auto project = [&](int i, bool quantized, float* out, bool accumulate) -> int {
     int64_t rows, d;
     layer_dims(sh, i, rows, d);
-    hipError_t e = weight(i, quantized);
-    if (e != hipSuccess) return e;
-    GemmArgs a{};
-    a.M = n; a.N = rows; a.K = d;
-    a.A = in; a.lda = d; a.transA = 0;
-    a.B = Wf; a.ldb = d; a.transB = 1;
+    GPTQ_TRY(weight(i, quantized));
+    GPTQ_TRY(absmax(Wf, rows * d, mx + 1, mx, s));
+    float wmax = 0.0f;
+    GPTQ_TRY(hipMemcpyAsync(&wmax, mx, 4, hipMemcpyDeviceToHost, s));
+    GPTQ_TRY(hipStreamSynchronize(s));
+    int k = 0;
+    if (wmax > 0.0f && std::isfinite(wmax)) k = std::min(100, std::max(-100, 14 - std::ilogb(wmax)));
+    _Float16* W3 = reinterpret_cast<_Float16*>(work + L.off_w3);
+    GPTQ_TRY(split3(Wf, rows, d, d, std::ldexp(1.0f, k), 0, W3, s));
+    GemmF16 a{};
+    a.M = n; a.N = rows; a.K = split3_pitch(d);
+    a.A = reinterpret_cast<const _Float16*>(work + L.off_xs); a.lda = a.K;
+    a.B = W3; a.ldb = a.K;
     a.C = out; a.ldc = rows;
-    a.alpha = 1.0f; a.beta = accumulate ? 1.0f : 0.0f; a.tri = 0;
-    return gemm_f32(a, s);
+    a.alpha = std::ldexp(1.0f, -k); a.beta = accumulate ? 1.0f : 0.0f;
+    GPTQ_TRY(gemm_f16nt(a, s));
+    return GPTQ_OK;
   };
   // one pass over the block; quantize: run each stage's solve before its layers are used
   auto pass = [&](bool quantized, bool quantize) -> int {
     int st;
     GPTQ_TRY(rmsnorm(xf, n, hd, hd, eps, xa, hd, s));
-    if (quantize && (st = stage(0, xa, hd, 0, 2)) != GPTQ_OK) return st;
-    GPTQ_TRY(project(0, quantized, xa, q, false));
-    GPTQ_TRY(project(1, quantized, xa, k, false));
-    GPTQ_TRY(project(2, quantized, xa, v, false));
+    GPTQ_TRY(split_input(xa, hd));
+    if (quantize && (st = stage(0, hd, 0, 2)) != GPTQ_OK) return st;
+    if ((st = project(0, quantized, q, false)) != GPTQ_OK) return st;
+    if ((st = project(1, quantized, k, false)) != GPTQ_OK) return st;
+    if ((st = project(2, quantized, v, false)) != GPTQ_OK) return st;
     GPTQ_TRY(causal_attention(q, k, v, sh.seqs, sh.seq_len, sh.heads, hd / sh.heads, hd, at, hd, S, s));
-    if (quantize && (st = stage(1, at, hd, 3, 3)) != GPTQ_OK) return st;
+    GPTQ_TRY(split_input(at, hd));
+    if (quantize && (st = stage(1, hd, 3, 3)) != GPTQ_OK) return st;
     GPTQ_TRY(hipMemcpyAsync(h1, xf, (size_t)n * hd * 4, hipMemcpyDeviceToDevice, s));
-    GPTQ_TRY(project(3, quantized, at, h1, true));
+    if ((st = project(3, quantized, h1, true)) != GPTQ_OK) return st;
     GPTQ_TRY(rmsnorm(h1, n, hd, hd, eps, xm, hd, s));
-    if (quantize && (st = stage(2, xm, hd, 4, 5)) != GPTQ_OK) return st;
-    GPTQ_TRY(project(4, quantized, xm, gb, false));
-    GPTQ_TRY(project(5, quantized, xm, ub, false));
+    GPTQ_TRY(split_input(xm, hd));
+    if (quantize && (st = stage(2, hd, 4, 5)) != GPTQ_OK) return st;
+    if ((st = project(4, quantized, gb, false)) != GPTQ_OK) return st;
+    if ((st = project(5, quantized, ub, false)) != GPTQ_OK) return st;
     GPTQ_TRY(silu_mul(gb, ub, n * di, gb, s));
-    if (quantize && (st = stage(3, gb, di, 6, 6)) != GPTQ_OK) return st;
+    GPTQ_TRY(split_input(gb, di));
+    if (quantize && (st = stage(3, di, 6, 6)) != GPTQ_OK) return st;
     GPTQ_TRY(hipMemcpyAsync(Y, h1, (size_t)n * hd * 4, hipMemcpyDeviceToDevice, s));
-    GPTQ_TRY(project(6, true, gb, Y, true));
+    if ((st = project(6, true, Y, true)) != GPTQ_OK) return st;
     return GPTQ_OK;
   };
 #undef GPTQ_TRY

@@ -171,6 +171,28 @@ hipError_t dequant_gemm(const void* x, int dtype, int64_t m, int64_t ldx, const 
                         const float* scales, const int32_t* zeros, const int32_t* gidx, int64_t rows, int64_t d,
                         int64_t g, float* y, int64_t ldy, hipStream_t s);
 
+// ------------------------------------------------------------------ fp16 products (gemm_f16.hip)
+// C[M x N] = alpha A B^T + beta C with A [M x K], B [N x K] fp16 row-major (k contiguous); K a
+// multiple of 64, lda and ldb multiples of 8, A and B 16-byte aligned. beta == 0 never reads C.
+struct GemmF16 {
+  int64_t M, N, K;
+  const _Float16* A; int64_t lda;
+  const _Float16* B; int64_t ldb;
+  float* C; int64_t ldc;
+  float alpha, beta;
+};
+hipError_t gemm_f16nt(const GemmF16& a, hipStream_t s);
+// Rows of scale * X [n x d] (pitch ldx) as fp16 [hi | hi | lo | 0] (act = 1) or [hi | lo | hi | 0]
+// (act = 0), pitch split3_pitch(d) = 3 d rounded up to 64: the operands of an fp32 product A W^T
+// formed as one fp16 GEMM. The [hi | lo] half of an act row (from column d) is also the input of a
+// split Hessian.
+int64_t split3_pitch(int64_t d);
+hipError_t split3(const float* X, int64_t n, int64_t d, int64_t ldx, float scale, int act, _Float16* S,
+                  hipStream_t s);
+// out[0] = max |x| over n floats; part holds kAbsmaxParts floats of scratch.
+constexpr int kAbsmaxParts = 1024;
+hipError_t absmax(const float* x, int64_t n, float* part, float* out, hipStream_t s);
+
 // ------------------------------------------------------------------ decoder block (block.hip)
 // W[r, k] = scales[r, G] (codes[r, k] - zeros[r, G]), G = gidx[k] (or k / g when gidx is null),
 // as dense fp32 rows of leading dimension ldw.
@@ -191,7 +213,7 @@ hipError_t to_f32(const void* x, int dtype, int64_t n, float* y, hipStream_t s);
 // Hessian, factor and column-loop workspaces.
 struct BlockLayout {
   size_t off_xf, off_xa, off_q, off_k, off_v, off_at, off_h1, off_xm, off_g, off_u, off_s, off_wf, off_h, off_uf,
-      off_xs, off_h2, off_hw, off_fw, off_qw, hess_bytes, factor_bytes, quant_bytes, total;
+      off_xs, off_w3, off_mx, off_h2, off_hw, off_fw, off_qw, hess_bytes, factor_bytes, quant_bytes, total;
 };
 BlockLayout block_layout(const gptq_block_shape_t& sh, const gptq_params_t& p);
 int quantize_block(const gptq_block_shape_t& sh, const void* X, int x_dtype, const gptq_params_t& p,
