@@ -85,6 +85,42 @@ __global__ __launch_bounds__(256) void causal_softmax_kernel(float* __restrict__
   for (int64_t j = threadIdx.x; j < L; j += 256) row[j] = j <= i ? row[j] * inv : 0.0f;
 }
 
+// The same softmax with the row held in registers (NPT scores per thread, L <= 256 NPT): the scores
+// j <= i are read once and the row is written once.
+template <int NPT>
+__global__ __launch_bounds__(256) void causal_softmax_reg_kernel(float* __restrict__ S, int64_t L, float scale) {
+  __shared__ float red[4];
+  const int64_t i = (int64_t)blockIdx.x % L;
+  float* row = S + (int64_t)blockIdx.x * L;
+  float v[NPT];
+  float mx = -INFINITY;
+#pragma unroll
+  for (int c = 0; c < NPT; ++c) {
+    const int64_t j = threadIdx.x + 256 * c;
+    v[c] = j <= i ? scale * row[j] : -INFINITY;
+    mx = fmaxf(mx, v[c]);
+  }
+#pragma unroll
+  for (int m = 32; m > 0; m >>= 1) mx = fmaxf(mx, __shfl_xor(mx, m, 64));
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = mx;
+  __syncthreads();
+  mx = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+  __syncthreads();
+  float sum = 0.f;
+#pragma unroll
+  for (int c = 0; c < NPT; ++c) {
+    const int64_t j = threadIdx.x + 256 * c;
+    v[c] = j <= i ? expf(v[c] - mx) : 0.0f;
+    sum += v[c];
+  }
+  const float inv = 1.0f / block_sum(sum, red);
+#pragma unroll
+  for (int c = 0; c < NPT; ++c) {
+    const int64_t j = threadIdx.x + 256 * c;
+    if (j < L) row[j] = v[c] * inv;
+  }
+}
+
 // y may be g itself (each element reads its own g and u before writing)
 __global__ __launch_bounds__(256) void silu_mul_kernel(const float* g, const float* __restrict__ u, int64_t n,
                                                        float* y) {
@@ -149,7 +185,13 @@ hipError_t causal_attention(const float* Q, const float* K, const float* V, int6
     a.batch = heads; a.sA = dh; a.sB = dh; a.sC = L * L;
     hipError_t e = gemm_f32(a, s);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(causal_softmax_kernel, dim3((unsigned)(heads * L)), dim3(256), 0, s, S, L, scale);
+    const dim3 rows_grid((unsigned)(heads * L));
+    if (L <= 512)
+      hipLaunchKernelGGL(causal_softmax_reg_kernel<2>, rows_grid, dim3(256), 0, s, S, L, scale);
+    else if (L <= 2048)
+      hipLaunchKernelGGL(causal_softmax_reg_kernel<8>, rows_grid, dim3(256), 0, s, S, L, scale);
+    else
+      hipLaunchKernelGGL(causal_softmax_kernel, rows_grid, dim3(256), 0, s, S, L, scale);
     GemmArgs b{};
     b.M = L; b.N = dh; b.K = L;
     b.A = S; b.lda = L; b.transA = 0; b.lowerA = 1;
