@@ -2,9 +2,9 @@
 // two-term fp16 split that lets it stand in for an fp32 product.
 //
 // A [M x K] and B [N x K] are fp16, row-major with k contiguous; products are exact in fp32 and sums
-// are fp32. A 256-thread workgroup (4 wave64s in a 2x2 grid) owns a 128 x 128 tile of C, each wave
-// 2x2 blocks of 32x32 (the kernel takes the blocks per wave and the stage depth as parameters). K is
-// staged through LDS 64 at a time, double buffered: lane l reads 8
+// are fp32. A 1024-thread workgroup (16 wave64s in a 4x4 grid) owns a 256 x 256 tile of C, each wave
+// 2x2 blocks of 32x32 (the kernel takes the wave grid, the blocks per wave and the stage depth as
+// parameters). K is staged through LDS 32 at a time, double buffered: lane l reads 8
 // consecutive k of row l % 32 (k = 8 (l / 32) .. +7 of each 16-wide step) with one 16-byte LDS read
 // per operand block. Tiles run in groups of 16 row tiles by every column tile, row tile fastest, so
 // the workgroups in flight share a few A strips and every B strip through L2 and the Infinity Cache.
@@ -23,11 +23,13 @@ namespace {
 constexpr int HK = 64;         // K granularity of the operands (the deepest LDS stage)
 constexpr int HGROUP = 16;     // row tiles per group
 
-// A wave owns BM x BN blocks of 32x32 (waves 2 x 2, tile 64 BM x 64 BN); K is staged KS at a time.
-template <int BM, int BN, int KS>
-__global__ __launch_bounds__(256) void gemm_f16nt_kernel(GemmF16 a, int64_t tiles_m, int64_t tiles_n) {
-  constexpr int TM = 64 * BM, TN = 64 * BN, ROW = KS + 8, PQ = KS / 8;
-  constexpr int PA = TM * KS / 8 / 256, PB = TN * KS / 8 / 256;   // 16-byte pieces per thread
+// A wave owns BM x BN blocks of 32x32; WGM x WGN waves (tile 32 BM WGM x 32 BN WGN); K is staged KS at
+// a time.
+template <int WGM, int WGN, int BM, int BN, int KS>
+__global__ __launch_bounds__(64 * WGM * WGN) void gemm_f16nt_kernel(GemmF16 a, int64_t tiles_m, int64_t tiles_n) {
+  constexpr int NTH = 64 * WGM * WGN;
+  constexpr int TM = 32 * BM * WGM, TN = 32 * BN * WGN, ROW = KS + 8, PQ = KS / 8;
+  constexpr int PA = TM * KS / 8 / NTH, PB = TN * KS / 8 / NTH;   // 16-byte pieces per thread
   // grouped order: group g covers row tiles [16 g, 16 g + 16) and every column tile
   const int64_t per_group = (int64_t)HGROUP * tiles_n;
   const int64_t g = blockIdx.x / per_group, in = blockIdx.x % per_group;
@@ -40,7 +42,7 @@ __global__ __launch_bounds__(256) void gemm_f16nt_kernel(GemmF16 a, int64_t tile
   __shared__ __align__(16) _Float16 Bs[2][TN * ROW];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int wm = wave >> 1, wn = wave & 1;
+  const int wm = wave / WGN, wn = wave % WGN;
   const int li = lane & 31, lh = lane >> 5;
 
   floatx16 acc[BM][BN];
@@ -57,13 +59,13 @@ __global__ __launch_bounds__(256) void gemm_f16nt_kernel(GemmF16 a, int64_t tile
   auto gload = [&](int64_t k0) {
 #pragma unroll
     for (int i = 0; i < PA; ++i) {
-      const int p = tid + 256 * i, r = p / PQ, kq = p % PQ;
+      const int p = tid + NTH * i, r = p / PQ, kq = p % PQ;
       const int64_t mr = m0 + r;
       ra[i] = mr < a.M ? *reinterpret_cast<const u32x4*>(a.A + mr * a.lda + k0 + 8 * kq) : u32x4{0u, 0u, 0u, 0u};
     }
 #pragma unroll
     for (int i = 0; i < PB; ++i) {
-      const int p = tid + 256 * i, r = p / PQ, kq = p % PQ;
+      const int p = tid + NTH * i, r = p / PQ, kq = p % PQ;
       const int64_t nr = n0 + r;
       rb[i] = nr < a.N ? *reinterpret_cast<const u32x4*>(a.B + nr * a.ldb + k0 + 8 * kq) : u32x4{0u, 0u, 0u, 0u};
     }
@@ -71,12 +73,12 @@ __global__ __launch_bounds__(256) void gemm_f16nt_kernel(GemmF16 a, int64_t tile
   auto lstore = [&](int buf) {
 #pragma unroll
     for (int i = 0; i < PA; ++i) {
-      const int p = tid + 256 * i, r = p / PQ, kq = p % PQ;
+      const int p = tid + NTH * i, r = p / PQ, kq = p % PQ;
       *reinterpret_cast<u32x4*>(&As[buf][r * ROW + 8 * kq]) = ra[i];
     }
 #pragma unroll
     for (int i = 0; i < PB; ++i) {
-      const int p = tid + 256 * i, r = p / PQ, kq = p % PQ;
+      const int p = tid + NTH * i, r = p / PQ, kq = p % PQ;
       *reinterpret_cast<u32x4*>(&Bs[buf][r * ROW + 8 * kq]) = rb[i];
     }
   };
@@ -127,12 +129,13 @@ __global__ __launch_bounds__(256) void gemm_f16nt_kernel(GemmF16 a, int64_t tile
       }
 }
 
-template <int BM, int BN, int KS>
+template <int WGM, int WGN, int BM, int BN, int KS>
 hipError_t launch_f16nt(const GemmF16& a, hipStream_t s) {
-  const int64_t tiles_m = (a.M + 64 * BM - 1) / (64 * BM), tiles_n = (a.N + 64 * BN - 1) / (64 * BN);
+  constexpr int TM = 32 * BM * WGM, TN = 32 * BN * WGN;
+  const int64_t tiles_m = (a.M + TM - 1) / TM, tiles_n = (a.N + TN - 1) / TN;
   if (tiles_m * tiles_n > 0x7fffffff) return hipErrorInvalidValue;
-  hipLaunchKernelGGL((gemm_f16nt_kernel<BM, BN, KS>), dim3((unsigned)(tiles_m * tiles_n)), dim3(256), 0, s, a,
-                     tiles_m, tiles_n);
+  hipLaunchKernelGGL((gemm_f16nt_kernel<WGM, WGN, BM, BN, KS>), dim3((unsigned)(tiles_m * tiles_n)),
+                     dim3(64 * WGM * WGN), 0, s, a, tiles_m, tiles_n);
   return hipGetLastError();
 }
 
@@ -188,9 +191,11 @@ hipError_t gemm_f16nt(const GemmF16& a, hipStream_t s) {
   if (a.M <= 0 || a.N <= 0) return hipSuccess;
   if (a.K % HK != 0 || a.lda % 8 != 0 || a.ldb % 8 != 0 || (uintptr_t)a.A % 16 != 0 || (uintptr_t)a.B % 16 != 0)
     return hipErrorInvalidValue;
-  // 2x2 blocks per wave with a 64-deep stage: two workgroups per CU. Measured on the Llama-7B block's
-  // products against 4x2, 2x4 (one wave per SIMD) and a 32-deep stage: 12-25% faster.
-  return launch_f16nt<2, 2, 64>(a, s);
+  // 16 waves in a 4x4 grid, 2x2 blocks each: a 256 x 256 tile with a 32-deep stage, one workgroup
+  // (four waves per SIMD) per CU. Measured on the Llama-7B block's products against 4-wave 128 x 128
+  // tiles with a 64-deep stage (about 5% slower), 8-wave 256 x 128 and 128 x 256 tiles (1-3% slower)
+  // and 4-wave tiles with 4x2 or 2x4 blocks per wave (one wave per SIMD, 12-25% slower).
+  return launch_f16nt<4, 4, 2, 2, 32>(a, s);
 }
 
 int64_t split3_pitch(int64_t d) { return (3 * d + HK - 1) / HK * HK; }
