@@ -4,7 +4,7 @@
 // A [M x K] and B [N x K] are fp16, row-major with k contiguous; products are exact in fp32 and sums
 // are fp32. A 1024-thread workgroup (16 wave64s in a 4x4 grid) owns a 256 x 256 tile of C, each wave
 // 2x2 blocks of 32x32 (the kernel takes the wave grid, the blocks per wave and the stage depth as
-// parameters). K is staged through LDS 32 at a time, double buffered: lane l reads 8
+// parameters). K is staged through LDS 64 at a time, double buffered: lane l reads 8
 // consecutive k of row l % 32 (k = 8 (l / 32) .. +7 of each 16-wide step) with one 16-byte LDS read
 // per operand block. Tiles run in groups of 16 row tiles by every column tile, row tile fastest, so
 // the workgroups in flight share a few A strips and every B strip through L2 and the Infinity Cache.
@@ -191,11 +191,12 @@ hipError_t gemm_f16nt(const GemmF16& a, hipStream_t s) {
   if (a.M <= 0 || a.N <= 0) return hipSuccess;
   if (a.K % HK != 0 || a.lda % 8 != 0 || a.ldb % 8 != 0 || (uintptr_t)a.A % 16 != 0 || (uintptr_t)a.B % 16 != 0)
     return hipErrorInvalidValue;
-  // 16 waves in a 4x4 grid, 2x2 blocks each: a 256 x 256 tile with a 32-deep stage, one workgroup
-  // (four waves per SIMD) per CU. Measured on the Llama-7B block's products against 4-wave 128 x 128
-  // tiles with a 64-deep stage (about 5% slower), 8-wave 256 x 128 and 128 x 256 tiles (1-3% slower)
-  // and 4-wave tiles with 4x2 or 2x4 blocks per wave (one wave per SIMD, 12-25% slower).
-  return launch_f16nt<4, 4, 2, 2, 32>(a, s);
+  // 16 waves in a 4x4 grid, 2x2 blocks each: a 256 x 256 tile with a 64-deep stage (147 KB of LDS),
+  // one workgroup (four waves per SIMD) per CU. Measured on the Llama-7B block's products: 6% faster
+  // than a 32-deep stage, which was about 5% faster than 4-wave 128 x 128 tiles (and 1-3% faster
+  // than 8-wave 256 x 128 or 128 x 256 tiles); 4-wave tiles with 4x2 or 2x4 blocks per wave (one wave
+  // per SIMD) were 12-25% slower than the 128 x 128 ones.
+  return launch_f16nt<4, 4, 2, 2, 64>(a, s);
 }
 
 int64_t split3_pitch(int64_t d) { return (3 * d + HK - 1) / HK * HK; }
