@@ -168,23 +168,32 @@ hipError_t rmsnorm(const float* x, int64_t m, int64_t d, int64_t ldx, float eps,
   return hipGetLastError();
 }
 
-// One sequence at a time, every head in one batched product: S_h = Q_h K_h^T (lower triangle of
-// tiles only), the causal softmax over all heads' rows, then O_h = P_h V_h with the k loop of each
-// row tile stopping at its last row (P is zero above the diagonal). S holds heads x L x L floats.
+// One sequence at a time, every head in one batched product. The scores S_h = Q_h K_h^T run on the
+// split fp16 GEMM: Q and K, viewed as [tokens x heads] rows of dh, are split once per call into
+// [hi | hi | lo] and [hi | lo | hi] rows (qk3 holds both), and tiles wholly above the diagonal are
+// skipped (the softmax reads only j <= i). Then the causal softmax over all heads' rows, and
+// O_h = P_h V_h in fp32 with the k loop of each row tile stopping at its last row (P is zero above
+// the diagonal). S holds heads x L x L floats.
 hipError_t causal_attention(const float* Q, const float* K, const float* V, int64_t seqs, int64_t L, int64_t heads,
-                            int64_t dh, int64_t ld, float* O, int64_t ldo, float* S, hipStream_t s) {
+                            int64_t dh, int64_t ld, float* O, int64_t ldo, float* S, _Float16* qk3, hipStream_t s) {
   const float scale = 1.0f / sqrtf((float)dh);
+  const int64_t n = seqs * L, kq = split3_pitch(dh);
+  _Float16* q3 = qk3;
+  _Float16* k3 = qk3 + n * heads * kq;
+  hipError_t e = split3(Q, n * heads, dh, dh, 1.0f, 1, q3, s);
+  if (e != hipSuccess) return e;
+  if ((e = split3(K, n * heads, dh, dh, 1.0f, 0, k3, s)) != hipSuccess) return e;
   for (int64_t sq = 0; sq < seqs; ++sq) {
-    const int64_t off = sq * L * ld;
-    GemmArgs a{};
-    a.M = L; a.N = L; a.K = dh;
-    a.A = Q + off; a.lda = ld; a.transA = 0;
-    a.B = K + off; a.ldb = ld; a.transB = 1;
+    const int64_t off = sq * L * ld, off3 = sq * L * heads * kq;
+    GemmF16 a{};
+    a.M = L; a.N = L; a.K = kq;
+    a.A = q3 + off3; a.lda = heads * kq;
+    a.B = k3 + off3; a.ldb = heads * kq;
     a.C = S; a.ldc = L;
-    a.alpha = 1.0f; a.beta = 0.0f; a.tri = 1;
-    a.batch = heads; a.sA = dh; a.sB = dh; a.sC = L * L;
-    hipError_t e = gemm_f32(a, s);
-    if (e != hipSuccess) return e;
+    a.alpha = 1.0f; a.beta = 0.0f;
+    a.batch = heads; a.sA = kq; a.sB = kq; a.sC = L * L;
+    a.lower = 1;
+    if ((e = gemm_f16nt(a, s)) != hipSuccess) return e;
     const dim3 rows_grid((unsigned)(heads * L));
     if (L <= 512)
       hipLaunchKernelGGL(causal_softmax_reg_kernel<2>, rows_grid, dim3(256), 0, s, S, L, scale);
@@ -251,6 +260,7 @@ BlockLayout block_layout(const gptq_block_shape_t& sh, const gptq_params_t& p) {
   L.off_g = take((size_t)n * di * 4);
   L.off_u = take((size_t)n * di * 4);
   L.off_s = take((size_t)sh.heads * sh.seq_len * sh.seq_len * 4);
+  L.off_qk3 = take((size_t)2 * n * sh.heads * split3_pitch(hd / sh.heads) * 2);   // split Q and K
   L.off_wf = take((size_t)di * hd * 4);
   L.off_h = take((size_t)dm * dm * 4);
   L.off_uf = take((size_t)dm * dm * 4);
@@ -389,7 +399,8 @@ int quantize_block(const gptq_block_shape_t& sh, const void* X, int x_dtype, con
     if ((st = project(0, quantized, q, false)) != GPTQ_OK) return st;
     if ((st = project(1, quantized, k, false)) != GPTQ_OK) return st;
     if ((st = project(2, quantized, v, false)) != GPTQ_OK) return st;
-    GPTQ_TRY(causal_attention(q, k, v, sh.seqs, sh.seq_len, sh.heads, hd / sh.heads, hd, at, hd, S, s));
+    GPTQ_TRY(causal_attention(q, k, v, sh.seqs, sh.seq_len, sh.heads, hd / sh.heads, hd, at, hd, S,
+                              reinterpret_cast<_Float16*>(work + L.off_qk3), s));
     GPTQ_TRY(split_input(at, hd));
     if (quantize && (st = stage(1, hd, 3, 3)) != GPTQ_OK) return st;
     GPTQ_TRY(hipMemcpyAsync(h1, xf, (size_t)n * hd * 4, hipMemcpyDeviceToDevice, s));

@@ -174,12 +174,16 @@ hipError_t dequant_gemm(const void* x, int dtype, int64_t m, int64_t ldx, const 
 // ------------------------------------------------------------------ fp16 products (gemm_f16.hip)
 // C[M x N] = alpha A B^T + beta C with A [M x K], B [N x K] fp16 row-major (k contiguous); K a
 // multiple of 64, lda and ldb multiples of 8, A and B 16-byte aligned. beta == 0 never reads C.
+// batch > 1: `batch` products, the b-th on A + b sA, B + b sB, C + b sC (sA, sB multiples of 8).
+// lower: tiles lying wholly above the diagonal (every n > m) are skipped and their C left as is.
 struct GemmF16 {
   int64_t M, N, K;
   const _Float16* A; int64_t lda;
   const _Float16* B; int64_t ldb;
   float* C; int64_t ldc;
   float alpha, beta;
+  int64_t batch, sA, sB, sC;
+  int lower;
 };
 hipError_t gemm_f16nt(const GemmF16& a, hipStream_t s);
 // Rows of scale * X [n x d] (pitch ldx) as fp16 [hi | hi | lo | 0] (act = 1) or [hi | lo | hi | 0]
@@ -201,9 +205,10 @@ hipError_t dequantize(const uint8_t* codes, int64_t rows, int64_t d, const float
 // Row-wise x / sqrt(mean(x^2) + eps).
 hipError_t rmsnorm(const float* x, int64_t m, int64_t d, int64_t ldx, float eps, float* y, int64_t ldy, hipStream_t s);
 // Multi-head causal attention over seqs sequences of L tokens; Q, K, V, O are [seqs L x heads dh]
-// (leading dimensions ld, ld, ld, ldo); S is heads x L x L fp32 scratch.
+// (leading dimensions ld, ld, ld, ldo; Q and K contiguous, ld = heads dh); S is heads x L x L fp32
+// scratch and qk3 holds 2 seqs L heads split3_pitch(dh) halves of scratch.
 hipError_t causal_attention(const float* Q, const float* K, const float* V, int64_t seqs, int64_t L, int64_t heads,
-                            int64_t dh, int64_t ld, float* O, int64_t ldo, float* S, hipStream_t s);
+                            int64_t dh, int64_t ld, float* O, int64_t ldo, float* S, _Float16* qk3, hipStream_t s);
 // y = silu(g) * u elementwise; y may be g.
 hipError_t silu_mul(const float* g, const float* u, int64_t n, float* y, hipStream_t s);
 hipError_t to_f32(const void* x, int dtype, int64_t n, float* y, hipStream_t s);
@@ -213,7 +218,7 @@ hipError_t to_f32(const void* x, int dtype, int64_t n, float* y, hipStream_t s);
 // Hessian, factor and column-loop workspaces.
 struct BlockLayout {
   size_t off_xf, off_xa, off_q, off_k, off_v, off_at, off_h1, off_xm, off_g, off_u, off_s, off_wf, off_h, off_uf,
-      off_xs, off_w3, off_mx, off_h2, off_hw, off_fw, off_qw, hess_bytes, factor_bytes, quant_bytes, total;
+      off_qk3, off_xs, off_w3, off_mx, off_h2, off_hw, off_fw, off_qw, hess_bytes, factor_bytes, quant_bytes, total;
 };
 BlockLayout block_layout(const gptq_block_shape_t& sh, const gptq_params_t& p);
 int quantize_block(const gptq_block_shape_t& sh, const void* X, int x_dtype, const gptq_params_t& p,
