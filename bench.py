@@ -372,13 +372,14 @@ def bench_block(args):
     cols = sum(shape.layer_dims(i)[1] for i in range(7))
     fl = block_flops(case.hidden, case.heads, case.inter, case.seqs, case.seq_len)
     achieved = sum(fl.values()) / (ms / 1000.0) / 1e12
-    # the time this work needs with every product at its unit's peak: the projections run as three
-    # fp16 products and each stage Hessian as the fp16 Hessian of the 2d-wide split input, the rest
-    # on the fp32 units
+    # the time this work needs with every product at its unit's peak: the projections and the
+    # attention scores (half the attention flops) run as three fp16 products, each stage Hessian as
+    # the fp16 Hessian of the 2d-wide split input, and P V, the factors and the column loops on the
+    # fp32 units
     n = case.seqs * case.seq_len
-    f16_exec = 3.0 * fl["projections"] + sum(n * 2.0 * d * (2.0 * d + 1.0) for d in
-                                             (case.hidden, case.hidden, case.hidden, case.inter))
-    f32_exec = fl["attention"] + fl["factors"] + fl["column_loops"]
+    f16_exec = 3.0 * (fl["projections"] + fl["attention"] / 2) + sum(
+        n * 2.0 * d * (2.0 * d + 1.0) for d in (case.hidden, case.hidden, case.hidden, case.inter))
+    f32_exec = fl["attention"] / 2 + fl["factors"] + fl["column_loops"]
     ideal_s = f16_exec / (PEAK_F16_TFLOPS * 1e12) + f32_exec / (PEAK_F32_TFLOPS * 1e12)
     blended_peak = sum(fl.values()) / ideal_s / 1e12
     out = {
