@@ -11,9 +11,10 @@ original weights. Then:
   within 1e-5 relative, loss within 1e-3 relative; the processing order checked against diag(H));
 * the block output matches the oracle's forward pass through the GPU's quantized weights within
   1e-5 relative (Frobenius) and 1e-4 of max |Y| elementwise.
-Shapes are ragged against every tile (hidden 256, 192 and 120, MLP width 688, 520 and 200, sequence
-lengths 200, 150 and 70), cover fp16, bf16 and fp32 storage, head widths 64, 30 and 8, and one
-2048-token sequence of 32 heads whose attention products run on the 128-wide tiles.
+Shapes are ragged against every tile (hidden 256, 192, 120 and 64, MLP width 688, 520, 200 and 96,
+sequence lengths 200, 150, 70 and 2100). They cover fp16, bf16 and fp32 storage, head widths 64,
+32, 30 and 8, one 2048-token sequence of 32 heads whose attention products run on the large tiles,
+and one 2100-token sequence (the softmax's path for rows longer than 2048).
 """
 
 import numpy as np
@@ -33,6 +34,8 @@ ROWWISE = synth.BlockCase(hidden=192, heads=3, inter=520, seqs=3, seq_len=150, w
 ODD_HEADS = synth.BlockCase(hidden=120, heads=4, inter=200, seqs=2, seq_len=70)
 # 32 heads of 2048 tokens: the attention products take 128-wide tiles, as at the Llama-7B shape
 LONG = synth.BlockCase(hidden=256, heads=32, inter=688, seqs=1, seq_len=2048)
+# one sequence longer than 2048 tokens: the softmax takes its three-pass kernel
+OVERLONG = synth.BlockCase(hidden=64, heads=2, inter=96, seqs=1, seq_len=2100)
 
 CASES = [
     ("g128", MAIN, dict(bits=4, group_size=128, act_order=False), True),
@@ -41,6 +44,7 @@ CASES = [
     ("3bit-per-row", ROWWISE, dict(bits=3, group_size=0, act_order=True), True),
     ("odd-head-width", ODD_HEADS, dict(bits=4, group_size=32, act_order=False), True),
     ("long-sequence-many-heads", LONG, dict(bits=4, group_size=128, act_order=True), True),
+    ("sequence-over-2048", OVERLONG, dict(bits=4, group_size=32, act_order=False), True),
     ("sym-static-compact", MAIN, dict(bits=4, group_size=128, act_order=True, sym=True, static_groups=True,
                                       compact_meta=True), True),
 ]
