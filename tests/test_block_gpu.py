@@ -207,3 +207,29 @@ def test_llama7b_block_full_size():
     fro, mx = np.linalg.norm(dy) / np.linalg.norm(want_y), np.max(np.abs(dy)) / np.max(np.abs(want_y))
     print(f"[block full] output: Frobenius {fro:.2e}, max {mx:.2e}", flush=True)
     assert fro <= 1e-5 and mx <= 1e-4
+
+
+def test_block_reports_failed_stages():
+    """Errors come back as statuses, with every kernel ending normally: an all-zero block input has
+    a zero Hessian (its mean diagonal fails the factor's check), and stage inputs beyond the fp16
+    range (weights scaled by 1e6 give attention outputs near 1e5) give a non-finite Hessian."""
+    torch = torch_cuda()
+    import post_weight_quantization_20_amd as g
+    case = synth.BlockCase(hidden=64, heads=2, inter=96, seqs=1, seq_len=80)
+    W = synth.block_weights(case, 3)
+    shape = g.BlockShape(case.hidden, case.heads, case.inter, case.seqs, case.seq_len, 1e-6)
+    params = g.Params(bits=4, group_size=32, block_size=32, act_order=False, damp=0.01)
+    zero = torch.zeros((case.seqs * case.seq_len, case.hidden), dtype=torch.float16, device="cuda")
+    with pytest.raises(g.GPTQError) as e:
+        g.gptq_quantize_block(zero, [dev_tensor(w, "f16") for w in W], shape, params)
+    assert e.value.status == g.GPTQ_EINVAL
+    big = [dev_tensor((synth.to_f64(w, "f16") * 1e6).astype(np.float32), "f32") for w in W]
+    with pytest.raises(g.GPTQError) as e:
+        g.gptq_quantize_block(dev_tensor(synth.block_x(case, 3), "f16"), big, shape, params)
+    assert e.value.status == g.GPTQ_EINVAL
+    torch.cuda.synchronize()
+    # the library is still usable afterwards
+    r = g.gptq_quantize_block(dev_tensor(synth.block_x(case, 3), "f16"), [dev_tensor(w, "f16") for w in W], shape,
+                              params)
+    torch.cuda.synchronize()
+    assert torch.isfinite(r.Y).all()
