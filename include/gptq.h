@@ -127,13 +127,14 @@ gptq_status_t gptq_hessian_accumulate(float *H, int64_t d, const void *X, int32_
  * (GPTQ tools page, "How it works", Steps 4 and 6; "Optional refinements", Act-order).
  *
  *   H        device float[d * d], the accumulated sum of gptq_hessian_accumulate (upper triangle
- *            read). Not modified.
+ *            read). Not modified, unless U == H.
  *   n_total  number of tokens summed into H (> 0); Hhat = H / n_total + lambda I with
  *            lambda = p->damp * mean(diag(H / n_total)).
  *   p        settings; reads damp, act_order, sym, static_groups.
- *   U        device float[d * d], output, must not overlap H: upper-triangular U with
- *            Hhat_perm^-1 = U^T U, in processing order (row/column j is original column perm[j]);
- *            zeros below the diagonal.
+ *   U        device float[d * d], output: upper-triangular U with Hhat_perm^-1 = U^T U, in
+ *            processing order (row/column j is original column perm[j]); zeros below the diagonal.
+ *            Either U == H (the factor overwrites H in place, with no second d x d buffer) or the
+ *            two do not overlap; a partial overlap is GPTQ_EINVAL.
  *   perm     device int32[d], output: the processing order. Identity without act-order; with it,
  *            columns by descending diag(H), equal values by lower index first.
  *   work     device workspace of at least gptq_workspace_bytes(GPTQ_WS_FACTOR, 0, d, p) bytes.

@@ -16,8 +16,10 @@ It is a plain, slow, step-by-step statement of what the solver computes, written
 * "What Is GPTQ? Classic 4-Bit LLM Quantization" (ai-tldr.dev), "How it works", Step 3 (groups).
 
 Arithmetic is float64 throughout (inputs are upcast exactly), with one exception: the two
-rounding decisions (a code from w / scale, a zero point from -wmin / scale) divide in float32,
-because the pages' sketch computes on float32 tensors and the GPU kernels decide in float32.
+rounding decisions (a code from w / scale, a zero point from -wmin / scale) divide in float32. The
+tools page's sketch converts the weights to float32 before its loop, so its w / scale and
+-wmin / scale are float32 divisions of float32 values; the oracle takes those two quotients the same
+way, from its float64 operands rounded to float32, and keeps float64 everywhere else.
 Dense algebra uses library primitives: BLAS matrix products and the LAPACK Cholesky routines
 (potrf / potri) that the sketch's cholesky / cholesky_inverse / cholesky(upper) calls name.
 

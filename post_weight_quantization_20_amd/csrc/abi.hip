@@ -87,7 +87,7 @@ gptq_status_t gptq_factor(const float* H, int64_t d, int64_t n_total, const gptq
   const char* h0 = reinterpret_cast<const char*>(H);
   const char* u0 = reinterpret_cast<const char*>(U);
   const size_t bytes = (size_t)d * d * sizeof(float);
-  if (h0 < u0 + bytes && u0 < h0 + bytes) return GPTQ_EINVAL;
+  if (h0 != u0 && h0 < u0 + bytes && u0 < h0 + bytes) return GPTQ_EINVAL;   // in place, or apart
   if (work_bytes < gptq::factor_workspace_bytes(d)) return GPTQ_ENOMEM;
   hipStream_t s = static_cast<hipStream_t>(stream);
   int* status_dev = nullptr;

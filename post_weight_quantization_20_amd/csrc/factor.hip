@@ -129,10 +129,11 @@ __global__ void iota_kernel(int32_t* perm, int64_t d) {
 }
 
 // A[i][j] (j <= i) = Hhat[p(i)][p(j)], p(i) = perm[d-1-i]: the damped, normalised Hessian in
-// processing order, reversed. H's upper triangle is authoritative.
-__global__ __launch_bounds__(256) void gather_kernel(const float* __restrict__ H, int64_t d, int64_t n,
-                                                     const int32_t* __restrict__ perm, FactorWork w,
-                                                     float* __restrict__ A) {
+// processing order, reversed. H's upper triangle is authoritative. Off the diagonal this reads only
+// H's strict upper triangle and writes only A's strict lower one; the diagonal comes from the copy
+// diag_stats_kernel took (keys), so A may be H itself (the factor in place).
+__global__ __launch_bounds__(256) void gather_kernel(const float* H, int64_t d, int64_t n,
+                                                     const int32_t* __restrict__ perm, FactorWork w, float* A) {
   const int64_t i = blockIdx.x;
   const int64_t pi = perm[d - 1 - i];
   const double lam = *w.lam;
@@ -140,8 +141,7 @@ __global__ __launch_bounds__(256) void gather_kernel(const float* __restrict__ H
   for (int64_t j = threadIdx.x; j <= i; j += 256) {
     const int64_t pj = perm[d - 1 - j];
     const int64_t r = min(pi, pj), c = max(pi, pj);
-    double v = (double)H[r * d + c] * inv_n;
-    if (pi == pj) v += lam;
+    const double v = pi == pj ? (double)w.keys[pi] * inv_n + lam : (double)H[r * d + c] * inv_n;
     A[i * d + j] = (float)v;
   }
 }

@@ -88,7 +88,7 @@ __global__ __launch_bounds__(256) void quant_block_kernel(QArgs a) {
 
   bool filled = false;
   if constexpr (CPL >= 4) {
-   if (nc == BP && a.d % 4 == 0 && a.b % 4 == 0) {
+   if (nc == BP && a.d % 4 == 0 && a.b % 4 == 0 && (uintptr_t)a.U % 16 == 0) {
     // full block: unconditional 16-byte loads, all in flight together
     filled = true;
     constexpr int Q = BP / 4;  // float4 per row

@@ -20,13 +20,25 @@ hipError_t helpers(Helpers** out) {
   if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
   std::lock_guard<std::mutex> lock(g_create);
   if (!g_helpers[dev]) {
-    Helpers* h = new Helpers{};
-    for (auto& st : h->stream)
-      if ((e = hipStreamCreateWithFlags(&st, hipStreamNonBlocking)) != hipSuccess) return e;
-    for (auto& ev : h->event)
-      if ((e = hipEventCreateWithFlags(&ev, hipEventDisableTiming)) != hipSuccess) return e;
-    h->mu = new std::mutex;
-    g_helpers[dev] = h;
+    // built completely before it is published; on a failed create, what was created is destroyed
+    // and nothing is cached, so a later call tries again
+    Helpers h{};
+    int ns = 0, ne = 0;   // streams and events created so far
+    while (e == hipSuccess && ns < 2) {
+      e = hipStreamCreateWithFlags(&h.stream[ns], hipStreamNonBlocking);
+      if (e == hipSuccess) ++ns;
+    }
+    while (e == hipSuccess && ne < 8) {
+      e = hipEventCreateWithFlags(&h.event[ne], hipEventDisableTiming);
+      if (e == hipSuccess) ++ne;
+    }
+    if (e != hipSuccess) {
+      for (int i = 0; i < ne; ++i) (void)hipEventDestroy(h.event[i]);
+      for (int i = 0; i < ns; ++i) (void)hipStreamDestroy(h.stream[i]);
+      return e;
+    }
+    h.mu = new std::mutex;
+    g_helpers[dev] = new Helpers(h);
   }
   *out = g_helpers[dev];
   return hipSuccess;

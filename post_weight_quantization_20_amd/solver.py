@@ -85,6 +85,20 @@ def _need_cuda(*ts) -> None:
             raise ValueError("tensors must be on the GPU")
 
 
+def _want(t: torch.Tensor, shape: tuple, dtype, name: str, device=None) -> None:
+    """A caller-supplied tensor must have exactly this shape and dtype, be contiguous and sit on the
+    given device: the library writes through its pointer without knowing its size."""
+    if tuple(t.shape) != tuple(shape) or t.dtype != dtype or not t.is_contiguous():
+        raise ValueError(f"{name} must be a contiguous {dtype} tensor of shape {tuple(shape)}")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name} must be on {device}")
+
+
+def _want_work(work: torch.Tensor, nbytes: int, device) -> None:
+    if work.dtype != torch.uint8 or not work.is_contiguous() or work.numel() < nbytes or work.device != device:
+        raise ValueError(f"work must be a contiguous uint8 tensor of at least {nbytes} bytes on {device}")
+
+
 def gptq_workspace_bytes(kind: int, a: int, d: int, params: Optional[Params] = None) -> int:
     p = ctypes.byref(params.c()) if params is not None else None
     return int(_lib.lib().gptq_workspace_bytes(kind, a, d, p))
@@ -105,8 +119,12 @@ def gptq_hessian_accumulate(H: torch.Tensor, X: torch.Tensor, work: Optional[tor
     if X.dim() != 2 or X.shape[1] != d or X.stride(1) != 1 or X.dtype not in _DTYPE:
         raise ValueError("X must be [tokens, d] with unit column stride, fp32/fp16/bf16")
     n = X.shape[0]
+    if X.device != H.device:
+        raise ValueError("X must be on H's device")
     if work is None:
         work = _workspace(GPTQ_WS_HESSIAN, n, d, None, H.device)
+    elif work.dtype != torch.uint8 or not work.is_contiguous() or work.device != H.device:
+        raise ValueError("work must be a contiguous uint8 tensor on H's device")
     _check(_lib.lib().gptq_hessian_accumulate(_ptr(H), d, _ptr(X), _DTYPE[X.dtype], n, X.stride(0), _ptr(work),
                                               work.numel(), _stream(stream)))
 
@@ -115,17 +133,24 @@ def gptq_factor(H: torch.Tensor, n_total: int, params: Params, U: Optional[torch
                 perm: Optional[torch.Tensor] = None, work: Optional[torch.Tensor] = None,
                 stream=None) -> Tuple[torch.Tensor, torch.Tensor]:
     """(U, perm): U upper with (H/n + lambda I)[perm][:, perm]^-1 = U^T U. Raises GPTQError (with
-    .info) when the damped Hessian is not positive definite."""
+    .info) when the damped Hessian is not positive definite. U may be H itself (the factor in place,
+    which overwrites H)."""
     _need_cuda(H, U, perm, work)
     d = H.shape[0]
     if H.dtype != torch.float32 or H.shape != (d, d) or not H.is_contiguous():
         raise ValueError("H must be a contiguous float32 [d, d] tensor")
     if U is None:
         U = torch.empty((d, d), dtype=torch.float32, device=H.device)
+    else:
+        _want(U, (d, d), torch.float32, "U", H.device)
     if perm is None:
         perm = torch.empty(d, dtype=torch.int32, device=H.device)
+    else:
+        _want(perm, (d,), torch.int32, "perm", H.device)
     if work is None:
         work = _workspace(GPTQ_WS_FACTOR, 0, d, params, H.device)
+    else:
+        _want_work(work, gptq_workspace_bytes(GPTQ_WS_FACTOR, 0, d, params), H.device)
     info = ctypes.c_int64(0)
     st = _lib.lib().gptq_factor(_ptr(H), d, int(n_total), ctypes.byref(params.c()), _ptr(U), _ptr(perm), _ptr(work),
                                 work.numel(), ctypes.byref(info), _stream(stream))
@@ -141,20 +166,26 @@ def gptq_quantize_layer(W: torch.Tensor, U: torch.Tensor, perm: torch.Tensor, pa
     rows, d = W.shape
     if W.stride(1) != 1 or W.dtype not in _DTYPE:
         raise ValueError("W must be [rows, d] with unit column stride, fp32/fp16/bf16")
-    if U.shape != (d, d) or U.dtype != torch.float32 or not U.is_contiguous():
-        raise ValueError("U must be a contiguous float32 [d, d] tensor")
-    if perm.shape != (d,) or perm.dtype != torch.int32:
-        raise ValueError("perm must be int32 [d]")
     dev = W.device
+    _want(U, (d, d), torch.float32, "U", dev)
+    _want(perm, (d,), torch.int32, "perm", dev)
+    ng = params.groups(d)
     if out is None:
-        ng = params.groups(d)
         out = QuantOutput(codes=torch.empty((rows, d), dtype=torch.uint8, device=dev),
                           scales=torch.empty((rows, ng), dtype=torch.float32, device=dev),
                           zeros=torch.empty((rows, ng), dtype=torch.int32, device=dev),
                           g_idx=torch.empty(d, dtype=torch.int32, device=dev),
                           loss=torch.empty(1, dtype=torch.float64, device=dev))
+    else:
+        _want(out.codes, (rows, d), torch.uint8, "out.codes", dev)
+        _want(out.scales, (rows, ng), torch.float32, "out.scales", dev)
+        _want(out.zeros, (rows, ng), torch.int32, "out.zeros", dev)
+        _want(out.g_idx, (d,), torch.int32, "out.g_idx", dev)
+        _want(out.loss, (1,), torch.float64, "out.loss", dev)
     if work is None:
         work = _workspace(GPTQ_WS_QUANTIZE, rows, d, params, dev)
+    else:
+        _want_work(work, gptq_workspace_bytes(GPTQ_WS_QUANTIZE, rows, d, params), dev)
     st = _lib.lib().gptq_quantize_layer(_ptr(W), _DTYPE[W.dtype], rows, d, W.stride(0), _ptr(U), _ptr(perm),
                                         ctypes.byref(params.c()), _ptr(out.codes), _ptr(out.scales),
                                         _ptr(out.zeros), _ptr(out.g_idx), _ptr(out.loss), _ptr(work), work.numel(),
@@ -177,6 +208,8 @@ def gptq_pack(codes: torch.Tensor, bits: int, packed: Optional[torch.Tensor] = N
         raise ValueError("codes must be contiguous uint8 [rows, d]")
     if packed is None:
         packed = torch.empty((rows, packed_words(d, bits)), dtype=torch.int32, device=codes.device)
+    else:
+        _want(packed, (rows, packed_words(d, bits)), torch.int32, "packed", codes.device)
     _check(_lib.lib().gptq_pack(_ptr(codes), rows, d, int(bits), _ptr(packed), _stream(stream)))
     return packed
 
@@ -190,6 +223,8 @@ def gptq_pack_dense(codes: torch.Tensor, bits: int, packed: Optional[torch.Tenso
         raise ValueError("codes must be contiguous uint8 [rows, d]")
     if packed is None:
         packed = torch.empty((rows, packed_words(d, bits, True)), dtype=torch.int32, device=codes.device)
+    else:
+        _want(packed, (rows, packed_words(d, bits, True)), torch.int32, "packed", codes.device)
     _check(_lib.lib().gptq_pack_dense(_ptr(codes), rows, d, int(bits), _ptr(packed), _stream(stream)))
     return packed
 
@@ -206,6 +241,8 @@ def gptq_pack_ordered(codes: torch.Tensor, bits: int, order: torch.Tensor, packe
         raise ValueError("order must be contiguous int32 [d]")
     if packed is None:
         packed = torch.empty((rows, packed_words(d, bits)), dtype=torch.int32, device=codes.device)
+    else:
+        _want(packed, (rows, packed_words(d, bits)), torch.int32, "packed", codes.device)
     _check(_lib.lib().gptq_pack_ordered(_ptr(codes), rows, d, int(bits), _ptr(order), _ptr(packed), _stream(stream)))
     return packed
 
@@ -221,6 +258,9 @@ def gptq_permute_columns(x: torch.Tensor, order: torch.Tensor, out: Optional[tor
         raise ValueError("order must be contiguous int32 [d]")
     if out is None:
         out = torch.empty((m, d), dtype=x.dtype, device=x.device)
+    elif out.dim() != 2 or tuple(out.shape) != (m, d) or out.stride(1) != 1 or out.dtype != x.dtype \
+            or out.device != x.device:
+        raise ValueError("out must be [m, d] with unit column stride, x's dtype and device")
     _check(_lib.lib().gptq_permute_columns(_ptr(x), _DTYPE[x.dtype], m, d, x.stride(0), _ptr(order), _ptr(out),
                                            out.stride(0), _stream(stream)))
     return out
@@ -248,8 +288,8 @@ def gptq_dequant_gemm(x: torch.Tensor, packed: torch.Tensor, scales: torch.Tenso
     m = x.shape[0]
     if y is None:
         y = torch.empty((m, rows), dtype=torch.float32, device=x.device)
-    if y.dtype != torch.float32 or y.dim() != 2 or y.shape != (m, rows) or y.stride(1) != 1:
-        raise ValueError("y must be float32 [m, rows] with unit column stride")
+    if y.dtype != torch.float32 or y.dim() != 2 or y.shape != (m, rows) or y.stride(1) != 1 or y.device != x.device:
+        raise ValueError("y must be float32 [m, rows] with unit column stride, on x's device")
     layout = GPTQ_LAYOUT_DENSE if dense else GPTQ_LAYOUT_FIELDS
     _check(_lib.lib().gptq_dequant_gemm(_ptr(x), _DTYPE[x.dtype], m, x.stride(0), _ptr(packed), int(bits), layout,
                                         _ptr(scales), _ptr(zeros), _ptr(g_idx), rows, d, int(group_size), _ptr(y),
@@ -356,11 +396,13 @@ def gptq_quantize_block(X: torch.Tensor, weights, shape: BlockShape, params: Par
         widths = (shape.hidden, shape.hidden, shape.hidden, shape.inter)
         hess = [torch.empty((w, w), dtype=torch.float32, device=dev) for w in widths]
         hptr = (ctypes.c_void_p * 4)(*[h.data_ptr() for h in hess])
+    nb = gptq_block_workspace_bytes(shape, params)
+    if nb == 0:
+        raise ValueError("invalid block shape or settings")
     if work is None:
-        nb = gptq_block_workspace_bytes(shape, params)
-        if nb == 0:
-            raise ValueError("invalid block shape or settings")
         work = torch.empty(nb, dtype=torch.uint8, device=dev)
+    else:
+        _want_work(work, nb, dev)
     info = (ctypes.c_int64 * 2)()
     st = _lib.lib().gptq_quantize_block(ctypes.byref(shape.c()), _ptr(X), _DTYPE[X.dtype], ctypes.byref(params.c()),
                                         int(bool(true_sequential)), arr, _ptr(Y), hptr, _ptr(work), work.numel(),

@@ -93,6 +93,31 @@ def check_quant_parity(gpu, o_quant, codes_tol=0.001):
     assert abs(gpu["loss"] - o_quant.loss) <= LOSS_RTOL * abs(o_quant.loss), (gpu["loss"], o_quant.loss)
 
 
+FACTOR_VS_LAPACK = 10.0   # factor error allowed, in units of float32 LAPACK's error on the same matrix
+
+
+def lapack_f32_factor(Hh: np.ndarray) -> np.ndarray:
+    """The upper Cholesky factor of Hh^-1 computed by LAPACK in float32 along the sketch's literal
+    route (potrf, potri, potrf): what float32 arithmetic achieves on this matrix."""
+    from scipy.linalg import lapack
+    L, info = lapack.spotrf(Hh.astype(np.float32), lower=1)
+    assert info == 0
+    Ai, info = lapack.spotri(L, lower=1)
+    assert info == 0
+    Ai = np.tril(Ai) + np.tril(Ai, -1).T
+    U, info = lapack.spotrf(Ai, lower=0)
+    assert info == 0
+    return np.triu(U).astype(np.float64)
+
+
+def factor_errors(U: np.ndarray, Hh: np.ndarray, Uo: np.ndarray):
+    """(max |U - Uo| / max |Uo|, max |U^T U Hh - I|) of a factor U against the float64 oracle's Uo."""
+    U = U.astype(np.float64)
+    err = float(np.max(np.abs(U - Uo)) / np.max(np.abs(Uo)))
+    resid = float(np.max(np.abs(U.T @ U @ Hh - np.eye(Hh.shape[0]))))
+    return err, resid
+
+
 def load_probes():
     if not os.path.exists(PROBES_LIB):
         pytest.skip("probe library not built (run __graft_entry__.build())")

@@ -100,8 +100,9 @@ def test_factor_rejects_bad_arguments():
     f = lib.gptq_factor
     assert f(None, 16, 10, ctypes.byref(p), FAKE, FAKE, FAKE, big, ctypes.byref(info), None) == -1
     assert f(FAKE, 16, 0, ctypes.byref(p), ctypes.c_void_p(0x100000), FAKE, FAKE, big, ctypes.byref(info), None) == -1
-    # U overlapping H
+    # U overlapping H without being H (U == H is the factor in place)
     assert f(FAKE, 16, 10, ctypes.byref(p), ctypes.c_void_p(0x1000 + 64), FAKE, FAKE, big, ctypes.byref(info), None) == -1
+    assert f(FAKE, 16, 10, ctypes.byref(p), ctypes.c_void_p(0x1000 - 4), FAKE, FAKE, big, ctypes.byref(info), None) == -1
     assert f(FAKE, 16, 10, ctypes.byref(_p(L, sym=2)), ctypes.c_void_p(0x100000), FAKE, FAKE, big,
              ctypes.byref(info), None) == -1
     assert f(FAKE, 16, 10, ctypes.byref(_p(L, static_groups=-1)), ctypes.c_void_p(0x100000), FAKE, FAKE, big,

@@ -26,10 +26,9 @@ import dataclasses
 
 import numpy as np
 import pytest
-from scipy.linalg import lapack
 
 import synth
-from gpu_util import LOSS_RTOL, SCALE_RTOL, TAU, dequant, torch_cuda
+from gpu_util import FACTOR_VS_LAPACK, LOSS_RTOL, SCALE_RTOL, TAU, dequant, lapack_f32_factor, torch_cuda
 from oracle import gptq_ref as ref
 
 pytestmark = pytest.mark.gpu
@@ -38,7 +37,6 @@ U32 = 2.0 ** -24
 SAMPLE_ROWS = 48
 SAMPLE_PAIRS = 256
 SAMPLE_COLS = 12
-FACTOR_VS_LAPACK = 10.0
 
 
 def _run_gpu(case, X_host, W_host):
@@ -90,17 +88,9 @@ def _check_hessian(Hg, Ho, X_host, case, rng):
 
 
 def _lapack_f32_error(Hh, Uo):
-    """Error of the same factor computed by LAPACK in float32 (the sketch's literal route: potrf,
-    potri, potrf), relative to max |U|: what float32 arithmetic achieves on this matrix."""
-    A = Hh.astype(np.float32)
-    L, info = lapack.spotrf(A, lower=1)
-    assert info == 0
-    Ai, info = lapack.spotri(L, lower=1)
-    assert info == 0
-    Ai = np.tril(Ai) + np.tril(Ai, -1).T
-    U32f, info = lapack.spotrf(Ai, lower=0)
-    assert info == 0
-    return float(np.max(np.abs(np.triu(U32f) - Uo)) / np.max(np.abs(Uo)))
+    """Error of the same factor computed by LAPACK in float32, relative to max |U|."""
+    U32f = lapack_f32_factor(Hh)
+    return float(np.max(np.abs(U32f - Uo)) / np.max(np.abs(Uo)))
 
 
 def _check_factor(Ug, Hh, Uo, lam, rng):

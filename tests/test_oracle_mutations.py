@@ -6,13 +6,25 @@ one pin-style check rejects it. The committed oracle is never modified.
 """
 
 import inspect
+import json
+import os
 import sys
 import types
+from fractions import Fraction
 
 import numpy as np
 import pytest
 
 from oracle import gptq_ref as ref
+
+HAND = json.load(open(os.path.join(os.path.dirname(__file__), "golden", "hand_worked.json")))
+
+
+def _f16_value(bits: int) -> float:
+    """Value of an IEEE 754 binary16 bit pattern (5 exponent bits biased by 15, 10 fraction bits)."""
+    e, m = (bits >> 10) & 0x1F, bits & 0x3FF
+    v = m * 2.0 ** -24 if e == 0 else (1.0 + m / 1024.0) * 2.0 ** (e - 15)
+    return -v if bits >> 15 else v
 
 MUTATIONS = [
     ("drop lazy update", "Wp[:, e_blk:] -= Err @ U[b:e_blk, e_blk:]", "pass"),
@@ -55,6 +67,16 @@ MUTATIONS = [
      "g = np.arange(d) * len(np.unique(g_idx)) // d"),
     ("dequant product transposed", "return np.asarray(x, dtype=np.float64) @ W.T",
      "return (np.asarray(x, dtype=np.float64)[:, :W.shape[0]] @ W).T"),
+    ("brute force zero sign", "dq = s[r] * (grids - z[r])", "dq = s[r] * (grids + z[r])"),
+    ("brute force drops the top code", "np.arange(maxq + 1, dtype=np.float64)", "np.arange(maxq, dtype=np.float64)"),
+    ("brute force keeps the last row's optimum", "best += float(f[k])", "best = float(f[k])"),
+    ("fp16 scale truncated", "    s = np.asarray(scale32, dtype=np.float32).astype(np.float16).astype(np.float64)",
+     "    s = (np.asarray(scale32, dtype=np.float32).view(np.uint32) & np.uint32(0xFFFFE000)).view(np.float32)"
+     ".astype(np.float16).astype(np.float64)"),
+    ("follow scale window too wide", "def _follow_scale(own: np.ndarray, s32: np.ndarray, other: Optional[np.ndarray], rtol: float = 1e-5):",
+     "def _follow_scale(own: np.ndarray, s32: np.ndarray, other: Optional[np.ndarray], rtol: float = 1e-2):"),
+    ("follow scale takes any scale", "    return np.where(ok, other, own), int(np.count_nonzero(ok & (other != own)))",
+     "    return other, int(np.count_nonzero(ok & (other != own)))"),
 ]
 
 
@@ -155,6 +177,36 @@ def _checks(m):
                 or qc.zeros.min() < 0 or qc.zeros.max() > 15
                 or not np.array_equal(ref.dequantize(ref.pack(qc.codes, 4), qc.scales, qc.zeros, qc.g_idx, d), qc.Q)):
             failed.append("compact metadata")
+        # brute force: the hand-worked two-weight optimum (not round-to-nearest), and with a
+        # diagonal Hessian the separable minimum, round-to-nearest's weighted error
+        e = HAND["brute_force_two_weights"]
+        Wb = np.array([[float(Fraction(v)) for v in e["weights"]]])
+        Hb = np.array([[float(Fraction(v)) for v in r] for r in e["hhat"]])
+        fb, Qb = m.brute_force(Wb, Hb, 2)
+        if (not np.isclose(fb, float(Fraction(e["optimal_objective"])), rtol=1e-12)
+                or not np.allclose(Qb[0], [float(Fraction(v)) for v in e["optimal_values"]], atol=1e-15)):
+            failed.append("brute force hand example")
+        Wd = W[:3, :5] + 0.01
+        hd = np.linspace(0.5, 4.0, 5)
+        fd, _ = m.brute_force(Wd, np.diag(hd), 2)
+        if not np.isclose(fd, np.sum(hd[None, :] * (Wd - ref.rtn(Wd, 2, 0).Q) ** 2), rtol=1e-12):
+            failed.append("brute force diagonal -> rtn")
+        # 16-bit scales: hand-derived float16 patterns, and the boundary rule of following
+        for c in HAND["float16_scale_rounding"]["cases"]:
+            x = float(Fraction(c["exact"]))
+            with np.errstate(over="ignore"):
+                got = m.fp16_scale(np.array([x]))[0]
+            if got != _f16_value(int(c["float16"], 16)):
+                failed.append("fp16 scale bit patterns")
+                break
+        mid = float(Fraction(2049, 2048))
+        own = m.fp16_scale(np.array([mid]))
+        far = 1.0 + 2.0 ** -12
+        if (m._follow_scale(own, np.array([mid]), np.array([_f16_value(0x3C02)]))[0][0] != own[0]
+                or m._follow_scale(m.fp16_scale(np.array([far])), np.array([far]),
+                                   np.array([_f16_value(0x3C01)]))[0][0] != 1.0
+                or m._follow_scale(own, np.array([mid]), np.array([_f16_value(0x3C01)]))[0][0] != _f16_value(0x3C01)):
+            failed.append("follow scale boundary")
         # H = I must reduce to round-to-nearest with dynamic grids
         rI = m.gptq(W, None, 4, 16, 32, H=np.eye(d) * 2.0, n=1)
         if not np.array_equal(rI.quant.codes, ref.rtn(W, 4, 16).codes):

@@ -4,8 +4,10 @@ Each test names the passage or the closed form it checks. Together they are chos
 dropped term, a wrong sign or index, or a transposed operand anywhere in the oracle fails one of them.
 """
 
+import itertools
 import json
 import os
+from fractions import Fraction
 
 import numpy as np
 import pytest
@@ -13,6 +15,7 @@ import pytest
 from oracle import gptq_ref as ref
 
 GOLD = json.load(open(os.path.join(os.path.dirname(__file__), "golden", "worked_examples.json")))
+HAND = json.load(open(os.path.join(os.path.dirname(__file__), "golden", "hand_worked.json")))
 
 
 def _correlated_x(rng, n, d, mix=0.8):
@@ -223,6 +226,100 @@ def test_no_lower_than_brute_force():
         obj = ref.objective(W, r.quant.Q, r.Hhat)
         assert obj >= best * (1 - 1e-12) - 1e-18, trial
         assert obj == pytest.approx(r.quant.loss, rel=1e-9)
+
+
+def test_brute_force_hand_worked_instance():
+    """The exhaustive optimum of a two-weight 2-bit row worked by hand (tests/golden/hand_worked.json):
+    the 16 code pairs enumerated here in exact rational arithmetic, then found by brute_force. Its
+    optimum is not round-to-nearest, so a search that returned round-to-nearest would fail."""
+    e = HAND["brute_force_two_weights"]
+    w = [Fraction(v) for v in e["weights"]]
+    Hh = [[Fraction(v) for v in r] for r in e["hhat"]]
+    maxq = (1 << e["bits"]) - 1
+    s, z = Fraction(e["scale"]), e["zero"]
+    assert s == (max(w) - min(w)) / maxq                       # the row's min/max grid
+    assert abs(-min(w) / s - z) <= Fraction(1, 2)                # the zero is the nearest integer
+
+    def f(q):
+        D = [w[i] - s * (q[i] - z) for i in range(2)]
+        return sum(D[i] * Hh[i][j] * D[j] for i in range(2) for j in range(2))
+
+    table = sorted((f(q), q) for q in itertools.product(range(maxq + 1), repeat=2))
+    assert table[0] == (Fraction(e["optimal_objective"]), tuple(e["optimal_codes"]))
+    assert table[1][0] > table[0][0]                            # a unique optimum
+    assert f(tuple(e["rtn_codes"])) == Fraction(e["rtn_objective"])
+    W = np.array([[float(v) for v in w]])
+    H64 = np.array([[float(v) for v in r] for r in Hh])
+    best, Q = ref.brute_force(W, H64, e["bits"])
+    assert best == pytest.approx(float(Fraction(e["optimal_objective"])), rel=1e-12)
+    assert np.allclose(Q[0], [float(Fraction(v)) for v in e["optimal_values"]], rtol=0, atol=1e-15)
+    t = ref.rtn(W, e["bits"], 0)
+    assert list(t.codes[0]) == e["rtn_codes"]
+
+
+@pytest.mark.parametrize("bits", [2, 3])
+def test_brute_force_with_diagonal_hessian_is_rtn(bits):
+    """With a diagonal Hhat the objective is sum_j h_j (w_j - q_j)^2, each term minimised on its own
+    by the grid value nearest w_j, so the exhaustive optimum is round-to-nearest's error, written out
+    here as that sum."""
+    rng = np.random.default_rng(38 + bits)
+    for trial in range(120):
+        d = int(rng.integers(2, 7 if bits == 2 else 6))
+        W = rng.standard_normal((3, d)) * 0.02 + rng.uniform(-0.02, 0.02, (3, 1))
+        h = rng.uniform(0.1, 10.0, d)
+        best, Q = ref.brute_force(W, np.diag(h), bits)
+        t = ref.rtn(W, bits, 0)
+        want = float(np.sum(h[None, :] * (W - t.Q) ** 2))
+        assert best == pytest.approx(want, rel=1e-12, abs=1e-30), trial
+        assert np.allclose(Q, t.Q, rtol=0, atol=1e-15), trial
+
+
+def _f16_value(bits: int) -> float:
+    """Value of an IEEE 754 binary16 bit pattern: sign bit, 5 exponent bits biased by 15, 10 fraction
+    bits; exponent field 0 holds the subnormals m 2^-24."""
+    e, m = (bits >> 10) & 0x1F, bits & 0x3FF
+    assert e != 0x1F
+    v = m * 2.0 ** -24 if e == 0 else (1.0 + m / 1024.0) * 2.0 ** (e - 15)
+    return -v if bits >> 15 else v
+
+
+@pytest.mark.filterwarnings("ignore:overflow encountered in cast")
+def test_fp16_scale_hand_derived_bit_patterns():
+    """Compact scales round to the nearest float16, ties to even, with zero and overflow kept inside
+    the finite positive range: each case's float16 bit pattern is derived by hand in
+    tests/golden/hand_worked.json (exact midpoints included)."""
+    for c in HAND["float16_scale_rounding"]["cases"]:
+        x = float(Fraction(c["exact"]))
+        assert float(np.float32(x)) == x or c["exact"] in ("2/15", "1/150"), c["value"]
+        got = ref.fp16_scale(np.array([x]))[0]
+        assert got == _f16_value(int(c["float16"], 16)), c["value"]
+
+
+def test_follow_scale_adopts_only_at_float16_boundaries():
+    """_follow_scale may replace this oracle's 16-bit scale by the other side's only when the float32
+    scale lies within rtol of a float16 rounding boundary and the other scale is one of the two
+    float16 values around it."""
+    one, nxt, nxt2 = _f16_value(0x3C00), _f16_value(0x3C01), _f16_value(0x3C02)
+    mid = float(Fraction(2049, 2048))                 # the midpoint of 0x3C00 and 0x3C01
+    own = ref.fp16_scale(np.array([mid]))
+    assert own[0] == one                              # ties to even
+    out, n = ref._follow_scale(own, np.array([mid]), np.array([nxt]))
+    assert out[0] == nxt and n == 1                   # the other neighbour: adopted and counted
+    out, n = ref._follow_scale(own, np.array([mid]), np.array([one]))
+    assert out[0] == one and n == 0                   # the same choice: nothing counted
+    out, n = ref._follow_scale(own, np.array([mid]), np.array([nxt2]))
+    assert out[0] == one and n == 0                   # not a neighbour: refused
+    near = mid * (1.0 + 2.0 ** -21)                   # 4.8e-7 above the boundary: inside rtol
+    own_n = ref.fp16_scale(np.array([near]))
+    assert own_n[0] == nxt
+    out, n = ref._follow_scale(own_n, np.array([near]), np.array([one]))
+    assert out[0] == one and n == 1
+    far = 1.0 + 2.0 ** -12                            # 2.4e-4 from the nearest boundary: outside rtol
+    own_f = ref.fp16_scale(np.array([far]))
+    out, n = ref._follow_scale(own_f, np.array([far]), np.array([nxt]))
+    assert out[0] == own_f[0] == one and n == 0       # refused although a neighbour
+    out, n = ref._follow_scale(own, np.array([mid]), None)
+    assert out[0] == one and n == 0
 
 
 def test_two_weight_never_worse_than_rtn():
