@@ -29,7 +29,8 @@
  *   - Matrices are row-major. Pointers named as device memory must be device memory of the current
  *     HIP device; the caller allocates and owns every buffer and the library allocates no device
  *     memory. The only state it keeps: on first use on a device it creates two helper streams and a
- *     few events there (kept until the process ends), on which parts of a call run concurrently.
+ *     few events there (kept until the process ends), on which parts of a call run concurrently;
+ *     and one static device array, the workspace of gptq_factor_noalloc.
  *   - `stream` is a hipStream_t (NULL: the default stream). Work is queued on it and the call returns
  *     without waiting, except gptq_factor, which waits once for its own work (see there). Work a call
  *     places on the helper streams starts after the work queued on `stream` before the call and
@@ -146,6 +147,24 @@ gptq_status_t gptq_hessian_accumulate(float *H, int64_t d, const void *X, int32_
  */
 gptq_status_t gptq_factor(const float *H, int64_t d, int64_t n_total, const gptq_params_t *p, float *U,
                           int32_t *perm, void *work, size_t work_bytes, int64_t *info, void *stream);
+
+/*
+ * gptq_factor for callers that cannot allocate device memory: code under HIP graph capture, tight
+ * serving loops, harnesses that forbid allocation. Same arguments, results and errors as
+ * gptq_factor, without `work`: its workspace is a static device array inside the library (about
+ * 19 MB, held on each device the library runs on until the process ends), and every launch goes to
+ * `stream` (no helper stream or event is created). The call allocates nothing; the caller still
+ * passes H, U and perm (U == H allowed, as for gptq_factor).
+ *
+ *   d  at most GPTQ_FACTOR_NOALLOC_MAX_D; larger d returns GPTQ_EUNSUPPORTED.
+ *
+ * All calls on one device share that device's array, and each call overwrites it: calls that
+ * overlap on one device (on different streams or host threads) race. Like gptq_factor, the call
+ * waits for the stream once to read the pivot check.
+ */
+#define GPTQ_FACTOR_NOALLOC_MAX_D 12288
+gptq_status_t gptq_factor_noalloc(const float *H, int64_t d, int64_t n_total, const gptq_params_t *p, float *U,
+                                  int32_t *perm, int64_t *info, void *stream);
 
 /*
  * The GPTQ column loop for one layer (GPTQ tools page, "How it works", Steps 5, 7 and 8; the

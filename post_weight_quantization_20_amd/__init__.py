@@ -14,6 +14,7 @@ from .solver import (  # noqa: F401
     GPTQ_EUNSUPPORTED,
     GPTQ_F16,
     GPTQ_F32,
+    GPTQ_FACTOR_NOALLOC_MAX_D,
     GPTQ_LAYOUT_DENSE,
     GPTQ_LAYOUT_FIELDS,
     GPTQ_OK,
@@ -29,6 +30,7 @@ from .solver import (  # noqa: F401
     gptq_block_workspace_bytes,
     gptq_dequant_gemm,
     gptq_factor,
+    gptq_factor_noalloc,
     gptq_hessian_accumulate,
     gptq_pack,
     gptq_pack_dense,

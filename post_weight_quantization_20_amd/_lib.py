@@ -44,6 +44,8 @@ SIGNATURES = {
                                           c_void_p]),
     "gptq_factor": (c_int32, [c_void_p, c_int64, c_int64, ctypes.POINTER(gptq_params_t), c_void_p, c_void_p, c_void_p,
                               c_size_t, ctypes.POINTER(c_int64), c_void_p]),
+    "gptq_factor_noalloc": (c_int32, [c_void_p, c_int64, c_int64, ctypes.POINTER(gptq_params_t), c_void_p,
+                                      c_void_p, ctypes.POINTER(c_int64), c_void_p]),
     "gptq_quantize_layer": (c_int32, [c_void_p, c_int32, c_int64, c_int64, c_int64, c_void_p, c_void_p,
                                       ctypes.POINTER(gptq_params_t), c_void_p, c_void_p, c_void_p, c_void_p, c_void_p,
                                       c_void_p, c_size_t, c_void_p]),

@@ -16,7 +16,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libgptq.so")
-SOURCES = ["abi.hip", "runtime.hip", "gemm_f32.hip", "hessian.hip", "factor.hip", "quant.hip", "dequant.hip", "block.hip", "gemm_f16.hip"]
+SOURCES = ["abi.hip", "runtime.hip", "gemm_f32.hip", "hessian.hip", "factor.hip", "quant.hip", "dequant.hip", "block.hip", "gemm_f16.hip", "noalloc.hip"]
 ARCH = "gfx950"
 
 FLAGS = [

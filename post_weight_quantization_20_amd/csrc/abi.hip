@@ -79,20 +79,18 @@ gptq_status_t gptq_hessian_accumulate(float* H, int64_t d, const void* X, int32_
   return hip_status(gptq::hessian_f16(H, d, X, x_dtype, n_tok, ld_x, work, work_bytes, s));
 }
 
-gptq_status_t gptq_factor(const float* H, int64_t d, int64_t n_total, const gptq_params_t* p, float* U,
-                          int32_t* perm, void* work, size_t work_bytes, int64_t* info, void* stream) {
-  if (!H || !U || !perm || !info || !work || d <= 0 || d > kMaxDim || n_total <= 0) return GPTQ_EINVAL;
-  gptq_status_t st = check_params(p, d, false);
-  if (st != GPTQ_OK) return st;
-  const char* h0 = reinterpret_cast<const char*>(H);
-  const char* u0 = reinterpret_cast<const char*>(U);
-  const size_t bytes = (size_t)d * d * sizeof(float);
-  if (h0 != u0 && h0 < u0 + bytes && u0 < h0 + bytes) return GPTQ_EINVAL;   // in place, or apart
-  if (work_bytes < gptq::factor_workspace_bytes(d)) return GPTQ_ENOMEM;
-  hipStream_t s = static_cast<hipStream_t>(stream);
+}  // extern "C"
+
+namespace {
+
+// The checks and the call shared by gptq_factor and gptq_factor_noalloc: work is the workspace (the
+// caller's, or the static scratch), one_stream keeps every launch on the caller's stream.
+gptq_status_t factor_call(const float* H, int64_t d, int64_t n_total, const gptq_params_t* p, float* U,
+                          int32_t* perm, void* work, int64_t* info, hipStream_t s, bool one_stream) {
   int* status_dev = nullptr;
   int64_t* info_dev = nullptr;
-  hipError_t e = gptq::factor(H, d, n_total, p->damp, p->act_order, U, perm, work, s, &status_dev, &info_dev);
+  hipError_t e = gptq::factor(H, d, n_total, p->damp, p->act_order, U, perm, work, s, &status_dev, &info_dev,
+                              one_stream);
   if (e != hipSuccess) return GPTQ_EHIP;
   int64_t dev_info = 0;
   int dev_status = 0;
@@ -104,6 +102,43 @@ gptq_status_t gptq_factor(const float* H, int64_t d, int64_t n_total, const gptq
   *info = dev_info > 0 ? d - dev_info + 1 : 0;
   if (dev_status != 0) return GPTQ_EINVAL;
   return dev_info != 0 ? GPTQ_ENOTPD : GPTQ_OK;
+}
+
+gptq_status_t factor_args(const float* H, int64_t d, int64_t n_total, const gptq_params_t* p, const float* U,
+                          const int32_t* perm, const int64_t* info) {
+  if (!H || !U || !perm || !info || d <= 0 || d > kMaxDim || n_total <= 0) return GPTQ_EINVAL;
+  gptq_status_t st = check_params(p, d, false);
+  if (st != GPTQ_OK) return st;
+  const char* h0 = reinterpret_cast<const char*>(H);
+  const char* u0 = reinterpret_cast<const char*>(U);
+  const size_t bytes = (size_t)d * d * sizeof(float);
+  if (h0 != u0 && h0 < u0 + bytes && u0 < h0 + bytes) return GPTQ_EINVAL;   // in place, or apart
+  return GPTQ_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+gptq_status_t gptq_factor(const float* H, int64_t d, int64_t n_total, const gptq_params_t* p, float* U,
+                          int32_t* perm, void* work, size_t work_bytes, int64_t* info, void* stream) {
+  gptq_status_t st = factor_args(H, d, n_total, p, U, perm, info);
+  if (st != GPTQ_OK) return st;
+  if (!work) return GPTQ_EINVAL;
+  if (work_bytes < gptq::factor_workspace_bytes(d)) return GPTQ_ENOMEM;
+  return factor_call(H, d, n_total, p, U, perm, work, info, static_cast<hipStream_t>(stream), false);
+}
+
+gptq_status_t gptq_factor_noalloc(const float* H, int64_t d, int64_t n_total, const gptq_params_t* p, float* U,
+                                  int32_t* perm, int64_t* info, void* stream) {
+  gptq_status_t st = factor_args(H, d, n_total, p, U, perm, info);
+  if (st != GPTQ_OK) return st;
+  if (d > GPTQ_FACTOR_NOALLOC_MAX_D) return GPTQ_EUNSUPPORTED;
+  static_assert(GPTQ_FACTOR_NOALLOC_MAX_D == gptq::kNoallocMaxD, "scratch sized for another maximum");
+  if (gptq::factor_workspace_bytes(d) > gptq::kNoallocScratchBytes) return GPTQ_EUNSUPPORTED;
+  void* scratch = nullptr;
+  if (gptq::noalloc_scratch(&scratch) != hipSuccess) return GPTQ_EHIP;
+  return factor_call(H, d, n_total, p, U, perm, scratch, info, static_cast<hipStream_t>(stream), true);
 }
 
 gptq_status_t gptq_quantize_layer(const void* W, int32_t w_dtype, int64_t rows, int64_t d, int64_t ld_w,

@@ -548,7 +548,7 @@ size_t factor_workspace_bytes(int64_t d) { return 256 + factor_keys_bytes(d) + 3
 // Returns hipSuccess after queueing everything; *status_out / *info_out are device addresses of the
 // status word and pivot index (read by the caller after a stream synchronisation).
 hipError_t factor(const float* H, int64_t d, int64_t n, double damp, int act_order, float* U, int32_t* perm,
-                  void* work, hipStream_t s, int** status_dev, int64_t** info_dev) {
+                  void* work, hipStream_t s, int** status_dev, int64_t** info_dev, bool one_stream) {
   char* wb = static_cast<char*>(work);
   FactorWork w;
   w.lam = reinterpret_cast<double*>(wb);
@@ -580,13 +580,19 @@ hipError_t factor(const float* H, int64_t d, int64_t n, double damp, int act_ord
   // the column panel the inverse step overwrites), and touches only columns left of block j + 1,
   // which the later Cholesky steps neither read nor write. A cross-stream wait costs the host several
   // microseconds, so hs waits once per TB Cholesky steps and then runs those TB inverse steps.
+  // With one_stream, hs is s itself and the steps simply follow one another.
   constexpr int64_t TB = 4;
   Helpers* hp = nullptr;
-  hipError_t e = helpers(&hp);
-  if (e != hipSuccess) return e;
-  hipStream_t hs = hp->stream[1];
-  hipEvent_t ev_step = hp->event[4], ev_done = hp->event[5];
-  helpers_lock(hp);
+  hipError_t e = hipSuccess;
+  hipStream_t hs = s;
+  hipEvent_t ev_step = nullptr, ev_done = nullptr;
+  if (!one_stream) {
+    if ((e = helpers(&hp)) != hipSuccess) return e;
+    hs = hp->stream[1];
+    ev_step = hp->event[4];
+    ev_done = hp->event[5];
+    helpers_lock(hp);
+  }
   const int64_t nblk = (d + NB - 1) / NB;
   const int vec = d % 4 == 0 && (uintptr_t)U % 16 == 0;
   for (int64_t kt = 0; kt < nblk && e == hipSuccess; kt += TB) {
@@ -618,8 +624,10 @@ hipError_t factor(const float* H, int64_t d, int64_t n, double damp, int act_ord
       }
     }
     if (e != hipSuccess) break;
-    if ((e = hipEventRecord(ev_step, s)) != hipSuccess) break;
-    if ((e = hipStreamWaitEvent(hs, ev_step, 0)) != hipSuccess) break;
+    if (!one_stream) {
+      if ((e = hipEventRecord(ev_step, s)) != hipSuccess) break;
+      if ((e = hipStreamWaitEvent(hs, ev_step, 0)) != hipSuccess) break;
+    }
     // inverse steps kt .. kend - 1 on hs (their diagonal blocks are already inverted)
     for (int64_t k = kt; k < kend && e == hipSuccess; ++k) {
       const int64_t k0 = k * NB, k1 = std::min(d, k0 + NB), kb = k1 - k0;
@@ -666,11 +674,13 @@ hipError_t factor(const float* H, int64_t d, int64_t n, double damp, int act_ord
       }
     }
   }
-  // join the helper stream (also after a failed launch, so nothing is left behind)
-  hipError_t j = hipEventRecord(ev_done, hs);
-  if (j == hipSuccess) j = hipStreamWaitEvent(s, ev_done, 0);
-  helpers_unlock(hp);
-  if (e == hipSuccess) e = j;
+  if (!one_stream) {
+    // join the helper stream (also after a failed launch, so nothing is left behind)
+    hipError_t j = hipEventRecord(ev_done, hs);
+    if (j == hipSuccess) j = hipStreamWaitEvent(s, ev_done, 0);
+    helpers_unlock(hp);
+    if (e == hipSuccess) e = j;
+  }
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(flip_kernel, dim3((unsigned)d), dim3(256), 0, s, U, d);
   return hipGetLastError();

@@ -158,6 +158,27 @@ def gptq_factor(H: torch.Tensor, n_total: int, params: Params, U: Optional[torch
     return U, perm
 
 
+GPTQ_FACTOR_NOALLOC_MAX_D = 12288
+
+
+def gptq_factor_noalloc(H: torch.Tensor, n_total: int, params: Params, U: torch.Tensor, perm: torch.Tensor,
+                        stream=None) -> Tuple[torch.Tensor, torch.Tensor]:
+    """gptq_factor with the library's static scratch instead of a workspace, every launch on one
+    stream, and no allocation in the call (U and perm are the caller's; U may be H). d is at most
+    GPTQ_FACTOR_NOALLOC_MAX_D. Calls that overlap on one device race on the shared scratch."""
+    _need_cuda(H, U, perm)
+    d = H.shape[0]
+    if H.dtype != torch.float32 or H.shape != (d, d) or not H.is_contiguous():
+        raise ValueError("H must be a contiguous float32 [d, d] tensor")
+    _want(U, (d, d), torch.float32, "U", H.device)
+    _want(perm, (d,), torch.int32, "perm", H.device)
+    info = ctypes.c_int64(0)
+    st = _lib.lib().gptq_factor_noalloc(_ptr(H), d, int(n_total), ctypes.byref(params.c()), _ptr(U), _ptr(perm),
+                                        ctypes.byref(info), _stream(stream))
+    _check(st, info.value)
+    return U, perm
+
+
 def gptq_quantize_layer(W: torch.Tensor, U: torch.Tensor, perm: torch.Tensor, params: Params,
                         out: Optional[QuantOutput] = None, work: Optional[torch.Tensor] = None,
                         stream=None) -> QuantOutput:

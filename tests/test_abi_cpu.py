@@ -115,6 +115,27 @@ def test_factor_rejects_bad_arguments():
     assert info.value == 7  # untouched on rejection
 
 
+def test_factor_noalloc_rejects_bad_arguments():
+    """The allocation-free factor takes gptq_factor's checks, and rejects d above its static scratch's
+    maximum before touching the device."""
+    L = _lib()
+    lib = L.lib()
+    info = ctypes.c_int64(7)
+    p = _p(L)
+    f = lib.gptq_factor_noalloc
+    far = ctypes.c_void_p(1 << 40)
+    assert f(None, 16, 10, ctypes.byref(p), far, FAKE, ctypes.byref(info), None) == -1
+    assert f(FAKE, 16, 0, ctypes.byref(p), far, FAKE, ctypes.byref(info), None) == -1
+    assert f(FAKE, 16, 10, ctypes.byref(p), ctypes.c_void_p(0x1000 + 64), FAKE, ctypes.byref(info), None) == -1
+    assert f(FAKE, 16, 10, ctypes.byref(_p(L, damp=-1.0)), far, FAKE, ctypes.byref(info), None) == -1
+    assert f(FAKE, 16, 10, ctypes.byref(p), far, FAKE, None, None) == -1
+    assert f(FAKE, 12289, 10, ctypes.byref(p), far, FAKE, ctypes.byref(info), None) == -3
+    assert info.value == 7  # untouched on rejection
+    from post_weight_quantization_20_amd import solver
+    assert solver.GPTQ_FACTOR_NOALLOC_MAX_D == 12288
+    assert "#define GPTQ_FACTOR_NOALLOC_MAX_D 12288" in open(HEADER).read()
+
+
 def test_quantize_rejects_bad_arguments():
     L = _lib()
     lib = L.lib()
