@@ -294,7 +294,7 @@ def quantize_layer(W: np.ndarray, U: np.ndarray, bits: int, group_size: int, blo
     """
     W = np.asarray(W, dtype=np.float64)
     rows, d = W.shape
-    U = np.asarray(U, dtype=np.float64)
+    U = np.asarray(U)            # float64, or float32 (each block's rows are upcast exactly when used)
     if U.shape != (d, d):
         raise ValueError("U shape")
     g = check_geometry(d, group_size, block_size)
@@ -342,6 +342,7 @@ def quantize_layer(W: np.ndarray, U: np.ndarray, bits: int, group_size: int, blo
     s = z = None
     for b in range(0, d, B):
         e_blk = min(b + B, d)
+        Ub = np.asarray(U[b:e_blk], dtype=np.float64)     # the block's rows of U: Ub[i - b] is U[i]
         Err = np.zeros((rows, e_blk - b), dtype=np.float64)
         for i in range(b, e_blk):
             if static_groups and grid is None:
@@ -369,13 +370,13 @@ def quantize_layer(W: np.ndarray, U: np.ndarray, bits: int, group_size: int, blo
                 near += nt
             codes_p[:, i] = q
             Qp[:, i] = dq
-            err = (w - dq) / U[i, i]
+            err = (w - dq) / Ub[i - b, i]
             Err[:, i - b] = err
             row_loss += err * err
             if i + 1 < e_blk:
-                Wp[:, i + 1:e_blk] -= np.outer(err, U[i, i + 1:e_blk])
+                Wp[:, i + 1:e_blk] -= np.outer(err, Ub[i - b, i + 1:e_blk])
         if e_blk < d:
-            Wp[:, e_blk:] -= Err @ U[b:e_blk, e_blk:]
+            Wp[:, e_blk:] -= Err @ Ub[:, e_blk:]
 
     codes = np.zeros((rows, d), dtype=np.uint8)
     codes[:, perm] = codes_p.astype(np.uint8)

@@ -130,9 +130,12 @@ def test_llama7b_block_full_size():
     * stage 0's Hessian on sampled entries (its input, RMSNorm(X), is cheap to form for every token),
       within the float32 summation bound over one token slice plus the fp16 split and the input's
       rounding;
-    * q and down (stages 0 and 3, widths 4096 and 11008): the oracle's factor of the GPU's Hessian,
-      sampled rows of the column loop to the layer bar, and the reported loss against the damped
-      quadratic form of the whole dequantized layer;
+    * all seven layers, stage by stage (q, k, v on stage 0; o on 1; gate, up on 2; down on 3, widths
+      4096 and 11008): the oracle's factor of the GPU's stage Hessian (the one processing order all
+      of a stage's layers share), sampled rows of each layer's column loop to the layer bar, and each
+      reported loss against the damped quadratic form of the whole dequantized layer. Stages 1-3
+      are staged parity: their inputs come from the quantized earlier stages over all 262144 tokens,
+      which the oracle cannot recompute within a test, so it solves on the GPU's Hessians;
     * the block output of the first sequence (2048 tokens, every head), against the oracle's forward
       pass through all seven of the GPU's quantized layers."""
     import types
@@ -156,7 +159,8 @@ def test_llama7b_block_full_size():
                  g_idx=q.g_idx.cpu().numpy(), loss=float(q.loss.cpu().numpy()[0]), packed=None,
                  perm=p.cpu().numpy().astype(np.int64)) for q, p in zip(r.layers, r.perms)]
     Y0 = r.Y[:L].cpu().numpy().astype(np.float64)
-    H0, H3 = r.hessians[0].cpu().numpy(), r.hessians[3].cpu().numpy()
+    Hst = [h.cpu().numpy() for h in r.hessians]
+    H0 = Hst[0]
     del r
     torch.cuda.empty_cache()
     n = case.seqs * L
@@ -182,21 +186,27 @@ def test_llama7b_block_full_size():
     print(f"[block full] max |dH|/bound {float(np.max(np.abs(got - want) / bound)):.3f}", flush=True)
     del A
 
-    # q (stage 0) and down (stage 3): oracle factor of the GPU's Hessian, sampled rows, loss
-    for li, Hu in ((0, H0), (6, H3)):
-        rows_l, d = synth.block_layer_dims(case, li)
-        lc = types.SimpleNamespace(bits=4, group_size=128, block_size=128, w_dtype="f16", rows=rows_l, d=d)
-        Hs = _sym(Hu)
-        perm = _checked_perm(outs[li]["perm"], Hs)
+    # every layer, stage by stage: oracle factor of the GPU's stage Hessian, sampled rows, loss
+    stage_of = (0, 0, 0, 1, 2, 2, 3)
+    for si in range(4):
+        lis = [li for li in range(7) if stage_of[li] == si]
+        Hs = _sym(Hst[si])
+        perm = _checked_perm(outs[lis[0]]["perm"], Hs)
+        for li in lis[1:]:
+            assert np.array_equal(outs[li]["perm"], outs[lis[0]]["perm"]), "a stage's layers share one order"
         Hh, perm, lam = ref.damp_and_order(Hs, n, 0.01, True, perm=perm)
-        print(f"[block full] oracle factor d={d}", flush=True)
+        print(f"[block full] stage {si}: oracle factor d={Hs.shape[0]}", flush=True)
         Uo = ref.inverse_cholesky_upper(Hh)
-        rows = np.unique(np.concatenate([np.arange(8), rng.choice(rows_l, 16, replace=False),
-                                         np.arange(rows_l - 8, rows_l)]))
-        print(f"[block full] layer {blk.LAYERS[li]}: sampled rows and loss", flush=True)
-        _check_rows(lc, W_host[li], outs[li], Hh, Uo, perm, rows)
-        _check_loss_identity(lc, W_host[li], outs[li], Hh, perm)
+        for li in lis:
+            rows_l, d = synth.block_layer_dims(case, li)
+            lc = types.SimpleNamespace(bits=4, group_size=128, block_size=128, w_dtype="f16", rows=rows_l, d=d)
+            rows = np.unique(np.concatenate([np.arange(8), rng.choice(rows_l, 16, replace=False),
+                                             np.arange(rows_l - 8, rows_l)]))
+            print(f"[block full] layer {blk.LAYERS[li]}: sampled rows and loss", flush=True)
+            _check_rows(lc, W_host[li], outs[li], Hh, Uo, perm, rows)
+            _check_loss_identity(lc, W_host[li], outs[li], Hh, perm)
         del Hs, Hh, Uo
+    del Hst
 
     # the first sequence's block output through the GPU's quantized layers
     print("[block full] oracle forward of sequence 0", flush=True)

@@ -15,11 +15,11 @@ those). Compared:
   (W - Q)_r Hhat (W - Q)_r^T), which holds at any size;
 * pack: every word against the closed-form bit positions.
 
-q_proj runs exactly the benchmark's workload (4096 x 4096, 262144 tokens). down_proj keeps its width,
-rows and act-order with 4096 tokens, so the oracle's factor of an 11008-wide Hessian stays affordable;
-its Hessian then takes the path without token splits, as the full token count does. The Llama-7B
-decoder block keeps every layer's rows and width and shares each input's Hessian and factor among the
-layers that read it, with 8192 tokens (4096 for the 11008-wide input).
+q_proj and down_proj run their workloads exactly (4096 x 4096 and 4096 x 11008 with act-order, 262144
+tokens each). fc2 (12288 x 49152) is checked in stages (see its test). The Llama-7B decoder block's
+shared-input cases keep every layer's rows and width and share each input's Hessian and factor among
+the layers that read it, with 8192 tokens (4096 for the 11008-wide input); the whole block at its full
+262144 tokens is tests/test_block_gpu.py::test_llama7b_block_full_size.
 """
 
 import dataclasses
@@ -72,6 +72,15 @@ def _oracle_hessian(case, X_host):
     return ref.hessian(synth.to_f64(X_host[c * ch:(c + 1) * ch], case.x_dtype) for c in range(case.n_chunks))
 
 
+def _abs_gram(X_host, dtype, cols, step=16384):
+    """2 |X[:, cols]|^T |X[:, cols]| in float64, in passes over the token rows."""
+    G = np.zeros((len(cols), len(cols)))
+    for t0 in range(0, X_host.shape[0], step):
+        a = np.abs(synth.to_f64(X_host[t0:t0 + step][:, cols], dtype))
+        G += 2.0 * a.T @ a
+    return G
+
+
 def _check_hessian(Hg, Ho, X_host, case, rng):
     n, d = case.n, case.d
     up = np.triu_indices(d)
@@ -81,8 +90,8 @@ def _check_hessian(Hg, Ho, X_host, case, rng):
     i = rng.integers(0, d, SAMPLE_PAIRS)
     j = rng.integers(0, d, SAMPLE_PAIRS)
     i, j = np.minimum(i, j), np.maximum(i, j)
-    col = lambda c: np.abs(synth.to_f64(X_host[:, c], case.x_dtype))
-    absH = np.array([2.0 * np.dot(col(a), col(b)) for a, b in zip(i, j)])
+    cols, inv = np.unique(np.concatenate([i, j]), return_inverse=True)
+    absH = _abs_gram(X_host, case.x_dtype, cols)[inv[:SAMPLE_PAIRS], inv[SAMPLE_PAIRS:]]
     bound = (n * U32 / (1 - n * U32)) * absH + 1e-30
     assert np.all(np.abs(Hg[i, j].astype(np.float64) - Ho[i, j]) <= bound)
 
@@ -93,10 +102,27 @@ def _lapack_f32_error(Hh, Uo):
     return float(np.max(np.abs(U32f - Uo)) / np.max(np.abs(Uo)))
 
 
+def _sym(Hu):
+    """The symmetric matrix whose upper triangle Hu holds (the GPU writes only that), in float64."""
+    Hu = np.triu(Hu.astype(np.float64))
+    return Hu + np.triu(Hu, 1).T
+
+
+def _factor_on_gpu_hessian(Hg, n, case, perm, rng):
+    """The factor judged on the matrix it was given: the GPU's U against the oracle's factor of the
+    GPU's own (float32-summed) Hessian, damped and ordered the same way."""
+    Hh_g, _, lam_g = ref.damp_and_order(_sym(Hg), n, case.damp, case.act_order,
+                                        perm=perm if case.act_order else None)
+    Uo_g = ref.inverse_cholesky_upper(Hh_g)
+    return Hh_g, Uo_g, lam_g
+
+
 def _check_factor(Ug, Hh, Uo, lam, rng):
-    """U against the oracle's: within FACTOR_VS_LAPACK times the error of float32 LAPACK on the same
-    matrix. The residual (U^T U Hhat - I) on sampled columns stays within d * kappa * u32, with kappa
-    bounded from above (lambda_max <= the largest absolute row sum, lambda_min >= lam)."""
+    """U against the oracle's factor of the same damped matrix (the GPU's Hessian, so that the
+    Hessian's own float32 error, checked apart, is not counted twice): within FACTOR_VS_LAPACK times
+    the error of float32 LAPACK on that matrix. The residual (U^T U Hhat - I) on sampled columns
+    stays within d * kappa * u32, with kappa bounded from above (lambda_max <= the largest absolute
+    row sum, lambda_min >= lam)."""
     d = Hh.shape[0]
     ks = rng.choice(d, SAMPLE_COLS, replace=False)
     U64 = Ug.astype(np.float64)
@@ -112,10 +138,24 @@ def _check_factor(Ug, Hh, Uo, lam, rng):
     print(f"d={d} kappa<={kappa:.3g} U max rel err {err:.3g} (float32 LAPACK {ref32:.3g})")
 
 
-def _checked_perm(gperm, H, rtol=1e-5):
+def _checked_perm(gperm, H, rtol=1e-5, Hg=None, n=None):
+    """The GPU's act-order processing order, checked. With the GPU's own Hessian Hg (summed over n
+    tokens in float32): its diagonal is exactly non-increasing along the order, ties by lower index
+    (the sort itself), and every diagonal entry is within the float32 summation bound of the
+    oracle's (a sum of n non-negative terms: gamma_n times the sum). Keys closer than that bound may
+    come in either order. Without Hg: descending in the oracle's diagonal within rtol."""
     d = H.shape[0]
     assert np.array_equal(np.sort(gperm), np.arange(d))
     own = ref.act_order_perm(H)
+    if Hg is not None:
+        kg = np.diag(Hg).astype(np.float64)
+        assert np.array_equal(np.argsort(-kg, kind="stable"), gperm), "GPU order is not its keys' sorted order"
+        gam = n * U32 / (1 - n * U32)
+        dev = np.abs(kg - np.diag(H)) / np.diag(H)
+        print(f"act-order keys: max relative deviation {float(np.max(dev)):.3g} (float32 bound {gam:.3g}); "
+              f"{int(np.count_nonzero(own != gperm))} positions differ from the oracle's own order", flush=True)
+        assert np.all(dev <= gam)
+        return gperm
     if np.array_equal(own, gperm):
         return own
     dk = np.diag(H)[gperm]
@@ -174,11 +214,15 @@ def _fullsize(case, seed):
     assert n == case.n
     _check_hessian(out["H"], H, X_host, case, rng)
     del X_host
-    perm = _checked_perm(out["perm"], H) if case.act_order else np.arange(case.d)
+    perm = _checked_perm(out["perm"], H, Hg=out["H"], n=n) if case.act_order else np.arange(case.d)
     Hh, perm, lam = ref.damp_and_order(H, n, case.damp, case.act_order, perm=perm if case.act_order else None)
-    print("[fullsize] oracle factor", flush=True)
+    print("[fullsize] oracle factors (exact Hessian; the GPU's Hessian)", flush=True)
     Uo = ref.inverse_cholesky_upper(Hh)
-    _check_factor(out["U"], Hh, Uo, lam, rng)
+    Hh_g, Uo_g, lam_g = _factor_on_gpu_hessian(out.pop("H"), n, case, perm, rng)
+    _check_factor(out["U"], Hh_g, Uo_g, lam_g, rng)
+    print(f"[fullsize] U against the exact Hessian's factor: max rel err "
+          f"{float(np.max(np.abs(out['U'] - Uo)) / np.max(np.abs(Uo))):.3g}", flush=True)
+    del Hh_g, Uo_g
     rows = np.unique(np.concatenate([np.arange(16), rng.choice(case.rows, SAMPLE_ROWS - 32, replace=False),
                                      np.arange(case.rows - 16, case.rows)]))
     print("[fullsize] oracle column loop on sampled rows", flush=True)
@@ -192,9 +236,12 @@ def test_q_proj_full_size():
     _fullsize(synth.case_from_config("q_proj"), 101)
 
 
-def test_down_proj_width_act_order():
-    """down_proj's 4096 x 11008 layer with act-order and 4096 Laplace-distributed tokens."""
-    _fullsize(synth.case_from_config("down_proj", n=4096), 102)
+def test_down_proj_full_size():
+    """The down_proj workload itself: 4096 x 11008 fp16 with act-order, 262144 Laplace-distributed
+    tokens with 0.5% outlier channels x30 (tools page, "How it works", Step 1: a few hundred
+    sequences of 2048 tokens). Its 11008-wide Hessian is the one the decoder block's down stage
+    forms."""
+    _fullsize(synth.case_from_config("down_proj"), 102)
 
 
 def _tie(num, den, tau=TAU):
@@ -204,14 +251,17 @@ def _tie(num, den, tau=TAU):
     return np.abs(f - 0.5) < tau
 
 
-def test_fc2_full_size_properties():
+def test_fc2_full_size():
     """OPT-175B fc2-shaped layer at full size (12288 x 49152, 131072 tokens, 3-bit, one group per
-    row). The oracle cannot factor a 49152-wide Hessian within a test, so it checks what it computes
-    one by one and what holds at any size: sampled Hessian entries and the whole diagonal; the
-    factor's residual (U^T U Hhat - I) e_k on sampled columns, with Hhat e_k formed from X; every
-    row's scale and zero point (one group per row: the grid of the unmodified row); every row's code
-    of the first processed column (no error feedback has reached it); the packed words; and, in
-    aggregate over sampled rows, a lower damped objective than round-to-nearest."""
+    row). The oracle cannot form or factor a 49152-wide Hessian within a test, so parity is staged:
+    * Hessian: sampled entries and the whole diagonal against the exact sums from X;
+    * factor: the residual (U^T U Hhat - I) e_k on 64 sampled columns, with Hhat e_k formed from X;
+    * column loop: only once the GPU's U has passed that check, the oracle runs the loop itself over
+      all 49152 columns for 16 sampled rows on that U (read one block of rows at a time): codes and
+      zeros identical outside tie windows, scales within 1e-5, and the rows' reconstruction error
+      (their damped objective, formed from X) within 1e-3 of the oracle's loss;
+    * every row's scale and zero (one group per row: the grid of the unmodified row), every row's
+      first-column code, the packed words, and the sampled rows' objective below round-to-nearest's."""
     torch = torch_cuda()
     case = synth.case_from_config("fc2")
     rng = np.random.default_rng(103)
@@ -225,25 +275,32 @@ def test_fc2_full_size_properties():
     i = rng.integers(0, d, SAMPLE_PAIRS)
     j = rng.integers(0, d, SAMPLE_PAIRS)
     i, j = np.minimum(i, j), np.maximum(i, j)
-    col = lambda c: synth.to_f64(X[:, c], case.x_dtype)
-    exact = np.array([2.0 * np.dot(col(a), col(b)) for a, b in zip(i, j)])
-    absH = np.array([2.0 * np.dot(np.abs(col(a)), np.abs(col(b))) for a, b in zip(i, j)])
-    assert np.all(np.abs(Hg[i, j] - exact) <= (n * U32 / (1 - n * U32)) * absH + 1e-30)
-    # one pass over X: the diagonal, H e_k for sampled k, and X (W - Q)^T for sampled rows
+    cols, inv = np.unique(np.concatenate([i, j]), return_inverse=True)
+    # one pass over X: the sampled pairs' exact and absolute sums, the diagonal, H e_k for sampled k,
+    # and X (W - Q)^T for the sampled rows
     W = synth.to_f64(W_host, case.w_dtype)
-    ks = rng.choice(d, 4, replace=False)
-    rows = rng.choice(case.rows, 16, replace=False)
+    ks = rng.choice(d, 64, replace=False)
+    rows = np.sort(rng.choice(case.rows, 16, replace=False))
     Qg = dequant(out["codes"][rows], out["scales"][rows], out["zeros"][rows], out["g_idx"])
     Qr = ref.rtn(W[rows], case.bits, case.group_size).Q
     DT = np.concatenate([W[rows] - Qg, W[rows] - Qr]).T
     diag = np.zeros(d)
     HE = np.zeros((d, len(ks)))
     XD = np.zeros(2 * len(rows))
+    G = np.zeros((len(cols), len(cols)))
+    Ga = np.zeros((len(cols), len(cols)))
     for t0 in range(0, n, 8192):
         xs = synth.to_f64(X[t0:t0 + 8192], case.x_dtype)
         diag += 2.0 * np.einsum("ij,ij->j", xs, xs)
         HE += 2.0 * xs.T @ xs[:, ks]
         XD += np.sum((xs @ DT) ** 2, axis=0)
+        xc = xs[:, cols]
+        G += 2.0 * xc.T @ xc
+        Ga += 2.0 * np.abs(xc).T @ np.abs(xc)
+    del xs, xc
+    exact = G[inv[:SAMPLE_PAIRS], inv[SAMPLE_PAIRS:]]
+    absH = Ga[inv[:SAMPLE_PAIRS], inv[SAMPLE_PAIRS:]]
+    assert np.all(np.abs(Hg[i, j] - exact) <= (n * U32 / (1 - n * U32)) * absH + 1e-30)
     assert np.all(np.abs(np.diag(Hg) - diag) <= (n * U32 / (1 - n * U32)) * diag)
     del Hg, X
     # factor: residual on sampled columns, Hhat e_k = (H e_k) / n + lam e_k
@@ -258,10 +315,9 @@ def test_fc2_full_size_properties():
     for r0 in range(0, d, 4096):
         R += Ug[r0:r0 + 4096].astype(np.float64).T @ V[r0:r0 + 4096]
     R[ks, np.arange(len(ks))] -= 1.0
-    print(f"[fullsize] fc2 factor residual {np.max(np.abs(R)):.3g}", flush=True)
+    print(f"[fullsize] fc2 factor residual on {len(ks)} columns {np.max(np.abs(R)):.3g}", flush=True)
     # float32 arithmetic leaves about 5e-6 here; an operand read while being overwritten left 1e-2
     assert np.max(np.abs(R)) <= 1e-3
-    del Ug
     # one group per row: every row's grid comes from the unmodified row
     s_o, z_o = ref.group_grid(W, maxq)
     s_g = out["scales"][:, 0].astype(np.float64)
@@ -281,11 +337,23 @@ def test_fc2_full_size_properties():
     # codes in range, packed words at their bit positions
     assert int(out["codes"].max()) <= maxq
     _check_pack(case, out)
-    # aggregate comparison with round-to-nearest on the sampled rows (damped objective from X)
+    # staged parity of the column loop: the oracle's loop on the sampled rows, on the GPU's checked U
+    print(f"[fullsize] fc2 oracle column loop on {len(rows)} rows x {d} columns (GPU's U)", flush=True)
+    codes = out["codes"][rows]
+    o = ref.quantize_layer(W[rows], Ug, case.bits, case.group_size, case.block_size,
+                           follow=(codes, out["zeros"][rows]), tau=TAU)
+    del Ug
+    mism = int(np.count_nonzero(codes != o.codes))
+    assert mism == 0, f"{mism} of {codes.size} sampled codes differ outside tie windows"
+    assert np.array_equal(out["zeros"][rows], o.zeros)
+    assert o.adopted_diff <= 1e-3 * codes.size, (o.adopted_diff, codes.size)
+    assert float(np.max(np.abs(s_g[rows] - o.scales[:, 0]) / o.scales[:, 0])) <= SCALE_RTOL
     Dg, Dr = DT[:, :len(rows)], DT[:, len(rows):]
     obj_g = 2.0 / n * XD[:len(rows)].sum() + lam * np.sum(Dg ** 2)
     obj_r = 2.0 / n * XD[len(rows):].sum() + lam * np.sum(Dr ** 2)
-    print(f"[fullsize] fc2 damped objective on {len(rows)} rows: GPTQ {obj_g:.4g}, RTN {obj_r:.4g}", flush=True)
+    print(f"[fullsize] fc2 sampled rows: GPU objective {obj_g:.6g}, oracle loss {o.loss:.6g}, RTN {obj_r:.4g}; "
+          f"{o.near_ties} decisions in tie windows, {o.adopted_diff} taken differently", flush=True)
+    assert abs(obj_g - o.loss) <= LOSS_RTOL * o.loss, (obj_g, o.loss)
     assert obj_g < obj_r
 
 
@@ -334,10 +402,12 @@ def test_llama7b_block_shared_hessians(input_id):
     assert n_o == n
     _check_hessian(Hg, Ho, X_host, case, rng)
     del X_host
-    p = _checked_perm(pg, Ho)
+    p = _checked_perm(pg, Ho, Hg=Hg, n=n)
     Hh, p, lam = ref.damp_and_order(Ho, n, case.damp, True, perm=p)
     Uo = ref.inverse_cholesky_upper(Hh)
-    _check_factor(Ug, Hh, Uo, lam, rng)
+    Hh_g, Uo_g, lam_g = _factor_on_gpu_hessian(Hg, n, case, p, rng)
+    _check_factor(Ug, Hh_g, Uo_g, lam_g, rng)
+    del Hh_g, Uo_g
     for c, W_host, out in outs:
         rows = np.unique(np.concatenate([np.arange(8), rng.choice(c.rows, 24, replace=False),
                                          np.arange(c.rows - 8, c.rows)]))

@@ -27,14 +27,16 @@ def _f16_value(bits: int) -> float:
     return -v if bits >> 15 else v
 
 MUTATIONS = [
-    ("drop lazy update", "Wp[:, e_blk:] -= Err @ U[b:e_blk, e_blk:]", "pass"),
-    ("wrong update sign", "Wp[:, i + 1:e_blk] -= np.outer(err, U[i, i + 1:e_blk])",
-     "Wp[:, i + 1:e_blk] += np.outer(err, U[i, i + 1:e_blk])"),
-    ("transposed factor row", "Wp[:, i + 1:e_blk] -= np.outer(err, U[i, i + 1:e_blk])",
+    ("drop lazy update", "Wp[:, e_blk:] -= Err @ Ub[:, e_blk:]", "pass"),
+    ("wrong update sign", "Wp[:, i + 1:e_blk] -= np.outer(err, Ub[i - b, i + 1:e_blk])",
+     "Wp[:, i + 1:e_blk] += np.outer(err, Ub[i - b, i + 1:e_blk])"),
+    ("transposed factor row", "Wp[:, i + 1:e_blk] -= np.outer(err, Ub[i - b, i + 1:e_blk])",
      "Wp[:, i + 1:e_blk] -= np.outer(err, U[i + 1:e_blk, i])"),
-    ("unscaled error", "err = (w - dq) / U[i, i]", "err = (w - dq)"),
-    ("transposed lazy operand", "Wp[:, e_blk:] -= Err @ U[b:e_blk, e_blk:]",
+    ("unscaled error", "err = (w - dq) / Ub[i - b, i]", "err = (w - dq)"),
+    ("transposed lazy operand", "Wp[:, e_blk:] -= Err @ Ub[:, e_blk:]",
      "Wp[:, e_blk:] -= Err @ U[e_blk:, b:e_blk].T[:, :U.shape[0] - e_blk]"),
+    ("factor block taken by columns", "Ub = np.asarray(U[b:e_blk], dtype=np.float64)",
+     "Ub = np.asarray(U[:, b:e_blk].T, dtype=np.float64)"),
     ("grid from original weights", "s, z = grid_of(Wp[:, i:min(i + g, d)], gi)",
      "s, z = grid_of(W[:, perm][:, i:min(i + g, d)], gi)"),
     ("zero not added", "q = np.clip(_round_ratio(w, scale) + zero, 0.0, float(maxq))",
