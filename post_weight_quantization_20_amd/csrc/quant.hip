@@ -27,20 +27,25 @@ struct QArgs {
   float* Wp;             // working weights, processing order, [rows x ldw]
   int64_t ldw;
   int64_t rows, d;
-  int64_t b;             // first column of the block
-  int ncols;             // columns in this block (<= 16 * CPL)
+  int64_t s0;            // first column of the super-block
+  int sw;                // columns of the super-block
+  int B;                 // block width, <= 16 * CPL
+  int ldws;              // leading dimension of the super-block's copy in LDS
   const float* U;        // [d x d], processing order
   int64_t g;             // group size (columns)
-  int grid_in_block;     // groups start inside blocks (g <= B); else the grid was computed for the block
+  int grid_mode;         // 0: groups nest in blocks (g <= B), grids taken inside the column chain;
+                         // 1: a group spans blocks of this super-block, its grid taken from the LDS copy
+                         //    at its first block; 2: the grid was computed before the launch (a group
+                         //    longer than the super-block)
   float maxq;
   uint8_t* codes_p;      // [rows x d], processing order
   float* scales;         // [rows x ngroups]
   int32_t* zeros;        // [rows x ngroups]
   int64_t ngroups;
-  int sym;               // symmetric grids (in-block grids only)
-  int compact;           // 16-bit scales, zeros clamped to the code width (in-block grids only)
+  int sym;               // symmetric grids
+  int compact;           // 16-bit scales, zeros clamped to the code width
   const int32_t* colgrp; // static groups: group of each processing column (its grid is in scales/zeros)
-  float* err;            // this block's errors: [rows x 16 * CPL] at leading dimension err_ld
+  float* err;            // the super-block's errors: [rows x >= sw] at leading dimension err_ld
   int64_t err_ld;
   double* row_loss;      // [rows]
 };
@@ -60,68 +65,59 @@ GPTQ_DEV void lds_load(const float* p, float (&v)[N]) {
   }
 }
 
+// One super-block of columns [s0, s0 + sw) for 16 rows of W. The rows' part of the super-block sits
+// in LDS for the whole launch. Each block of B columns runs the column chain in registers, and its
+// errors then update the super-block's later columns in LDS as 16 x 16 x 4 fp32 MFMA tiles (the lazy
+// batch inside the super-block); columns beyond the super-block take the super-block's errors in one
+// product after the launch.
 // STATIC: every column takes the grid of its static group, colgrp[b + k] (loaded one chunk ahead with
 // U's rows); no grid is computed here.
 template <int CPL, bool STATIC>
-__global__ __launch_bounds__(256) void quant_block_kernel(QArgs a) {
+__global__ __launch_bounds__(256) void quant_super_kernel(QArgs a) {
   constexpr int BP = 16 * CPL;
   extern __shared__ float sm[];
-  float* Us = sm;                  // [BP][BP]: strict upper part of U's block, zeros elsewhere
+  float* Ws = sm;                  // [16 rows][ldws]: the rows' super-block, updated in place
+  float* Us = Ws + 16 * a.ldws;    // [BP][BP]: strict upper part of U's block, zeros elsewhere
   float* invd = Us + BP * BP;      // [BP]: 1 / U[k][k]
   float* Es = invd + BP;           // [16 rows][BP]: scaled errors of the block
   uint8_t* Qs = reinterpret_cast<uint8_t*>(Es + 16 * BP);  // [16 rows][BP]: codes of the block
 
   const int tid = threadIdx.x;
-  const int nc = a.ncols;
   const int lane = tid & 63, wave = tid >> 6;
   const int lr = lane & 15;
   const int rloc = wave * 4 + (lane >> 4);
-  const int64_t row = (int64_t)blockIdx.x * 16 + rloc;
+  const int64_t row0 = (int64_t)blockIdx.x * 16;
+  const int64_t row = row0 + rloc;
   const bool row_ok = row < a.rows;
+  const int sw = a.sw;
 
-  // lane lr starts with block columns lr*CPL .. lr*CPL+CPL-1 in w[0..CPL-1] (read first, so that
-  // these loads overlap the staging of U's block)
-  float w[CPL];
-  const float* wrow = a.Wp + row * a.ldw + a.b;
-#pragma unroll
-  for (int c = 0; c < CPL; ++c) w[c] = (row_ok && lr * CPL + c < nc) ? wrow[lr * CPL + c] : 0.0f;
-
-  bool filled = false;
-  if constexpr (CPL >= 4) {
-   if (nc == BP && a.d % 4 == 0 && a.b % 4 == 0 && (uintptr_t)a.U % 16 == 0) {
-    // full block: unconditional 16-byte loads, all in flight together
-    filled = true;
-    constexpr int Q = BP / 4;  // float4 per row
-    float4 v[BP * Q / 256];
-#pragma unroll
-    for (int i = 0; i < BP * Q / 256; ++i) {
-      const int e = tid + i * 256, k = e / Q, j = (e % Q) * 4;
-      v[i] = *reinterpret_cast<const float4*>(a.U + (a.b + k) * a.d + a.b + j);
-    }
-#pragma unroll
-    for (int i = 0; i < BP * Q / 256; ++i) {
-      const int e = tid + i * 256, k = e / Q, j = (e % Q) * 4;
-      float4 u = v[i];
-      u.x = (j + 0 > k) ? u.x : 0.0f;
-      u.y = (j + 1 > k) ? u.y : 0.0f;
-      u.z = (j + 2 > k) ? u.z : 0.0f;
-      u.w = (j + 3 > k) ? u.w : 0.0f;
-      *reinterpret_cast<float4*>(Us + k * BP + j) = u;
-    }
-   }
-  }
-  if (!filled) {
-    for (int e = tid; e < BP * BP; e += 256) {
-      const int k = e / BP, j = e % BP;
-      Us[e] = (j > k && j < nc) ? a.U[(a.b + k) * a.d + a.b + j] : 0.0f;
+  // The rows' super-block into LDS; rows past the end read as zeros. Wp's rows are zero-padded to
+  // ldw (a multiple of 4), so 16-byte pieces up to the super-block's end rounded to 4 stay inside.
+  {
+    const bool vec = a.ldw % 4 == 0 && a.s0 % 4 == 0 && (uintptr_t)a.Wp % 16 == 0;
+    const int q4 = (sw + 3) / 4;
+    for (int e = tid; e < 16 * q4; e += 256) {
+      const int r = e / q4, c = (e % q4) * 4;
+      const int64_t gr = row0 + r;
+      float4 v = float4{0.0f, 0.0f, 0.0f, 0.0f};
+      if (gr < a.rows) {
+        const float* p = a.Wp + gr * a.ldw + a.s0 + c;
+        if (vec) {
+          v = *reinterpret_cast<const float4*>(p);
+        } else {
+          v.x = p[0];
+          v.y = c + 1 < sw ? p[1] : 0.0f;
+          v.z = c + 2 < sw ? p[2] : 0.0f;
+          v.w = c + 3 < sw ? p[3] : 0.0f;
+        }
+      }
+      *reinterpret_cast<float4*>(Ws + r * a.ldws + c) = v;
     }
   }
-  for (int k = tid; k < BP; k += 256) invd[k] = (k < nc) ? 1.0f / a.U[(a.b + k) * a.d + a.b + k] : 0.0f;
-  __syncthreads();
 
-  float s = 1.0f, z = 0.0f, rs = 1.0f;
-  if (!STATIC && !a.grid_in_block) {
-    const int64_t gi = a.b / a.g;
+  float s = 1.0f, z = 0.0f, rs = 1.0f;   // the current group's grid, carried across blocks
+  if (!STATIC && a.grid_mode == 2) {
+    const int64_t gi = a.s0 / a.g;
     if (row_ok) {
       s = a.scales[row * a.ngroups + gi];
       z = (float)a.zeros[row * a.ngroups + gi];
@@ -129,153 +125,287 @@ __global__ __launch_bounds__(256) void quant_block_kernel(QArgs a) {
     rs = 1.0f / s;
   }
   float loss = 0.0f;
-  // groups nest inside blocks when g <= B, so they start at block columns 0, g, 2g, ...
-  int next_group = (!STATIC && a.grid_in_block) ? 0 : (1 << 30);
-  const int gsz = (int)min<int64_t>(a.g, (int64_t)BP);
+  float* wsrow = Ws + rloc * a.ldws;
+  const int nblk = (sw + a.B - 1) / a.B;
 
-  // Chunk o quantizes block columns o*CPL .. o*CPL+CPL-1. Before it, the lanes of each row have
-  // been rotated o times by one lane, so lane 0 holds those columns and lane l holds the columns
-  // of original lane (l + o) mod 16 (already quantized ones meet zeros in U and stay unchanged).
-  // What a chunk reads from LDS (U's rows for its columns, their reciprocal diagonal) is read one
-  // chunk ahead, into the other of two register sets; U and the diagonal are not written after the
-  // barrier above, and the chunk's own stores go to the codes and errors.
-  const int nchunks = (nc + CPL - 1) / CPL;
-  // static groups: the scale and zero of each of a chunk's columns (one chunk ahead, like U's rows)
-  float sA[STATIC ? CPL : 1], zA[STATIC ? CPL : 1], sB[STATIC ? CPL : 1], zB[STATIC ? CPL : 1];
-  auto fetch_grid = [&](int o, float (&sv)[STATIC ? CPL : 1], float (&zv)[STATIC ? CPL : 1]) {
-    if constexpr (STATIC) {
+  for (int jb = 0; jb < nblk; ++jb) {
+    const int boff = jb * a.B;            // the block's first column within the super-block
+    const int64_t b = a.s0 + boff;        // and within the row
+    const int nc = min(a.B, sw - boff);
+    __syncthreads();   // the previous block's update of Ws is complete, and Us, Es, Qs are free
+
+    // U's block and its reciprocal diagonal
+    bool filled = false;
+    if constexpr (CPL >= 4) {
+     if (nc == BP && a.d % 4 == 0 && b % 4 == 0 && (uintptr_t)a.U % 16 == 0) {
+      // full block: unconditional 16-byte loads, all in flight together
+      filled = true;
+      constexpr int Q = BP / 4;  // float4 per row
+      float4 v[BP * Q / 256];
+#pragma unroll
+      for (int i = 0; i < BP * Q / 256; ++i) {
+        const int e = tid + i * 256, k = e / Q, j = (e % Q) * 4;
+        v[i] = *reinterpret_cast<const float4*>(a.U + (b + k) * a.d + b + j);
+      }
+#pragma unroll
+      for (int i = 0; i < BP * Q / 256; ++i) {
+        const int e = tid + i * 256, k = e / Q, j = (e % Q) * 4;
+        float4 u = v[i];
+        u.x = (j + 0 > k) ? u.x : 0.0f;
+        u.y = (j + 1 > k) ? u.y : 0.0f;
+        u.z = (j + 2 > k) ? u.z : 0.0f;
+        u.w = (j + 3 > k) ? u.w : 0.0f;
+        *reinterpret_cast<float4*>(Us + k * BP + j) = u;
+      }
+     }
+    }
+    if (!filled) {
+      for (int e = tid; e < BP * BP; e += 256) {
+        const int k = e / BP, j = e % BP;
+        Us[e] = (j > k && j < nc) ? a.U[(b + k) * a.d + b + j] : 0.0f;
+      }
+    }
+    for (int k = tid; k < BP; k += 256) invd[k] = (k < nc) ? 1.0f / a.U[(b + k) * a.d + b + k] : 0.0f;
+
+    // lane lr starts with block columns lr*CPL .. lr*CPL+CPL-1 in w[0..CPL-1]
+    float w[CPL];
+#pragma unroll
+    for (int c = 0; c < CPL; ++c) w[c] = (lr * CPL + c < nc) ? wsrow[boff + lr * CPL + c] : 0.0f;
+
+    // a group that spans blocks: its grid from the current weights of its columns in LDS (the
+    // earlier blocks' updates of this super-block are in, and those of earlier super-blocks)
+    if (!STATIC && a.grid_mode == 1 && b % a.g == 0) {
+      const int gend = (int)min<int64_t>(boff + a.g, sw);
+      float mn = INFINITY, mx = -INFINITY;
+      for (int c = boff + lr; c < gend; c += 16) {
+        const float v = wsrow[c];
+        mn = fminf(mn, v);
+        mx = fmaxf(mx, v);
+      }
+      mn = fminf(mn, row_ror<8>(mn)); mx = fmaxf(mx, row_ror<8>(mx));
+      mn = fminf(mn, row_ror<4>(mn)); mx = fmaxf(mx, row_ror<4>(mx));
+      mn = fminf(mn, row_ror<2>(mn)); mx = fmaxf(mx, row_ror<2>(mx));
+      mn = fminf(mn, row_ror<1>(mn)); mx = fmaxf(mx, row_ror<1>(mx));
+      make_grid(mn, mx, a.maxq, a.sym != 0, a.compact != 0, s, z, rs);
+      if (lr == 0 && row_ok) {
+        const int64_t gi = (uint32_t)b / (uint32_t)a.g;   // column and group indices stay below 2^31
+        a.scales[row * a.ngroups + gi] = s;
+        a.zeros[row * a.ngroups + gi] = (int32_t)z;
+      }
+    }
+    __syncthreads();   // U's block staged
+
+    // groups nest inside blocks when g <= B, so they start at block columns 0, g, 2g, ...
+    int next_group = (!STATIC && a.grid_mode == 0) ? 0 : (1 << 30);
+    const int gsz = (int)min<int64_t>(a.g, (int64_t)BP);
+
+    // Chunk o quantizes block columns o*CPL .. o*CPL+CPL-1. Before it, the lanes of each row have
+    // been rotated o times by one lane, so lane 0 holds those columns and lane l holds the columns
+    // of original lane (l + o) mod 16 (already quantized ones meet zeros in U and stay unchanged).
+    // What a chunk reads from LDS (U's rows for its columns, their reciprocal diagonal) is read one
+    // chunk ahead, into the other of two register sets; U and the diagonal are not written during the
+    // chain, and the chunk's own stores go to the codes and errors.
+    const int nchunks = (nc + CPL - 1) / CPL;
+    // static groups: the scale and zero of each of a chunk's columns (one chunk ahead, like U's rows)
+    float sA[STATIC ? CPL : 1], zA[STATIC ? CPL : 1], sB[STATIC ? CPL : 1], zB[STATIC ? CPL : 1];
+    auto fetch_grid = [&](int o, float (&sv)[STATIC ? CPL : 1], float (&zv)[STATIC ? CPL : 1]) {
+      if constexpr (STATIC) {
+#pragma unroll
+        for (int c = 0; c < CPL; ++c) {
+          const int k = min(o * CPL + c, nc - 1);
+          const int64_t G = a.colgrp[b + k];
+          sv[c] = row_ok ? a.scales[row * a.ngroups + G] : 1.0f;
+          zv[c] = row_ok ? (float)a.zeros[row * a.ngroups + G] : 0.0f;
+        }
+      }
+    };
+    auto fetch = [&](int o, float (&iv)[CPL], float (&ur)[CPL][CPL]) {
+      const int cbase = ((lr + o) & 15) * CPL;
+      lds_load<CPL>(invd + o * CPL, iv);
+#pragma unroll
+      for (int c = 0; c < CPL; ++c) lds_load<CPL>(Us + (o * CPL + c) * BP + cbase, ur[c]);
+    };
+    // CHECKS: the chunk may start a group or run past the block's last column (a plain chunk, full
+    // and without a group start, runs the column chain with no branch or select)
+    auto chunk = [&](int o, const float (&iv)[CPL], const float (&ur)[CPL][CPL], const float (&sv)[STATIC ? CPL : 1],
+                     const float (&zv)[STATIC ? CPL : 1], auto checks) {
+      constexpr bool CHECKS = decltype(checks)::value;
+      const int cbase = ((lr + o) & 15) * CPL;  // block column of w[0] in this lane
+      float qv[CPL], ev[CPL];
+      float rsv[STATIC ? CPL : 1];
+      if constexpr (STATIC) {
+#pragma unroll
+        for (int c = 0; c < CPL; ++c) rsv[c] = 1.0f / sv[c];
+      }
 #pragma unroll
       for (int c = 0; c < CPL; ++c) {
-        const int k = min(o * CPL + c, nc - 1);
-        const int64_t G = a.colgrp[a.b + k];
-        sv[c] = row_ok ? a.scales[row * a.ngroups + G] : 1.0f;
-        zv[c] = row_ok ? (float)a.zeros[row * a.ngroups + G] : 0.0f;
+        const int k = o * CPL + c;
+        if constexpr (STATIC) {
+          s = sv[c];
+          z = zv[c];
+          rs = rsv[c];
+        }
+        if (CHECKS && k == next_group) {
+          next_group += gsz;
+          // group grid from the current weights of block columns [k, k + g); min and max over the
+          // row's 16 lanes by DPP rotations
+          const int kend = min(k + gsz, nc);
+          float mn = INFINITY, mx = -INFINITY;
+#pragma unroll
+          for (int t = 0; t < CPL; ++t) {
+            const int col = cbase + t;
+            if (col >= k && col < kend) { mn = fminf(mn, w[t]); mx = fmaxf(mx, w[t]); }
+          }
+          mn = fminf(mn, row_ror<8>(mn)); mx = fmaxf(mx, row_ror<8>(mx));
+          mn = fminf(mn, row_ror<4>(mn)); mx = fmaxf(mx, row_ror<4>(mx));
+          mn = fminf(mn, row_ror<2>(mn)); mx = fmaxf(mx, row_ror<2>(mx));
+          mn = fminf(mn, row_ror<1>(mn)); mx = fmaxf(mx, row_ror<1>(mx));
+          make_grid(mn, mx, a.maxq, a.sym != 0, a.compact != 0, s, z, rs);
+          if (lr == 0 && row_ok && k < nc) {
+            // column and group indices stay below 2^31
+            const int64_t gi = (uint32_t)(b + k) / (uint32_t)a.g;
+            a.scales[row * a.ngroups + gi] = s;
+            a.zeros[row * a.ngroups + gi] = (int32_t)z;
+          }
+        }
+        // q = clamp(rint(w / s) + z, 0, maxq) and the value s (q - z). On the chain: q - z is
+        // rint(w / s) clamped to [-z, maxq - z] (exact in fp32: small integers), and w - s (q - z) is
+        // one fused multiply-add.
+        const float wk = row_bcast<0>(w[c]);
+        const float x = div_rn(wk, s, rs);
+        const float qd = __builtin_amdgcn_fmed3f(rintf(x), -z, a.maxq - z);
+        const float q = qd + z;
+        float e = __builtin_fmaf(-s, qd, wk) * iv[c];
+        if (CHECKS) e = (k < nc) ? e : 0.0f;
+        loss = __builtin_fmaf(e, e, loss);
+#pragma unroll
+        for (int t = 0; t < CPL; ++t) w[t] = __builtin_fmaf(-e, ur[c][t], w[t]);
+        qv[c] = q;
+        ev[c] = e;
+      }
+      if (lr == 0) {
+#pragma unroll
+        for (int c = 0; c < CPL; ++c) {
+          Qs[rloc * BP + o * CPL + c] = (uint8_t)qv[c];
+          Es[rloc * BP + o * CPL + c] = ev[c];
+        }
+      }
+#pragma unroll
+      for (int t = 0; t < CPL; ++t) w[t] = row_ror15(w[t]);
+    };
+    auto run = [&](int o, const float (&iv)[CPL], const float (&ur)[CPL][CPL], const float (&sv)[STATIC ? CPL : 1],
+                   const float (&zv)[STATIC ? CPL : 1]) {
+      if (o * CPL + CPL <= nc && next_group >= o * CPL + CPL) chunk(o, iv, ur, sv, zv, std::false_type{});
+      else chunk(o, iv, ur, sv, zv, std::true_type{});
+    };
+    float ivA[CPL], urA[CPL][CPL], ivB[CPL], urB[CPL][CPL];
+    if (nchunks > 0) {
+      fetch(0, ivA, urA);
+      fetch_grid(0, sA, zA);
+    }
+    for (int o = 0; o < nchunks; o += 2) {
+      if (o + 1 < nchunks) {
+        fetch(o + 1, ivB, urB);
+        fetch_grid(o + 1, sB, zB);
+      }
+      run(o, ivA, urA, sA, zA);
+      if (o + 1 < nchunks) {
+        if (o + 2 < nchunks) {
+          fetch(o + 2, ivA, urA);
+          fetch_grid(o + 2, sA, zA);
+        }
+        run(o + 1, ivB, urB, sB, zB);
       }
     }
-  };
-  auto fetch = [&](int o, float (&iv)[CPL], float (&ur)[CPL][CPL]) {
-    const int cbase = ((lr + o) & 15) * CPL;
-    lds_load<CPL>(invd + o * CPL, iv);
-#pragma unroll
-    for (int c = 0; c < CPL; ++c) lds_load<CPL>(Us + (o * CPL + c) * BP + cbase, ur[c]);
-  };
-  // CHECKS: the chunk may start a group or run past the block's last column (a plain chunk, full
-  // and without a group start, runs the column chain with no branch or select)
-  auto chunk = [&](int o, const float (&iv)[CPL], const float (&ur)[CPL][CPL], const float (&sv)[STATIC ? CPL : 1],
-                   const float (&zv)[STATIC ? CPL : 1], auto checks) {
-    constexpr bool CHECKS = decltype(checks)::value;
-    const int cbase = ((lr + o) & 15) * CPL;  // block column of w[0] in this lane
-    float qv[CPL], ev[CPL];
-    float rsv[STATIC ? CPL : 1];
-    if constexpr (STATIC) {
-#pragma unroll
-      for (int c = 0; c < CPL; ++c) rsv[c] = 1.0f / sv[c];
-    }
-#pragma unroll
-    for (int c = 0; c < CPL; ++c) {
-      const int k = o * CPL + c;
-      if constexpr (STATIC) {
-        s = sv[c];
-        z = zv[c];
-        rs = rsv[c];
+    __syncthreads();   // the block's codes and errors are in Qs and Es
+
+    if (row_ok) {
+      uint8_t* crow = a.codes_p + row * a.d + b;
+      float* erow = a.err + row * a.err_ld + boff;
+      const int j0 = lr * CPL;
+      const bool vec = CPL == 8 && nc == BP && a.d % 8 == 0 && b % 8 == 0 && a.err_ld % 4 == 0 && boff % 4 == 0 &&
+                       (uintptr_t)a.codes_p % 8 == 0 && (uintptr_t)a.err % 16 == 0;
+      if constexpr (CPL == 8) {
+        if (vec) {
+          *reinterpret_cast<uint2*>(crow + j0) = *reinterpret_cast<const uint2*>(Qs + rloc * BP + j0);
+          *reinterpret_cast<float4*>(erow + j0) = *reinterpret_cast<const float4*>(Es + rloc * BP + j0);
+          *reinterpret_cast<float4*>(erow + j0 + 4) = *reinterpret_cast<const float4*>(Es + rloc * BP + j0 + 4);
+        }
       }
-      if (CHECKS && k == next_group) {
-        next_group += gsz;
-        // group grid from the current weights of block columns [k, k + g); min and max over the
-        // row's 16 lanes by DPP rotations
-        const int kend = min(k + gsz, nc);
-        float mn = INFINITY, mx = -INFINITY;
+      if (!(CPL == 8 && vec)) {
 #pragma unroll
         for (int t = 0; t < CPL; ++t) {
-          const int col = cbase + t;
-          if (col >= k && col < kend) { mn = fminf(mn, w[t]); mx = fmaxf(mx, w[t]); }
-        }
-        mn = fminf(mn, row_ror<8>(mn)); mx = fmaxf(mx, row_ror<8>(mx));
-        mn = fminf(mn, row_ror<4>(mn)); mx = fmaxf(mx, row_ror<4>(mx));
-        mn = fminf(mn, row_ror<2>(mn)); mx = fmaxf(mx, row_ror<2>(mx));
-        mn = fminf(mn, row_ror<1>(mn)); mx = fmaxf(mx, row_ror<1>(mx));
-        make_grid(mn, mx, a.maxq, a.sym != 0, a.compact != 0, s, z, rs);
-        if (lr == 0 && row_ok && k < nc) {
-          // column and group indices stay below 2^31
-          const int64_t gi = (uint32_t)(a.b + k) / (uint32_t)a.g;
-          a.scales[row * a.ngroups + gi] = s;
-          a.zeros[row * a.ngroups + gi] = (int32_t)z;
+          const int j = j0 + t;
+          if (j < nc) {
+            crow[j] = Qs[rloc * BP + j];
+            erow[j] = Es[rloc * BP + j];
+          }
         }
       }
-      // q = clamp(rint(w / s) + z, 0, maxq) and the value s (q - z). On the chain: q - z is
-      // rint(w / s) clamped to [-z, maxq - z] (exact in fp32: small integers), and w - s (q - z) is
-      // one fused multiply-add.
-      const float wk = row_bcast<0>(w[c]);
-      const float x = div_rn(wk, s, rs);
-      const float qd = __builtin_amdgcn_fmed3f(rintf(x), -z, a.maxq - z);
-      const float q = qd + z;
-      float e = __builtin_fmaf(-s, qd, wk) * iv[c];
-      if (CHECKS) e = (k < nc) ? e : 0.0f;
-      loss = __builtin_fmaf(e, e, loss);
-#pragma unroll
-      for (int t = 0; t < CPL; ++t) w[t] = __builtin_fmaf(-e, ur[c][t], w[t]);
-      qv[c] = q;
-      ev[c] = e;
     }
-    if (lr == 0) {
-#pragma unroll
-      for (int c = 0; c < CPL; ++c) {
-        Qs[rloc * BP + o * CPL + c] = (uint8_t)qv[c];
-        Es[rloc * BP + o * CPL + c] = ev[c];
-      }
-    }
-#pragma unroll
-    for (int t = 0; t < CPL; ++t) w[t] = row_ror15(w[t]);
-  };
-  auto run = [&](int o, const float (&iv)[CPL], const float (&ur)[CPL][CPL], const float (&sv)[STATIC ? CPL : 1],
-                 const float (&zv)[STATIC ? CPL : 1]) {
-    if (o * CPL + CPL <= nc && next_group >= o * CPL + CPL) chunk(o, iv, ur, sv, zv, std::false_type{});
-    else chunk(o, iv, ur, sv, zv, std::true_type{});
-  };
-  float ivA[CPL], urA[CPL][CPL], ivB[CPL], urB[CPL][CPL];
-  if (nchunks > 0) {
-    fetch(0, ivA, urA);
-    fetch_grid(0, sA, zA);
-  }
-  for (int o = 0; o < nchunks; o += 2) {
-    if (o + 1 < nchunks) {
-      fetch(o + 1, ivB, urB);
-      fetch_grid(o + 1, sB, zB);
-    }
-    run(o, ivA, urA, sA, zA);
-    if (o + 1 < nchunks) {
-      if (o + 2 < nchunks) {
-        fetch(o + 2, ivA, urA);
-        fetch_grid(o + 2, sA, zA);
-      }
-      run(o + 1, ivB, urB, sB, zB);
-    }
-  }
-  __syncthreads();
 
-  if (row_ok) {
-    uint8_t* crow = a.codes_p + row * a.d + a.b;
-    float* erow = a.err + row * a.err_ld;
-    const int j0 = lr * CPL;
-    const bool vec = CPL == 8 && nc == BP && a.d % 8 == 0 && a.b % 8 == 0 && a.err_ld % 4 == 0 &&
-                     (uintptr_t)a.codes_p % 8 == 0 && (uintptr_t)a.err % 16 == 0;
-    if constexpr (CPL == 8) {
-      if (vec) {
-        *reinterpret_cast<uint2*>(crow + j0) = *reinterpret_cast<const uint2*>(Qs + rloc * BP + j0);
-        *reinterpret_cast<float4*>(erow + j0) = *reinterpret_cast<const float4*>(Es + rloc * BP + j0);
-        *reinterpret_cast<float4*>(erow + j0 + 4) = *reinterpret_cast<const float4*>(Es + rloc * BP + j0 + 4);
-      }
-    }
-    if (!(CPL == 8 && vec)) {
+    // The block's errors into the super-block's later columns: Ws[:, c0:sw] -= E U[b:b+nc, s0+c0:s0+sw],
+    // 16-column tiles dealt to the four waves, two at a time. v_mfma_f32_16x16x4f32 takes A[l % 16][k +
+    // l / 16] and B[k + l / 16][l % 16] from lane l, and register r of its result holds row
+    // 4 (l / 16) + r, column l % 16: here A = E (the 16 rows by the block's columns), B = U's rows of the
+    // block, C = the tile of Ws.
+    const int c0 = boff + nc;
+    if (c0 < sw) {
+      const int l16 = lane & 15, lq = lane >> 4;
+      const int ksteps = (nc + 3) / 4;
+      const int ntiles = (sw - c0 + 15) / 16;
+      constexpr int KC = 8;   // k-steps whose operands are fetched together, one group ahead
+      for (int t = wave; t < ntiles; t += 8) {
+        const bool two = t + 4 < ntiles;
+        const int col0 = c0 + 16 * t + l16, col1 = col0 + 64;
+        const bool ok0 = col0 < sw, ok1 = two && col1 < sw;
+        const float* up = a.U + (b + lq) * a.d + a.s0;
+        auto fetch_k = [&](int k0, float (&av)[KC], float (&b0)[KC], float (&b1)[KC]) {
 #pragma unroll
-      for (int t = 0; t < CPL; ++t) {
-        const int j = j0 + t;
-        if (j < nc) crow[j] = Qs[rloc * BP + j];
-        erow[j] = (j < nc) ? Es[rloc * BP + j] : 0.0f;
+          for (int i = 0; i < KC; ++i) {
+            const int kk = k0 + i, k = 4 * kk + lq;
+            const bool ok = kk < ksteps && k < nc;
+            const float* ur = up + (int64_t)(4 * kk) * a.d;
+            av[i] = ok ? -Es[l16 * BP + k] : 0.0f;
+            b0[i] = (ok && ok0) ? ur[col0] : 0.0f;
+            b1[i] = (ok && ok1) ? ur[col1] : 0.0f;
+          }
+        };
+        float avA[KC], b0A[KC], b1A[KC], avB[KC], b0B[KC], b1B[KC];
+        fetch_k(0, avA, b0A, b1A);
+        floatx4 acc0, acc1;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          acc0[r] = Ws[(4 * lq + r) * a.ldws + col0];
+          acc1[r] = two ? Ws[(4 * lq + r) * a.ldws + col1] : 0.0f;
+        }
+        auto mma = [&](const float (&av)[KC], const float (&b0)[KC], const float (&b1)[KC]) {
+#pragma unroll
+          for (int i = 0; i < KC; ++i) {
+            acc0 = __builtin_amdgcn_mfma_f32_16x16x4f32(av[i], b0[i], acc0, 0, 0, 0);
+            acc1 = __builtin_amdgcn_mfma_f32_16x16x4f32(av[i], b1[i], acc1, 0, 0, 0);
+          }
+        };
+        for (int k0 = 0; k0 < ksteps; k0 += 2 * KC) {
+          if (k0 + KC < ksteps) fetch_k(k0 + KC, avB, b0B, b1B);
+          mma(avA, b0A, b1A);
+          if (k0 + KC < ksteps) {
+            if (k0 + 2 * KC < ksteps) fetch_k(k0 + 2 * KC, avA, b0A, b1A);
+            mma(avB, b0B, b1B);
+          }
+        }
+        if (ok0) {
+#pragma unroll
+          for (int r = 0; r < 4; ++r) Ws[(4 * lq + r) * a.ldws + col0] = acc0[r];
+        }
+        if (ok1) {
+#pragma unroll
+          for (int r = 0; r < 4; ++r) Ws[(4 * lq + r) * a.ldws + col1] = acc1[r];
+        }
       }
     }
-    if (lr == 0) a.row_loss[row] += (double)loss;
   }
+  if (lr == 0 && row_ok) a.row_loss[row] += (double)loss;
 }
 
 // Group grid for groups longer than a block: min/max of the current weights of columns
@@ -510,32 +640,36 @@ __global__ __launch_bounds__(256) void pack_kernel(const uint8_t* __restrict__ c
   }
 }
 
+int64_t super_width_max(int B) { return std::max<int64_t>(1, 512 / B) * B; }
+
+// LDS leading dimension of a super-block's copy: whole 16-column tiles plus 4 floats of padding.
+int super_ld(int sw) { return (sw + 15) / 16 * 16 + 4; }
+
 template <int CPL>
-size_t qsmem() {
+size_t qsmem(int sw) {
   constexpr size_t BP = 16 * CPL;
-  return (BP * BP + BP + 16 * BP) * sizeof(float) + 16 * BP;
+  return (16 * (size_t)super_ld(sw) + BP * BP + BP + 16 * BP) * sizeof(float) + 16 * BP;
 }
 
 template <int CPL, bool STATIC>
-void launch_block(const QArgs& a, hipStream_t s) {
+void launch_super(const QArgs& a, hipStream_t s) {
   static bool attr = false;
   if (!attr) {
-    (void)hipFuncSetAttribute((const void*)quant_block_kernel<CPL, STATIC>,
-                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)qsmem<CPL>());
+    (void)hipFuncSetAttribute((const void*)quant_super_kernel<CPL, STATIC>,
+                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)qsmem<CPL>(512 + 16 * CPL));
     attr = true;
   }
-  hipLaunchKernelGGL((quant_block_kernel<CPL, STATIC>), dim3((unsigned)((a.rows + 15) / 16)), dim3(256), qsmem<CPL>(),
-                     s, a);
+  hipLaunchKernelGGL((quant_super_kernel<CPL, STATIC>), dim3((unsigned)((a.rows + 15) / 16)), dim3(256),
+                     qsmem<CPL>(a.sw), s, a);
 }
 
 template <int CPL>
-void launch_block(const QArgs& a, bool is_static, hipStream_t s) {
-  if (is_static) launch_block<CPL, true>(a, s);
-  else launch_block<CPL, false>(a, s);
+void launch_super(const QArgs& a, bool is_static, hipStream_t s) {
+  if (is_static) launch_super<CPL, true>(a, s);
+  else launch_super<CPL, false>(a, s);
 }
 
 int cpl_for(int B) { return B <= 16 ? 1 : B <= 32 ? 2 : B <= 64 ? 4 : 8; }
-int64_t super_width_max(int B) { return std::max<int64_t>(1, 512 / B) * B; }
 
 }  // namespace
 
@@ -602,35 +736,29 @@ hipError_t quantize(const void* W, int w_dtype, int64_t rows, int64_t d, int64_t
   hipError_t e;
   const int cpl = cpl_for(B);
   const int64_t sw = super_width(B, g, d);
-  GemmArgs t{};  // W[:, c0:c1] -= Err U[rows of the errors, c0:c1]
+  // where group grids are taken (see QArgs::grid_mode)
+  const int grid_mode = static_groups ? 2 : g <= B ? 0 : g <= sw ? 1 : 2;
+  GemmArgs t{};  // W[:, s1:] -= Err U[s0:s1, s1:]
   t.M = rows; t.transA = 0; t.ldb = d; t.transB = 0; t.ldc = L.ldw;
   t.alpha = -1.0f; t.beta = 1.0f; t.tri = 0; t.lda = L.ld_err;
   for (int64_t s0 = 0; s0 < d && rows > 0; s0 += sw) {
     const int64_t s1 = std::min(d, s0 + sw);
-    for (int64_t b = s0; b < s1; b += B) {
-      const int nc = (int)std::min<int64_t>(B, d - b);
-      const bool in_block = g <= B;
-      if (!static_groups && !in_block && b % g == 0) {
-        hipLaunchKernelGGL(group_grid_kernel, dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, s, Wp, L.ldw, rows, b,
-                           std::min<int64_t>(g, d - b), maxq, sym, compact, b / g, scales, zeros, ngroups);
-      }
-      QArgs a;
-      a.Wp = Wp; a.ldw = L.ldw; a.rows = rows; a.d = d; a.b = b; a.ncols = nc; a.U = U; a.g = g;
-      a.grid_in_block = in_block; a.maxq = maxq; a.codes_p = codes_p; a.scales = scales; a.zeros = zeros;
-      a.ngroups = ngroups; a.err = err + (b - s0); a.err_ld = L.ld_err; a.row_loss = row_loss;
-      a.sym = sym; a.compact = compact; a.colgrp = colgrp;
-      const bool st = static_groups != 0;
-      switch (cpl) {
-        case 1: launch_block<1>(a, st, s); break;
-        case 2: launch_block<2>(a, st, s); break;
-        case 4: launch_block<4>(a, st, s); break;
-        default: launch_block<8>(a, st, s); break;
-      }
-      if (b + nc < s1) {  // lazy batch inside the super-block
-        t.N = s1 - b - nc; t.K = nc;
-        t.A = err + (b - s0); t.B = U + b * d + b + nc; t.C = Wp + b + nc;
-        if ((e = gemm_f32(t, s)) != hipSuccess) return e;
-      }
+    if (!static_groups && grid_mode == 2 && s0 % g == 0) {
+      // a group longer than the super-block: its grid from the current weights of all its columns
+      hipLaunchKernelGGL(group_grid_kernel, dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, s, Wp, L.ldw, rows, s0,
+                         std::min<int64_t>(g, d - s0), maxq, sym, compact, s0 / g, scales, zeros, ngroups);
+    }
+    QArgs a;
+    a.Wp = Wp; a.ldw = L.ldw; a.rows = rows; a.d = d; a.s0 = s0; a.sw = (int)(s1 - s0); a.B = B;
+    a.ldws = super_ld(a.sw); a.U = U; a.g = g; a.grid_mode = grid_mode; a.maxq = maxq; a.codes_p = codes_p;
+    a.scales = scales; a.zeros = zeros; a.ngroups = ngroups; a.err = err; a.err_ld = L.ld_err;
+    a.row_loss = row_loss; a.sym = sym; a.compact = compact; a.colgrp = colgrp;
+    const bool st = static_groups != 0;
+    switch (cpl) {
+      case 1: launch_super<1>(a, st, s); break;
+      case 2: launch_super<2>(a, st, s); break;
+      case 4: launch_super<4>(a, st, s); break;
+      default: launch_super<8>(a, st, s); break;
     }
     if (s1 < d) {  // the super-block's errors to every later column at once
       t.N = d - s1; t.K = s1 - s0;

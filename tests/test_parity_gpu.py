@@ -350,6 +350,53 @@ def test_quantize_parity_compact(kw, act, sym, static):
     assert np.array_equal(out["scales"].astype(np.float64), o.scales)
 
 
+SPLIT_CASES = [
+    dict(bits=4, group_size=128, block_size=128, d=700, act=True),
+    dict(bits=4, group_size=256, block_size=64, d=700, act=False),        # groups spanning blocks
+    dict(bits=3, group_size=0, block_size=128, d=390, act=False),
+    dict(bits=4, group_size=64, block_size=128, d=520, act=True, static=True),
+    dict(bits=4, group_size=32, block_size=32, d=300, act=True, sym=True, compact=True),
+    dict(bits=4, group_size=1024, block_size=128, d=2300, act=False),     # groups longer than a super-block
+]
+
+
+@pytest.mark.parametrize("kw", SPLIT_CASES, ids=[str(i) for i in range(len(SPLIT_CASES))])
+def test_quantize_rows_split(kw):
+    """2100 rows (131 full 16-row workgroups and a ragged one): against the oracle on the same U, and
+    bit for bit against the rows quantized in two separate calls of 1056 and 1044 rows. Rows are
+    independent, so splitting them changes nothing."""
+    torch = torch_cuda()
+    import post_weight_quantization_20_amd as g
+    kw = dict(kw)
+    d, act = kw.pop("d"), kw.pop("act")
+    sym, static, compact = kw.pop("sym", False), kw.pop("static", False), kw.pop("compact", False)
+    print(f"[split] {kw} d {d} act {act} sym {sym} static {static} compact {compact}", flush=True)
+    case = _case("qsl", 70 + d, rows=2100, d=d, n=2 * d, chunk=4096, x_dtype="f32", w_dtype="f32", act_order=act,
+                 **kw)
+    W = synth.weight(case)
+    H, n = ref.hessian([synth.to_f64(synth.x_chunk(case, 0), "f32")])
+    Hh, perm, lam = ref.damp_and_order(H, n, case.damp, act)
+    U32 = ref.inverse_cholesky_upper(Hh).astype(np.float32)
+    p = params_of(case, sym=sym, static_groups=static, compact_meta=compact)
+    Ud, pd = torch.from_numpy(U32).cuda(), torch.from_numpy(perm.astype(np.int32)).cuda()
+    Wd = torch.from_numpy(W).cuda()
+    q = g.gptq_quantize_layer(Wd, Ud, pd, p)
+    parts = [g.gptq_quantize_layer(Wd[r0:r1], Ud, pd, p) for r0, r1 in ((0, 1056), (1056, 2100))]
+    torch.cuda.synchronize()
+    out = dict(codes=q.codes.cpu().numpy(), scales=q.scales.cpu().numpy(), zeros=q.zeros.cpu().numpy(),
+               g_idx=q.g_idx.cpu().numpy(), loss=float(q.loss.cpu().numpy()[0]))
+    for name in ("codes", "scales", "zeros"):
+        whole = out[name]
+        split = np.concatenate([getattr(t, name).cpu().numpy() for t in parts])
+        assert np.array_equal(whole.view(np.uint8), split.view(np.uint8)), name
+    assert out["loss"] == pytest.approx(sum(float(t.loss.cpu().numpy()[0]) for t in parts), rel=1e-12)
+    follow = (out["codes"][:, perm], out["zeros"]) + ((out["scales"],) if compact else ())
+    o = ref.quantize_layer(W.astype(np.float64), U32.astype(np.float64), case.bits, case.group_size,
+                           case.block_size, perm=perm, follow=follow, tau=TAU, sym=sym, static_groups=static,
+                           compact=compact)
+    check_quant_parity(out, o)
+
+
 # ------------------------------------------------------------------ whole layer
 
 ECASES = [
