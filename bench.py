@@ -60,6 +60,83 @@ def parse():
     return ap.parse_args()
 
 
+def host_info() -> dict:
+    """The host CPU model and the BLAS library numpy uses (for the CPU baseline)."""
+    model = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    blas = None
+    try:
+        from threadpoolctl import threadpool_info
+        libs = [i for i in threadpool_info() if i.get("user_api") == "blas"]
+        if libs:
+            blas = f"{libs[0].get('internal_api')} {libs[0].get('version')} ({libs[0].get('num_threads')} threads)"
+    except Exception:
+        pass
+    return {"cpu_model": model, "blas": blas, "logical_cpus": os.cpu_count()}
+
+
+def super_width(B: int, g: int, d: int) -> int:
+    """Width of the column loop's super-blocks: the library's rule (up to 512 columns, a multiple of
+    the block, nesting with groups wider than a block), used here only to count the lazy products'
+    flops."""
+    for m in range(max(1, 512 // B), 0, -1):
+        sw = m * B
+        if g <= B or g >= d or sw % g == 0 or g % sw == 0:
+            return sw
+    return B
+
+
+def phase_roofline(rows: int, d: int, n: int, B: int, g: int, ms: dict) -> dict:
+    """Each phase's algorithmic work over its measured device time, against the unit that bounds it:
+    the Hessian's n d (d + 1) flops (the symmetric half) on the fp16 matrix cores; the factor's
+    2/3 d^3 on the fp32 ones; the lazy products that carry each super-block's errors to the later
+    columns (their exact flops) on the fp32 ones; the column loop's 9 bytes per weight (fp32 weight in,
+    code and fp32 error out) against HBM, with its time per column, since a chain of dependent steps
+    per column bounds it; and the pack's 1.5 bytes per weight against HBM."""
+    sw = super_width(B, g, d)
+    lazy = 0.0
+    for s0 in range(0, d, sw):
+        s1 = min(d, s0 + sw)
+        lazy += 2.0 * rows * (s1 - s0) * (d - s1)
+
+    def flop_entry(name, kernel, flops, t_ms, peak):
+        a = flops / (t_ms / 1e3) / 1e12
+        return {"phase": name, "kernels": kernel, "bound": "mfma", "work": flops, "work_unit": "flop",
+                "ms": round(t_ms, 4), "achieved": round(a, 2), "peak": peak, "unit": "TFLOP/s",
+                "frac": round(a / peak, 4)}
+
+    def byte_entry(name, kernel, byts, t_ms, extra=None):
+        a = byts / (t_ms / 1e3) / 1e9
+        e = {"phase": name, "kernels": kernel, "bound": "hbm", "work": byts, "work_unit": "byte",
+             "ms": round(t_ms, 4), "achieved": round(a, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+             "frac": round(a / PEAK_HBM_GBS, 5)}
+        if extra:
+            e.update(extra)
+        return e
+
+    out = [flop_entry("hessian", "hess_kernel, reduce_partials", float(n) * d * (d + 1), ms["hessian"],
+                      PEAK_F16_TFLOPS),
+           flop_entry("factor", "chol_diag_kernel, gemm_f32_kernel, gather/flip", 2.0 * d ** 3 / 3, ms["factor"],
+                      PEAK_F32_TFLOPS)]
+    if "lazy_products" in ms:
+        out.append(flop_entry("lazy_products", f"gemm_f32_kernel (errors of each {sw}-column super-block to "
+                              "the later columns)", lazy, ms["lazy_products"], PEAK_F32_TFLOPS))
+        cl = ms["column_loop"]
+        out.append(byte_entry("column_loop", "quant_super_kernel (in-block chain and the lazy updates inside a "
+                              "super-block)", 9.0 * rows * d, cl,
+                              {"ns_per_column": round(cl * 1e6 / d, 2),
+                               "clocks_per_column_at_2p4GHz": round(cl * 1e-3 * 2.4e9 / d, 1)}))
+    out.append(byte_entry("pack", "pack_kernel", 1.5 * rows * d, ms["pack"]))
+    return {"entries": out, "super_width": sw}
+
+
 def source_hash(rel: str) -> str:
     with open(os.path.join(ROOT, rel), "rb") as f:
         return hashlib.sha256(f.read()).hexdigest()[:16]
@@ -127,6 +204,7 @@ def cpu_baseline(case, budget_s: float):
         "unit": "weight-columns/s",
         "cores": int(cores),
         "kind": "oracle",
+        "host": host_info(),
         "sec_per_layer": total,
         "phases_s": {"hessian": hess_full, "factor": fac, "quantize": quant_full, "pack": tp},
         "sample": (f"float64 oracle: Hessian on {tok_sample} of {case.n} tokens, factor at full d={d}, "
@@ -512,6 +590,16 @@ def main():
             "peak": PEAK_F16_TFLOPS, "unit": "TFLOP/s", "frac": round(achieved / PEAK_F16_TFLOPS, 4),
             "traffic": traffic, "flops_per_launch": flops, "avg_launch_ms": round(hess_kernel_ms, 4)}
 
+    # where the column loop's time goes: three more calls with events between their launches (not
+    # part of the timed steps above)
+    parts = {"column_loop": 0.0, "lazy_products": 0.0, "other": 0.0}
+    reps = 3
+    for _ in range(reps):
+        _, pm = g.gptq_quantize_layer_timed(W, U, perm, params, out=qout, work=ws_q)
+        for k in parts:
+            parts[k] += pm[k] / reps
+    phase_ms = {"hessian": float(hess_ms), "factor": float(fac_ms), "pack": float(pack_ms), **parts}
+
     out = {
         "metric": "GPTQ sec/layer + weight-columns/s at 4096x4096 int4 g128; % MFMA / HBM peak",
         "value": round(d / sec_layer, 1),
@@ -536,6 +624,9 @@ def main():
         "solver_only_ms": round(float(fac_ms + quant_ms + pack_ms), 4),
         "weights_per_s": round(rows * d / sec_layer, 1),
         "roofline": roof,
+        "quantize_parts_ms": {k: round(v, 4) for k, v in parts.items()},
+        "phase_roofline": phase_roofline(rows, d, n, case.block_size,
+                                         d if case.group_size <= 0 else case.group_size, phase_ms),
     }
     if args.copy_calibration:
         src = torch.empty(1 << 28, dtype=torch.float32, device=dev).fill_(1.0)

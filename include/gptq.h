@@ -195,6 +195,20 @@ gptq_status_t gptq_quantize_layer(const void *W, int32_t w_dtype, int64_t rows, 
                                   size_t work_bytes, void *stream);
 
 /*
+ * gptq_quantize_layer with a breakdown of where its device time goes (measurement: the same work
+ * and results, plus events recorded between its launches). Same arguments, plus:
+ *   part_ms  host double[3], output: device milliseconds of the column-loop kernels (the in-block
+ *            chain with the lazy updates inside each super-block of up to 512 columns), of the lazy
+ *            products that carry each super-block's errors to the later columns (fp32 MFMA GEMMs),
+ *            and of the rest (working copy, indices, un-permute, loss). NULL is GPTQ_EINVAL.
+ * Unlike gptq_quantize_layer it waits for the stream before returning.
+ */
+gptq_status_t gptq_quantize_layer_timed(const void *W, int32_t w_dtype, int64_t rows, int64_t d, int64_t ld_w,
+                                        const float *U, const int32_t *perm, const gptq_params_t *p, uint8_t *codes,
+                                        float *scales, int32_t *zeros, int32_t *g_idx, double *loss, void *work,
+                                        size_t work_bytes, double *part_ms, void *stream);
+
+/*
  * Packs codes in fixed fields along the columns (GPTQ tools page, "How it works", Step 8: eight 4-bit
  * codes per 32-bit word): a nibble per code for bits 1..4, a byte per code for bits 5..8.
  *

@@ -49,6 +49,9 @@ SIGNATURES = {
     "gptq_quantize_layer": (c_int32, [c_void_p, c_int32, c_int64, c_int64, c_int64, c_void_p, c_void_p,
                                       ctypes.POINTER(gptq_params_t), c_void_p, c_void_p, c_void_p, c_void_p, c_void_p,
                                       c_void_p, c_size_t, c_void_p]),
+    "gptq_quantize_layer_timed": (c_int32, [c_void_p, c_int32, c_int64, c_int64, c_int64, c_void_p, c_void_p,
+                                            ctypes.POINTER(gptq_params_t), c_void_p, c_void_p, c_void_p, c_void_p,
+                                            c_void_p, c_void_p, c_size_t, ctypes.POINTER(c_double), c_void_p]),
     "gptq_pack": (c_int32, [c_void_p, c_int64, c_int64, c_int32, c_void_p, c_void_p]),
     "gptq_pack_dense": (c_int32, [c_void_p, c_int64, c_int64, c_int32, c_void_p, c_void_p]),
     "gptq_pack_ordered": (c_int32, [c_void_p, c_int64, c_int64, c_int32, c_void_p, c_void_p, c_void_p]),

@@ -141,10 +141,14 @@ gptq_status_t gptq_factor_noalloc(const float* H, int64_t d, int64_t n_total, co
   return factor_call(H, d, n_total, p, U, perm, scratch, info, static_cast<hipStream_t>(stream), true);
 }
 
-gptq_status_t gptq_quantize_layer(const void* W, int32_t w_dtype, int64_t rows, int64_t d, int64_t ld_w,
-                                  const float* U, const int32_t* perm, const gptq_params_t* p, uint8_t* codes,
-                                  float* scales, int32_t* zeros, int32_t* g_idx, double* loss, void* work,
-                                  size_t work_bytes, void* stream) {
+}  // extern "C"
+
+namespace {
+
+gptq_status_t quantize_call(const void* W, int32_t w_dtype, int64_t rows, int64_t d, int64_t ld_w, const float* U,
+                            const int32_t* perm, const gptq_params_t* p, uint8_t* codes, float* scales,
+                            int32_t* zeros, int32_t* g_idx, double* loss, void* work, size_t work_bytes,
+                            void* stream, double* part_ms) {
   if (rows < 0 || rows > kMaxDim || d <= 0 || d > kMaxDim || !dtype_ok(w_dtype)) return GPTQ_EINVAL;
   if (!U || !perm || !g_idx || !loss || !work) return GPTQ_EINVAL;
   if (rows > 0 && (!W || !codes || !scales || !zeros || ld_w < d)) return GPTQ_EINVAL;
@@ -154,7 +158,29 @@ gptq_status_t gptq_quantize_layer(const void* W, int32_t w_dtype, int64_t rows, 
   const int64_t g = p->group_size <= 0 ? d : p->group_size;
   hipStream_t s = static_cast<hipStream_t>(stream);
   return hip_status(gptq::quantize(W, w_dtype, rows, d, ld_w, U, perm, p->bits, g, p->block_size, p->sym,
-                                   p->static_groups, p->compact_meta, codes, scales, zeros, g_idx, loss, work, s));
+                                   p->static_groups, p->compact_meta, codes, scales, zeros, g_idx, loss, work, s,
+                                   part_ms));
+}
+
+}  // namespace
+
+extern "C" {
+
+gptq_status_t gptq_quantize_layer(const void* W, int32_t w_dtype, int64_t rows, int64_t d, int64_t ld_w,
+                                  const float* U, const int32_t* perm, const gptq_params_t* p, uint8_t* codes,
+                                  float* scales, int32_t* zeros, int32_t* g_idx, double* loss, void* work,
+                                  size_t work_bytes, void* stream) {
+  return quantize_call(W, w_dtype, rows, d, ld_w, U, perm, p, codes, scales, zeros, g_idx, loss, work, work_bytes,
+                       stream, nullptr);
+}
+
+gptq_status_t gptq_quantize_layer_timed(const void* W, int32_t w_dtype, int64_t rows, int64_t d, int64_t ld_w,
+                                        const float* U, const int32_t* perm, const gptq_params_t* p, uint8_t* codes,
+                                        float* scales, int32_t* zeros, int32_t* g_idx, double* loss, void* work,
+                                        size_t work_bytes, double* part_ms, void* stream) {
+  if (!part_ms) return GPTQ_EINVAL;
+  return quantize_call(W, w_dtype, rows, d, ld_w, U, perm, p, codes, scales, zeros, g_idx, loss, work, work_bytes,
+                       stream, part_ms);
 }
 
 gptq_status_t gptq_pack(const uint8_t* codes, int64_t rows, int64_t d, int32_t bits, int32_t* packed, void* stream) {

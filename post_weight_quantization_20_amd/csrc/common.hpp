@@ -160,10 +160,13 @@ struct QuantLayout {
 QuantLayout quant_layout(int64_t rows, int64_t d, int block);
 // sym: symmetric grids; static_groups: grids of original column groups fixed before the loop;
 // compact: 16-bit scales and zeros clamped to the code width, used as stored.
+// part_ms (optional, host double[3]): device time of the call's parts, from events recorded between
+// its launches (measurement only; the call then waits for the stream): the column-loop kernels, the
+// lazy products across super-blocks, and the rest (working copy, indices, un-permute, loss).
 hipError_t quantize(const void* W, int w_dtype, int64_t rows, int64_t d, int64_t ld_w, const float* U,
                     const int32_t* perm, int bits, int64_t g, int B, int sym, int static_groups, int compact,
                     uint8_t* codes, float* scales, int32_t* zeros, int32_t* g_idx, double* loss, void* work,
-                    hipStream_t s);
+                    hipStream_t s, double* part_ms = nullptr);
 // Field layout (nibbles up to 4 bits, bytes above) and the dense bit stream.
 hipError_t pack(const uint8_t* codes, int64_t rows, int64_t d, int bits, int32_t* packed, hipStream_t s);
 hipError_t pack_dense(const uint8_t* codes, int64_t rows, int64_t d, int bits, int32_t* packed, hipStream_t s);

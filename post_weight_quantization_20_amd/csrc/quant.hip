@@ -20,6 +20,8 @@
 // GEMM) multiplies into the columns after the block.
 #include "common.hpp"
 
+#include <vector>
+
 namespace gptq {
 namespace {
 
@@ -707,8 +709,23 @@ QuantLayout quant_layout(int64_t rows, int64_t d, int block) {
 hipError_t quantize(const void* W, int w_dtype, int64_t rows, int64_t d, int64_t ld_w, const float* U,
                     const int32_t* perm, int bits, int64_t g, int B, int sym, int static_groups, int compact,
                     uint8_t* codes, float* scales, int32_t* zeros, int32_t* g_idx, double* loss, void* work,
-                    hipStream_t s) {
+                    hipStream_t s, double* part_ms) {
   const QuantLayout L = quant_layout(rows, d, B);
+  // measurement: an event after each group of launches, the interval before it charged to a part
+  std::vector<hipEvent_t> evs;
+  std::vector<int> parts;
+  auto mark = [&](int part) {
+    if (!part_ms) return;
+    hipEvent_t ev = nullptr;
+    if (hipEventCreate(&ev) != hipSuccess) return;
+    if (hipEventRecord(ev, s) != hipSuccess) {
+      (void)hipEventDestroy(ev);
+      return;
+    }
+    evs.push_back(ev);
+    parts.push_back(part);
+  };
+  mark(2);
   char* wb = static_cast<char*>(work);
   float* Wp = reinterpret_cast<float*>(wb + L.off_wp);
   uint8_t* codes_p = reinterpret_cast<uint8_t*>(wb + L.off_codes);
@@ -733,6 +750,7 @@ hipError_t quantize(const void* W, int w_dtype, int64_t rows, int64_t d, int64_t
                        ld_w, rows, d, perm, Wp, L.ldw, vec);
     hipLaunchKernelGGL(zero_f64, dim3((unsigned)((rows + 255) / 256)), dim3(256), 0, s, row_loss, rows);
   }
+  mark(2);
   hipError_t e;
   const int cpl = cpl_for(B);
   const int64_t sw = super_width(B, g, d);
@@ -760,10 +778,12 @@ hipError_t quantize(const void* W, int w_dtype, int64_t rows, int64_t d, int64_t
       case 4: launch_super<4>(a, st, s); break;
       default: launch_super<8>(a, st, s); break;
     }
+    mark(0);
     if (s1 < d) {  // the super-block's errors to every later column at once
       t.N = d - s1; t.K = s1 - s0;
       t.A = err; t.B = U + s0 * d + s1; t.C = Wp + s1;
       if ((e = gemm_f32(t, s)) != hipSuccess) return e;
+      mark(1);
     }
   }
   if (rows > 0) {
@@ -773,7 +793,18 @@ hipError_t quantize(const void* W, int w_dtype, int64_t rows, int64_t d, int64_t
                        rows, d, iperm, codes, vec);
   }
   hipLaunchKernelGGL(loss_kernel, dim3(1), dim3(1024), 0, s, row_loss, rows, loss);
-  return hipGetLastError();
+  e = hipGetLastError();
+  if (part_ms) {
+    mark(2);
+    part_ms[0] = part_ms[1] = part_ms[2] = 0.0;
+    if (e == hipSuccess && !evs.empty()) e = hipEventSynchronize(evs.back());
+    for (size_t i = 1; i < evs.size() && e == hipSuccess; ++i) {
+      float ms = 0.0f;
+      if ((e = hipEventElapsedTime(&ms, evs[i - 1], evs[i])) == hipSuccess) part_ms[parts[i]] += ms;
+    }
+    for (hipEvent_t ev : evs) (void)hipEventDestroy(ev);
+  }
+  return e;
 }
 
 hipError_t pack(const uint8_t* codes, int64_t rows, int64_t d, int bits, int32_t* packed, hipStream_t s) {

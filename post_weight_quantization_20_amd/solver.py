@@ -179,10 +179,7 @@ def gptq_factor_noalloc(H: torch.Tensor, n_total: int, params: Params, U: torch.
     return U, perm
 
 
-def gptq_quantize_layer(W: torch.Tensor, U: torch.Tensor, perm: torch.Tensor, params: Params,
-                        out: Optional[QuantOutput] = None, work: Optional[torch.Tensor] = None,
-                        stream=None) -> QuantOutput:
-    """The column loop: codes (original order), per-group scales and zeros, g_idx and the loss."""
+def _quantize_args(W, U, perm, params, out, work):
     _need_cuda(W, U, perm, work)
     rows, d = W.shape
     if W.stride(1) != 1 or W.dtype not in _DTYPE:
@@ -207,12 +204,33 @@ def gptq_quantize_layer(W: torch.Tensor, U: torch.Tensor, perm: torch.Tensor, pa
         work = _workspace(GPTQ_WS_QUANTIZE, rows, d, params, dev)
     else:
         _want_work(work, gptq_workspace_bytes(GPTQ_WS_QUANTIZE, rows, d, params), dev)
-    st = _lib.lib().gptq_quantize_layer(_ptr(W), _DTYPE[W.dtype], rows, d, W.stride(0), _ptr(U), _ptr(perm),
-                                        ctypes.byref(params.c()), _ptr(out.codes), _ptr(out.scales),
-                                        _ptr(out.zeros), _ptr(out.g_idx), _ptr(out.loss), _ptr(work), work.numel(),
-                                        _stream(stream))
-    _check(st)
+    args = (_ptr(W), _DTYPE[W.dtype], rows, d, W.stride(0), _ptr(U), _ptr(perm), ctypes.byref(params.c()),
+            _ptr(out.codes), _ptr(out.scales), _ptr(out.zeros), _ptr(out.g_idx), _ptr(out.loss), _ptr(work),
+            work.numel())
+    return out, args
+
+
+def gptq_quantize_layer(W: torch.Tensor, U: torch.Tensor, perm: torch.Tensor, params: Params,
+                        out: Optional[QuantOutput] = None, work: Optional[torch.Tensor] = None,
+                        stream=None) -> QuantOutput:
+    """The column loop: codes (original order), per-group scales and zeros, g_idx and the loss."""
+    out, args = _quantize_args(W, U, perm, params, out, work)
+    _check(_lib.lib().gptq_quantize_layer(*args, _stream(stream)))
     return out
+
+
+QUANTIZE_PARTS = ("column_loop", "lazy_products", "other")
+
+
+def gptq_quantize_layer_timed(W: torch.Tensor, U: torch.Tensor, perm: torch.Tensor, params: Params,
+                              out: Optional[QuantOutput] = None, work: Optional[torch.Tensor] = None,
+                              stream=None) -> Tuple[QuantOutput, dict]:
+    """gptq_quantize_layer plus the device milliseconds of its parts (QUANTIZE_PARTS), from events
+    between its launches; waits for the stream."""
+    out, args = _quantize_args(W, U, perm, params, out, work)
+    ms = (ctypes.c_double * 3)()
+    _check(_lib.lib().gptq_quantize_layer_timed(*args, ms, _stream(stream)))
+    return out, dict(zip(QUANTIZE_PARTS, (float(ms[0]), float(ms[1]), float(ms[2]))))
 
 
 def packed_words(d: int, bits: int, dense: bool = False) -> int:

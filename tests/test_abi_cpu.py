@@ -136,6 +136,21 @@ def test_factor_noalloc_rejects_bad_arguments():
     assert "#define GPTQ_FACTOR_NOALLOC_MAX_D 12288" in open(HEADER).read()
 
 
+def test_quantize_timed_rejects_missing_output():
+    """The timed column loop needs somewhere to put its part times; without it nothing is queued."""
+    L = _lib()
+    lib = L.lib()
+    p = _p(L)
+    f = lib.gptq_quantize_layer_timed
+    big = ctypes.c_size_t(1 << 40)
+    assert f(FAKE, 1, 16, 64, 64, FAKE, FAKE, ctypes.byref(p), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, big, None,
+             None) == -1
+    ms = (ctypes.c_double * 3)(7.0, 7.0, 7.0)
+    assert f(FAKE, 1, 16, 64, 63, FAKE, FAKE, ctypes.byref(p), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, big, ms,
+             None) == -1   # ld_w < d
+    assert list(ms) == [7.0, 7.0, 7.0]
+
+
 def test_quantize_rejects_bad_arguments():
     L = _lib()
     lib = L.lib()
