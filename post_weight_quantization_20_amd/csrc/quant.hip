@@ -74,7 +74,12 @@ GPTQ_DEV void lds_load(const float* p, float (&v)[N]) {
 // product after the launch.
 // STATIC: every column takes the grid of its static group, colgrp[b + k] (loaded one chunk ahead with
 // U's rows); no grid is computed here.
-template <int CPL, bool STATIC>
+// SUB: the block's chain in 16-column sub-blocks with one column a lane (B a multiple of 16 is not
+// needed, but in-block groups must start at multiples of 16 columns): each column's chain updates
+// only its own sub-block, and a sub-block's errors reach the block's later columns as 16 x 16 x 4
+// MFMA tiles in LDS. Otherwise every lane holds CPL columns of the block and each column's update
+// reaches all of them.
+template <int CPL, bool STATIC, bool SUB>
 __global__ __launch_bounds__(256) void quant_super_kernel(QArgs a) {
   constexpr int BP = 16 * CPL;
   extern __shared__ float sm[];
@@ -197,6 +202,111 @@ __global__ __launch_bounds__(256) void quant_super_kernel(QArgs a) {
     }
     __syncthreads();   // U's block staged
 
+    if constexpr (SUB) {
+      const int l16 = lane & 15, lq = lane >> 4;
+      float* esrow = Es + rloc * BP;
+      uint8_t* qsrow = Qs + rloc * BP;
+      for (int cs = 0; cs < nc; cs += 16) {
+        const int ncs = min(16, nc - cs);
+        float ws = (lr < ncs) ? wsrow[boff + cs + lr] : 0.0f;   // this lane's column
+        float u[16], iv[16];
+#pragma unroll
+        for (int c = 0; c < 16; ++c) {
+          u[c] = Us[(cs + c) * BP + cs + lr];   // U[cs + c][cs + lr]: zero unless lr > c
+          iv[c] = invd[cs + c];
+        }
+        // a group starting here (in-block groups of a multiple of 16 columns): its grid from the
+        // current weights of its columns, which every earlier sub-block's errors have reached
+        if (!STATIC && a.grid_mode == 0 && cs % a.g == 0) {
+          const int gend = (int)min<int64_t>(cs + a.g, nc);
+          float mn = INFINITY, mx = -INFINITY;
+          for (int c = cs + lr; c < gend; c += 16) {
+            const float v = wsrow[boff + c];
+            mn = fminf(mn, v);
+            mx = fmaxf(mx, v);
+          }
+          mn = fminf(mn, row_ror<8>(mn)); mx = fmaxf(mx, row_ror<8>(mx));
+          mn = fminf(mn, row_ror<4>(mn)); mx = fmaxf(mx, row_ror<4>(mx));
+          mn = fminf(mn, row_ror<2>(mn)); mx = fmaxf(mx, row_ror<2>(mx));
+          mn = fminf(mn, row_ror<1>(mn)); mx = fmaxf(mx, row_ror<1>(mx));
+          make_grid(mn, mx, a.maxq, a.sym != 0, a.compact != 0, s, z, rs);
+          if (lr == 0 && row_ok) {
+            const int64_t gi = (uint32_t)(b + cs) / (uint32_t)a.g;
+            a.scales[row * a.ngroups + gi] = s;
+            a.zeros[row * a.ngroups + gi] = (int32_t)z;
+          }
+        }
+        // static groups: this lane's column's grid, broadcast to the row at each column
+        float sg = 1.0f, zg = 0.0f, rsg = 1.0f;
+        if constexpr (STATIC) {
+          const int64_t G = a.colgrp[b + cs + min(lr, ncs - 1)];
+          if (row_ok) {
+            sg = a.scales[row * a.ngroups + G];
+            zg = (float)a.zeros[row * a.ngroups + G];
+          }
+          rsg = 1.0f / sg;
+        }
+        // Column c: every lane of the row runs the chain on the broadcast weight, and the lanes that
+        // hold later columns of the sub-block take its update (U's strict upper part: zero for lanes
+        // lr <= c). Columns past the block's end hold zeros with zero rows of U and 1 / U[k][k] = 0,
+        // so they change nothing.
+        static_for<0, 16>([&](auto cc) {
+          constexpr int c = decltype(cc)::value;
+          if constexpr (STATIC) {
+            s = row_bcast<c>(sg);
+            z = row_bcast<c>(zg);
+            rs = row_bcast<c>(rsg);
+          }
+          const float wk = row_bcast<c>(ws);
+          const float x = div_rn(wk, s, rs);
+          const float qd = __builtin_amdgcn_fmed3f(rintf(x), -z, a.maxq - z);
+          const float e = __builtin_fmaf(-s, qd, wk) * iv[c];
+          ws = __builtin_fmaf(-e, u[c], ws);
+        });
+        // After column lr, nothing changes lane lr's weight again: it is the weight its column was
+        // quantized from, and the same steps give that column's code and error once more, here.
+        {
+          const float so = STATIC ? sg : s, zo = STATIC ? zg : z, rso = STATIC ? rsg : rs;
+          const float x = div_rn(ws, so, rso);
+          const float qd = __builtin_amdgcn_fmed3f(rintf(x), -zo, a.maxq - zo);
+          float e = __builtin_fmaf(-so, qd, ws) * invd[cs + lr];
+          e = lr < ncs ? e : 0.0f;
+          loss = __builtin_fmaf(e, e, loss);
+          esrow[cs + lr] = e;
+          qsrow[cs + lr] = (uint8_t)(qd + zo);
+        }
+        __syncthreads();   // the sub-block's errors of all 16 rows are in Es
+        // ... into the block's later columns of Ws: A = E (16 rows x the sub-block's columns),
+        // B = U's rows of the sub-block, C = a 16-column tile of Ws
+        const int c0 = cs + 16;
+        if (c0 < nc) {
+          const int ntiles = (nc - c0 + 15) / 16;
+          float av[4];
+#pragma unroll
+          for (int kk = 0; kk < 4; ++kk) {
+            const int k = cs + 4 * kk + lq;
+            av[kk] = k < nc ? -Es[l16 * BP + k] : 0.0f;
+          }
+          for (int t = wave; t < ntiles; t += 4) {
+            const int col = c0 + 16 * t + l16;
+            floatx4 acc;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) acc[r] = Ws[(4 * lq + r) * a.ldws + boff + col];
+#pragma unroll
+            for (int kk = 0; kk < 4; ++kk) {
+              const int k = cs + 4 * kk + lq;
+              const float bv = (k < nc && col < nc) ? Us[k * BP + col] : 0.0f;
+              acc = __builtin_amdgcn_mfma_f32_16x16x4f32(av[kk], bv, acc, 0, 0, 0);
+            }
+            if (col < nc) {
+#pragma unroll
+              for (int r = 0; r < 4; ++r) Ws[(4 * lq + r) * a.ldws + boff + col] = acc[r];
+            }
+          }
+        }
+        __syncthreads();   // Ws updated before the next sub-block reads it
+      }
+    } else {
     // groups nest inside blocks when g <= B, so they start at block columns 0, g, 2g, ...
     int next_group = (!STATIC && a.grid_mode == 0) ? 0 : (1 << 30);
     const int gsz = (int)min<int64_t>(a.g, (int64_t)BP);
@@ -320,6 +430,7 @@ __global__ __launch_bounds__(256) void quant_super_kernel(QArgs a) {
       }
     }
     __syncthreads();   // the block's codes and errors are in Qs and Es
+    }
 
     if (row_ok) {
       uint8_t* crow = a.codes_p + row * a.d + b;
@@ -406,6 +517,13 @@ __global__ __launch_bounds__(256) void quant_super_kernel(QArgs a) {
         }
       }
     }
+  }
+  if constexpr (SUB) {
+    // each lane summed its own columns' squared errors: the row's sum over its 16 lanes
+    loss += row_ror<8>(loss);
+    loss += row_ror<4>(loss);
+    loss += row_ror<2>(loss);
+    loss += row_ror<1>(loss);
   }
   if (lr == 0 && row_ok) a.row_loss[row] += (double)loss;
 }
@@ -653,22 +771,28 @@ size_t qsmem(int sw) {
   return (16 * (size_t)super_ld(sw) + BP * BP + BP + 16 * BP) * sizeof(float) + 16 * BP;
 }
 
-template <int CPL, bool STATIC>
+template <int CPL, bool STATIC, bool SUB>
 void launch_super(const QArgs& a, hipStream_t s) {
   static bool attr = false;
   if (!attr) {
-    (void)hipFuncSetAttribute((const void*)quant_super_kernel<CPL, STATIC>,
+    (void)hipFuncSetAttribute((const void*)quant_super_kernel<CPL, STATIC, SUB>,
                               hipFuncAttributeMaxDynamicSharedMemorySize, (int)qsmem<CPL>(512 + 16 * CPL));
     attr = true;
   }
-  hipLaunchKernelGGL((quant_super_kernel<CPL, STATIC>), dim3((unsigned)((a.rows + 15) / 16)), dim3(256),
+  hipLaunchKernelGGL((quant_super_kernel<CPL, STATIC, SUB>), dim3((unsigned)((a.rows + 15) / 16)), dim3(256),
                      qsmem<CPL>(a.sw), s, a);
 }
 
 template <int CPL>
 void launch_super(const QArgs& a, bool is_static, hipStream_t s) {
-  if (is_static) launch_super<CPL, true>(a, s);
-  else launch_super<CPL, false>(a, s);
+  if (is_static) launch_super<CPL, true, false>(a, s);
+  else launch_super<CPL, false, false>(a, s);
+}
+
+// The sub-block chain for 128-column blocks (B > 64), when in-block groups start at multiples of 16.
+void launch_super_sub(const QArgs& a, bool is_static, hipStream_t s) {
+  if (is_static) launch_super<8, true, true>(a, s);
+  else launch_super<8, false, true>(a, s);
 }
 
 int cpl_for(int B) { return B <= 16 ? 1 : B <= 32 ? 2 : B <= 64 ? 4 : 8; }
@@ -772,11 +896,16 @@ hipError_t quantize(const void* W, int w_dtype, int64_t rows, int64_t d, int64_t
     a.scales = scales; a.zeros = zeros; a.ngroups = ngroups; a.err = err; a.err_ld = L.ld_err;
     a.row_loss = row_loss; a.sym = sym; a.compact = compact; a.colgrp = colgrp;
     const bool st = static_groups != 0;
-    switch (cpl) {
-      case 1: launch_super<1>(a, st, s); break;
-      case 2: launch_super<2>(a, st, s); break;
-      case 4: launch_super<4>(a, st, s); break;
-      default: launch_super<8>(a, st, s); break;
+    const bool sub = cpl == 8 && (st || grid_mode != 0 || g % 16 == 0);
+    if (sub) {
+      launch_super_sub(a, st, s);
+    } else {
+      switch (cpl) {
+        case 1: launch_super<1>(a, st, s); break;
+        case 2: launch_super<2>(a, st, s); break;
+        case 4: launch_super<4>(a, st, s); break;
+        default: launch_super<8>(a, st, s); break;
+      }
     }
     mark(0);
     if (s1 < d) {  // the super-block's errors to every later column at once
