@@ -82,12 +82,15 @@ GPTQ_DEV void lds_load(const float* p, float (&v)[N]) {
 template <int CPL, bool STATIC, bool SUB>
 __global__ __launch_bounds__(256) void quant_super_kernel(QArgs a) {
   constexpr int BP = 16 * CPL;
+  // Row strides of U's block and of the errors, padded so that the MFMA operand reads (four rows of
+  // U at once; one error column over the 16 rows) fall in distinct LDS banks.
+  constexpr int US = BP + 16, ES = BP + 2;
   extern __shared__ float sm[];
   float* Ws = sm;                  // [16 rows][ldws]: the rows' super-block, updated in place
-  float* Us = Ws + 16 * a.ldws;    // [BP][BP]: strict upper part of U's block, zeros elsewhere
-  float* invd = Us + BP * BP;      // [BP]: 1 / U[k][k]
-  float* Es = invd + BP;           // [16 rows][BP]: scaled errors of the block
-  uint8_t* Qs = reinterpret_cast<uint8_t*>(Es + 16 * BP);  // [16 rows][BP]: codes of the block
+  float* Us = Ws + 16 * a.ldws;    // [BP][US]: strict upper part of U's block, zeros elsewhere
+  float* invd = Us + BP * US;      // [BP]: 1 / U[k][k]
+  float* Es = invd + BP;           // [16 rows][ES]: scaled errors of the block
+  uint8_t* Qs = reinterpret_cast<uint8_t*>(Es + 16 * ES);  // [16 rows][BP]: codes of the block
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
@@ -162,14 +165,14 @@ __global__ __launch_bounds__(256) void quant_super_kernel(QArgs a) {
         u.y = (j + 1 > k) ? u.y : 0.0f;
         u.z = (j + 2 > k) ? u.z : 0.0f;
         u.w = (j + 3 > k) ? u.w : 0.0f;
-        *reinterpret_cast<float4*>(Us + k * BP + j) = u;
+        *reinterpret_cast<float4*>(Us + k * US + j) = u;
       }
      }
     }
     if (!filled) {
       for (int e = tid; e < BP * BP; e += 256) {
         const int k = e / BP, j = e % BP;
-        Us[e] = (j > k && j < nc) ? a.U[(b + k) * a.d + b + j] : 0.0f;
+        Us[k * US + j] = (j > k && j < nc) ? a.U[(b + k) * a.d + b + j] : 0.0f;
       }
     }
     for (int k = tid; k < BP; k += 256) invd[k] = (k < nc) ? 1.0f / a.U[(b + k) * a.d + b + k] : 0.0f;
@@ -204,7 +207,7 @@ __global__ __launch_bounds__(256) void quant_super_kernel(QArgs a) {
 
     if constexpr (SUB) {
       const int l16 = lane & 15, lq = lane >> 4;
-      float* esrow = Es + rloc * BP;
+      float* esrow = Es + rloc * ES;
       uint8_t* qsrow = Qs + rloc * BP;
       for (int cs = 0; cs < nc; cs += 16) {
         const int ncs = min(16, nc - cs);
@@ -212,7 +215,7 @@ __global__ __launch_bounds__(256) void quant_super_kernel(QArgs a) {
         float u[16], iv[16];
 #pragma unroll
         for (int c = 0; c < 16; ++c) {
-          u[c] = Us[(cs + c) * BP + cs + lr];   // U[cs + c][cs + lr]: zero unless lr > c
+          u[c] = Us[(cs + c) * US + cs + lr];   // U[cs + c][cs + lr]: zero unless lr > c
           iv[c] = invd[cs + c];
         }
         // a group starting here (in-block groups of a multiple of 16 columns): its grid from the
@@ -285,7 +288,7 @@ __global__ __launch_bounds__(256) void quant_super_kernel(QArgs a) {
 #pragma unroll
           for (int kk = 0; kk < 4; ++kk) {
             const int k = cs + 4 * kk + lq;
-            av[kk] = k < nc ? -Es[l16 * BP + k] : 0.0f;
+            av[kk] = k < nc ? -Es[l16 * ES + k] : 0.0f;
           }
           for (int t = wave; t < ntiles; t += 4) {
             const int col = c0 + 16 * t + l16;
@@ -295,7 +298,7 @@ __global__ __launch_bounds__(256) void quant_super_kernel(QArgs a) {
 #pragma unroll
             for (int kk = 0; kk < 4; ++kk) {
               const int k = cs + 4 * kk + lq;
-              const float bv = (k < nc && col < nc) ? Us[k * BP + col] : 0.0f;
+              const float bv = (k < nc && col < nc) ? Us[k * US + col] : 0.0f;
               acc = __builtin_amdgcn_mfma_f32_16x16x4f32(av[kk], bv, acc, 0, 0, 0);
             }
             if (col < nc) {
@@ -335,7 +338,7 @@ __global__ __launch_bounds__(256) void quant_super_kernel(QArgs a) {
       const int cbase = ((lr + o) & 15) * CPL;
       lds_load<CPL>(invd + o * CPL, iv);
 #pragma unroll
-      for (int c = 0; c < CPL; ++c) lds_load<CPL>(Us + (o * CPL + c) * BP + cbase, ur[c]);
+      for (int c = 0; c < CPL; ++c) lds_load<CPL>(Us + (o * CPL + c) * US + cbase, ur[c]);
     };
     // CHECKS: the chunk may start a group or run past the block's last column (a plain chunk, full
     // and without a group start, runs the column chain with no branch or select)
@@ -399,7 +402,7 @@ __global__ __launch_bounds__(256) void quant_super_kernel(QArgs a) {
 #pragma unroll
         for (int c = 0; c < CPL; ++c) {
           Qs[rloc * BP + o * CPL + c] = (uint8_t)qv[c];
-          Es[rloc * BP + o * CPL + c] = ev[c];
+          Es[rloc * ES + o * CPL + c] = ev[c];
         }
       }
 #pragma unroll
@@ -441,8 +444,10 @@ __global__ __launch_bounds__(256) void quant_super_kernel(QArgs a) {
       if constexpr (CPL == 8) {
         if (vec) {
           *reinterpret_cast<uint2*>(crow + j0) = *reinterpret_cast<const uint2*>(Qs + rloc * BP + j0);
-          *reinterpret_cast<float4*>(erow + j0) = *reinterpret_cast<const float4*>(Es + rloc * BP + j0);
-          *reinterpret_cast<float4*>(erow + j0 + 4) = *reinterpret_cast<const float4*>(Es + rloc * BP + j0 + 4);
+          const float2* es = reinterpret_cast<const float2*>(Es + rloc * ES + j0);   // rows 8-byte aligned
+          const float2 e0 = es[0], e1 = es[1], e2 = es[2], e3 = es[3];
+          *reinterpret_cast<float4*>(erow + j0) = float4{e0.x, e0.y, e1.x, e1.y};
+          *reinterpret_cast<float4*>(erow + j0 + 4) = float4{e2.x, e2.y, e3.x, e3.y};
         }
       }
       if (!(CPL == 8 && vec)) {
@@ -451,7 +456,7 @@ __global__ __launch_bounds__(256) void quant_super_kernel(QArgs a) {
           const int j = j0 + t;
           if (j < nc) {
             crow[j] = Qs[rloc * BP + j];
-            erow[j] = Es[rloc * BP + j];
+            erow[j] = Es[rloc * ES + j];
           }
         }
       }
@@ -479,7 +484,7 @@ __global__ __launch_bounds__(256) void quant_super_kernel(QArgs a) {
             const int kk = k0 + i, k = 4 * kk + lq;
             const bool ok = kk < ksteps && k < nc;
             const float* ur = up + (int64_t)(4 * kk) * a.d;
-            av[i] = ok ? -Es[l16 * BP + k] : 0.0f;
+            av[i] = ok ? -Es[l16 * ES + k] : 0.0f;
             b0[i] = (ok && ok0) ? ur[col0] : 0.0f;
             b1[i] = (ok && ok1) ? ur[col1] : 0.0f;
           }
@@ -768,7 +773,7 @@ int super_ld(int sw) { return (sw + 15) / 16 * 16 + 4; }
 template <int CPL>
 size_t qsmem(int sw) {
   constexpr size_t BP = 16 * CPL;
-  return (16 * (size_t)super_ld(sw) + BP * BP + BP + 16 * BP) * sizeof(float) + 16 * BP;
+  return (16 * (size_t)super_ld(sw) + BP * (BP + 16) + BP + 16 * (BP + 2)) * sizeof(float) + 16 * BP;
 }
 
 template <int CPL, bool STATIC, bool SUB>
