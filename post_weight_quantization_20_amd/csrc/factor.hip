@@ -579,8 +579,9 @@ hipError_t factor(const float* H, int64_t d, int64_t n, double damp, int act_ord
   // step j starts after Cholesky step j is complete, its trailing update included (that update reads
   // the column panel the inverse step overwrites), and touches only columns left of block j + 1,
   // which the later Cholesky steps neither read nor write. A cross-stream wait costs the host several
-  // microseconds, so hs waits once per TB Cholesky steps and then runs those TB inverse steps.
-  // With one_stream, hs is s itself and the steps simply follow one another.
+  // microseconds, so hs waits once per TB Cholesky steps and then runs those TB inverse steps; the
+  // last TB steps go one at a time, so that after the last Cholesky step only one inverse step is
+  // left. With one_stream, hs is s itself and the steps simply follow one another.
   constexpr int64_t TB = 4;
   Helpers* hp = nullptr;
   hipError_t e = hipSuccess;
@@ -595,8 +596,8 @@ hipError_t factor(const float* H, int64_t d, int64_t n, double damp, int act_ord
   }
   const int64_t nblk = (d + NB - 1) / NB;
   const int vec = d % 4 == 0 && (uintptr_t)U % 16 == 0;
-  for (int64_t kt = 0; kt < nblk && e == hipSuccess; kt += TB) {
-    const int64_t kend = std::min(nblk, kt + TB);
+  for (int64_t kt = 0, kend = 0; kt < nblk && e == hipSuccess; kt = kend) {
+    kend = kt + TB <= nblk - TB ? kt + TB : kt + 1;
     for (int64_t k = kt; k < kend && e == hipSuccess; ++k) {
       const int64_t k0 = k * NB, k1 = std::min(d, k0 + NB), kb = k1 - k0;
       // the diagonal block, and the column panel P below it staged for the panel solve (the
