@@ -432,6 +432,11 @@ __global__ __launch_bounds__(256) void quant_super_kernel(QArgs a) {
         run(o + 1, ivB, urB, sB, zB);
       }
     }
+    // the errors of columns nc .. 16 ceil(nc / 16) - 1 read as zeros in the update below
+    for (int e = tid; e < 16 * 16; e += 256) {
+      const int k = nc + e % 16;
+      if (k < (nc + 15) / 16 * 16) Es[(e / 16) * ES + k] = 0.0f;
+    }
     __syncthreads();   // the block's codes and errors are in Qs and Es
     }
 
@@ -462,65 +467,93 @@ __global__ __launch_bounds__(256) void quant_super_kernel(QArgs a) {
       }
     }
 
-    // The block's errors into the super-block's later columns: Ws[:, c0:sw] -= E U[b:b+nc, s0+c0:s0+sw],
-    // 16-column tiles dealt to the four waves, two at a time. v_mfma_f32_16x16x4f32 takes A[l % 16][k +
-    // l / 16] and B[k + l / 16][l % 16] from lane l, and register r of its result holds row
-    // 4 (l / 16) + r, column l % 16: here A = E (the 16 rows by the block's columns), B = U's rows of the
-    // block, C = the tile of Ws.
+    // The block's errors into the super-block's later columns: Ws[:, c0:sw] -= E U[b:b+nc, s0+c0:s0+sw].
+    // v_mfma_f32_16x16x4f32 takes A[l % 16][k + l / 16] and B[k + l / 16][l % 16] from lane l, and
+    // register r of its result holds row 4 (l / 16) + r, column l % 16: here A = E (the 16 rows by the
+    // block's columns), B = U's rows of the block, C = Ws. The columns go in 32-column strips, each two
+    // 16-column tiles interleaved: tile u of strip j gives its column n to global column
+    // c0 + 32 j + 2 n + u, so that one 8-byte load fetches a lane's operands of both tiles. Wave w
+    // holds strips w, w + 4, ... (up to MS at once) with every accumulator live, and the loop runs over
+    // k outermost, the operands of the next KC k-steps in flight while the current ones feed the MFMAs.
     const int c0 = boff + nc;
     if (c0 < sw) {
       const int l16 = lane & 15, lq = lane >> 4;
       const int ksteps = (nc + 3) / 4;
-      const int ntiles = (sw - c0 + 15) / 16;
-      constexpr int KC = 8;   // k-steps whose operands are fetched together, one group ahead
-      for (int t = wave; t < ntiles; t += 8) {
-        const bool two = t + 4 < ntiles;
-        const int col0 = c0 + 16 * t + l16, col1 = col0 + 64;
-        const bool ok0 = col0 < sw, ok1 = two && col1 < sw;
-        const float* up = a.U + (b + lq) * a.d + a.s0;
-        auto fetch_k = [&](int k0, float (&av)[KC], float (&b0)[KC], float (&b1)[KC]) {
+      const int nst = (sw - c0 + 31) / 32;
+      constexpr int MS = 3, KC = 4;
+      // 8-byte loads when aligned and both columns of every pair exist together (an even width left)
+      const bool v2 = (a.s0 + c0) % 2 == 0 && a.d % 2 == 0 && (uintptr_t)a.U % 8 == 0 && (sw - c0) % 2 == 0;
+      auto strips = [&](auto vec) {
+        constexpr bool V2 = decltype(vec)::value;
+        for (int j0 = 0; j0 < nst; j0 += 4 * MS) {
+          // Strip m's columns of this lane (within the super-block), and the columns its loads read:
+          // a column past the super-block reads column c0 instead, into an accumulator that is not
+          // stored. The loads are unconditional: a masked load, or a select on its value, would
+          // make the wave wait for it ahead of the MFMAs that do not need it.
+          int col[MS], rd0[MS], rd1[MS];
+          bool okc[MS][2];
+          floatx4 acc[MS][2];
 #pragma unroll
-          for (int i = 0; i < KC; ++i) {
-            const int kk = k0 + i, k = 4 * kk + lq;
-            const bool ok = kk < ksteps && k < nc;
-            const float* ur = up + (int64_t)(4 * kk) * a.d;
-            av[i] = ok ? -Es[l16 * ES + k] : 0.0f;
-            b0[i] = (ok && ok0) ? ur[col0] : 0.0f;
-            b1[i] = (ok && ok1) ? ur[col1] : 0.0f;
+          for (int m = 0; m < MS; ++m) {
+            const int j = j0 + wave + 4 * m;
+            col[m] = c0 + 32 * j + 2 * l16;
+            okc[m][0] = j < nst && col[m] < sw;
+            okc[m][1] = j < nst && col[m] + 1 < sw;
+            rd0[m] = okc[m][0] ? col[m] : c0;
+            rd1[m] = okc[m][1] ? col[m] + 1 : c0;
+#pragma unroll
+            for (int u = 0; u < 2; ++u)
+#pragma unroll
+              for (int r = 0; r < 4; ++r)
+                acc[m][u][r] = okc[m][u] ? Ws[(4 * lq + r) * a.ldws + col[m] + u] : 0.0f;
           }
-        };
-        float avA[KC], b0A[KC], b1A[KC], avB[KC], b0B[KC], b1B[KC];
-        fetch_k(0, avA, b0A, b1A);
-        floatx4 acc0, acc1;
+          float avA[KC], avB[KC];
+          float2 bvA[KC][MS], bvB[KC][MS];
+          // The errors of columns nc .. 16 ceil(nc / 16) - 1 are zero, which covers every k the
+          // k-steps reach past the block; those k read U's row b.
+          auto fetch = [&](int kg, float (&av)[KC], float2 (&bv)[KC][MS]) {
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          acc0[r] = Ws[(4 * lq + r) * a.ldws + col0];
-          acc1[r] = two ? Ws[(4 * lq + r) * a.ldws + col1] : 0.0f;
-        }
-        auto mma = [&](const float (&av)[KC], const float (&b0)[KC], const float (&b1)[KC]) {
+            for (int i = 0; i < KC; ++i) {
+              const int k = 4 * (kg + i) + lq;
+              av[i] = -Es[l16 * ES + k];
+              const float* ur = a.U + (b + (k < nc ? k : 0)) * a.d + a.s0;
 #pragma unroll
-          for (int i = 0; i < KC; ++i) {
-            acc0 = __builtin_amdgcn_mfma_f32_16x16x4f32(av[i], b0[i], acc0, 0, 0, 0);
-            acc1 = __builtin_amdgcn_mfma_f32_16x16x4f32(av[i], b1[i], acc1, 0, 0, 0);
+              for (int m = 0; m < MS; ++m) {
+                if constexpr (V2) bv[i][m] = *reinterpret_cast<const float2*>(ur + rd0[m]);
+                else bv[i][m] = float2{ur[rd0[m]], ur[rd1[m]]};
+              }
+            }
+          };
+          auto mma = [&](const float (&av)[KC], const float2 (&bv)[KC][MS]) {
+#pragma unroll
+            for (int i = 0; i < KC; ++i)
+#pragma unroll
+              for (int m = 0; m < MS; ++m) {
+                acc[m][0] = __builtin_amdgcn_mfma_f32_16x16x4f32(av[i], bv[i][m].x, acc[m][0], 0, 0, 0);
+                acc[m][1] = __builtin_amdgcn_mfma_f32_16x16x4f32(av[i], bv[i][m].y, acc[m][1], 0, 0, 0);
+              }
+          };
+          fetch(0, avA, bvA);
+          for (int kg = 0; kg < ksteps; kg += 2 * KC) {
+            if (kg + KC < ksteps) fetch(kg + KC, avB, bvB);
+            mma(avA, bvA);
+            if (kg + KC < ksteps) {
+              if (kg + 2 * KC < ksteps) fetch(kg + 2 * KC, avA, bvA);
+              mma(avB, bvB);
+            }
           }
-        };
-        for (int k0 = 0; k0 < ksteps; k0 += 2 * KC) {
-          if (k0 + KC < ksteps) fetch_k(k0 + KC, avB, b0B, b1B);
-          mma(avA, b0A, b1A);
-          if (k0 + KC < ksteps) {
-            if (k0 + 2 * KC < ksteps) fetch_k(k0 + 2 * KC, avA, b0A, b1A);
-            mma(avB, b0B, b1B);
-          }
-        }
-        if (ok0) {
 #pragma unroll
-          for (int r = 0; r < 4; ++r) Ws[(4 * lq + r) * a.ldws + col0] = acc0[r];
-        }
-        if (ok1) {
+          for (int m = 0; m < MS; ++m)
 #pragma unroll
-          for (int r = 0; r < 4; ++r) Ws[(4 * lq + r) * a.ldws + col1] = acc1[r];
+            for (int u = 0; u < 2; ++u)
+              if (okc[m][u]) {
+#pragma unroll
+                for (int r = 0; r < 4; ++r) Ws[(4 * lq + r) * a.ldws + col[m] + u] = acc[m][u][r];
+              }
         }
-      }
+      };
+      if (v2) strips(std::true_type{});
+      else strips(std::false_type{});
     }
   }
   if constexpr (SUB) {
