@@ -212,12 +212,11 @@ __global__ __launch_bounds__(256) void quant_super_kernel(QArgs a) {
       for (int cs = 0; cs < nc; cs += 16) {
         const int ncs = min(16, nc - cs);
         float ws = (lr < ncs) ? wsrow[boff + cs + lr] : 0.0f;   // this lane's column
-        float u[16], iv[16];
+        // U[cs + c][cs + lr] / U[cs + c][cs + c], zero unless lr > c: the update of this lane's column
+        // by column c's unscaled difference w - s (q - z), scaled here, off the chain
+        float u[16];
 #pragma unroll
-        for (int c = 0; c < 16; ++c) {
-          u[c] = Us[(cs + c) * US + cs + lr];   // U[cs + c][cs + lr]: zero unless lr > c
-          iv[c] = invd[cs + c];
-        }
+        for (int c = 0; c < 16; ++c) u[c] = Us[(cs + c) * US + cs + lr] * invd[cs + c];
         // a group starting here (in-block groups of a multiple of 16 columns): its grid from the
         // current weights of its columns, which every earlier sub-block's errors have reached
         if (!STATIC && a.grid_mode == 0 && cs % a.g == 0) {
@@ -250,9 +249,9 @@ __global__ __launch_bounds__(256) void quant_super_kernel(QArgs a) {
           rsg = 1.0f / sg;
         }
         // Column c: every lane of the row runs the chain on the broadcast weight, and the lanes that
-        // hold later columns of the sub-block take its update (U's strict upper part: zero for lanes
-        // lr <= c). Columns past the block's end hold zeros with zero rows of U and 1 / U[k][k] = 0,
-        // so they change nothing.
+        // hold later columns of the sub-block take its update, the difference w - s (q - z) times
+        // U's row scaled by 1 / U[c][c] (zero for lanes lr <= c). Columns past the block's end hold
+        // zeros with zero rows of U and 1 / U[k][k] = 0, so they change nothing.
         static_for<0, 16>([&](auto cc) {
           constexpr int c = decltype(cc)::value;
           if constexpr (STATIC) {
@@ -263,8 +262,7 @@ __global__ __launch_bounds__(256) void quant_super_kernel(QArgs a) {
           const float wk = row_bcast<c>(ws);
           const float x = div_rn(wk, s, rs);
           const float qd = __builtin_amdgcn_fmed3f(rintf(x), -z, a.maxq - z);
-          const float e = __builtin_fmaf(-s, qd, wk) * iv[c];
-          ws = __builtin_fmaf(-e, u[c], ws);
+          ws = __builtin_fmaf(-__builtin_fmaf(-s, qd, wk), u[c], ws);
         });
         // After column lr, nothing changes lane lr's weight again: it is the weight its column was
         // quantized from, and the same steps give that column's code and error once more, here.
