@@ -276,37 +276,42 @@ __global__ __launch_bounds__(256) void quant_super_kernel(QArgs a) {
           esrow[cs + lr] = e;
           qsrow[cs + lr] = (uint8_t)(qd + zo);
         }
-        __syncthreads();   // the sub-block's errors of all 16 rows are in Es
-        // ... into the block's later columns of Ws: A = E (16 rows x the sub-block's columns),
-        // B = U's rows of the sub-block, C = a 16-column tile of Ws
+        // ... into the block's later columns, for this wave's four rows only, so no other wave waits:
+        // v_mfma_f32_4x4x1f32 with 16 blocks takes A[l % 4][k] (the same four rows in every block)
+        // and B[k][l] from lane l, and register r of lane l holds row r, column l, of a 4 x 64 tile.
+        // A = E (the wave's rows by the sub-block's columns), B = U's rows of the sub-block, C = 64
+        // of the block's later columns of Ws. The lanes' stores above and the reads below cross
+        // lanes of this wave only.
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+        __builtin_amdgcn_wave_barrier();
         const int c0 = cs + 16;
         if (c0 < nc) {
-          const int ntiles = (nc - c0 + 15) / 16;
-          float av[4];
+          const int rb = 4 * wave;   // the wave's first row of the 16
+          float av[16];
 #pragma unroll
-          for (int kk = 0; kk < 4; ++kk) {
-            const int k = cs + 4 * kk + lq;
-            av[kk] = k < nc ? -Es[l16 * ES + k] : 0.0f;
-          }
-          for (int t = wave; t < ntiles; t += 4) {
-            const int col = c0 + 16 * t + l16;
+          for (int k = 0; k < 16; ++k) av[k] = -Es[(rb + (lane & 3)) * ES + cs + k];
+          for (int h = c0; h < nc; h += 64) {
+            const int col = h + lane;
+            const bool ok = col < nc;
+            const int cr = ok ? col : cs;   // a column inside U's block for the loads
             floatx4 acc;
 #pragma unroll
-            for (int r = 0; r < 4; ++r) acc[r] = Ws[(4 * lq + r) * a.ldws + boff + col];
+            for (int r = 0; r < 4; ++r) acc[r] = Ws[(rb + r) * a.ldws + boff + cr];
+            float bv[16];
 #pragma unroll
-            for (int kk = 0; kk < 4; ++kk) {
-              const int k = cs + 4 * kk + lq;
-              const float bv = (k < nc && col < nc) ? Us[k * US + col] : 0.0f;
-              acc = __builtin_amdgcn_mfma_f32_16x16x4f32(av[kk], bv, acc, 0, 0, 0);
-            }
-            if (col < nc) {
+            for (int k = 0; k < 16; ++k) bv[k] = Us[(cs + k) * US + cr];
 #pragma unroll
-              for (int r = 0; r < 4; ++r) Ws[(4 * lq + r) * a.ldws + boff + col] = acc[r];
+            for (int k = 0; k < 16; ++k) acc = __builtin_amdgcn_mfma_f32_4x4x1f32(av[k], bv[k], acc, 0, 0, 0);
+            if (ok) {
+#pragma unroll
+              for (int r = 0; r < 4; ++r) Ws[(rb + r) * a.ldws + boff + col] = acc[r];
             }
           }
         }
-        __syncthreads();   // Ws updated before the next sub-block reads it
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+        __builtin_amdgcn_wave_barrier();   // this wave's Ws columns updated before its next sub-block
       }
+      __syncthreads();   // the block's codes and errors of all 16 rows are in Qs and Es
     } else {
     // groups nest inside blocks when g <= B, so they start at block columns 0, g, 2g, ...
     int next_group = (!STATIC && a.grid_mode == 0) ? 0 : (1 << 30);

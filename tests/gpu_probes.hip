@@ -43,6 +43,16 @@ __global__ void mfma_f32_16_kernel(const float* A, const float* B, float* D) {
   for (int r = 0; r < 4; ++r) D[(4 * (l / 16) + r) * 16 + l % 16] = acc[r];
 }
 
+// D (4 x 64) = A (4 x 4) B (4 x 64), fp32; one wave, four steps of the 16-block 4 x 4 x 1 MFMA. Lane
+// l supplies A[l % 4][k] (the same four rows to every block) and B[k][l]; register r of lane l is
+// taken to hold D[r][l].
+__global__ void mfma_f32_4x4_kernel(const float* A, const float* B, float* D) {
+  const int l = threadIdx.x;
+  floatx4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
+  for (int k = 0; k < 4; ++k) acc = __builtin_amdgcn_mfma_f32_4x4x1f32(A[(l % 4) * 4 + k], B[k * 64 + l], acc, 0, 0, 0);
+  for (int r = 0; r < 4; ++r) D[r * 64 + l] = acc[r];
+}
+
 // out[src * 64 + lane] = value of lane (16 * (lane / 16) + src), through row_bcast<src>; one wave.
 __global__ void bcast_kernel(const float* in, float* out) {
   const int l = threadIdx.x;
@@ -91,6 +101,11 @@ int probe_mfma_f32(const float* A, const float* B, float* D) {
 
 int probe_mfma_f32_16(const float* A, const float* B, float* D) {
   hipLaunchKernelGGL(mfma_f32_16_kernel, dim3(1), dim3(64), 0, 0, A, B, D);
+  return sync_status();
+}
+
+int probe_mfma_f32_4x4(const float* A, const float* B, float* D) {
+  hipLaunchKernelGGL(mfma_f32_4x4_kernel, dim3(1), dim3(64), 0, 0, A, B, D);
   return sync_status();
 }
 

@@ -122,7 +122,7 @@ def load_probes():
     if not os.path.exists(PROBES_LIB):
         pytest.skip("probe library not built (run __graft_entry__.build())")
     L = ctypes.CDLL(PROBES_LIB)
-    for n in ("probe_mfma_f16", "probe_mfma_bf16", "probe_mfma_f32", "probe_row_bcast", "probe_row_ror15",
-              "probe_div"):
+    for n in ("probe_mfma_f16", "probe_mfma_bf16", "probe_mfma_f32", "probe_mfma_f32_16", "probe_mfma_f32_4x4",
+              "probe_row_bcast", "probe_row_ror15", "probe_div"):
         getattr(L, n).restype = ctypes.c_int
     return L

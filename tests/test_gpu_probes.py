@@ -54,6 +54,18 @@ def test_mfma_f32_16x16_layout():
     assert np.array_equal(d.cpu().numpy(), A @ B)
 
 
+def test_mfma_f32_4x4_layout():
+    torch = torch_cuda()
+    L = load_probes()
+    rng = np.random.default_rng(5)
+    A = rng.integers(-8, 9, size=(4, 4)).astype(np.float32)
+    B = rng.integers(-8, 9, size=(4, 64)).astype(np.float32)
+    a, b = torch.from_numpy(A).cuda(), torch.from_numpy(B).cuda()
+    d = torch.zeros((4, 64), dtype=torch.float32, device="cuda")
+    assert L.probe_mfma_f32_4x4(_p(a), _p(b), _p(d)) == 0
+    assert np.array_equal(d.cpu().numpy(), A @ B)
+
+
 def test_row_broadcast_and_rotation():
     torch = torch_cuda()
     L = load_probes()
