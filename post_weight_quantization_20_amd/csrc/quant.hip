@@ -290,23 +290,45 @@ __global__ __launch_bounds__(256) void quant_super_kernel(QArgs a) {
           float av[16];
 #pragma unroll
           for (int k = 0; k < 16; ++k) av[k] = -Es[(rb + (lane & 3)) * ES + cs + k];
-          for (int h = c0; h < nc; h += 64) {
-            const int col = h + lane;
-            const bool ok = col < nc;
-            const int cr = ok ? col : cs;   // a column inside U's block for the loads
-            floatx4 acc;
+          // columns c0 + lane and c0 + 64 + lane; each sum split over even and odd k, so that four
+          // independent accumulators hide the MFMA latency
+          const bool two = nc - c0 > 64;
+          int cr[2];
+          bool ok[2];
 #pragma unroll
-            for (int r = 0; r < 4; ++r) acc[r] = Ws[(rb + r) * a.ldws + boff + cr];
-            float bv[16];
-#pragma unroll
-            for (int k = 0; k < 16; ++k) bv[k] = Us[(cs + k) * US + cr];
-#pragma unroll
-            for (int k = 0; k < 16; ++k) acc = __builtin_amdgcn_mfma_f32_4x4x1f32(av[k], bv[k], acc, 0, 0, 0);
-            if (ok) {
-#pragma unroll
-              for (int r = 0; r < 4; ++r) Ws[(rb + r) * a.ldws + boff + col] = acc[r];
-            }
+          for (int h = 0; h < 2; ++h) {
+            const int col = c0 + 64 * h + lane;
+            ok[h] = col < nc && (h == 0 || two);
+            cr[h] = ok[h] ? col : cs;   // a column inside U's block for the loads
           }
+          floatx4 acc[2][2];
+          float bv[2][16];
+#pragma unroll
+          for (int h = 0; h < 2; ++h) {
+            if (h == 1 && !two) break;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) acc[h][0][r] = Ws[(rb + r) * a.ldws + boff + cr[h]];
+            acc[h][1] = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+            for (int k = 0; k < 16; ++k) bv[h][k] = Us[(cs + k) * US + cr[h]];
+          }
+          if (two) {
+#pragma unroll
+            for (int k = 0; k < 16; ++k) {
+              acc[0][k & 1] = __builtin_amdgcn_mfma_f32_4x4x1f32(av[k], bv[0][k], acc[0][k & 1], 0, 0, 0);
+              acc[1][k & 1] = __builtin_amdgcn_mfma_f32_4x4x1f32(av[k], bv[1][k], acc[1][k & 1], 0, 0, 0);
+            }
+          } else {
+#pragma unroll
+            for (int k = 0; k < 16; ++k)
+              acc[0][k & 1] = __builtin_amdgcn_mfma_f32_4x4x1f32(av[k], bv[0][k], acc[0][k & 1], 0, 0, 0);
+          }
+#pragma unroll
+          for (int h = 0; h < 2; ++h)
+            if (ok[h]) {
+#pragma unroll
+              for (int r = 0; r < 4; ++r) Ws[(rb + r) * a.ldws + boff + c0 + 64 * h + lane] = acc[h][0][r] + acc[h][1][r];
+            }
         }
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
         __builtin_amdgcn_wave_barrier();   // this wave's Ws columns updated before its next sub-block
