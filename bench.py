@@ -547,10 +547,9 @@ def main():
     stream = torch.cuda.current_stream()
 
     def step(ev=None):
-        H.zero_()
         if ev is not None:
             ev[0].record(stream)
-        g.gptq_hessian_accumulate(H, X, work=ws_h)
+        g.gptq_hessian_compute(H, X, work=ws_h)   # H = 2 X^T X over all calibration tokens
         if ev is not None:
             ev[1].record(stream)
         g.gptq_factor(H, n, params, U=U, perm=perm, work=ws_f)

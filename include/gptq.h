@@ -6,7 +6,8 @@
  * columns not yet quantized through the Cholesky factor of the inverse Hessian of the layer's
  * calibration inputs X (tokens x d). The four calls below are its steps, in order:
  *
- *   gptq_hessian_accumulate  H += 2 X_c^T X_c for each token chunk X_c
+ *   gptq_hessian_accumulate  H += 2 X_c^T X_c for each token chunk X_c (gptq_hessian_compute:
+ *                            H = 2 X_c^T X_c, for the first chunk)
  *   gptq_factor              damping, optional act-order, U = upper Cholesky factor of Hhat^-1
  *   gptq_quantize_layer      the column loop with lazy block updates; codes, scales, zeros, loss
  *   gptq_pack                eight 4-bit codes per 32-bit word (four 8-bit ones)
@@ -122,6 +123,17 @@ typedef struct {
  */
 gptq_status_t gptq_hessian_accumulate(float *H, int64_t d, const void *X, int32_t x_dtype, int64_t n_tok,
                                       int64_t ld_x, void *work, size_t work_bytes, void *stream);
+
+/*
+ * H = 2 * X^T X over one chunk of calibration tokens: gptq_hessian_accumulate for the first chunk,
+ * without zeroing H first (the same source passages). Same arguments and errors as
+ * gptq_hessian_accumulate. H's upper triangle (i <= j) is overwritten and H is not read; entries
+ * below the diagonal are written inside 256 x 256 diagonal tiles only, as there. With n_tok == 0
+ * the whole of H is set to zero. The result is bit for bit that of zeroing H and calling
+ * gptq_hessian_accumulate with the same chunk and workspace.
+ */
+gptq_status_t gptq_hessian_compute(float *H, int64_t d, const void *X, int32_t x_dtype, int64_t n_tok,
+                                   int64_t ld_x, void *work, size_t work_bytes, void *stream);
 
 /*
  * Damping, processing order and the upper Cholesky factor of the damped inverse Hessian

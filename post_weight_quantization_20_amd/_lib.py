@@ -42,6 +42,8 @@ class gptq_block_layer_t(ctypes.Structure):
 SIGNATURES = {
     "gptq_hessian_accumulate": (c_int32, [c_void_p, c_int64, c_void_p, c_int32, c_int64, c_int64, c_void_p, c_size_t,
                                           c_void_p]),
+    "gptq_hessian_compute": (c_int32, [c_void_p, c_int64, c_void_p, c_int32, c_int64, c_int64, c_void_p, c_size_t,
+                                       c_void_p]),
     "gptq_factor": (c_int32, [c_void_p, c_int64, c_int64, ctypes.POINTER(gptq_params_t), c_void_p, c_void_p, c_void_p,
                               c_size_t, ctypes.POINTER(c_int64), c_void_p]),
     "gptq_factor_noalloc": (c_int32, [c_void_p, c_int64, c_int64, ctypes.POINTER(gptq_params_t), c_void_p,

@@ -61,22 +61,41 @@ size_t gptq_workspace_bytes(int32_t kind, int64_t a, int64_t d, const gptq_param
   }
 }
 
-gptq_status_t gptq_hessian_accumulate(float* H, int64_t d, const void* X, int32_t x_dtype, int64_t n_tok,
-                                      int64_t ld_x, void* work, size_t work_bytes, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// gptq_hessian_accumulate (H += 2 X^T X) and gptq_hessian_compute (H = 2 X^T X)
+gptq_status_t hessian_call(float* H, int64_t d, const void* X, int32_t x_dtype, int64_t n_tok, int64_t ld_x,
+                           void* work, size_t work_bytes, void* stream, bool overwrite) {
   if (!H || d <= 0 || d > kMaxDim || n_tok < 0 || n_tok > kMaxDim || !dtype_ok(x_dtype)) return GPTQ_EINVAL;
-  if (n_tok == 0) return GPTQ_OK;
-  if (!X || ld_x < d) return GPTQ_EINVAL;
   hipStream_t s = static_cast<hipStream_t>(stream);
+  if (n_tok == 0) return overwrite ? hip_status(gptq::zero_matrix(H, d * d, s)) : GPTQ_OK;
+  if (!X || ld_x < d) return GPTQ_EINVAL;
   if (x_dtype == GPTQ_F32) {
     gptq::GemmArgs a{};
     a.M = d; a.N = d; a.K = n_tok;
     a.A = static_cast<const float*>(X); a.lda = ld_x; a.transA = 1;
     a.B = static_cast<const float*>(X); a.ldb = ld_x; a.transB = 0;
     a.C = H; a.ldc = d;
-    a.alpha = 2.0f; a.beta = 1.0f; a.tri = 2;
+    a.alpha = 2.0f; a.beta = overwrite ? 0.0f : 1.0f; a.tri = 2;
     return hip_status(gptq::gemm_f32(a, s));
   }
-  return hip_status(gptq::hessian_f16(H, d, X, x_dtype, n_tok, ld_x, work, work_bytes, s));
+  return hip_status(gptq::hessian_f16(H, d, X, x_dtype, n_tok, ld_x, work, work_bytes, s, overwrite));
+}
+
+}  // namespace
+
+extern "C" {
+
+gptq_status_t gptq_hessian_accumulate(float* H, int64_t d, const void* X, int32_t x_dtype, int64_t n_tok,
+                                      int64_t ld_x, void* work, size_t work_bytes, void* stream) {
+  return hessian_call(H, d, X, x_dtype, n_tok, ld_x, work, work_bytes, stream, false);
+}
+
+gptq_status_t gptq_hessian_compute(float* H, int64_t d, const void* X, int32_t x_dtype, int64_t n_tok,
+                                   int64_t ld_x, void* work, size_t work_bytes, void* stream) {
+  return hessian_call(H, d, X, x_dtype, n_tok, ld_x, work, work_bytes, stream, true);
 }
 
 }  // extern "C"

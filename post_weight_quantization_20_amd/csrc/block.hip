@@ -328,9 +328,9 @@ int quantize_block(const gptq_block_shape_t& sh, const void* X, int x_dtype, con
     int st;
     const _Float16* Xs = reinterpret_cast<const _Float16*>(work + L.off_xs) + d;
     float* H2 = reinterpret_cast<float*>(work + L.off_h2);
-    GPTQ_TRY(hipMemsetAsync(H2, 0, (size_t)4 * d * d * 4, s));
-    if ((st = gptq_hessian_accumulate(H2, 2 * d, Xs, GPTQ_F16, n, split3_pitch(d), work + L.off_hw, L.hess_bytes,
-                                      s)) != GPTQ_OK)
+    // overwritten, not accumulated: the fold below reads H2 on and above its diagonal only
+    if ((st = gptq_hessian_compute(H2, 2 * d, Xs, GPTQ_F16, n, split3_pitch(d), work + L.off_hw, L.hess_bytes,
+                                   s)) != GPTQ_OK)
       return st;
     hipLaunchKernelGGL(fold_split_kernel, dim3(grid_for(d * d)), dim3(256), 0, s, H2, d, H);
     GPTQ_TRY(hipGetLastError());

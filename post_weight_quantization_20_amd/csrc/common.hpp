@@ -124,7 +124,9 @@ hipError_t gemm_f32(const GemmArgs& a, hipStream_t s);
 // H (upper tiles) += 2 X^T X for X = [n x d] fp16 / bf16 (leading dimension ldx) on MFMA.
 size_t hessian_workspace_bytes(int64_t n, int64_t d);
 hipError_t hessian_f16(float* H, int64_t d, const void* X, int dtype, int64_t n, int64_t ldx,
-                       void* work, size_t work_bytes, hipStream_t s);
+                       void* work, size_t work_bytes, hipStream_t s, bool overwrite = false);
+// H[0:n) = 0 by a fill kernel (no memset, so that the call may be captured in a graph)
+hipError_t zero_matrix(float* H, int64_t n, hipStream_t s);
 
 // Factor: damping, processing order and U (see factor.hip). status_dev / info_dev receive device
 // addresses of the mean-diagonal check and the first failed pivot (1-based, reversed order).

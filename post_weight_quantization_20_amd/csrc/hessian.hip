@@ -62,6 +62,7 @@ struct HessArgs {
   int64_t split_len;   // tokens per split (multiple of SPLIT_ALIGN)
   float* partial;      // S > 1: one HT x HT partial tile per workgroup
   int vec;             // 16-byte loads allowed
+  int overwrite;       // H's tiles are set to 2 X^T X instead of added to
 };
 
 // Upper-triangle tile pairs (ti <= tj) in an order that keeps neighbours close: super-blocks of
@@ -176,7 +177,8 @@ GPTQ_DEV void zero_acc(floatx16 (&acc)[4][4]) {
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
 }
 
-// Adds 2 * acc to H (one split), or stores the split's partial tile for reduce_partials.
+// Adds 2 * acc to H (sets H to it with overwrite) when there is one split, or stores the split's
+// partial tile for reduce_partials.
 // Accumulator register r of lane l holds row 8*(r/4) + 4*(l/32) + r%4, column l%32 of its 32x32
 // block.
 GPTQ_DEV void finish_tile(const HessArgs& a, const Work& w, const floatx16 (&acc)[4][4]) {
@@ -194,7 +196,7 @@ GPTQ_DEV void finish_tile(const HessArgs& a, const Work& w, const floatx16 (&acc
           const int64_t c = w.fb + wn * 128 + j * 32 + li;
           if (m < a.d && c < a.d) {
             float* h = a.H + m * a.d + c;
-            *h = __builtin_fmaf(2.0f, acc[i][j][r], *h);
+            *h = a.overwrite ? 2.0f * acc[i][j][r] : __builtin_fmaf(2.0f, acc[i][j][r], *h);
           }
         }
     return;
@@ -212,8 +214,8 @@ GPTQ_DEV void finish_tile(const HessArgs& a, const Work& w, const floatx16 (&acc
       }
 }
 
-// H (upper tiles) += 2 * the sum of each tile's partials in token order. Workgroup (tile, chunk)
-// takes 1024 consecutive elements of one tile, four per thread.
+// H (upper tiles) += 2 * the sum of each tile's partials in token order (= with overwrite, and H is
+// not read). Workgroup (tile, chunk) takes 1024 consecutive elements of one tile, four per thread.
 __global__ __launch_bounds__(256) void reduce_partials(HessArgs a) {
   constexpr int CHUNKS = HT * HT / 1024;
   const int tile = blockIdx.x / CHUNKS;
@@ -227,7 +229,7 @@ __global__ __launch_bounds__(256) void reduce_partials(HessArgs a) {
   const int64_t gc0 = (int64_t)tj * HT + e % HT;
   float* h = a.H + gm * a.d + gc0;
   if (a.d % 4 == 0 && (uintptr_t)a.H % 16 == 0 && gc0 + 4 <= a.d) {   // one 16-byte read-modify-write
-    floatx4 v = *reinterpret_cast<const floatx4*>(h);
+    floatx4 v = a.overwrite ? floatx4{0.0f, 0.0f, 0.0f, 0.0f} : *reinterpret_cast<const floatx4*>(h);
 #pragma unroll
     for (int k = 0; k < 4; ++k) v[k] = __builtin_fmaf(2.0f, s[k], v[k]);
     *reinterpret_cast<floatx4*>(h) = v;
@@ -235,7 +237,7 @@ __global__ __launch_bounds__(256) void reduce_partials(HessArgs a) {
   }
 #pragma unroll
   for (int k = 0; k < 4; ++k)
-    if (gc0 + k < a.d) h[k] = __builtin_fmaf(2.0f, s[k], h[k]);
+    if (gc0 + k < a.d) h[k] = __builtin_fmaf(2.0f, s[k], a.overwrite ? 0.0f : h[k]);
 }
 
 // ------------------------------------------------------------------ register-staged path
@@ -594,8 +596,20 @@ size_t hessian_workspace_bytes(int64_t n, int64_t d) {
   return (size_t)p.grid * HT * HT * sizeof(float);
 }
 
+namespace {
+__global__ __launch_bounds__(256) void zero_f32(float* __restrict__ p, int64_t n) {
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256) p[i] = 0.0f;
+}
+}  // namespace
+
+hipError_t zero_matrix(float* H, int64_t n, hipStream_t s) {
+  if (n <= 0) return hipSuccess;
+  hipLaunchKernelGGL(zero_f32, dim3((unsigned)std::min<int64_t>((n + 255) / 256, 65536)), dim3(256), 0, s, H, n);
+  return hipGetLastError();
+}
+
 hipError_t hessian_f16(float* H, int64_t d, const void* X, int dtype, int64_t n, int64_t ldx, void* work,
-                       size_t work_bytes, hipStream_t s) {
+                       size_t work_bytes, hipStream_t s, bool overwrite) {
   if (n <= 0 || d <= 0) return hipSuccess;
   Plan p = plan(n, d);
   if (p.S > 1 && (work == nullptr || work_bytes < hessian_workspace_bytes(n, d))) {
@@ -618,6 +632,7 @@ hipError_t hessian_f16(float* H, int64_t d, const void* X, int dtype, int64_t n,
   a.q = p.q;
   a.split_len = p.split_len;
   a.vec = ((uintptr_t)X % 16 == 0) && (ldx % 8 == 0);
+  a.overwrite = overwrite ? 1 : 0;
   // the DMA path needs 16-byte units that never straddle the end of a row, and 32-bit offsets
   // within a stage
   const bool dma = a.vec && d % 8 == 0 && (int64_t)DK * ldx * 2 < ((int64_t)1 << 31);

@@ -109,9 +109,7 @@ def _workspace(kind: int, a: int, d: int, params: Optional[Params], device) -> t
     return torch.empty(max(n, 1), dtype=torch.uint8, device=device)
 
 
-def gptq_hessian_accumulate(H: torch.Tensor, X: torch.Tensor, work: Optional[torch.Tensor] = None,
-                            stream=None) -> None:
-    """H (float32 [d, d], upper triangle) += 2 X^T X for X [tokens, d] (fp32 / fp16 / bf16)."""
+def _hessian_args(H: torch.Tensor, X: torch.Tensor, work: Optional[torch.Tensor], stream):
     _need_cuda(H, X, work)
     d = H.shape[0]
     if H.dtype != torch.float32 or H.shape != (d, d) or not H.is_contiguous():
@@ -125,8 +123,20 @@ def gptq_hessian_accumulate(H: torch.Tensor, X: torch.Tensor, work: Optional[tor
         work = _workspace(GPTQ_WS_HESSIAN, n, d, None, H.device)
     elif work.dtype != torch.uint8 or not work.is_contiguous() or work.device != H.device:
         raise ValueError("work must be a contiguous uint8 tensor on H's device")
-    _check(_lib.lib().gptq_hessian_accumulate(_ptr(H), d, _ptr(X), _DTYPE[X.dtype], n, X.stride(0), _ptr(work),
-                                              work.numel(), _stream(stream)))
+    return (_ptr(H), d, _ptr(X), _DTYPE[X.dtype], n, X.stride(0), _ptr(work), work.numel(), _stream(stream))
+
+
+def gptq_hessian_accumulate(H: torch.Tensor, X: torch.Tensor, work: Optional[torch.Tensor] = None,
+                            stream=None) -> None:
+    """H (float32 [d, d], upper triangle) += 2 X^T X for X [tokens, d] (fp32 / fp16 / bf16)."""
+    _check(_lib.lib().gptq_hessian_accumulate(*_hessian_args(H, X, work, stream)))
+
+
+def gptq_hessian_compute(H: torch.Tensor, X: torch.Tensor, work: Optional[torch.Tensor] = None,
+                         stream=None) -> None:
+    """H (float32 [d, d], upper triangle) = 2 X^T X for X [tokens, d]: the first chunk, without
+    zeroing H first."""
+    _check(_lib.lib().gptq_hessian_compute(*_hessian_args(H, X, work, stream)))
 
 
 def gptq_factor(H: torch.Tensor, n_total: int, params: Params, U: Optional[torch.Tensor] = None,

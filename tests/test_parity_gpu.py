@@ -129,6 +129,34 @@ def test_hessian_deterministic_with_token_splits(d):
     _check_hessian(outs[0], [xh], "f16")
 
 
+@pytest.mark.parametrize("x_dtype,d,n", [("f16", 264, 8192), ("f16", 260, 8192), ("bf16", 300, 1000),
+                                         ("f32", 300, 1000), ("f16", 776, 700)])
+@pytest.mark.parametrize("split", [True, False])
+def test_hessian_compute_overwrites(x_dtype, d, n, split):
+    """gptq_hessian_compute on an H full of NaN gives, on and above the diagonal, bit for bit what
+    zeroing H and accumulating the same chunk gives (with the token-split workspace and without),
+    and matches the float64 sum; with no tokens it zeroes H."""
+    torch = torch_cuda()
+    import post_weight_quantization_20_amd as g
+    case = _case("hc", 14, d=d, n=n, chunk=n, x_dtype=x_dtype)
+    xh = synth.x_chunk(case, 0)
+    x = dev_tensor(xh, x_dtype)
+    nbytes = g.gptq_workspace_bytes(g.GPTQ_WS_HESSIAN, n, d)
+    work = torch.empty(max(nbytes, 1), dtype=torch.uint8, device="cuda") if split else \
+        torch.empty(1, dtype=torch.uint8, device="cuda")
+    H0 = torch.zeros((d, d), dtype=torch.float32, device="cuda")
+    g.gptq_hessian_accumulate(H0, x, work=work)
+    H1 = torch.full((d, d), float("nan"), dtype=torch.float32, device="cuda")
+    g.gptq_hessian_compute(H1, x, work=work)
+    torch.cuda.synchronize()
+    a0, a1 = np.triu(H0.cpu().numpy()), np.triu(H1.cpu().numpy())
+    assert np.array_equal(a0.view(np.uint32), a1.view(np.uint32))
+    _check_hessian(a1, [xh], x_dtype)
+    g.gptq_hessian_compute(H1, x[:0])
+    torch.cuda.synchronize()
+    assert not torch.any(H1 != 0).item()
+
+
 # ------------------------------------------------------------------ factor
 
 @pytest.mark.parametrize("d,act", [(300, False), (300, True), (129, True), (7, False), (640, False)])
