@@ -580,8 +580,8 @@ hipError_t factor(const float* H, int64_t d, int64_t n, double damp, int act_ord
   // the column panel the inverse step overwrites), and touches only columns left of block j + 1,
   // which the later Cholesky steps neither read nor write. A cross-stream wait costs the host several
   // microseconds, so hs waits once per TB Cholesky steps and then runs those TB inverse steps; the
-  // last TB steps go one at a time, so that after the last Cholesky step only one inverse step is
-  // left. With one_stream, hs is s itself and the steps simply follow one another.
+  // last TB steps go a pair at a time, so that after the last Cholesky step only one pair of inverse
+  // steps is left. With one_stream, hs is s itself and the steps simply follow one another.
   constexpr int64_t TB = 4;
   Helpers* hp = nullptr;
   hipError_t e = hipSuccess;
@@ -596,32 +596,53 @@ hipError_t factor(const float* H, int64_t d, int64_t n, double damp, int act_ord
   }
   const int64_t nblk = (d + NB - 1) / NB;
   const int vec = d % 4 == 0 && (uintptr_t)U % 16 == 0;
+  // Cholesky step k on the caller's stream: the diagonal block (its kernel's other workgroups stage
+  // the column panel P below it: the panel solve's workgroups of one row strip must not overwrite
+  // the columns another one still reads), then the panel solve P <- P L_kk^-T
+  auto chol_step = [&](int64_t k) -> hipError_t {
+    const int64_t k0 = k * NB, k1 = std::min(d, k0 + NB), kb = k1 - k0;
+    const Copy2D pc = make_copy(stage_main, kb, U + k1 * d + k0, d, d - k1, kb);
+    hipLaunchKernelGGL(chol_diag_kernel, dim3(1 + copy_groups(d - k1, kb)), dim3(256), chol_smem(), s, U, d, k0,
+                       (int)kb, vec, w.info, pc);
+    hipError_t r = hipGetLastError();
+    if (r != hipSuccess || k1 >= d) return r;
+    GemmArgs t{};
+    t.M = d - k1; t.N = kb; t.K = kb;
+    t.A = stage_main; t.lda = kb; t.transA = 0;
+    t.B = U + k0 * d + k0; t.ldb = d; t.transB = 1;
+    t.C = U + k1 * d + k0; t.ldc = d;
+    t.alpha = 1.0f; t.beta = 0.0f; t.tri = 0;
+    return gemm_f32(t, s);
+  };
+  // The trailing updates go by pairs of steps (k, k + 1): after step k's panel solve only the next
+  // block column takes its update, A[k1:, k1:k2] -= P_k P_k[0:k2-k1]^T (its diagonal block whole: the
+  // part above the diagonal is never read and the diagonal kernel rewrites it); after step k + 1,
+  // the rest takes both panels' updates in one product, A[k2:, k2:] -= [P_k P_k+1] [P_k P_k+1]^T
+  // (lower part, K = 256: the two panels are adjacent columns of A).
   for (int64_t kt = 0, kend = 0; kt < nblk && e == hipSuccess; kt = kend) {
-    kend = kt + TB <= nblk - TB ? kt + TB : kt + 1;
-    for (int64_t k = kt; k < kend && e == hipSuccess; ++k) {
+    // batches of TB steps, the last ones a pair at a time; a batch ends after a pair's product
+    kend = std::min(nblk, kt + TB <= nblk - TB ? kt + TB : kt + 2);
+    for (int64_t k = kt; k < kend && e == hipSuccess; k += 2) {
       const int64_t k0 = k * NB, k1 = std::min(d, k0 + NB), kb = k1 - k0;
-      // the diagonal block, and the column panel P below it staged for the panel solve (the
-      // product's workgroups of one row strip must not overwrite the columns another one still reads)
-      const Copy2D pc = make_copy(stage_main, kb, U + k1 * d + k0, d, d - k1, kb);
-      hipLaunchKernelGGL(chol_diag_kernel, dim3(1 + copy_groups(d - k1, kb)), dim3(256), chol_smem(), s, U, d, k0,
-                         (int)kb, vec, w.info, pc);
-      if ((e = hipGetLastError()) != hipSuccess) break;
-      if (k1 < d) {
-        // panel solve: P <- P L_kk^-T
-        GemmArgs t{};
-        t.M = d - k1; t.N = kb; t.K = kb;
-        t.A = stage_main; t.lda = kb; t.transA = 0;
-        t.B = U + k0 * d + k0; t.ldb = d; t.transB = 1;
-        t.C = U + k1 * d + k0; t.ldc = d;
-        t.alpha = 1.0f; t.beta = 0.0f; t.tri = 0;
-        if ((e = gemm_f32(t, s)) != hipSuccess) break;
-        GemmArgs u{};  // trailing update: A22 -= P P^T (lower part)
-        u.M = d - k1; u.N = d - k1; u.K = kb;
-        u.A = U + k1 * d + k0; u.lda = d; u.transA = 0;
-        u.B = U + k1 * d + k0; u.ldb = d; u.transB = 1;
-        u.C = U + k1 * d + k1; u.ldc = d;
-        u.alpha = -1.0f; u.beta = 1.0f; u.tri = 1;
-        if ((e = gemm_f32(u, s)) != hipSuccess) break;
+      if ((e = chol_step(k)) != hipSuccess) break;
+      if (k1 >= d) break;
+      const int64_t k2 = std::min(d, k1 + NB);
+      GemmArgs ua{};
+      ua.M = d - k1; ua.N = k2 - k1; ua.K = kb;
+      ua.A = U + k1 * d + k0; ua.lda = d; ua.transA = 0;
+      ua.B = U + k1 * d + k0; ua.ldb = d; ua.transB = 1;
+      ua.C = U + k1 * d + k1; ua.ldc = d;
+      ua.alpha = -1.0f; ua.beta = 1.0f; ua.tri = 0;
+      if ((e = gemm_f32(ua, s)) != hipSuccess) break;
+      if ((e = chol_step(k + 1)) != hipSuccess) break;
+      if (k2 < d) {
+        GemmArgs ub{};
+        ub.M = d - k2; ub.N = d - k2; ub.K = k2 - k0;
+        ub.A = U + k2 * d + k0; ub.lda = d; ub.transA = 0;
+        ub.B = U + k2 * d + k0; ub.ldb = d; ub.transB = 1;
+        ub.C = U + k2 * d + k2; ub.ldc = d;
+        ub.alpha = -1.0f; ub.beta = 1.0f; ub.tri = 1;
+        if ((e = gemm_f32(ub, s)) != hipSuccess) break;
       }
     }
     if (e != hipSuccess) break;
