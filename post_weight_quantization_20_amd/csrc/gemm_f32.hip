@@ -115,7 +115,7 @@ GPTQ_DEV void tri_tile(int64_t t, int64_t n, bool lower, int64_t& tm, int64_t& t
 }
 
 template <int T, bool AK, bool BK>
-__global__ __launch_bounds__(256) void gemm_f32_kernel(GemmArgs a, int64_t tiles_n, int vecA, int vecB) {
+__global__ __launch_bounds__(256, 2) void gemm_f32_kernel(GemmArgs a, int64_t tiles_n, int vecA, int vecB) {
   constexpr int WB = T / 64;  // 32x32 blocks per wave per dimension
   int64_t tm, tn;
   if (a.tri == 0) { tm = blockIdx.x / tiles_n; tn = blockIdx.x % tiles_n; }
@@ -129,8 +129,12 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmArgs a, int64_t tiles
 
   using SA = Stage<T, AK>;
   using SB = Stage<T, BK>;
-  __shared__ __align__(16) float As[2][SA::SIZE];
-  __shared__ __align__(16) float Bs[2][SB::SIZE];
+  // the two operands' double-buffered stages, and after the loop the T x (T + 8) tile of results
+  constexpr int TL = T + 8;
+  constexpr int SMEM = std::max(2 * (SA::SIZE + SB::SIZE), T * TL);
+  __shared__ __align__(16) float smem[SMEM];
+  float (*As)[SA::SIZE] = reinterpret_cast<float (*)[SA::SIZE]>(smem);
+  float (*Bs)[SB::SIZE] = reinterpret_cast<float (*)[SB::SIZE]>(smem + 2 * SA::SIZE);
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
@@ -165,20 +169,39 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmArgs a, int64_t tiles
       la.load(a.A, a.lda, m0, a.M, (kt + 1) * GK, a.K, vecA, tid);
       lb.load(a.B, a.ldb, n0, a.N, (kt + 1) * GK, a.K, vecB, tid);
     }
+    // the operands of the next group of 8 k are read while the current group's MFMAs run
+    float4 av[2][WB], bv[2][WB];
 #pragma unroll
-    for (int kg = 0; kg < GK; kg += 8) {
-      float4 av[WB], bv[WB];
+    for (int i = 0; i < WB; ++i) av[0][i] = operand4<T, AK>(As[cur], wm * (T / 2) + i * 32, 0, lane);
 #pragma unroll
-      for (int i = 0; i < WB; ++i) av[i] = operand4<T, AK>(As[cur], wm * (T / 2) + i * 32, kg, lane);
+    for (int j = 0; j < WB; ++j) bv[0][j] = operand4<T, BK>(Bs[cur], wn * (T / 2) + j * 32, 0, lane);
 #pragma unroll
-      for (int j = 0; j < WB; ++j) bv[j] = operand4<T, BK>(Bs[cur], wn * (T / 2) + j * 32, kg, lane);
+    for (int g = 0; g < GK / 8; ++g) {
+      const int c = g & 1;
+      if (g + 1 < GK / 8) {
+#pragma unroll
+        for (int i = 0; i < WB; ++i) av[c ^ 1][i] = operand4<T, AK>(As[cur], wm * (T / 2) + i * 32, 8 * (g + 1), lane);
+#pragma unroll
+        for (int j = 0; j < WB; ++j) bv[c ^ 1][j] = operand4<T, BK>(Bs[cur], wn * (T / 2) + j * 32, 8 * (g + 1), lane);
+      }
 #pragma unroll
       for (int e = 0; e < 4; ++e)
 #pragma unroll
         for (int i = 0; i < WB; ++i)
 #pragma unroll
           for (int j = 0; j < WB; ++j)
-            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(f4(av[i], e), f4(bv[j], e), acc[i][j], 0, 0, 0);
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(f4(av[c][i], e), f4(bv[c][j], e), acc[i][j], 0, 0, 0);
+    }
+    // instruction order for the scheduler: the first two groups' LDS reads, then each group's MFMAs
+    // followed by the reads of the group after next
+    {
+      constexpr int RA = AK ? WB : 4 * WB, RB = BK ? WB : 4 * WB;  // LDS reads per group, at most
+      __builtin_amdgcn_sched_group_barrier(0x100, 2 * (RA + RB), 0);
+#pragma unroll
+      for (int g = 0; g < GK / 8; ++g) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 4 * WB * WB, 0);
+        if (g + 2 < GK / 8) __builtin_amdgcn_sched_group_barrier(0x100, RA + RB, 0);
+      }
     }
     if (more) {
       la.store(As[cur ^ 1], tid);
@@ -187,50 +210,79 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmArgs a, int64_t tiles
     __syncthreads();
   }
 
-  // Epilogue. Accumulator register r of lane l holds row 8*(r/4) + 4*(l/32) + r%4, column l%32
-  // of its 32x32 block.
-  const bool full = m0 + T <= a.M && n0 + T <= a.N;
-  if (full) {
-    // tile inside C, one 32x32 block at a time: its reads of C, then its writes (on a triangle's
-    // diagonal tile, only the elements inside the triangle are written)
-#pragma unroll
-    for (int i = 0; i < WB; ++i)
-#pragma unroll
-      for (int j = 0; j < WB; ++j) {
-        float* cb = a.C + (m0 + wm * (T / 2) + i * 32 + 4 * lk) * a.ldc + n0 + wn * (T / 2) + j * 32 + li;
-        float cv[16];
-        if (a.beta != 0.0f) {
-#pragma unroll
-          for (int r = 0; r < 16; ++r) cv[r] = cb[(8 * (r >> 2) + (r & 3)) * a.ldc];
-        }
-        const int64_t mb = m0 + wm * (T / 2) + i * 32 + 4 * lk, nb = n0 + wn * (T / 2) + j * 32 + li;
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          float v = a.alpha * acc[i][j][r];
-          if (a.beta != 0.0f) v = __builtin_fmaf(a.beta, cv[r], v);
-          const int64_t m = mb + 8 * (r >> 2) + (r & 3);
-          const bool keep = a.tri == 0 || (a.tri == 1 ? m >= nb : m <= nb);
-          if (keep) cb[(8 * (r >> 2) + (r & 3)) * a.ldc] = v;
-        }
-      }
-    return;
-  }
+  // Epilogue through LDS (the stages are free after the loop's last barrier). Accumulator register
+  // r of lane l holds row 8*(r/4) + 4*(l/32) + r%4, column l%32 of its 32x32 block; the rows of the
+  // tile are padded to T + 8 floats so that the two half-waves' stores (4 rows apart) fall in
+  // distinct banks. Then the workgroup reads C, adds and writes back along rows, each thread's loads
+  // all in flight before its first store.
 #pragma unroll
   for (int i = 0; i < WB; ++i)
 #pragma unroll
     for (int j = 0; j < WB; ++j)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int64_t m = m0 + wm * (T / 2) + i * 32 + 8 * (r >> 2) + 4 * lk + (r & 3);
-        const int64_t n = n0 + wn * (T / 2) + j * 32 + li;
-        if (m >= a.M || n >= a.N) continue;
-        if (a.tri == 1 && m < n) continue;
-        if (a.tri == 2 && m > n) continue;
-        float* c = a.C + m * a.ldc + n;
-        float v = a.alpha * acc[i][j][r];
-        if (a.beta != 0.0f) v = __builtin_fmaf(a.beta, *c, v);
-        *c = v;
+      for (int r = 0; r < 16; ++r)
+        smem[(wm * (T / 2) + i * 32 + 8 * (r >> 2) + 4 * lk + (r & 3)) * TL + wn * (T / 2) + j * 32 + li] =
+            a.alpha * acc[i][j][r];
+  __syncthreads();
+  const bool full = m0 + T <= a.M && n0 + T <= a.N && a.ldc % 4 == 0 && (uintptr_t)a.C % 16 == 0;
+  if (full) {
+    // 16-byte accesses; on a triangle's diagonal tile only the elements inside it are written
+    constexpr int PT = T * T / 4 / 256;
+    const bool whole = a.tri == 0 || (a.tri == 1 ? m0 >= n0 + T - 1 : m0 + T - 1 <= n0);
+    float4 cv[PT];
+    if (a.beta != 0.0f) {
+#pragma unroll
+      for (int q = 0; q < PT; ++q) {
+        const int e = tid + q * 256, row = e / (T / 4), c4 = e % (T / 4) * 4;
+        cv[q] = *reinterpret_cast<const float4*>(a.C + (m0 + row) * a.ldc + n0 + c4);
       }
+    }
+#pragma unroll
+    for (int q = 0; q < PT; ++q) {
+      const int e = tid + q * 256, row = e / (T / 4), c4 = e % (T / 4) * 4;
+      float4 v = *reinterpret_cast<const float4*>(smem + row * TL + c4);
+      if (a.beta != 0.0f) {
+        v.x = __builtin_fmaf(a.beta, cv[q].x, v.x);
+        v.y = __builtin_fmaf(a.beta, cv[q].y, v.y);
+        v.z = __builtin_fmaf(a.beta, cv[q].z, v.z);
+        v.w = __builtin_fmaf(a.beta, cv[q].w, v.w);
+      }
+      float* c = a.C + (m0 + row) * a.ldc + n0 + c4;
+      if (whole) {
+        *reinterpret_cast<float4*>(c) = v;
+      } else {
+        const int64_t m = m0 + row, n = n0 + c4;
+        const float vv[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+          if (a.tri == 1 ? m >= n + u : m <= n + u) c[u] = vv[u];
+      }
+    }
+    return;
+  }
+  // a tile on the edge of C: element by element, 16 at a time, each group's loads first
+  constexpr int PE = 16;
+#pragma unroll 1
+  for (int q0 = 0; q0 < T * T / 256; q0 += PE) {
+    float cv[PE];
+#pragma unroll
+    for (int q = 0; q < PE; ++q) {
+      const int e = tid + (q0 + q) * 256;
+      const int64_t m = m0 + e / T, n = n0 + e % T;
+      const bool in = m < a.M && n < a.N;
+      cv[q] = (a.beta != 0.0f && in) ? a.C[m * a.ldc + n] : 0.0f;
+    }
+#pragma unroll
+    for (int q = 0; q < PE; ++q) {
+      const int e = tid + (q0 + q) * 256;
+      const int64_t m = m0 + e / T, n = n0 + e % T;
+      if (m >= a.M || n >= a.N) continue;
+      if (a.tri == 1 && m < n) continue;
+      if (a.tri == 2 && m > n) continue;
+      const float v = smem[(e / T) * TL + e % T];
+      a.C[m * a.ldc + n] = a.beta != 0.0f ? __builtin_fmaf(a.beta, cv[q], v) : v;
+    }
+  }
 }
 
 bool aligned16(const void* p, int64_t ld) { return ((uintptr_t)p % 16 == 0) && (ld % 4 == 0); }
