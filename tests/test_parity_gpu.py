@@ -159,7 +159,10 @@ def test_hessian_compute_overwrites(x_dtype, d, n, split):
 
 # ------------------------------------------------------------------ factor
 
-@pytest.mark.parametrize("d,act", [(300, False), (300, True), (129, True), (7, False), (640, False)])
+# 8250 and 8378: wide enough for the inverse to go two block steps at a time (an odd number of blocks,
+# then an even one whose last pair holds a ragged block)
+@pytest.mark.parametrize("d,act", [(300, False), (300, True), (129, True), (7, False), (640, False),
+                                   (8250, False), (8378, True)])
 def test_factor_parity(d, act):
     """U from the same float32 H against the oracle's float64 U: the largest elementwise error
     (relative to max |U|) and the residual U^T U Hhat - I each within FACTOR_VS_LAPACK times what
