@@ -582,9 +582,10 @@ hipError_t factor(const float* H, int64_t d, int64_t n, double damp, int act_ord
   // step j starts after Cholesky step j is complete, its trailing update included (that update reads
   // the column panel the inverse step overwrites), and touches only columns left of block j + 1,
   // which the later Cholesky steps neither read nor write. A cross-stream wait costs the host several
-  // microseconds, so hs waits once per TB Cholesky steps and then runs those TB inverse steps; the
-  // last TB steps go a pair at a time, so that after the last Cholesky step only one pair of inverse
-  // steps is left. With one_stream, hs is s itself and the steps simply follow one another.
+  // microseconds, so hs waits once per TB Cholesky steps (once per group of steps when the groups
+  // below are longer) and then runs those inverse steps; with pairs the last TB steps go a pair at a
+  // time, so that after the last Cholesky step only one pair of inverse steps is left. With
+  // one_stream, hs is s itself and the steps simply follow one another.
   constexpr int64_t TB = 4;
   Helpers* hp = nullptr;
   hipError_t e = hipSuccess;
@@ -712,35 +713,40 @@ hipError_t factor(const float* H, int64_t d, int64_t n, double damp, int act_ord
     }
     return hipSuccess;
   };
-  // The trailing updates go by pairs of steps (k, k + 1): after step k's panel solve only the next
-  // block column takes its update, A[k1:, k1:k2] -= P_k P_k[0:k2-k1]^T (its diagonal block whole: the
-  // part above the diagonal is never read and the diagonal kernel rewrites it); after step k + 1,
-  // the rest takes both panels' updates in one product, A[k2:, k2:] -= [P_k P_k+1] [P_k P_k+1]^T
-  // (lower part, K = 256: the two panels are adjacent columns of A).
+  // The trailing updates go by groups of G adjacent steps. After each panel solve of a group only the
+  // group's later block columns take its update, A[k1:, k1:ge] -= P_k P_k[0:ge-k1]^T (their diagonal
+  // blocks whole: the part above the diagonal is never read and the diagonal kernel rewrites it);
+  // after the group's last step the rest takes all of the group's panels in one product,
+  // A[ge:, ge:] -= P P^T (lower part, K = G NB: the panels are adjacent columns of A).
+  // G: 2 below d = 8192, 4 up to 32768, 8 beyond (measured: d = 49152 786 ms with pairs, 740 with
+  // groups of 4, 721 with 8; d = 11008 13.6, 13.4 and 13.5 ms; d = 4096 keeps pairs, whose
+  // diagonal blocks set its pace)
+  const int64_t G = d >= 32768 ? 8 : d >= 8192 ? 4 : 2;
   for (int64_t kt = 0, kend = 0; kt < nblk && e == hipSuccess; kt = kend) {
-    // batches of TB steps, the last ones a pair at a time; a batch ends after a pair's product
-    kend = std::min(nblk, kt + TB <= nblk - TB ? kt + TB : kt + 2);
-    for (int64_t k = kt; k < kend && e == hipSuccess; k += 2) {
-      const int64_t k0 = k * NB, k1 = std::min(d, k0 + NB), kb = k1 - k0;
-      if ((e = chol_step(k)) != hipSuccess) break;
-      if (k1 >= d) break;
-      const int64_t k2 = std::min(d, k1 + NB);
-      GemmArgs ua{};
-      ua.M = d - k1; ua.N = k2 - k1; ua.K = kb;
-      ua.A = U + k1 * d + k0; ua.lda = d; ua.transA = 0;
-      ua.B = U + k1 * d + k0; ua.ldb = d; ua.transB = 1;
-      ua.C = U + k1 * d + k1; ua.ldc = d;
-      ua.alpha = -1.0f; ua.beta = 1.0f; ua.tri = 0;
-      if ((e = gemm_f32(ua, s)) != hipSuccess) break;
-      if ((e = chol_step(k + 1)) != hipSuccess) break;
-      if (k2 < d) {
+    // batches of TB steps that end on group boundaries, the last ones a group at a time
+    kend = G > 2 ? std::min(nblk, kt + G) : std::min(nblk, kt + TB <= nblk - TB ? kt + TB : kt + 2);
+    for (int64_t g0 = kt; g0 < kend && e == hipSuccess; g0 += G) {
+      const int64_t gend = std::min(kend, g0 + G), ge = std::min(d, gend * NB);
+      for (int64_t k = g0; k < gend && e == hipSuccess; ++k) {
+        const int64_t k0 = k * NB, k1 = std::min(d, k0 + NB), kb = k1 - k0;
+        if ((e = chol_step(k)) != hipSuccess) break;
+        if (k1 >= ge) break;
+        GemmArgs ua{};
+        ua.M = d - k1; ua.N = ge - k1; ua.K = kb;
+        ua.A = U + k1 * d + k0; ua.lda = d; ua.transA = 0;
+        ua.B = U + k1 * d + k0; ua.ldb = d; ua.transB = 1;
+        ua.C = U + k1 * d + k1; ua.ldc = d;
+        ua.alpha = -1.0f; ua.beta = 1.0f; ua.tri = 0;
+        e = gemm_f32(ua, s);
+      }
+      if (e == hipSuccess && ge < d) {
         GemmArgs ub{};
-        ub.M = d - k2; ub.N = d - k2; ub.K = k2 - k0;
-        ub.A = U + k2 * d + k0; ub.lda = d; ub.transA = 0;
-        ub.B = U + k2 * d + k0; ub.ldb = d; ub.transB = 1;
-        ub.C = U + k2 * d + k2; ub.ldc = d;
+        ub.M = d - ge; ub.N = d - ge; ub.K = ge - g0 * NB;
+        ub.A = U + ge * d + g0 * NB; ub.lda = d; ub.transA = 0;
+        ub.B = U + ge * d + g0 * NB; ub.ldb = d; ub.transB = 1;
+        ub.C = U + ge * d + ge; ub.ldc = d;
         ub.alpha = -1.0f; ub.beta = 1.0f; ub.tri = 1;
-        if ((e = gemm_f32(ub, s)) != hipSuccess) break;
+        e = gemm_f32(ub, s);
       }
     }
     if (e != hipSuccess) break;
