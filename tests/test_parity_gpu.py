@@ -276,6 +276,10 @@ QCASES = [
     dict(bits=4, group_size=128, block_size=8),
     dict(bits=4, group_size=384, block_size=128, d=1000),   # super-blocks narrowed to nest with groups
     dict(bits=4, group_size=200, block_size=100, d=700),    # padded error slots overlap the next block's
+    # 1024 rows or more and more than two 512-column super-blocks: the column loop overlaps the far
+    # products on the helper stream
+    dict(bits=4, group_size=128, block_size=128, d=1600, rows=1100),
+    dict(bits=3, group_size=64, block_size=128, d=1700, rows=1030),
 ]
 
 
