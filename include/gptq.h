@@ -164,7 +164,7 @@ gptq_status_t gptq_factor(const float *H, int64_t d, int64_t n_total, const gptq
  * gptq_factor for callers that cannot allocate device memory: code under HIP graph capture, tight
  * serving loops, harnesses that forbid allocation. Same arguments, results and errors as
  * gptq_factor, without `work`: its workspace is a static device array inside the library (about
- * 19 MB, held on each device the library runs on until the process ends), and every launch goes to
+ * 25 MB, held on each device the library runs on until the process ends), and every launch goes to
  * `stream` (no helper stream or event is created). The call allocates nothing; the caller still
  * passes H, U and perm (U == H allowed, as for gptq_factor).
  *

@@ -154,7 +154,7 @@ gptq_status_t gptq_factor_noalloc(const float* H, int64_t d, int64_t n_total, co
   if (st != GPTQ_OK) return st;
   if (d > GPTQ_FACTOR_NOALLOC_MAX_D) return GPTQ_EUNSUPPORTED;
   static_assert(GPTQ_FACTOR_NOALLOC_MAX_D == gptq::kNoallocMaxD, "scratch sized for another maximum");
-  if (gptq::factor_workspace_bytes(d, true) > gptq::kNoallocScratchBytes) return GPTQ_EUNSUPPORTED;
+  if (gptq::factor_workspace_bytes(d) > gptq::kNoallocScratchBytes) return GPTQ_EUNSUPPORTED;
   void* scratch = nullptr;
   if (gptq::noalloc_scratch(&scratch) != hipSuccess) return GPTQ_EHIP;
   return factor_call(H, d, n_total, p, U, perm, scratch, info, static_cast<hipStream_t>(stream), true);

@@ -131,7 +131,7 @@ hipError_t zero_matrix(float* H, int64_t n, hipStream_t s);
 // Factor: damping, processing order and U (see factor.hip). status_dev / info_dev receive device
 // addresses of the mean-diagonal check and the first failed pivot (1-based, reversed order).
 // one_stream: everything runs on s (no helper stream, event or mutex is created or used).
-size_t factor_workspace_bytes(int64_t d, bool one_stream = false);
+size_t factor_workspace_bytes(int64_t d);
 hipError_t factor(const float* H, int64_t d, int64_t n, double damp, int act_order, float* U, int32_t* perm,
                   void* work, hipStream_t s, int** status_dev, int64_t** info_dev, bool one_stream = false);
 
@@ -139,7 +139,7 @@ hipError_t factor(const float* H, int64_t d, int64_t n, double damp, int act_ord
 // a static device array of kNoallocScratchBytes, looked up once per device.
 constexpr int64_t kNoallocMaxD = 12288;
 constexpr size_t kNoallocScratchBytes =
-    256 + ((size_t)kNoallocMaxD * 4 + 255) / 256 * 256 + 3 * (size_t)kNoallocMaxD * 128 * 4;
+    256 + ((size_t)kNoallocMaxD * 4 + 255) / 256 * 256 + 4 * (size_t)kNoallocMaxD * 128 * 4;
 hipError_t noalloc_scratch(void** ptr);
 
 // Helper streams and events of the current device for work that overlaps within one call (created

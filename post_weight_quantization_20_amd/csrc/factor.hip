@@ -540,13 +540,10 @@ size_t chol_smem() { return ((size_t)2 * NB * LDB + 4 * SB * LDT) * sizeof(float
 }  // namespace
 
 // Workspace: the status words, the sort keys, and the panel buffers that stage the operand of the
-// products that overwrite their own input: d x NB floats on the caller's stream, and on the helper
-// stream d x NB for row panels and d x 2 NB for the two column panels of a pair of inverse steps
-// (d x NB when everything runs on one stream and the inverse goes one step at a time).
+// products that overwrite their own input: d x NB floats for the Cholesky's panel solve, and for the
+// inverse d x NB for row panels and d x 2 NB for the two column panels of a pair of steps.
 size_t factor_keys_bytes(int64_t d) { return ((size_t)d * sizeof(float) + 255) / 256 * 256; }
-size_t factor_workspace_bytes(int64_t d, bool one_stream) {
-  return 256 + factor_keys_bytes(d) + (one_stream ? 3 : 4) * (size_t)d * NB * sizeof(float);
-}
+size_t factor_workspace_bytes(int64_t d) { return 256 + factor_keys_bytes(d) + 4 * (size_t)d * NB * sizeof(float); }
 
 // Returns hipSuccess after queueing everything; *status_out / *info_out are device addresses of the
 // status word and pivot index (read by the caller after a stream synchronisation).
@@ -560,7 +557,7 @@ hipError_t factor(const float* H, int64_t d, int64_t n, double damp, int act_ord
   w.keys = reinterpret_cast<float*>(wb + 256);
   float* stage_main = reinterpret_cast<float*>(wb + 256 + factor_keys_bytes(d));   // d x NB, caller's stream
   float* stage_row = stage_main + d * NB;                                           // NB x d, helper stream
-  float* stage_col = stage_row + d * NB;                           // d x 2 NB (d x NB with one_stream), helper stream
+  float* stage_col = stage_row + d * NB;                                            // d x 2 NB, helper stream
   *status_dev = w.status;
   *info_dev = w.info;
 
@@ -755,10 +752,11 @@ hipError_t factor(const float* H, int64_t d, int64_t n, double damp, int act_ord
       if ((e = hipStreamWaitEvent(hs, ev_step, 0)) != hipSuccess) break;
     }
     // inverse steps kt .. kend - 1 on hs (their diagonal blocks are already inverted), a pair at a
-    // time when a second panel buffer is there and the products are large enough for K = 2 NB to pay
-    // (measured: 3 % faster at d = 11008, 9 % at d = 49152, 2 % slower at d = 4096)
+    // time where the products are large enough for K = 2 NB to pay (measured: 3 % faster at
+    // d = 11008, 9 % at d = 49152, 2 % slower at d = 4096); the same steps with one_stream, so that
+    // both give the same U bit for bit
     for (int64_t k = kt; k < kend && e == hipSuccess;) {
-      if (!one_stream && d >= 8192 && k + 1 < kend) {
+      if (d >= 8192 && k + 1 < kend) {
         e = inv_pair(k);
         k += 2;
       } else {
