@@ -107,8 +107,8 @@ typedef struct {
  * Technical Guide, "Computing the Hessian": a sum of outer products of the layer inputs).
  *
  *   H      device float[d * d]. Accumulated in place; zero it before the first chunk. Only the
- *          upper triangle (i <= j) is written and authoritative; entries below the diagonal are
- *          left as they were except inside 256 x 256 diagonal tiles.
+ *          upper triangle (i <= j) is authoritative; entries below the diagonal are left as they
+ *          were, except inside 256 x 256 diagonal tiles, where they may take their part of the sum.
  *   d      number of input features, >= 1.
  *   X      device array [n_tok x ld_x] of x_dtype (GPTQ_F32, GPTQ_F16 or GPTQ_BF16), token-major:
  *          row t holds the d features of token t. Not modified. May be NULL when n_tok == 0.
@@ -128,9 +128,9 @@ gptq_status_t gptq_hessian_accumulate(float *H, int64_t d, const void *X, int32_
  * H = 2 * X^T X over one chunk of calibration tokens: gptq_hessian_accumulate for the first chunk,
  * without zeroing H first (the same source passages). Same arguments and errors as
  * gptq_hessian_accumulate. H's upper triangle (i <= j) is overwritten and H is not read; entries
- * below the diagonal are written inside 256 x 256 diagonal tiles only, as there. With n_tok == 0
- * the whole of H is set to zero. The result is bit for bit that of zeroing H and calling
- * gptq_hessian_accumulate with the same chunk and workspace.
+ * below the diagonal are written inside 256 x 256 diagonal tiles only (their part of the sum, or
+ * zero). With n_tok == 0 the whole of H is set to zero. The result is bit for bit that of zeroing H
+ * and calling gptq_hessian_accumulate with the same chunk and workspace.
  */
 gptq_status_t gptq_hessian_compute(float *H, int64_t d, const void *X, int32_t x_dtype, int64_t n_tok,
                                    int64_t ld_x, void *work, size_t work_bytes, void *stream);

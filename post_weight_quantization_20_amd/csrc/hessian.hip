@@ -481,6 +481,16 @@ GPTQ_DEV void dma_tile(const HessArgs& a, const Work& w, floatx16 (&acc)[4][4], 
   for (int s = 0; s < NST && s < nst; ++s) issue(s);
   if (nst <= 0) return;
   stage_wait<L>(min(NST - 1, nst - 1));
+  if (DIAG && wm == 1 && wn == 0) {
+    // On a diagonal tile this wave's 128 x 128 quadrant lies below the diagonal, where H is not
+    // authoritative: it only loads its share of each stage and meets the barriers, and its sums
+    // stay zero (fewer matrix-core cycles for a kernel that the power limit holds back).
+    for (int it = 0; it < nst; ++it) {
+      stage_wait<L>(min(NST - 2, nst - 2 - it));
+      if (it + NST < nst) issue(it + NST);
+    }
+    return;
+  }
   V a0[4], b0[4], a1[4], b1[4];
   read_step(0, 0, a0, b0);
   for (int it = 0; it < nst; ++it) {
