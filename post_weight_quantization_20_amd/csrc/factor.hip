@@ -111,7 +111,7 @@ Copy2D make_copy(float* dst, int64_t ldd, const float* src, int64_t lds, int64_t
   return c;
 }
 
-// Workgroups for a copy of `rows` rows of up to NB columns (one per 4096 four-element pieces).
+// Workgroups for a copy of `rows` x `cols` (one per 4096 four-element pieces, at most 1024).
 unsigned copy_groups(int64_t rows, int64_t cols) {
   const int64_t pieces = std::max<int64_t>(rows, 0) * ((std::max<int64_t>(cols, 0) + 3) / 4);
   return (unsigned)std::min<int64_t>((pieces + 4095) / 4096, 1024);
@@ -576,9 +576,9 @@ hipError_t factor(const float* H, int64_t d, int64_t n, double damp, int act_ord
   }
   // Blocked right-looking Cholesky of the reversed matrix on the caller's stream (diagonal blocks end
   // up inverted), and the blocked right-looking inverse of the factor on a helper stream hs. Inverse
-  // step j starts after Cholesky step j is complete, its trailing update included (that update reads
-  // the column panel the inverse step overwrites), and touches only columns left of block j + 1,
-  // which the later Cholesky steps neither read nor write. A cross-stream wait costs the host several
+  // step j starts after the group of Cholesky steps that holds step j is complete, its trailing
+  // update included (that update reads the column panels the inverse steps overwrite), and touches
+  // only columns left of block j + 1, which the later Cholesky steps neither read nor write. A cross-stream wait costs the host several
   // microseconds, so hs waits once per TB Cholesky steps (once per group of steps when the groups
   // below are longer) and then runs those inverse steps; with pairs the last TB steps go a pair at a
   // time, so that after the last Cholesky step only one pair of inverse steps is left. With
