@@ -225,8 +225,12 @@ __global__ __launch_bounds__(256) void dq_fast_kernel(DqArgs a) {
 
 typedef _Float16 half4_t __attribute__((ext_vector_type(4)));
 
-// 3..16 input rows on the matrix cores. A workgroup owns 16 weight rows; its KS waves split the
-// columns into 128-column units (wave w takes unit pairs w, w + KS, ...), each unit inside one group.
+// 3..16 input rows on the matrix cores. A workgroup owns 16 NT weight rows; its KS waves split the
+// columns into 128-column units, four consecutive units (a quad) at a time (wave w takes quads
+// w, w + KS, ...), each unit inside one group. A quad's codes are 256 contiguous bytes of each row:
+// they are loaded four rows per instruction (16 bytes a lane along the run), which keeps the reads
+// of HBM in long runs, and go through a padded, wave-private LDS area to the operand layout below
+// (64-byte pieces of 16 rows per instruction streamed a third slower).
 // v_mfma_f32_16x16x16f16 with A = x (16 input rows, rows >= m zero) and B = the codes as exact fp16
 // integers accumulates T = sum x q over a unit; a second product with B = 1 gives sum x in the same
 // lanes, and s (T - z sum x) is added per unit. Lane l holds B[k][j] and A[i][k] for j, i = l % 16 and
@@ -235,19 +239,21 @@ typedef _Float16 half4_t __attribute__((ext_vector_type(4)));
 // The KS partial tiles are summed in LDS in wave order.
 template <int KS, int NT>
 __global__ __launch_bounds__(64 * KS) void dq_mfma_kernel(DqArgs a) {
-  __shared__ floatx4 part[KS][NT][64];
+  // a wave's staged quad: per tile 16 rows of 16 + 1 vectors of 16 bytes (the pad vector puts the
+  // 16 rows' reads of one vector in distinct banks); after the loop the area holds the partial tiles
+  constexpr int SROW = 17;
+  constexpr int STAGE = 16 * SROW;
+  __shared__ u32x4 stage[KS][NT][STAGE];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int jl = lane & 15, c = lane >> 4;
   // NT tiles of 16 weight rows share each unit's inputs (A operand) and its sum of x
   const int64_t j0 = (int64_t)blockIdx.x * 16 * NT;
-  const u32x4* prow[NT];
   const float* srow[NT];
   const int32_t* zrow[NT];
   const int64_t nw = a.d >> 3;
 #pragma unroll
   for (int t = 0; t < NT; ++t) {
     const int64_t row = min(j0 + 16 * t + jl, a.rows - 1);
-    prow[t] = reinterpret_cast<const u32x4*>(a.packed + row * nw);
     srow[t] = a.scales + row * a.ngroups;
     zrow[t] = a.zeros + row * a.ngroups;
   }
@@ -269,15 +275,6 @@ __global__ __launch_bounds__(64 * KS) void dq_mfma_kernel(DqArgs a) {
   };
   struct Inputs {
     u32x4 x[4];
-  };
-  auto load_codes = [&](uint32_t u, Codes& cd) {
-    const uint32_t grp = a.cpg ? u / a.cpg : 0u;
-#pragma unroll
-    for (int t = 0; t < NT; ++t) {
-      cd.w[t] = __builtin_nontemporal_load(prow[t] + 4 * (int64_t)u + c);
-      cd.sc[t] = srow[t][grp];
-      cd.z[t] = zrow[t][grp];
-    }
   };
   auto load_inputs = [&](uint32_t u, Inputs& in) {
 #pragma unroll
@@ -314,44 +311,74 @@ __global__ __launch_bounds__(64 * KS) void dq_mfma_kernel(DqArgs a) {
     }
   };
 
-  // Unit pairs w, w + KS, ... The codes of the next two pairs (one with two tiles, for registers) and
-  // the inputs of the next one are in flight while a pair is computed (the inputs come from L2, the
-  // codes from HBM).
-  constexpr bool kDeep = NT == 1;
-  const uint32_t pairs = (units + 1) / 2;
-  Codes c1[2], c2[kDeep ? 2 : 1];
-  Inputs x1[2];
-  auto fetch_codes = [&](uint32_t pr, Codes* cd) {
-    load_codes(2 * pr, cd[0]);
-    if (2 * pr + 1 < units) load_codes(2 * pr + 1, cd[1]);
+  // The wave's units in order: the four of quad w, then those of quad w + KS, and so on. When a quad
+  // starts, its codes (loaded one quad earlier) go to LDS and the wave's next quad is loaded; the
+  // metadata and inputs of each unit are loaded two units ahead.
+  const uint32_t quads = (units + 3) / 4;
+  const uint32_t nvec = 4 * units;   // 16-byte vectors of codes in a row
+  u32x4 raw[NT][4];
+  auto load_quad = [&](uint32_t q) {
+    const uint32_t v = 16 * q + (uint32_t)(lane & 15);
+#pragma unroll
+    for (int t = 0; t < NT; ++t)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int64_t row = min(j0 + 16 * t + 4 * i + (lane >> 4), a.rows - 1);
+        raw[t][i] = v < nvec ? __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(a.packed + row * nw) + v)
+                             : u32x4{0u, 0u, 0u, 0u};
+      }
   };
-  auto fetch_inputs = [&](uint32_t pr) {
-    load_inputs(2 * pr, x1[0]);
-    if (2 * pr + 1 < units) load_inputs(2 * pr + 1, x1[1]);
+  auto store_quad = [&]() {
+#pragma unroll
+    for (int t = 0; t < NT; ++t)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) stage[wave][t][(4 * i + (lane >> 4)) * SROW + (lane & 15)] = raw[t][i];
   };
-  const uint32_t p0 = wave;
-  if (p0 < pairs) {
-    fetch_codes(p0, c1);
-    fetch_inputs(p0);
-  }
-  if constexpr (kDeep) {
-    if (p0 + KS < pairs) fetch_codes(p0 + KS, c2);
-  }
-  for (uint32_t pr = p0; pr < pairs; pr += KS) {
-    const Codes k0 = c1[0], k1 = c1[1];
-    const Inputs i0 = x1[0], i1 = x1[1];
-    if constexpr (kDeep) {
-      c1[0] = c2[0];
-      c1[1] = c2[1];
-      if (pr + 2 * KS < pairs) fetch_codes(pr + 2 * KS, c2);
-    } else {
-      if (pr + KS < pairs) fetch_codes(pr + KS, c1);
+  auto load_meta = [&](uint32_t u, Codes& cd) {
+    const uint32_t grp = a.cpg ? u / a.cpg : 0u;
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+      cd.sc[t] = srow[t][grp];
+      cd.z[t] = zrow[t][grp];
     }
-    if (pr + KS < pairs) fetch_inputs(pr + KS);
-    unit(k0, i0);
-    if (2 * pr + 1 < units) unit(k1, i1);
+  };
+  auto next_unit = [&](uint32_t u) { return (u & 3u) != 3u && u + 1 < units ? u + 1 : (u & ~3u) + 4 * KS; };
+  uint32_t u = 4 * (uint32_t)wave;
+  uint32_t u1 = next_unit(u);
+  Codes cn, cn2;
+  Inputs xn, xn2;
+  if (u < units) {
+    load_quad((uint32_t)wave);
+    load_meta(u, cn);
+    load_inputs(u, xn);
   }
-
+  if (u1 < units) {
+    load_meta(u1, cn2);
+    load_inputs(u1, xn2);
+  }
+  while (u < units) {
+    if ((u & 3u) == 0) {
+      store_quad();
+      const uint32_t qn = u / 4 + KS;
+      if (qn < quads) load_quad(qn);
+    }
+    Codes cd = cn;
+    const Inputs xi = xn;
+#pragma unroll
+    for (int t = 0; t < NT; ++t) cd.w[t] = stage[wave][t][jl * SROW + 4 * (int)(u & 3u) + c];
+    cn = cn2;
+    xn = xn2;
+    const uint32_t u2 = u1 < units ? next_unit(u1) : u1;
+    if (u2 < units) {
+      load_meta(u2, cn2);
+      load_inputs(u2, xn2);
+    }
+    unit(cd, xi);
+    u = u1;
+    u1 = u2;
+  }
+  __syncthreads();   // every wave is done with its stage area, which now takes the partial tiles
+  floatx4 (*part)[NT][64] = reinterpret_cast<floatx4 (*)[NT][64]>(&stage[0][0][0]);
 #pragma unroll
   for (int t = 0; t < NT; ++t) part[wave][t][lane] = acc[t];
   __syncthreads();
@@ -648,8 +675,9 @@ hipError_t dequant_gemm(const void* x, int dtype, int64_t m, int64_t ldx, const 
       // units per group; waves per workgroup so that about 12 waves per CU are in flight
       a.cpg = g >= d ? 0u : (uint32_t)(g / 128);
       const int64_t tiles = (rows + 15) / 16;
-      if (tiles >= 768) {
-        // two 16-row tiles per wave share the inputs; 8 waves split the columns
+      if (tiles >= 768 && a.m > 4) {
+        // two 16-row tiles per wave share the inputs; 8 waves split the columns (with four inputs
+        // or fewer, one tile a wave and two workgroups a CU run faster: fc2 117 against 122 us)
         hipLaunchKernelGGL((dq_mfma_kernel<8, 2>), dim3((unsigned)((tiles + 1) / 2)), dim3(512), 0, s, a);
       } else {
         hipLaunchKernelGGL((dq_mfma_kernel<8, 1>), dim3((unsigned)tiles), dim3(512), 0, s, a);
