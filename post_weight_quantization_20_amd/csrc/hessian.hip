@@ -18,7 +18,7 @@
 // buffer descriptor's range check. A register-staged path (8x8 transposes in registers, then LDS)
 // covers X that is not 16-byte aligned or whose width is not a multiple of 8.
 //
-// When the upper-triangle tiles alone cannot fill the 256 CUs, the token range is split S ways.
+// When the upper-triangle tiles alone cannot fill the 256 CUs, the token range is split 8 ways.
 // Each split writes its partial tile to the workspace and a second kernel adds the partials of
 // every tile to H in token order across the whole GPU, so the result does not depend on
 // scheduling.
@@ -55,12 +55,13 @@ struct HessArgs {
   int64_t n, ldx;
   int T;               // tiles per dimension
   int ntiles;          // T (T + 1) / 2
-  int S;               // token splits: 1, or a multiple of 8 (split s runs on XCD s % 8)
+  int S;               // token splits: 1 or 8
   int per_xcd;         // S == 1: tiles per XCD (contiguous in the tile order)
-  int full;            // S > 1: workgroup slots per XCD that take a whole (tile, split) item
-  int q;               // S > 1: parts each remaining item is cut into
+  int full;            // S == 8: workgroup slots per XCD that take a whole (tile, split) item,
+                       // 32 times the number of whole 32-tile groups
+  int q;               // S == 8: parts each remaining item is cut into
   int64_t split_len;   // tokens per split (multiple of SPLIT_ALIGN)
-  float* partial;      // S > 1: one HT x HT partial tile per workgroup
+  float* partial;      // S == 8: one HT x HT partial tile per workgroup
   int vec;             // 16-byte loads allowed
   int overwrite;       // H's tiles are set to 2 X^T X instead of added to
 };
@@ -89,35 +90,38 @@ GPTQ_DEV void tile_at(int slot, int T, int& ti, int& tj) {
 }
 
 // Workgroup b runs on XCD b % 8 (32 CUs each). Without token splits, XCD x takes a contiguous run
-// of tiles over all tokens. With S = 8 m splits, XCD x takes splits x, x + 8, ...: its m * ntiles
-// (tile, split) items run 32 at a time in tile order, so the workgroups running together share
-// feature strips at the same tokens. Whole rounds of 32 items come first; the items of the last,
-// partial round are each cut into q token ranges so that that round fills the XCD too.
+// of tiles over all tokens. With 8 splits there are 8 ntiles (tile, split) items, ntiles per XCD:
+//  - Whole groups first. The tile order is cut into groups of 32 consecutive tiles, and XCD round r
+//    of XCD x (its slots 32 r .. 32 r + 31, which run together) takes group j % G of split j / G
+//    with j = 8 r + x and G groups in all. A round's 32 workgroups read the same tokens of one split
+//    and share its feature strips in the XCD's L2, and the XCDs running the same split at the same
+//    time (8 / G of them, or all 8 for G >= 8) read the same token range, so a line one XCD brings
+//    in from HBM serves the others' L2 misses from the Infinity Cache.
+//  - Then the tiles past the last whole group: XCD x takes them in split x, each cut into q token
+//    ranges so that this last, partial round fills the XCD too.
 struct Work {
   int tile, split, part, nparts;
   int64_t fa, fb, t_begin, t_end;
   bool diag;
 };
 
-GPTQ_DEV int xcd_items(const HessArgs& a) { return (a.S / 8) * a.ntiles; }
-
 GPTQ_DEV bool map_block(const HessArgs& a, Work& w) {
   const int xcd = blockIdx.x % 8, slot = blockIdx.x / 8;
   int64_t lo, hi;
   if (a.S > 1) {
-    int k;
     if (slot < a.full) {
-      k = slot;
+      const int j = 8 * (slot / 32) + xcd, ngroups = a.full / 32;
+      w.split = j / ngroups;
+      w.tile = (j % ngroups) * 32 + slot % 32;
       w.part = 0;
       w.nparts = 1;
     } else {
-      k = a.full + (slot - a.full) / a.q;
+      w.tile = a.full + (slot - a.full) / a.q;
+      w.split = xcd;
       w.part = (slot - a.full) % a.q;
       w.nparts = a.q;
-      if (k >= xcd_items(a)) return false;
+      if (w.tile >= a.ntiles) return false;
     }
-    w.tile = k % a.ntiles;
-    w.split = xcd + 8 * (k / a.ntiles);
     lo = (int64_t)w.split * a.split_len;
     hi = lo + a.split_len;
     if (w.nparts > 1) {
@@ -148,11 +152,11 @@ GPTQ_DEV bool map_block(const HessArgs& a, Work& w) {
 template <typename F>
 GPTQ_DEV void for_each_partial(const HessArgs& a, int tile, F&& f) {
   for (int split = 0; split < a.S; ++split) {
-    const int k = (split / 8) * a.ntiles + tile, xcd = split % 8;
-    if (k < a.full) {
-      f(8 * k + xcd);
+    if (tile < a.full) {
+      const int j = split * (a.full / 32) + tile / 32;
+      f(8 * (32 * (j / 8) + tile % 32) + j % 8);
     } else {
-      for (int p = 0; p < a.q; ++p) f(8 * (a.full + (k - a.full) * a.q + p) + xcd);
+      for (int p = 0; p < a.q; ++p) f(8 * (a.full + (tile - a.full) * a.q + p) + split);
     }
   }
 }
@@ -549,7 +553,7 @@ __global__ __launch_bounds__(256) void hess_kernel(HessArgs a) {
 }
 
 // Token splits: none when the tiles alone give every CU three or more workgroups or when there are
-// too few tokens; otherwise 8, one per XCD (the partial last round is cut finer, see map_block).
+// too few tokens; otherwise 8 (the partial last round is cut finer, see map_block).
 int choose_splits(int64_t ntiles, int64_t n) {
   if (ntiles >= 3 * NCU) return 1;
   if (n < 8 * 16 * HK) return 1;
@@ -585,9 +589,8 @@ Plan plan(int64_t n, int64_t d) {
   p.per_xcd = (p.ntiles + 7) / 8;
   if (p.S > 1) {
     constexpr int PER = NCU / 8;    // CUs per XCD
-    const int items = (p.S / 8) * p.ntiles;
-    p.full = items / PER * PER;
-    const int r = items - p.full;
+    p.full = p.ntiles / PER * PER;    // whole 32-tile groups
+    const int r = p.ntiles - p.full;
     p.q = r > 0 ? std::max(1, PER / r) : 1;
     // parts shorter than a few stages are not worth their partial tiles
     while (p.q > 1 && p.split_len / p.q < 8 * SPLIT_ALIGN) --p.q;

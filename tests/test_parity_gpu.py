@@ -110,10 +110,12 @@ def test_hessian_strided_views(width, offset):
     _check_hessian(H.cpu().numpy(), [x], "f16")
 
 
-@pytest.mark.parametrize("d", [260, 264])
+@pytest.mark.parametrize("d", [260, 264, 3848])
 def test_hessian_deterministic_with_token_splits(d):
     """One long chunk (token splits with the ordered fixup) gives the same H twice, bit for bit, and
-    matches the float64 sum (d = 264 streams through LDS directly, d = 260 through registers)."""
+    matches the float64 sum (d = 264 streams through LDS directly, d = 260 through registers; at
+    d = 3848, 136 tiles with a ragged last one, four whole 32-tile groups run split by split and the
+    last 8 tiles are cut into token parts)."""
     torch = torch_cuda()
     import post_weight_quantization_20_amd as g
     case = _case("h2", 12, d=d, n=8192, chunk=8192)
@@ -130,7 +132,7 @@ def test_hessian_deterministic_with_token_splits(d):
 
 
 @pytest.mark.parametrize("x_dtype,d,n", [("f16", 264, 8192), ("f16", 260, 8192), ("bf16", 300, 1000),
-                                         ("f32", 300, 1000), ("f16", 776, 700)])
+                                         ("f32", 300, 1000), ("f16", 776, 700), ("bf16", 4096, 9000)])
 @pytest.mark.parametrize("split", [True, False])
 def test_hessian_compute_overwrites(x_dtype, d, n, split):
     """gptq_hessian_compute on an H full of NaN gives, on and above the diagonal, bit for bit what
