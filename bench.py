@@ -23,6 +23,7 @@ import argparse
 import hashlib
 import json
 import os
+import subprocess
 import sys
 import time
 
@@ -57,6 +58,9 @@ def parse():
                          "the same order in every call (gptq_pack_ordered, gptq_permute_columns)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run one plain 1 GiB device-to-device copy (a known-size reference for HBM counters)")
+    ap.add_argument("--sustained-hessian", type=float, default=None, metavar="SECONDS",
+                    help="run gptq_hessian_compute back to back on the workload for about this long and report "
+                         "its time per call with the package power and shader clocks amd-smi reads meanwhile")
     return ap.parse_args()
 
 
@@ -410,6 +414,67 @@ def block_cpu_baseline(case, W, X):
     }
 
 
+def smi_sample():
+    """Socket power (W) and the per-XCD shader clocks (MHz) that amd-smi reports, or None."""
+    try:
+        r = subprocess.run(["amd-smi", "metric", "-p", "-c", "--json"], capture_output=True, text=True, timeout=30)
+        j = json.loads(r.stdout[r.stdout.index("{"):r.stdout.rindex("}") + 1])
+        gd = j["gpu_data"][0]
+        clk = gd["clock"]
+        return {"socket_power_w": gd["power"]["socket_power"]["value"],
+                "gfx_mhz": [clk[k]["clk"]["value"] for k in sorted(clk) if k.startswith("gfx_")],
+                "mem_mhz": clk.get("mem_0", {}).get("clk", {}).get("value")}
+    except (OSError, ValueError, KeyError, IndexError, TypeError, subprocess.TimeoutExpired):
+        return None
+
+
+def bench_sustained_hessian(args):
+    """gptq_hessian_compute back to back for about args.sustained_hessian seconds: the time per call
+    under sustained load, with amd-smi's power and clock readings taken while it runs (the Hessian is
+    the kernel that draws the package to its power limit)."""
+    import torch
+    import post_weight_quantization_20_amd as g
+    import synth
+
+    case = synth.case_from_config(args.workload)
+    dev = torch.device("cuda:0")
+    d, n = case.d, case.n
+    print(f"[bench] generating {args.workload}: X {n}x{d} {case.x_dtype}", file=sys.stderr, flush=True)
+    X = torch.from_numpy(synth.x_tokens(case)).to(dev)
+    H = torch.empty((d, d), dtype=torch.float32, device=dev)
+    ws = torch.empty(max(1, g.gptq_workspace_bytes(g.GPTQ_WS_HESSIAN, n, d)), dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream()
+    for _ in range(5):
+        g.gptq_hessian_compute(H, X, work=ws)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    g.gptq_hessian_compute(H, X, work=ws)
+    torch.cuda.synchronize()
+    calls = max(10, int(args.sustained_hessian / max(time.perf_counter() - t0, 1e-4)))
+    idle = smi_sample()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(calls):
+        g.gptq_hessian_compute(H, X, work=ws)
+    e1.record(stream)
+    samples = []
+    t_end = time.perf_counter() + 0.8 * args.sustained_hessian
+    while time.perf_counter() < t_end:
+        time.sleep(0.5)
+        s = smi_sample()
+        if s is not None:
+            samples.append(s)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / calls
+    flops = float(n) * d * (d + 1)
+    out = {"metric": "hess_kernel under sustained load (gptq_hessian_compute back to back)", "value": round(ms, 4),
+           "unit": "ms per call", "higher_is_better": False, "calls": calls, "dtype": "f16 products, f32 sums",
+           "data": "synthetic (seeded)", "config": {"workload": f"{args.workload}: X {n}x{d} {case.x_dtype}"},
+           "achieved_tflops": round(flops / ms / 1e9, 1), "frac_of_fp16_peak": round(flops / ms / 1e9 / 2500.0, 4),
+           "smi_idle": idle, "smi_during": samples}
+    print(json.dumps(out), flush=True)
+
+
 def bench_block(args):
     import torch
     import post_weight_quantization_20_amd as g
@@ -507,6 +572,9 @@ def main():
         return
     if args.block:
         bench_block(args)
+        return
+    if args.sustained_hessian:
+        bench_sustained_hessian(args)
         return
 
     import torch
