@@ -652,15 +652,42 @@ __global__ __launch_bounds__(256) void static_grid_kernel(const void* __restrict
 }
 
 // Working copy in processing order: Wp[r][j] = W[r][perm[j]] as fp32; zero padding to ldw (a
-// multiple of 4). A thread writes four consecutive columns, as one 16-byte store when Wp allows.
+// multiple of 4). A thread writes four consecutive columns, as one 16-byte store when Wp allows. With
+// pvec (perm 16-byte aligned, W's rows starting on 4-element boundaries of an aligned base), a thread
+// reads its four entries of perm at once, and where they are four consecutive columns it reads their
+// weights with one 8-byte (fp16, bf16) or 16-byte (fp32) load.
 __global__ __launch_bounds__(256) void gather_w_kernel(const void* __restrict__ W, int dtype, int64_t ldw_in,
                                                        int64_t rows, int64_t d, const int32_t* __restrict__ perm,
-                                                       float* __restrict__ Wp, int64_t ldw, int vec) {
+                                                       float* __restrict__ Wp, int64_t ldw, int vec, int pvec) {
   for (int64_t r = blockIdx.y; r < rows; r += gridDim.y)
     for (int64_t j = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4; j < ldw; j += (int64_t)gridDim.x * 1024) {
       float v[4];
+      bool done = false;
+      if (pvec && j + 4 <= d) {
+        const int4 pj = *reinterpret_cast<const int4*>(perm + j);
+        const int64_t e = r * ldw_in + pj.x;
+        if (pj.y == pj.x + 1 && pj.z == pj.x + 2 && pj.w == pj.x + 3 && e % 4 == 0) {
+          if (dtype == F32) {
+            const float4 q = *reinterpret_cast<const float4*>(static_cast<const float*>(W) + e);
+            v[0] = q.x; v[1] = q.y; v[2] = q.z; v[3] = q.w;
+          } else {
+            const uint2 q = *reinterpret_cast<const uint2*>(static_cast<const uint16_t*>(W) + e);
+            const uint16_t h[4] = {(uint16_t)(q.x & 0xffffu), (uint16_t)(q.x >> 16), (uint16_t)(q.y & 0xffffu),
+                                   (uint16_t)(q.y >> 16)};
 #pragma unroll
-      for (int t = 0; t < 4; ++t) v[t] = (j + t < d) ? load_as_f32(W, dtype, r * ldw_in + perm[j + t]) : 0.0f;
+            for (int t = 0; t < 4; ++t) v[t] = dtype == F16 ? (float)__builtin_bit_cast(_Float16, h[t]) : bf16_bits_to_f32(h[t]);
+          }
+        } else {
+          const int pp[4] = {pj.x, pj.y, pj.z, pj.w};
+#pragma unroll
+          for (int t = 0; t < 4; ++t) v[t] = load_as_f32(W, dtype, r * ldw_in + pp[t]);
+        }
+        done = true;
+      }
+      if (!done) {
+#pragma unroll
+        for (int t = 0; t < 4; ++t) v[t] = (j + t < d) ? load_as_f32(W, dtype, r * ldw_in + perm[j + t]) : 0.0f;
+      }
       float* o = Wp + r * ldw + j;
       if (vec) {
         *reinterpret_cast<float4*>(o) = make_float4(v[0], v[1], v[2], v[3]);
@@ -689,7 +716,9 @@ __global__ void index_kernel(const int32_t* __restrict__ perm, int64_t d, int64_
 }
 
 // codes[r][c] = codes_p[r][iperm[c]] (back to the original column order). A thread writes four
-// consecutive codes, as one 4-byte store when the row allows.
+// consecutive codes, as one 4-byte store when the row allows; iperm (in the workspace, 16-byte
+// aligned) is read four entries at a time, and where they are four consecutive positions starting
+// on a 4-byte boundary the codes are read with one 4-byte load.
 __global__ __launch_bounds__(256) void unpermute_kernel(const uint8_t* __restrict__ codes_p, int64_t rows, int64_t d,
                                                         const int32_t* __restrict__ iperm, uint8_t* __restrict__ codes,
                                                         int vec) {
@@ -698,8 +727,12 @@ __global__ __launch_bounds__(256) void unpermute_kernel(const uint8_t* __restric
       const uint8_t* src = codes_p + r * d;
       uint8_t* dst = codes + r * d + c;
       if (vec && c + 4 <= d) {
-        const uint32_t w = src[iperm[c]] | (src[iperm[c + 1]] << 8) | (src[iperm[c + 2]] << 16) |
-                           ((uint32_t)src[iperm[c + 3]] << 24);
+        const int4 ic = *reinterpret_cast<const int4*>(iperm + c);
+        uint32_t w;
+        if (ic.y == ic.x + 1 && ic.z == ic.x + 2 && ic.w == ic.x + 3 && (r * d + ic.x) % 4 == 0)
+          w = *reinterpret_cast<const uint32_t*>(src + ic.x);
+        else
+          w = src[ic.x] | (src[ic.y] << 8) | (src[ic.z] << 16) | ((uint32_t)src[ic.w] << 24);
         *reinterpret_cast<uint32_t*>(dst) = w;
       } else {
         for (int64_t t = 0; t < 4 && c + t < d; ++t) dst[t] = src[iperm[c + t]];
@@ -933,8 +966,10 @@ hipError_t quantize(const void* W, int w_dtype, int64_t rows, int64_t d, int64_t
   if (rows > 0) {
     const unsigned gx = (unsigned)std::min<int64_t>((L.ldw + 1023) / 1024, 64);
     const int vec = (uintptr_t)Wp % 16 == 0;
+    const int esz = w_dtype == F32 ? 4 : 2;
+    const int pvec = (uintptr_t)perm % 16 == 0 && (uintptr_t)W % (4 * esz) == 0;
     hipLaunchKernelGGL(gather_w_kernel, dim3(gx, (unsigned)std::min<int64_t>(rows, 65535)), dim3(256), 0, s, W, w_dtype,
-                       ld_w, rows, d, perm, Wp, L.ldw, vec);
+                       ld_w, rows, d, perm, Wp, L.ldw, vec, pvec);
     hipLaunchKernelGGL(zero_f64, dim3((unsigned)((rows + 255) / 256)), dim3(256), 0, s, row_loss, rows);
   }
   mark(2);
