@@ -716,9 +716,9 @@ __global__ void index_kernel(const int32_t* __restrict__ perm, int64_t d, int64_
 }
 
 // codes[r][c] = codes_p[r][iperm[c]] (back to the original column order). A thread writes four
-// consecutive codes, as one 4-byte store when the row allows; iperm (in the workspace, 16-byte
-// aligned) is read four entries at a time, and where they are four consecutive positions starting
-// on a 4-byte boundary the codes are read with one 4-byte load.
+// consecutive codes. With vec (rows of 4-byte multiples, codes and codes_p 4-byte aligned, iperm
+// 16-byte aligned) it reads four entries of iperm at once, reads the codes with one 4-byte load where
+// they are four consecutive positions starting on a 4-byte boundary, and stores them as one word.
 __global__ __launch_bounds__(256) void unpermute_kernel(const uint8_t* __restrict__ codes_p, int64_t rows, int64_t d,
                                                         const int32_t* __restrict__ iperm, uint8_t* __restrict__ codes,
                                                         int vec) {
@@ -1015,7 +1015,7 @@ hipError_t quantize(const void* W, int w_dtype, int64_t rows, int64_t d, int64_t
   }
   if (rows > 0) {
     const unsigned gx = (unsigned)std::min<int64_t>((d + 1023) / 1024, 64);
-    const int vec = (uintptr_t)codes % 4 == 0 && d % 4 == 0;
+    const int vec = (uintptr_t)codes % 4 == 0 && d % 4 == 0 && (uintptr_t)iperm % 16 == 0 && (uintptr_t)codes_p % 4 == 0;
     hipLaunchKernelGGL(unpermute_kernel, dim3(gx, (unsigned)std::min<int64_t>(rows, 65535)), dim3(256), 0, s, codes_p,
                        rows, d, iperm, codes, vec);
   }
